@@ -1,0 +1,72 @@
+"""Drive the oracle through a whole decode-step workload -- TEST INFRASTRUCTURE.
+
+Steps, mirroring what a serving engine does for one decode iteration after
+its prompts are cached:
+  1. cache every prompt token's K/V into its slot (the oracle's own write),
+  2. copy the blocks the copy-on-write plan lists,
+  3. cache the token each sequence appends,
+  4. decode attention for each sequence's query over its whole context.
+All inputs come from ``workloads``; slots/tables/pairs from ``oracle.paging``.
+"""
+from __future__ import annotations
+
+from typing import Optional, Sequence
+
+import numpy as np
+import torch
+
+import workloads
+from . import HostPool
+from .paging import plan
+
+
+class OracleRun:
+    def __init__(self, wl, prompts: Optional[Sequence[int]] = None, scales=None, prompt_kv=None,
+                 free_order=None):
+        """prompts: restrict the prompt writes to these prompts (sampled checks);
+        scales: precomputed (k_scale, v_scale) for fp8 pools;
+        prompt_kv: optional dict prompt -> (k, v) already drawn;
+        free_order: override the workload's free-list order (placement tests)."""
+        self.wl = wl
+        order = workloads.free_list_order(wl) if free_order is None else free_order
+        self.plan = plan(wl, order)
+        ks, vs = scales if scales is not None else workloads.fp8_scales(wl)
+        self.k_scale, self.v_scale = ks, vs
+        self.pool = HostPool(wl.num_blocks, wl.block_size, wl.num_kv_heads, wl.head_dim, wl.kv_dtype, ks, vs)
+        todo = range(wl.num_prompts) if prompts is None else prompts
+        for p in todo:
+            if wl.prompt_lens[p] == 0:
+                continue
+            k, v = prompt_kv[p] if prompt_kv is not None and p in prompt_kv else workloads.prompt_kv(wl, p)
+            self.pool.reshape_and_cache(k, v, wl.src_dtype, self.plan["prompt_slots"][p])
+        self.pool.copy_blocks(self.plan["pairs"])
+        kn, vn = workloads.new_kv(wl)
+        slots = self.plan["new_slots"]
+        if prompts is not None:
+            keep = np.isin(np.asarray(wl.parent), np.asarray(list(prompts)))
+            slots = np.where(keep, slots, -1)
+        self.pool.reshape_and_cache(kn, vn, wl.src_dtype, slots)
+        self.q = workloads.q_values(wl)
+
+    @property
+    def tables(self) -> np.ndarray:
+        return self.plan["tables"]
+
+    def decode(self, seqs: Optional[Sequence[int]] = None) -> np.ndarray:
+        wl = self.wl
+        return self.pool.decode(self.q, wl.q_dtype, self.tables, wl.context_lens, wl.scale, wl.num_q_heads, seqs)
+
+
+def tolerance(kv_dtype: str):
+    """(atol, rtol) of the elementwise bound |gpu - oracle| <= atol + rtol*|oracle|."""
+    return (2e-3, 5e-2) if kv_dtype == "fp8e4m3" else (2e-3, 1e-2)
+
+
+def check_close(got: np.ndarray, want: np.ndarray, kv_dtype: str) -> None:
+    atol, rtol = tolerance(kv_dtype)
+    got = np.asarray(got, dtype=np.float64)
+    bad = ~(np.abs(got - want) <= atol + rtol * np.abs(want))
+    if bad.any():
+        idx = np.argwhere(bad)[:5]
+        raise AssertionError(f"{int(bad.sum())} of {bad.size} elements out of tolerance; first {idx.tolist()}: "
+                             f"got {got[tuple(idx.T)]}, want {want[tuple(idx.T)]}")

@@ -1,0 +1,293 @@
+"""Seeded synthetic inputs for paged decode attention.
+
+This module only *draws* inputs: configuration shapes, context lengths, the
+order of the free-block list (which fixes where blocks land in the pool), and
+the values of q and of every token's K/V.  It contains none of the paged
+attention arithmetic (no slot/offset math, no block allocation, no attention,
+no quantisation), so both the HIP path and the CPU oracle can consume it
+without sharing any of the method's code.
+
+Shapes follow the workloads the pages describe:
+  * LLaMA-13B-like head shapes (40 heads x 128) -- page "vLLM KV Cache 实现机制",
+    §2.2 (capacity estimate).
+  * LLaMA-7B-like heads (32 x 128) at max_num_seqs 256 -- same page, §5.1
+    (launch flags) and page "vLLM — 把操作系统的分页搬进 GPU KV cache", case 1.
+  * Parallel sampling with n = 4 candidates sharing a prompt -- the latter
+    page, case 2.
+  * block_size 16 by default, 32 as the alternative -- page "vLLM 与 KV Cache",
+    how-it-works point 1, and "vLLM KV Cache 实现机制" §2.3 table.
+  * fp8 KV cache dtype -- "vLLM KV Cache 实现机制" §2.3 table.
+
+Every random stream comes from numpy's SeedSequence with entropy
+449000 + config index and a spawn key naming the stream, so any piece (one
+sequence's K/V, the q tensor, the lengths) can be regenerated on its own.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+from concurrent.futures import ThreadPoolExecutor
+from typing import Dict, List, Optional, Sequence, Tuple
+
+import numpy as np
+import torch
+
+# dtype names used across the repository (the C ABI uses the same order)
+DTYPES = ("f32", "f16", "bf16", "fp8e4m3")
+TORCH_DTYPE = {
+    "f32": torch.float32,
+    "f16": torch.float16,
+    "bf16": torch.bfloat16,
+    "fp8e4m3": torch.float8_e4m3fn,
+}
+ELEM_BYTES = {"f32": 4, "f16": 2, "bf16": 2, "fp8e4m3": 1}
+
+# spawn-key streams
+_STREAM_LENS, _STREAM_PLACE, _STREAM_Q, _STREAM_PROMPT_KV, _STREAM_NEW_KV = 0, 1, 2, 3, 4
+
+POISON_BYTE = 0xFF  # NaN bit pattern in every supported KV dtype
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    """One decode-step workload.
+
+    Sequences are grouped under prompts: sequence ``s`` continues prompt
+    ``parent[s]`` (prompt_len tokens already cached) with one new token, so its
+    context length after the step is ``prompt_lens[parent[s]] + 1``.  When
+    several sequences share a parent they are parallel-sampling candidates that
+    share the prompt's blocks.
+    """
+
+    name: str
+    index: int                # seed index
+    num_q_heads: int
+    num_kv_heads: int
+    head_dim: int
+    kv_dtype: str             # pool dtype
+    q_dtype: str              # dtype of q and of the output
+    src_dtype: str            # dtype of K/V handed to the cache write
+    block_size: int
+    prompt_lens: Tuple[int, ...]
+    parent: Tuple[int, ...]
+    num_blocks: int           # pool size in blocks
+    partition_tokens: int = 0  # 0 = library chooses the context split
+    same_candidates: bool = False  # candidates of a prompt get identical q / new K/V
+
+    @property
+    def num_seqs(self) -> int:
+        return len(self.parent)
+
+    @property
+    def num_prompts(self) -> int:
+        return len(self.prompt_lens)
+
+    @property
+    def group(self) -> int:
+        return self.num_q_heads // self.num_kv_heads
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.head_dim)
+
+    @property
+    def context_lens(self) -> np.ndarray:
+        pl = np.asarray(self.prompt_lens, dtype=np.int64)
+        return (pl[np.asarray(self.parent, dtype=np.int64)] + 1).astype(np.int32)
+
+    @property
+    def max_blocks_per_seq(self) -> int:
+        return max(1, -(-int(self.context_lens.max()) // self.block_size))
+
+    def seed(self, stream: int, key: int = 0) -> np.random.SeedSequence:
+        return np.random.SeedSequence(entropy=449_000 + self.index, spawn_key=(stream, key))
+
+
+def _rng(wl: Workload, stream: int, key: int = 0) -> np.random.Generator:
+    return np.random.default_rng(wl.seed(stream, key))
+
+
+# --------------------------------------------------------------------------
+# configurations
+
+
+def _pool_blocks(prompt_lens: Sequence[int], parent: Sequence[int], bs: int) -> int:
+    """Pool sizing recipe: 1.2 x an upper bound of the blocks the step needs.
+
+    Upper bound per prompt: its cached tokens rounded up to whole blocks, plus
+    one fresh block per candidate for the token the step appends.
+    """
+    cands = np.bincount(np.asarray(parent), minlength=len(prompt_lens))
+    need = sum(-(-int(L) // bs) + int(c) for L, c in zip(prompt_lens, cands))
+    return int(math.ceil(1.2 * need))
+
+
+def _make(name, index, hq, hkv, d, kv, q, bs, ctx_lens=None, prompt_lens=None, parent=None,
+          num_blocks=None, src=None, partition_tokens=0, same_candidates=False) -> Workload:
+    if prompt_lens is None:
+        ctx = [int(x) for x in ctx_lens]
+        prompt_lens = [c - 1 for c in ctx]
+        parent = list(range(len(ctx)))
+    if num_blocks is None:
+        num_blocks = _pool_blocks(prompt_lens, parent, bs)
+    if src is None:
+        src = "bf16" if kv == "fp8e4m3" else kv
+    return Workload(name=name, index=index, num_q_heads=hq, num_kv_heads=hkv, head_dim=d,
+                    kv_dtype=kv, q_dtype=q, src_dtype=src, block_size=bs,
+                    prompt_lens=tuple(int(x) for x in prompt_lens), parent=tuple(int(p) for p in parent),
+                    num_blocks=int(num_blocks), partition_tokens=partition_tokens,
+                    same_candidates=same_candidates)
+
+
+def _lens_uniform(index: int, n: int, lo: int, hi: int) -> np.ndarray:
+    rng = np.random.default_rng(np.random.SeedSequence(449_000 + index, spawn_key=(_STREAM_LENS, 0)))
+    return rng.integers(lo, hi, size=n, endpoint=True)
+
+
+def _lens_lognormal(index: int, n: int, median: float, sigma: float, lo: int, hi: int) -> np.ndarray:
+    rng = np.random.default_rng(np.random.SeedSequence(449_000 + index, spawn_key=(_STREAM_LENS, 0)))
+    x = rng.lognormal(mean=math.log(median), sigma=sigma, size=n)
+    return np.clip(np.rint(x), lo, hi).astype(np.int64)
+
+
+def config_c1() -> Workload:
+    """Tiny: 4 MHA heads x 64, fp32, bs 16, pool 32 blocks, lengths {1,15,16,33}."""
+    return _make("c1_tiny_f32", 1, 4, 4, 64, "f32", "f32", 16, ctx_lens=[1, 15, 16, 33], num_blocks=32)
+
+
+def config_c2(num_seqs=64, lo=128, hi=2048, heads=40, index=2, name="c2_llama13b_f16") -> Workload:
+    """LLaMA-13B-shaped layer: 40 MHA heads x 128, fp16, bs 16, lengths U[128, 2048]."""
+    return _make(name, index, heads, heads, 128, "f16", "f16", 16,
+                 ctx_lens=_lens_uniform(index, num_seqs, lo, hi))
+
+
+def config_c3(block_size=16, num_seqs=256, heads=32, lo=16, hi=4096, index=3, name=None) -> Workload:
+    """LLaMA-7B-shaped: 32 MHA heads x 128, bf16, 256 seqs, lognormal(512, 0.8) clipped [16, 4096]."""
+    name = name or f"c3_llama7b_bf16_bs{block_size}"
+    return _make(name, index, heads, heads, 128, "bf16", "bf16", block_size,
+                 ctx_lens=_lens_lognormal(index, num_seqs, 512.0, 0.8, lo, hi))
+
+
+def config_c4(num_prompts=64, n=4, prompt_len=1023, heads=32, same_candidates=False, index=4,
+              name=None) -> Workload:
+    """Parallel sampling: prompts shared by n candidates (ref_count n), fp16, bs 16.
+
+    prompt_len 1023 puts the appended token in the last slot of a partly
+    filled shared block, so the step copies that block for all but one
+    candidate; prompt_len 1024 is the block-aligned variant (no copy).
+    """
+    name = name or f"c4_parallel_sampling_f16_p{prompt_len}"
+    parent = [p for p in range(num_prompts) for _ in range(n)]
+    return _make(name, index, heads, heads, 128, "f16", "f16", 16,
+                 prompt_lens=[prompt_len] * num_prompts, parent=parent, same_candidates=same_candidates)
+
+
+def config_c5(kv="fp8e4m3", num_seqs=128, lo=2048, hi=8192, hq=32, hkv=8, partition_tokens=512,
+              index=5, name=None) -> Workload:
+    """GQA long context: 32 q heads / 8 KV heads x 128, bf16 q, fp8 (or bf16) KV, U[2048, 8192]."""
+    name = name or f"c5_gqa_long_{kv}"
+    return _make(name, index, hq, hkv, 128, kv, "bf16", 16,
+                 ctx_lens=_lens_uniform(index, num_seqs, lo, hi), partition_tokens=partition_tokens)
+
+
+def full_configs() -> Dict[str, Workload]:
+    """The five workloads at their stated sizes (c3 at both block sizes, c5 in fp8 and bf16)."""
+    ws = [config_c1(), config_c2(), config_c3(16), config_c3(32), config_c4(), config_c4(prompt_len=1024),
+          config_c5("fp8e4m3"), config_c5("bf16")]
+    return {w.name: w for w in ws}
+
+
+def small_configs() -> Dict[str, Workload]:
+    """Reduced versions the oracle finishes in seconds; they still span several
+    blocks per sequence, several work splits and ragged last blocks."""
+    ws = [
+        config_c1(),
+        config_c2(num_seqs=6, lo=40, hi=700, heads=4, name="c2s_f16"),
+        config_c3(16, num_seqs=12, heads=3, lo=16, hi=900, name="c3s_bf16_bs16"),
+        config_c3(32, num_seqs=12, heads=3, lo=16, hi=900, name="c3s_bf16_bs32"),
+        config_c4(num_prompts=3, n=4, prompt_len=95, heads=2, name="c4s_cow_f16"),
+        config_c4(num_prompts=2, n=4, prompt_len=96, heads=2, name="c4s_aligned_f16"),
+        config_c4(num_prompts=2, n=4, prompt_len=47, heads=2, same_candidates=True, name="c4s_same_f16"),
+        config_c5("fp8e4m3", num_seqs=5, lo=300, hi=1500, hq=8, hkv=2, name="c5s_fp8"),
+        config_c5("bf16", num_seqs=5, lo=300, hi=1500, hq=8, hkv=2, name="c5s_bf16"),
+    ]
+    return {w.name: w for w in ws}
+
+
+def custom(name, hq, hkv, d, kv, q, bs, ctx_lens, num_blocks=None, index=90, partition_tokens=0,
+           src=None) -> Workload:
+    """Free-form workload for edge-case tests."""
+    return _make(name, index, hq, hkv, d, kv, q, bs, ctx_lens=ctx_lens, num_blocks=num_blocks,
+                 partition_tokens=partition_tokens, src=src)
+
+
+# --------------------------------------------------------------------------
+# draws
+
+
+def free_list_order(wl: Workload) -> np.ndarray:
+    """Seeded permutation of all physical block ids: the order in which the
+    free list hands blocks out (random physical placement)."""
+    return _rng(wl, _STREAM_PLACE).permutation(wl.num_blocks).astype(np.int32)
+
+
+def _normal(rng: np.random.Generator, shape, dtype: str) -> torch.Tensor:
+    x = torch.from_numpy(rng.standard_normal(size=shape, dtype=np.float32))
+    return x if dtype == "f32" else x.to(TORCH_DTYPE[dtype])
+
+
+def q_values(wl: Workload) -> torch.Tensor:
+    """q [S][Hq][d] ~ N(0,1), rounded (RNE) to the q dtype."""
+    if wl.same_candidates:
+        per_prompt = _normal(_rng(wl, _STREAM_Q), (wl.num_prompts, wl.num_q_heads, wl.head_dim), wl.q_dtype)
+        return per_prompt[torch.as_tensor(wl.parent, dtype=torch.long)].contiguous()
+    return _normal(_rng(wl, _STREAM_Q), (wl.num_seqs, wl.num_q_heads, wl.head_dim), wl.q_dtype)
+
+
+def prompt_kv(wl: Workload, p: int) -> Tuple[torch.Tensor, torch.Tensor]:
+    """K and V of prompt p's cached tokens: each [prompt_len][Hkv][d] in src dtype."""
+    rng = _rng(wl, _STREAM_PROMPT_KV, p)
+    shape = (wl.prompt_lens[p], wl.num_kv_heads, wl.head_dim)
+    k = _normal(rng, shape, wl.src_dtype)
+    v = _normal(rng, shape, wl.src_dtype)
+    return k, v
+
+
+def all_prompt_kv(wl: Workload, prompts: Optional[Sequence[int]] = None, threads: int = 8):
+    prompts = range(wl.num_prompts) if prompts is None else prompts
+    with ThreadPoolExecutor(threads) as ex:
+        return list(ex.map(lambda p: prompt_kv(wl, p), prompts))
+
+
+def new_kv(wl: Workload) -> Tuple[torch.Tensor, torch.Tensor]:
+    """K and V of the token each sequence appends in the step: [S][Hkv][d] in src dtype."""
+    rng = _rng(wl, _STREAM_NEW_KV)
+    n = wl.num_prompts if wl.same_candidates else wl.num_seqs
+    shape = (n, wl.num_kv_heads, wl.head_dim)
+    k = _normal(rng, shape, wl.src_dtype)
+    v = _normal(rng, shape, wl.src_dtype)
+    if wl.same_candidates:
+        idx = torch.as_tensor(wl.parent, dtype=torch.long)
+        k, v = k[idx].contiguous(), v[idx].contiguous()
+    return k, v
+
+
+def fp8_scales(wl: Workload, threads: int = 8) -> Tuple[float, float]:
+    """Per-tensor fp8 scales (recipe; the pages fix none): amax(|x|) / 448 over
+    every K (resp. V) value of the workload, computed in fp32.  1.0 for non-fp8
+    pools."""
+    if wl.kv_dtype != "fp8e4m3":
+        return 1.0, 1.0
+
+    def amax(p):
+        k, v = prompt_kv(wl, p)
+        return float(k.float().abs().max()) if k.numel() else 0.0, float(v.float().abs().max()) if v.numel() else 0.0
+
+    with ThreadPoolExecutor(threads) as ex:
+        mx = list(ex.map(amax, range(wl.num_prompts)))
+    kn, vn = new_kv(wl)
+    km = max([m[0] for m in mx] + [float(kn.float().abs().max())])
+    vm = max([m[1] for m in mx] + [float(vn.float().abs().max())])
+    ks = float(np.float32(km) / np.float32(448.0))
+    vs = float(np.float32(vm) / np.float32(448.0))
+    return ks, vs
