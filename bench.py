@@ -1,0 +1,205 @@
+#!/usr/bin/env python
+"""Paged decode attention benchmark on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+One step = one decode iteration of the whole hot path for a batch resident in
+HBM: copy_blocks (copy-on-write pairs, none for workloads without sharing),
+reshape_and_cache (the new token of every sequence) and paged_attention_decode.
+Prints one JSON line.  `value` is KV bytes read per step / wall time per step
+(GB/s); `roofline` is the decode kernel's algorithmic bytes over its own
+event-timed duration against the MI355X HBM peak; `cpu_baseline` is the fp64
+CPU oracle timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+import workloads as W
+
+METRIC = "paged decode attention: achieved KV HBM GB/s (% of peak) + µs/step, batch 256"
+HBM_PEAK_GBS = 8000.0
+DEFAULT_WORKLOAD = "c3_llama7b_bf16_bs16"
+
+
+def get_workload(name: str) -> W.Workload:
+    allw = {**W.full_configs(), **W.small_configs()}
+    if name not in allw:
+        raise SystemExit(f"unknown workload {name}; choose from {sorted(allw)}")
+    return allw[name]
+
+
+def build_session(wl: W.Workload, device, prompt_batch: int = 16, free_order=None):
+    """Pool + block manager + cached prompts + one planned step for a workload.
+    Returns (session, q, k_new, v_new) with the step's inputs on the device."""
+    import paged_kv_cache_449_amd as pk
+    from paged_kv_cache_449_amd.session import DecodeSession
+
+    ks, vs = W.fp8_scales(wl)
+    pool = pk.KVPool(wl.num_blocks, wl.block_size, wl.num_kv_heads, wl.head_dim, W.TORCH_DTYPE[wl.kv_dtype],
+                     device, ks, vs)
+    # every slot starts as all-ones bytes (NaN in every KV dtype)
+    pool.k_cache.view(torch.uint8).fill_(W.POISON_BYTE)
+    pool.v_cache.view(torch.uint8).fill_(W.POISON_BYTE)
+    mgr = pk.BlockManager(wl.num_blocks, wl.block_size,
+                          W.free_list_order(wl) if free_order is None else free_order)
+    sess = DecodeSession(pool, mgr, wl.num_q_heads)
+    for b0 in range(0, wl.num_prompts, prompt_batch):
+        ps = list(range(b0, min(b0 + prompt_batch, wl.num_prompts)))
+        kvs = W.all_prompt_kv(wl, ps)
+        sess.cache_prompts([(("p", p), k, v) for p, (k, v) in zip(ps, kvs)])
+    children = {}
+    for s, p in enumerate(wl.parent):
+        children.setdefault(p, []).append(("s", s))
+    for p in range(wl.num_prompts):
+        sess.fork(("p", p), children.get(p, []))
+        sess.free(("p", p))
+    sess.prepare_step([("s", s) for s in range(wl.num_seqs)])
+    q = W.q_values(wl).to(device)
+    kn, vn = W.new_kv(wl)
+    torch.cuda.synchronize(device)
+    return sess, q, kn.to(device), vn.to(device)
+
+
+def decode_bytes(wl: W.Workload) -> dict:
+    """Algorithmic bytes of one decode launch: every cached token's K and V
+    row of every kv head (2 * Hkv * D * elem bytes per token), q and out, the
+    table entries of the blocks in use and the lengths."""
+    n = wl.context_lens.astype(np.int64)
+    eb = W.ELEM_BYTES[wl.kv_dtype]
+    qb = W.ELEM_BYTES[wl.q_dtype]
+    kv = int(n.sum()) * 2 * wl.num_kv_heads * wl.head_dim * eb
+    qo = 2 * wl.num_seqs * wl.num_q_heads * wl.head_dim * qb
+    tables = int((-(-n // wl.block_size)).sum()) * 4 + wl.num_seqs * 4
+    return {"kv": kv, "total": kv + qo + tables, "tokens": int(n.sum())}
+
+
+def cpu_baseline(wl: W.Workload, target_s: float = 12.0) -> dict:
+    """The fp64 oracle on one host core over the first sequences of the
+    workload, sized to about target_s seconds of CPU work."""
+    from oracle.run import OracleRun
+
+    n = wl.context_lens.astype(np.int64)
+    per_tok = 2 * wl.num_kv_heads * wl.head_dim * W.ELEM_BYTES[wl.kv_dtype]
+    # calibrate on a few sequences, then size the sample
+    probe = list(range(min(4, wl.num_seqs)))
+    prompts = sorted({wl.parent[s] for s in probe})
+    run = OracleRun(wl, prompts=prompts)
+    t = time.perf_counter()
+    run.decode(probe)
+    dt = time.perf_counter() - t
+    rate = float(n[probe].sum()) / max(dt, 1e-6)     # tokens per second
+    want = rate * target_s
+    k = int(np.searchsorted(np.cumsum(n), want)) + 1
+    k = max(1, min(k, wl.num_seqs))
+    seqs = list(range(k))
+    prompts = sorted({wl.parent[s] for s in seqs})
+    run = OracleRun(wl, prompts=prompts, scales=(run.k_scale, run.v_scale))
+    t = time.perf_counter()
+    run.decode(seqs)
+    dt = time.perf_counter() - t
+    toks = int(n[seqs].sum())
+    return {"value": round(toks * per_tok / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"sequences 0..{k - 1} of {wl.num_seqs} ({toks} of {int(n.sum())} cached tokens), "
+                      f"{dt:.1f} s single-threaded fp64"}
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args(argv)
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: this build runs the decode path on a single MI355X "
+              "(sharding across GPUs is a design note only); run with --gpus 1", file=sys.stderr)
+        return 2
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+
+    import paged_kv_cache_449_amd as pk
+
+    wl = get_workload(args.workload)
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    print(f"[bench] building {wl.name}", file=sys.stderr, flush=True)
+    sess, q, kn, vn = build_session(wl, dev)
+    out = torch.empty_like(q)
+    pool = sess.pool
+    pt = wl.partition_tokens
+
+    def one_step(ev=None):
+        pk.copy_blocks(pool, sess.pairs)
+        pk.reshape_and_cache(pool, kn, vn, sess.slot_mapping)
+        if ev is not None:
+            ev[0].record()
+        pk.paged_attention_decode(pool, q, sess.block_tables, sess.context_lens, wl.scale, out=out,
+                                  partition_tokens=pt)
+        if ev is not None:
+            ev[1].record()
+
+    for _ in range(args.warmup):
+        one_step()
+    torch.cuda.synchronize(dev)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize(dev)
+    t0 = time.perf_counter()
+    g0.record()
+    for i in range(args.steps):
+        one_step(evs[i])
+    g1.record()
+    torch.cuda.synchronize(dev)
+    wall = time.perf_counter() - t0
+    dec_ms = np.array([a.elapsed_time(b) for a, b in evs])
+    step_ms = wall * 1e3 / args.steps
+    nb = decode_bytes(wl)
+    dec_mean_s = float(dec_ms.mean()) / 1e3
+    achieved = nb["total"] / dec_mean_s / 1e9
+    print(f"[bench] decode kernel mean {dec_ms.mean() * 1e3:.1f} us (min {dec_ms.min() * 1e3:.1f}, "
+          f"max {dec_ms.max() * 1e3:.1f}); step {step_ms * 1e3:.1f} us", file=sys.stderr, flush=True)
+
+    res = {
+        "metric": METRIC,
+        "value": round(nb["kv"] / (step_ms / 1e3) / 1e9, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 4),
+        "us_per_step": round(step_ms * 1e3, 1),
+        "pct_of_hbm_peak": round(100 * nb["kv"] / (step_ms / 1e3) / 1e9 / HBM_PEAK_GBS, 1),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "num_seqs": wl.num_seqs, "num_q_heads": wl.num_q_heads,
+                   "num_kv_heads": wl.num_kv_heads, "head_dim": wl.head_dim, "block_size": wl.block_size,
+                   "kv_dtype": wl.kv_dtype, "q_dtype": wl.q_dtype, "cached_tokens": nb["tokens"],
+                   "kv_bytes_per_step": nb["kv"], "partition_tokens": pt, "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "paged_decode_kernel", "kernel_us": round(float(dec_ms.mean()) * 1e3, 2),
+                     "bytes_per_launch": nb["total"]},
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
+        res["cpu_baseline"] = cpu_baseline(wl)
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

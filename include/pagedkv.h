@@ -1,0 +1,211 @@
+/*
+ * pagedkv.h -- C ABI of libpagedkv.so: a paged KV-cache pool and decode
+ * attention over it, for AMD Instinct MI355X (gfx950).
+ *
+ * The method (the pages cited are "vLLM 与 KV Cache" (jeffliulab.github.io),
+ * "vLLM KV Cache 实现机制" (devpress.csdn.net) and "vLLM — 把操作系统的分页搬进
+ * GPU KV cache" (estelledc.github.io)):
+ *   - Each sequence's K/V cache is cut into fixed-size blocks of block_size
+ *     tokens (16 by default) that live anywhere in one preallocated pool;
+ *     a per-sequence block table maps logical block i to its physical block.
+ *     ("vLLM 与 KV Cache": virtual-memory table, how-it-works points 1-3;
+ *     "vLLM KV Cache 实现机制": §1.2 diagram, §4.1 pool diagram.)
+ *   - Decode attention reads K/V through that table: look up the physical
+ *     block, then offset into it. ("vLLM — 把操作系统的分页搬进 GPU KV cache":
+ *     core mechanisms, kernel paragraph.)
+ *   - Blocks shared by several sequences are copied before the first write
+ *     into them (copy-on-write). (Same page: core mechanism 3, case 2,
+ *     pitfalls.)
+ * Block allocation, reference counts and the copy-on-write plan belong to
+ * the caller's block manager; this library only moves and reads bytes.
+ *
+ * Conventions for every call:
+ *   - Device pointers are plain device memory on the device that was current
+ *     when the pool was created; the caller owns them and keeps them alive
+ *     until the stream work that uses them has finished.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Work is only
+ *     enqueued: no call synchronises the device and, apart from
+ *     kv_pool_create, none allocates device memory.
+ *   - Host-side arguments are checked before anything is enqueued; a failed
+ *     check returns an error status and enqueues nothing.
+ *   - Device-side data (lengths, table entries, slots, pairs) are
+ *     preconditions, not checked for meaning.  The kernels never access
+ *     memory outside the pool, the table rows or the outputs for any values
+ *     of them: an out-of-range block id or slot is skipped, a context length
+ *     above max_blocks * block_size is clamped to it, and a length <= 0
+ *     yields a zero output row.
+ *   - Calls are reentrant; a pool has no lock, so the caller orders work on
+ *     streams that touch the same pool.
+ */
+#ifndef PAGEDKV_H
+#define PAGEDKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  KV_OK = 0,
+  KV_ERR_INVALID_ARG = 1,  /* null pointer, bad size, inconsistent shapes */
+  KV_ERR_UNSUPPORTED = 2,  /* dtype / head_dim / block_size combination not built */
+  KV_ERR_OOM = 3,          /* kv_pool_create could not allocate */
+  KV_ERR_HIP = 4,          /* a HIP runtime call or kernel launch failed */
+  KV_ERR_WORKSPACE = 5     /* workspace missing or smaller than required */
+} kv_status_t;
+
+typedef enum {
+  KV_F32 = 0,
+  KV_F16 = 1,
+  KV_BF16 = 2,
+  KV_FP8_E4M3FN = 3        /* OCP E4M3FN: bias 7, no infinities, max 448 */
+} kv_dtype_t;
+
+typedef struct kv_pool kv_pool_t;  /* opaque pool descriptor (host memory) */
+
+/*
+ * kv_pool_create -- allocate a K pool and a V pool of num_blocks blocks on
+ * the current device; the library owns the memory and kv_pool_destroy frees
+ * it.  The pool is preallocated once and carved into equal blocks ("vLLM KV
+ * Cache 实现机制" §4.1; "vLLM — 把操作系统的分页搬进 GPU KV cache", case 1).
+ *
+ * Layout of each pool: [num_blocks][num_kv_heads][block_size][head_dim] of
+ * `dtype`, row-major, so element (b, h, o, j) is at element offset
+ * ((b*num_kv_heads + h)*block_size + o)*head_dim + j.  One (block, head)
+ * tile of block_size*head_dim elements is contiguous.
+ *
+ * Supported: block_size in {8, 16, 32, 64}; head_dim in {64, 128, 256};
+ * dtype any kv_dtype_t.  num_blocks * num_kv_heads * block_size * head_dim
+ * must fit in int64 and every block id must fit in int32.
+ * The memory is not initialised.  Returns KV_ERR_OOM if hipMalloc fails.
+ */
+kv_status_t kv_pool_create(int32_t num_blocks, int32_t block_size, int32_t num_kv_heads, int32_t head_dim,
+                           kv_dtype_t dtype, kv_pool_t** out);
+
+/*
+ * kv_pool_create_from -- describe caller-owned buffers (e.g. framework
+ * tensors) as a pool with the layout above.  bytes_each is the size of each
+ * of k_buf and v_buf and must be at least the pool size; both must be
+ * 16-byte aligned.  kv_pool_destroy does not free them.
+ */
+kv_status_t kv_pool_create_from(int32_t num_blocks, int32_t block_size, int32_t num_kv_heads, int32_t head_dim,
+                                kv_dtype_t dtype, void* k_buf, void* v_buf, size_t bytes_each, kv_pool_t** out);
+
+/* kv_pool_destroy -- free the descriptor (and the memory, if the library
+ * allocated it).  NULL is accepted.  The caller ensures no enqueued work
+ * still uses the pool. */
+kv_status_t kv_pool_destroy(kv_pool_t* pool);
+
+/*
+ * kv_pool_info -- device addresses of the K and V pools, bytes of each, and
+ * element strides of the four layout dimensions (block, head, token slot,
+ * dim).  Any output pointer may be NULL.
+ */
+kv_status_t kv_pool_info(const kv_pool_t* pool, void** k, void** v, size_t* bytes_each, int64_t strides[4]);
+
+/*
+ * kv_pool_set_scales -- per-tensor fp32 scales of an fp8 pool: a stored code
+ * c stands for decode(c) * scale.  Default 1.  Must be finite and > 0.
+ * KV_ERR_INVALID_ARG for non-fp8 pools.  ("vLLM KV Cache 实现机制" §2.3 table
+ * and §5.1 flags name fp8 as a KV cache dtype; the scale convention is this
+ * library's.)
+ */
+kv_status_t kv_pool_set_scales(kv_pool_t* pool, float k_scale, float v_scale);
+
+/*
+ * reshape_and_cache -- store the K and V of num_tokens new tokens into their
+ * slots ("vLLM 与 KV Cache": why a KV cache -- only the new token's K/V is
+ * computed and appended; how-it-works points 2-3).
+ *
+ *   k_new, v_new  device, [num_tokens][num_kv_heads][head_dim] of src_dtype,
+ *                 contiguous, 16-byte aligned.
+ *   slot_mapping  device int64 [num_tokens]: slot s names token offset
+ *                 s % block_size of physical block s / block_size, i.e. the
+ *                 caller computes block_table[pos / bs] * bs + pos % bs.
+ *                 A negative slot skips the token; so does a slot at or above
+ *                 num_blocks * block_size.
+ * Same src and pool dtype: the bytes are copied.  fp8 pool with src f32, f16
+ * or bf16: each element becomes E4M3FN(fp32(x) / k_scale) (v_scale for V),
+ * rounded to nearest even and saturated to +-448.  Other dtype pairs:
+ * KV_ERR_UNSUPPORTED.  Two tokens with the same slot race (precondition:
+ * slots unique).  num_tokens == 0 enqueues nothing.
+ */
+kv_status_t reshape_and_cache(kv_pool_t* pool, const void* k_new, const void* v_new, kv_dtype_t src_dtype,
+                              const int64_t* slot_mapping, int32_t num_tokens, void* stream);
+
+/*
+ * paged_attention_decode -- one query token per sequence attends to its whole
+ * cached context through the block table ("vLLM — 把操作系统的分页搬进 GPU KV
+ * cache": core mechanisms and kernel paragraph; lessons: decode is bound by
+ * KV read bandwidth).
+ *
+ *   q             device [num_seqs][num_q_heads][head_dim] of q_dtype.
+ *   out           device [num_seqs][num_q_heads][head_dim] of q_dtype.
+ *   block_tables  device int32 [num_seqs][max_blocks]; entry i of row s is the
+ *                 physical block of logical block i of sequence s.  Entries
+ *                 at or beyond ceil(context_len / block_size) are not read.
+ *   context_lens  device int32 [num_seqs]: tokens in each sequence's cache,
+ *                 including the one appended this step.
+ *   scale         softmax scale (typically 1/sqrt(head_dim)).
+ * out[s][h] = sum_t softmax_t(scale * q[s][h] . K_t) V_t over t < context_len,
+ * with K_t/V_t of kv head h / (num_q_heads / num_kv_heads).  Accumulation is
+ * fp32; the result is rounded to nearest even into q_dtype.  For fp8 pools K
+ * and V are decoded exactly and multiplied by their scales.
+ *
+ * q_dtype must equal the pool dtype, except fp8 pools, which take f32, f16
+ * or bf16 queries.  num_q_heads must be a multiple of num_kv_heads, with at
+ * most 8 query heads per kv head.
+ *
+ * Work split: the cached tokens of all (kv head, sequence) pairs are laid end
+ * to end and cut into equal runs of whole blocks, one per worker wavefront,
+ * so long and short sequences cost the same per token.  partition_tokens == 0
+ * lets the library size the runs from the device's compute-unit count;
+ * otherwise each run is partition_tokens tokens (a multiple of block_size).
+ * A sequence cut into several runs is merged in the same launch by the
+ * worker that finishes last (log-sum-exp merge of the partial results, in a
+ * fixed order, so results are bitwise reproducible).
+ *
+ * When partition_tokens is given and the batch would need more than 65528
+ * runs, the runs are lengthened to the smallest whole number of blocks that
+ * fits.
+ *
+ * workspace: device memory of at least paged_attention_workspace_size()
+ * bytes, 256-byte aligned.  Its first 256 KiB hold arrival counters and must
+ * be zero before the first use; every completed call leaves them zero again,
+ * so one workspace serves calls of any shape without clearing.  The rest holds
+ * partial results.  Calls sharing a workspace must not overlap.
+ */
+kv_status_t paged_attention_decode(const kv_pool_t* pool, const void* q, kv_dtype_t q_dtype, void* out,
+                                   const int32_t* block_tables, int32_t max_blocks, const int32_t* context_lens,
+                                   int32_t num_seqs, int32_t num_q_heads, float scale, int32_t partition_tokens,
+                                   void* workspace, size_t workspace_bytes, void* stream);
+
+/* paged_attention_workspace_size -- bytes of workspace the call above needs
+ * for these arguments (depends on the pool's device, not on lengths). */
+kv_status_t paged_attention_workspace_size(const kv_pool_t* pool, int32_t num_seqs, int32_t num_q_heads,
+                                           int32_t max_blocks, int32_t partition_tokens, size_t* bytes);
+
+/*
+ * copy_blocks -- copy-on-write support: for each pair (src, dst) copy the
+ * whole physical block src onto dst in both pools (every head, every token
+ * slot).  ("vLLM — 把操作系统的分页搬进 GPU KV cache": core mechanism 3, case 2
+ * and pitfalls -- n candidates sharing a prompt copy n-1 blocks on their first
+ * step.)  All pairs are copied by one launch.
+ *
+ *   pairs  device int32 [num_pairs][2].  Preconditions: dst ids distinct and
+ *          not also used as src.  Pairs with an id outside [0, num_blocks)
+ *          are skipped.
+ * num_pairs == 0 enqueues nothing.
+ */
+kv_status_t copy_blocks(kv_pool_t* pool, const int32_t* pairs, int32_t num_pairs, void* stream);
+
+/* kv_status_string -- static description of a status code. */
+const char* kv_status_string(kv_status_t status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGEDKV_H */

@@ -1,0 +1,234 @@
+"""Python binding of libpagedkv.so (paged KV-cache pool + decode attention for
+MI355X / gfx950).
+
+The functions carry the C ABI's names and only marshal arguments: torch
+tensors supply device memory and the current HIP stream; every step of the
+path runs in the library's HIP kernels.  There is no fallback: if the shared
+library is missing or fails to load, every call raises.
+
+    pool = KVPool(num_blocks, block_size, num_kv_heads, head_dim, torch.bfloat16)
+    reshape_and_cache(pool, k_new, v_new, slot_mapping)
+    copy_blocks(pool, pairs)
+    out = paged_attention_decode(pool, q, block_tables, context_lens, scale)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+from .block_manager import BlockManager, PoolExhausted  # noqa: F401
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpagedkv.so")
+
+KV_OK, KV_ERR_INVALID_ARG, KV_ERR_UNSUPPORTED, KV_ERR_OOM, KV_ERR_HIP, KV_ERR_WORKSPACE = range(6)
+KV_F32, KV_F16, KV_BF16, KV_FP8_E4M3FN = range(4)
+
+DTYPE_CODE = {torch.float32: KV_F32, torch.float16: KV_F16, torch.bfloat16: KV_BF16,
+              torch.float8_e4m3fn: KV_FP8_E4M3FN}
+
+_lib_handle: Optional[ctypes.CDLL] = None
+
+
+class PagedKVError(RuntimeError):
+    def __init__(self, status: int, call: str):
+        super().__init__(f"{call}: {status_string(status)} (status {status})")
+        self.status = status
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libpagedkv.so; raises if it has not been built."""
+    global _lib_handle
+    if _lib_handle is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built; run `python -m paged_kv_cache_449_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        i32, i64, vp, sz, f32 = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_float
+        pp = ctypes.POINTER(ctypes.c_void_p)
+        L.kv_pool_create.argtypes = [i32, i32, i32, i32, ctypes.c_int, pp]
+        L.kv_pool_create_from.argtypes = [i32, i32, i32, i32, ctypes.c_int, vp, vp, sz, pp]
+        L.kv_pool_destroy.argtypes = [vp]
+        L.kv_pool_info.argtypes = [vp, pp, pp, ctypes.POINTER(sz), ctypes.POINTER(i64)]
+        L.kv_pool_set_scales.argtypes = [vp, f32, f32]
+        L.reshape_and_cache.argtypes = [vp, vp, vp, ctypes.c_int, vp, i32, vp]
+        L.paged_attention_decode.argtypes = [vp, vp, ctypes.c_int, vp, vp, i32, vp, i32, i32, f32, i32, vp, sz, vp]
+        L.paged_attention_workspace_size.argtypes = [vp, i32, i32, i32, i32, ctypes.POINTER(sz)]
+        L.copy_blocks.argtypes = [vp, vp, i32, vp]
+        L.kv_status_string.argtypes = [ctypes.c_int]
+        L.kv_status_string.restype = ctypes.c_char_p
+        for fn in ("kv_pool_create", "kv_pool_create_from", "kv_pool_destroy", "kv_pool_info", "kv_pool_set_scales",
+                   "reshape_and_cache", "paged_attention_decode", "paged_attention_workspace_size", "copy_blocks"):
+            getattr(L, fn).restype = ctypes.c_int
+        _lib_handle = L
+    return _lib_handle
+
+
+def status_string(status: int) -> str:
+    return lib().kv_status_string(status).decode()
+
+
+def _check(status: int, call: str) -> None:
+    if status != KV_OK:
+        raise PagedKVError(status, call)
+
+
+def _stream(device: torch.device, stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return int(stream.cuda_stream)
+
+
+def _dev_ptr(t: torch.Tensor, name: str, device: torch.device) -> int:
+    if not t.is_cuda or t.device != device:
+        raise ValueError(f"{name} must be on {device}, got {t.device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+class KVPool:
+    """K and V pools, each a device tensor [num_blocks][num_kv_heads][block_size][head_dim],
+    described to the library with kv_pool_create_from (torch owns the memory)."""
+
+    def __init__(self, num_blocks: int, block_size: int, num_kv_heads: int, head_dim: int, dtype: torch.dtype,
+                 device=None, k_scale: float = 1.0, v_scale: float = 1.0):
+        if dtype not in DTYPE_CODE:
+            raise ValueError(f"unsupported KV dtype {dtype}")
+        self.device = torch.device(device) if device is not None else torch.device("cuda", torch.cuda.current_device())
+        self.num_blocks, self.block_size, self.num_kv_heads, self.head_dim = num_blocks, block_size, num_kv_heads, head_dim
+        self.dtype = dtype
+        shape = (num_blocks, num_kv_heads, block_size, head_dim)
+        self.k_cache = torch.empty(shape, dtype=dtype, device=self.device)
+        self.v_cache = torch.empty(shape, dtype=dtype, device=self.device)
+        h = ctypes.c_void_p()
+        nbytes = self.k_cache.numel() * self.k_cache.element_size()
+        with torch.cuda.device(self.device):
+            _check(lib().kv_pool_create_from(num_blocks, block_size, num_kv_heads, head_dim, DTYPE_CODE[dtype],
+                                             self.k_cache.data_ptr(), self.v_cache.data_ptr(), nbytes,
+                                             ctypes.byref(h)), "kv_pool_create_from")
+        self.handle = h
+        self.k_scale, self.v_scale = 1.0, 1.0
+        if dtype == torch.float8_e4m3fn:
+            kv_pool_set_scales(self, k_scale, v_scale)
+        self._workspace: Optional[torch.Tensor] = None
+
+    @property
+    def block_bytes(self) -> int:
+        return self.num_kv_heads * self.block_size * self.head_dim * self.k_cache.element_size()
+
+    def workspace(self, nbytes: int) -> torch.Tensor:
+        """A zero-initialised device workspace of at least nbytes, reused across calls."""
+        if self._workspace is None or self._workspace.numel() < nbytes:
+            self._workspace = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=self.device)
+        return self._workspace
+
+    def close(self) -> None:
+        if getattr(self, "handle", None) is not None and self.handle.value:
+            lib().kv_pool_destroy(self.handle)
+            self.handle = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def kv_pool_set_scales(pool: KVPool, k_scale: float, v_scale: float) -> None:
+    _check(lib().kv_pool_set_scales(pool.handle, float(k_scale), float(v_scale)), "kv_pool_set_scales")
+    pool.k_scale, pool.v_scale = float(k_scale), float(v_scale)
+
+
+def kv_pool_info(pool: KVPool):
+    k, v = ctypes.c_void_p(), ctypes.c_void_p()
+    nbytes = ctypes.c_size_t()
+    strides = (ctypes.c_int64 * 4)()
+    _check(lib().kv_pool_info(pool.handle, ctypes.byref(k), ctypes.byref(v), ctypes.byref(nbytes), strides),
+           "kv_pool_info")
+    return k.value, v.value, nbytes.value, tuple(strides)
+
+
+class LibraryPool:
+    """A pool whose memory the library allocates (kv_pool_create) and frees."""
+
+    def __init__(self, num_blocks: int, block_size: int, num_kv_heads: int, head_dim: int, dtype: torch.dtype):
+        h = ctypes.c_void_p()
+        _check(lib().kv_pool_create(num_blocks, block_size, num_kv_heads, head_dim, DTYPE_CODE[dtype],
+                                    ctypes.byref(h)), "kv_pool_create")
+        self.handle = h
+
+    def close(self) -> None:
+        if self.handle.value:
+            _check(lib().kv_pool_destroy(self.handle), "kv_pool_destroy")
+            self.handle = ctypes.c_void_p()
+
+
+def kv_pool_create(num_blocks: int, block_size: int, num_kv_heads: int, head_dim: int,
+                   dtype: torch.dtype) -> LibraryPool:
+    return LibraryPool(num_blocks, block_size, num_kv_heads, head_dim, dtype)
+
+
+def reshape_and_cache(pool: KVPool, k: torch.Tensor, v: torch.Tensor, slot_mapping: torch.Tensor,
+                      stream=None) -> None:
+    """Store k/v [T][Hkv][D] into the pool at slot_mapping (int64 [T], <0 skips)."""
+    if k.shape != v.shape or k.dim() != 3 or k.shape[1:] != (pool.num_kv_heads, pool.head_dim):
+        raise ValueError(f"k/v must be [T][{pool.num_kv_heads}][{pool.head_dim}], got {tuple(k.shape)}")
+    if k.dtype != v.dtype or k.dtype not in DTYPE_CODE:
+        raise ValueError("k and v must share a supported dtype")
+    if slot_mapping.dtype != torch.int64 or slot_mapping.shape != (k.shape[0],):
+        raise ValueError("slot_mapping must be int64 [T]")
+    d = pool.device
+    _check(lib().reshape_and_cache(pool.handle, _dev_ptr(k, "k", d), _dev_ptr(v, "v", d), DTYPE_CODE[k.dtype],
+                                   _dev_ptr(slot_mapping, "slot_mapping", d), k.shape[0], _stream(d, stream)),
+           "reshape_and_cache")
+
+
+def copy_blocks(pool: KVPool, pairs: torch.Tensor, stream=None) -> None:
+    """Copy whole blocks for each (src, dst) row of pairs (int32 [P][2])."""
+    if pairs.dtype != torch.int32 or pairs.dim() != 2 or pairs.shape[1] != 2:
+        raise ValueError("pairs must be int32 [P][2]")
+    if pairs.shape[0] == 0:
+        return
+    d = pool.device
+    _check(lib().copy_blocks(pool.handle, _dev_ptr(pairs, "pairs", d), pairs.shape[0], _stream(d, stream)),
+           "copy_blocks")
+
+
+def paged_attention_workspace_size(pool: KVPool, num_seqs: int, num_q_heads: int, max_blocks: int,
+                                   partition_tokens: int = 0) -> int:
+    n = ctypes.c_size_t()
+    _check(lib().paged_attention_workspace_size(pool.handle, num_seqs, num_q_heads, max_blocks, partition_tokens,
+                                                ctypes.byref(n)), "paged_attention_workspace_size")
+    return n.value
+
+
+def paged_attention_decode(pool: KVPool, q: torch.Tensor, block_tables: torch.Tensor, context_lens: torch.Tensor,
+                           scale: float, out: Optional[torch.Tensor] = None, partition_tokens: int = 0,
+                           workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Decode attention of q [S][Hq][D] over each sequence's paged context."""
+    if q.dim() != 3 or q.shape[2] != pool.head_dim or q.dtype not in DTYPE_CODE:
+        raise ValueError(f"q must be [S][Hq][{pool.head_dim}] of a supported dtype")
+    S, Hq = q.shape[0], q.shape[1]
+    if block_tables.dtype != torch.int32 or block_tables.dim() != 2 or block_tables.shape[0] != S:
+        raise ValueError("block_tables must be int32 [S][max_blocks]")
+    if context_lens.dtype != torch.int32 or context_lens.shape != (S,):
+        raise ValueError("context_lens must be int32 [S]")
+    if out is None:
+        out = torch.empty_like(q)
+    elif out.shape != q.shape or out.dtype != q.dtype:
+        raise ValueError("out must match q")
+    max_blocks = block_tables.shape[1]
+    need = paged_attention_workspace_size(pool, S, Hq, max_blocks, partition_tokens)
+    if workspace is None:
+        workspace = pool.workspace(need)
+    d = pool.device
+    _check(lib().paged_attention_decode(pool.handle, _dev_ptr(q, "q", d), DTYPE_CODE[q.dtype],
+                                        _dev_ptr(out, "out", d), _dev_ptr(block_tables, "block_tables", d), max_blocks,
+                                        _dev_ptr(context_lens, "context_lens", d), S, Hq, float(scale),
+                                        partition_tokens, _dev_ptr(workspace, "workspace", d),
+                                        workspace.numel() * workspace.element_size(), _stream(d, stream)),
+           "paged_attention_decode")
+    return out

@@ -1,0 +1,59 @@
+"""Build libpagedkv.so (HIP for gfx950) in-tree.
+
+    python -m paged_kv_cache_449_amd.build
+
+Compiles every csrc/*.hip to an object under _build/ (in parallel), then
+links paged_kv_cache_449_amd/libpagedkv.so.  Always recompiles.
+"""
+from __future__ import annotations
+
+import glob
+import os
+import subprocess
+import sys
+from concurrent.futures import ThreadPoolExecutor
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+BUILD = os.path.join(ROOT, "_build")
+LIB = os.path.join(PKG, "libpagedkv.so")
+ARCH = os.environ.get("PAGEDKV_ARCH", "gfx950")
+
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+CFLAGS = [
+    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall",
+    # no packed fp32 arithmetic on this target
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-I", INCLUDE, "-I", CSRC,
+]
+
+
+def _compile(src: str) -> str:
+    obj = os.path.join(BUILD, os.path.basename(src)[:-4] + ".o")
+    cmd = [HIPCC, *CFLAGS, "-c", src, "-o", obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    noise = "'-packed-fp32-ops' is not a recognized feature"
+    msg = "\n".join(line for line in (r.stdout + r.stderr).splitlines() if noise not in line)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed on {src}:\n{msg}")
+    if msg.strip():
+        print(msg, file=sys.stderr)
+    return obj
+
+
+def build(jobs: int = 0) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+    jobs = jobs or min(16, os.cpu_count() or 4, len(srcs))
+    with ThreadPoolExecutor(jobs) as ex:
+        objs = list(ex.map(_compile, srcs))
+    tmp = LIB + ".tmp"
+    subprocess.check_call([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs])
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build())

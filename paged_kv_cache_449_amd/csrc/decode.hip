@@ -1,0 +1,129 @@
+// Host entry points of paged decode attention: argument checks, work split,
+// workspace layout and dispatch to the kernel instantiations.
+#include <stdlib.h>
+
+#include "decode_kernel.h"
+
+namespace {
+
+using namespace pkv;
+
+// Worker wavefronts per compute unit when the library sizes the split.
+// PAGEDKV_DECODE_WAVES_PER_CU overrides it (tuning).
+int waves_per_cu() {
+  static int v = [] {
+    const char* e = getenv("PAGEDKV_DECODE_WAVES_PER_CU");
+    int x = e ? atoi(e) : 0;
+    return (x >= 1 && x <= 64) ? x : 16;
+  }();
+  return v;
+}
+
+struct Plan {
+  int32_t chunk;        // 0 = derived in the kernel
+  int32_t num_workers;  // multiple of 8
+  size_t counters_bytes;
+  size_t bytes;
+};
+
+kv_status_t make_plan(const kv_pool_t* pool, int32_t num_seqs, int32_t num_q_heads, int32_t max_blocks,
+                      int32_t partition_tokens, Plan* plan) {
+  if (!pool || num_seqs < 0 || num_q_heads <= 0 || max_blocks <= 0 || partition_tokens < 0) return KV_ERR_INVALID_ARG;
+  if (num_q_heads % pool->num_kv_heads) return KV_ERR_INVALID_ARG;
+  const int G = num_q_heads / pool->num_kv_heads;
+  if (G != 1 && G != 2 && G != 4 && G != 8) return KV_ERR_UNSUPPORTED;
+  const int64_t units = (int64_t)num_seqs * pool->num_kv_heads * max_blocks;  // upper bound of blocks
+  if (units > (1LL << 30) || (int64_t)max_blocks * pool->block_size > (1LL << 30)) return KV_ERR_INVALID_ARG;
+  int64_t workers;
+  if (partition_tokens > 0) {
+    if (partition_tokens % pool->block_size) return KV_ERR_INVALID_ARG;
+    int64_t chunk = partition_tokens / pool->block_size;
+    // longer runs when the batch would need more runs than counter slots
+    const int64_t min_chunk = (units + kCounterSlots - 9) / (kCounterSlots - 8);
+    if (chunk < min_chunk) chunk = min_chunk;
+    plan->chunk = (int32_t)chunk;
+    workers = (units + chunk - 1) / chunk;
+  } else {
+    plan->chunk = 0;
+    workers = (int64_t)pool->num_cus * waves_per_cu();
+    if (workers > units) workers = units;
+  }
+  if (workers < 1) workers = 1;
+  workers = (workers + 7) & ~7LL;
+  if (workers > kCounterSlots) return KV_ERR_INVALID_ARG;
+  plan->num_workers = (int32_t)workers;
+  plan->counters_bytes = (size_t)kCounterSlots * sizeof(int32_t);
+  plan->bytes = plan->counters_bytes + (size_t)2 * workers * G * (pool->head_dim + 4) * sizeof(float);
+  return KV_OK;
+}
+
+}  // namespace
+
+extern "C" kv_status_t paged_attention_workspace_size(const kv_pool_t* pool, int32_t num_seqs, int32_t num_q_heads,
+                                                      int32_t max_blocks, int32_t partition_tokens, size_t* bytes) {
+  if (!bytes) return KV_ERR_INVALID_ARG;
+  Plan plan;
+  kv_status_t st = make_plan(pool, num_seqs, num_q_heads, max_blocks, partition_tokens, &plan);
+  if (st != KV_OK) return st;
+  *bytes = plan.bytes;
+  return KV_OK;
+}
+
+extern "C" kv_status_t paged_attention_decode(const kv_pool_t* pool, const void* q, kv_dtype_t q_dtype, void* out,
+                                              const int32_t* block_tables, int32_t max_blocks,
+                                              const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
+                                              float scale, int32_t partition_tokens, void* workspace,
+                                              size_t workspace_bytes, void* stream) {
+  Plan plan;
+  kv_status_t st = make_plan(pool, num_seqs, num_q_heads, max_blocks, partition_tokens, &plan);
+  if (st != KV_OK) return st;
+  if (!valid_dtype(q_dtype)) return KV_ERR_INVALID_ARG;
+  if (num_seqs == 0) return KV_OK;
+  if (!q || !out || !block_tables || !context_lens) return KV_ERR_INVALID_ARG;
+  if ((((uintptr_t)q) | ((uintptr_t)out)) & 15) return KV_ERR_INVALID_ARG;
+  if (!(scale == scale) || scale > 3.0e38f || scale < -3.0e38f) return KV_ERR_INVALID_ARG;
+  if (!workspace || workspace_bytes < plan.bytes || ((uintptr_t)workspace & 255)) return KV_ERR_WORKSPACE;
+
+  const int D = pool->head_dim;
+  const int G = num_q_heads / pool->num_kv_heads;
+  DecodeParams p;
+  p.k_pool = (const uint8_t*)pool->k;
+  p.v_pool = (const uint8_t*)pool->v;
+  p.q = (const uint8_t*)q;
+  p.out = (uint8_t*)out;
+  p.block_tables = block_tables;
+  p.context_lens = context_lens;
+  p.counters = (int32_t*)workspace;
+  p.partials = (float*)((uint8_t*)workspace + plan.counters_bytes);
+  p.num_seqs = num_seqs;
+  p.num_kv_heads = pool->num_kv_heads;
+  p.max_blocks = max_blocks;
+  p.num_blocks = pool->num_blocks;
+  p.log2_bs = pool->log2_block_size;
+  p.chunk = plan.chunk;
+  p.num_workers = plan.num_workers;
+  const bool fp8 = pool->dtype == KV_FP8_E4M3FN;
+  p.q_scale = scale * kLog2e * (fp8 ? pool->k_scale : 1.0f);
+  p.v_scale = fp8 ? pool->v_scale : 1.0f;
+
+  // a wave load covers 64 / (lanes per token row) tokens of one block
+  const int lanes_per_row = D * (int)elem_bytes(pool->dtype) / 16;
+  if (64 / lanes_per_row > pool->block_size) return KV_ERR_UNSUPPORTED;
+
+  hipStream_t s = (hipStream_t)stream;
+  if (!fp8) {
+    if (q_dtype != pool->dtype) return KV_ERR_UNSUPPORTED;
+    switch (pool->dtype) {
+      case KV_F32: return launch_decode_f32_f32(p, D, G, s);
+      case KV_F16: return launch_decode_f16_f16(p, D, G, s);
+      case KV_BF16: return launch_decode_bf16_bf16(p, D, G, s);
+      default: return KV_ERR_UNSUPPORTED;
+    }
+  }
+  switch (q_dtype) {
+    case KV_F32: return launch_decode_fp8_f32(p, D, G, s);
+    case KV_F16: return launch_decode_fp8_f16(p, D, G, s);
+    case KV_BF16: return launch_decode_fp8_bf16(p, D, G, s);
+    default: return KV_ERR_UNSUPPORTED;
+  }
+}

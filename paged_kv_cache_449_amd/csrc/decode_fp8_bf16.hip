@@ -1,0 +1,8 @@
+// Decode kernel instantiations for fp8 KV pools with bf16 queries.
+#include "decode_kernel.h"
+
+namespace pkv {
+kv_status_t launch_decode_fp8_bf16(const DecodeParams& p, int D, int G, hipStream_t s) {
+  return launch_decode<fp8_t, bf16_t>(p, D, G, s);
+}
+}  // namespace pkv

@@ -1,0 +1,433 @@
+// Paged decode attention kernel (wave-per-worker, balanced split-KV).
+//
+// What it computes: for every sequence s and query head hq,
+//   out[s][hq] = sum_t softmax_t(scale * q[s][hq] . K_t) * V_t,  t < len[s],
+// where K_t/V_t are read through the block table: physical block
+// block_tables[s][t / bs], slot t % bs, kv head hq / G.  The table lookup is
+// one integer load per block followed by an offset computation ("vLLM — 把操作
+// 系统的分页搬进 GPU KV cache": core mechanisms, kernel paragraph).  Decode is
+// bound by the KV read bandwidth (same page, lessons), so the kernel is built
+// as an HBM stream on the vector ALUs; there is no dense contraction for the
+// matrix cores when each kv head serves one query row.
+//
+// Work split.  The blocks of all (kv head, sequence) pairs are laid end to end
+// in (kv head, sequence, block) order -- T blocks in all -- and worker w (one
+// 64-lane wavefront) takes blocks [w*chunk, (w+1)*chunk).  Every worker
+// streams the same number of bytes however the context lengths are spread.
+// A run of one (kv head, sequence) that lies inside one worker is finished by
+// it; a run cut between workers leaves one partial (running max m, sum l,
+// unnormalised accumulator) per worker, and the worker that finishes last
+// (an atomic counter per run) merges them in worker order.
+//
+// Worker ids are assigned so that consecutive ids run on the same XCD (the
+// dispatcher deals work-groups round robin over the 8 XCDs): neighbouring
+// runs -- e.g. candidates sharing a prompt's blocks -- then share that XCD's
+// L2.
+//
+// Lane layout.  A token row of head_dim elements is read by L lanes with one
+// 16-byte load each; a wave load covers TPL = 64/L consecutive tokens of one
+// block tile (a tile [bs][head_dim] of one kv head is contiguous in the pool).
+// The L lanes of a row reduce their partial dot products with DPP; each row
+// keeps its own online-softmax state over the tokens it sees, and the TPL
+// rows are merged once at the end of a run.
+#pragma once
+
+#include "common.h"
+
+namespace pkv {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kLoadsPerStep = 4;  // wave loads of K (and of V) issued together
+// Arrival counters of split runs, indexed by the run's first worker (a worker
+// starts at most one run that continues past its end).  The region has a
+// fixed size and sits at the start of the workspace, so calls with different
+// batch shapes can share one workspace: each call leaves it zero.
+constexpr int kCounterSlots = 65536;
+
+struct DecodeParams {
+  const uint8_t* k_pool;
+  const uint8_t* v_pool;
+  const uint8_t* q;
+  uint8_t* out;
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  int32_t* counters;     // [kCounterSlots], zero between calls
+  float* partials;       // [2 * num_workers][G][head_dim + 4]
+  int32_t num_seqs;
+  int32_t num_kv_heads;
+  int32_t max_blocks;
+  int32_t num_blocks;
+  int32_t log2_bs;
+  int32_t chunk;         // blocks per worker; 0 = ceil(T / num_workers)
+  int32_t num_workers;   // multiple of 8
+  float q_scale;         // softmax scale * log2(e) * k_scale
+  float v_scale;
+};
+
+template <typename KV, int D>
+struct DecodeShape {
+  static constexpr int EB = elem_size<KV>::value;
+  static constexpr int VEC = 16 / EB;   // elements per lane per load
+  static constexpr int L = D / VEC;     // lanes per token row
+  static constexpr int TPL = 64 / L;    // tokens per wave load
+  static constexpr int REC = D + 4;     // floats per partial record: acc[D], m, l, pad
+  static_assert(L >= 1 && L <= 64 && (64 % L) == 0, "row layout");
+};
+
+__device__ inline int clamp_len(int n, int max_len) { return n < 0 ? 0 : (n > max_len ? max_len : n); }
+
+__device__ inline float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Load VEC elements of type T (4-byte aligned) and widen them to fp32.
+template <typename T, int VEC>
+__device__ inline void load_row_f32(const uint8_t* p, float* o) {
+  constexpr int PW = unpack<T>::per_word;
+  constexpr int NW = VEC / PW;
+  const uint32_t* w = (const uint32_t*)p;
+#pragma unroll
+  for (int i = 0; i < NW; ++i) unpack<T>::run(w[i], o + i * PW);
+}
+
+// Store VEC fp32 values * mul as type T (4-byte aligned destination).
+template <typename T, int VEC>
+__device__ inline void store_row(uint8_t* p, const float* v, float mul) {
+  constexpr int PW = pack_out<T>::per_word;
+  constexpr int NW = VEC / PW;
+  uint32_t* w = (uint32_t*)p;
+#pragma unroll
+  for (int i = 0; i < NW; ++i) {
+    float t[PW];
+#pragma unroll
+    for (int j = 0; j < PW; ++j) t[j] = v[i * PW + j] * mul;
+    w[i] = pack_out<T>::run(t);
+  }
+}
+
+// Online-softmax update of one state (m, l, acc) with NS new scores whose
+// exponentials are returned in pw (scores are already in log2 units).
+template <int NS>
+__device__ inline float softmax_step(float& m, float& l, const float* sc, float* pw) {
+  float mx = sc[0];
+#pragma unroll
+  for (int u = 1; u < NS; ++u) mx = fmaxf(mx, sc[u]);
+  const float mn = fmaxf(m, mx);
+  const float mu = mn == -INFINITY ? 0.0f : mn;
+  const float alpha = fexp2(m - mu);
+  float ps = 0.0f;
+#pragma unroll
+  for (int u = 0; u < NS; ++u) {
+    pw[u] = fexp2(sc[u] - mu);
+    ps += pw[u];
+  }
+  l = l * alpha + ps;
+  m = mn;
+  return alpha;
+}
+
+template <typename KV, typename QT, int D, int G>
+__device__ inline void decode_run(const DecodeParams& p, int w, int chunk, int wstart, int pos, int s, int h,
+                                  int off, int len, int n, int nb) {
+  using Sh = DecodeShape<KV, D>;
+  constexpr int VEC = Sh::VEC, L = Sh::L, TPL = Sh::TPL, REC = Sh::REC;
+  constexpr int U = kLoadsPerStep;
+  constexpr int QE = elem_size<QT>::value;
+  const int lane = threadIdx.x;
+  const int row = lane / L;
+  const int col = lane % L;
+  const int Hq = p.num_kv_heads * G;
+
+  // query rows of the G heads served by kv head h, pre-scaled into log2 units
+  float qv[G][VEC];
+  {
+    const int64_t qe = ((int64_t)s * Hq + (int64_t)h * G) * D + (int64_t)col * VEC;
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      load_row_f32<QT, VEC>(p.q + (qe + (int64_t)g * D) * QE, qv[g]);
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) qv[g][i] *= p.q_scale;
+    }
+  }
+
+  float m[G], l[G], acc[G][VEC];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    m[g] = -INFINITY;
+    l[g] = 0.0f;
+#pragma unroll
+    for (int i = 0; i < VEC; ++i) acc[g][i] = 0.0f;
+  }
+
+  const int64_t tile = ((int64_t)D * Sh::EB) << p.log2_bs;   // bytes of one (block, head) tile
+  const int64_t blk_stride = tile * p.num_kv_heads;
+  const uint8_t* kh = p.k_pool + tile * h + col * 16;
+  const uint8_t* vh = p.v_pool + tile * h + col * 16;
+  const int row_bytes = D * Sh::EB;
+  const int bs_mask = (1 << p.log2_bs) - 1;
+  const int32_t* trow = p.block_tables + (int64_t)s * p.max_blocks + off;
+
+  for (int wb = 0; wb < len; wb += 64) {
+    const int cnt = min(64, len - wb);
+    int tab = -1;
+    if (lane < cnt) {
+      const int e = trow[wb + lane];
+      tab = (uint32_t)e < (uint32_t)p.num_blocks ? e : -1;
+    }
+    const int tlo = (off + wb) << p.log2_bs;
+    const int thi = min((off + wb + cnt) << p.log2_bs, n);
+    const int nl = (thi - tlo + TPL - 1) / TPL;   // wave loads in this window
+
+    for (int j0 = 0; j0 < nl; j0 += U) {
+      uint4 kr[U], vr[U];
+      bool ok[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int j = j0 + u;
+        const int t = tlo + j * TPL + row;
+        int bi = (j * TPL) >> p.log2_bs;
+        bi = bi < 63 ? bi : 63;
+        const int phys = __builtin_amdgcn_readlane(tab, bi);
+        ok[u] = (j < nl) && (t < thi) && (phys >= 0);
+        kr[u] = make_uint4(0, 0, 0, 0);
+        vr[u] = make_uint4(0, 0, 0, 0);
+        if (ok[u]) {
+          const int64_t o = blk_stride * phys + (int64_t)(t & bs_mask) * row_bytes;
+          kr[u] = *(const uint4*)(kh + o);
+          vr[u] = *(const uint4*)(vh + o);
+        }
+      }
+      // scores: partial dot over this lane's VEC elements, reduced over the row
+      float sc[G][U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        float kf[VEC];
+        const uint32_t kw[4] = {kr[u].x, kr[u].y, kr[u].z, kr[u].w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) unpack<KV>::run(kw[i], kf + i * unpack<KV>::per_word);
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          float d = 0.0f;
+#pragma unroll
+          for (int i = 0; i < VEC; ++i) d = fmaf(qv[g][i], kf[i], d);
+          d = group_sum<L>(d);
+          sc[g][u] = ok[u] ? d : -INFINITY;
+        }
+      }
+      float pw[G][U];
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        const float alpha = softmax_step<U>(m[g], l[g], sc[g], pw[g]);
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) acc[g][i] *= alpha;
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        float vf[VEC];
+        const uint32_t vw[4] = {vr[u].x, vr[u].y, vr[u].z, vr[u].w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) unpack<KV>::run(vw[i], vf + i * unpack<KV>::per_word);
+#pragma unroll
+        for (int g = 0; g < G; ++g)
+#pragma unroll
+          for (int i = 0; i < VEC; ++i) acc[g][i] = fmaf(pw[g][u], vf[i], acc[g][i]);
+      }
+    }
+  }
+
+  // merge the TPL row states (rows hold the same columns)
+#pragma unroll
+  for (int o = L; o < 64; o <<= 1) {
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const float mo = __shfl_xor(m[g], o);
+      const float lo = __shfl_xor(l[g], o);
+      const float mn = fmaxf(m[g], mo);
+      const float mu = mn == -INFINITY ? 0.0f : mn;
+      const float a = fexp2(m[g] - mu), b = fexp2(mo - mu);
+      l[g] = l[g] * a + lo * b;
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) acc[g][i] = acc[g][i] * a + __shfl_xor(acc[g][i], o) * b;
+      m[g] = mn;
+    }
+  }
+
+  const int64_t oe = ((int64_t)s * Hq + (int64_t)h * G) * D + (int64_t)col * VEC;
+  if (off == 0 && off + len == nb) {   // the whole run is ours
+    if (row == 0) {
+#pragma unroll
+      for (int g = 0; g < G; ++g)
+        store_row<QT, VEC>(p.out + (oe + (int64_t)g * D) * QE, acc[g], l[g] > 0.0f ? p.v_scale / l[g] : 0.0f);
+    }
+    return;
+  }
+
+  // partial: publish (acc, m, l), then the last worker of the run merges
+  const int k = pos == wstart ? 0 : 1;
+  float* rec = p.partials + (int64_t)(2 * w + k) * G * REC;
+  if (row == 0) {
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+#pragma unroll
+      for (int i = 0; i < VEC; i += 4)
+        *(float4*)(rec + g * REC + col * VEC + i) = make_float4(acc[g][i], acc[g][i + 1], acc[g][i + 2], acc[g][i + 3]);
+      if (col == 0) {
+        rec[g * REC + D] = m[g];
+        rec[g * REC + D + 1] = l[g];
+      }
+    }
+  }
+  __threadfence();
+  const int seg_start = pos - off;
+  const int first_w = seg_start / chunk;
+  const int last_w = (seg_start + nb - 1) / chunk;
+  int done = 0;
+  if (lane == 0) done = atomicAdd(p.counters + first_w, 1);
+  done = __shfl(done, 0);
+  if (done != last_w - first_w) return;
+  __threadfence();
+
+  float M[G];
+#pragma unroll
+  for (int g = 0; g < G; ++g) M[g] = -INFINITY;
+  for (int v = first_w; v <= last_w; ++v) {
+    const float* r = p.partials + (int64_t)(2 * v + (v * chunk >= seg_start ? 0 : 1)) * G * REC;
+#pragma unroll
+    for (int g = 0; g < G; ++g) M[g] = fmaxf(M[g], r[g * REC + D]);
+  }
+  float lsum[G], o[G][VEC];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    lsum[g] = 0.0f;
+#pragma unroll
+    for (int i = 0; i < VEC; ++i) o[g][i] = 0.0f;
+  }
+  for (int v = first_w; v <= last_w; ++v) {
+    const float* r = p.partials + (int64_t)(2 * v + (v * chunk >= seg_start ? 0 : 1)) * G * REC;
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const float mu = M[g] == -INFINITY ? 0.0f : M[g];
+      const float f = fexp2(r[g * REC + D] - mu);
+      lsum[g] = fmaf(f, r[g * REC + D + 1], lsum[g]);
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) o[g][i] = fmaf(f, r[g * REC + col * VEC + i], o[g][i]);
+    }
+  }
+  if (row == 0) {
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+      store_row<QT, VEC>(p.out + (oe + (int64_t)g * D) * QE, o[g], lsum[g] > 0.0f ? p.v_scale / lsum[g] : 0.0f);
+  }
+  if (lane == 0) p.counters[first_w] = 0;
+}
+
+template <typename KV, typename QT, int D, int G>
+__global__ __launch_bounds__(64) void paged_decode_kernel(const DecodeParams p) {
+  const int lane = threadIdx.x;
+  const int S = p.num_seqs;
+  const int bs = 1 << p.log2_bs;
+  const int max_len = p.max_blocks << p.log2_bs;
+  const int per_xcd = p.num_workers >> 3;
+  const int w = (int)(blockIdx.x & 7) * per_xcd + (int)(blockIdx.x >> 3);
+
+  // blocks per kv head, and whether some sequence is empty
+  int total = 0;
+  bool empty = false;
+  for (int base = 0; base < S; base += 64) {
+    const int s = base + lane;
+    int nb = 0;
+    if (s < S) {
+      const int n = clamp_len(p.context_lens[s], max_len);
+      nb = (n + bs - 1) >> p.log2_bs;
+      empty |= n == 0;
+    }
+    total += wave_sum_i32(nb);
+  }
+
+  if (w == 0 && __ballot(empty)) {
+    // empty contexts attend to nothing: their rows are zero
+    constexpr int QE = elem_size<QT>::value;
+    const int Hq = p.num_kv_heads * G;
+    for (int s = 0; s < S; ++s) {
+      if (clamp_len(p.context_lens[s], max_len) != 0) continue;
+      uint8_t* o = p.out + (int64_t)s * Hq * D * QE;
+      for (int i = lane * 4; i < Hq * D * QE; i += 256) *(uint32_t*)(o + i) = 0u;
+    }
+  }
+
+  const int T = total * p.num_kv_heads;
+  const int chunk = p.chunk > 0 ? p.chunk : max(1, (T + p.num_workers - 1) / p.num_workers);
+  const int start = w * chunk;
+  if (start >= T) return;
+  const int end = min(start + chunk, T);
+  int h = start / total;
+  const int r = start - h * total;
+
+  // the sequence whose run contains block r of kv head h
+  int s = 0, pre = 0;
+  bool found = false;
+  {
+    int carry = 0;
+    for (int base = 0; base < S; base += 64) {
+      const int sl = base + lane;
+      int nb = 0;
+      if (sl < S) nb = (clamp_len(p.context_lens[sl], max_len) + bs - 1) >> p.log2_bs;
+      const int incl = wave_inclusive_scan_i32(nb, lane);
+      const int excl = carry + incl - nb;
+      const unsigned long long hit = __ballot(nb > 0 && excl <= r && r < excl + nb);
+      if (hit) {
+        const int src = __builtin_ctzll(hit);
+        s = base + src;
+        pre = __shfl(excl, src);
+        found = true;
+        break;
+      }
+      carry += __shfl(incl, 63);
+    }
+  }
+
+  if (!found) return;  // lengths changed under the launch: nothing consistent to do
+  int off = r - pre;
+  int pos = start;
+  int n = clamp_len(p.context_lens[s], max_len);
+  int nb = (n + bs - 1) >> p.log2_bs;
+  while (true) {
+    const int len = min(nb - off, end - pos);
+    decode_run<KV, QT, D, G>(p, w, chunk, start, pos, s, h, off, len, n, nb);
+    pos += len;
+    if (pos >= end) break;
+    do {
+      if (++s == S) {
+        s = 0;
+        if (++h == p.num_kv_heads) return;
+      }
+      n = clamp_len(p.context_lens[s], max_len);
+      nb = (n + bs - 1) >> p.log2_bs;
+    } while (nb == 0);
+    off = 0;
+  }
+}
+
+// Launch one instantiation; defined per KV/Q dtype pair in decode_*.hip.
+template <typename KV, typename QT>
+kv_status_t launch_decode(const DecodeParams& p, int D, int G, hipStream_t stream) {
+#define PKV_CASE(DD, GG)                                                                                     \
+  if (D == DD && G == GG) {                                                                                  \
+    hipLaunchKernelGGL((paged_decode_kernel<KV, QT, DD, GG>), dim3(p.num_workers), dim3(64), 0, stream, p); \
+    return launch_status();                                                                                  \
+  }
+#define PKV_CASES(DD) PKV_CASE(DD, 1) PKV_CASE(DD, 2) PKV_CASE(DD, 4) PKV_CASE(DD, 8)
+  PKV_CASES(64)
+  PKV_CASES(128)
+  PKV_CASES(256)
+#undef PKV_CASES
+#undef PKV_CASE
+  return KV_ERR_UNSUPPORTED;
+}
+
+kv_status_t launch_decode_f32_f32(const DecodeParams& p, int D, int G, hipStream_t s);
+kv_status_t launch_decode_f16_f16(const DecodeParams& p, int D, int G, hipStream_t s);
+kv_status_t launch_decode_bf16_bf16(const DecodeParams& p, int D, int G, hipStream_t s);
+kv_status_t launch_decode_fp8_f32(const DecodeParams& p, int D, int G, hipStream_t s);
+kv_status_t launch_decode_fp8_f16(const DecodeParams& p, int D, int G, hipStream_t s);
+kv_status_t launch_decode_fp8_bf16(const DecodeParams& p, int D, int G, hipStream_t s);
+
+}  // namespace pkv

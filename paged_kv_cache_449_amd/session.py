@@ -1,0 +1,83 @@
+"""A batch of sequences decoding over one KV pool.
+
+Host side: a BlockManager (free list, reference counts, tables, slots and
+copy-on-write plan).  Device side: the pool, plus the per-step slot mapping,
+copy pairs, block tables and context lengths.  A decode step enqueues, on the
+current stream:
+    copy_blocks(pairs)                      copy-on-write of shared blocks
+    reshape_and_cache(k_new, v_new, slots)  append each sequence's new token
+    paged_attention_decode(q, ...)          attend over the whole context
+(the order a serving engine runs them in once the new token's K/V exist:
+"vLLM 与 KV Cache", why a KV cache; "vLLM — 把操作系统的分页搬进 GPU KV cache",
+core mechanisms and case 2).
+"""
+from __future__ import annotations
+
+from typing import Hashable, List, Optional, Sequence
+
+import numpy as np
+import torch
+
+from . import KVPool, copy_blocks, paged_attention_decode, reshape_and_cache
+from .block_manager import BlockManager
+
+
+class DecodeSession:
+    def __init__(self, pool: KVPool, manager: BlockManager, num_q_heads: int):
+        if manager.num_blocks != pool.num_blocks or manager.block_size != pool.block_size:
+            raise ValueError("manager and pool disagree on the block layout")
+        self.pool, self.manager, self.num_q_heads = pool, manager, num_q_heads
+        self.seqs: List[Hashable] = []
+        self.slot_mapping: Optional[torch.Tensor] = None
+        self.pairs: Optional[torch.Tensor] = None
+        self.block_tables: Optional[torch.Tensor] = None
+        self.context_lens: Optional[torch.Tensor] = None
+
+    def _dev(self, a: np.ndarray) -> torch.Tensor:
+        return torch.from_numpy(np.ascontiguousarray(a)).to(self.pool.device, non_blocking=False)
+
+    def cache_prompts(self, items: Sequence) -> None:
+        """items: (seq, k, v) with k/v [L][Hkv][D] (host or device); registers
+        each sequence and writes its tokens with one reshape_and_cache call."""
+        slots, ks, vs = [], [], []
+        for seq, k, v in items:
+            slots.append(self.manager.add_sequence(seq, k.shape[0]))
+            ks.append(k)
+            vs.append(v)
+        if not ks or sum(k.shape[0] for k in ks) == 0:
+            return
+        k = torch.cat(ks).to(self.pool.device)
+        v = torch.cat(vs).to(self.pool.device)
+        reshape_and_cache(self.pool, k, v, self._dev(np.concatenate(slots)))
+
+    def fork(self, parent: Hashable, children: Sequence[Hashable]) -> None:
+        self.manager.fork(parent, children)
+
+    def free(self, seq: Hashable) -> None:
+        self.manager.free(seq)
+
+    def prepare_step(self, seqs: Sequence[Hashable], max_blocks: Optional[int] = None) -> None:
+        """Reserve one new slot per sequence (planning copy-on-write) and upload
+        the step's slot mapping, copy pairs, block tables and lengths."""
+        self.seqs = list(seqs)
+        slots = np.empty(len(self.seqs), dtype=np.int64)
+        pairs = []
+        for i, s in enumerate(self.seqs):
+            slot, pair = self.manager.append_slot(s)
+            slots[i] = slot
+            if pair is not None:
+                pairs.append(pair)
+        self.slot_mapping = self._dev(slots)
+        self.pairs = self._dev(np.asarray(pairs, dtype=np.int32).reshape(-1, 2))
+        self.block_tables = self._dev(self.manager.block_tables(self.seqs, max_blocks))
+        self.context_lens = self._dev(self.manager.context_lens(self.seqs))
+
+    def step(self, q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor, out: Optional[torch.Tensor] = None,
+             partition_tokens: int = 0, scale: Optional[float] = None) -> torch.Tensor:
+        """Enqueue one decode step; re-running it after the same prepare_step
+        rewrites the same bytes and recomputes the same outputs."""
+        scale = (1.0 / self.pool.head_dim ** 0.5) if scale is None else scale
+        copy_blocks(self.pool, self.pairs)
+        reshape_and_cache(self.pool, k_new, v_new, self.slot_mapping)
+        return paged_attention_decode(self.pool, q, self.block_tables, self.context_lens, scale, out=out,
+                                      partition_tokens=partition_tokens)
