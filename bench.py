@@ -118,6 +118,10 @@ def main(argv=None) -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--placement", choices=["shuffled", "sequential"], default="shuffled",
+                    help="shuffled: blocks from a seeded random free list (the workload); sequential: "
+                         "the free list in id order, so each sequence's blocks are contiguous (the "
+                         "paged-vs-contiguous comparison)")
     args = ap.parse_args(argv)
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -134,7 +138,8 @@ def main(argv=None) -> int:
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     print(f"[bench] building {wl.name}", file=sys.stderr, flush=True)
-    sess, q, kn, vn = build_session(wl, dev)
+    order = None if args.placement == "shuffled" else np.arange(wl.num_blocks, dtype=np.int32)
+    sess, q, kn, vn = build_session(wl, dev, free_order=order)
     out = torch.empty_like(q)
     pool = sess.pool
     pt = wl.partition_tokens
@@ -188,7 +193,8 @@ def main(argv=None) -> int:
         "config": {"workload": wl.name, "num_seqs": wl.num_seqs, "num_q_heads": wl.num_q_heads,
                    "num_kv_heads": wl.num_kv_heads, "head_dim": wl.head_dim, "block_size": wl.block_size,
                    "kv_dtype": wl.kv_dtype, "q_dtype": wl.q_dtype, "cached_tokens": nb["tokens"],
-                   "kv_bytes_per_step": nb["kv"], "partition_tokens": pt, "parallelism": "single GPU"},
+                   "kv_bytes_per_step": nb["kv"], "partition_tokens": pt, "placement": args.placement,
+                   "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
                      "kernel": "paged_decode_kernel", "kernel_us": round(float(dec_ms.mean()) * 1e3, 2),

@@ -14,7 +14,7 @@ int waves_per_cu() {
   static int v = [] {
     const char* e = getenv("PAGEDKV_DECODE_WAVES_PER_CU");
     int x = e ? atoi(e) : 0;
-    return (x >= 1 && x <= 64) ? x : 16;
+    return (x >= 1 && x <= 64) ? x : 8;
   }();
   return v;
 }

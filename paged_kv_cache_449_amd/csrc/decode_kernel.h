@@ -124,6 +124,111 @@ __device__ inline float softmax_step(float& m, float& l, const float* sc, float*
   return alpha;
 }
 
+// Buffer resource word 3 for raw (untyped) buffer loads on gfx9-family parts.
+constexpr int kBufferWord3 = 0x00020000;
+// Lane offset that lies outside every tile: the load returns zeros.
+constexpr uint32_t kMaskedOffset = 0x80000000u;
+
+__device__ inline int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+// Registers of one step: U wave loads of K and of V.
+template <int U>
+struct StepRegs {
+  uint4 k[U];
+  uint4 v[U];
+};
+
+// Per-run constants shared by the load and compute phases.
+struct RunCtx {
+  const uint8_t* k_head;   // pool base + kv head offset (uniform)
+  const uint8_t* v_head;
+  int64_t blk_stride;      // bytes between consecutive physical blocks
+  uint32_t tile_bytes;     // bytes of one (block, head) tile
+  uint32_t lane_off;       // col * 16
+  int row_bytes;
+  int log2_bs;
+  int bs_mask;
+};
+
+// Issue the U K and V loads of step `step` of the current table window.
+// Tokens at or past `thi`, and blocks whose table entry is out of range,
+// read as zeros (offset outside the tile, or an empty tile).
+template <int U, int TPL>
+__device__ inline void issue_step(const RunCtx& c, int tab, int tlo, int thi, int step, int row,
+                                  StepRegs<U>& r) {
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int j = step * U + u;                    // wave load index in the window
+    const int bi = min((j * TPL) >> c.log2_bs, 63);
+    const int phys = __builtin_amdgcn_readlane(tab, bi);
+    const bool pvalid = phys >= 0;
+    const int64_t boff = pvalid ? c.blk_stride * phys : 0;
+    const uint32_t nrec = pvalid ? c.tile_bytes : 0u;
+    __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void*)(c.k_head + boff), (short)0, (int)nrec,
+                                                                  kBufferWord3);
+    __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void*)(c.v_head + boff), (short)0, (int)nrec,
+                                                                  kBufferWord3);
+    const int t = tlo + j * TPL + row;
+    const uint32_t off = t < thi ? (uint32_t)((t & c.bs_mask) * c.row_bytes) + c.lane_off : kMaskedOffset;
+    r.k[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0));
+    r.v[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, 0));
+  }
+}
+
+// Scores, online-softmax update and V accumulation for one step.
+template <typename KV, int VEC, int L, int TPL, int G, int U>
+__device__ inline void compute_step(const StepRegs<U>& r, const float (&qv)[G][VEC], float (&m)[G], float (&l)[G],
+                                    float (&acc)[G][VEC], int tab, int tlo, int thi, int step, int row,
+                                    int log2_bs) {
+  float sc[G][U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int j = step * U + u;
+    const int bi = min((j * TPL) >> log2_bs, 63);
+    const bool ok = (tlo + j * TPL + row < thi) && (__builtin_amdgcn_readlane(tab, bi) >= 0);
+    float kf[VEC];
+    const uint32_t kw[4] = {r.k[u].x, r.k[u].y, r.k[u].z, r.k[u].w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) unpack<KV>::run(kw[i], kf + i * unpack<KV>::per_word);
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      float d = 0.0f;
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) d = fmaf(qv[g][i], kf[i], d);
+      d = group_sum<L>(d);
+      sc[g][u] = ok ? d : -INFINITY;
+    }
+  }
+  float pw[G][U];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    const float alpha = softmax_step<U>(m[g], l[g], sc[g], pw[g]);
+#pragma unroll
+    for (int i = 0; i < VEC; ++i) acc[g][i] *= alpha;
+  }
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    float vf[VEC];
+    const uint32_t vw[4] = {r.v[u].x, r.v[u].y, r.v[u].z, r.v[u].w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) unpack<KV>::run(vw[i], vf + i * unpack<KV>::per_word);
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) acc[g][i] = fmaf(pw[g][u], vf[i], acc[g][i]);
+  }
+}
+
+__device__ inline void store_coherent(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ inline float load_coherent(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// One run: blocks [off, off+len) of the (kv head h, sequence s) stream, which
+// has nb blocks and n tokens.  pos is the run's place in the flattened
+// stream and wstart the worker's first block.  All scalars are uniform.
 template <typename KV, typename QT, int D, int G>
 __device__ inline void decode_run(const DecodeParams& p, int w, int chunk, int wstart, int pos, int s, int h,
                                   int off, int len, int n, int nb) {
@@ -157,80 +262,42 @@ __device__ inline void decode_run(const DecodeParams& p, int w, int chunk, int w
     for (int i = 0; i < VEC; ++i) acc[g][i] = 0.0f;
   }
 
-  const int64_t tile = ((int64_t)D * Sh::EB) << p.log2_bs;   // bytes of one (block, head) tile
-  const int64_t blk_stride = tile * p.num_kv_heads;
-  const uint8_t* kh = p.k_pool + tile * h + col * 16;
-  const uint8_t* vh = p.v_pool + tile * h + col * 16;
-  const int row_bytes = D * Sh::EB;
-  const int bs_mask = (1 << p.log2_bs) - 1;
+  RunCtx c;
+  const int64_t tile = ((int64_t)D * Sh::EB) << p.log2_bs;
+  c.k_head = p.k_pool + tile * h;
+  c.v_head = p.v_pool + tile * h;
+  c.blk_stride = tile * p.num_kv_heads;
+  c.tile_bytes = (uint32_t)tile;
+  c.lane_off = (uint32_t)col * 16u;
+  c.row_bytes = D * Sh::EB;
+  c.log2_bs = p.log2_bs;
+  c.bs_mask = (1 << p.log2_bs) - 1;
   const int32_t* trow = p.block_tables + (int64_t)s * p.max_blocks + off;
 
+  auto load_tab = [&](int wb) {
+    const int cnt = min(64, len - wb);
+    int e = -1;
+    if (lane < cnt) e = trow[wb + lane];
+    return (uint32_t)e < (uint32_t)p.num_blocks ? e : -1;
+  };
+
+  int tab = load_tab(0);
   for (int wb = 0; wb < len; wb += 64) {
     const int cnt = min(64, len - wb);
-    int tab = -1;
-    if (lane < cnt) {
-      const int e = trow[wb + lane];
-      tab = (uint32_t)e < (uint32_t)p.num_blocks ? e : -1;
-    }
+    // the next window's table entries load while this window streams
+    const int tab_next = wb + 64 < len ? load_tab(wb + 64) : -1;
     const int tlo = (off + wb) << p.log2_bs;
     const int thi = min((off + wb + cnt) << p.log2_bs, n);
-    const int nl = (thi - tlo + TPL - 1) / TPL;   // wave loads in this window
-
-    for (int j0 = 0; j0 < nl; j0 += U) {
-      uint4 kr[U], vr[U];
-      bool ok[U];
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int j = j0 + u;
-        const int t = tlo + j * TPL + row;
-        int bi = (j * TPL) >> p.log2_bs;
-        bi = bi < 63 ? bi : 63;
-        const int phys = __builtin_amdgcn_readlane(tab, bi);
-        ok[u] = (j < nl) && (t < thi) && (phys >= 0);
-        kr[u] = make_uint4(0, 0, 0, 0);
-        vr[u] = make_uint4(0, 0, 0, 0);
-        if (ok[u]) {
-          const int64_t o = blk_stride * phys + (int64_t)(t & bs_mask) * row_bytes;
-          kr[u] = *(const uint4*)(kh + o);
-          vr[u] = *(const uint4*)(vh + o);
-        }
-      }
-      // scores: partial dot over this lane's VEC elements, reduced over the row
-      float sc[G][U];
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        float kf[VEC];
-        const uint32_t kw[4] = {kr[u].x, kr[u].y, kr[u].z, kr[u].w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) unpack<KV>::run(kw[i], kf + i * unpack<KV>::per_word);
-#pragma unroll
-        for (int g = 0; g < G; ++g) {
-          float d = 0.0f;
-#pragma unroll
-          for (int i = 0; i < VEC; ++i) d = fmaf(qv[g][i], kf[i], d);
-          d = group_sum<L>(d);
-          sc[g][u] = ok[u] ? d : -INFINITY;
-        }
-      }
-      float pw[G][U];
-#pragma unroll
-      for (int g = 0; g < G; ++g) {
-        const float alpha = softmax_step<U>(m[g], l[g], sc[g], pw[g]);
-#pragma unroll
-        for (int i = 0; i < VEC; ++i) acc[g][i] *= alpha;
-      }
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        float vf[VEC];
-        const uint32_t vw[4] = {vr[u].x, vr[u].y, vr[u].z, vr[u].w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) unpack<KV>::run(vw[i], vf + i * unpack<KV>::per_word);
-#pragma unroll
-        for (int g = 0; g < G; ++g)
-#pragma unroll
-          for (int i = 0; i < VEC; ++i) acc[g][i] = fmaf(pw[g][u], vf[i], acc[g][i]);
-      }
+    const int steps = (thi - tlo + U * TPL - 1) / (U * TPL);
+    StepRegs<U> a, b;
+    issue_step<U, TPL>(c, tab, tlo, thi, 0, row, a);
+    for (int st = 0; st < steps; st += 2) {
+      if (st + 1 < steps) issue_step<U, TPL>(c, tab, tlo, thi, st + 1, row, b);
+      compute_step<KV, VEC, L, TPL, G, U>(a, qv, m, l, acc, tab, tlo, thi, st, row, p.log2_bs);
+      if (st + 2 < steps) issue_step<U, TPL>(c, tab, tlo, thi, st + 2, row, a);
+      if (st + 1 < steps) compute_step<KV, VEC, L, TPL, G, U>(b, qv, m, l, acc, tab, tlo, thi, st + 1, row, p.log2_bs);
     }
+    tab = tab_next;
   }
 
   // merge the TPL row states (rows hold the same columns)
@@ -260,30 +327,32 @@ __device__ inline void decode_run(const DecodeParams& p, int w, int chunk, int w
     return;
   }
 
-  // partial: publish (acc, m, l), then the last worker of the run merges
+  // Partial: publish (acc, m, l) with stores that write through to the
+  // device coherence point, wait for them to complete, then count this
+  // worker in; the worker that completes the count merges.  Its loads of the
+  // records are coherent loads, so no cache-wide writeback or invalidate is
+  // needed on either side.
   const int k = pos == wstart ? 0 : 1;
   float* rec = p.partials + (int64_t)(2 * w + k) * G * REC;
   if (row == 0) {
 #pragma unroll
     for (int g = 0; g < G; ++g) {
 #pragma unroll
-      for (int i = 0; i < VEC; i += 4)
-        *(float4*)(rec + g * REC + col * VEC + i) = make_float4(acc[g][i], acc[g][i + 1], acc[g][i + 2], acc[g][i + 3]);
+      for (int i = 0; i < VEC; ++i) store_coherent(rec + g * REC + col * VEC + i, acc[g][i]);
       if (col == 0) {
-        rec[g * REC + D] = m[g];
-        rec[g * REC + D + 1] = l[g];
+        store_coherent(rec + g * REC + D, m[g]);
+        store_coherent(rec + g * REC + D + 1, l[g]);
       }
     }
   }
-  __threadfence();
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   const int seg_start = pos - off;
   const int first_w = seg_start / chunk;
   const int last_w = (seg_start + nb - 1) / chunk;
   int done = 0;
-  if (lane == 0) done = atomicAdd(p.counters + first_w, 1);
-  done = __shfl(done, 0);
+  if (lane == 0) done = __hip_atomic_fetch_add(p.counters + first_w, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  done = uniform(__shfl(done, 0));
   if (done != last_w - first_w) return;
-  __threadfence();
 
   float M[G];
 #pragma unroll
@@ -291,7 +360,7 @@ __device__ inline void decode_run(const DecodeParams& p, int w, int chunk, int w
   for (int v = first_w; v <= last_w; ++v) {
     const float* r = p.partials + (int64_t)(2 * v + (v * chunk >= seg_start ? 0 : 1)) * G * REC;
 #pragma unroll
-    for (int g = 0; g < G; ++g) M[g] = fmaxf(M[g], r[g * REC + D]);
+    for (int g = 0; g < G; ++g) M[g] = fmaxf(M[g], load_coherent(r + g * REC + D));
   }
   float lsum[G], o[G][VEC];
 #pragma unroll
@@ -305,10 +374,10 @@ __device__ inline void decode_run(const DecodeParams& p, int w, int chunk, int w
 #pragma unroll
     for (int g = 0; g < G; ++g) {
       const float mu = M[g] == -INFINITY ? 0.0f : M[g];
-      const float f = fexp2(r[g * REC + D] - mu);
-      lsum[g] = fmaf(f, r[g * REC + D + 1], lsum[g]);
+      const float f = fexp2(load_coherent(r + g * REC + D) - mu);
+      lsum[g] = fmaf(f, load_coherent(r + g * REC + D + 1), lsum[g]);
 #pragma unroll
-      for (int i = 0; i < VEC; ++i) o[g][i] = fmaf(f, r[g * REC + col * VEC + i], o[g][i]);
+      for (int i = 0; i < VEC; ++i) o[g][i] = fmaf(f, load_coherent(r + g * REC + col * VEC + i), o[g][i]);
     }
   }
   if (row == 0) {
@@ -316,7 +385,7 @@ __device__ inline void decode_run(const DecodeParams& p, int w, int chunk, int w
     for (int g = 0; g < G; ++g)
       store_row<QT, VEC>(p.out + (oe + (int64_t)g * D) * QE, o[g], lsum[g] > 0.0f ? p.v_scale / lsum[g] : 0.0f);
   }
-  if (lane == 0) p.counters[first_w] = 0;
+  if (lane == 0) __hip_atomic_store(p.counters + first_w, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 template <typename KV, typename QT, int D, int G>
@@ -341,6 +410,7 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(const DecodeParams p) 
     }
     total += wave_sum_i32(nb);
   }
+  total = uniform(total);
 
   if (w == 0 && __ballot(empty)) {
     // empty contexts attend to nothing: their rows are zero
@@ -385,9 +455,10 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(const DecodeParams p) 
   }
 
   if (!found) return;  // lengths changed under the launch: nothing consistent to do
-  int off = r - pre;
+  s = uniform(s);
+  int off = uniform(r - pre);
   int pos = start;
-  int n = clamp_len(p.context_lens[s], max_len);
+  int n = uniform(clamp_len(p.context_lens[s], max_len));
   int nb = (n + bs - 1) >> p.log2_bs;
   while (true) {
     const int len = min(nb - off, end - pos);
@@ -399,7 +470,7 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(const DecodeParams p) 
         s = 0;
         if (++h == p.num_kv_heads) return;
       }
-      n = clamp_len(p.context_lens[s], max_len);
+      n = uniform(clamp_len(p.context_lens[s], max_len));
       nb = (n + bs - 1) >> p.log2_bs;
     } while (nb == 0);
     off = 0;
