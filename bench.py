@@ -111,6 +111,38 @@ def cpu_baseline(wl: W.Workload, target_s: float = 12.0) -> dict:
                       f"{dt:.1f} s single-threaded fp64"}
 
 
+KERNEL_SOURCES = ("paged_kv_cache_449_amd/csrc/common.h", "paged_kv_cache_449_amd/csrc/decode_kernel.h",
+                  "paged_kv_cache_449_amd/csrc/decode.hip")
+TRAFFIC_FILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles", "decode_traffic.json")
+
+
+def kernel_source_digest() -> str:
+    """sha256 over the decode kernel's sources: counters taken on other
+    sources do not describe this kernel."""
+    import hashlib
+    h = hashlib.sha256()
+    root = os.path.dirname(os.path.abspath(__file__))
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(root, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(wl_name: str):
+    """HBM bytes per decode launch from the committed rocprofv3 counter
+    summary, if it was taken on this workload and on the current kernel
+    sources; else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    entry = rec.get("workloads", {}).get(wl_name)
+    if not entry or rec.get("kernel_source_sha256") != kernel_source_digest():
+        return None
+    return entry.get("traffic_bytes_per_launch")
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -118,6 +150,9 @@ def main(argv=None) -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="run one plain 1 GiB device copy before the timed steps: under rocprofv3 --pmc its "
+                         "FETCH_SIZE/WRITE_SIZE give the counters' scale against bytes known to move")
     ap.add_argument("--placement", choices=["shuffled", "sequential"], default="shuffled",
                     help="shuffled: blocks from a seeded random free list (the workload); sequential: "
                          "the free list in id order, so each sequence's blocks are contiguous (the "
@@ -154,6 +189,14 @@ def main(argv=None) -> int:
         if ev is not None:
             ev[1].record()
 
+    if args.calibrate_copy:
+        # an elementwise kernel that reads 1 GiB and writes 1 GiB (a plain
+        # same-dtype copy may go to a DMA engine, which the counters miss)
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        torch.bitwise_not(src, out=dst)
+        torch.cuda.synchronize(dev)
+        del src, dst
     for _ in range(args.warmup):
         one_step()
     torch.cuda.synchronize(dev)
@@ -196,7 +239,7 @@ def main(argv=None) -> int:
                    "kv_bytes_per_step": nb["kv"], "partition_tokens": pt, "placement": args.placement,
                    "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(wl.name),
                      "kernel": "paged_decode_kernel", "kernel_us": round(float(dec_ms.mean()) * 1e3, 2),
                      "bytes_per_launch": nb["total"]},
     }

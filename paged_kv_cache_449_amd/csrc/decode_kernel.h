@@ -20,9 +20,9 @@
 // (an atomic counter per run) merges them in worker order.
 //
 // Worker ids are assigned so that consecutive ids run on the same XCD (the
-// dispatcher deals work-groups round robin over the 8 XCDs): neighbouring
-// runs -- e.g. candidates sharing a prompt's blocks -- then share that XCD's
-// L2.
+// dispatcher deals work-groups round robin over the 8 XCDs) and every XCD
+// gets an equal share of the workers that have blocks: neighbouring runs --
+// e.g. candidates sharing a prompt's blocks -- then share that XCD's L2.
 //
 // Lane layout.  A token row of head_dim elements is read by L lanes with one
 // 16-byte load each; a wave load covers TPL = 64/L consecutive tokens of one
@@ -394,8 +394,6 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(const DecodeParams p) 
   const int S = p.num_seqs;
   const int bs = 1 << p.log2_bs;
   const int max_len = p.max_blocks << p.log2_bs;
-  const int per_xcd = p.num_workers >> 3;
-  const int w = (int)(blockIdx.x & 7) * per_xcd + (int)(blockIdx.x >> 3);
 
   // blocks per kv head, and whether some sequence is empty
   int total = 0;
@@ -412,7 +410,7 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(const DecodeParams p) 
   }
   total = uniform(total);
 
-  if (w == 0 && __ballot(empty)) {
+  if (blockIdx.x == 0 && __ballot(empty)) {
     // empty contexts attend to nothing: their rows are zero
     constexpr int QE = elem_size<QT>::value;
     const int Hq = p.num_kv_heads * G;
@@ -425,6 +423,13 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(const DecodeParams p) 
 
   const int T = total * p.num_kv_heads;
   const int chunk = p.chunk > 0 ? p.chunk : max(1, (T + p.num_workers - 1) / p.num_workers);
+  // Only the first `active` worker ids have blocks.  They are spread over
+  // all 8 XCDs: work-group b runs on XCD b % 8 and becomes worker
+  // (b % 8) * (active8 / 8) + b / 8, so each XCD holds one contiguous range
+  // of the stream (neighbouring runs share its L2).
+  const int active8 = (((T + chunk - 1) / chunk) + 7) & ~7;   // <= num_workers
+  if ((int)blockIdx.x >= active8) return;
+  const int w = (int)(blockIdx.x & 7) * (active8 >> 3) + (int)(blockIdx.x >> 3);
   const int start = w * chunk;
   if (start >= T) return;
   const int end = min(start + chunk, T);

@@ -45,14 +45,17 @@ def replay(lens, hkv, max_blocks, bs, partition_tokens, **kw):
     written = np.zeros((hkv, S), dtype=np.int32)
     records = {}         # (slot) -> (h, s) written
     counters = np.zeros(COUNTER_SLOTS, dtype=np.int32)
-    per_xcd = W >> 3
+    active8 = ((-(-T // chunk)) + 7) & ~7
+    assert active8 <= W
     seen_workers = set()
     # workers in dispatch order; the merge decision depends only on counts,
     # so any completion order gives the same result -- use a shuffled one
     order = np.random.default_rng(0).permutation(W)
     for bid in order:
-        w = (bid & 7) * per_xcd + (bid >> 3)
-        assert 0 <= w < W and w not in seen_workers
+        if bid >= active8:
+            continue
+        w = (bid & 7) * (active8 >> 3) + (bid >> 3)
+        assert 0 <= w < active8 and w not in seen_workers
         seen_workers.add(w)
         start = w * chunk
         if start >= T:
@@ -103,6 +106,7 @@ def replay(lens, hkv, max_blocks, bs, partition_tokens, **kw):
                 if nb[s] > 0:
                     break
             off = 0
+    assert seen_workers == set(range(active8))
     for h in range(hkv):
         for s in range(S):
             assert (streamed[h, s, :nb[s]] == 1).all() and (streamed[h, s, nb[s]:] == 0).all()
