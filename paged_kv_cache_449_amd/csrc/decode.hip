@@ -19,6 +19,14 @@ int waves_per_cu() {
   return v;
 }
 
+// Query groups (G > 1) run on the matrix cores where the dtype pair has a
+// 16-bit operand type and blocks hold whole 16-token tiles;
+// PAGEDKV_DECODE_MFMA=0 keeps them on the vector ALUs (read at every call).
+bool mfma_allowed() {
+  const char* e = getenv("PAGEDKV_DECODE_MFMA");
+  return !(e && e[0] == '0');
+}
+
 struct Plan {
   int32_t chunk;        // 0 = derived in the kernel
   int32_t num_workers;  // multiple of 8
@@ -111,19 +119,20 @@ extern "C" kv_status_t paged_attention_decode(const kv_pool_t* pool, const void*
   if (64 / lanes_per_row > pool->block_size) return KV_ERR_UNSUPPORTED;
 
   hipStream_t s = (hipStream_t)stream;
+  const bool mfma = G > 1 && mfma_allowed();
   if (!fp8) {
     if (q_dtype != pool->dtype) return KV_ERR_UNSUPPORTED;
     switch (pool->dtype) {
-      case KV_F32: return launch_decode_f32_f32(p, D, G, s);
-      case KV_F16: return launch_decode_f16_f16(p, D, G, s);
-      case KV_BF16: return launch_decode_bf16_bf16(p, D, G, s);
+      case KV_F32: return launch_decode_f32_f32(p, D, G, mfma, s);
+      case KV_F16: return launch_decode_f16_f16(p, D, G, mfma, s);
+      case KV_BF16: return launch_decode_bf16_bf16(p, D, G, mfma, s);
       default: return KV_ERR_UNSUPPORTED;
     }
   }
   switch (q_dtype) {
-    case KV_F32: return launch_decode_fp8_f32(p, D, G, s);
-    case KV_F16: return launch_decode_fp8_f16(p, D, G, s);
-    case KV_BF16: return launch_decode_fp8_bf16(p, D, G, s);
+    case KV_F32: return launch_decode_fp8_f32(p, D, G, mfma, s);
+    case KV_F16: return launch_decode_fp8_f16(p, D, G, mfma, s);
+    case KV_BF16: return launch_decode_fp8_bf16(p, D, G, mfma, s);
     default: return KV_ERR_UNSUPPORTED;
   }
 }

@@ -2,7 +2,7 @@
 #include "decode_kernel.h"
 
 namespace pkv {
-kv_status_t launch_decode_f16_f16(const DecodeParams& p, int D, int G, hipStream_t s) {
-  return launch_decode<f16_t, f16_t>(p, D, G, s);
+kv_status_t launch_decode_f16_f16(const DecodeParams& p, int D, int G, bool mfma, hipStream_t s) {
+  return launch_decode<f16_t, f16_t>(p, D, G, mfma, s);
 }
 }  // namespace pkv

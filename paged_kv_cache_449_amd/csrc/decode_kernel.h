@@ -32,6 +32,8 @@
 // rows are merged once at the end of a run.
 #pragma once
 
+#include <type_traits>
+
 #include "common.h"
 
 namespace pkv {
@@ -226,12 +228,84 @@ __device__ inline float load_coherent(const float* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// One run: blocks [off, off+len) of the (kv head h, sequence s) stream, which
-// has nb blocks and n tokens.  pos is the run's place in the flattened
-// stream and wstart the worker's first block.  All scalars are uniform.
+// ------------------------------------------------------ split-run bookkeeping
+//
+// A run cut between workers leaves one partial record per worker:
+// [G][D + 4] floats holding the unnormalised accumulator acc[g][0..D), the
+// running max (log2 units) at [g][D] and the running sum at [g][D + 1].  A
+// worker has at most two partial runs: the one it starts with (slot 0) and
+// the one it ends with (slot 1).
+
+// Record of this worker for the run that reaches position `pos`.
+template <int D, int G>
+__device__ inline float* partial_record(const DecodeParams& p, int w, int wstart, int pos) {
+  const int k = pos == wstart ? 0 : 1;
+  return p.partials + (int64_t)(2 * w + k) * G * (D + 4);
+}
+
+// Publish-side half of the hand-over: the caller has stored its record with
+// store_coherent (written through to the device coherence point).  Wait for
+// those stores to complete, then count this worker in.  Returns true in the
+// worker that completes the count, which then merges.  Its loads of the
+// records are coherent loads, so no cache-wide writeback or invalidate is
+// needed on either side.
+__device__ inline bool arrive(const DecodeParams& p, int first_w, int last_w) {
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  int done = 0;
+  if (threadIdx.x == 0)
+    done = __hip_atomic_fetch_add(p.counters + first_w, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  done = uniform(__shfl(done, 0));
+  return done == last_w - first_w;
+}
+
+// Merge the records of workers first_w..last_w (in worker order, so results
+// are reproducible) into out rows oe .. oe + G*D (elements), then clear the
+// run's counter for the next call.  seg_start is the run's first position in
+// the flattened stream.  Each lane owns 4 consecutive elements of [G][D] per
+// pass.
+template <typename QT, int D, int G>
+__device__ inline void merge_records(const DecodeParams& p, int first_w, int last_w, int seg_start, int chunk,
+                                     int64_t oe) {
+  constexpr int REC = D + 4;
+  constexpr int QE = elem_size<QT>::value;
+  static_assert(D % 4 == 0, "record layout");
+  for (int e0 = threadIdx.x * 4; e0 < G * D; e0 += 256) {
+    const int g = e0 / D, d = e0 % D;
+    float M = -INFINITY;
+    for (int v = first_w; v <= last_w; ++v) {
+      const float* r = p.partials + (int64_t)(2 * v + (v * chunk >= seg_start ? 0 : 1)) * G * REC + g * REC;
+      M = fmaxf(M, load_coherent(r + D));
+    }
+    const float mu = M == -INFINITY ? 0.0f : M;
+    float lsum = 0.0f, o[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int v = first_w; v <= last_w; ++v) {
+      const float* r = p.partials + (int64_t)(2 * v + (v * chunk >= seg_start ? 0 : 1)) * G * REC + g * REC;
+      const float f = fexp2(load_coherent(r + D) - mu);
+      lsum = fmaf(f, load_coherent(r + D + 1), lsum);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o[i] = fmaf(f, load_coherent(r + d + i), o[i]);
+    }
+    store_row<QT, 4>(p.out + (oe + e0) * QE, o, lsum > 0.0f ? p.v_scale / lsum : 0.0f);
+  }
+  if (threadIdx.x == 0) __hip_atomic_store(p.counters + first_w, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Table window: lane i holds the physical block of logical block wb + i of
+// the run (-1 past the run or for an id outside the pool).
+__device__ inline int load_table_window(const DecodeParams& p, const int32_t* trow, int wb, int len) {
+  const int cnt = min(64, len - wb);
+  int e = -1;
+  if ((int)threadIdx.x < cnt) e = trow[wb + threadIdx.x];
+  return (uint32_t)e < (uint32_t)p.num_blocks ? e : -1;
+}
+
+// One run on the vector ALUs: blocks [off, off+len) of the (kv head h,
+// sequence s) stream, which has nb blocks and n tokens.  pos is the run's
+// place in the flattened stream and wstart the worker's first block.  All
+// scalars are uniform.
 template <typename KV, typename QT, int D, int G>
-__device__ inline void decode_run(const DecodeParams& p, int w, int chunk, int wstart, int pos, int s, int h,
-                                  int off, int len, int n, int nb) {
+__device__ inline void valu_run(const DecodeParams& p, int w, int chunk, int wstart, int pos, int s, int h,
+                                int off, int len, int n, int nb) {
   using Sh = DecodeShape<KV, D>;
   constexpr int VEC = Sh::VEC, L = Sh::L, TPL = Sh::TPL, REC = Sh::REC;
   constexpr int U = kLoadsPerStep;
@@ -274,18 +348,11 @@ __device__ inline void decode_run(const DecodeParams& p, int w, int chunk, int w
   c.bs_mask = (1 << p.log2_bs) - 1;
   const int32_t* trow = p.block_tables + (int64_t)s * p.max_blocks + off;
 
-  auto load_tab = [&](int wb) {
-    const int cnt = min(64, len - wb);
-    int e = -1;
-    if (lane < cnt) e = trow[wb + lane];
-    return (uint32_t)e < (uint32_t)p.num_blocks ? e : -1;
-  };
-
-  int tab = load_tab(0);
+  int tab = load_table_window(p, trow, 0, len);
   for (int wb = 0; wb < len; wb += 64) {
     const int cnt = min(64, len - wb);
     // the next window's table entries load while this window streams
-    const int tab_next = wb + 64 < len ? load_tab(wb + 64) : -1;
+    const int tab_next = wb + 64 < len ? load_table_window(p, trow, wb + 64, len) : -1;
     const int tlo = (off + wb) << p.log2_bs;
     const int thi = min((off + wb + cnt) << p.log2_bs, n);
     const int steps = (thi - tlo + U * TPL - 1) / (U * TPL);
@@ -327,13 +394,9 @@ __device__ inline void decode_run(const DecodeParams& p, int w, int chunk, int w
     return;
   }
 
-  // Partial: publish (acc, m, l) with stores that write through to the
-  // device coherence point, wait for them to complete, then count this
-  // worker in; the worker that completes the count merges.  Its loads of the
-  // records are coherent loads, so no cache-wide writeback or invalidate is
-  // needed on either side.
-  const int k = pos == wstart ? 0 : 1;
-  float* rec = p.partials + (int64_t)(2 * w + k) * G * REC;
+  // Partial: publish (acc, m, l) through the device coherence point; the
+  // worker that completes the run's count merges.
+  float* rec = partial_record<D, G>(p, w, wstart, pos);
   if (row == 0) {
 #pragma unroll
     for (int g = 0; g < G; ++g) {
@@ -345,50 +408,22 @@ __device__ inline void decode_run(const DecodeParams& p, int w, int chunk, int w
       }
     }
   }
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   const int seg_start = pos - off;
   const int first_w = seg_start / chunk;
   const int last_w = (seg_start + nb - 1) / chunk;
-  int done = 0;
-  if (lane == 0) done = __hip_atomic_fetch_add(p.counters + first_w, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  done = uniform(__shfl(done, 0));
-  if (done != last_w - first_w) return;
-
-  float M[G];
-#pragma unroll
-  for (int g = 0; g < G; ++g) M[g] = -INFINITY;
-  for (int v = first_w; v <= last_w; ++v) {
-    const float* r = p.partials + (int64_t)(2 * v + (v * chunk >= seg_start ? 0 : 1)) * G * REC;
-#pragma unroll
-    for (int g = 0; g < G; ++g) M[g] = fmaxf(M[g], load_coherent(r + g * REC + D));
-  }
-  float lsum[G], o[G][VEC];
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    lsum[g] = 0.0f;
-#pragma unroll
-    for (int i = 0; i < VEC; ++i) o[g][i] = 0.0f;
-  }
-  for (int v = first_w; v <= last_w; ++v) {
-    const float* r = p.partials + (int64_t)(2 * v + (v * chunk >= seg_start ? 0 : 1)) * G * REC;
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      const float mu = M[g] == -INFINITY ? 0.0f : M[g];
-      const float f = fexp2(load_coherent(r + g * REC + D) - mu);
-      lsum[g] = fmaf(f, load_coherent(r + g * REC + D + 1), lsum[g]);
-#pragma unroll
-      for (int i = 0; i < VEC; ++i) o[g][i] = fmaf(f, load_coherent(r + g * REC + col * VEC + i), o[g][i]);
-    }
-  }
-  if (row == 0) {
-#pragma unroll
-    for (int g = 0; g < G; ++g)
-      store_row<QT, VEC>(p.out + (oe + (int64_t)g * D) * QE, o[g], lsum[g] > 0.0f ? p.v_scale / lsum[g] : 0.0f);
-  }
-  if (lane == 0) __hip_atomic_store(p.counters + first_w, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (arrive(p, first_w, last_w))
+    merge_records<QT, D, G>(p, first_w, last_w, seg_start, chunk, ((int64_t)s * Hq + (int64_t)h * G) * D);
 }
 
-template <typename KV, typename QT, int D, int G>
+}  // namespace pkv
+
+#include "decode_mfma.h"
+
+namespace pkv {
+
+// One worker wavefront per work-group.  MFMA selects the matrix-core run
+// (query groups with a 16-bit operand type) over the vector-ALU run.
+template <typename KV, typename QT, int D, int G, bool MFMA>
 __global__ __launch_bounds__(64) void paged_decode_kernel(const DecodeParams p) {
   const int lane = threadIdx.x;
   const int S = p.num_seqs;
@@ -467,7 +502,10 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(const DecodeParams p) 
   int nb = (n + bs - 1) >> p.log2_bs;
   while (true) {
     const int len = min(nb - off, end - pos);
-    decode_run<KV, QT, D, G>(p, w, chunk, start, pos, s, h, off, len, n, nb);
+    if constexpr (MFMA)
+      mfma_run<KV, QT, D, G>(p, w, chunk, start, pos, s, h, off, len, n, nb);
+    else
+      valu_run<KV, QT, D, G>(p, w, chunk, start, pos, s, h, off, len, n, nb);
     pos += len;
     if (pos >= end) break;
     do {
@@ -483,12 +521,24 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(const DecodeParams p) 
 }
 
 // Launch one instantiation; defined per KV/Q dtype pair in decode_*.hip.
+// use_mfma asks for the matrix-core run; it is honoured where the dtype pair
+// has an operand type and blocks hold whole 16-token tiles.
 template <typename KV, typename QT>
-kv_status_t launch_decode(const DecodeParams& p, int D, int G, hipStream_t stream) {
-#define PKV_CASE(DD, GG)                                                                                     \
-  if (D == DD && G == GG) {                                                                                  \
-    hipLaunchKernelGGL((paged_decode_kernel<KV, QT, DD, GG>), dim3(p.num_workers), dim3(64), 0, stream, p); \
-    return launch_status();                                                                                  \
+kv_status_t launch_decode(const DecodeParams& p, int D, int G, bool use_mfma, hipStream_t stream) {
+  constexpr bool kHasMfma = !std::is_void<typename mfma_operand<KV, QT>::type>::value;
+  const bool mfma = kHasMfma && use_mfma && p.log2_bs >= 4;
+#define PKV_CASE(DD, GG)                                                                                   \
+  if (D == DD && G == GG) {                                                                                \
+    if constexpr (kHasMfma && GG > 1) {                                                                    \
+      if (mfma) {                                                                                          \
+        hipLaunchKernelGGL((paged_decode_kernel<KV, QT, DD, GG, true>), dim3(p.num_workers), dim3(64), 0, \
+                           stream, p);                                                                     \
+        return launch_status();                                                                            \
+      }                                                                                                    \
+    }                                                                                                      \
+    hipLaunchKernelGGL((paged_decode_kernel<KV, QT, DD, GG, false>), dim3(p.num_workers), dim3(64), 0,    \
+                       stream, p);                                                                         \
+    return launch_status();                                                                                \
   }
 #define PKV_CASES(DD) PKV_CASE(DD, 1) PKV_CASE(DD, 2) PKV_CASE(DD, 4) PKV_CASE(DD, 8)
   PKV_CASES(64)
@@ -499,11 +549,11 @@ kv_status_t launch_decode(const DecodeParams& p, int D, int G, hipStream_t strea
   return KV_ERR_UNSUPPORTED;
 }
 
-kv_status_t launch_decode_f32_f32(const DecodeParams& p, int D, int G, hipStream_t s);
-kv_status_t launch_decode_f16_f16(const DecodeParams& p, int D, int G, hipStream_t s);
-kv_status_t launch_decode_bf16_bf16(const DecodeParams& p, int D, int G, hipStream_t s);
-kv_status_t launch_decode_fp8_f32(const DecodeParams& p, int D, int G, hipStream_t s);
-kv_status_t launch_decode_fp8_f16(const DecodeParams& p, int D, int G, hipStream_t s);
-kv_status_t launch_decode_fp8_bf16(const DecodeParams& p, int D, int G, hipStream_t s);
+kv_status_t launch_decode_f32_f32(const DecodeParams& p, int D, int G, bool mfma, hipStream_t s);
+kv_status_t launch_decode_f16_f16(const DecodeParams& p, int D, int G, bool mfma, hipStream_t s);
+kv_status_t launch_decode_bf16_bf16(const DecodeParams& p, int D, int G, bool mfma, hipStream_t s);
+kv_status_t launch_decode_fp8_f32(const DecodeParams& p, int D, int G, bool mfma, hipStream_t s);
+kv_status_t launch_decode_fp8_f16(const DecodeParams& p, int D, int G, bool mfma, hipStream_t s);
+kv_status_t launch_decode_fp8_bf16(const DecodeParams& p, int D, int G, bool mfma, hipStream_t s);
 
 }  // namespace pkv

@@ -1,0 +1,318 @@
+// Paged decode attention on the matrix cores, for query groups (several query
+// heads per kv head).
+//
+// With G query heads per kv head, each K/V tile read through the block table
+// serves G queries, so QK^T and PV are small dense contractions:
+//   S[t][g] = sum_d K[t][d] q[g][d]          (16 tokens x G heads per tile)
+//   O[g][d] += sum_t P[t][g] V[t][d]
+// The tile is 16 tokens of one block (block_size >= 16) of one kv head.
+//
+//   QK  v_mfma_f32_16x16x32_{bf16,f16}: A = K rows (row i = token), B = q
+//       (column j = head, zero for j >= G), D/32 steps over head_dim.  Lane
+//       (kg = lane/16, t = lane%16) streams the contiguous quarter
+//       [kg*D/4, (kg+1)*D/4) of token t's row; q is laid out with the same
+//       (kg, element) -> dim mapping, so the contraction pairs matching dims
+//       whatever order the instruction walks its k index in.
+//   PV  v_mfma_f32_16x16x16_{bf16,f16}: A = V^T (row i = dim within a
+//       16-column slice, k = token), B = P (k = token, column j = head).  The
+//       QK result leaves lane (kg, j) holding S[4kg + r][j], r = 0..3, which
+//       is exactly that lane's B operand (P[4kg + e][j]), so P never moves
+//       between lanes.  V^T comes from the tile staged in LDS (rows padded
+//       so the four row groups of a read fall in different banks).
+//
+// fp8 pools are widened exactly to the operand type (E4M3FN is a subset of
+// both bf16 and f16).  P is rounded to the operand type; the running sum adds
+// the rounded values, so numerator and denominator use the same weights.
+// The online softmax keeps one running max per head (lanes j, j+16, j+32,
+// j+48 agree on it) and per-lane partial sums that are added at the end.
+#pragma once
+
+namespace pkv {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+
+// Operand type of the matrix instructions for a (KV, query) dtype pair; void
+// where the pair runs on the vector ALUs instead.
+template <typename KV, typename QT> struct mfma_operand { using type = void; };
+template <> struct mfma_operand<bf16_t, bf16_t> { using type = bf16_t; };
+template <> struct mfma_operand<f16_t, f16_t> { using type = f16_t; };
+template <> struct mfma_operand<fp8_t, bf16_t> { using type = bf16_t; };
+template <> struct mfma_operand<fp8_t, f16_t> { using type = f16_t; };
+
+template <typename MT> struct mfma_ops;
+template <> struct mfma_ops<bf16_t> {
+  // two fp8 codes (bytes 0,1 or 2,3 of w) -> two bf16, exact
+  template <bool HI>
+  __device__ static inline uint32_t from_fp8(uint32_t w) {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
+  }
+  // two fp32 -> two bf16, round to nearest even
+  __device__ static inline uint32_t pack(float a, float b) {
+    bf16x2v v;
+    v.x = (__bf16)a;
+    v.y = (__bf16)b;
+    return __builtin_bit_cast(uint32_t, v);
+  }
+  __device__ static inline float lo(uint32_t w) { return __uint_as_float(w << 16); }
+  __device__ static inline float hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+  __device__ static inline f32x4 qk(uint4 a, uint4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
+                                                   0, 0, 0);
+  }
+  __device__ static inline f32x4 pv(uint2 a, uint2 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a), __builtin_bit_cast(s16x4, b), c,
+                                                     0, 0, 0);
+  }
+};
+template <> struct mfma_ops<f16_t> {
+  template <bool HI>
+  __device__ static inline uint32_t from_fp8(uint32_t w) {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, HI));
+  }
+  __device__ static inline uint32_t pack(float a, float b) {
+    half2v v;
+    v.x = (_Float16)a;
+    v.y = (_Float16)b;
+    return __builtin_bit_cast(uint32_t, v);
+  }
+  __device__ static inline float lo(uint32_t w) { return (float)__builtin_bit_cast(half2v, w).x; }
+  __device__ static inline float hi(uint32_t w) { return (float)__builtin_bit_cast(half2v, w).y; }
+  __device__ static inline f32x4 qk(uint4 a, uint4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0,
+                                                  0, 0);
+  }
+  __device__ static inline f32x4 pv(uint2 a, uint2 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, a), __builtin_bit_cast(f16x4, b), c, 0,
+                                                 0, 0);
+  }
+};
+
+template <typename KV, int D>
+struct MfmaShape {
+  static constexpr int EB = elem_size<KV>::value;
+  static constexpr int ROW = D * EB;             // bytes of one token row
+  static constexpr int KL = ROW / 64;            // 16-byte loads per lane: a quarter row
+  static constexpr int VL = 16 * ROW / 1024;     // wave loads of one 16-token V tile
+  static constexpr int KS = D / 32;              // QK instructions per tile
+  static constexpr int DT = D / 16;              // PV instructions per tile (16 dims each)
+  static constexpr int LSTRIDE = 2 * D + 16;     // LDS bytes per staged V row (operand type)
+  static_assert(KL >= 1 && VL >= 1 && KS >= 1, "tile shape");
+};
+
+template <typename KV, int D>
+struct MfmaTileRegs {
+  uint4 k[MfmaShape<KV, D>::KL];
+  uint4 v[MfmaShape<KV, D>::VL];
+};
+
+// Issue the loads of 16-token tile j of the current table window (tokens
+// tlo + 16j ...).  Tokens at or past thi and blocks whose table entry is out
+// of range read as zeros.
+template <typename KV, int D>
+__device__ inline void mfma_issue(const RunCtx& c, int tab, int tlo, int thi, int j, MfmaTileRegs<KV, D>& r) {
+  using Sh = MfmaShape<KV, D>;
+  const int lane = threadIdx.x;
+  const int bi = (j * 16) >> c.log2_bs;
+  const int phys = __builtin_amdgcn_readlane(tab, bi);
+  const bool pvalid = phys >= 0;
+  const int64_t boff = pvalid ? c.blk_stride * phys : 0;
+  const uint32_t nrec = pvalid ? c.tile_bytes : 0u;
+  __amdgpu_buffer_rsrc_t rk =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(c.k_head + boff), (short)0, (int)nrec, kBufferWord3);
+  __amdgpu_buffer_rsrc_t rv =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(c.v_head + boff), (short)0, (int)nrec, kBufferWord3);
+  const int t0 = tlo + j * 16;             // first token of the tile
+  const int o0 = (j * 16) & c.bs_mask;     // its slot in the block
+  // K: lane (kg, t) reads the quarter row kg of token t
+  const int t = lane & 15, kg = lane >> 4;
+  const uint32_t kb = t0 + t < thi ? (uint32_t)((o0 + t) * Sh::ROW + kg * (Sh::ROW / 4)) : kMaskedOffset;
+#pragma unroll
+  for (int q = 0; q < Sh::KL; ++q)
+    r.k[q] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, kb + q * 16, 0, 0));
+  // V: the 16 x ROW tile, contiguous, 16 bytes per lane per wave load
+#pragma unroll
+  for (int u = 0; u < Sh::VL; ++u) {
+    const int byte = (u * 64 + lane) * 16;
+    const int vr = byte / Sh::ROW, vc = byte % Sh::ROW;
+    const uint32_t vo = t0 + vr < thi ? (uint32_t)((o0 + vr) * Sh::ROW + vc) : kMaskedOffset;
+    r.v[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rv, vo, 0, 0));
+  }
+}
+
+// K operand words of QK step st (8 elements of the operand type) from the
+// lane's quarter row.
+template <typename KV, typename MT, int D>
+__device__ inline uint4 mfma_k_operand(const MfmaTileRegs<KV, D>& r, int st) {
+  if constexpr (elem_size<KV>::value == 2) {
+    return r.k[st];
+  } else {
+    // fp8: step st uses bytes 8st .. 8st+7 of the quarter row
+    const uint4 w = r.k[st >> 1];
+    const uint32_t a = (st & 1) ? w.z : w.x;
+    const uint32_t b = (st & 1) ? w.w : w.y;
+    return make_uint4(mfma_ops<MT>::template from_fp8<false>(a), mfma_ops<MT>::template from_fp8<true>(a),
+                      mfma_ops<MT>::template from_fp8<false>(b), mfma_ops<MT>::template from_fp8<true>(b));
+  }
+}
+
+template <typename KV, typename QT, int D, int G>
+__device__ inline void mfma_run(const DecodeParams& p, int w, int chunk, int wstart, int pos, int s, int h, int off,
+                                int len, int n, int nb) {
+  using MT = typename mfma_operand<KV, QT>::type;
+  using Ops = mfma_ops<MT>;
+  using Sh = MfmaShape<KV, D>;
+  static_assert(G >= 1 && G <= 16, "query group");
+  constexpr int KS = Sh::KS, DT = Sh::DT, LSTRIDE = Sh::LSTRIDE;
+  constexpr int QE = elem_size<QT>::value;
+  __shared__ __attribute__((aligned(16))) uint8_t vlds[16 * LSTRIDE];
+
+  const int lane = threadIdx.x;
+  const int j16 = lane & 15;   // token row (QK A) / head column (B, D)
+  const int kg = lane >> 4;    // k group
+  const int Hq = p.num_kv_heads * G;
+
+  // q operand: lane (kg, j) holds q[j][kg*D/4 + 8st .. +8] for step st
+  uint4 qop[KS];
+  {
+    const int64_t qe = ((int64_t)s * Hq + (int64_t)h * G + j16) * D + kg * (D / 4);
+#pragma unroll
+    for (int st = 0; st < KS; ++st) qop[st] = make_uint4(0u, 0u, 0u, 0u);
+    if (j16 < G) {
+#pragma unroll
+      for (int st = 0; st < KS; ++st) qop[st] = *(const uint4*)(p.q + (qe + st * 8) * QE);
+    }
+  }
+
+  f32x4 acc[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  float m = -INFINITY;   // running max of head j16 (log2 units)
+  float l = 0.0f;        // this lane's share of the running sum
+
+  RunCtx c;
+  const int64_t tile = (int64_t)Sh::ROW << p.log2_bs;
+  c.k_head = p.k_pool + tile * h;
+  c.v_head = p.v_pool + tile * h;
+  c.blk_stride = tile * p.num_kv_heads;
+  c.tile_bytes = (uint32_t)tile;
+  c.lane_off = 0;
+  c.row_bytes = Sh::ROW;
+  c.log2_bs = p.log2_bs;
+  c.bs_mask = (1 << p.log2_bs) - 1;
+  const int32_t* trow = p.block_tables + (int64_t)s * p.max_blocks + off;
+
+  auto compute = [&](const MfmaTileRegs<KV, D>& r, int tab, int tlo, int thi, int j) {
+    // S^T tile: lane (kg, j16) gets scores of tokens 4kg + i, i = 0..3, head j16
+    f32x4 sc = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int st = 0; st < KS; ++st) sc = Ops::qk(mfma_k_operand<KV, MT, D>(r, st), qop[st], sc);
+    const int bi = (j * 16) >> p.log2_bs;
+    const bool bvalid = __builtin_amdgcn_readlane(tab, bi) >= 0;
+    const int t0 = tlo + j * 16 + 4 * kg;
+    float x[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) x[i] = (j16 < G && bvalid && t0 + i < thi) ? sc[i] * p.q_scale : -INFINITY;
+    float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float mn = fmaxf(m, mx);
+    const float mu = mn == -INFINITY ? 0.0f : mn;
+    const float alpha = fexp2(m - mu);
+    m = mn;
+    const uint32_t p01 = Ops::pack(fexp2(x[0] - mu), fexp2(x[1] - mu));
+    const uint32_t p23 = Ops::pack(fexp2(x[2] - mu), fexp2(x[3] - mu));
+    l = l * alpha + ((Ops::lo(p01) + Ops::hi(p01)) + (Ops::lo(p23) + Ops::hi(p23)));
+    if (__ballot(alpha != 1.0f)) {
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) acc[dt] *= alpha;
+    }
+    // stage V in LDS as the operand type, rows padded to LSTRIDE bytes
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < Sh::VL; ++u) {
+      const int byte = (u * 64 + lane) * 16;
+      const int vr = byte / Sh::ROW, ve = (byte % Sh::ROW) / Sh::EB;   // row, first element
+      uint8_t* dst = vlds + vr * LSTRIDE + ve * 2;
+      if constexpr (Sh::EB == 2) {
+        *(uint4*)dst = r.v[u];
+      } else {
+        const uint4 w4 = r.v[u];
+        *(uint4*)dst = make_uint4(Ops::template from_fp8<false>(w4.x), Ops::template from_fp8<true>(w4.x),
+                                  Ops::template from_fp8<false>(w4.y), Ops::template from_fp8<true>(w4.y));
+        *(uint4*)(dst + 16) = make_uint4(Ops::template from_fp8<false>(w4.z), Ops::template from_fp8<true>(w4.z),
+                                         Ops::template from_fp8<false>(w4.w), Ops::template from_fp8<true>(w4.w));
+      }
+    }
+    __syncthreads();
+    const uint2 pop = make_uint2(p01, p23);
+    const uint16_t* l16 = (const uint16_t*)vlds;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      // lane (kg, i) needs V[4kg + e][16 dt + i], e = 0..3
+      const int base = (4 * kg) * (LSTRIDE / 2) + dt * 16 + j16;
+      const uint32_t a0 = (uint32_t)l16[base] | ((uint32_t)l16[base + LSTRIDE / 2] << 16);
+      const uint32_t a1 = (uint32_t)l16[base + LSTRIDE] | ((uint32_t)l16[base + 3 * (LSTRIDE / 2)] << 16);
+      acc[dt] = Ops::pv(make_uint2(a0, a1), pop, acc[dt]);
+    }
+  };
+
+  int tab = load_table_window(p, trow, 0, len);
+  for (int wb = 0; wb < len; wb += 64) {
+    const int cnt = min(64, len - wb);
+    const int tab_next = wb + 64 < len ? load_table_window(p, trow, wb + 64, len) : -1;
+    const int tlo = (off + wb) << p.log2_bs;
+    const int thi = min((off + wb + cnt) << p.log2_bs, n);
+    const int tiles = (thi - tlo + 15) >> 4;
+    MfmaTileRegs<KV, D> a, b;
+    mfma_issue<KV, D>(c, tab, tlo, thi, 0, a);
+    for (int j = 0; j < tiles; j += 2) {
+      if (j + 1 < tiles) mfma_issue<KV, D>(c, tab, tlo, thi, j + 1, b);
+      compute(a, tab, tlo, thi, j);
+      if (j + 2 < tiles) mfma_issue<KV, D>(c, tab, tlo, thi, j + 2, a);
+      if (j + 1 < tiles) compute(b, tab, tlo, thi, j + 1);
+    }
+    tab = tab_next;
+  }
+
+  // total sum of head j16 over the four k groups
+  l += __shfl_xor(l, 16);
+  l += __shfl_xor(l, 32);
+
+  // lane (kg, j16) holds O[j16][16 dt + 4kg + i], i = 0..3
+  const int64_t orow = ((int64_t)s * Hq + (int64_t)h * G) * D;
+  if (off == 0 && off + len == nb) {   // the whole run is ours
+    if (j16 < G) {
+      const float mul = l > 0.0f ? p.v_scale / l : 0.0f;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const float v4[4] = {acc[dt][0], acc[dt][1], acc[dt][2], acc[dt][3]};
+        store_row<QT, 4>(p.out + (orow + (int64_t)j16 * D + dt * 16 + 4 * kg) * QE, v4, mul);
+      }
+    }
+    return;
+  }
+
+  float* rec = partial_record<D, G>(p, w, wstart, pos);
+  if (j16 < G) {
+    float* rg = rec + j16 * (D + 4);
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) store_coherent(rg + dt * 16 + 4 * kg + i, acc[dt][i]);
+    if (kg == 0) {
+      store_coherent(rg + D, m);
+      store_coherent(rg + D + 1, l);
+    }
+  }
+  const int seg_start = pos - off;
+  const int first_w = seg_start / chunk;
+  const int last_w = (seg_start + nb - 1) / chunk;
+  if (arrive(p, first_w, last_w)) merge_records<QT, D, G>(p, first_w, last_w, seg_start, chunk, orow);
+}
+
+}  // namespace pkv

@@ -49,6 +49,30 @@ def test_fp8_codes_decode_exactly(pk):
     np.testing.assert_array_equal(out[0][ok], want[ok])
 
 
+@pytest.mark.parametrize("qdt", [torch.bfloat16, torch.float16])
+def test_fp8_codes_decode_exactly_on_matrix_cores(pk, qdt):
+    """The same exhaustive check with a query group of 2 (matrix-core path,
+    where codes are widened to the 16-bit operand type): one-token context,
+    so p = 1 and out = decode(code) * v_scale, exactly representable."""
+    from gpu_harness import announce
+    announce(f"fp8 codes, query group, q {qdt}")
+    dev = _dev()
+    pool = pk.KVPool(4, 16, 1, 128, torch.float8_e4m3fn, dev, 1.0, 0.5)
+    pool.k_cache.view(torch.uint8).zero_()
+    codes = torch.arange(256, dtype=torch.int32).to(torch.uint8).reshape(2, 128)
+    for half in range(2):
+        pool.v_cache.view(torch.uint8)[2, 0, 0, :] = codes[half].to(dev)
+        q = torch.randn(1, 2, 128, device=dev).to(qdt)
+        bt = torch.tensor([[2]], dtype=torch.int32, device=dev)
+        cl = torch.tensor([1], dtype=torch.int32, device=dev)
+        out = pk.paged_attention_decode(pool, q, bt, cl, 0.1).cpu().double().numpy()
+        want = np.array([oracle.e4m3_to_f64(c) * 0.5 for c in range(128 * half, 128 * half + 128)])
+        for g in range(2):
+            np.testing.assert_array_equal(np.isnan(out[0, g]), np.isnan(want))
+            ok = ~np.isnan(want)    # every finite code * 0.5 is exact in bf16 and f16
+            np.testing.assert_array_equal(out[0, g][ok], want[ok])
+
+
 def test_fp8_scale_applies_to_values(pk):
     dev = _dev()
     pool = pk.KVPool(2, 16, 1, 128, torch.float8_e4m3fn, dev, 0.5, 0.25)

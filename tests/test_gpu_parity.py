@@ -89,3 +89,14 @@ def test_identical_candidates_agree(gpu):
         c = [s for s, q in enumerate(wl.parent) if q == p]
         for s in c[1:]:
             check_close(got["out"][s], got["out"][c[0]].astype(np.float64), wl.kv_dtype)
+
+
+@pytest.mark.parametrize("path", ["valu", "mfma"])
+@pytest.mark.parametrize("name", ["c5s_fp8", "c5s_bf16"])
+@pytest.mark.parametrize("pt", [0, 16, 512])
+def test_query_group_paths(gpu, name, path, pt, monkeypatch):
+    """Query groups run on the matrix cores by default; PAGEDKV_DECODE_MFMA=0
+    keeps them on the vector ALUs.  Both agree with the oracle at every split."""
+    monkeypatch.setenv("PAGEDKV_DECODE_MFMA", "1" if path == "mfma" else "0")
+    wl = W.small_configs()[name]
+    check_close(gpu(wl, partition_tokens=pt)["out"], OracleRun(wl).decode(), wl.kv_dtype)
