@@ -130,6 +130,10 @@ __device__ inline float softmax_step(float& m, float& l, const float* sc, float*
 constexpr int kBufferWord3 = 0x00020000;
 // Lane offset that lies outside every tile: the load returns zeros.
 constexpr uint32_t kMaskedOffset = 0x80000000u;
+// Cache policy of the K/V stream loads: non-temporal (each byte is used once
+// per launch).  On MI355X this lifts a random-4-KiB-tile read stream from
+// about 6.1 to about 6.8 TB/s.
+constexpr int kStreamPolicy = 2;
 
 __device__ inline int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
@@ -163,17 +167,17 @@ __device__ inline void issue_step(const RunCtx& c, int tab, int tlo, int thi, in
     const int j = step * U + u;                    // wave load index in the window
     const int bi = min((j * TPL) >> c.log2_bs, 63);
     const int phys = __builtin_amdgcn_readlane(tab, bi);
-    const bool pvalid = phys >= 0;
-    const int64_t boff = pvalid ? c.blk_stride * phys : 0;
-    const uint32_t nrec = pvalid ? c.tile_bytes : 0u;
+    // an invalid entry (-1) gives an empty descriptor at the head's base
+    const int64_t boff = c.blk_stride * max(phys, 0);
+    const uint32_t nrec = c.tile_bytes & (uint32_t)~(phys >> 31);
     __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void*)(c.k_head + boff), (short)0, (int)nrec,
                                                                   kBufferWord3);
     __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void*)(c.v_head + boff), (short)0, (int)nrec,
                                                                   kBufferWord3);
     const int t = tlo + j * TPL + row;
     const uint32_t off = t < thi ? (uint32_t)((t & c.bs_mask) * c.row_bytes) + c.lane_off : kMaskedOffset;
-    r.k[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0));
-    r.v[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, 0));
+    r.k[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, kStreamPolicy));
+    r.v[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, kStreamPolicy));
   }
 }
 
@@ -356,13 +360,16 @@ __device__ inline void valu_run(const DecodeParams& p, int w, int chunk, int wst
     const int tlo = (off + wb) << p.log2_bs;
     const int thi = min((off + wb + cnt) << p.log2_bs, n);
     const int steps = (thi - tlo + U * TPL - 1) / (U * TPL);
+    // Two register sets in flight.  Issues are unconditional so the wait
+    // counts stay exact: a step past the window reads zeros (its offsets lie
+    // outside the tile) and computes nothing (every score is masked).
     StepRegs<U> a, b;
     issue_step<U, TPL>(c, tab, tlo, thi, 0, row, a);
     for (int st = 0; st < steps; st += 2) {
-      if (st + 1 < steps) issue_step<U, TPL>(c, tab, tlo, thi, st + 1, row, b);
+      issue_step<U, TPL>(c, tab, tlo, thi, st + 1, row, b);
       compute_step<KV, VEC, L, TPL, G, U>(a, qv, m, l, acc, tab, tlo, thi, st, row, p.log2_bs);
-      if (st + 2 < steps) issue_step<U, TPL>(c, tab, tlo, thi, st + 2, row, a);
-      if (st + 1 < steps) compute_step<KV, VEC, L, TPL, G, U>(b, qv, m, l, acc, tab, tlo, thi, st + 1, row, p.log2_bs);
+      issue_step<U, TPL>(c, tab, tlo, thi, st + 2, row, a);
+      compute_step<KV, VEC, L, TPL, G, U>(b, qv, m, l, acc, tab, tlo, thi, st + 1, row, p.log2_bs);
     }
     tab = tab_next;
   }

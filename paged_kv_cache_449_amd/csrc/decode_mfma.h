@@ -117,18 +117,21 @@ template <typename KV, int D>
 __device__ inline void mfma_issue(const RunCtx& c, int tab, int tlo, int thi, int j, MfmaTileRegs<KV, D>& r) {
   using Sh = MfmaShape<KV, D>;
   const int lane = threadIdx.x;
-  const int bi = (j * 16) >> c.log2_bs;
+  const int bi = min((j * 16) >> c.log2_bs, 63);
   const int phys = __builtin_amdgcn_readlane(tab, bi);
-  const bool pvalid = phys >= 0;
-  const int64_t boff = pvalid ? c.blk_stride * phys : 0;
-  const uint32_t nrec = pvalid ? c.tile_bytes : 0u;
+  // an invalid entry (-1) gives an empty descriptor at the head's base
+  const int64_t boff = c.blk_stride * max(phys, 0);
+  const uint32_t nrec = c.tile_bytes & (uint32_t)~(phys >> 31);
   __amdgpu_buffer_rsrc_t rk =
       __builtin_amdgcn_make_buffer_rsrc((void*)(c.k_head + boff), (short)0, (int)nrec, kBufferWord3);
   __amdgpu_buffer_rsrc_t rv =
       __builtin_amdgcn_make_buffer_rsrc((void*)(c.v_head + boff), (short)0, (int)nrec, kBufferWord3);
   const int t0 = tlo + j * 16;             // first token of the tile
   const int o0 = (j * 16) & c.bs_mask;     // its slot in the block
-  // K: lane (kg, t) reads the quarter row kg of token t
+  // K: lane (kg, t) reads the quarter row kg of token t.  One instruction
+  // covers half of each 128-byte line it touches, so these loads keep the
+  // default cache policy (a non-temporal line can be gone before the second
+  // half is read); the contiguous V tile streams non-temporally.
   const int t = lane & 15, kg = lane >> 4;
   const uint32_t kb = t0 + t < thi ? (uint32_t)((o0 + t) * Sh::ROW + kg * (Sh::ROW / 4)) : kMaskedOffset;
 #pragma unroll
@@ -140,7 +143,7 @@ __device__ inline void mfma_issue(const RunCtx& c, int tab, int tlo, int thi, in
     const int byte = (u * 64 + lane) * 16;
     const int vr = byte / Sh::ROW, vc = byte % Sh::ROW;
     const uint32_t vo = t0 + vr < thi ? (uint32_t)((o0 + vr) * Sh::ROW + vc) : kMaskedOffset;
-    r.v[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rv, vo, 0, 0));
+    r.v[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rv, vo, 0, kStreamPolicy));
   }
 }
 
@@ -211,7 +214,7 @@ __device__ inline void mfma_run(const DecodeParams& p, int w, int chunk, int wst
     f32x4 sc = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int st = 0; st < KS; ++st) sc = Ops::qk(mfma_k_operand<KV, MT, D>(r, st), qop[st], sc);
-    const int bi = (j * 16) >> p.log2_bs;
+    const int bi = min((j * 16) >> p.log2_bs, 63);
     const bool bvalid = __builtin_amdgcn_readlane(tab, bi) >= 0;
     const int t0 = tlo + j * 16 + 4 * kg;
     float x[4];
@@ -268,13 +271,15 @@ __device__ inline void mfma_run(const DecodeParams& p, int w, int chunk, int wst
     const int tlo = (off + wb) << p.log2_bs;
     const int thi = min((off + wb + cnt) << p.log2_bs, n);
     const int tiles = (thi - tlo + 15) >> 4;
+    // Two tiles in flight; unconditional issues keep the wait counts exact
+    // (a tile past the window reads zeros and its scores are all masked).
     MfmaTileRegs<KV, D> a, b;
     mfma_issue<KV, D>(c, tab, tlo, thi, 0, a);
     for (int j = 0; j < tiles; j += 2) {
-      if (j + 1 < tiles) mfma_issue<KV, D>(c, tab, tlo, thi, j + 1, b);
+      mfma_issue<KV, D>(c, tab, tlo, thi, j + 1, b);
       compute(a, tab, tlo, thi, j);
-      if (j + 2 < tiles) mfma_issue<KV, D>(c, tab, tlo, thi, j + 2, a);
-      if (j + 1 < tiles) compute(b, tab, tlo, thi, j + 1);
+      mfma_issue<KV, D>(c, tab, tlo, thi, j + 2, a);
+      compute(b, tab, tlo, thi, j + 1);
     }
     tab = tab_next;
   }
