@@ -106,9 +106,14 @@ struct CopyParams {
 };
 
 constexpr int kCopyUnroll = 4;  // 16-byte pieces in flight per lane
+constexpr int kBufWord3 = 0x00020000;
+constexpr int kNonTemporal = 2;  // cache policy: each byte is moved once
+typedef unsigned u32x4 __attribute__((__vector_size__(16)));
 
 // grid.x = num_pairs * 2 * parts: each work-group copies a contiguous share of
-// one block of one pool.
+// one block of one pool.  Buffer descriptors bound both sides to the share,
+// so the tail needs no per-lane branches (out-of-range loads read zero and
+// out-of-range stores are dropped).
 __global__ __launch_bounds__(256) void copy_blocks_kernel(CopyParams p) {
   const int part = blockIdx.x % p.parts;
   const int rest = blockIdx.x / p.parts;
@@ -118,20 +123,22 @@ __global__ __launch_bounds__(256) void copy_blocks_kernel(CopyParams p) {
   const int32_t dst = p.pairs[2 * pair + 1];
   if ((uint32_t)src >= (uint32_t)p.num_blocks || (uint32_t)dst >= (uint32_t)p.num_blocks) return;
   uint8_t* base = pool ? p.v_pool : p.k_pool;
-  const uint4* s = (const uint4*)(base + (int64_t)src * p.block_bytes);
-  uint4* d = (uint4*)(base + (int64_t)dst * p.block_bytes);
-  const int64_t n16 = p.block_bytes / 16;
-  const int64_t share = (n16 + p.parts - 1) / p.parts;
+  const int64_t share = ((p.block_bytes / 16 + p.parts - 1) / p.parts) * 16;
   const int64_t lo = (int64_t)part * share;
-  const int64_t hi = lo + share < n16 ? lo + share : n16;
-  for (int64_t i = lo + threadIdx.x; i < hi; i += 256 * kCopyUnroll) {
-    uint4 t[kCopyUnroll];
+  if (lo >= p.block_bytes) return;
+  const int n = (int)(lo + share < p.block_bytes ? share : p.block_bytes - lo);
+  __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(base + (int64_t)src * p.block_bytes + lo), (short)0, n, kBufWord3);
+  __amdgpu_buffer_rsrc_t rd =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(base + (int64_t)dst * p.block_bytes + lo), (short)0, n, kBufWord3);
+  for (int i = threadIdx.x * 16; i < n; i += 256 * 16 * kCopyUnroll) {
+    u32x4 t[kCopyUnroll];
 #pragma unroll
     for (int u = 0; u < kCopyUnroll; ++u)
-      if (i + u * 256 < hi) t[u] = s[i + u * 256];
+      t[u] = __builtin_amdgcn_raw_buffer_load_b128(rs, i + u * 256 * 16, 0, kNonTemporal);
 #pragma unroll
     for (int u = 0; u < kCopyUnroll; ++u)
-      if (i + u * 256 < hi) d[i + u * 256] = t[u];
+      __builtin_amdgcn_raw_buffer_store_b128(t[u], rd, i + u * 256 * 16, 0, kNonTemporal);
   }
 }
 
@@ -186,7 +193,9 @@ extern "C" kv_status_t copy_blocks(kv_pool_t* pool, const int32_t* pairs, int32_
   p.num_pairs = num_pairs;
   p.num_blocks = pool->num_blocks;
   p.block_bytes = (int64_t)pool->num_kv_heads * pool->block_size * pool->head_dim * elem_bytes(pool->dtype);
-  // about 16 KiB per work-group
+  // about 16 KiB per work-group (one round of 4 x 16 bytes per lane); a
+  // buffer descriptor spans at most 2 GiB
+  if (p.block_bytes % 16 || p.block_bytes >= (1LL << 31)) return KV_ERR_UNSUPPORTED;
   int64_t parts = (p.block_bytes + 16383) / 16384;
   p.parts = (int32_t)(parts < 1 ? 1 : parts);
   const int64_t grid = (int64_t)num_pairs * 2 * p.parts;

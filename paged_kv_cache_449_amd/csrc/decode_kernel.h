@@ -225,11 +225,31 @@ __device__ inline void compute_step(const StepRegs<U>& r, const float (&qv)[G][V
   }
 }
 
-__device__ inline void store_coherent(float* p, float v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+// Device-scope coherent record traffic.  Cache policy sc1 is what the
+// compiler emits for relaxed agent-scope atomic loads and stores on gfx950
+// (stores write through to the device coherence point, loads do not return
+// stale cache lines); here it is applied to 16-byte buffer accesses so a
+// record moves in whole 16-byte pieces rather than 4-byte stores, each of
+// which costs a full memory write when it is written through.
+constexpr int kCoherentPolicy = 16;
+typedef unsigned u32x4 __attribute__((__vector_size__(16)));
+
+struct RecordRef {
+  __amdgpu_buffer_rsrc_t rsrc;
+};
+
+template <int D, int G>
+__device__ inline RecordRef record_ref(const float* rec) {
+  return {__builtin_amdgcn_make_buffer_rsrc((void*)rec, (short)0, G * (D + 4) * 4, kBufferWord3)};
 }
-__device__ inline float load_coherent(const float* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+// store floats [i, i+4) of the record (i a multiple of 4)
+__device__ inline void record_store4(const RecordRef& r, int i, float a, float b, float c, float d) {
+  const uint4 v = make_uint4(__float_as_uint(a), __float_as_uint(b), __float_as_uint(c), __float_as_uint(d));
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r.rsrc, i * 4, 0, kCoherentPolicy);
+}
+__device__ inline float4 record_load4(const RecordRef& r, int i) {
+  const uint4 v = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r.rsrc, i * 4, 0, kCoherentPolicy));
+  return make_float4(__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z), __uint_as_float(v.w));
 }
 
 // ------------------------------------------------------ split-run bookkeeping
@@ -248,7 +268,7 @@ __device__ inline float* partial_record(const DecodeParams& p, int w, int wstart
 }
 
 // Publish-side half of the hand-over: the caller has stored its record with
-// store_coherent (written through to the device coherence point).  Wait for
+// record_store4 (written through to the device coherence point).  Wait for
 // those stores to complete, then count this worker in.  Returns true in the
 // worker that completes the count, which then merges.  Its loads of the
 // records are coherent loads, so no cache-wide writeback or invalidate is
@@ -277,17 +297,21 @@ __device__ inline void merge_records(const DecodeParams& p, int first_w, int las
     const int g = e0 / D, d = e0 % D;
     float M = -INFINITY;
     for (int v = first_w; v <= last_w; ++v) {
-      const float* r = p.partials + (int64_t)(2 * v + (v * chunk >= seg_start ? 0 : 1)) * G * REC + g * REC;
-      M = fmaxf(M, load_coherent(r + D));
+      const RecordRef r = record_ref<D, G>(p.partials + (int64_t)(2 * v + (v * chunk >= seg_start ? 0 : 1)) * G * REC);
+      M = fmaxf(M, record_load4(r, g * REC + D).x);
     }
     const float mu = M == -INFINITY ? 0.0f : M;
     float lsum = 0.0f, o[4] = {0.0f, 0.0f, 0.0f, 0.0f};
     for (int v = first_w; v <= last_w; ++v) {
-      const float* r = p.partials + (int64_t)(2 * v + (v * chunk >= seg_start ? 0 : 1)) * G * REC + g * REC;
-      const float f = fexp2(load_coherent(r + D) - mu);
-      lsum = fmaf(f, load_coherent(r + D + 1), lsum);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) o[i] = fmaf(f, load_coherent(r + d + i), o[i]);
+      const RecordRef r = record_ref<D, G>(p.partials + (int64_t)(2 * v + (v * chunk >= seg_start ? 0 : 1)) * G * REC);
+      const float4 ml = record_load4(r, g * REC + D);
+      const float4 a = record_load4(r, g * REC + d);
+      const float f = fexp2(ml.x - mu);
+      lsum = fmaf(f, ml.y, lsum);
+      o[0] = fmaf(f, a.x, o[0]);
+      o[1] = fmaf(f, a.y, o[1]);
+      o[2] = fmaf(f, a.z, o[2]);
+      o[3] = fmaf(f, a.w, o[3]);
     }
     store_row<QT, 4>(p.out + (oe + e0) * QE, o, lsum > 0.0f ? p.v_scale / lsum : 0.0f);
   }
@@ -403,16 +427,14 @@ __device__ inline void valu_run(const DecodeParams& p, int w, int chunk, int wst
 
   // Partial: publish (acc, m, l) through the device coherence point; the
   // worker that completes the run's count merges.
-  float* rec = partial_record<D, G>(p, w, wstart, pos);
+  const RecordRef rec = record_ref<D, G>(partial_record<D, G>(p, w, wstart, pos));
   if (row == 0) {
 #pragma unroll
     for (int g = 0; g < G; ++g) {
 #pragma unroll
-      for (int i = 0; i < VEC; ++i) store_coherent(rec + g * REC + col * VEC + i, acc[g][i]);
-      if (col == 0) {
-        store_coherent(rec + g * REC + D, m[g]);
-        store_coherent(rec + g * REC + D + 1, l[g]);
-      }
+      for (int i = 0; i < VEC; i += 4)
+        record_store4(rec, g * REC + col * VEC + i, acc[g][i], acc[g][i + 1], acc[g][i + 2], acc[g][i + 3]);
+      if (col == 0) record_store4(rec, g * REC + D, m[g], l[g], 0.0f, 0.0f);
     }
   }
   const int seg_start = pos - off;

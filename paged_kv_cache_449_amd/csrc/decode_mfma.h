@@ -302,17 +302,13 @@ __device__ inline void mfma_run(const DecodeParams& p, int w, int chunk, int wst
     return;
   }
 
-  float* rec = partial_record<D, G>(p, w, wstart, pos);
+  const RecordRef rec = record_ref<D, G>(partial_record<D, G>(p, w, wstart, pos));
   if (j16 < G) {
-    float* rg = rec + j16 * (D + 4);
+    const int rg = j16 * (D + 4);
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) store_coherent(rg + dt * 16 + 4 * kg + i, acc[dt][i]);
-    if (kg == 0) {
-      store_coherent(rg + D, m);
-      store_coherent(rg + D + 1, l);
-    }
+      record_store4(rec, rg + dt * 16 + 4 * kg, acc[dt][0], acc[dt][1], acc[dt][2], acc[dt][3]);
+    if (kg == 0) record_store4(rec, rg + D, m, l, 0.0f, 0.0f);
   }
   const int seg_start = pos - off;
   const int first_w = seg_start / chunk;
