@@ -110,6 +110,14 @@ struct MfmaTileRegs {
   uint4 v[MfmaShape<KV, D>::VL];
 };
 
+// Tiles loaded and computed together in one pipeline step: two for 1-byte
+// elements so a step moves 8 KiB, as one 16-bit tile does.
+template <typename KV, int D>
+struct MfmaStep {
+  static constexpr int TPS = MfmaShape<KV, D>::ROW <= 128 ? 2 : 1;
+  MfmaTileRegs<KV, D> t[TPS];
+};
+
 // Issue the loads of 16-token tile j of the current table window (tokens
 // tlo + 16j ...).  Tokens at or past thi and blocks whose table entry is out
 // of range read as zeros.
@@ -171,6 +179,7 @@ __device__ inline void mfma_run(const DecodeParams& p, int w, int chunk, int wst
   using Sh = MfmaShape<KV, D>;
   static_assert(G >= 1 && G <= 16, "query group");
   constexpr int KS = Sh::KS, DT = Sh::DT, LSTRIDE = Sh::LSTRIDE;
+  constexpr int TPS = MfmaStep<KV, D>::TPS;
   constexpr int QE = elem_size<QT>::value;
   __shared__ __attribute__((aligned(16))) uint8_t vlds[16 * LSTRIDE];
 
@@ -271,15 +280,26 @@ __device__ inline void mfma_run(const DecodeParams& p, int w, int chunk, int wst
     const int tlo = (off + wb) << p.log2_bs;
     const int thi = min((off + wb + cnt) << p.log2_bs, n);
     const int tiles = (thi - tlo + 15) >> 4;
-    // Two tiles in flight; unconditional issues keep the wait counts exact
-    // (a tile past the window reads zeros and its scores are all masked).
-    MfmaTileRegs<KV, D> a, b;
-    mfma_issue<KV, D>(c, tab, tlo, thi, 0, a);
-    for (int j = 0; j < tiles; j += 2) {
-      mfma_issue<KV, D>(c, tab, tlo, thi, j + 1, b);
-      compute(a, tab, tlo, thi, j);
-      mfma_issue<KV, D>(c, tab, tlo, thi, j + 2, a);
-      compute(b, tab, tlo, thi, j + 1);
+    // Two step register sets in flight (8 KiB each): issue the next step,
+    // compute this one.  Issues are unconditional so the compiler's wait
+    // counts stay exact (a tile past the window reads zeros and its scores
+    // are all masked).
+    const int steps = (tiles + TPS - 1) / TPS;
+    MfmaStep<KV, D> a, b;
+    auto issue = [&](MfmaStep<KV, D>& r, int st) {
+#pragma unroll
+      for (int q = 0; q < TPS; ++q) mfma_issue<KV, D>(c, tab, tlo, thi, st * TPS + q, r.t[q]);
+    };
+    auto run_step = [&](const MfmaStep<KV, D>& r, int st) {
+#pragma unroll
+      for (int q = 0; q < TPS; ++q) compute(r.t[q], tab, tlo, thi, st * TPS + q);
+    };
+    issue(a, 0);
+    for (int st = 0; st < steps; st += 2) {
+      issue(b, st + 1);
+      run_step(a, st);
+      issue(a, st + 2);
+      run_step(b, st + 1);
     }
     tab = tab_next;
   }
