@@ -58,10 +58,13 @@ kv_status_t make_plan(const kv_pool_t* pool, int32_t num_seqs, int32_t num_q_hea
   }
   if (workers < 1) workers = 1;
   workers = (workers + 7) & ~7LL;
-  if (workers > kCounterSlots) return KV_ERR_INVALID_ARG;
+  // chunks (virtual workers): the library-sized split may cut the stream
+  // kSharedSplit times finer when sequences share blocks
+  const int64_t chunks = partition_tokens > 0 ? workers : workers * kSharedSplit;
+  if (chunks > kCounterSlots) return KV_ERR_INVALID_ARG;
   plan->num_workers = (int32_t)workers;
   plan->counters_bytes = (size_t)kCounterSlots * sizeof(int32_t);
-  plan->bytes = plan->counters_bytes + (size_t)2 * workers * G * (pool->head_dim + 4) * sizeof(float);
+  plan->bytes = plan->counters_bytes + (size_t)2 * chunks * G * (pool->head_dim + 4) * sizeof(float);
   return KV_OK;
 }
 

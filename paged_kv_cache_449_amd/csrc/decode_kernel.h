@@ -45,6 +45,12 @@ constexpr int kLoadsPerStep = 4;  // wave loads of K (and of V) issued together
 // fixed size and sits at the start of the workspace, so calls with different
 // batch shapes can share one workspace: each call leaves it zero.
 constexpr int kCounterSlots = 65536;
+// When sequences share blocks (copy-on-write candidates of one prompt), the
+// library-sized split cuts the stream kSharedSplit times finer and each
+// worker takes kSharedSplit chunks, one per round: the candidates' runs then
+// sit in neighbouring chunks that run at the same time on one XCD and meet
+// in its L2.
+constexpr int kSharedSplit = 4;
 
 struct DecodeParams {
   const uint8_t* k_pool;
@@ -130,10 +136,12 @@ __device__ inline float softmax_step(float& m, float& l, const float* sc, float*
 constexpr int kBufferWord3 = 0x00020000;
 // Lane offset that lies outside every tile: the load returns zeros.
 constexpr uint32_t kMaskedOffset = 0x80000000u;
-// Cache policy of the K/V stream loads: non-temporal (each byte is used once
-// per launch).  On MI355X this lifts a random-4-KiB-tile read stream from
-// about 6.1 to about 6.8 TB/s.
+// Cache policy of the K/V stream loads: non-temporal when each byte is used
+// once per launch (on MI355X this lifts a random-4-KiB-tile read stream from
+// about 6.1 to about 6.8 TB/s); the default policy when sequences share
+// blocks, so a block read for one candidate can serve the others from L2.
 constexpr int kStreamPolicy = 2;
+constexpr int kSharedPolicy = 0;
 
 __device__ inline int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
@@ -159,7 +167,7 @@ struct RunCtx {
 // Issue the U K and V loads of step `step` of the current table window.
 // Tokens at or past `thi`, and blocks whose table entry is out of range,
 // read as zeros (offset outside the tile, or an empty tile).
-template <int U, int TPL>
+template <int U, int TPL, int POL>
 __device__ inline void issue_step(const RunCtx& c, int tab, int tlo, int thi, int step, int row,
                                   StepRegs<U>& r) {
 #pragma unroll
@@ -176,8 +184,8 @@ __device__ inline void issue_step(const RunCtx& c, int tab, int tlo, int thi, in
                                                                   kBufferWord3);
     const int t = tlo + j * TPL + row;
     const uint32_t off = t < thi ? (uint32_t)((t & c.bs_mask) * c.row_bytes) + c.lane_off : kMaskedOffset;
-    r.k[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, kStreamPolicy));
-    r.v[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, kStreamPolicy));
+    r.k[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, POL));
+    r.v[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, POL));
   }
 }
 
@@ -331,7 +339,7 @@ __device__ inline int load_table_window(const DecodeParams& p, const int32_t* tr
 // sequence s) stream, which has nb blocks and n tokens.  pos is the run's
 // place in the flattened stream and wstart the worker's first block.  All
 // scalars are uniform.
-template <typename KV, typename QT, int D, int G>
+template <typename KV, typename QT, int D, int G, int POL>
 __device__ inline void valu_run(const DecodeParams& p, int w, int chunk, int wstart, int pos, int s, int h,
                                 int off, int len, int n, int nb) {
   using Sh = DecodeShape<KV, D>;
@@ -388,11 +396,11 @@ __device__ inline void valu_run(const DecodeParams& p, int w, int chunk, int wst
     // counts stay exact: a step past the window reads zeros (its offsets lie
     // outside the tile) and computes nothing (every score is masked).
     StepRegs<U> a, b;
-    issue_step<U, TPL>(c, tab, tlo, thi, 0, row, a);
+    issue_step<U, TPL, POL>(c, tab, tlo, thi, 0, row, a);
     for (int st = 0; st < steps; st += 2) {
-      issue_step<U, TPL>(c, tab, tlo, thi, st + 1, row, b);
+      issue_step<U, TPL, POL>(c, tab, tlo, thi, st + 1, row, b);
       compute_step<KV, VEC, L, TPL, G, U>(a, qv, m, l, acc, tab, tlo, thi, st, row, p.log2_bs);
-      issue_step<U, TPL>(c, tab, tlo, thi, st + 2, row, a);
+      issue_step<U, TPL, POL>(c, tab, tlo, thi, st + 2, row, a);
       compute_step<KV, VEC, L, TPL, G, U>(b, qv, m, l, acc, tab, tlo, thi, st + 1, row, p.log2_bs);
     }
     tab = tab_next;
@@ -450,52 +458,16 @@ __device__ inline void valu_run(const DecodeParams& p, int w, int chunk, int wst
 
 namespace pkv {
 
-// One worker wavefront per work-group.  MFMA selects the matrix-core run
-// (query groups with a 16-bit operand type) over the vector-ALU run.
-template <typename KV, typename QT, int D, int G, bool MFMA>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(MFMA ? 2 : 1)))
-void paged_decode_kernel(const DecodeParams p) {
+// Stream chunk v: blocks [v*chunk, (v+1)*chunk) of the flattened
+// (kv head, sequence, block) stream, which has `total` blocks per kv head
+// and T in all.
+template <typename KV, typename QT, int D, int G, bool MFMA, int POL>
+__device__ inline void decode_chunk(const DecodeParams& p, int v, int chunk, int T, int total) {
   const int lane = threadIdx.x;
   const int S = p.num_seqs;
   const int bs = 1 << p.log2_bs;
   const int max_len = p.max_blocks << p.log2_bs;
-
-  // blocks per kv head, and whether some sequence is empty
-  int total = 0;
-  bool empty = false;
-  for (int base = 0; base < S; base += 64) {
-    const int s = base + lane;
-    int nb = 0;
-    if (s < S) {
-      const int n = clamp_len(p.context_lens[s], max_len);
-      nb = (n + bs - 1) >> p.log2_bs;
-      empty |= n == 0;
-    }
-    total += wave_sum_i32(nb);
-  }
-  total = uniform(total);
-
-  if (blockIdx.x == 0 && __ballot(empty)) {
-    // empty contexts attend to nothing: their rows are zero
-    constexpr int QE = elem_size<QT>::value;
-    const int Hq = p.num_kv_heads * G;
-    for (int s = 0; s < S; ++s) {
-      if (clamp_len(p.context_lens[s], max_len) != 0) continue;
-      uint8_t* o = p.out + (int64_t)s * Hq * D * QE;
-      for (int i = lane * 4; i < Hq * D * QE; i += 256) *(uint32_t*)(o + i) = 0u;
-    }
-  }
-
-  const int T = total * p.num_kv_heads;
-  const int chunk = p.chunk > 0 ? p.chunk : max(1, (T + p.num_workers - 1) / p.num_workers);
-  // Only the first `active` worker ids have blocks.  They are spread over
-  // all 8 XCDs: work-group b runs on XCD b % 8 and becomes worker
-  // (b % 8) * (active8 / 8) + b / 8, so each XCD holds one contiguous range
-  // of the stream (neighbouring runs share its L2).
-  const int active8 = (((T + chunk - 1) / chunk) + 7) & ~7;   // <= num_workers
-  if ((int)blockIdx.x >= active8) return;
-  const int w = (int)(blockIdx.x & 7) * (active8 >> 3) + (int)(blockIdx.x >> 3);
-  const int start = w * chunk;
+  const int start = v * chunk;
   if (start >= T) return;
   const int end = min(start + chunk, T);
   int h = start / total;
@@ -533,9 +505,9 @@ void paged_decode_kernel(const DecodeParams p) {
   while (true) {
     const int len = min(nb - off, end - pos);
     if constexpr (MFMA)
-      mfma_run<KV, QT, D, G>(p, w, chunk, start, pos, s, h, off, len, n, nb);
+      mfma_run<KV, QT, D, G, POL>(p, v, chunk, start, pos, s, h, off, len, n, nb);
     else
-      valu_run<KV, QT, D, G>(p, w, chunk, start, pos, s, h, off, len, n, nb);
+      valu_run<KV, QT, D, G, POL>(p, v, chunk, start, pos, s, h, off, len, n, nb);
     pos += len;
     if (pos >= end) break;
     do {
@@ -547,6 +519,71 @@ void paged_decode_kernel(const DecodeParams p) {
       nb = (n + bs - 1) >> p.log2_bs;
     } while (nb == 0);
     off = 0;
+  }
+}
+
+// One worker wavefront per work-group.  MFMA selects the matrix-core run
+// (query groups with a 16-bit operand type) over the vector-ALU run.
+template <typename KV, typename QT, int D, int G, bool MFMA>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(MFMA ? 2 : 1)))
+void paged_decode_kernel(const DecodeParams p) {
+  const int lane = threadIdx.x;
+  const int S = p.num_seqs;
+  const int bs = 1 << p.log2_bs;
+  const int max_len = p.max_blocks << p.log2_bs;
+
+  // Blocks per kv head; whether some sequence is empty; whether some
+  // sequence starts with the same physical block as its predecessor
+  // (copy-on-write candidates sharing a prompt).
+  int total = 0;
+  bool empty = false, shared = false;
+  for (int base = 0; base < S; base += 64) {
+    const int s = base + lane;
+    int nb = 0;
+    if (s < S) {
+      const int n = clamp_len(p.context_lens[s], max_len);
+      nb = (n + bs - 1) >> p.log2_bs;
+      empty |= n == 0;
+      if (s > 0 && n > 0 && clamp_len(p.context_lens[s - 1], max_len) > 0) {
+        const int b0 = p.block_tables[(int64_t)s * p.max_blocks];
+        shared |= (uint32_t)b0 < (uint32_t)p.num_blocks && b0 == p.block_tables[(int64_t)(s - 1) * p.max_blocks];
+      }
+    }
+    total += wave_sum_i32(nb);
+  }
+  total = uniform(total);
+  const bool any_shared = __ballot(shared) != 0;
+
+  if (blockIdx.x == 0 && __ballot(empty)) {
+    // empty contexts attend to nothing: their rows are zero
+    constexpr int QE = elem_size<QT>::value;
+    const int Hq = p.num_kv_heads * G;
+    for (int s = 0; s < S; ++s) {
+      if (clamp_len(p.context_lens[s], max_len) != 0) continue;
+      uint8_t* o = p.out + (int64_t)s * Hq * D * QE;
+      for (int i = lane * 4; i < Hq * D * QE; i += 256) *(uint32_t*)(o + i) = 0u;
+    }
+  }
+
+  // The stream of T blocks is cut into chunks of `chunk` blocks, one per
+  // virtual worker v (records and counters are indexed by v).  Work-group b
+  // takes one chunk per round; in every round the ids are spread over the 8
+  // XCDs (work-group b runs on XCD b % 8 and takes id
+  // round_base + (b % 8) * (per_round / 8) + b / 8), so each XCD holds one
+  // contiguous range of the stream and neighbouring runs share its L2.
+  const int T = total * p.num_kv_heads;
+  const int rounds = (p.chunk == 0 && any_shared) ? kSharedSplit : 1;
+  const int chunk = p.chunk > 0 ? p.chunk : max(1, (T + p.num_workers * rounds - 1) / (p.num_workers * rounds));
+  const int nv = (T + chunk - 1) / chunk;                               // chunks with blocks
+  const int per_round = rounds == 1 ? ((nv + 7) & ~7) : p.num_workers;  // <= num_workers
+  if ((int)blockIdx.x >= per_round) return;
+  for (int rd = 0; rd < rounds; ++rd) {
+    const int v = rd * per_round + (int)(blockIdx.x & 7) * (per_round >> 3) + (int)(blockIdx.x >> 3);
+    if (v >= nv) continue;
+    if (any_shared)
+      decode_chunk<KV, QT, D, G, MFMA, kSharedPolicy>(p, v, chunk, T, total);
+    else
+      decode_chunk<KV, QT, D, G, MFMA, kStreamPolicy>(p, v, chunk, T, total);
   }
 }
 

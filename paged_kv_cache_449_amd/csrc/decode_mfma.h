@@ -110,18 +110,18 @@ struct MfmaTileRegs {
   uint4 v[MfmaShape<KV, D>::VL];
 };
 
-// Tiles loaded and computed together in one pipeline step: two for 1-byte
-// elements so a step moves 8 KiB, as one 16-bit tile does.
+// Tiles loaded and computed together in one pipeline step.  One: two fp8
+// tiles per step (8 KiB, as one 16-bit tile) measured 2% slower on MI355X.
 template <typename KV, int D>
 struct MfmaStep {
-  static constexpr int TPS = MfmaShape<KV, D>::ROW <= 128 ? 2 : 1;
+  static constexpr int TPS = 1;
   MfmaTileRegs<KV, D> t[TPS];
 };
 
 // Issue the loads of 16-token tile j of the current table window (tokens
 // tlo + 16j ...).  Tokens at or past thi and blocks whose table entry is out
 // of range read as zeros.
-template <typename KV, int D>
+template <typename KV, int D, int POL>
 __device__ inline void mfma_issue(const RunCtx& c, int tab, int tlo, int thi, int j, MfmaTileRegs<KV, D>& r) {
   using Sh = MfmaShape<KV, D>;
   const int lane = threadIdx.x;
@@ -151,7 +151,7 @@ __device__ inline void mfma_issue(const RunCtx& c, int tab, int tlo, int thi, in
     const int byte = (u * 64 + lane) * 16;
     const int vr = byte / Sh::ROW, vc = byte % Sh::ROW;
     const uint32_t vo = t0 + vr < thi ? (uint32_t)((o0 + vr) * Sh::ROW + vc) : kMaskedOffset;
-    r.v[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rv, vo, 0, kStreamPolicy));
+    r.v[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rv, vo, 0, POL));
   }
 }
 
@@ -171,7 +171,7 @@ __device__ inline uint4 mfma_k_operand(const MfmaTileRegs<KV, D>& r, int st) {
   }
 }
 
-template <typename KV, typename QT, int D, int G>
+template <typename KV, typename QT, int D, int G, int POL>
 __device__ inline void mfma_run(const DecodeParams& p, int w, int chunk, int wstart, int pos, int s, int h, int off,
                                 int len, int n, int nb) {
   using MT = typename mfma_operand<KV, QT>::type;
@@ -280,15 +280,15 @@ __device__ inline void mfma_run(const DecodeParams& p, int w, int chunk, int wst
     const int tlo = (off + wb) << p.log2_bs;
     const int thi = min((off + wb + cnt) << p.log2_bs, n);
     const int tiles = (thi - tlo + 15) >> 4;
-    // Two step register sets in flight (8 KiB each): issue the next step,
-    // compute this one.  Issues are unconditional so the compiler's wait
+    // Two step register sets in flight: issue the next step, compute this
+    // one.  Issues are unconditional so the compiler's wait
     // counts stay exact (a tile past the window reads zeros and its scores
     // are all masked).
     const int steps = (tiles + TPS - 1) / TPS;
     MfmaStep<KV, D> a, b;
     auto issue = [&](MfmaStep<KV, D>& r, int st) {
 #pragma unroll
-      for (int q = 0; q < TPS; ++q) mfma_issue<KV, D>(c, tab, tlo, thi, st * TPS + q, r.t[q]);
+      for (int q = 0; q < TPS; ++q) mfma_issue<KV, D, POL>(c, tab, tlo, thi, st * TPS + q, r.t[q]);
     };
     auto run_step = [&](const MfmaStep<KV, D>& r, int st) {
 #pragma unroll

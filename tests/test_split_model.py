@@ -13,9 +13,11 @@ import numpy as np
 import pytest
 
 COUNTER_SLOTS = 65536
+SHARED_SPLIT = 4
 
 
 def plan(num_seqs, hkv, max_blocks, bs, partition_tokens, num_cus=256, waves_per_cu=16):
+    """(chunk or 0, launched workers, record chunks the workspace holds)."""
     units = num_seqs * hkv * max_blocks
     if partition_tokens > 0:
         chunk = partition_tokens // bs
@@ -27,35 +29,41 @@ def plan(num_seqs, hkv, max_blocks, bs, partition_tokens, num_cus=256, waves_per
         workers = min(num_cus * waves_per_cu, units)
     workers = max(workers, 1)
     workers = (workers + 7) & ~7
-    assert workers <= COUNTER_SLOTS
-    return chunk, workers
+    chunks = workers if partition_tokens > 0 else workers * SHARED_SPLIT
+    assert chunks <= COUNTER_SLOTS
+    return chunk, workers, chunks
 
 
-def replay(lens, hkv, max_blocks, bs, partition_tokens, **kw):
+def replay(lens, hkv, max_blocks, bs, partition_tokens, shared=False, **kw):
     S = len(lens)
     max_len = max_blocks * bs
     n = np.clip(lens, 0, max_len)
     nb = -(-n // bs)
     total = int(nb.sum())
     T = total * hkv
-    chunk0, W = plan(S, hkv, max_blocks, bs, partition_tokens, **kw)
-    chunk = chunk0 if chunk0 > 0 else max(1, -(-T // W))
+    chunk0, W, CH = plan(S, hkv, max_blocks, bs, partition_tokens, **kw)
+    rounds = SHARED_SPLIT if (chunk0 == 0 and shared) else 1
+    chunk = chunk0 if chunk0 > 0 else max(1, -(-T // (W * rounds)))
+    nv = -(-T // chunk)
+    per_round = ((nv + 7) & ~7) if rounds == 1 else W
+    assert per_round <= W and nv <= rounds * per_round
     pre = np.concatenate([[0], np.cumsum(nb)])
     streamed = np.zeros((hkv, S, max_blocks), dtype=np.int32)
     written = np.zeros((hkv, S), dtype=np.int32)
     records = {}         # (slot) -> (h, s) written
     counters = np.zeros(COUNTER_SLOTS, dtype=np.int32)
-    active8 = ((-(-T // chunk)) + 7) & ~7
-    assert active8 <= W
     seen_workers = set()
-    # workers in dispatch order; the merge decision depends only on counts,
+    # chunks in dispatch order; the merge decision depends only on counts,
     # so any completion order gives the same result -- use a shuffled one
-    order = np.random.default_rng(0).permutation(W)
-    for bid in order:
-        if bid >= active8:
+    order = [(rd, bid) for rd in range(rounds) for bid in range(W)]
+    order = [order[i] for i in np.random.default_rng(0).permutation(len(order))]
+    for rd, bid in order:
+        if bid >= per_round:
             continue
-        w = (bid & 7) * (active8 >> 3) + (bid >> 3)
-        assert 0 <= w < active8 and w not in seen_workers
+        w = rd * per_round + (bid & 7) * (per_round >> 3) + (bid >> 3)
+        if w >= nv:
+            continue
+        assert 0 <= w < CH and w not in seen_workers
         seen_workers.add(w)
         start = w * chunk
         if start >= T:
@@ -79,11 +87,11 @@ def replay(lens, hkv, max_blocks, bs, partition_tokens, **kw):
             else:
                 k = 0 if pos == start else 1
                 slot = 2 * w + k
-                assert slot < 2 * W and slot not in records
+                assert slot < 2 * CH and slot not in records
                 records[slot] = (h, s)
                 seg_start = pos - off
                 first_w, last_w = seg_start // chunk, (seg_start + nb[s] - 1) // chunk
-                assert first_w < last_w < W and first_w < COUNTER_SLOTS
+                assert first_w < last_w < nv and first_w < COUNTER_SLOTS
                 counters[first_w] += 1
                 if counters[first_w] - 1 == last_w - first_w:
                     got = set()
@@ -106,7 +114,7 @@ def replay(lens, hkv, max_blocks, bs, partition_tokens, **kw):
                 if nb[s] > 0:
                     break
             off = 0
-    assert seen_workers == set(range(active8))
+    assert seen_workers == set(range(nv))
     for h in range(hkv):
         for s in range(S):
             assert (streamed[h, s, :nb[s]] == 1).all() and (streamed[h, s, nb[s]:] == 0).all()
@@ -127,10 +135,11 @@ CASES = [
 ]
 
 
+@pytest.mark.parametrize("shared", [False, True])
 @pytest.mark.parametrize("case", CASES)
-def test_split_bookkeeping(case):
+def test_split_bookkeeping(case, shared):
     lens, hkv, mb, bs, pt = case
-    replay(np.asarray(lens), hkv, mb, bs, pt)
+    replay(np.asarray(lens), hkv, mb, bs, pt, shared=shared)
 
 
 @pytest.mark.parametrize("seed", range(6))
@@ -143,10 +152,12 @@ def test_split_bookkeeping_random(seed, cus):
     lens = rng.integers(0, mb * bs + 1, size=S)
     hkv = int(rng.integers(1, 9))
     pt = int(rng.choice([0, bs, 3 * bs, 32 * bs]))
-    replay(lens, hkv, mb, bs, pt, num_cus=cus, waves_per_cu=int(rng.integers(1, 20)))
+    replay(lens, hkv, mb, bs, pt, shared=bool(seed % 2), num_cus=cus, waves_per_cu=int(rng.integers(1, 20)))
 
 
 def test_workload_shapes_fit():
     import workloads as W
     for wl in W.full_configs().values():
-        replay(wl.context_lens, wl.num_kv_heads, wl.max_blocks_per_seq, wl.block_size, wl.partition_tokens)
+        shared = len(set(wl.parent)) < wl.num_seqs
+        replay(wl.context_lens, wl.num_kv_heads, wl.max_blocks_per_seq, wl.block_size, wl.partition_tokens,
+               shared=shared)
