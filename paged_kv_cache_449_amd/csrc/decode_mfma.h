@@ -8,17 +8,22 @@
 // The tile is 16 tokens of one block (block_size >= 16) of one kv head.
 //
 //   QK  v_mfma_f32_16x16x32_{bf16,f16}: A = K rows (row i = token), B = q
-//       (column j = head, zero for j >= G), D/32 steps over head_dim.  Lane
-//       (kg = lane/16, t = lane%16) streams the contiguous quarter
-//       [kg*D/4, (kg+1)*D/4) of token t's row; q is laid out with the same
-//       (kg, element) -> dim mapping, so the contraction pairs matching dims
-//       whatever order the instruction walks its k index in.
+//       (column j = head, zero for j >= G), D/32 steps over head_dim.  The K
+//       tile is loaded contiguously and staged in LDS; lane (kg = lane/16,
+//       t = lane%16) then reads the contiguous quarter [kg*D/4, (kg+1)*D/4)
+//       of token t's row.  q is laid out with the same (kg, element) -> dim
+//       mapping, so the contraction pairs matching dims whatever order the
+//       instruction walks its k index in.
 //   PV  v_mfma_f32_16x16x16_{bf16,f16}: A = V^T (row i = dim within a
 //       16-column slice, k = token), B = P (k = token, column j = head).  The
 //       QK result leaves lane (kg, j) holding S[4kg + r][j], r = 0..3, which
 //       is exactly that lane's B operand (P[4kg + e][j]), so P never moves
-//       between lanes.  V^T comes from the tile staged in LDS (rows padded
-//       so the four row groups of a read fall in different banks).
+//       between lanes.  V^T comes from the tile staged in LDS through the
+//       gfx950 transposing read ds_read_b64_tr_b16: within each 16-lane
+//       group, lane 4a + b receives element b of the 8-byte chunks that
+//       lanes 4k + a (k = 0..3) address, so lane (kg, 4a + b) pointing its
+//       own chunk at row 4kg + (lane%16)/4, columns 16dt + 4(lane%4) .. +3
+//       receives V[4kg + k][16dt + 4a + b], k = 0..3: its A operand.
 //
 // fp8 pools are widened exactly to the operand type (E4M3FN is a subset of
 // both bf16 and f16).  P is rounded to the operand type; the running sum adds
@@ -44,8 +49,17 @@ template <> struct mfma_operand<f16_t, f16_t> { using type = f16_t; };
 template <> struct mfma_operand<fp8_t, bf16_t> { using type = bf16_t; };
 template <> struct mfma_operand<fp8_t, f16_t> { using type = f16_t; };
 
+#define PKV_LDS __attribute__((address_space(3)))
+typedef __bf16 lds_bf16x4 __attribute__((__vector_size__(8)));
+typedef __fp16 lds_f16x4 __attribute__((__vector_size__(8)));
+
 template <typename MT> struct mfma_ops;
 template <> struct mfma_ops<bf16_t> {
+  // transposing LDS read of four 16-bit values (see the file comment)
+  __device__ static inline uint2 read_tr(const uint8_t* lds) {
+    const PKV_LDS lds_bf16x4* p = (const PKV_LDS lds_bf16x4*)(lds);
+    return __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4bf16((PKV_LDS lds_bf16x4*)p));
+  }
   // two fp8 codes (bytes 0,1 or 2,3 of w) -> two bf16, exact
   template <bool HI>
   __device__ static inline uint32_t from_fp8(uint32_t w) {
@@ -70,6 +84,10 @@ template <> struct mfma_ops<bf16_t> {
   }
 };
 template <> struct mfma_ops<f16_t> {
+  __device__ static inline uint2 read_tr(const uint8_t* lds) {
+    const PKV_LDS lds_f16x4* p = (const PKV_LDS lds_f16x4*)(lds);
+    return __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4f16((PKV_LDS lds_f16x4*)p));
+  }
   template <bool HI>
   __device__ static inline uint32_t from_fp8(uint32_t w) {
     return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, HI));
@@ -100,8 +118,17 @@ struct MfmaShape {
   static constexpr int VL = 16 * ROW / 1024;     // wave loads of one 16-token V tile
   static constexpr int KS = D / 32;              // QK instructions per tile
   static constexpr int DT = D / 16;              // PV instructions per tile (16 dims each)
-  static constexpr int LSTRIDE = 2 * D + 16;     // LDS bytes per staged V row (operand type)
-  static_assert(KL >= 1 && VL >= 1 && KS >= 1, "tile shape");
+  // LDS bytes per staged V row (operand type): 32 bytes past a multiple of
+  // 256 for D = 128 and 256, so the 16 rows x 32 bytes a transposing read
+  // touches spread over all banks
+  static constexpr int LSTRIDE = 2 * D + 32;
+  // K tiles are loaded contiguously and staged in LDS: a lane reading its own
+  // token's quarter row straight from memory makes each load touch 16 lines,
+  // which stalled the address units on the L1 (for about a third of the
+  // kernel on 128-byte fp8 rows).  Rows are padded by 16 bytes so the 16 rows
+  // of a read fall in different banks.
+  static constexpr int KSTRIDE = ROW + 16;
+  static_assert(KL >= 1 && VL >= 1 && KS >= 1 && KL == VL, "tile shape");
 };
 
 template <typename KV, int D>
@@ -136,16 +163,14 @@ __device__ inline void mfma_issue(const RunCtx& c, int tab, int tlo, int thi, in
       __builtin_amdgcn_make_buffer_rsrc((void*)(c.v_head + boff), (short)0, (int)nrec, kBufferWord3);
   const int t0 = tlo + j * 16;             // first token of the tile
   const int o0 = (j * 16) & c.bs_mask;     // its slot in the block
-  // K: lane (kg, t) reads the quarter row kg of token t.  One instruction
-  // covers half of each 128-byte line it touches, so these loads keep the
-  // default cache policy (a non-temporal line can be gone before the second
-  // half is read); the contiguous V tile streams non-temporally.
-  const int t = lane & 15, kg = lane >> 4;
-  const uint32_t kb = t0 + t < thi ? (uint32_t)((o0 + t) * Sh::ROW + kg * (Sh::ROW / 4)) : kMaskedOffset;
+  // K and V: the 16 x ROW tiles, contiguous, 16 bytes per lane per wave load
 #pragma unroll
-  for (int q = 0; q < Sh::KL; ++q)
-    r.k[q] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, kb + q * 16, 0, 0));
-  // V: the 16 x ROW tile, contiguous, 16 bytes per lane per wave load
+  for (int q = 0; q < Sh::KL; ++q) {
+    const int byte = (q * 64 + lane) * 16;
+    const int kr = byte / Sh::ROW, kc = byte % Sh::ROW;
+    const uint32_t ko = t0 + kr < thi ? (uint32_t)((o0 + kr) * Sh::ROW + kc) : kMaskedOffset;
+    r.k[q] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, ko, 0, POL));
+  }
 #pragma unroll
   for (int u = 0; u < Sh::VL; ++u) {
     const int byte = (u * 64 + lane) * 16;
@@ -158,12 +183,12 @@ __device__ inline void mfma_issue(const RunCtx& c, int tab, int tlo, int thi, in
 // K operand words of QK step st (8 elements of the operand type) from the
 // lane's quarter row.
 template <typename KV, typename MT, int D>
-__device__ inline uint4 mfma_k_operand(const MfmaTileRegs<KV, D>& r, int st) {
+__device__ inline uint4 mfma_k_operand(const uint4 (&kq)[MfmaShape<KV, D>::KL], int st) {
   if constexpr (elem_size<KV>::value == 2) {
-    return r.k[st];
+    return kq[st];
   } else {
     // fp8: step st uses bytes 8st .. 8st+7 of the quarter row
-    const uint4 w = r.k[st >> 1];
+    const uint4 w = kq[st >> 1];
     const uint32_t a = (st & 1) ? w.z : w.x;
     const uint32_t b = (st & 1) ? w.w : w.y;
     return make_uint4(mfma_ops<MT>::template from_fp8<false>(a), mfma_ops<MT>::template from_fp8<true>(a),
@@ -182,6 +207,7 @@ __device__ inline void mfma_run(const DecodeParams& p, int w, int chunk, int wst
   constexpr int TPS = MfmaStep<KV, D>::TPS;
   constexpr int QE = elem_size<QT>::value;
   __shared__ __attribute__((aligned(16))) uint8_t vlds[16 * LSTRIDE];
+  __shared__ __attribute__((aligned(16))) uint8_t klds[16 * Sh::KSTRIDE];
 
   const int lane = threadIdx.x;
   const int j16 = lane & 15;   // token row (QK A) / head column (B, D)
@@ -219,10 +245,34 @@ __device__ inline void mfma_run(const DecodeParams& p, int w, int chunk, int wst
   const int32_t* trow = p.block_tables + (int64_t)s * p.max_blocks + off;
 
   auto compute = [&](const MfmaTileRegs<KV, D>& r, int tab, int tlo, int thi, int j) {
+    // stage the tile in LDS: V as the operand type (rows padded to LSTRIDE
+    // bytes), K as loaded (rows padded to KSTRIDE bytes)
+    __syncthreads();   // the previous tile's LDS reads are done
+#pragma unroll
+    for (int u = 0; u < Sh::VL; ++u) {
+      const int byte = (u * 64 + lane) * 16;
+      const int vr = byte / Sh::ROW, ve = (byte % Sh::ROW) / Sh::EB;   // row, first element
+      uint8_t* dst = vlds + vr * LSTRIDE + ve * 2;
+      if constexpr (Sh::EB == 2) {
+        *(uint4*)dst = r.v[u];
+      } else {
+        const uint4 w4 = r.v[u];
+        *(uint4*)dst = make_uint4(Ops::template from_fp8<false>(w4.x), Ops::template from_fp8<true>(w4.x),
+                                  Ops::template from_fp8<false>(w4.y), Ops::template from_fp8<true>(w4.y));
+        *(uint4*)(dst + 16) = make_uint4(Ops::template from_fp8<false>(w4.z), Ops::template from_fp8<true>(w4.z),
+                                         Ops::template from_fp8<false>(w4.w), Ops::template from_fp8<true>(w4.w));
+      }
+      *(uint4*)(klds + vr * Sh::KSTRIDE + (byte % Sh::ROW)) = r.k[u];
+    }
+    __syncthreads();
+    // K operand: lane (kg, t) holds the quarter row kg of token t
+    uint4 kq[Sh::KL];
+#pragma unroll
+    for (int q = 0; q < Sh::KL; ++q) kq[q] = *(const uint4*)(klds + j16 * Sh::KSTRIDE + kg * (Sh::ROW / 4) + q * 16);
     // S^T tile: lane (kg, j16) gets scores of tokens 4kg + i, i = 0..3, head j16
     f32x4 sc = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-    for (int st = 0; st < KS; ++st) sc = Ops::qk(mfma_k_operand<KV, MT, D>(r, st), qop[st], sc);
+    for (int st = 0; st < KS; ++st) sc = Ops::qk(mfma_k_operand<KV, MT, D>(kq, st), qop[st], sc);
     const int bi = min((j * 16) >> p.log2_bs, 63);
     const bool bvalid = __builtin_amdgcn_readlane(tab, bi) >= 0;
     const int t0 = tlo + j * 16 + 4 * kg;
@@ -243,34 +293,11 @@ __device__ inline void mfma_run(const DecodeParams& p, int w, int chunk, int wst
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) acc[dt] *= alpha;
     }
-    // stage V in LDS as the operand type, rows padded to LSTRIDE bytes
-    __syncthreads();
-#pragma unroll
-    for (int u = 0; u < Sh::VL; ++u) {
-      const int byte = (u * 64 + lane) * 16;
-      const int vr = byte / Sh::ROW, ve = (byte % Sh::ROW) / Sh::EB;   // row, first element
-      uint8_t* dst = vlds + vr * LSTRIDE + ve * 2;
-      if constexpr (Sh::EB == 2) {
-        *(uint4*)dst = r.v[u];
-      } else {
-        const uint4 w4 = r.v[u];
-        *(uint4*)dst = make_uint4(Ops::template from_fp8<false>(w4.x), Ops::template from_fp8<true>(w4.x),
-                                  Ops::template from_fp8<false>(w4.y), Ops::template from_fp8<true>(w4.y));
-        *(uint4*)(dst + 16) = make_uint4(Ops::template from_fp8<false>(w4.z), Ops::template from_fp8<true>(w4.z),
-                                         Ops::template from_fp8<false>(w4.w), Ops::template from_fp8<true>(w4.w));
-      }
-    }
-    __syncthreads();
     const uint2 pop = make_uint2(p01, p23);
-    const uint16_t* l16 = (const uint16_t*)vlds;
+    // lane (kg, i) needs V[4kg + e][16 dt + i], e = 0..3: one transposing read
+    const uint8_t* tr = vlds + (4 * kg + (j16 >> 2)) * LSTRIDE + (lane & 3) * 8;
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      // lane (kg, i) needs V[4kg + e][16 dt + i], e = 0..3
-      const int base = (4 * kg) * (LSTRIDE / 2) + dt * 16 + j16;
-      const uint32_t a0 = (uint32_t)l16[base] | ((uint32_t)l16[base + LSTRIDE / 2] << 16);
-      const uint32_t a1 = (uint32_t)l16[base + LSTRIDE] | ((uint32_t)l16[base + 3 * (LSTRIDE / 2)] << 16);
-      acc[dt] = Ops::pv(make_uint2(a0, a1), pop, acc[dt]);
-    }
+    for (int dt = 0; dt < DT; ++dt) acc[dt] = Ops::pv(Ops::read_tr(tr + dt * 32), pop, acc[dt]);
   };
 
   int tab = load_table_window(p, trow, 0, len);
