@@ -143,6 +143,31 @@ def measured_traffic(wl_name: str):
     return entry.get("traffic_bytes_per_launch")
 
 
+def swap_measurement(pool, n: int, reps: int = 5) -> dict:
+    """swap_blocks of n pool blocks (K and V) to pinned host memory and back
+    into the same blocks (their contents are unchanged), HIP-event timed."""
+    import paged_kv_cache_449_amd as pk
+    dev = pool.device
+    area = pk.HostSwapArea(pool, n)
+    ids = torch.arange(n, dtype=torch.int32, device=dev)
+    pairs = torch.stack([ids, ids], 1).contiguous()
+    nbytes = 2 * n * pool.block_bytes
+    res = {"blocks": n, "bytes": nbytes}
+    for name, direction in (("out", pk.KV_SWAP_OUT), ("in", pk.KV_SWAP_IN)):
+        pk.swap_blocks(pool, area, pairs, direction)
+        torch.cuda.synchronize(dev)
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for a, b in evs:
+            a.record()
+            pk.swap_blocks(pool, area, pairs, direction)
+            b.record()
+        torch.cuda.synchronize(dev)
+        us = float(np.median([a.elapsed_time(b) for a, b in evs])) * 1e3
+        res[f"{name}_us"] = round(us, 1)
+        res[f"{name}_GBs"] = round(nbytes / us / 1e3, 2)
+    return res
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -153,6 +178,9 @@ def main(argv=None) -> int:
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run one plain 1 GiB device copy before the timed steps: under rocprofv3 --pmc its "
                          "FETCH_SIZE/WRITE_SIZE give the counters' scale against bytes known to move")
+    ap.add_argument("--swap-blocks", type=int, default=0,
+                    help="also time swap_blocks moving this many pool blocks to pinned host memory and back "
+                         "(reported under 'swap'; not part of the step)")
     ap.add_argument("--placement", choices=["shuffled", "sequential"], default="shuffled",
                     help="shuffled: blocks from a seeded random free list (the workload); sequential: "
                          "the free list in id order, so each sequence's blocks are contiguous (the "
@@ -243,6 +271,8 @@ def main(argv=None) -> int:
                      "kernel": "paged_decode_kernel", "kernel_us": round(float(dec_ms.mean()) * 1e3, 2),
                      "bytes_per_launch": nb["total"]},
     }
+    if args.swap_blocks > 0:
+        res["swap"] = swap_measurement(pool, min(args.swap_blocks, wl.num_blocks))
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(wl)

@@ -161,11 +161,16 @@ kv_status_t reshape_and_cache(kv_pool_t* pool, const void* k_new, const void* v_
  * Work split: the cached tokens of all (kv head, sequence) pairs are laid end
  * to end and cut into equal runs of whole blocks, one per worker wavefront,
  * so long and short sequences cost the same per token.  partition_tokens == 0
- * lets the library size the runs from the device's compute-unit count;
- * otherwise each run is partition_tokens tokens (a multiple of block_size).
- * A sequence cut into several runs is merged in the same launch by the
- * worker that finishes last (log-sum-exp merge of the partial results, in a
- * fixed order, so results are bitwise reproducible).
+ * lets the library size the runs from the device's compute-unit count (four
+ * times finer when some sequence starts with the same physical block as the
+ * one before it, so candidates sharing a prompt's blocks are read at the same
+ * time); otherwise each run is partition_tokens tokens (a multiple of
+ * block_size).  A sequence cut into several runs is merged in the same launch
+ * by the worker that finishes last (log-sum-exp merge of the partial results,
+ * in a fixed order, so results are bitwise reproducible).  Query groups
+ * (num_q_heads > num_kv_heads) with a 16-bit operand type (bf16 or f16
+ * queries) and block_size >= 16 run on the matrix cores; the environment
+ * variable PAGEDKV_DECODE_MFMA=0 keeps them on the vector ALUs.
  *
  * When partition_tokens is given and the batch would need more than 65528
  * runs, the runs are lengthened to the smallest whole number of blocks that
@@ -200,6 +205,37 @@ kv_status_t paged_attention_workspace_size(const kv_pool_t* pool, int32_t num_se
  * num_pairs == 0 enqueues nothing.
  */
 kv_status_t copy_blocks(kv_pool_t* pool, const int32_t* pairs, int32_t num_pairs, void* stream);
+
+typedef enum {
+  KV_SWAP_OUT = 0,  /* pool block src -> host block dst */
+  KV_SWAP_IN = 1    /* host block src -> pool block dst */
+} kv_swap_dir_t;
+
+/*
+ * swap_blocks -- move whole blocks between the pool and a host swap area, for
+ * offloading a preempted sequence's KV to CPU memory and bringing it back
+ * ("vLLM KV Cache 实现机制" §2.1 storage tiers and §3.3 RECOMPUTE vs offload
+ * table; "vLLM — 把操作系统的分页搬进 GPU KV cache", case 3: SWAP copies
+ * blocks to CPU memory and back over the host link).  All pairs move in one
+ * launch: the device reads and writes the host memory directly.
+ *
+ *   host_k, host_v   host memory the device can access: pinned memory from
+ *                    hipHostMalloc (or a framework's pinned allocator); each
+ *                    holds num_host_blocks blocks in the pool's layout
+ *                    ([num_host_blocks][num_kv_heads][block_size][head_dim] of
+ *                    the pool dtype, 16-byte aligned).  Memory that is not
+ *                    pinned or not mapped for the pool's device is rejected
+ *                    with KV_ERR_INVALID_ARG.
+ *   pairs            device int32 [num_pairs][2] (src, dst).  KV_SWAP_OUT
+ *                    copies pool block src to host block dst; KV_SWAP_IN
+ *                    copies host block src to pool block dst.  Pairs with an
+ *                    id outside its side's range are skipped.  Preconditions:
+ *                    destinations distinct.
+ * num_pairs == 0 enqueues nothing.  The host memory must stay alive and
+ * untouched by the CPU until the stream work has finished.
+ */
+kv_status_t swap_blocks(kv_pool_t* pool, void* host_k, void* host_v, int64_t num_host_blocks, const int32_t* pairs,
+                        int32_t num_pairs, kv_swap_dir_t direction, void* stream);
 
 /* kv_status_string -- static description of a status code. */
 const char* kv_status_string(kv_status_t status);

@@ -67,6 +67,8 @@ def lib() -> ctypes.CDLL:
         L.oracle_decode.argtypes = [vp, vp, i32, i64, i32, i32, i32, f64, f64, vp, i32, i32, i32,
                                     vp, i32, vp, f64, vp, i32, vp]
         L.oracle_decode.restype = i32
+        L.oracle_swap_blocks.argtypes = [vp, vp, i64, vp, vp, i64, i64, vp, i64, i32]
+        L.oracle_swap_blocks.restype = i32
         L.oracle_kv_footprint_bytes.argtypes = [i32, i32, i32, i64, i32]
         L.oracle_kv_footprint_bytes.restype = f64
         _lib = L
@@ -149,6 +151,17 @@ class HostPool:
                                      _ptr(pairs), pairs.shape[0])
         if rc:
             raise OracleError(f"oracle_copy_blocks rc={rc}")
+
+    def swap(self, host_k: np.ndarray, host_v: np.ndarray, pairs: np.ndarray, out: bool) -> None:
+        """Move whole blocks to (out) or from a host swap area held as uint8
+        arrays of host_blocks * block_bytes each."""
+        pairs = np.ascontiguousarray(np.asarray(pairs, dtype=np.int32).reshape(-1, 2))
+        assert host_k.dtype == np.uint8 and host_k.size % self.block_bytes == 0 and host_k.size == host_v.size
+        rc = lib().oracle_swap_blocks(_ptr(self.k), _ptr(self.v), self.num_blocks, _ptr(host_k), _ptr(host_v),
+                                     host_k.size // self.block_bytes, self.block_bytes, _ptr(pairs), pairs.shape[0],
+                                     1 if out else 0)
+        if rc:
+            raise OracleError(f"oracle_swap_blocks rc={rc}")
 
     def decode(self, q, q_dtype: str, block_tables: np.ndarray, context_lens: np.ndarray, scale: float,
                num_q_heads: int, seqs: Optional[Sequence[int]] = None) -> np.ndarray:

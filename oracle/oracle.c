@@ -207,6 +207,28 @@ int oracle_copy_blocks(void* kpool, void* vpool, int64_t block_bytes, int64_t nu
   return OR_OK;
 }
 
+/* Move whole blocks between the pool and a host swap area (offload / SWAP
+ * preemption: page "vLLM KV Cache 实现机制" §2.1 storage tiers; page "vLLM —
+ * 把操作系统的分页搬进 GPU KV cache", case 3).  out != 0: pool block src ->
+ * host block dst; out == 0: host block src -> pool block dst.  Ids out of
+ * range are an error here (the oracle is strict). */
+int oracle_swap_blocks(void* kpool, void* vpool, int64_t num_blocks, void* khost, void* vhost, int64_t host_blocks,
+                       int64_t block_bytes, const int32_t* pairs, int64_t P, int out) {
+  if (!kpool || !vpool || !khost || !vhost || (P > 0 && !pairs)) return OR_BAD_ARG;
+  for (int64_t i = 0; i < P; ++i) {
+    int64_t s = pairs[2 * i], d = pairs[2 * i + 1];
+    int64_t sn = out ? num_blocks : host_blocks, dn = out ? host_blocks : num_blocks;
+    if (s < 0 || d < 0 || s >= sn || d >= dn) return OR_BAD_BLOCK;
+    char* sk = (char*)(out ? kpool : khost) + s * block_bytes;
+    char* sv = (char*)(out ? vpool : vhost) + s * block_bytes;
+    char* dk = (char*)(out ? khost : kpool) + d * block_bytes;
+    char* dv = (char*)(out ? vhost : vpool) + d * block_bytes;
+    memcpy(dk, sk, (size_t)block_bytes);
+    memcpy(dv, sv, (size_t)block_bytes);
+  }
+  return OR_OK;
+}
+
 /* ------------------------------------------------------------------ decode */
 
 /*

@@ -10,6 +10,7 @@ library is missing or fails to load, every call raises.
     reshape_and_cache(pool, k_new, v_new, slot_mapping)
     copy_blocks(pool, pairs)
     out = paged_attention_decode(pool, q, block_tables, context_lens, scale)
+    swap_blocks(pool, HostSwapArea(pool, n), pairs, KV_SWAP_OUT)
 """
 from __future__ import annotations
 
@@ -26,6 +27,7 @@ LIB_PATH = os.path.join(_HERE, "libpagedkv.so")
 
 KV_OK, KV_ERR_INVALID_ARG, KV_ERR_UNSUPPORTED, KV_ERR_OOM, KV_ERR_HIP, KV_ERR_WORKSPACE = range(6)
 KV_F32, KV_F16, KV_BF16, KV_FP8_E4M3FN = range(4)
+KV_SWAP_OUT, KV_SWAP_IN = range(2)
 
 DTYPE_CODE = {torch.float32: KV_F32, torch.float16: KV_F16, torch.bfloat16: KV_BF16,
               torch.float8_e4m3fn: KV_FP8_E4M3FN}
@@ -57,10 +59,12 @@ def lib() -> ctypes.CDLL:
         L.paged_attention_decode.argtypes = [vp, vp, ctypes.c_int, vp, vp, i32, vp, i32, i32, f32, i32, vp, sz, vp]
         L.paged_attention_workspace_size.argtypes = [vp, i32, i32, i32, i32, ctypes.POINTER(sz)]
         L.copy_blocks.argtypes = [vp, vp, i32, vp]
+        L.swap_blocks.argtypes = [vp, vp, vp, i64, vp, i32, ctypes.c_int, vp]
         L.kv_status_string.argtypes = [ctypes.c_int]
         L.kv_status_string.restype = ctypes.c_char_p
         for fn in ("kv_pool_create", "kv_pool_create_from", "kv_pool_destroy", "kv_pool_info", "kv_pool_set_scales",
-                   "reshape_and_cache", "paged_attention_decode", "paged_attention_workspace_size", "copy_blocks"):
+                   "reshape_and_cache", "paged_attention_decode", "paged_attention_workspace_size", "copy_blocks",
+                   "swap_blocks"):
             getattr(L, fn).restype = ctypes.c_int
         _lib_handle = L
     return _lib_handle
@@ -195,6 +199,32 @@ def copy_blocks(pool: KVPool, pairs: torch.Tensor, stream=None) -> None:
     d = pool.device
     _check(lib().copy_blocks(pool.handle, _dev_ptr(pairs, "pairs", d), pairs.shape[0], _stream(d, stream)),
            "copy_blocks")
+
+
+class HostSwapArea:
+    """Pinned host memory for swapped-out blocks: K and V, each
+    [num_blocks][num_kv_heads][block_size][head_dim] of the pool dtype."""
+
+    def __init__(self, pool: KVPool, num_blocks: int):
+        shape = (num_blocks, pool.num_kv_heads, pool.block_size, pool.head_dim)
+        self.num_blocks = num_blocks
+        self.k_cache = torch.empty(shape, dtype=pool.dtype, pin_memory=True)
+        self.v_cache = torch.empty(shape, dtype=pool.dtype, pin_memory=True)
+
+
+def swap_blocks(pool: KVPool, area: HostSwapArea, pairs: torch.Tensor, direction: int, stream=None) -> None:
+    """KV_SWAP_OUT: pool block src -> host block dst; KV_SWAP_IN: host block src
+    -> pool block dst, for each (src, dst) row of pairs (device int32 [P][2])."""
+    if pairs.dtype != torch.int32 or pairs.dim() != 2 or pairs.shape[1] != 2:
+        raise ValueError("pairs must be int32 [P][2]")
+    if area.k_cache.dtype != pool.dtype or area.k_cache.shape[1:] != pool.k_cache.shape[1:]:
+        raise ValueError("swap area and pool disagree on the block layout")
+    if pairs.shape[0] == 0:
+        return
+    d = pool.device
+    _check(lib().swap_blocks(pool.handle, area.k_cache.data_ptr(), area.v_cache.data_ptr(), area.num_blocks,
+                             _dev_ptr(pairs, "pairs", d), pairs.shape[0], int(direction), _stream(d, stream)),
+           "swap_blocks")
 
 
 def paged_attention_workspace_size(pool: KVPool, num_seqs: int, num_q_heads: int, max_blocks: int,

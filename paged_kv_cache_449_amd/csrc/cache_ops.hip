@@ -142,7 +142,95 @@ __global__ __launch_bounds__(256) void copy_blocks_kernel(CopyParams p) {
   }
 }
 
+// ------------------------------------------------------------ swap copies
+
+struct SwapParams {
+  uint8_t* dev_k;
+  uint8_t* dev_v;
+  uint8_t* host_k;        // device-accessible addresses of the host buffers
+  uint8_t* host_v;
+  const int32_t* pairs;
+  int32_t num_pairs;
+  int32_t dev_blocks;
+  int64_t host_blocks;
+  int64_t block_bytes;
+  int32_t parts;
+  int32_t out;            // 1: device -> host, 0: host -> device
+};
+
+// Same shape as copy_blocks_kernel; one side of every copy is host memory the
+// device reads or writes over the host link.
+__global__ __launch_bounds__(256) void swap_blocks_kernel(SwapParams p) {
+  const int part = blockIdx.x % p.parts;
+  const int rest = blockIdx.x / p.parts;
+  const int pool = rest & 1;
+  const int pair = rest >> 1;
+  const int32_t src = p.pairs[2 * pair];
+  const int32_t dst = p.pairs[2 * pair + 1];
+  const int64_t src_n = p.out ? p.dev_blocks : p.host_blocks;
+  const int64_t dst_n = p.out ? p.host_blocks : p.dev_blocks;
+  if (src < 0 || src >= src_n || dst < 0 || dst >= dst_n) return;
+  uint8_t* dev = pool ? p.dev_v : p.dev_k;
+  uint8_t* host = pool ? p.host_v : p.host_k;
+  uint8_t* sbase = p.out ? dev : host;
+  uint8_t* dbase = p.out ? host : dev;
+  const int64_t share = ((p.block_bytes / 16 + p.parts - 1) / p.parts) * 16;
+  const int64_t lo = (int64_t)part * share;
+  if (lo >= p.block_bytes) return;
+  const int n = (int)(lo + share < p.block_bytes ? share : p.block_bytes - lo);
+  __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(sbase + (int64_t)src * p.block_bytes + lo), (short)0, n, kBufWord3);
+  __amdgpu_buffer_rsrc_t rd =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(dbase + (int64_t)dst * p.block_bytes + lo), (short)0, n, kBufWord3);
+  for (int i = threadIdx.x * 16; i < n; i += 256 * 16 * kCopyUnroll) {
+    u32x4 t[kCopyUnroll];
+#pragma unroll
+    for (int u = 0; u < kCopyUnroll; ++u)
+      t[u] = __builtin_amdgcn_raw_buffer_load_b128(rs, i + u * 256 * 16, 0, kNonTemporal);
+#pragma unroll
+    for (int u = 0; u < kCopyUnroll; ++u)
+      __builtin_amdgcn_raw_buffer_store_b128(t[u], rd, i + u * 256 * 16, 0, kNonTemporal);
+  }
+}
+
 }  // namespace
+
+extern "C" kv_status_t swap_blocks(kv_pool_t* pool, void* host_k, void* host_v, int64_t num_host_blocks,
+                                   const int32_t* pairs, int32_t num_pairs, kv_swap_dir_t direction, void* stream) {
+  if (!pool || num_pairs < 0 || num_host_blocks < 0) return KV_ERR_INVALID_ARG;
+  if (direction != KV_SWAP_OUT && direction != KV_SWAP_IN) return KV_ERR_INVALID_ARG;
+  if (num_pairs == 0) return KV_OK;
+  if (!pairs || !host_k || !host_v || num_host_blocks == 0) return KV_ERR_INVALID_ARG;
+  if (((uintptr_t)host_k | (uintptr_t)host_v) & 15) return KV_ERR_INVALID_ARG;
+  SwapParams p;
+  p.block_bytes = (int64_t)pool->num_kv_heads * pool->block_size * pool->head_dim * elem_bytes(pool->dtype);
+  if (p.block_bytes % 16 || p.block_bytes >= (1LL << 31)) return KV_ERR_UNSUPPORTED;
+  if (num_host_blocks > (INT64_MAX / p.block_bytes)) return KV_ERR_INVALID_ARG;
+  // the host buffers must be pinned memory mapped for this device (a failed
+  // lookup's error is cleared so it does not surface at a later launch)
+  void* hk = nullptr;
+  void* hv = nullptr;
+  if (hipHostGetDevicePointer(&hk, host_k, 0) != hipSuccess || !hk ||
+      hipHostGetDevicePointer(&hv, host_v, 0) != hipSuccess || !hv) {
+    (void)hipGetLastError();
+    return KV_ERR_INVALID_ARG;
+  }
+  p.dev_k = (uint8_t*)pool->k;
+  p.dev_v = (uint8_t*)pool->v;
+  p.host_k = (uint8_t*)hk;
+  p.host_v = (uint8_t*)hv;
+  p.pairs = pairs;
+  p.num_pairs = num_pairs;
+  p.dev_blocks = pool->num_blocks;
+  p.host_blocks = num_host_blocks;
+  p.out = direction == KV_SWAP_OUT ? 1 : 0;
+  int64_t parts = (p.block_bytes + 16383) / 16384;
+  p.parts = (int32_t)(parts < 1 ? 1 : parts);
+  const int64_t grid = (int64_t)num_pairs * 2 * p.parts;
+  if (grid > 0x7fffffff) return KV_ERR_INVALID_ARG;
+  hipLaunchKernelGGL(swap_blocks_kernel, dim3(grid), dim3(256), 0, (hipStream_t)stream, p);
+  return launch_status();
+}
 
 extern "C" kv_status_t reshape_and_cache(kv_pool_t* pool, const void* k_new, const void* v_new, kv_dtype_t src_dtype,
                                          const int64_t* slot_mapping, int32_t num_tokens, void* stream) {

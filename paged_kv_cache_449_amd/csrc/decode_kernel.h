@@ -525,7 +525,7 @@ __device__ inline void decode_chunk(const DecodeParams& p, int v, int chunk, int
 // One worker wavefront per work-group.  MFMA selects the matrix-core run
 // (query groups with a 16-bit operand type) over the vector-ALU run.
 template <typename KV, typename QT, int D, int G, bool MFMA>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(MFMA ? 2 : 1)))
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(MFMA && D <= 128 ? 2 : 1)))
 void paged_decode_kernel(const DecodeParams p) {
   const int lane = threadIdx.x;
   const int S = p.num_seqs;

@@ -28,9 +28,9 @@ def _declared_functions():
 
 def test_header_declares_the_four_calls_and_helpers():
     names = _declared_functions()
-    for n in ["kv_pool_create", "reshape_and_cache", "paged_attention_decode", "copy_blocks"]:
+    for n in ["kv_pool_create", "reshape_and_cache", "paged_attention_decode", "copy_blocks", "swap_blocks"]:
         assert n in names
-    assert len(names) == 10, names
+    assert len(names) == 11, names
 
 
 def test_library_exports_every_declared_symbol():
@@ -61,6 +61,7 @@ def test_null_and_shape_arguments_rejected_on_host():
         pk.KV_ERR_INVALID_ARG
     assert L.reshape_and_cache(None, None, None, pk.KV_F16, None, 4, None) == pk.KV_ERR_INVALID_ARG
     assert L.copy_blocks(None, None, 3, None) == pk.KV_ERR_INVALID_ARG
+    assert L.swap_blocks(None, None, None, 4, None, 3, 0, None) == pk.KV_ERR_INVALID_ARG
     n = ctypes.c_size_t()
     assert L.paged_attention_workspace_size(None, 4, 4, 4, 0, ctypes.byref(n)) == pk.KV_ERR_INVALID_ARG
     assert L.kv_pool_destroy(None) == pk.KV_OK

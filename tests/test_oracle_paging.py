@@ -213,3 +213,54 @@ def test_footprint_matches_pool_bytes_per_token():
     wl = W.config_c2()
     pool_block_bytes = wl.num_kv_heads * wl.block_size * wl.head_dim * 2
     assert 2 * pool_block_bytes / wl.block_size == oracle.kv_footprint_bytes(1, 40, 128, 1, 2) == 20480
+
+
+def test_swap_out_and_in_moves_whole_blocks():
+    """Swap out copies pool blocks to the named host blocks, swap in copies
+    host blocks back to the named pool blocks; nothing else changes.  Checked
+    against numpy block slicing of the same bytes."""
+    pool = oracle.HostPool(6, 16, 2, 64, "bf16", fill=0)
+    rng = np.random.default_rng(3)
+    pool.k[:] = rng.integers(0, 255, pool.k.shape, dtype=np.uint8)
+    pool.v[:] = rng.integers(0, 255, pool.v.shape, dtype=np.uint8)
+    bb = pool.block_bytes
+    hk = np.zeros(4 * bb, np.uint8)
+    hv = np.zeros(4 * bb, np.uint8)
+    k0, v0 = pool.k.copy(), pool.v.copy()
+    pool.swap(hk, hv, np.array([[5, 0], [1, 3]], np.int32), out=True)
+    assert np.array_equal(hk.reshape(4, bb)[0], k0.reshape(6, bb)[5])
+    assert np.array_equal(hv.reshape(4, bb)[3], v0.reshape(6, bb)[1])
+    assert not hk.reshape(4, bb)[1].any() and not hk.reshape(4, bb)[2].any()
+    assert np.array_equal(pool.k, k0) and np.array_equal(pool.v, v0)
+    # bring host block 3 back into pool block 2 and host block 0 into pool block 4
+    pool.swap(hk, hv, np.array([[3, 2], [0, 4]], np.int32), out=False)
+    K, K0 = pool.k.reshape(6, bb), k0.reshape(6, bb)
+    V, V0 = pool.v.reshape(6, bb), v0.reshape(6, bb)
+    assert np.array_equal(K[2], K0[1]) and np.array_equal(V[2], V0[1])
+    assert np.array_equal(K[4], K0[5]) and np.array_equal(V[4], V0[5])
+    for b in (0, 1, 3, 5):
+        assert np.array_equal(K[b], K0[b]) and np.array_equal(V[b], V0[b])
+    with pytest.raises(oracle.OracleError):
+        pool.swap(hk, hv, np.array([[0, 4]], np.int32), out=True)   # host has 4 blocks
+
+
+def test_swap_round_trip_restores_decode():
+    """Swapping a sequence's blocks out and back in to other physical blocks,
+    with its table rewritten, leaves its decode output bit-identical."""
+    wl = W.small_configs()["c2s_f16"]
+    run = OracleRun(wl)
+    base = run.decode()
+    s = int(np.argmin(wl.context_lens))
+    blocks = run.tables[s][run.tables[s] >= 0]
+    used = set(run.tables[run.tables >= 0].tolist())
+    free = [b for b in range(wl.num_blocks) if b not in used][:len(blocks)]
+    assert len(free) == len(blocks)
+    bb = run.pool.block_bytes
+    hk = np.zeros(len(blocks) * bb, np.uint8)
+    hv = np.zeros_like(hk)
+    run.pool.swap(hk, hv, np.stack([blocks, np.arange(len(blocks))], 1), out=True)
+    run.pool.swap(hk, hv, np.stack([np.arange(len(blocks)), free], 1), out=False)
+    tables = run.tables.copy()
+    tables[s, :len(blocks)] = free
+    got = run.pool.decode(run.q, wl.q_dtype, tables, wl.context_lens, wl.scale, wl.num_q_heads)
+    np.testing.assert_array_equal(got, base)
