@@ -61,7 +61,7 @@ def build_session(wl: W.Workload, device, prompt_batch: int = 16, free_order=Non
     for p in range(wl.num_prompts):
         sess.fork(("p", p), children.get(p, []))
         sess.free(("p", p))
-    sess.prepare_step([("s", s) for s in range(wl.num_seqs)])
+    sess.prepare_step([("s", s) for s in range(wl.num_seqs)], counts=wl.q_lens.tolist())
     q = W.q_values(wl).to(device)
     kn, vn = W.new_kv(wl)
     torch.cuda.synchronize(device)

@@ -193,6 +193,47 @@ kv_status_t paged_attention_workspace_size(const kv_pool_t* pool, int32_t num_se
                                            int32_t max_blocks, int32_t partition_tokens, size_t* bytes);
 
 /*
+ * paged_attention_prefill -- several new query tokens per sequence attend
+ * causally to the cached context through the block table: a chunk of a
+ * prompt being prefilled into the pool, or speculative tokens being verified
+ * ("vLLM — 把操作系统的分页搬进 GPU KV cache": related work (FlashAttention is
+ * the prefill twin of PagedAttention) and fit (speculative decoding on top);
+ * the paged read path is the decode one above).
+ *
+ *   q, out        device [total_q][num_q_heads][head_dim] of q_dtype.
+ *   query_start   device int32 [num_seqs + 1], nondecreasing, query_start[0]
+ *                 = 0: sequence s owns query rows [query_start[s],
+ *                 query_start[s+1]).  Its m_s new tokens are the last m_s of
+ *                 its context_lens[s] cached tokens (their K/V already stored
+ *                 with reshape_and_cache), so row i sits at position
+ *                 context_lens[s] - m_s + (i - query_start[s]).
+ * out[i][h] = sum_t softmax_t(scale * q[i][h] . K_t) V_t over t <= position
+ * of row i, kv head h / (num_q_heads / num_kv_heads); fp32 accumulation, the
+ * result rounded to nearest even into q_dtype.  Rows not owned by any
+ * sequence are not written; m_s is clamped to [0, context_lens[s]].
+ *
+ * Runs on the matrix cores: q_dtype bf16 with bf16 or fp8 pools, f16 with f16
+ * or fp8 pools; block_size >= 16; num_q_heads / num_kv_heads in {1, 2, 4, 8,
+ * 16} (other combinations: KV_ERR_UNSUPPORTED).  Work split as in decode: the
+ * (kv head, sequence, 16-row tile) runs are laid end to end and cut into
+ * equal chunks; cut runs are merged in the same launch.
+ *
+ * workspace: at least paged_attention_prefill_workspace_size() bytes,
+ * 256-byte aligned, with the same counter convention as decode (first 256 KiB
+ * zero before first use, left zero by every call); calls sharing a workspace
+ * must not overlap.
+ */
+kv_status_t paged_attention_prefill(const kv_pool_t* pool, const void* q, kv_dtype_t q_dtype, void* out,
+                                    const int32_t* block_tables, int32_t max_blocks, const int32_t* context_lens,
+                                    const int32_t* query_start, int32_t num_seqs, int32_t total_q,
+                                    int32_t num_q_heads, float scale, void* workspace, size_t workspace_bytes,
+                                    void* stream);
+
+/* paged_attention_prefill_workspace_size -- bytes of workspace the call above
+ * needs (depends on the pool's device and head_dim only). */
+kv_status_t paged_attention_prefill_workspace_size(const kv_pool_t* pool, int32_t num_q_heads, size_t* bytes);
+
+/*
  * copy_blocks -- copy-on-write support: for each pair (src, dst) copy the
  * whole physical block src onto dst in both pools (every head, every token
  * slot).  ("vLLM — 把操作系统的分页搬进 GPU KV cache": core mechanism 3, case 2

@@ -69,6 +69,9 @@ def lib() -> ctypes.CDLL:
         L.oracle_decode.restype = i32
         L.oracle_swap_blocks.argtypes = [vp, vp, i64, vp, vp, i64, i64, vp, i64, i32]
         L.oracle_swap_blocks.restype = i32
+        L.oracle_prefill.argtypes = [vp, vp, i32, i64, i32, i32, i32, f64, f64, vp, i32, i32, i32,
+                                     vp, i32, vp, vp, f64, vp]
+        L.oracle_prefill.restype = i32
         L.oracle_kv_footprint_bytes.argtypes = [i32, i32, i32, i64, i32]
         L.oracle_kv_footprint_bytes.restype = f64
         _lib = L
@@ -162,6 +165,26 @@ class HostPool:
                                      1 if out else 0)
         if rc:
             raise OracleError(f"oracle_swap_blocks rc={rc}")
+
+    def prefill(self, q, q_dtype: str, block_tables: np.ndarray, context_lens: np.ndarray,
+                query_start: np.ndarray, scale: float, num_q_heads: int) -> np.ndarray:
+        """Causal attention of each sequence's new query rows (the last
+        query_start[s+1] - query_start[s] of its context) over its paged
+        context; q [total_q][Hq][D] -> fp64 [total_q][Hq][D]."""
+        qr = _raw(q)
+        bt = np.ascontiguousarray(block_tables, dtype=np.int32)
+        cl = np.ascontiguousarray(context_lens, dtype=np.int32)
+        qs = np.ascontiguousarray(query_start, dtype=np.int32)
+        S, max_blocks = bt.shape
+        total_q = int(qs[-1])
+        out = np.full((total_q, num_q_heads, self.head_dim), np.nan, dtype=np.float64)
+        rc = lib().oracle_prefill(_ptr(self.k), _ptr(self.v), DT_CODE[self.dtype], self.num_blocks, self.block_size,
+                                  self.num_kv_heads, self.head_dim, self.k_scale, self.v_scale, _ptr(qr),
+                                  DT_CODE[q_dtype], S, num_q_heads, _ptr(bt), max_blocks, _ptr(cl), _ptr(qs),
+                                  float(scale), _ptr(out))
+        if rc:
+            raise OracleError(f"oracle_prefill rc={rc}")
+        return out
 
     def decode(self, q, q_dtype: str, block_tables: np.ndarray, context_lens: np.ndarray, scale: float,
                num_q_heads: int, seqs: Optional[Sequence[int]] = None) -> np.ndarray:

@@ -231,6 +231,51 @@ int oracle_swap_blocks(void* kpool, void* vpool, int64_t num_blocks, void* khost
 
 /* ------------------------------------------------------------------ decode */
 
+/* Contiguous K and V (fp64, dequantised) of the first n tokens of sequence s,
+ * KV head hk: token t lives at slot t % B of block block_tables[s][t / B]. */
+static int materialise_kv(const void* kpool, const void* vpool, int kv_dtype, int64_t num_blocks, int B, int H,
+                          int D, double k_scale, double v_scale, const int32_t* block_tables, int max_blocks,
+                          int s, int hk, int n, double* Kc, double* Vc) {
+  int fp8 = kv_dtype == OR_FP8E4M3;
+  for (int t = 0; t < n; ++t) {
+    int32_t blk = block_tables[(size_t)s * max_blocks + t / B];
+    int o = t % B;
+    if (blk < 0 || blk >= num_blocks) return OR_BAD_BLOCK;
+    size_t base = ((size_t)((int64_t)blk * H + hk) * B + o) * D;
+    for (int j = 0; j < D; ++j) {
+      double kv = load_elem(kpool, kv_dtype, base + j);
+      double vv = load_elem(vpool, kv_dtype, base + j);
+      Kc[(size_t)t * D + j] = fp8 ? kv * k_scale : kv;
+      Vc[(size_t)t * D + j] = fp8 ? vv * v_scale : vv;
+    }
+  }
+  return OR_OK;
+}
+
+/* Textbook softmax attention of one query row qd over tokens 0..nt-1:
+ * score_t = scale * <qd, Kc[t]>, m = max score, p_t = exp(score_t - m),
+ * l = sum p_t, o = sum_t p_t Vc[t] / l.  sc is scratch of nt doubles. */
+static void attend(const double* qd, const double* Kc, const double* Vc, int nt, int D, double scale, double* sc,
+                   double* o) {
+  double m = -INFINITY;
+  for (int t = 0; t < nt; ++t) {
+    double acc = 0.0;
+    for (int j = 0; j < D; ++j) acc += qd[j] * Kc[(size_t)t * D + j];
+    sc[t] = scale * acc;
+    if (sc[t] > m) m = sc[t];
+  }
+  double l = 0.0;
+  for (int t = 0; t < nt; ++t) {
+    sc[t] = exp(sc[t] - m);
+    l += sc[t];
+  }
+  for (int j = 0; j < D; ++j) {
+    double acc = 0.0;
+    for (int t = 0; t < nt; ++t) acc += sc[t] * Vc[(size_t)t * D + j];
+    o[j] = acc / l;
+  }
+}
+
 /*
  * out[s][hq][:] (fp64) for every sequence s listed in `seqs` (all when seqs
  * is NULL):
@@ -249,7 +294,6 @@ int oracle_decode(const void* kpool, const void* vpool, int kv_dtype, int64_t nu
   if (!kpool || !vpool || !q || !block_tables || !context_lens || !out) return OR_BAD_ARG;
   if (B <= 0 || H <= 0 || D <= 0 || Hq <= 0 || Hq % H != 0 || max_blocks <= 0) return OR_BAD_ARG;
   int g = Hq / H;
-  int fp8 = kv_dtype == OR_FP8E4M3;
   int count = seqs ? n_seqs : S;
   for (int si = 0; si < count; ++si) {
     int s = seqs ? seqs[si] : si;
@@ -260,43 +304,62 @@ int oracle_decode(const void* kpool, const void* vpool, int kv_dtype, int64_t nu
     double* Vc = (double*)malloc(sizeof(double) * (size_t)n * D);
     double* sc = (double*)malloc(sizeof(double) * (size_t)n);
     double* qd = (double*)malloc(sizeof(double) * (size_t)D);
-    if (!Kc || !Vc || !sc || !qd) { free(Kc); free(Vc); free(sc); free(qd); return OR_NOMEM; }
-    for (int hk = 0; hk < H; ++hk) {
-      /* 1. materialise the contiguous K/V of this (sequence, kv head) */
-      for (int t = 0; t < n; ++t) {
-        int32_t blk = block_tables[(size_t)s * max_blocks + t / B];
-        int o = t % B;
-        if (blk < 0 || blk >= num_blocks) { free(Kc); free(Vc); free(sc); free(qd); return OR_BAD_BLOCK; }
-        size_t base = ((size_t)((int64_t)blk * H + hk) * B + o) * D;
-        for (int j = 0; j < D; ++j) {
-          double kv = load_elem(kpool, kv_dtype, base + j);
-          double vv = load_elem(vpool, kv_dtype, base + j);
-          Kc[(size_t)t * D + j] = fp8 ? kv * k_scale : kv;
-          Vc[(size_t)t * D + j] = fp8 ? vv * v_scale : vv;
-        }
-      }
-      /* 2. textbook softmax attention for each query head of the group */
-      for (int gi = 0; gi < g; ++gi) {
+    int rc = (Kc && Vc && sc && qd) ? OR_OK : OR_NOMEM;
+    for (int hk = 0; hk < H && rc == OR_OK; ++hk) {
+      rc = materialise_kv(kpool, vpool, kv_dtype, num_blocks, B, H, D, k_scale, v_scale, block_tables,
+                          max_blocks, s, hk, n, Kc, Vc);
+      for (int gi = 0; gi < g && rc == OR_OK; ++gi) {
         int hq = hk * g + gi;
         size_t qoff = ((size_t)s * Hq + hq) * D;
         for (int j = 0; j < D; ++j) qd[j] = load_elem(q, q_dtype, qoff + j);
-        double m = -INFINITY;
-        for (int t = 0; t < n; ++t) {
-          double acc = 0.0;
-          for (int j = 0; j < D; ++j) acc += qd[j] * Kc[(size_t)t * D + j];
-          sc[t] = scale * acc;
-          if (sc[t] > m) m = sc[t];
-        }
-        double l = 0.0;
-        for (int t = 0; t < n; ++t) {
-          sc[t] = exp(sc[t] - m);
-          l += sc[t];
-        }
-        double* o = out + qoff;
-        for (int j = 0; j < D; ++j) {
-          double acc = 0.0;
-          for (int t = 0; t < n; ++t) acc += sc[t] * Vc[(size_t)t * D + j];
-          o[j] = acc / l;
+        attend(qd, Kc, Vc, n, D, scale, sc, out + qoff);
+      }
+    }
+    free(Kc);
+    free(Vc);
+    free(sc);
+    free(qd);
+    if (rc != OR_OK) return rc;
+  }
+  return OR_OK;
+}
+
+/*
+ * Several new query tokens per sequence attending causally to the paged
+ * context (chunked prefill / verification of speculative tokens).  Sequence
+ * s owns query rows [query_start[s], query_start[s+1]); its m new tokens are
+ * the last m of its n = context_lens[s] cached tokens, so query row i sits at
+ * position n - m + (i - query_start[s]) and attends to tokens 0..position.
+ * Per (row, query head) the result is the decode formula above restricted to
+ * those tokens.  q and out are [total_q][Hq][D]; out is fp64.
+ */
+int oracle_prefill(const void* kpool, const void* vpool, int kv_dtype, int64_t num_blocks, int B, int H, int D,
+                   double k_scale, double v_scale, const void* q, int q_dtype, int S, int Hq,
+                   const int32_t* block_tables, int max_blocks, const int32_t* context_lens,
+                   const int32_t* query_start, double scale, double* out) {
+  if (!kpool || !vpool || !q || !block_tables || !context_lens || !query_start || !out) return OR_BAD_ARG;
+  if (B <= 0 || H <= 0 || D <= 0 || Hq <= 0 || Hq % H != 0 || max_blocks <= 0) return OR_BAD_ARG;
+  int g = Hq / H;
+  for (int s = 0; s < S; ++s) {
+    int n = context_lens[s];
+    int q0 = query_start[s], m = query_start[s + 1] - q0;
+    if (m < 0 || m > n || n < 1 || (int64_t)n > (int64_t)max_blocks * B) return OR_BAD_LEN;
+    if (m == 0) continue;
+    double* Kc = (double*)malloc(sizeof(double) * (size_t)n * D);
+    double* Vc = (double*)malloc(sizeof(double) * (size_t)n * D);
+    double* sc = (double*)malloc(sizeof(double) * (size_t)n);
+    double* qd = (double*)malloc(sizeof(double) * (size_t)D);
+    int rc = (Kc && Vc && sc && qd) ? OR_OK : OR_NOMEM;
+    for (int hk = 0; hk < H && rc == OR_OK; ++hk) {
+      rc = materialise_kv(kpool, vpool, kv_dtype, num_blocks, B, H, D, k_scale, v_scale, block_tables,
+                          max_blocks, s, hk, n, Kc, Vc);
+      for (int i = 0; i < m && rc == OR_OK; ++i) {
+        int seen = n - m + i + 1;
+        for (int gi = 0; gi < g; ++gi) {
+          int hq = hk * g + gi;
+          size_t qoff = ((size_t)(q0 + i) * Hq + hq) * D;
+          for (int j = 0; j < D; ++j) qd[j] = load_elem(q, q_dtype, qoff + j);
+          attend(qd, Kc, Vc, seen, D, scale, sc, out + qoff);
         }
       }
     }
@@ -304,6 +367,7 @@ int oracle_decode(const void* kpool, const void* vpool, int kv_dtype, int64_t nu
     free(Vc);
     free(sc);
     free(qd);
+    if (rc != OR_OK) return rc;
   }
   return OR_OK;
 }

@@ -23,7 +23,7 @@ Procedure (the harness's fixed choice where the pages leave an order open):
      logical block takes the next block from the front of the free list.
   2. Every candidate of a prompt starts with a copy of the prompt's table; each
      prompt block's reference count is the number of candidates.
-  3. The decode step appends one token per sequence, in sequence order.  If
+  3. The step appends each sequence's new tokens, in sequence order.  If
      the position starts a new logical block a fresh block is taken.  Else if
      the last block is shared (count > 1) a fresh block is taken, the pair
      (shared, fresh) is recorded for copying, the shared count drops by one and
@@ -71,7 +71,7 @@ def plan(wl, free_order) -> dict:
     Returns a dict with
       prompt_slots: list over prompts of int64 arrays (slot of each cached token)
       tables:       int32 [S][max_blocks], -1 where unused
-      new_slots:    int64 [S], slot of the token each sequence appends
+      new_slots:    int64 [total_q], slots of the tokens the sequences append (sequence order)
       pairs:        int32 [P][2] (src, dst) blocks to copy before the append
       refcount:     dict block -> count after the step
       free_left:    number of blocks still free
@@ -100,21 +100,25 @@ def plan(wl, free_order) -> dict:
             for b in table:
                 em.give_back(b)
 
-    new_slots = np.empty(wl.num_seqs, dtype=np.int64)
+    qn = wl.q_lens
+    new_slots = np.empty(int(qn.sum()), dtype=np.int64)
     pairs = []
+    i = 0
     for s, p in enumerate(wl.parent):
-        pos = wl.prompt_lens[p]
         table = seq_tables[s]
-        if pos % bs == 0:
-            table.append(em.take())
-        else:
-            last = table[-1]
-            if em.refcount[last] > 1:
-                fresh = em.take()
-                pairs.append((last, fresh))
-                em.refcount[last] -= 1
-                table[-1] = fresh
-        new_slots[s] = em.slot(table, pos)
+        for k in range(int(qn[s])):
+            pos = wl.prompt_lens[p] + k
+            if pos % bs == 0:
+                table.append(em.take())
+            else:
+                last = table[-1]
+                if em.refcount[last] > 1:
+                    fresh = em.take()
+                    pairs.append((last, fresh))
+                    em.refcount[last] -= 1
+                    table[-1] = fresh
+            new_slots[i] = em.slot(table, pos)
+            i += 1
 
     max_blocks = max(len(t) for t in seq_tables)
     tables = np.full((wl.num_seqs, max(max_blocks, 1)), -1, dtype=np.int32)

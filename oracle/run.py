@@ -43,7 +43,7 @@ class OracleRun:
         kn, vn = workloads.new_kv(wl)
         slots = self.plan["new_slots"]
         if prompts is not None:
-            keep = np.isin(np.asarray(wl.parent), np.asarray(list(prompts)))
+            keep = np.isin(np.repeat(np.asarray(wl.parent), wl.q_lens), np.asarray(list(prompts)))
             slots = np.where(keep, slots, -1)
         self.pool.reshape_and_cache(kn, vn, wl.src_dtype, slots)
         self.q = workloads.q_values(wl)
@@ -55,6 +55,36 @@ class OracleRun:
     def decode(self, seqs: Optional[Sequence[int]] = None) -> np.ndarray:
         wl = self.wl
         return self.pool.decode(self.q, wl.q_dtype, self.tables, wl.context_lens, wl.scale, wl.num_q_heads, seqs)
+
+    def prefill(self, seqs: Optional[Sequence[int]] = None) -> np.ndarray:
+        """Causal attention of every sequence's new tokens ([total_q][Hq][D]);
+        with `seqs`, only those sequences' rows are computed (others NaN)."""
+        wl = self.wl
+        qs = wl.query_start
+        if seqs is None:
+            return self.pool.prefill(self.q, wl.q_dtype, self.tables, wl.context_lens, qs, wl.scale, wl.num_q_heads)
+        sel = sorted(seqs)
+        sub_qs = np.concatenate([[0], np.cumsum([qs[s + 1] - qs[s] for s in sel])]).astype(np.int32)
+        rows = np.concatenate([np.arange(qs[s], qs[s + 1]) for s in sel])
+        q = self.q[torch.as_tensor(rows, dtype=torch.long)].contiguous()
+        got = self.pool.prefill(q, wl.q_dtype, self.tables[sel], wl.context_lens[sel], sub_qs, wl.scale,
+                                wl.num_q_heads)
+        out = np.full((wl.total_q, wl.num_q_heads, wl.head_dim), np.nan)
+        out[rows] = got
+        return out
+
+    def prefill_rows(self, s: int, a: int, b: int) -> np.ndarray:
+        """Rows a..b-1 of sequence s's new tokens ([b - a][Hq][D]).  Row i
+        sits at position n - m + i and sees only the tokens up to it, so the
+        rows are those of a call whose context ends at row b - 1."""
+        wl = self.wl
+        qs = wl.query_start
+        n, m = int(wl.context_lens[s]), int(qs[s + 1] - qs[s])
+        assert 0 <= a < b <= m
+        q = self.q[int(qs[s]) + a:int(qs[s]) + b].contiguous()
+        ctx = np.array([n - m + b], dtype=np.int32)
+        return self.pool.prefill(q, wl.q_dtype, self.tables[s:s + 1], ctx, np.array([0, b - a], dtype=np.int32),
+                                 wl.scale, wl.num_q_heads)
 
 
 def tolerance(kv_dtype: str):

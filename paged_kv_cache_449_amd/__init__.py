@@ -60,11 +60,14 @@ def lib() -> ctypes.CDLL:
         L.paged_attention_workspace_size.argtypes = [vp, i32, i32, i32, i32, ctypes.POINTER(sz)]
         L.copy_blocks.argtypes = [vp, vp, i32, vp]
         L.swap_blocks.argtypes = [vp, vp, vp, i64, vp, i32, ctypes.c_int, vp]
+        L.paged_attention_prefill.argtypes = [vp, vp, ctypes.c_int, vp, vp, i32, vp, vp, i32, i32, i32, f32, vp,
+                                              sz, vp]
+        L.paged_attention_prefill_workspace_size.argtypes = [vp, i32, ctypes.POINTER(sz)]
         L.kv_status_string.argtypes = [ctypes.c_int]
         L.kv_status_string.restype = ctypes.c_char_p
         for fn in ("kv_pool_create", "kv_pool_create_from", "kv_pool_destroy", "kv_pool_info", "kv_pool_set_scales",
                    "reshape_and_cache", "paged_attention_decode", "paged_attention_workspace_size", "copy_blocks",
-                   "swap_blocks"):
+                   "swap_blocks", "paged_attention_prefill", "paged_attention_prefill_workspace_size"):
             getattr(L, fn).restype = ctypes.c_int
         _lib_handle = L
     return _lib_handle
@@ -233,6 +236,42 @@ def paged_attention_workspace_size(pool: KVPool, num_seqs: int, num_q_heads: int
     _check(lib().paged_attention_workspace_size(pool.handle, num_seqs, num_q_heads, max_blocks, partition_tokens,
                                                 ctypes.byref(n)), "paged_attention_workspace_size")
     return n.value
+
+
+def paged_attention_prefill(pool: KVPool, q: torch.Tensor, block_tables: torch.Tensor, context_lens: torch.Tensor,
+                            query_start: torch.Tensor, scale: float, out: Optional[torch.Tensor] = None,
+                            workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Causal attention of each sequence's new query rows q [total_q][Hq][D]
+    (sequence s owns rows query_start[s]:query_start[s+1], the last tokens of
+    its context) over its paged context."""
+    if q.dim() != 3 or q.shape[2] != pool.head_dim or q.dtype not in DTYPE_CODE:
+        raise ValueError(f"q must be [total_q][Hq][{pool.head_dim}] of a supported dtype")
+    S = block_tables.shape[0]
+    if block_tables.dtype != torch.int32 or block_tables.dim() != 2:
+        raise ValueError("block_tables must be int32 [S][max_blocks]")
+    if context_lens.dtype != torch.int32 or context_lens.shape != (S,):
+        raise ValueError("context_lens must be int32 [S]")
+    if query_start.dtype != torch.int32 or query_start.shape != (S + 1,):
+        raise ValueError("query_start must be int32 [S + 1]")
+    total_q, Hq = q.shape[0], q.shape[1]
+    if out is None:
+        out = torch.empty_like(q)
+    elif out.shape != q.shape or out.dtype != q.dtype:
+        raise ValueError("out must match q")
+    n = ctypes.c_size_t()
+    _check(lib().paged_attention_prefill_workspace_size(pool.handle, Hq, ctypes.byref(n)),
+           "paged_attention_prefill_workspace_size")
+    if workspace is None:
+        workspace = pool.workspace(n.value)
+    d = pool.device
+    _check(lib().paged_attention_prefill(pool.handle, _dev_ptr(q, "q", d), DTYPE_CODE[q.dtype], _dev_ptr(out, "out", d),
+                                         _dev_ptr(block_tables, "block_tables", d), block_tables.shape[1],
+                                         _dev_ptr(context_lens, "context_lens", d),
+                                         _dev_ptr(query_start, "query_start", d), S, total_q, Hq, float(scale),
+                                         _dev_ptr(workspace, "workspace", d),
+                                         workspace.numel() * workspace.element_size(), _stream(d, stream)),
+           "paged_attention_prefill")
+    return out
 
 
 def paged_attention_decode(pool: KVPool, q: torch.Tensor, block_tables: torch.Tensor, context_lens: torch.Tensor,

@@ -187,6 +187,12 @@ __device__ inline int wave_sum_i32(int v) {
   return v;
 }
 
+__device__ inline int64_t wave_sum_i64(int64_t v) {
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
 __device__ inline int wave_inclusive_scan_i32(int v, int lane) {
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {

@@ -104,6 +104,8 @@ extern "C" kv_status_t paged_attention_decode(const kv_pool_t* pool, const void*
   p.out = (uint8_t*)out;
   p.block_tables = block_tables;
   p.context_lens = context_lens;
+  p.query_start = nullptr;
+  p.total_q = 0;
   p.counters = (int32_t*)workspace;
   p.partials = (float*)((uint8_t*)workspace + plan.counters_bytes);
   p.num_seqs = num_seqs;

@@ -59,9 +59,11 @@ struct DecodeParams {
   uint8_t* out;
   const int32_t* block_tables;
   const int32_t* context_lens;
+  const int32_t* query_start;  // multi-token attention: [num_seqs + 1] query row offsets
   int32_t* counters;     // [kCounterSlots], zero between calls
   float* partials;       // [2 * num_workers][G][head_dim + 4]
   int32_t num_seqs;
+  int32_t total_q;       // multi-token attention: rows of q and out
   int32_t num_kv_heads;
   int32_t max_blocks;
   int32_t num_blocks;
@@ -290,19 +292,29 @@ __device__ inline bool arrive(const DecodeParams& p, int first_w, int last_w) {
   return done == last_w - first_w;
 }
 
+// Output rows of a run's records: record row j -> element offset of its out
+// row (-1: the row holds no query).
+struct ContiguousRows {   // G query heads of one sequence: rows orow + j*D
+  int64_t orow;
+  int d;
+  __device__ int64_t operator()(int j) const { return orow + (int64_t)j * d; }
+};
+
 // Merge the records of workers first_w..last_w (in worker order, so results
-// are reproducible) into out rows oe .. oe + G*D (elements), then clear the
-// run's counter for the next call.  seg_start is the run's first position in
-// the flattened stream.  Each lane owns 4 consecutive elements of [G][D] per
+// are reproducible) into the out rows that `rows` names, then clear the run's
+// counter for the next call.  seg_start is the run's first position in the
+// flattened stream.  Each lane owns 4 consecutive elements of [G][D] per
 // pass.
-template <typename QT, int D, int G>
+template <typename QT, int D, int G, typename Rows>
 __device__ inline void merge_records(const DecodeParams& p, int first_w, int last_w, int seg_start, int chunk,
-                                     int64_t oe) {
+                                     const Rows& rows) {
   constexpr int REC = D + 4;
   constexpr int QE = elem_size<QT>::value;
   static_assert(D % 4 == 0, "record layout");
   for (int e0 = threadIdx.x * 4; e0 < G * D; e0 += 256) {
     const int g = e0 / D, d = e0 % D;
+    const int64_t orow = rows(g);
+    if (orow < 0) continue;
     float M = -INFINITY;
     for (int v = first_w; v <= last_w; ++v) {
       const RecordRef r = record_ref<D, G>(p.partials + (int64_t)(2 * v + (v * chunk >= seg_start ? 0 : 1)) * G * REC);
@@ -321,7 +333,7 @@ __device__ inline void merge_records(const DecodeParams& p, int first_w, int las
       o[2] = fmaf(f, a.z, o[2]);
       o[3] = fmaf(f, a.w, o[3]);
     }
-    store_row<QT, 4>(p.out + (oe + e0) * QE, o, lsum > 0.0f ? p.v_scale / lsum : 0.0f);
+    store_row<QT, 4>(p.out + (orow + d) * QE, o, lsum > 0.0f ? p.v_scale / lsum : 0.0f);
   }
   if (threadIdx.x == 0) __hip_atomic_store(p.counters + first_w, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -449,7 +461,8 @@ __device__ inline void valu_run(const DecodeParams& p, int w, int chunk, int wst
   const int first_w = seg_start / chunk;
   const int last_w = (seg_start + nb - 1) / chunk;
   if (arrive(p, first_w, last_w))
-    merge_records<QT, D, G>(p, first_w, last_w, seg_start, chunk, ((int64_t)s * Hq + (int64_t)h * G) * D);
+    merge_records<QT, D, G>(p, first_w, last_w, seg_start, chunk,
+                            ContiguousRows{((int64_t)s * Hq + (int64_t)h * G) * D, D});
 }
 
 }  // namespace pkv

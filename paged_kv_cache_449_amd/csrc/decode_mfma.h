@@ -26,8 +26,9 @@
 //       receives V[4kg + k][16dt + 4a + b], k = 0..3: its A operand.
 //
 // fp8 pools are widened exactly to the operand type (E4M3FN is a subset of
-// both bf16 and f16).  P is rounded to the operand type; the running sum adds
-// the rounded values, so numerator and denominator use the same weights.
+// both bf16 and f16).  P enters PV as two operands of the operand type: its
+// rounding and the rounding of the remainder (about 16 significant bits
+// together); the running sum adds the fp32 weights.
 // The online softmax keeps one running max per head (lanes j, j+16, j+32,
 // j+48 agree on it) and per-lane partial sums that are added at the end.
 #pragma once
@@ -196,13 +197,24 @@ __device__ inline uint4 mfma_k_operand(const uint4 (&kq)[MfmaShape<KV, D>::KL], 
   }
 }
 
-template <typename KV, typename QT, int D, int G, int POL>
-__device__ inline void mfma_run(const DecodeParams& p, int w, int chunk, int wstart, int pos, int s, int h, int off,
-                                int len, int n, int nb) {
+// Query row served by lane (kg, j) of a matrix-core run.
+struct MfmaRow {
+  bool valid;     // row j holds a query
+  int64_t qoff;   // element offset of its q row (and of its out row)
+  int limit;      // tokens at or past this index are masked for the row
+};
+
+// One run of up to 16 query rows against blocks [off, off+len) of the
+// (kv head h, sequence s) stream, which has nb blocks and n tokens; `rows`
+// maps record row j to the element offset of its out row (-1: no query).
+// R is the number of record rows.  All scalars are uniform.
+template <typename KV, typename QT, int D, int R, int POL, typename Rows>
+__device__ inline void mfma_rows_run(const DecodeParams& p, int w, int chunk, int wstart, int pos, int s, int h,
+                                     int off, int len, int n, int nb, const MfmaRow& row, const Rows& rows) {
   using MT = typename mfma_operand<KV, QT>::type;
   using Ops = mfma_ops<MT>;
   using Sh = MfmaShape<KV, D>;
-  static_assert(G >= 1 && G <= 16, "query group");
+  static_assert(R >= 1 && R <= 16, "query rows");
   constexpr int KS = Sh::KS, DT = Sh::DT, LSTRIDE = Sh::LSTRIDE;
   constexpr int TPS = MfmaStep<KV, D>::TPS;
   constexpr int QE = elem_size<QT>::value;
@@ -210,26 +222,23 @@ __device__ inline void mfma_run(const DecodeParams& p, int w, int chunk, int wst
   __shared__ __attribute__((aligned(16))) uint8_t klds[16 * Sh::KSTRIDE];
 
   const int lane = threadIdx.x;
-  const int j16 = lane & 15;   // token row (QK A) / head column (B, D)
+  const int j16 = lane & 15;   // token row (QK A) / query row (B, D)
   const int kg = lane >> 4;    // k group
-  const int Hq = p.num_kv_heads * G;
 
-  // q operand: lane (kg, j) holds q[j][kg*D/4 + 8st .. +8] for step st
+  // q operand: lane (kg, j) holds q row j at dims kg*D/4 + 8st .. +8 for step st
   uint4 qop[KS];
-  {
-    const int64_t qe = ((int64_t)s * Hq + (int64_t)h * G + j16) * D + kg * (D / 4);
 #pragma unroll
-    for (int st = 0; st < KS; ++st) qop[st] = make_uint4(0u, 0u, 0u, 0u);
-    if (j16 < G) {
+  for (int st = 0; st < KS; ++st) qop[st] = make_uint4(0u, 0u, 0u, 0u);
+  if (row.valid) {
+    const int64_t qe = row.qoff + kg * (D / 4);
 #pragma unroll
-      for (int st = 0; st < KS; ++st) qop[st] = *(const uint4*)(p.q + (qe + st * 8) * QE);
-    }
+    for (int st = 0; st < KS; ++st) qop[st] = *(const uint4*)(p.q + (qe + st * 8) * QE);
   }
 
   f32x4 acc[DT];
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-  float m = -INFINITY;   // running max of head j16 (log2 units)
+  float m = -INFINITY;   // running max of row j16 (log2 units)
   float l = 0.0f;        // this lane's share of the running sum
 
   RunCtx c;
@@ -269,16 +278,17 @@ __device__ inline void mfma_run(const DecodeParams& p, int w, int chunk, int wst
     uint4 kq[Sh::KL];
 #pragma unroll
     for (int q = 0; q < Sh::KL; ++q) kq[q] = *(const uint4*)(klds + j16 * Sh::KSTRIDE + kg * (Sh::ROW / 4) + q * 16);
-    // S^T tile: lane (kg, j16) gets scores of tokens 4kg + i, i = 0..3, head j16
+    // S^T tile: lane (kg, j16) gets scores of tokens 4kg + i, i = 0..3, row j16
     f32x4 sc = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int st = 0; st < KS; ++st) sc = Ops::qk(mfma_k_operand<KV, MT, D>(kq, st), qop[st], sc);
     const int bi = min((j * 16) >> p.log2_bs, 63);
     const bool bvalid = __builtin_amdgcn_readlane(tab, bi) >= 0;
     const int t0 = tlo + j * 16 + 4 * kg;
+    const int lim = min(thi, row.limit);
     float x[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) x[i] = (j16 < G && bvalid && t0 + i < thi) ? sc[i] * p.q_scale : -INFINITY;
+    for (int i = 0; i < 4; ++i) x[i] = (row.valid && bvalid && t0 + i < lim) ? sc[i] * p.q_scale : -INFINITY;
     float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
     mx = fmaxf(mx, __shfl_xor(mx, 16));
     mx = fmaxf(mx, __shfl_xor(mx, 32));
@@ -286,18 +296,29 @@ __device__ inline void mfma_run(const DecodeParams& p, int w, int chunk, int wst
     const float mu = mn == -INFINITY ? 0.0f : mn;
     const float alpha = fexp2(m - mu);
     m = mn;
-    const uint32_t p01 = Ops::pack(fexp2(x[0] - mu), fexp2(x[1] - mu));
-    const uint32_t p23 = Ops::pack(fexp2(x[2] - mu), fexp2(x[3] - mu));
-    l = l * alpha + ((Ops::lo(p01) + Ops::hi(p01)) + (Ops::lo(p23) + Ops::hi(p23)));
+    float e[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) e[i] = fexp2(x[i] - mu);
+    l = l * alpha + ((e[0] + e[1]) + (e[2] + e[3]));
+    // The weights enter the matrix cores as a rounded head plus the rounded
+    // remainder: one 16-bit operand alone (8 significant bits for bf16) would
+    // leave an error of up to ~2^-8 of the spread of V in rows that see few
+    // tokens.
+    const uint32_t h01 = Ops::pack(e[0], e[1]), h23 = Ops::pack(e[2], e[3]);
+    const uint32_t r01 = Ops::pack(e[0] - Ops::lo(h01), e[1] - Ops::hi(h01));
+    const uint32_t r23 = Ops::pack(e[2] - Ops::lo(h23), e[3] - Ops::hi(h23));
     if (__ballot(alpha != 1.0f)) {
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) acc[dt] *= alpha;
     }
-    const uint2 pop = make_uint2(p01, p23);
+    const uint2 ph = make_uint2(h01, h23), pr = make_uint2(r01, r23);
     // lane (kg, i) needs V[4kg + e][16 dt + i], e = 0..3: one transposing read
     const uint8_t* tr = vlds + (4 * kg + (j16 >> 2)) * LSTRIDE + (lane & 3) * 8;
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) acc[dt] = Ops::pv(Ops::read_tr(tr + dt * 32), pop, acc[dt]);
+    for (int dt = 0; dt < DT; ++dt) {
+      const auto vt = Ops::read_tr(tr + dt * 32);
+      acc[dt] = Ops::pv(vt, pr, Ops::pv(vt, ph, acc[dt]));
+    }
   };
 
   int tab = load_table_window(p, trow, 0, len);
@@ -308,9 +329,9 @@ __device__ inline void mfma_run(const DecodeParams& p, int w, int chunk, int wst
     const int thi = min((off + wb + cnt) << p.log2_bs, n);
     const int tiles = (thi - tlo + 15) >> 4;
     // Two step register sets in flight: issue the next step, compute this
-    // one.  Issues are unconditional so the compiler's wait
-    // counts stay exact (a tile past the window reads zeros and its scores
-    // are all masked).
+    // one.  Issues are unconditional so the compiler's wait counts stay
+    // exact (a tile past the window reads zeros and its scores are all
+    // masked).
     const int steps = (tiles + TPS - 1) / TPS;
     MfmaStep<KV, D> a, b;
     auto issue = [&](MfmaStep<KV, D>& r, int st) {
@@ -331,26 +352,25 @@ __device__ inline void mfma_run(const DecodeParams& p, int w, int chunk, int wst
     tab = tab_next;
   }
 
-  // total sum of head j16 over the four k groups
+  // total sum of row j16 over the four k groups
   l += __shfl_xor(l, 16);
   l += __shfl_xor(l, 32);
 
   // lane (kg, j16) holds O[j16][16 dt + 4kg + i], i = 0..3
-  const int64_t orow = ((int64_t)s * Hq + (int64_t)h * G) * D;
   if (off == 0 && off + len == nb) {   // the whole run is ours
-    if (j16 < G) {
+    if (row.valid) {
       const float mul = l > 0.0f ? p.v_scale / l : 0.0f;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
         const float v4[4] = {acc[dt][0], acc[dt][1], acc[dt][2], acc[dt][3]};
-        store_row<QT, 4>(p.out + (orow + (int64_t)j16 * D + dt * 16 + 4 * kg) * QE, v4, mul);
+        store_row<QT, 4>(p.out + (row.qoff + dt * 16 + 4 * kg) * QE, v4, mul);
       }
     }
     return;
   }
 
-  const RecordRef rec = record_ref<D, G>(partial_record<D, G>(p, w, wstart, pos));
-  if (j16 < G) {
+  const RecordRef rec = record_ref<D, R>(partial_record<D, R>(p, w, wstart, pos));
+  if (row.valid && j16 < R) {
     const int rg = j16 * (D + 4);
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
@@ -360,7 +380,21 @@ __device__ inline void mfma_run(const DecodeParams& p, int w, int chunk, int wst
   const int seg_start = pos - off;
   const int first_w = seg_start / chunk;
   const int last_w = (seg_start + nb - 1) / chunk;
-  if (arrive(p, first_w, last_w)) merge_records<QT, D, G>(p, first_w, last_w, seg_start, chunk, orow);
+  if (arrive(p, first_w, last_w)) merge_records<QT, D, R>(p, first_w, last_w, seg_start, chunk, rows);
+}
+
+// Decode: the G query heads of sequence s served by kv head h, one token each.
+template <typename KV, typename QT, int D, int G, int POL>
+__device__ inline void mfma_run(const DecodeParams& p, int w, int chunk, int wstart, int pos, int s, int h, int off,
+                                int len, int n, int nb) {
+  const int Hq = p.num_kv_heads * G;
+  const int j16 = threadIdx.x & 15;
+  const int64_t orow = ((int64_t)s * Hq + (int64_t)h * G) * D;
+  MfmaRow row;
+  row.valid = j16 < G;
+  row.qoff = orow + (int64_t)j16 * D;
+  row.limit = n;
+  mfma_rows_run<KV, QT, D, G, POL>(p, w, chunk, wstart, pos, s, h, off, len, n, nb, row, ContiguousRows{orow, D});
 }
 
 }  // namespace pkv

@@ -1,0 +1,88 @@
+// Host entry points of multi-token paged attention: argument checks,
+// workspace layout and dispatch to the kernel instantiations.
+#include "prefill_kernel.h"
+
+namespace {
+
+using namespace pkv;
+
+constexpr int kPrefillWavesPerCu = 8;
+constexpr int kRecordRows = 16;
+
+kv_status_t prefill_plan(const kv_pool_t* pool, int32_t num_q_heads, int32_t* workers, size_t* counters_bytes,
+                         size_t* bytes) {
+  if (!pool || num_q_heads <= 0 || num_q_heads % pool->num_kv_heads) return KV_ERR_INVALID_ARG;
+  const int G = num_q_heads / pool->num_kv_heads;
+  if (G != 1 && G != 2 && G != 4 && G != 8 && G != 16) return KV_ERR_UNSUPPORTED;
+  int64_t w = (int64_t)pool->num_cus * kPrefillWavesPerCu;
+  w = (w + 7) & ~7LL;
+  if (w < 8) w = 8;
+  if (w > kCounterSlots) w = kCounterSlots;
+  *workers = (int32_t)w;
+  *counters_bytes = (size_t)kCounterSlots * sizeof(int32_t);
+  *bytes = *counters_bytes + (size_t)2 * w * kRecordRows * (pool->head_dim + 4) * sizeof(float);
+  return KV_OK;
+}
+
+}  // namespace
+
+extern "C" kv_status_t paged_attention_prefill_workspace_size(const kv_pool_t* pool, int32_t num_q_heads,
+                                                              size_t* bytes) {
+  if (!bytes) return KV_ERR_INVALID_ARG;
+  int32_t workers;
+  size_t counters;
+  return prefill_plan(pool, num_q_heads, &workers, &counters, bytes);
+}
+
+extern "C" kv_status_t paged_attention_prefill(const kv_pool_t* pool, const void* q, kv_dtype_t q_dtype, void* out,
+                                               const int32_t* block_tables, int32_t max_blocks,
+                                               const int32_t* context_lens, const int32_t* query_start,
+                                               int32_t num_seqs, int32_t total_q, int32_t num_q_heads, float scale,
+                                               void* workspace, size_t workspace_bytes, void* stream) {
+  int32_t workers;
+  size_t counters_bytes, need;
+  kv_status_t st = prefill_plan(pool, num_q_heads, &workers, &counters_bytes, &need);
+  if (st != KV_OK) return st;
+  if (num_seqs < 0 || total_q < 0 || max_blocks <= 0 || !valid_dtype(q_dtype)) return KV_ERR_INVALID_ARG;
+  if (num_seqs == 0 || total_q == 0) return KV_OK;
+  if (!q || !out || !block_tables || !context_lens || !query_start) return KV_ERR_INVALID_ARG;
+  if ((((uintptr_t)q) | ((uintptr_t)out)) & 15) return KV_ERR_INVALID_ARG;
+  if (!(scale == scale) || scale > 3.0e38f || scale < -3.0e38f) return KV_ERR_INVALID_ARG;
+  if (pool->log2_block_size < 4) return KV_ERR_UNSUPPORTED;   // tiles of 16 tokens within one block
+  const int G = num_q_heads / pool->num_kv_heads;
+  // stream length bound: tiles * blocks per tile * kv heads must fit in int32
+  const int64_t tiles = ((int64_t)total_q * G + 15) / 16 + num_seqs;
+  if (tiles * max_blocks * pool->num_kv_heads > (1LL << 30) || (int64_t)max_blocks * pool->block_size > (1LL << 30))
+    return KV_ERR_INVALID_ARG;
+  if (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255)) return KV_ERR_WORKSPACE;
+
+  DecodeParams p;
+  p.k_pool = (const uint8_t*)pool->k;
+  p.v_pool = (const uint8_t*)pool->v;
+  p.q = (const uint8_t*)q;
+  p.out = (uint8_t*)out;
+  p.block_tables = block_tables;
+  p.context_lens = context_lens;
+  p.query_start = query_start;
+  p.counters = (int32_t*)workspace;
+  p.partials = (float*)((uint8_t*)workspace + counters_bytes);
+  p.num_seqs = num_seqs;
+  p.total_q = total_q;
+  p.num_kv_heads = pool->num_kv_heads;
+  p.max_blocks = max_blocks;
+  p.num_blocks = pool->num_blocks;
+  p.log2_bs = pool->log2_block_size;
+  p.chunk = 0;
+  p.num_workers = workers;
+  const bool fp8 = pool->dtype == KV_FP8_E4M3FN;
+  p.q_scale = scale * kLog2e * (fp8 ? pool->k_scale : 1.0f);
+  p.v_scale = fp8 ? pool->v_scale : 1.0f;
+
+  const int D = pool->head_dim;
+  hipStream_t s = (hipStream_t)stream;
+  if (pool->dtype == KV_BF16 && q_dtype == KV_BF16) return launch_prefill_bf16_bf16(p, D, G, s);
+  if (pool->dtype == KV_F16 && q_dtype == KV_F16) return launch_prefill_f16_f16(p, D, G, s);
+  if (fp8 && q_dtype == KV_BF16) return launch_prefill_fp8_bf16(p, D, G, s);
+  if (fp8 && q_dtype == KV_F16) return launch_prefill_fp8_f16(p, D, G, s);
+  return KV_ERR_UNSUPPORTED;
+}

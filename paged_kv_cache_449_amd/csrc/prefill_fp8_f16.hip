@@ -1,0 +1,8 @@
+// Multi-token paged attention instantiations for fp8 KV pools with f16 queries.
+#include "prefill_kernel.h"
+
+namespace pkv {
+kv_status_t launch_prefill_fp8_f16(const DecodeParams& p, int D, int G, hipStream_t s) {
+  return launch_prefill<fp8_t, f16_t>(p, D, G, s);
+}
+}  // namespace pkv

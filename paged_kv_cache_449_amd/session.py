@@ -18,7 +18,7 @@ from typing import Hashable, List, Optional, Sequence
 import numpy as np
 import torch
 
-from . import KVPool, copy_blocks, paged_attention_decode, reshape_and_cache
+from . import KVPool, copy_blocks, paged_attention_decode, paged_attention_prefill, reshape_and_cache
 from .block_manager import BlockManager
 
 
@@ -32,6 +32,7 @@ class DecodeSession:
         self.pairs: Optional[torch.Tensor] = None
         self.block_tables: Optional[torch.Tensor] = None
         self.context_lens: Optional[torch.Tensor] = None
+        self.query_start: Optional[torch.Tensor] = None
 
     def _dev(self, a: np.ndarray) -> torch.Tensor:
         return torch.from_numpy(np.ascontiguousarray(a)).to(self.pool.device, non_blocking=False)
@@ -56,21 +57,38 @@ class DecodeSession:
     def free(self, seq: Hashable) -> None:
         self.manager.free(seq)
 
-    def prepare_step(self, seqs: Sequence[Hashable], max_blocks: Optional[int] = None) -> None:
-        """Reserve one new slot per sequence (planning copy-on-write) and upload
-        the step's slot mapping, copy pairs, block tables and lengths."""
+    def prepare_step(self, seqs: Sequence[Hashable], max_blocks: Optional[int] = None,
+                     counts: Optional[Sequence[int]] = None) -> None:
+        """Reserve the step's new slots -- one per sequence, or counts[i] for
+        sequence i -- planning copy-on-write, and upload the step's slot
+        mapping, copy pairs, block tables, lengths and query row offsets."""
         self.seqs = list(seqs)
-        slots = np.empty(len(self.seqs), dtype=np.int64)
+        counts = [1] * len(self.seqs) if counts is None else [int(c) for c in counts]
+        slots = np.empty(sum(counts), dtype=np.int64)
         pairs = []
-        for i, s in enumerate(self.seqs):
-            slot, pair = self.manager.append_slot(s)
-            slots[i] = slot
-            if pair is not None:
-                pairs.append(pair)
+        i = 0
+        for s, cnt in zip(self.seqs, counts):
+            for _ in range(cnt):
+                slot, pair = self.manager.append_slot(s)
+                slots[i] = slot
+                i += 1
+                if pair is not None:
+                    pairs.append(pair)
         self.slot_mapping = self._dev(slots)
         self.pairs = self._dev(np.asarray(pairs, dtype=np.int32).reshape(-1, 2))
         self.block_tables = self._dev(self.manager.block_tables(self.seqs, max_blocks))
         self.context_lens = self._dev(self.manager.context_lens(self.seqs))
+        self.query_start = self._dev(np.concatenate([[0], np.cumsum(counts)]).astype(np.int32))
+
+    def step_multi(self, q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
+                   out: Optional[torch.Tensor] = None, scale: Optional[float] = None) -> torch.Tensor:
+        """Enqueue one multi-token step: copy-on-write copies, the cache write
+        of every new token, then causal attention of the new tokens."""
+        scale = (1.0 / self.pool.head_dim ** 0.5) if scale is None else scale
+        copy_blocks(self.pool, self.pairs)
+        reshape_and_cache(self.pool, k_new, v_new, self.slot_mapping)
+        return paged_attention_prefill(self.pool, q, self.block_tables, self.context_lens, self.query_start, scale,
+                                       out=out)
 
     def step(self, q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor, out: Optional[torch.Tensor] = None,
              partition_tokens: int = 0, scale: Optional[float] = None) -> torch.Tensor:

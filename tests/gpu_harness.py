@@ -44,3 +44,27 @@ def run_gpu(wl, partition_tokens=None, free_order=None, repeat: int = 1):
         "pairs": sess.pairs.cpu().numpy(),
         "slots": sess.slot_mapping.cpu().numpy(),
     }
+
+
+def run_gpu_prefill(wl, repeat: int = 1):
+    """Build a multi-token workload on the GPU and run `repeat` steps (cache
+    writes of every new token, then causal attention of the new rows)."""
+    announce(f"{wl.name} prefill total_q={wl.total_q}")
+    dev = device()
+    sess, q, kn, vn = bench.build_session(wl, dev)
+    outs = []
+    for _ in range(repeat):
+        out = sess.step_multi(q, kn, vn, scale=wl.scale)
+        torch.cuda.synchronize(dev)
+        outs.append(out.float().cpu().double().numpy())
+    pool = sess.pool
+    return {
+        "session": sess,
+        "k": pool.k_cache.view(torch.uint8).cpu().numpy().reshape(-1),
+        "v": pool.v_cache.view(torch.uint8).cpu().numpy().reshape(-1),
+        "out": outs[0],
+        "outs": outs,
+        "tables": sess.block_tables.cpu().numpy(),
+        "slots": sess.slot_mapping.cpu().numpy(),
+        "q": q,
+    }

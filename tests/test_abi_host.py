@@ -28,9 +28,10 @@ def _declared_functions():
 
 def test_header_declares_the_four_calls_and_helpers():
     names = _declared_functions()
-    for n in ["kv_pool_create", "reshape_and_cache", "paged_attention_decode", "copy_blocks", "swap_blocks"]:
+    for n in ["kv_pool_create", "reshape_and_cache", "paged_attention_decode", "copy_blocks", "swap_blocks",
+              "paged_attention_prefill"]:
         assert n in names
-    assert len(names) == 11, names
+    assert len(names) == 13, names
 
 
 def test_library_exports_every_declared_symbol():

@@ -132,6 +132,15 @@ def test_shape_families(gpu, shape, pt_blocks):
     check_close(got["out"], ref.decode(), wl.kv_dtype)
 
 
+@pytest.mark.parametrize("kv,q,g", [("bf16", "bf16", 4), ("fp8e4m3", "bf16", 8), ("f16", "f16", 2)])
+def test_short_contexts_on_matrix_cores(gpu, kv, q, g):
+    """Contexts of a few tokens on the matrix-core path: the weights cannot
+    average rounding out, so these rows test the precision of P itself."""
+    lens = [2, 3, 4, 5, 2, 3, 2, 6, 7, 8, 2, 3, 9, 2, 4, 16, 17, 3, 2, 5] * 3
+    wl = W.custom(f"short_{kv}_g{g}", 2 * g, 2, 128, kv, q, 16, lens, index=94)
+    check_close(gpu(wl)["out"], OracleRun(wl).decode(), wl.kv_dtype)
+
+
 def test_host_side_errors(pk):
     dev = _dev()
     pool = pk.KVPool(8, 16, 2, 128, torch.float16, dev)

@@ -1,0 +1,89 @@
+"""GPU parity of multi-token causal paged attention (chunked prefill and
+speculative verification) through the C ABI against the CPU oracle.
+
+  * pools after the step's cache writes: whole-pool byte equality;
+  * output: |gpu - oracle| <= atol + rtol |oracle| elementwise with the
+    decode tolerances (the kernel computes in the same precisions), every
+    unowned slot poisoned with NaN bytes;
+  * at the full sizes: sampled sequences (the oracle computes them one by
+    one) plus properties checked on every row (finite, bitwise repeatable).
+"""
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from oracle.run import OracleRun, check_close
+
+pytestmark = pytest.mark.gpu
+
+SMALL = list(W.small_multi_token_configs())
+
+
+@pytest.fixture(scope="module")
+def gpu():
+    from gpu_harness import run_gpu_prefill
+    return run_gpu_prefill
+
+
+@pytest.mark.parametrize("name", SMALL)
+def test_prefill_matches_oracle(gpu, name):
+    wl = W.small_multi_token_configs()[name]
+    got = gpu(wl)
+    ref = OracleRun(wl)
+    np.testing.assert_array_equal(got["tables"], ref.tables)
+    np.testing.assert_array_equal(got["slots"], ref.plan["new_slots"])
+    assert np.array_equal(got["k"], ref.pool.k), "K pool bytes differ"
+    assert np.array_equal(got["v"], ref.pool.v), "V pool bytes differ"
+    assert np.isfinite(got["out"]).all()
+    check_close(got["out"], ref.prefill(), wl.kv_dtype)
+
+
+@pytest.mark.parametrize("G,D,kv,q", [(1, 128, "bf16", "bf16"), (2, 64, "f16", "f16"), (4, 128, "fp8e4m3", "bf16"),
+                                      (8, 256, "bf16", "bf16"), (16, 64, "fp8e4m3", "f16")])
+def test_ragged_and_empty_query_counts(gpu, G, D, kv, q):
+    """Sequences with no new tokens, one, a partial tile, several tiles,
+    chunks that start mid-block and chunks equal to the whole context."""
+    ctx = [50, 17, 64, 5, 130, 33]
+    qn = [0, 1, 13, 5, 40, 0]
+    wl = W._make(f"ragged_g{G}_d{D}_{kv}", 12 + G, 2 * G, 2, D, kv, q, 16, ctx_lens=ctx, query_lens=qn)
+    got = gpu(wl)
+    check_close(got["out"], OracleRun(wl).prefill(), wl.kv_dtype)
+
+
+def test_one_new_token_matches_decode_oracle(gpu):
+    """m = 1 for every sequence is the decode step: the multi-token kernel
+    agrees with the oracle's decode."""
+    base = W.small_configs()["c5s_bf16"]
+    wl = W._make("m1_gqa", 13, base.num_q_heads, base.num_kv_heads, base.head_dim, "bf16", "bf16", 16,
+                 ctx_lens=list(base.context_lens), query_lens=[1] * base.num_seqs)
+    got = gpu(wl)
+    check_close(got["out"], OracleRun(wl).decode(), wl.kv_dtype)
+
+
+def test_block_size_32(gpu):
+    wl = W._make("bs32", 14, 8, 2, 128, "bf16", "bf16", 32, ctx_lens=[100, 64, 31], query_lens=[70, 33, 31])
+    check_close(gpu(wl)["out"], OracleRun(wl).prefill(), wl.kv_dtype)
+
+
+def test_repeat_is_bitwise_deterministic(gpu):
+    wl = W.small_multi_token_configs()["p3s_fp8"]
+    got = gpu(wl, repeat=3)
+    for o in got["outs"][1:]:
+        assert np.array_equal(o, got["outs"][0])
+
+
+@pytest.mark.parametrize("name", list(W.multi_token_configs()))
+def test_full_size_sampled(gpu, name):
+    wl = W.multi_token_configs()[name]
+    got = gpu(wl, repeat=2)
+    out = got["out"]
+    assert np.isfinite(out).all()
+    assert np.array_equal(got["outs"][1], out)
+    ref = OracleRun(wl)
+    rng = np.random.default_rng(5)
+    qs = wl.query_start
+    for s in sorted(rng.choice(wl.num_seqs, size=min(4, wl.num_seqs), replace=False).tolist()):
+        m = int(qs[s + 1] - qs[s])
+        for a, b in {(0, min(m, 8)), (max(0, m - 8), m)}:   # the first and the last rows
+            check_close(out[qs[s] + a:qs[s] + b], ref.prefill_rows(s, a, b), wl.kv_dtype)

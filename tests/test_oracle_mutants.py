@@ -17,6 +17,9 @@ from oracle.run import OracleRun
 MUTANTS = {
     "dropped_scale": ("sc[t] = scale * acc;", "sc[t] = acc;"),
     "softmax_sign": ("sc[t] = exp(sc[t] - m);", "sc[t] = exp(m - sc[t]);"),
+    "causal_off_by_one": ("int seen = n - m + i + 1;", "int seen = n - m + i;"),
+    "causal_ignored": ("attend(qd, Kc, Vc, seen, D,", "attend(qd, Kc, Vc, n, D,"),
+    "query_row": ("size_t qoff = ((size_t)(q0 + i) * Hq + hq) * D;", "size_t qoff = ((size_t)(q0 + i) * Hq + gi) * D;"),
     "no_normalise": ("o[j] = acc / l;", "o[j] = acc;"),
     "block_index": ("block_tables[(size_t)s * max_blocks + t / B]", "block_tables[(size_t)s * max_blocks + t % B]"),
     "slot_offset": ("int o = t % B;", "int o = t / B;"),
@@ -31,12 +34,16 @@ MUTANTS = {
 }
 
 
-def _build_variant(tmp, name, edit):
+def _build_variant(tmp, name, edit, occurrence=0):
+    """Copy of the oracle source with the `occurrence`-th instance of the
+    edit's text replaced (every instance is planted on its own)."""
     src = open(oracle._SRC).read()
     if edit is not None:
         old, new = edit
-        assert src.count(old) == 1, name
-        src = src.replace(old, new)
+        at = -1
+        for _ in range(occurrence + 1):
+            at = src.index(old, at + 1)
+        src = src[:at] + new + src[at + len(old):]
     c = os.path.join(tmp, f"{name}.c")
     so = os.path.join(tmp, f"lib{name}.so")
     open(c, "w").write(src)
@@ -48,7 +55,8 @@ def _load(so):
     good = oracle.lib()
     L = ctypes.CDLL(so)
     for fn in ["oracle_f16_to_f64", "oracle_bf16_to_f64", "oracle_e4m3_to_f64", "oracle_f32_to_e4m3_sat",
-               "oracle_reshape_and_cache", "oracle_copy_blocks", "oracle_decode", "oracle_kv_footprint_bytes"]:
+               "oracle_reshape_and_cache", "oracle_copy_blocks", "oracle_decode", "oracle_prefill",
+               "oracle_kv_footprint_bytes"]:
         getattr(L, fn).argtypes = getattr(good, fn).argtypes
         getattr(L, fn).restype = getattr(good, fn).restype
     return L
@@ -58,6 +66,7 @@ def _pins_pass() -> bool:
     """A compact subset of the pins: formats exhaustively, decode vs the
     library routine on an MHA fp16, a GQA bf16 and a GQA fp8 workload."""
     from test_oracle_decode import _sdpa_expected
+    from test_oracle_prefill import _sdpa_causal
     from test_oracle_formats import _same
     try:
         ref16 = np.arange(65536, dtype=np.uint16).view(np.float16).astype(np.float64)
@@ -75,6 +84,10 @@ def _pins_pass() -> bool:
             wl = W.small_configs()[name]
             run = OracleRun(wl)
             np.testing.assert_allclose(run.decode(), _sdpa_expected(wl, run), rtol=1e-10, atol=1e-12)
+        for name in ["p1s_bf16", "p3s_fp8"]:
+            wl = W.small_multi_token_configs()[name]
+            run = OracleRun(wl)
+            np.testing.assert_allclose(run.prefill(), _sdpa_causal(wl, run), rtol=1e-10, atol=1e-12)
     except (AssertionError, oracle.OracleError):
         return False
     return True
@@ -87,10 +100,14 @@ def test_pins_accept_original_and_reject_every_mutant():
             oracle._lib = _load(_build_variant(tmp, "original", None))
             assert _pins_pass(), "pins reject the unmodified oracle"
             survivors = []
+            src = open(oracle._SRC).read()
             for name, edit in MUTANTS.items():
-                oracle._lib = _load(_build_variant(tmp, name, edit))
-                if _pins_pass():
-                    survivors.append(name)
+                count = src.count(edit[0])
+                assert count >= 1, name
+                for k in range(count):
+                    oracle._lib = _load(_build_variant(tmp, f"{name}_{k}", edit, k))
+                    if _pins_pass():
+                        survivors.append(f"{name}[{k}]")
             assert not survivors, f"mutants not caught by the pins: {survivors}"
     finally:
         oracle._lib = saved

@@ -1,0 +1,192 @@
+"""CPU model of the multi-token (prefill) kernel's work split.
+
+Replays the index arithmetic of each worker wavefront: the per-sequence row
+tiles (16 / G new tokens x G query heads), the blocks each tile reads (up to
+the position of its last token), the flattened (kv head, sequence, tile,
+block) stream cut into chunks, partial records, arrival counters and merges.
+Checks that every index stays inside its buffer (table rows, q/out rows,
+record slots, counters), that every block of every tile is streamed exactly
+once, and that every (query row, query head) output is written exactly once,
+for consistent and inconsistent query_start arrays.
+"""
+import numpy as np
+import pytest
+
+COUNTER_SLOTS = 65536
+WAVES_PER_CU = 8
+
+
+def workers_for(num_cus):
+    w = num_cus * WAVES_PER_CU
+    w = max(8, (w + 7) & ~7)
+    return min(w, COUNTER_SLOTS)
+
+
+def lengths(ctx, qs, total_q, max_len):
+    """(n, m, q0) per sequence, clamped as the kernel clamps them."""
+    out = []
+    for s in range(len(ctx)):
+        n = min(max(int(ctx[s]), 0), max_len)
+        a = min(max(int(qs[s]), 0), total_q)
+        b = min(max(int(qs[s + 1]), a), total_q)
+        out.append((n, min(b - a, n), a))
+    return out
+
+
+def tile_limit(n, m, Q, r):
+    return n - m + min((r + 1) * Q, m)
+
+
+def tiles_of(n, m, Q, bs):
+    """Blocks read by each row tile of a sequence."""
+    return [-(-tile_limit(n, m, Q, r) // bs) for r in range(-(-m // Q))]
+
+
+def replay(ctx, qs, total_q, hkv, G, max_blocks, bs, num_cus=256):
+    Q = 16 // G
+    S = len(ctx)
+    max_len = max_blocks * bs
+    W = workers_for(num_cus)
+    # host bound on a consistent stream
+    tiles_bound = -(-total_q * G // 16) + S
+    assert tiles_bound * max_blocks * hkv <= (1 << 30)
+    L = lengths(ctx, qs, total_q, max_len)
+    per_seq = [tiles_of(n, m, Q, bs) for n, m, _ in L]
+    nbs = [sum(t) for t in per_seq]
+    assert all(x <= (1 << 30) for x in nbs)
+    total = sum(nbs)
+    if total * hkv > (1 << 30):
+        return None            # the kernel computes nothing
+    T = total * hkv
+    if T == 0:
+        return None
+    chunk = max(1, -(-T // W))
+    nv = -(-T // chunk)
+    per_round = (nv + 7) & ~7
+    assert per_round <= W
+    # the stream, in order: (h, s, r, block offset)
+    streamed = {}
+    written = np.zeros((total_q, hkv * G), dtype=np.int32)
+    records = {}
+    counters = np.zeros(COUNTER_SLOTS, dtype=np.int32)
+    seen = set()
+    order = list(np.random.default_rng(1).permutation(W))
+    for bid in order:
+        bid = int(bid)
+        if bid >= per_round:
+            continue
+        v = (bid & 7) * (per_round >> 3) + (bid >> 3)
+        if v >= nv:
+            continue
+        assert v not in seen
+        seen.add(v)
+        start = v * chunk
+        end = min(start + chunk, T)
+        h, rr = divmod(start, total)
+        pre = np.concatenate([[0], np.cumsum(nbs)])
+        s = next(i for i in range(S) if nbs[i] > 0 and pre[i] <= rr < pre[i] + nbs[i])
+        n, m, q0 = L[s]
+        r, off = 0, rr - pre[s]
+        while off >= per_seq[s][r]:
+            off -= per_seq[s][r]
+            r += 1
+        pos = start
+        while True:
+            nb = per_seq[s][r]
+            ln = min(nb - off, end - pos)
+            assert ln >= 1 and off + ln <= nb <= max_blocks
+            for b in range(off, off + ln):
+                key = (h, s, r, b)
+                streamed[key] = streamed.get(key, 0) + 1
+            rows = []
+            for j in range(16):
+                tok = j // G
+                if r * Q + tok < m:
+                    row = q0 + r * Q + tok
+                    assert 0 <= row < total_q
+                    rows.append((row, h * G + j % G))
+            if off == 0 and off + ln == nb:
+                for row in rows:
+                    written[row] += 1
+            else:
+                slot = 2 * v + (0 if pos == start else 1)
+                assert slot < 2 * W and slot not in records
+                records[slot] = (h, s, r)
+                seg_start = pos - off
+                first_w, last_w = seg_start // chunk, (seg_start + nb - 1) // chunk
+                assert first_w < last_w < nv
+                counters[first_w] += 1
+                if counters[first_w] - 1 == last_w - first_w:
+                    for u in range(first_w, last_w + 1):
+                        k = 0 if u * chunk >= seg_start else 1
+                        assert records.get(2 * u + k) == (h, s, r)
+                    for row in rows:
+                        written[row] += 1
+                    counters[first_w] = 0
+            pos += ln
+            if pos >= end:
+                break
+            off = 0
+            r += 1
+            if r * Q < m:
+                continue
+            r = 0
+            while True:
+                s += 1
+                if s == S:
+                    s = 0
+                    h += 1
+                    assert h < hkv
+                n, m, q0 = L[s]
+                if m > 0:
+                    break
+    assert seen == set(range(nv))
+    for h in range(hkv):
+        for s in range(S):
+            for r, nb in enumerate(per_seq[s]):
+                for b in range(nb):
+                    assert streamed.get((h, s, r, b)) == 1
+    assert sum(streamed.values()) == T
+    assert not counters.any()
+    return written
+
+
+def _consistent(ctx, m):
+    qs = np.concatenate([[0], np.cumsum(m)]).astype(np.int64)
+    return qs, int(qs[-1])
+
+
+@pytest.mark.parametrize("G", [1, 2, 4, 8, 16])
+@pytest.mark.parametrize("bs", [16, 32])
+def test_consistent_rows_written_once(G, bs):
+    rng = np.random.default_rng(G * 100 + bs)
+    for _ in range(4):
+        S = int(rng.integers(1, 12))
+        m = rng.integers(0, 70, size=S)
+        ctx = m + rng.integers(0, 300, size=S)
+        ctx = np.maximum(ctx, 1)
+        qs, tq = _consistent(ctx, m)
+        mb = int(-(-ctx.max() // bs)) + int(rng.integers(0, 3))
+        hkv = int(rng.integers(1, 4))
+        for cus in (1, 4, 256):
+            written = replay(ctx, qs, tq, hkv, G, mb, bs, num_cus=cus)
+            if tq:
+                assert written is not None and (written == 1).all()
+
+
+def test_inconsistent_query_start_stays_in_bounds():
+    rng = np.random.default_rng(7)
+    for _ in range(20):
+        S = int(rng.integers(1, 9))
+        ctx = rng.integers(-5, 200, size=S)
+        qs = rng.integers(-20, 60, size=S + 1)
+        tq = int(rng.integers(1, 50))
+        replay(ctx, qs, tq, 2, 4, 16, 16, num_cus=2)   # asserts every index in range
+
+
+def test_workload_shapes_fit():
+    import workloads as W
+    for wl in list(W.multi_token_configs().values()) + list(W.small_multi_token_configs().values()):
+        written = replay(wl.context_lens, wl.query_start, wl.total_q, wl.num_kv_heads, wl.group,
+                         wl.max_blocks_per_seq, wl.block_size)
+        assert (written == 1).all()

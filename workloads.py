@@ -73,6 +73,7 @@ class Workload:
     num_blocks: int           # pool size in blocks
     partition_tokens: int = 0  # 0 = library chooses the context split
     same_candidates: bool = False  # candidates of a prompt get identical q / new K/V
+    query_lens: Tuple[int, ...] = ()  # new tokens per sequence; empty = one each (decode)
 
     @property
     def num_seqs(self) -> int:
@@ -91,9 +92,29 @@ class Workload:
         return 1.0 / math.sqrt(self.head_dim)
 
     @property
+    def q_lens(self) -> np.ndarray:
+        """New tokens (query rows) of each sequence in the step."""
+        if not self.query_lens:
+            return np.ones(self.num_seqs, dtype=np.int32)
+        return np.asarray(self.query_lens, dtype=np.int32)
+
+    @property
+    def total_q(self) -> int:
+        return int(self.q_lens.sum())
+
+    @property
+    def query_start(self) -> np.ndarray:
+        """int32 [S + 1]: sequence s owns query rows query_start[s]:query_start[s+1]."""
+        return np.concatenate([[0], np.cumsum(self.q_lens)]).astype(np.int32)
+
+    @property
+    def multi_token(self) -> bool:
+        return bool(self.query_lens)
+
+    @property
     def context_lens(self) -> np.ndarray:
         pl = np.asarray(self.prompt_lens, dtype=np.int64)
-        return (pl[np.asarray(self.parent, dtype=np.int64)] + 1).astype(np.int32)
+        return (pl[np.asarray(self.parent, dtype=np.int64)] + self.q_lens).astype(np.int32)
 
     @property
     def max_blocks_per_seq(self) -> int:
@@ -111,32 +132,39 @@ def _rng(wl: Workload, stream: int, key: int = 0) -> np.random.Generator:
 # configurations
 
 
-def _pool_blocks(prompt_lens: Sequence[int], parent: Sequence[int], bs: int) -> int:
+def _pool_blocks(prompt_lens: Sequence[int], parent: Sequence[int], bs: int, query_lens=None) -> int:
     """Pool sizing recipe: 1.2 x an upper bound of the blocks the step needs.
 
-    Upper bound per prompt: its cached tokens rounded up to whole blocks, plus
-    one fresh block per candidate for the token the step appends.
+    Upper bound per prompt: its cached tokens rounded up to whole blocks, plus,
+    per candidate, one fresh block more than its new tokens fill.
     """
     cands = np.bincount(np.asarray(parent), minlength=len(prompt_lens))
-    need = sum(-(-int(L) // bs) + int(c) for L, c in zip(prompt_lens, cands))
+    need = sum(-(-int(L) // bs) for L in prompt_lens)
+    if query_lens:
+        need += sum(-(-int(q) // bs) + 1 for q in query_lens)
+    else:
+        need += int(cands.sum())
     return int(math.ceil(1.2 * need))
 
 
 def _make(name, index, hq, hkv, d, kv, q, bs, ctx_lens=None, prompt_lens=None, parent=None,
-          num_blocks=None, src=None, partition_tokens=0, same_candidates=False) -> Workload:
+          num_blocks=None, src=None, partition_tokens=0, same_candidates=False, query_lens=None) -> Workload:
+    """ctx_lens are context lengths after the step (cached + new tokens)."""
     if prompt_lens is None:
         ctx = [int(x) for x in ctx_lens]
-        prompt_lens = [c - 1 for c in ctx]
+        qn = [1] * len(ctx) if query_lens is None else [int(x) for x in query_lens]
+        prompt_lens = [c - k for c, k in zip(ctx, qn)]
         parent = list(range(len(ctx)))
     if num_blocks is None:
-        num_blocks = _pool_blocks(prompt_lens, parent, bs)
+        num_blocks = _pool_blocks(prompt_lens, parent, bs, query_lens)
     if src is None:
         src = "bf16" if kv == "fp8e4m3" else kv
     return Workload(name=name, index=index, num_q_heads=hq, num_kv_heads=hkv, head_dim=d,
                     kv_dtype=kv, q_dtype=q, src_dtype=src, block_size=bs,
                     prompt_lens=tuple(int(x) for x in prompt_lens), parent=tuple(int(p) for p in parent),
                     num_blocks=int(num_blocks), partition_tokens=partition_tokens,
-                    same_candidates=same_candidates)
+                    same_candidates=same_candidates,
+                    query_lens=tuple(int(x) for x in query_lens) if query_lens is not None else ())
 
 
 def _lens_uniform(index: int, n: int, lo: int, hi: int) -> np.ndarray:
@@ -190,6 +218,56 @@ def config_c5(kv="fp8e4m3", num_seqs=128, lo=2048, hi=8192, hq=32, hkv=8, partit
                  ctx_lens=_lens_uniform(index, num_seqs, lo, hi), partition_tokens=partition_tokens)
 
 
+def config_prefill_chunk(num_seqs=16, chunk=512, lo=0, hi=3072, heads=32, index=6, name="p1_chunked_prefill_bf16",
+                         kv="bf16", q="bf16", hkv=None) -> Workload:
+    """Chunked prefill: each sequence appends a chunk of `chunk` prompt tokens
+    after U[lo, hi] cached ones and attends to them causally (LLaMA-7B-shaped
+    heads, bf16, bs 16)."""
+    cached = _lens_uniform(index, num_seqs, lo, hi)
+    return _make(name, index, heads, hkv or heads, 128, kv, q, 16, ctx_lens=cached + chunk,
+                 query_lens=[chunk] * num_seqs)
+
+
+def config_spec_verify(num_seqs=256, draft=4, heads=32, index=7, name="p2_spec_verify_bf16", lo=16,
+                       hi=4096) -> Workload:
+    """Speculative verification: the LLaMA-7B-shaped high-concurrency batch,
+    each sequence checking `draft` proposed tokens at once (lognormal cached
+    lengths as in the decode workload)."""
+    cached = _lens_lognormal(index, num_seqs, 512.0, 0.8, lo, hi)
+    return _make(name, index, heads, heads, 128, "bf16", "bf16", 16, ctx_lens=cached + draft,
+                 query_lens=[draft] * num_seqs)
+
+
+def config_prefill_gqa(num_seqs=32, chunk=128, lo=1024, hi=4096, index=8, name="p3_gqa_chunk_fp8", kv="fp8e4m3",
+                       hq=32, hkv=8) -> Workload:
+    """GQA (32 query / 8 KV heads) chunk of `chunk` new tokens over U[lo, hi]
+    cached ones, fp8 KV with bf16 queries."""
+    cached = _lens_uniform(index, num_seqs, lo, hi)
+    return _make(name, index, hq, hkv, 128, kv, "bf16", 16, ctx_lens=cached + chunk, query_lens=[chunk] * num_seqs)
+
+
+def multi_token_configs() -> Dict[str, Workload]:
+    """Multi-token (causal) attention workloads at their stated sizes."""
+    ws = [config_prefill_chunk(), config_spec_verify(), config_prefill_gqa()]
+    return {w.name: w for w in ws}
+
+
+def small_multi_token_configs() -> Dict[str, Workload]:
+    """Reduced multi-token workloads the oracle finishes in seconds: tiles that
+    span blocks, partial tiles, chunks starting mid-block, empty cached
+    prefixes, and every query-group size."""
+    ws = [
+        config_prefill_chunk(num_seqs=3, chunk=37, lo=0, hi=90, heads=2, name="p1s_bf16"),
+        config_spec_verify(num_seqs=9, draft=4, heads=3, hi=300, name="p2s_bf16"),
+        config_prefill_gqa(num_seqs=3, chunk=21, lo=30, hi=200, hq=8, hkv=2, name="p3s_fp8"),
+        config_prefill_gqa(num_seqs=4, chunk=9, lo=0, hi=70, hq=8, hkv=2, kv="bf16", name="p3s_bf16"),
+        _make("p4s_f16_g16", 9, 16, 1, 64, "f16", "f16", 32, ctx_lens=[40, 77], query_lens=[40, 5]),
+        _make("p5s_fp8_f16_g8", 10, 16, 2, 256, "fp8e4m3", "f16", 16, ctx_lens=[33, 100, 18],
+              query_lens=[16, 3, 18]),
+    ]
+    return {w.name: w for w in ws}
+
+
 def full_configs() -> Dict[str, Workload]:
     """The five workloads at their stated sizes (c3 at both block sizes, c5 in fp8 and bf16)."""
     ws = [config_c1(), config_c2(), config_c3(16), config_c3(32), config_c4(), config_c4(prompt_len=1024),
@@ -237,11 +315,12 @@ def _normal(rng: np.random.Generator, shape, dtype: str) -> torch.Tensor:
 
 
 def q_values(wl: Workload) -> torch.Tensor:
-    """q [S][Hq][d] ~ N(0,1), rounded (RNE) to the q dtype."""
+    """q [total_q][Hq][d] ~ N(0,1), rounded (RNE) to the q dtype (total_q = S
+    for decode: one query token per sequence)."""
     if wl.same_candidates:
         per_prompt = _normal(_rng(wl, _STREAM_Q), (wl.num_prompts, wl.num_q_heads, wl.head_dim), wl.q_dtype)
         return per_prompt[torch.as_tensor(wl.parent, dtype=torch.long)].contiguous()
-    return _normal(_rng(wl, _STREAM_Q), (wl.num_seqs, wl.num_q_heads, wl.head_dim), wl.q_dtype)
+    return _normal(_rng(wl, _STREAM_Q), (wl.total_q, wl.num_q_heads, wl.head_dim), wl.q_dtype)
 
 
 def prompt_kv(wl: Workload, p: int) -> Tuple[torch.Tensor, torch.Tensor]:
@@ -260,9 +339,10 @@ def all_prompt_kv(wl: Workload, prompts: Optional[Sequence[int]] = None, threads
 
 
 def new_kv(wl: Workload) -> Tuple[torch.Tensor, torch.Tensor]:
-    """K and V of the token each sequence appends in the step: [S][Hkv][d] in src dtype."""
+    """K and V of the tokens the sequences append in the step, in sequence
+    order: [total_q][Hkv][d] in src dtype."""
     rng = _rng(wl, _STREAM_NEW_KV)
-    n = wl.num_prompts if wl.same_candidates else wl.num_seqs
+    n = wl.num_prompts if wl.same_candidates else wl.total_q
     shape = (n, wl.num_kv_heads, wl.head_dim)
     k = _normal(rng, shape, wl.src_dtype)
     v = _normal(rng, shape, wl.src_dtype)
