@@ -25,12 +25,14 @@ import torch
 import workloads as W
 
 METRIC = "paged decode attention: achieved KV HBM GB/s (% of peak) + µs/step, batch 256"
+METRIC_MULTI = "paged multi-token causal attention: achieved TFLOP/s or KV GB/s (roofline bound) + µs/step"
 HBM_PEAK_GBS = 8000.0
+MFMA_PEAK_TFLOPS = 2500.0   # dense bf16/f16 matrix cores (fp8 KV is widened to bf16/f16)
 DEFAULT_WORKLOAD = "c3_llama7b_bf16_bs16"
 
 
 def get_workload(name: str) -> W.Workload:
-    allw = {**W.full_configs(), **W.small_configs()}
+    allw = {**W.full_configs(), **W.small_configs(), **W.multi_token_configs(), **W.small_multi_token_configs()}
     if name not in allw:
         raise SystemExit(f"unknown workload {name}; choose from {sorted(allw)}")
     return allw[name]
@@ -81,6 +83,53 @@ def decode_bytes(wl: W.Workload) -> dict:
     return {"kv": kv, "total": kv + qo + tables, "tokens": int(n.sum())}
 
 
+def prefill_cost(wl: W.Workload) -> dict:
+    """Algorithmic work of one multi-token launch.  flops: 4 * D per
+    (query row, query head, visible token) -- QK^T and PV, 2 * D each --
+    with row i of a sequence seeing n - m + i + 1 tokens.  bytes: every cached
+    token's K and V row of every kv head once, q and out, the table entries in
+    use, the lengths and the row offsets."""
+    n = wl.context_lens.astype(np.int64)
+    m = wl.q_lens.astype(np.int64)
+    pairs = int((m * (n - m) + m * (m + 1) // 2).sum())
+    flops = 4 * wl.head_dim * wl.num_q_heads * pairs
+    kv = int(n.sum()) * 2 * wl.num_kv_heads * wl.head_dim * W.ELEM_BYTES[wl.kv_dtype]
+    qo = 2 * wl.total_q * wl.num_q_heads * wl.head_dim * W.ELEM_BYTES[wl.q_dtype]
+    tables = int((-(-n // wl.block_size)).sum()) * 4 + wl.num_seqs * 4 + (wl.num_seqs + 1) * 4
+    return {"flops": flops, "kv": kv, "total": kv + qo + tables, "tokens": int(n.sum()), "row_token_pairs": pairs}
+
+
+def cpu_baseline_prefill(wl: W.Workload, target_s: float = 12.0) -> dict:
+    """The fp64 oracle on one host core over the first sequences of a
+    multi-token workload, sized to about target_s seconds, in the unit of the
+    workload's roofline bound."""
+    from oracle.run import OracleRun
+
+    n = wl.context_lens.astype(np.int64)
+    m = wl.q_lens.astype(np.int64)
+    pairs = m * (n - m) + m * (m + 1) // 2
+    run = OracleRun(wl)
+    t = time.perf_counter()
+    run.prefill_rows(0, 0, min(int(m[0]), 4)) if m[0] > 0 else None
+    probe_pairs = sum(int(n[0] - m[0]) + i + 1 for i in range(min(int(m[0]), 4)))
+    rate = probe_pairs / max(time.perf_counter() - t, 1e-6)
+    k = int(np.searchsorted(np.cumsum(pairs), rate * target_s)) + 1
+    k = max(1, min(k, wl.num_seqs))
+    t = time.perf_counter()
+    run.prefill(list(range(k)))
+    dt = time.perf_counter() - t
+    cost = prefill_cost(wl)
+    done = int(pairs[:k].sum())
+    if cost["flops"] / (MFMA_PEAK_TFLOPS * 1e12) >= cost["total"] / (HBM_PEAK_GBS * 1e9):
+        value, unit = 4 * wl.head_dim * wl.num_q_heads * done / dt / 1e12, "TFLOP/s"
+    else:
+        toks = int(n[:k].sum())
+        value, unit = toks * 2 * wl.num_kv_heads * wl.head_dim * W.ELEM_BYTES[wl.kv_dtype] / dt / 1e9, "GB/s"
+    return {"value": round(value, 6), "unit": unit, "cores": 1, "kind": "oracle",
+            "sample": f"sequences 0..{k - 1} of {wl.num_seqs} ({done} of {int(pairs.sum())} (row, token) pairs), "
+                      f"{dt:.1f} s single-threaded fp64"}
+
+
 def cpu_baseline(wl: W.Workload, target_s: float = 12.0) -> dict:
     """The fp64 oracle on one host core over the first sequences of the
     workload, sized to about target_s seconds of CPU work."""
@@ -111,34 +160,40 @@ def cpu_baseline(wl: W.Workload, target_s: float = 12.0) -> dict:
                       f"{dt:.1f} s single-threaded fp64"}
 
 
-KERNEL_SOURCES = ("paged_kv_cache_449_amd/csrc/common.h", "paged_kv_cache_449_amd/csrc/decode_kernel.h",
-                  "paged_kv_cache_449_amd/csrc/decode.hip")
-TRAFFIC_FILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles", "decode_traffic.json")
+_CSRC = "paged_kv_cache_449_amd/csrc/"
+KERNEL_SOURCES = {
+    "decode": tuple(_CSRC + f for f in ("common.h", "decode_kernel.h", "decode_mfma.h", "decode.hip")),
+    "prefill": tuple(_CSRC + f for f in ("common.h", "decode_kernel.h", "decode_mfma.h", "prefill_kernel.h",
+                                         "prefill.hip")),
+}
+_PROFILES = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles")
+TRAFFIC_FILES = {"decode": os.path.join(_PROFILES, "decode_traffic.json"),
+                 "prefill": os.path.join(_PROFILES, "prefill_traffic.json")}
 
 
-def kernel_source_digest() -> str:
-    """sha256 over the decode kernel's sources: counters taken on other
-    sources do not describe this kernel."""
+def kernel_source_digest(kind: str = "decode") -> str:
+    """sha256 over a kernel's sources: counters taken on other sources do not
+    describe this kernel."""
     import hashlib
     h = hashlib.sha256()
     root = os.path.dirname(os.path.abspath(__file__))
-    for rel in KERNEL_SOURCES:
+    for rel in KERNEL_SOURCES[kind]:
         with open(os.path.join(root, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()
 
 
-def measured_traffic(wl_name: str):
-    """HBM bytes per decode launch from the committed rocprofv3 counter
-    summary, if it was taken on this workload and on the current kernel
-    sources; else None."""
+def measured_traffic(wl_name: str, kind: str = "decode"):
+    """HBM bytes per launch of the decode or multi-token kernel from the
+    committed rocprofv3 counter summary, if it was taken on this workload and
+    on the current kernel sources; else None."""
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(TRAFFIC_FILES[kind]) as f:
             rec = json.load(f)
     except (OSError, ValueError):
         return None
     entry = rec.get("workloads", {}).get(wl_name)
-    if not entry or rec.get("kernel_source_sha256") != kernel_source_digest():
+    if not entry or rec.get("kernel_source_sha256") != kernel_source_digest(kind):
         return None
     return entry.get("traffic_bytes_per_launch")
 
@@ -166,6 +221,49 @@ def swap_measurement(pool, n: int, reps: int = 5) -> dict:
         res[f"{name}_us"] = round(us, 1)
         res[f"{name}_GBs"] = round(nbytes / us / 1e3, 2)
     return res
+
+
+def multi_token_result(wl: W.Workload, args, kern_ms: np.ndarray, step_ms: float) -> dict:
+    """JSON line of a multi-token workload: the roofline is the matrix cores
+    when the launch's flops take longer at peak than its bytes, else HBM."""
+    c = prefill_cost(wl)
+    kern_s = float(kern_ms.mean()) / 1e3
+    mfma = c["flops"] / (MFMA_PEAK_TFLOPS * 1e12) >= c["total"] / (HBM_PEAK_GBS * 1e9)
+    if mfma:
+        achieved, peak, unit = c["flops"] / kern_s / 1e12, MFMA_PEAK_TFLOPS, "TFLOP/s"
+        value = c["flops"] / (step_ms / 1e3) / 1e12
+    else:
+        achieved, peak, unit = c["total"] / kern_s / 1e9, HBM_PEAK_GBS, "GB/s"
+        value = c["kv"] / (step_ms / 1e3) / 1e9
+    print(f"[bench] prefill kernel mean {kern_ms.mean() * 1e3:.1f} us; step {step_ms * 1e3:.1f} us; "
+          f"{c['flops'] / kern_s / 1e12:.1f} TFLOP/s, {c['total'] / kern_s / 1e9:.1f} GB/s", file=sys.stderr,
+          flush=True)
+    return {
+        "metric": METRIC_MULTI,
+        "value": round(value, 2),
+        "unit": unit,
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 4),
+        "us_per_step": round(step_ms * 1e3, 1),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "num_seqs": wl.num_seqs, "total_q": wl.total_q,
+                   "num_q_heads": wl.num_q_heads, "num_kv_heads": wl.num_kv_heads, "head_dim": wl.head_dim,
+                   "block_size": wl.block_size, "kv_dtype": wl.kv_dtype, "q_dtype": wl.q_dtype,
+                   "cached_tokens": c["tokens"], "row_token_pairs": c["row_token_pairs"],
+                   "flops_per_launch": c["flops"], "bytes_per_launch": c["total"], "placement": args.placement,
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "mfma" if mfma else "hbm", "achieved": round(achieved, 2), "peak": peak,
+                     "unit": unit, "frac": round(achieved / peak, 4), "traffic": measured_traffic(wl.name, "prefill"),
+                     "kernel": "paged_prefill_kernel", "kernel_us": round(float(kern_ms.mean()) * 1e3, 2),
+                     "tflops": round(c["flops"] / kern_s / 1e12, 2),
+                     "kv_gbs": round(c["total"] / kern_s / 1e9, 1)},
+    }
 
 
 def main(argv=None) -> int:
@@ -207,13 +305,19 @@ def main(argv=None) -> int:
     pool = sess.pool
     pt = wl.partition_tokens
 
+    multi = wl.multi_token
+
     def one_step(ev=None):
         pk.copy_blocks(pool, sess.pairs)
         pk.reshape_and_cache(pool, kn, vn, sess.slot_mapping)
         if ev is not None:
             ev[0].record()
-        pk.paged_attention_decode(pool, q, sess.block_tables, sess.context_lens, wl.scale, out=out,
-                                  partition_tokens=pt)
+        if multi:
+            pk.paged_attention_prefill(pool, q, sess.block_tables, sess.context_lens, sess.query_start, wl.scale,
+                                       out=out)
+        else:
+            pk.paged_attention_decode(pool, q, sess.block_tables, sess.context_lens, wl.scale, out=out,
+                                      partition_tokens=pt)
         if ev is not None:
             ev[1].record()
 
@@ -240,6 +344,13 @@ def main(argv=None) -> int:
     wall = time.perf_counter() - t0
     dec_ms = np.array([a.elapsed_time(b) for a, b in evs])
     step_ms = wall * 1e3 / args.steps
+    if multi:
+        res = multi_token_result(wl, args, dec_ms, step_ms)
+        if not args.no_cpu_baseline:
+            print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
+            res["cpu_baseline"] = cpu_baseline_prefill(wl)
+        print(json.dumps(res), flush=True)
+        return 0
     nb = decode_bytes(wl)
     dec_mean_s = float(dec_ms.mean()) / 1e3
     achieved = nb["total"] / dec_mean_s / 1e9
