@@ -266,6 +266,43 @@ def multi_token_result(wl: W.Workload, args, kern_ms: np.ndarray, step_ms: float
     }
 
 
+def block_manager_result(steps: int = 512, num_seqs: int = 256) -> dict:
+    """Host block manager: batched decode-step slot reservations per second
+    through the library, with the oracle's allocator model timed on the same
+    loop, and the simulator's accounting on the synthetic traces."""
+    from paged_kv_cache_449_amd import simulate
+    from oracle.allocator import AllocatorModel
+
+    speed = simulate.manager_speed(num_seqs=num_seqs, steps=steps)
+    bs, P = 16, 512
+    m = AllocatorModel(num_seqs * (-(-(P + steps) // bs) + 1), bs)
+    for s in range(num_seqs):
+        m.add_sequence(s, P)
+    t = time.perf_counter()
+    for _ in range(steps):
+        for s in range(num_seqs):
+            m.append(s, 1)
+    dt = time.perf_counter() - t
+    tr = W.serving_trace()
+    pt = W.prefix_trace()
+    return {
+        "metric": "host block manager: decode-step slot reservations per second (batched, 256 sequences)",
+        "value": round(speed["slots_per_s"], 1), "unit": "slots/s", "n_gpus": 0, "steps": steps, "warmup": 0,
+        "ms_per_step": round(speed["us_per_step"] / 1e3, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "int64", "data": "synthetic",
+        "config": {"workload": "block_manager_decode_steps", "num_seqs": num_seqs, "prompt_len": P,
+                   "block_size": bs, "parallelism": "host"},
+        "cpu_baseline": {"value": round(num_seqs * steps / dt, 1), "unit": "slots/s", "cores": 1, "kind": "oracle",
+                         "sample": f"the same {steps} steps x {num_seqs} sequences through the oracle's model"},
+        "simulation": {
+            "utilisation": simulate.utilisation(tr.prompt_lens, tr.output_lens, tr.max_new_tokens, tr.block_size),
+            "parallel_sampling": [simulate.parallel_sampling(P_, 4, g) for P_, g in ((1023, 64), (1023, 256),
+                                                                                     (4096, 64))],
+            "prefix_caching": simulate.prefix_caching(pt.tokens, pt.output_lens, num_blocks=4096, concurrency=64,
+                                                      block_size=pt.block_size)},
+    }
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -283,7 +320,12 @@ def main(argv=None) -> int:
                     help="shuffled: blocks from a seeded random free list (the workload); sequential: "
                          "the free list in id order, so each sequence's blocks are contiguous (the "
                          "paged-vs-contiguous comparison)")
+    ap.add_argument("--block-manager", action="store_true",
+                    help="host block manager only (no GPU): reservation rate, oracle beside it, trace accounting")
     args = ap.parse_args(argv)
+    if args.block_manager:
+        print(json.dumps(block_manager_result()), flush=True)
+        return 0
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU: this build runs the decode path on a single MI355X "

@@ -53,7 +53,8 @@ typedef enum {
   KV_ERR_UNSUPPORTED = 2,  /* dtype / head_dim / block_size combination not built */
   KV_ERR_OOM = 3,          /* kv_pool_create could not allocate */
   KV_ERR_HIP = 4,          /* a HIP runtime call or kernel launch failed */
-  KV_ERR_WORKSPACE = 5     /* workspace missing or smaller than required */
+  KV_ERR_WORKSPACE = 5,    /* workspace missing or smaller than required */
+  KV_ERR_NO_BLOCKS = 6     /* block manager: no free or evictable block left */
 } kv_status_t;
 
 typedef enum {

@@ -25,7 +25,7 @@ from .block_manager import BlockManager, PoolExhausted  # noqa: F401
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libpagedkv.so")
 
-KV_OK, KV_ERR_INVALID_ARG, KV_ERR_UNSUPPORTED, KV_ERR_OOM, KV_ERR_HIP, KV_ERR_WORKSPACE = range(6)
+KV_OK, KV_ERR_INVALID_ARG, KV_ERR_UNSUPPORTED, KV_ERR_OOM, KV_ERR_HIP, KV_ERR_WORKSPACE, KV_ERR_NO_BLOCKS = range(7)
 KV_F32, KV_F16, KV_BF16, KV_FP8_E4M3FN = range(4)
 KV_SWAP_OUT, KV_SWAP_IN = range(2)
 
@@ -65,6 +65,25 @@ def lib() -> ctypes.CDLL:
         L.paged_attention_prefill_workspace_size.argtypes = [vp, i32, ctypes.POINTER(sz)]
         L.kv_status_string.argtypes = [ctypes.c_int]
         L.kv_status_string.restype = ctypes.c_char_p
+        # host block manager (block_manager.h)
+        u64 = ctypes.c_uint64
+        L.bm_create.argtypes = [i64, i32, vp, i32, pp]
+        L.bm_destroy.argtypes = [vp]
+        L.bm_destroy.restype = None
+        L.bm_add_sequence.argtypes = [vp, i64, vp, i32, u64, vp, vp]
+        L.bm_fork.argtypes = [vp, i64, vp, i32]
+        L.bm_append_slots.argtypes = [vp, i64, vp, i32, vp, vp, vp]
+        L.bm_append_batch.argtypes = [vp, vp, vp, i32, vp, vp, vp, vp]
+        L.bm_free.argtypes = [vp, i64]
+        L.bm_num_free_blocks.argtypes = [vp, vp]
+        L.bm_sequence_info.argtypes = [vp, i64, vp, vp]
+        L.bm_block_table.argtypes = [vp, i64, vp, i32]
+        L.bm_block_tables.argtypes = [vp, vp, i32, i32, vp, vp]
+        L.bm_ref_count.argtypes = [vp, i32, vp]
+        L.bm_stats.argtypes = [vp, vp]
+        for fn in ("bm_create", "bm_add_sequence", "bm_fork", "bm_append_slots", "bm_append_batch", "bm_free", "bm_num_free_blocks",
+                   "bm_sequence_info", "bm_block_table", "bm_block_tables", "bm_ref_count", "bm_stats"):
+            getattr(L, fn).restype = ctypes.c_int
         for fn in ("kv_pool_create", "kv_pool_create_from", "kv_pool_destroy", "kv_pool_info", "kv_pool_set_scales",
                    "reshape_and_cache", "paged_attention_decode", "paged_attention_workspace_size", "copy_blocks",
                    "swap_blocks", "paged_attention_prefill", "paged_attention_prefill_workspace_size"):

@@ -2,8 +2,9 @@
 
     python -m paged_kv_cache_449_amd.build
 
-Compiles every csrc/*.hip to an object under _build/ (in parallel), then
-links paged_kv_cache_449_amd/libpagedkv.so.  Always recompiles.
+Compiles every csrc/*.hip (hipcc, gfx950) and csrc/*.cpp (host C++) to an
+object under _build/ (in parallel), then links
+paged_kv_cache_449_amd/libpagedkv.so.  Always recompiles.
 """
 from __future__ import annotations
 
@@ -30,9 +31,17 @@ CFLAGS = [
 ]
 
 
+CXX = os.environ.get("CXX", "g++")
+HOST_CFLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra", "-I", INCLUDE, "-I", CSRC]
+
+
 def _compile(src: str) -> str:
-    obj = os.path.join(BUILD, os.path.basename(src)[:-4] + ".o")
-    cmd = [HIPCC, *CFLAGS, "-c", src, "-o", obj]
+    stem, ext = os.path.splitext(os.path.basename(src))
+    obj = os.path.join(BUILD, stem + ".o")
+    if ext == ".cpp":   # host-only code (the block manager)
+        cmd = [CXX, *HOST_CFLAGS, "-c", src, "-o", obj]
+    else:
+        cmd = [HIPCC, *CFLAGS, "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     noise = "'-packed-fp32-ops' is not a recognized feature"
     msg = "\n".join(line for line in (r.stdout + r.stderr).splitlines() if noise not in line)
@@ -45,7 +54,7 @@ def _compile(src: str) -> str:
 
 def build(jobs: int = 0) -> str:
     os.makedirs(BUILD, exist_ok=True)
-    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.cpp")))
     jobs = jobs or min(16, os.cpu_count() or 4, len(srcs))
     with ThreadPoolExecutor(jobs) as ex:
         objs = list(ex.map(_compile, srcs))

@@ -134,6 +134,7 @@ extern "C" const char* kv_status_string(kv_status_t status) {
     case KV_ERR_OOM: return "device allocation failed";
     case KV_ERR_HIP: return "HIP runtime or launch error";
     case KV_ERR_WORKSPACE: return "workspace missing or too small";
+    case KV_ERR_NO_BLOCKS: return "no free or evictable block left";
   }
   return "unknown status";
 }

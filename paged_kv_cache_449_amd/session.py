@@ -64,16 +64,7 @@ class DecodeSession:
         mapping, copy pairs, block tables, lengths and query row offsets."""
         self.seqs = list(seqs)
         counts = [1] * len(self.seqs) if counts is None else [int(c) for c in counts]
-        slots = np.empty(sum(counts), dtype=np.int64)
-        pairs = []
-        i = 0
-        for s, cnt in zip(self.seqs, counts):
-            for _ in range(cnt):
-                slot, pair = self.manager.append_slot(s)
-                slots[i] = slot
-                i += 1
-                if pair is not None:
-                    pairs.append(pair)
+        slots, pairs = self.manager.append_batch(self.seqs, counts)
         self.slot_mapping = self._dev(slots)
         self.pairs = self._dev(np.asarray(pairs, dtype=np.int32).reshape(-1, 2))
         self.block_tables = self._dev(self.manager.block_tables(self.seqs, max_blocks))

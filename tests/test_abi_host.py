@@ -1,12 +1,13 @@
 """CPU-only checks of the boundary and of the host logic above it.
 
-* libpagedkv.so loads and exports every function include/pagedkv.h declares
+* libpagedkv.so loads and exports every function include/*.h declares
   (no compute call: there may be no GPU here).
 * The library's host block manager produces exactly the oracle paging
   emulation's block tables, slots and copy-on-write pairs (index work:
   bit-exact), and honours its own invariants.
 """
 import ctypes
+import glob
 import os
 import re
 
@@ -18,20 +19,32 @@ from conftest import ROOT
 from oracle.paging import plan as oracle_plan
 
 HEADER = os.path.join(ROOT, "include", "pagedkv.h")
+BM_HEADER = os.path.join(ROOT, "include", "block_manager.h")
 
 
-def _declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)))
+def _declared_functions(path=None):
+    paths = [path] if path else sorted(glob.glob(os.path.join(ROOT, "include", "*.h")))
+    names = set()
+    for p in paths:
+        text = open(p).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        names |= set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M))
+    return sorted(names)
 
 
 def test_header_declares_the_four_calls_and_helpers():
-    names = _declared_functions()
+    names = _declared_functions(HEADER)
     for n in ["kv_pool_create", "reshape_and_cache", "paged_attention_decode", "copy_blocks", "swap_blocks",
               "paged_attention_prefill"]:
         assert n in names
     assert len(names) == 13, names
+
+
+def test_block_manager_header_declares_its_calls():
+    names = _declared_functions(BM_HEADER)
+    assert names == sorted(["bm_create", "bm_destroy", "bm_add_sequence", "bm_fork", "bm_append_slots", "bm_append_batch", "bm_free",
+                            "bm_num_free_blocks", "bm_sequence_info", "bm_block_table", "bm_block_tables",
+                            "bm_ref_count", "bm_stats"]), names
 
 
 def test_library_exports_every_declared_symbol():

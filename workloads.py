@@ -371,3 +371,58 @@ def fp8_scales(wl: Workload, threads: int = 8) -> Tuple[float, float]:
     ks = float(np.float32(km) / np.float32(448.0))
     vs = float(np.float32(vm) / np.float32(448.0))
     return ks, vs
+
+
+# --------------------------------------------------------------------------
+# request traces for the host block manager's simulator
+
+_STREAM_TRACE = 5
+
+
+def _trace_rng(index: int, key: int = 0) -> np.random.Generator:
+    return np.random.default_rng(np.random.SeedSequence(449_000 + index, spawn_key=(_STREAM_TRACE, key)))
+
+
+@dataclasses.dataclass(frozen=True)
+class RequestTrace:
+    """Requests admitted together: prompt and output lengths per request, the
+    length a contiguous allocator would reserve for each (prompt +
+    max_new_tokens), and optional prompt token ids."""
+    name: str
+    prompt_lens: Tuple[int, ...]
+    output_lens: Tuple[int, ...]
+    max_new_tokens: int
+    block_size: int = 16
+    tokens: Tuple[Tuple[int, ...], ...] = ()
+
+
+def serving_trace(num_requests: int = 256, index: int = 20, block_size: int = 16, max_new_tokens: int = 2048,
+                  name: str = "serving_lognormal") -> RequestTrace:
+    """Prompts lognormal(ln 512, 0.8) clipped to [16, 4096] (the LLaMA-7B
+    decode law); outputs lognormal(ln 128, 1.0) clipped to [1, max_new_tokens]
+    -- chat-like length mixes standing in for the ShareGPT traces the pages
+    mention."""
+    rng = _trace_rng(index)
+    p = np.clip(np.rint(rng.lognormal(math.log(512), 0.8, num_requests)), 16, 4096).astype(int)
+    o = np.clip(np.rint(rng.lognormal(math.log(128), 1.0, num_requests)), 1, max_new_tokens).astype(int)
+    return RequestTrace(name, tuple(p.tolist()), tuple(o.tolist()), max_new_tokens, block_size)
+
+
+def prefix_trace(num_requests: int = 512, num_templates: int = 8, index: int = 21, block_size: int = 16,
+                 vocab: int = 32000, name: str = "shared_system_prompts") -> RequestTrace:
+    """Requests that open with one of `num_templates` system prompts (lengths
+    U[64, 1024], picked with Zipf-like weights 1/(k+1)) followed by a user
+    part of U[16, 512] tokens; token ids uniform over the vocabulary; outputs
+    lognormal(ln 128, 1.0) clipped to [1, 1024]."""
+    rng = _trace_rng(index)
+    templates = [rng.integers(0, vocab, size=int(rng.integers(64, 1025))) for _ in range(num_templates)]
+    w = 1.0 / np.arange(1, num_templates + 1)
+    pick = rng.choice(num_templates, size=num_requests, p=w / w.sum())
+    toks, plens = [], []
+    for t in pick:
+        user = rng.integers(0, vocab, size=int(rng.integers(16, 513)))
+        seq = np.concatenate([templates[t], user]).astype(int)
+        toks.append(tuple(seq.tolist()))
+        plens.append(len(seq))
+    o = np.clip(np.rint(rng.lognormal(math.log(128), 1.0, num_requests)), 1, 1024).astype(int)
+    return RequestTrace(name, tuple(plens), tuple(o.tolist()), 1024, block_size, tuple(toks))
