@@ -32,7 +32,8 @@ DEFAULT_WORKLOAD = "c3_llama7b_bf16_bs16"
 
 
 def get_workload(name: str) -> W.Workload:
-    allw = {**W.full_configs(), **W.small_configs(), **W.multi_token_configs(), **W.small_multi_token_configs()}
+    allw = {**W.full_configs(), **W.small_configs(), **W.multi_token_configs(), **W.small_multi_token_configs(),
+            **W.variant_configs(), **W.small_variant_configs()}
     if name not in allw:
         raise SystemExit(f"unknown workload {name}; choose from {sorted(allw)}")
     return allw[name]
@@ -47,6 +48,8 @@ def build_session(wl: W.Workload, device, prompt_batch: int = 16, free_order=Non
     ks, vs = W.fp8_scales(wl)
     pool = pk.KVPool(wl.num_blocks, wl.block_size, wl.num_kv_heads, wl.head_dim, W.TORCH_DTYPE[wl.kv_dtype],
                      device, ks, vs)
+    if wl.head_scales:
+        pk.kv_pool_set_head_scales(pool, *W.fp8_head_scales(wl))
     # every slot starts as all-ones bytes (NaN in every KV dtype)
     pool.k_cache.view(torch.uint8).fill_(W.POISON_BYTE)
     pool.v_cache.view(torch.uint8).fill_(W.POISON_BYTE)

@@ -116,6 +116,21 @@ kv_status_t kv_pool_info(const kv_pool_t* pool, void** k, void** v, size_t* byte
 kv_status_t kv_pool_set_scales(kv_pool_t* pool, float k_scale, float v_scale);
 
 /*
+ * kv_pool_set_head_scales -- fp8 pools: one k and one v scale per kv head
+ * instead of one per tensor, for heads whose value ranges differ (a variant
+ * of the fp8 KV cache option, "vLLM KV Cache 实现机制" §2.3 table).
+ * k_scales and v_scales are host arrays of num_kv_heads fp32 values, each
+ * finite and > 0; they are copied into device memory the pool owns.  From
+ * then on reshape_and_cache encodes head h with its own scales and the
+ * attention calls decode with them.  Both NULL returns to the per-tensor
+ * scales (kv_pool_set_scales also does).  Call it while no kernel that
+ * reads or writes the pool is in flight.  KV_ERR_INVALID_ARG: not an fp8
+ * pool, exactly one array NULL, or a bad value; KV_ERR_OOM / KV_ERR_HIP for
+ * the device copy.
+ */
+kv_status_t kv_pool_set_head_scales(kv_pool_t* pool, const float* k_scales, const float* v_scales);
+
+/*
  * reshape_and_cache -- store the K and V of num_tokens new tokens into their
  * slots ("vLLM 与 KV Cache": why a KV cache -- only the new token's K/V is
  * computed and appended; how-it-works points 2-3).

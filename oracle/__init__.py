@@ -60,17 +60,18 @@ def lib() -> ctypes.CDLL:
         L.oracle_e4m3_to_f64.restype = f64
         L.oracle_f32_to_e4m3_sat.argtypes = [f32]
         L.oracle_f32_to_e4m3_sat.restype = ctypes.c_uint8
-        L.oracle_reshape_and_cache.argtypes = [vp, vp, i32, i64, i32, i32, i32, f32, f32, vp, vp, i32, vp, i64]
+        L.oracle_reshape_and_cache.argtypes = [vp, vp, i32, i64, i32, i32, i32, f32, f32, vp, vp, i32, vp, i64, vp,
+                                               vp]
         L.oracle_reshape_and_cache.restype = i32
         L.oracle_copy_blocks.argtypes = [vp, vp, i64, i64, vp, i64]
         L.oracle_copy_blocks.restype = i32
         L.oracle_decode.argtypes = [vp, vp, i32, i64, i32, i32, i32, f64, f64, vp, i32, i32, i32,
-                                    vp, i32, vp, f64, vp, i32, vp]
+                                    vp, i32, vp, f64, vp, i32, vp, vp, vp]
         L.oracle_decode.restype = i32
         L.oracle_swap_blocks.argtypes = [vp, vp, i64, vp, vp, i64, i64, vp, i64, i32]
         L.oracle_swap_blocks.restype = i32
         L.oracle_prefill.argtypes = [vp, vp, i32, i64, i32, i32, i32, f64, f64, vp, i32, i32, i32,
-                                     vp, i32, vp, vp, f64, vp]
+                                     vp, i32, vp, vp, f64, vp, vp, vp]
         L.oracle_prefill.restype = i32
         L.oracle_kv_footprint_bytes.argtypes = [i32, i32, i32, i64, i32]
         L.oracle_kv_footprint_bytes.restype = f64
@@ -124,15 +125,26 @@ def kv_footprint_bytes(layers: int, heads: int, head_dim: int, tokens: int, dtyp
 
 # ---------------------------------------------------------------- pool emulation
 
+def _opt(a):
+    return None if a is None else _ptr(a)
+
+
 class HostPool:
     """Host copy of the K and V pools, laid out [num_blocks][H][B][D] of the
     pool dtype, stored as raw bytes.  New pools are filled with 0xFF (NaN in
-    every supported dtype) so that any read of an unowned slot shows up."""
+    every supported dtype) so that any read of an unowned slot shows up.
+    fp8 pools use one scale per tensor, or one per kv head when head_scales
+    = (k [H], v [H]) fp32 arrays are given."""
 
     def __init__(self, num_blocks: int, block_size: int, num_kv_heads: int, head_dim: int, dtype: str,
-                 k_scale: float = 1.0, v_scale: float = 1.0, fill: int = 0xFF):
+                 k_scale: float = 1.0, v_scale: float = 1.0, fill: int = 0xFF, head_scales=None):
         self.num_blocks, self.block_size, self.num_kv_heads, self.head_dim = num_blocks, block_size, num_kv_heads, head_dim
         self.dtype, self.k_scale, self.v_scale = dtype, float(k_scale), float(v_scale)
+        self.k_head = self.v_head = None
+        if head_scales is not None:
+            self.k_head = np.ascontiguousarray(head_scales[0], dtype=np.float32)
+            self.v_head = np.ascontiguousarray(head_scales[1], dtype=np.float32)
+            assert self.k_head.shape == (num_kv_heads,) and self.v_head.shape == (num_kv_heads,)
         self.block_bytes = num_kv_heads * block_size * head_dim * ELEM_BYTES[dtype]
         self.k = np.full(num_blocks * self.block_bytes, fill, dtype=np.uint8)
         self.v = np.full(num_blocks * self.block_bytes, fill, dtype=np.uint8)
@@ -144,7 +156,7 @@ class HostPool:
         rc = lib().oracle_reshape_and_cache(_ptr(self.k), _ptr(self.v), DT_CODE[self.dtype], self.num_blocks,
                                            self.block_size, self.num_kv_heads, self.head_dim,
                                            self.k_scale, self.v_scale, _ptr(kr), _ptr(vr), DT_CODE[src_dtype],
-                                           _ptr(slots), T)
+                                           _ptr(slots), T, _opt(self.k_head), _opt(self.v_head))
         if rc:
             raise OracleError(f"oracle_reshape_and_cache rc={rc}")
 
@@ -181,7 +193,7 @@ class HostPool:
         rc = lib().oracle_prefill(_ptr(self.k), _ptr(self.v), DT_CODE[self.dtype], self.num_blocks, self.block_size,
                                   self.num_kv_heads, self.head_dim, self.k_scale, self.v_scale, _ptr(qr),
                                   DT_CODE[q_dtype], S, num_q_heads, _ptr(bt), max_blocks, _ptr(cl), _ptr(qs),
-                                  float(scale), _ptr(out))
+                                  float(scale), _ptr(out), _opt(self.k_head), _opt(self.v_head))
         if rc:
             raise OracleError(f"oracle_prefill rc={rc}")
         return out
@@ -198,7 +210,7 @@ class HostPool:
                                  self.num_kv_heads, self.head_dim, self.k_scale, self.v_scale, _ptr(qr),
                                  DT_CODE[q_dtype], S, num_q_heads, _ptr(bt), max_blocks, _ptr(cl), float(scale),
                                  None if sel is None else _ptr(sel), 0 if sel is None else sel.shape[0],
-                                 _ptr(out))
+                                 _ptr(out), _opt(self.k_head), _opt(self.v_head))
         if rc:
             raise OracleError(f"oracle_decode rc={rc}")
         return out

@@ -159,12 +159,13 @@ static float src_as_f32(const void* base, int dt, size_t idx) {
  * Write the K/V of T tokens into their slots.  Slot s means token offset
  * s mod B of physical block floor(s / B).  A negative slot skips the token.
  * Same source and pool dtype: bytes are copied.  fp8 pool: each element is
- * encoded as E4M3FN of (fp32(x) / fp32(scale)).
+ * encoded as E4M3FN of (fp32(x) / fp32(scale)), where scale is the tensor's
+ * scale, or head h's scale when k_head / v_head ([H] each) are given.
  * k, v: [T][H][D] in src_dtype.
  */
 int oracle_reshape_and_cache(void* kpool, void* vpool, int pool_dtype, int64_t num_blocks, int B, int H, int D,
                              float k_scale, float v_scale, const void* k, const void* v, int src_dtype,
-                             const int64_t* slots, int64_t T) {
+                             const int64_t* slots, int64_t T, const float* k_head, const float* v_head) {
   if (!kpool || !vpool || !k || !v || !slots || B <= 0 || H <= 0 || D <= 0) return OR_BAD_ARG;
   int quant = pool_dtype == OR_FP8E4M3 && src_dtype != OR_FP8E4M3;
   if (!quant && src_dtype != pool_dtype) return OR_BAD_ARG;
@@ -181,9 +182,10 @@ int oracle_reshape_and_cache(void* kpool, void* vpool, int pool_dtype, int64_t n
         memcpy((char*)kpool + dst * eb, (const char*)k + src * sb, D * eb);
         memcpy((char*)vpool + dst * eb, (const char*)v + src * sb, D * eb);
       } else {
+        const float ks = k_head ? k_head[h] : k_scale, vs = v_head ? v_head[h] : v_scale;
         for (int j = 0; j < D; ++j) {
-          float xk = src_as_f32(k, src_dtype, src + j) / k_scale;
-          float xv = src_as_f32(v, src_dtype, src + j) / v_scale;
+          float xk = src_as_f32(k, src_dtype, src + j) / ks;
+          float xv = src_as_f32(v, src_dtype, src + j) / vs;
           ((uint8_t*)kpool)[dst + j] = oracle_f32_to_e4m3_sat(xk);
           ((uint8_t*)vpool)[dst + j] = oracle_f32_to_e4m3_sat(xv);
         }
@@ -232,11 +234,15 @@ int oracle_swap_blocks(void* kpool, void* vpool, int64_t num_blocks, void* khost
 /* ------------------------------------------------------------------ decode */
 
 /* Contiguous K and V (fp64, dequantised) of the first n tokens of sequence s,
- * KV head hk: token t lives at slot t % B of block block_tables[s][t / B]. */
+ * KV head hk: token t lives at slot t % B of block block_tables[s][t / B].
+ * fp8 codes are multiplied by the tensor's scale, or head hk's scale when
+ * k_head / v_head are given. */
 static int materialise_kv(const void* kpool, const void* vpool, int kv_dtype, int64_t num_blocks, int B, int H,
-                          int D, double k_scale, double v_scale, const int32_t* block_tables, int max_blocks,
-                          int s, int hk, int n, double* Kc, double* Vc) {
+                          int D, double k_scale, double v_scale, const float* k_head, const float* v_head,
+                          const int32_t* block_tables, int max_blocks, int s, int hk, int n, double* Kc, double* Vc) {
   int fp8 = kv_dtype == OR_FP8E4M3;
+  if (k_head) k_scale = k_head[hk];
+  if (v_head) v_scale = v_head[hk];
   for (int t = 0; t < n; ++t) {
     int32_t blk = block_tables[(size_t)s * max_blocks + t / B];
     int o = t % B;
@@ -281,7 +287,8 @@ static void attend(const double* qd, const double* Kc, const double* Vc, int nt,
  * is NULL):
  *   n = context_lens[s]  (1 <= n <= max_blocks * B)
  *   for token t < n: blk = block_tables[s][t / B], o = t % B,
- *     Kc[t][:] = K[blk][hkv][o][:] * k_scale (fp8 pools only), same for V,
+ *     Kc[t][:] = K[blk][hkv][o][:] * k_scale (fp8 pools only; the scale of
+ *     kv head hkv when k_head / v_head are given), same for V,
  *     where hkv = hq / (Hq / H)
  *   score_t = scale * sum_j q[s][hq][j] * Kc[t][j]
  *   m = max_t score_t, p_t = exp(score_t - m), l = sum_t p_t
@@ -290,7 +297,7 @@ static void attend(const double* qd, const double* Kc, const double* Vc, int nt,
 int oracle_decode(const void* kpool, const void* vpool, int kv_dtype, int64_t num_blocks, int B, int H, int D,
                   double k_scale, double v_scale, const void* q, int q_dtype, int S, int Hq,
                   const int32_t* block_tables, int max_blocks, const int32_t* context_lens, double scale,
-                  const int32_t* seqs, int n_seqs, double* out) {
+                  const int32_t* seqs, int n_seqs, double* out, const float* k_head, const float* v_head) {
   if (!kpool || !vpool || !q || !block_tables || !context_lens || !out) return OR_BAD_ARG;
   if (B <= 0 || H <= 0 || D <= 0 || Hq <= 0 || Hq % H != 0 || max_blocks <= 0) return OR_BAD_ARG;
   int g = Hq / H;
@@ -306,8 +313,8 @@ int oracle_decode(const void* kpool, const void* vpool, int kv_dtype, int64_t nu
     double* qd = (double*)malloc(sizeof(double) * (size_t)D);
     int rc = (Kc && Vc && sc && qd) ? OR_OK : OR_NOMEM;
     for (int hk = 0; hk < H && rc == OR_OK; ++hk) {
-      rc = materialise_kv(kpool, vpool, kv_dtype, num_blocks, B, H, D, k_scale, v_scale, block_tables,
-                          max_blocks, s, hk, n, Kc, Vc);
+      rc = materialise_kv(kpool, vpool, kv_dtype, num_blocks, B, H, D, k_scale, v_scale, k_head, v_head,
+                          block_tables, max_blocks, s, hk, n, Kc, Vc);
       for (int gi = 0; gi < g && rc == OR_OK; ++gi) {
         int hq = hk * g + gi;
         size_t qoff = ((size_t)s * Hq + hq) * D;
@@ -336,7 +343,8 @@ int oracle_decode(const void* kpool, const void* vpool, int kv_dtype, int64_t nu
 int oracle_prefill(const void* kpool, const void* vpool, int kv_dtype, int64_t num_blocks, int B, int H, int D,
                    double k_scale, double v_scale, const void* q, int q_dtype, int S, int Hq,
                    const int32_t* block_tables, int max_blocks, const int32_t* context_lens,
-                   const int32_t* query_start, double scale, double* out) {
+                   const int32_t* query_start, double scale, double* out, const float* k_head,
+                   const float* v_head) {
   if (!kpool || !vpool || !q || !block_tables || !context_lens || !query_start || !out) return OR_BAD_ARG;
   if (B <= 0 || H <= 0 || D <= 0 || Hq <= 0 || Hq % H != 0 || max_blocks <= 0) return OR_BAD_ARG;
   int g = Hq / H;
@@ -351,8 +359,8 @@ int oracle_prefill(const void* kpool, const void* vpool, int kv_dtype, int64_t n
     double* qd = (double*)malloc(sizeof(double) * (size_t)D);
     int rc = (Kc && Vc && sc && qd) ? OR_OK : OR_NOMEM;
     for (int hk = 0; hk < H && rc == OR_OK; ++hk) {
-      rc = materialise_kv(kpool, vpool, kv_dtype, num_blocks, B, H, D, k_scale, v_scale, block_tables,
-                          max_blocks, s, hk, n, Kc, Vc);
+      rc = materialise_kv(kpool, vpool, kv_dtype, num_blocks, B, H, D, k_scale, v_scale, k_head, v_head,
+                          block_tables, max_blocks, s, hk, n, Kc, Vc);
       for (int i = 0; i < m && rc == OR_OK; ++i) {
         int seen = n - m + i + 1;
         for (int gi = 0; gi < g; ++gi) {

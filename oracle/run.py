@@ -32,7 +32,10 @@ class OracleRun:
         self.plan = plan(wl, order)
         ks, vs = scales if scales is not None else workloads.fp8_scales(wl)
         self.k_scale, self.v_scale = ks, vs
-        self.pool = HostPool(wl.num_blocks, wl.block_size, wl.num_kv_heads, wl.head_dim, wl.kv_dtype, ks, vs)
+        hs = workloads.fp8_head_scales(wl) if wl.head_scales else None
+        self.head_scales = hs
+        self.pool = HostPool(wl.num_blocks, wl.block_size, wl.num_kv_heads, wl.head_dim, wl.kv_dtype, ks, vs,
+                             head_scales=hs)
         todo = range(wl.num_prompts) if prompts is None else prompts
         for p in todo:
             if wl.prompt_lens[p] == 0:

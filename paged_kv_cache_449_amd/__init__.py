@@ -55,6 +55,7 @@ def lib() -> ctypes.CDLL:
         L.kv_pool_destroy.argtypes = [vp]
         L.kv_pool_info.argtypes = [vp, pp, pp, ctypes.POINTER(sz), ctypes.POINTER(i64)]
         L.kv_pool_set_scales.argtypes = [vp, f32, f32]
+        L.kv_pool_set_head_scales.argtypes = [vp, vp, vp]
         L.reshape_and_cache.argtypes = [vp, vp, vp, ctypes.c_int, vp, i32, vp]
         L.paged_attention_decode.argtypes = [vp, vp, ctypes.c_int, vp, vp, i32, vp, i32, i32, f32, i32, vp, sz, vp]
         L.paged_attention_workspace_size.argtypes = [vp, i32, i32, i32, i32, ctypes.POINTER(sz)]
@@ -85,6 +86,7 @@ def lib() -> ctypes.CDLL:
                    "bm_sequence_info", "bm_block_table", "bm_block_tables", "bm_ref_count", "bm_stats"):
             getattr(L, fn).restype = ctypes.c_int
         for fn in ("kv_pool_create", "kv_pool_create_from", "kv_pool_destroy", "kv_pool_info", "kv_pool_set_scales",
+                   "kv_pool_set_head_scales",
                    "reshape_and_cache", "paged_attention_decode", "paged_attention_workspace_size", "copy_blocks",
                    "swap_blocks", "paged_attention_prefill", "paged_attention_prefill_workspace_size"):
             getattr(L, fn).restype = ctypes.c_int
@@ -137,6 +139,7 @@ class KVPool:
                                              ctypes.byref(h)), "kv_pool_create_from")
         self.handle = h
         self.k_scale, self.v_scale = 1.0, 1.0
+        self.head_scales = None
         if dtype == torch.float8_e4m3fn:
             kv_pool_set_scales(self, k_scale, v_scale)
         self._workspace: Optional[torch.Tensor] = None
@@ -166,6 +169,24 @@ class KVPool:
 def kv_pool_set_scales(pool: KVPool, k_scale: float, v_scale: float) -> None:
     _check(lib().kv_pool_set_scales(pool.handle, float(k_scale), float(v_scale)), "kv_pool_set_scales")
     pool.k_scale, pool.v_scale = float(k_scale), float(v_scale)
+    pool.head_scales = None
+
+
+def kv_pool_set_head_scales(pool: KVPool, k_scales, v_scales) -> None:
+    """fp8 pools: one scale per kv head (sequences of num_kv_heads floats);
+    None, None returns to the per-tensor scales."""
+    import numpy as np
+    if k_scales is None and v_scales is None:
+        _check(lib().kv_pool_set_head_scales(pool.handle, None, None), "kv_pool_set_head_scales")
+        pool.head_scales = None
+        return
+    k = np.ascontiguousarray(k_scales, dtype=np.float32)
+    v = np.ascontiguousarray(v_scales, dtype=np.float32)
+    if k.shape != (pool.num_kv_heads,) or v.shape != (pool.num_kv_heads,):
+        raise ValueError(f"need {pool.num_kv_heads} scales each")
+    with torch.cuda.device(pool.device):
+        _check(lib().kv_pool_set_head_scales(pool.handle, k.ctypes.data, v.ctypes.data), "kv_pool_set_head_scales")
+    pool.head_scales = (k.copy(), v.copy())
 
 
 def kv_pool_info(pool: KVPool):

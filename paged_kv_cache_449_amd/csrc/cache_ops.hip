@@ -22,6 +22,7 @@ struct CacheWriteParams {
   int32_t log2_bs;
   float k_scale;
   float v_scale;
+  const float* head_scales;  // [2][num_kv_heads] per-head scales (k then v), or null
 };
 
 // One lane per 16 bytes of destination row.  Rows are (token, kv head) pairs
@@ -54,7 +55,7 @@ __global__ __launch_bounds__(256) void cache_write_kernel(CacheWriteParams p) {
   } else {
     // fp8 destination: VEC = 16 codes from 16 source elements.
     static_assert(DE == 1, "only fp8 pools quantise");
-    const float scale = is_v ? p.v_scale : p.k_scale;
+    const float scale = p.head_scales ? p.head_scales[(is_v ? p.num_kv_heads : 0) + h] : (is_v ? p.v_scale : p.k_scale);
     constexpr int SW = 16 * SE / 4;  // source 32-bit words
     uint32_t w[SW];
 #pragma unroll
@@ -250,6 +251,7 @@ extern "C" kv_status_t reshape_and_cache(kv_pool_t* pool, const void* k_new, con
   p.log2_bs = pool->log2_block_size;
   p.k_scale = pool->k_scale;
   p.v_scale = pool->v_scale;
+  p.head_scales = pool->per_head ? pool->head_scales : nullptr;
   hipStream_t st = (hipStream_t)stream;
   const int D = pool->head_dim;
   if (src_dtype == pool->dtype) {

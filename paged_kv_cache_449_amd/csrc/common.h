@@ -19,6 +19,8 @@ struct kv_pool {
   bool owned;
   float k_scale;
   float v_scale;
+  float* head_scales;   // device [2][num_kv_heads] (k then v) fp8 per-head scales
+  bool per_head;        // head_scales in use
   int device;
   int num_cus;
 };

@@ -118,6 +118,8 @@ extern "C" kv_status_t paged_attention_decode(const kv_pool_t* pool, const void*
   const bool fp8 = pool->dtype == KV_FP8_E4M3FN;
   p.q_scale = scale * kLog2e * (fp8 ? pool->k_scale : 1.0f);
   p.v_scale = fp8 ? pool->v_scale : 1.0f;
+  p.qk_scale = scale * kLog2e;
+  p.head_scales = fp8 && pool->per_head ? pool->head_scales : nullptr;
 
   // a wave load covers 64 / (lanes per token row) tokens of one block
   const int lanes_per_row = D * (int)elem_bytes(pool->dtype) / 16;

@@ -72,7 +72,17 @@ struct DecodeParams {
   int32_t num_workers;   // multiple of 8
   float q_scale;         // softmax scale * log2(e) * k_scale
   float v_scale;
+  const float* head_scales;  // fp8 per-kv-head scales [2][num_kv_heads] (k then v), or null
+  float qk_scale;            // softmax scale * log2(e) (per-head scales multiply it)
 };
+
+// Scales a run of kv head h uses: the per-tensor ones, or head h's.
+__device__ inline float run_q_scale(const DecodeParams& p, int h) {
+  return p.head_scales ? p.qk_scale * p.head_scales[h] : p.q_scale;
+}
+__device__ inline float run_v_scale(const DecodeParams& p, int h) {
+  return p.head_scales ? p.head_scales[p.num_kv_heads + h] : p.v_scale;
+}
 
 template <typename KV, int D>
 struct DecodeShape {
@@ -307,7 +317,7 @@ struct ContiguousRows {   // G query heads of one sequence: rows orow + j*D
 // pass.
 template <typename QT, int D, int G, typename Rows>
 __device__ inline void merge_records(const DecodeParams& p, int first_w, int last_w, int seg_start, int chunk,
-                                     const Rows& rows) {
+                                     const Rows& rows, float v_scale) {
   constexpr int REC = D + 4;
   constexpr int QE = elem_size<QT>::value;
   static_assert(D % 4 == 0, "record layout");
@@ -333,7 +343,7 @@ __device__ inline void merge_records(const DecodeParams& p, int first_w, int las
       o[2] = fmaf(f, a.z, o[2]);
       o[3] = fmaf(f, a.w, o[3]);
     }
-    store_row<QT, 4>(p.out + (orow + d) * QE, o, lsum > 0.0f ? p.v_scale / lsum : 0.0f);
+    store_row<QT, 4>(p.out + (orow + d) * QE, o, lsum > 0.0f ? v_scale / lsum : 0.0f);
   }
   if (threadIdx.x == 0) __hip_atomic_store(p.counters + first_w, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -362,6 +372,7 @@ __device__ inline void valu_run(const DecodeParams& p, int w, int chunk, int wst
   const int row = lane / L;
   const int col = lane % L;
   const int Hq = p.num_kv_heads * G;
+  const float qs = run_q_scale(p, h), vs = run_v_scale(p, h);
 
   // query rows of the G heads served by kv head h, pre-scaled into log2 units
   float qv[G][VEC];
@@ -371,7 +382,7 @@ __device__ inline void valu_run(const DecodeParams& p, int w, int chunk, int wst
     for (int g = 0; g < G; ++g) {
       load_row_f32<QT, VEC>(p.q + (qe + (int64_t)g * D) * QE, qv[g]);
 #pragma unroll
-      for (int i = 0; i < VEC; ++i) qv[g][i] *= p.q_scale;
+      for (int i = 0; i < VEC; ++i) qv[g][i] *= qs;
     }
   }
 
@@ -440,7 +451,7 @@ __device__ inline void valu_run(const DecodeParams& p, int w, int chunk, int wst
     if (row == 0) {
 #pragma unroll
       for (int g = 0; g < G; ++g)
-        store_row<QT, VEC>(p.out + (oe + (int64_t)g * D) * QE, acc[g], l[g] > 0.0f ? p.v_scale / l[g] : 0.0f);
+        store_row<QT, VEC>(p.out + (oe + (int64_t)g * D) * QE, acc[g], l[g] > 0.0f ? vs / l[g] : 0.0f);
     }
     return;
   }
@@ -462,7 +473,7 @@ __device__ inline void valu_run(const DecodeParams& p, int w, int chunk, int wst
   const int last_w = (seg_start + nb - 1) / chunk;
   if (arrive(p, first_w, last_w))
     merge_records<QT, D, G>(p, first_w, last_w, seg_start, chunk,
-                            ContiguousRows{((int64_t)s * Hq + (int64_t)h * G) * D, D});
+                            ContiguousRows{((int64_t)s * Hq + (int64_t)h * G) * D, D}, vs);
 }
 
 }  // namespace pkv

@@ -224,6 +224,7 @@ __device__ inline void mfma_rows_run(const DecodeParams& p, int w, int chunk, in
   const int lane = threadIdx.x;
   const int j16 = lane & 15;   // token row (QK A) / query row (B, D)
   const int kg = lane >> 4;    // k group
+  const float qs = run_q_scale(p, h), vs = run_v_scale(p, h);
 
   // q operand: lane (kg, j) holds q row j at dims kg*D/4 + 8st .. +8 for step st
   uint4 qop[KS];
@@ -288,7 +289,7 @@ __device__ inline void mfma_rows_run(const DecodeParams& p, int w, int chunk, in
     const int lim = min(thi, row.limit);
     float x[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) x[i] = (row.valid && bvalid && t0 + i < lim) ? sc[i] * p.q_scale : -INFINITY;
+    for (int i = 0; i < 4; ++i) x[i] = (row.valid && bvalid && t0 + i < lim) ? sc[i] * qs : -INFINITY;
     float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
     mx = fmaxf(mx, __shfl_xor(mx, 16));
     mx = fmaxf(mx, __shfl_xor(mx, 32));
@@ -359,7 +360,7 @@ __device__ inline void mfma_rows_run(const DecodeParams& p, int w, int chunk, in
   // lane (kg, j16) holds O[j16][16 dt + 4kg + i], i = 0..3
   if (off == 0 && off + len == nb) {   // the whole run is ours
     if (row.valid) {
-      const float mul = l > 0.0f ? p.v_scale / l : 0.0f;
+      const float mul = l > 0.0f ? vs / l : 0.0f;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
         const float v4[4] = {acc[dt][0], acc[dt][1], acc[dt][2], acc[dt][3]};
@@ -380,7 +381,7 @@ __device__ inline void mfma_rows_run(const DecodeParams& p, int w, int chunk, in
   const int seg_start = pos - off;
   const int first_w = seg_start / chunk;
   const int last_w = (seg_start + nb - 1) / chunk;
-  if (arrive(p, first_w, last_w)) merge_records<QT, D, R>(p, first_w, last_w, seg_start, chunk, rows);
+  if (arrive(p, first_w, last_w)) merge_records<QT, D, R>(p, first_w, last_w, seg_start, chunk, rows, vs);
 }
 
 // Decode: the G query heads of sequence s served by kv head h, one token each.

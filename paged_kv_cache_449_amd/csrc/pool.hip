@@ -32,6 +32,8 @@ kv_status_t fill(kv_pool_t* p, int32_t num_blocks, int32_t block_size, int32_t n
   p->dtype = dtype;
   p->k_scale = 1.0f;
   p->v_scale = 1.0f;
+  p->head_scales = nullptr;
+  p->per_head = false;
   if (hipGetDevice(&p->device) != hipSuccess) return KV_ERR_HIP;
   if (hipDeviceGetAttribute(&p->num_cus, hipDeviceAttributeMultiprocessorCount, p->device) != hipSuccess)
     return KV_ERR_HIP;
@@ -99,6 +101,7 @@ extern "C" kv_status_t kv_pool_destroy(kv_pool_t* pool) {
     if (hipFree(pool->k) != hipSuccess) st = KV_ERR_HIP;
     if (hipFree(pool->v) != hipSuccess) st = KV_ERR_HIP;
   }
+  if (pool->head_scales && hipFree(pool->head_scales) != hipSuccess) st = KV_ERR_HIP;
   delete pool;
   return st;
 }
@@ -123,6 +126,35 @@ extern "C" kv_status_t kv_pool_set_scales(kv_pool_t* pool, float k_scale, float 
   if (!(k_scale > 0.0f) || !(v_scale > 0.0f) || k_scale > 3.0e38f || v_scale > 3.0e38f) return KV_ERR_INVALID_ARG;
   pool->k_scale = k_scale;
   pool->v_scale = v_scale;
+  pool->per_head = false;
+  return KV_OK;
+}
+
+extern "C" kv_status_t kv_pool_set_head_scales(kv_pool_t* pool, const float* k_scales, const float* v_scales) {
+  if (!pool || pool->dtype != KV_FP8_E4M3FN || (!k_scales) != (!v_scales)) return KV_ERR_INVALID_ARG;
+  if (!k_scales) {
+    pool->per_head = false;
+    return KV_OK;
+  }
+  const int H = pool->num_kv_heads;
+  for (int h = 0; h < H; ++h) {
+    const float a = k_scales[h], b = v_scales[h];
+    if (!(a > 0.0f) || !(b > 0.0f) || a > 3.0e38f || b > 3.0e38f) return KV_ERR_INVALID_ARG;
+  }
+  if (!pool->head_scales) {
+    int cur = -1;
+    if (hipGetDevice(&cur) != hipSuccess || hipSetDevice(pool->device) != hipSuccess) return KV_ERR_HIP;
+    const hipError_t e = hipMalloc(&pool->head_scales, 2 * (size_t)H * sizeof(float));
+    (void)hipSetDevice(cur);
+    if (e != hipSuccess) {
+      pool->head_scales = nullptr;
+      return KV_ERR_OOM;
+    }
+  }
+  if (hipMemcpy(pool->head_scales, k_scales, (size_t)H * sizeof(float), hipMemcpyHostToDevice) != hipSuccess ||
+      hipMemcpy(pool->head_scales + H, v_scales, (size_t)H * sizeof(float), hipMemcpyHostToDevice) != hipSuccess)
+    return KV_ERR_HIP;
+  pool->per_head = true;
   return KV_OK;
 }
 

@@ -31,6 +31,8 @@ MUTANTS = {
     "f16_subnormal": ("v = ldexp((double)m, -24);", "v = ldexp((double)m, -25);"),
     "tie_to_odd": ("else c = (lo % 2 == 0) ? lo : hi;", "else c = (lo % 2 == 0) ? hi : lo;"),
     "write_slot": ("int64_t b = s / B, o = s % B;", "int64_t b = s / B, o = (s + 1) % B;"),
+    "head_scale_read": ("if (k_head) k_scale = k_head[hk];", "if (k_head) k_scale = k_head[0];"),
+    "head_scale_write": ("const float ks = k_head ? k_head[h] : k_scale,", "const float ks = k_head ? k_head[0] : k_scale,"),
 }
 
 
@@ -67,6 +69,7 @@ def _pins_pass() -> bool:
     library routine on an MHA fp16, a GQA bf16 and a GQA fp8 workload."""
     from test_oracle_decode import _sdpa_expected
     from test_oracle_prefill import _sdpa_causal
+    from test_oracle_variants import _sdpa as _sdpa_variant
     from test_oracle_formats import _same
     try:
         ref16 = np.arange(65536, dtype=np.uint16).view(np.float16).astype(np.float64)
@@ -88,6 +91,9 @@ def _pins_pass() -> bool:
             wl = W.small_multi_token_configs()[name]
             run = OracleRun(wl)
             np.testing.assert_allclose(run.prefill(), _sdpa_causal(wl, run), rtol=1e-10, atol=1e-12)
+        wl = W.small_variant_configs()["c5s_fp8_headscale"]
+        run = OracleRun(wl)
+        np.testing.assert_allclose(run.decode(), _sdpa_variant(wl, run), rtol=1e-10, atol=1e-12)
     except (AssertionError, oracle.OracleError):
         return False
     return True

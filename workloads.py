@@ -74,6 +74,7 @@ class Workload:
     partition_tokens: int = 0  # 0 = library chooses the context split
     same_candidates: bool = False  # candidates of a prompt get identical q / new K/V
     query_lens: Tuple[int, ...] = ()  # new tokens per sequence; empty = one each (decode)
+    head_scales: bool = False  # fp8: one scale per kv head; K/V of head h drawn with gain HEAD_GAINS[h % 4]
 
     @property
     def num_seqs(self) -> int:
@@ -148,7 +149,8 @@ def _pool_blocks(prompt_lens: Sequence[int], parent: Sequence[int], bs: int, que
 
 
 def _make(name, index, hq, hkv, d, kv, q, bs, ctx_lens=None, prompt_lens=None, parent=None,
-          num_blocks=None, src=None, partition_tokens=0, same_candidates=False, query_lens=None) -> Workload:
+          num_blocks=None, src=None, partition_tokens=0, same_candidates=False, query_lens=None,
+          head_scales=False) -> Workload:
     """ctx_lens are context lengths after the step (cached + new tokens)."""
     if prompt_lens is None:
         ctx = [int(x) for x in ctx_lens]
@@ -164,7 +166,8 @@ def _make(name, index, hq, hkv, d, kv, q, bs, ctx_lens=None, prompt_lens=None, p
                     prompt_lens=tuple(int(x) for x in prompt_lens), parent=tuple(int(p) for p in parent),
                     num_blocks=int(num_blocks), partition_tokens=partition_tokens,
                     same_candidates=same_candidates,
-                    query_lens=tuple(int(x) for x in query_lens) if query_lens is not None else ())
+                    query_lens=tuple(int(x) for x in query_lens) if query_lens is not None else (),
+                    head_scales=bool(head_scales))
 
 
 def _lens_uniform(index: int, n: int, lo: int, hi: int) -> np.ndarray:
@@ -211,11 +214,12 @@ def config_c4(num_prompts=64, n=4, prompt_len=1023, heads=32, same_candidates=Fa
 
 
 def config_c5(kv="fp8e4m3", num_seqs=128, lo=2048, hi=8192, hq=32, hkv=8, partition_tokens=512,
-              index=5, name=None) -> Workload:
+              index=5, name=None, head_scales=False, q="bf16") -> Workload:
     """GQA long context: 32 q heads / 8 KV heads x 128, bf16 q, fp8 (or bf16) KV, U[2048, 8192]."""
     name = name or f"c5_gqa_long_{kv}"
-    return _make(name, index, hq, hkv, 128, kv, "bf16", 16,
-                 ctx_lens=_lens_uniform(index, num_seqs, lo, hi), partition_tokens=partition_tokens)
+    return _make(name, index, hq, hkv, 128, kv, q, 16,
+                 ctx_lens=_lens_uniform(index, num_seqs, lo, hi), partition_tokens=partition_tokens,
+                 head_scales=head_scales)
 
 
 def config_prefill_chunk(num_seqs=16, chunk=512, lo=0, hi=3072, heads=32, index=6, name="p1_chunked_prefill_bf16",
@@ -292,6 +296,33 @@ def small_configs() -> Dict[str, Workload]:
     return {w.name: w for w in ws}
 
 
+def variant_configs() -> Dict[str, Workload]:
+    """Variants of the decode workloads at full size: block sizes 8 and 64
+    for the LLaMA-7B shape, an 8:1 query group (32 q / 4 KV heads) in fp8 and
+    bf16, and per-head fp8 scales on the GQA long-context batch."""
+    ws = [config_c3(8), config_c3(64),
+          config_c5("fp8e4m3", hkv=4, name="c5_gqa8_long_fp8e4m3"), config_c5("bf16", hkv=4, name="c5_gqa8_long_bf16"),
+          config_c5("fp8e4m3", head_scales=True, name="c5_gqa_long_fp8_headscale")]
+    return {w.name: w for w in ws}
+
+
+def small_variant_configs() -> Dict[str, Workload]:
+    """Reduced variants for parity: block sizes 8 and 64, 8:1 groups,
+    per-head fp8 scales with bf16 and f16 queries, and per-head scales in a
+    multi-token step."""
+    ws = [
+        config_c3(8, num_seqs=10, heads=3, lo=16, hi=500, name="c3s_bf16_bs8"),
+        config_c3(64, num_seqs=10, heads=3, lo=16, hi=900, name="c3s_bf16_bs64"),
+        config_c5("fp8e4m3", num_seqs=5, lo=300, hi=1500, hq=16, hkv=2, name="c5s_gqa8_fp8"),
+        config_c5("fp8e4m3", num_seqs=5, lo=300, hi=1500, hq=8, hkv=4, head_scales=True, name="c5s_fp8_headscale"),
+        config_c5("fp8e4m3", num_seqs=4, lo=20, hi=600, hq=4, hkv=4, head_scales=True, q="f16",
+                  name="c5s_fp8_headscale_mha_f16"),
+        _make("p6s_fp8_headscale", 15, 8, 4, 128, "fp8e4m3", "bf16", 16, ctx_lens=[60, 37, 130],
+              query_lens=[20, 37, 9], head_scales=True),
+    ]
+    return {w.name: w for w in ws}
+
+
 def custom(name, hq, hkv, d, kv, q, bs, ctx_lens, num_blocks=None, index=90, partition_tokens=0,
            src=None) -> Workload:
     """Free-form workload for edge-case tests."""
@@ -323,13 +354,25 @@ def q_values(wl: Workload) -> torch.Tensor:
     return _normal(_rng(wl, _STREAM_Q), (wl.total_q, wl.num_q_heads, wl.head_dim), wl.q_dtype)
 
 
+HEAD_GAINS = (0.25, 1.0, 4.0, 0.5)   # powers of two: exact in every source dtype
+
+
+def _head_gain(wl: Workload, x: torch.Tensor) -> torch.Tensor:
+    """Per-head magnitudes for per-head-scale workloads: head h scaled by
+    HEAD_GAINS[h % 4] (exact), so heads need different fp8 scales."""
+    if not wl.head_scales:
+        return x
+    g = torch.tensor([HEAD_GAINS[h % 4] for h in range(wl.num_kv_heads)], dtype=torch.float32)
+    return (x.float() * g[None, :, None]).to(x.dtype)
+
+
 def prompt_kv(wl: Workload, p: int) -> Tuple[torch.Tensor, torch.Tensor]:
     """K and V of prompt p's cached tokens: each [prompt_len][Hkv][d] in src dtype."""
     rng = _rng(wl, _STREAM_PROMPT_KV, p)
     shape = (wl.prompt_lens[p], wl.num_kv_heads, wl.head_dim)
     k = _normal(rng, shape, wl.src_dtype)
     v = _normal(rng, shape, wl.src_dtype)
-    return k, v
+    return _head_gain(wl, k), _head_gain(wl, v)
 
 
 def all_prompt_kv(wl: Workload, prompts: Optional[Sequence[int]] = None, threads: int = 8):
@@ -344,8 +387,8 @@ def new_kv(wl: Workload) -> Tuple[torch.Tensor, torch.Tensor]:
     rng = _rng(wl, _STREAM_NEW_KV)
     n = wl.num_prompts if wl.same_candidates else wl.total_q
     shape = (n, wl.num_kv_heads, wl.head_dim)
-    k = _normal(rng, shape, wl.src_dtype)
-    v = _normal(rng, shape, wl.src_dtype)
+    k = _head_gain(wl, _normal(rng, shape, wl.src_dtype))
+    v = _head_gain(wl, _normal(rng, shape, wl.src_dtype))
     if wl.same_candidates:
         idx = torch.as_tensor(wl.parent, dtype=torch.long)
         k, v = k[idx].contiguous(), v[idx].contiguous()
@@ -371,6 +414,27 @@ def fp8_scales(wl: Workload, threads: int = 8) -> Tuple[float, float]:
     ks = float(np.float32(km) / np.float32(448.0))
     vs = float(np.float32(vm) / np.float32(448.0))
     return ks, vs
+
+
+def fp8_head_scales(wl: Workload, threads: int = 8) -> Tuple[np.ndarray, np.ndarray]:
+    """Per-kv-head fp8 scales (recipe): amax(|x|) / 448 over every K (resp.
+    V) value of head h in the workload, in fp32.  Arrays of num_kv_heads."""
+    H = wl.num_kv_heads
+
+    def amax(p):
+        k, v = prompt_kv(wl, p)
+        z = np.zeros(H, dtype=np.float32)
+        if not k.numel():
+            return z, z
+        return (k.float().abs().amax(dim=(0, 2)).numpy(), v.float().abs().amax(dim=(0, 2)).numpy())
+
+    with ThreadPoolExecutor(threads) as ex:
+        mx = list(ex.map(amax, range(wl.num_prompts)))
+    kn, vn = new_kv(wl)
+    km = np.max(np.stack([m[0] for m in mx] + [kn.float().abs().amax(dim=(0, 2)).numpy()]), axis=0)
+    vm = np.max(np.stack([m[1] for m in mx] + [vn.float().abs().amax(dim=(0, 2)).numpy()]), axis=0)
+    return (km.astype(np.float32) / np.float32(448.0)).astype(np.float32), \
+        (vm.astype(np.float32) / np.float32(448.0)).astype(np.float32)
 
 
 # --------------------------------------------------------------------------
