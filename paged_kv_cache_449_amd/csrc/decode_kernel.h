@@ -313,15 +313,15 @@ struct ContiguousRows {   // G query heads of one sequence: rows orow + j*D
 // Merge the records of workers first_w..last_w (in worker order, so results
 // are reproducible) into the out rows that `rows` names, then clear the run's
 // counter for the next call.  seg_start is the run's first position in the
-// flattened stream.  Each lane owns 4 consecutive elements of [G][D] per
-// pass.
-template <typename QT, int D, int G, typename Rows>
+// flattened stream.  Each of the NT threads owns 4 consecutive elements of
+// [G][D] per pass.
+template <typename QT, int D, int G, typename Rows, int NT = 64>
 __device__ inline void merge_records(const DecodeParams& p, int first_w, int last_w, int seg_start, int chunk,
                                      const Rows& rows, float v_scale) {
   constexpr int REC = D + 4;
   constexpr int QE = elem_size<QT>::value;
   static_assert(D % 4 == 0, "record layout");
-  for (int e0 = threadIdx.x * 4; e0 < G * D; e0 += 256) {
+  for (int e0 = threadIdx.x * 4; e0 < G * D; e0 += 4 * NT) {
     const int g = e0 / D, d = e0 % D;
     const int64_t orow = rows(g);
     if (orow < 0) continue;
@@ -352,8 +352,9 @@ __device__ inline void merge_records(const DecodeParams& p, int first_w, int las
 // the run (-1 past the run or for an id outside the pool).
 __device__ inline int load_table_window(const DecodeParams& p, const int32_t* trow, int wb, int len) {
   const int cnt = min(64, len - wb);
+  const int lane = (int)(threadIdx.x & 63);
   int e = -1;
-  if ((int)threadIdx.x < cnt) e = trow[wb + threadIdx.x];
+  if (lane < cnt) e = trow[wb + lane];
   return (uint32_t)e < (uint32_t)p.num_blocks ? e : -1;
 }
 

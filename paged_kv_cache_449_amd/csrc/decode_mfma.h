@@ -152,7 +152,7 @@ struct MfmaStep {
 template <typename KV, int D, int POL>
 __device__ inline void mfma_issue(const RunCtx& c, int tab, int tlo, int thi, int j, MfmaTileRegs<KV, D>& r) {
   using Sh = MfmaShape<KV, D>;
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x & 63;
   const int bi = min((j * 16) >> c.log2_bs, 63);
   const int phys = __builtin_amdgcn_readlane(tab, bi);
   // an invalid entry (-1) gives an empty descriptor at the head's base

@@ -2,26 +2,49 @@
 // workspace layout and dispatch to the kernel instantiations.
 #include "prefill_kernel.h"
 
+#include <cstdlib>
+#include <cstring>
+
 namespace {
 
 using namespace pkv;
 
+// One-wave workers (16-row tiles) and four-wave work-groups (64-row blocks).
 constexpr int kPrefillWavesPerCu = 8;
-constexpr int kRecordRows = 16;
+constexpr int kPrefillGroupsPerCu = 2;
+// Rows per (sequence, kv head), on average, from which the four-wave
+// work-groups pay off: below it most of a 64-row block would be empty.
+constexpr int kGroupMinRows = 48;
 
-kv_status_t prefill_plan(const kv_pool_t* pool, int32_t num_q_heads, int32_t* workers, size_t* counters_bytes,
-                         size_t* bytes) {
+int64_t round_workers(int64_t w) {
+  w = (w + 7) & ~7LL;
+  if (w < 8) w = 8;
+  return w > kCounterSlots ? kCounterSlots : w;
+}
+
+// Launch shape of either path; the workspace fits both.
+kv_status_t prefill_plan(const kv_pool_t* pool, int32_t num_q_heads, bool wg, int32_t* workers,
+                         size_t* counters_bytes, size_t* bytes) {
   if (!pool || num_q_heads <= 0 || num_q_heads % pool->num_kv_heads) return KV_ERR_INVALID_ARG;
   const int G = num_q_heads / pool->num_kv_heads;
   if (G != 1 && G != 2 && G != 4 && G != 8 && G != 16) return KV_ERR_UNSUPPORTED;
-  int64_t w = (int64_t)pool->num_cus * kPrefillWavesPerCu;
-  w = (w + 7) & ~7LL;
-  if (w < 8) w = 8;
-  if (w > kCounterSlots) w = kCounterSlots;
-  *workers = (int32_t)w;
+  const int64_t w_wave = round_workers((int64_t)pool->num_cus * kPrefillWavesPerCu);
+  const int64_t w_wg = round_workers((int64_t)pool->num_cus * kPrefillGroupsPerCu);
+  *workers = (int32_t)(wg ? w_wg : w_wave);
   *counters_bytes = (size_t)kCounterSlots * sizeof(int32_t);
-  *bytes = *counters_bytes + (size_t)2 * w * kRecordRows * (pool->head_dim + 4) * sizeof(float);
+  const size_t rec = (size_t)(pool->head_dim + 4) * sizeof(float);
+  const size_t wave_recs = (size_t)2 * w_wave * 16 * rec, wg_recs = (size_t)2 * w_wg * kWgRows * rec;
+  *bytes = *counters_bytes + (wave_recs > wg_recs ? wave_recs : wg_recs);
   return KV_OK;
+}
+
+// PAGEDKV_PREFILL_PATH=wave / group forces a path (tests); otherwise the
+// average rows per (sequence, kv head) decides.
+bool use_groups(int64_t total_q, int G, int num_seqs) {
+  const char* e = getenv("PAGEDKV_PREFILL_PATH");
+  if (e && strcmp(e, "wave") == 0) return false;
+  if (e && strcmp(e, "group") == 0) return true;
+  return total_q * G >= (int64_t)kGroupMinRows * num_seqs;
 }
 
 }  // namespace
@@ -31,7 +54,7 @@ extern "C" kv_status_t paged_attention_prefill_workspace_size(const kv_pool_t* p
   if (!bytes) return KV_ERR_INVALID_ARG;
   int32_t workers;
   size_t counters;
-  return prefill_plan(pool, num_q_heads, &workers, &counters, bytes);
+  return prefill_plan(pool, num_q_heads, false, &workers, &counters, bytes);
 }
 
 extern "C" kv_status_t paged_attention_prefill(const kv_pool_t* pool, const void* q, kv_dtype_t q_dtype, void* out,
@@ -41,7 +64,9 @@ extern "C" kv_status_t paged_attention_prefill(const kv_pool_t* pool, const void
                                                void* workspace, size_t workspace_bytes, void* stream) {
   int32_t workers;
   size_t counters_bytes, need;
-  kv_status_t st = prefill_plan(pool, num_q_heads, &workers, &counters_bytes, &need);
+  const bool wg = pool && num_q_heads > 0 && num_q_heads % pool->num_kv_heads == 0 &&
+                  use_groups(total_q, num_q_heads / pool->num_kv_heads, num_seqs > 0 ? num_seqs : 1);
+  kv_status_t st = prefill_plan(pool, num_q_heads, wg, &workers, &counters_bytes, &need);
   if (st != KV_OK) return st;
   if (num_seqs < 0 || total_q < 0 || max_blocks <= 0 || !valid_dtype(q_dtype)) return KV_ERR_INVALID_ARG;
   if (num_seqs == 0 || total_q == 0) return KV_OK;
@@ -82,9 +107,9 @@ extern "C" kv_status_t paged_attention_prefill(const kv_pool_t* pool, const void
 
   const int D = pool->head_dim;
   hipStream_t s = (hipStream_t)stream;
-  if (pool->dtype == KV_BF16 && q_dtype == KV_BF16) return launch_prefill_bf16_bf16(p, D, G, s);
-  if (pool->dtype == KV_F16 && q_dtype == KV_F16) return launch_prefill_f16_f16(p, D, G, s);
-  if (fp8 && q_dtype == KV_BF16) return launch_prefill_fp8_bf16(p, D, G, s);
-  if (fp8 && q_dtype == KV_F16) return launch_prefill_fp8_f16(p, D, G, s);
+  if (pool->dtype == KV_BF16 && q_dtype == KV_BF16) return launch_prefill_bf16_bf16(p, D, G, wg, s);
+  if (pool->dtype == KV_F16 && q_dtype == KV_F16) return launch_prefill_f16_f16(p, D, G, wg, s);
+  if (fp8 && q_dtype == KV_BF16) return launch_prefill_fp8_bf16(p, D, G, wg, s);
+  if (fp8 && q_dtype == KV_F16) return launch_prefill_fp8_f16(p, D, G, wg, s);
   return KV_ERR_UNSUPPORTED;
 }

@@ -195,12 +195,390 @@ void paged_prefill_kernel(const DecodeParams p) {
   prefill_chunk<KV, QT, D, G>(p, v, chunk, T, total);
 }
 
+// ------------------------------------------------------------------------
+// Work-group variant for long chunks.  Four waves share one (sequence, kv
+// head) row block of 4 row tiles (64 rows): each 64-token step, wave w loads
+// tile w of the step into its own LDS slot, and after one barrier every wave
+// runs its 16 rows against all four tiles.  A block of K/V is then read once
+// per 64 rows instead of once per 16, and each wave issues a quarter of the
+// loads.  The stream is the (kv head, sequence, row block, block) sequence;
+// split row blocks leave 64-row records that the last-arriving work-group
+// merges with all its threads.
+
+constexpr int kWgWaves = 4;
+constexpr int kWgRows = 16 * kWgWaves;
+
+// Out rows of a row block's records: row j is row tile 4rb + j / 16, slot
+// j % 16 of it.
+struct BlockRows {
+  int64_t qs;      // the sequence's first query row
+  int rb;
+  int m;
+  int q;           // tokens per row tile (16 / G)
+  int hq;
+  int hG;
+  int g;
+  int d;
+  __device__ int64_t operator()(int j) const {
+    const int r = kWgWaves * rb + j / 16;
+    const int tok = r * q + (j % 16) / g;
+    if (tok >= m) return -1;
+    return ((qs + tok) * hq + hG + (j % 16) % g) * (int64_t)d;
+  }
+};
+
+// Blocks of all row blocks of a sequence with n cached tokens, m of them new.
+__device__ inline int sequence_rowblock_blocks(int n, int m, int QB, int log2_bs) {
+  const int bs = 1 << log2_bs;
+  int tot = 0;
+  for (int rb = 0; rb * QB < m; ++rb) tot += (tile_limit(n, m, QB, rb) + bs - 1) >> log2_bs;
+  return tot;
+}
+
+template <typename KV, typename QT, int D, int G>
+__device__ inline void prefill_wg_run(const DecodeParams& p, int w, int chunk, int wstart, int pos, int s, int h,
+                                      int rb, int off, int len, int n, int m, int qs) {
+  using MT = typename mfma_operand<KV, QT>::type;
+  using Ops = mfma_ops<MT>;
+  using Sh = MfmaShape<KV, D>;
+  constexpr int Q = 16 / G;
+  constexpr int KS = Sh::KS, DT = Sh::DT, LSTRIDE = Sh::LSTRIDE, KSTRIDE = Sh::KSTRIDE;
+  constexpr int QE = elem_size<QT>::value;
+  constexpr int VBYTES = 16 * LSTRIDE, KBYTES = 16 * KSTRIDE;
+  __shared__ __attribute__((aligned(16))) uint8_t vlds[kWgWaves * VBYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t klds[kWgWaves * KBYTES];
+  __shared__ int last_flag;
+
+  const int wave = (int)(threadIdx.x >> 6);
+  const int lane = (int)(threadIdx.x & 63);
+  const int j16 = lane & 15;
+  const int kg = lane >> 4;
+  const int Hq = p.num_kv_heads * G;
+  const float qsc = run_q_scale(p, h), vsc = run_v_scale(p, h);
+
+  // this wave's rows: row tile r = 4 rb + wave
+  const int r = kWgWaves * rb + wave;
+  const int tok = r * Q + j16 / G;
+  const bool valid = tok < m;
+  const int64_t qoff = ((int64_t)(qs + tok) * Hq + (int64_t)h * G + j16 % G) * D;
+  const int limit = n - m + tok + 1;
+  const int lim_blk = tile_limit(n, m, kWgWaves * Q, rb);   // tokens the row block reads
+  const int nb = (lim_blk + (1 << p.log2_bs) - 1) >> p.log2_bs;
+
+  uint4 qop[KS];
+#pragma unroll
+  for (int st = 0; st < KS; ++st) qop[st] = make_uint4(0u, 0u, 0u, 0u);
+  if (valid) {
+    const int64_t qe = qoff + kg * (D / 4);
+#pragma unroll
+    for (int st = 0; st < KS; ++st) qop[st] = *(const uint4*)(p.q + (qe + st * 8) * QE);
+  }
+
+  f32x4 acc[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  float mx_run = -INFINITY;
+  float l = 0.0f;
+
+  RunCtx c;
+  const int64_t tile = (int64_t)Sh::ROW << p.log2_bs;
+  c.k_head = p.k_pool + tile * h;
+  c.v_head = p.v_pool + tile * h;
+  c.blk_stride = tile * p.num_kv_heads;
+  c.tile_bytes = (uint32_t)tile;
+  c.lane_off = 0;
+  c.row_bytes = Sh::ROW;
+  c.log2_bs = p.log2_bs;
+  c.bs_mask = (1 << p.log2_bs) - 1;
+  const int32_t* trow = p.block_tables + (int64_t)s * p.max_blocks + off;
+
+  // this wave's tile of the step, into LDS slot `wave`
+  auto stage = [&](const MfmaTileRegs<KV, D>& t) {
+    uint8_t* vb = vlds + wave * VBYTES;
+    uint8_t* kb = klds + wave * KBYTES;
+#pragma unroll
+    for (int u = 0; u < Sh::VL; ++u) {
+      const int byte = (u * 64 + lane) * 16;
+      const int vr = byte / Sh::ROW, ve = (byte % Sh::ROW) / Sh::EB;
+      uint8_t* dst = vb + vr * LSTRIDE + ve * 2;
+      if constexpr (Sh::EB == 2) {
+        *(uint4*)dst = t.v[u];
+      } else {
+        const uint4 w4 = t.v[u];
+        *(uint4*)dst = make_uint4(Ops::template from_fp8<false>(w4.x), Ops::template from_fp8<true>(w4.x),
+                                  Ops::template from_fp8<false>(w4.y), Ops::template from_fp8<true>(w4.y));
+        *(uint4*)(dst + 16) = make_uint4(Ops::template from_fp8<false>(w4.z), Ops::template from_fp8<true>(w4.z),
+                                         Ops::template from_fp8<false>(w4.w), Ops::template from_fp8<true>(w4.w));
+      }
+      *(uint4*)(kb + vr * KSTRIDE + (byte % Sh::ROW)) = t.k[u];
+    }
+  };
+
+  // this wave's 16 rows against the four tiles of step st (LDS slots 0..3,
+  // tiles 4st .. 4st+3 of the window): QK of the four tiles interleaved, one
+  // online-softmax update for the 64 tokens, then PV on 16x16x32 steps that
+  // pair tiles (0, 1) and (2, 3).  In a paired step the contraction index
+  // 8kg + e stands for token 4kg + e of the first tile (e < 4) and token
+  // 4kg + e - 4 of the second, on both operands: two transposing reads give
+  // the V^T words, the two tiles' score words the P words.
+  auto compute_step = [&](int tab, int tlo, int thi, int st) {
+    f32x4 sc[kWgWaves];
+#pragma unroll
+    for (int t = 0; t < kWgWaves; ++t) sc[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int q = 0; q < Sh::KL; ++q) {
+      uint4 kq[kWgWaves];
+#pragma unroll
+      for (int t = 0; t < kWgWaves; ++t)
+        kq[t] = *(const uint4*)(klds + t * KBYTES + j16 * KSTRIDE + kg * (Sh::ROW / 4) + q * 16);
+      // the QK steps this quarter-row word feeds: one (16-bit K) or two (fp8 K)
+#pragma unroll
+      for (int k = 0; k < KS / Sh::KL; ++k) {
+        const int kst = q * (KS / Sh::KL) + k;
+#pragma unroll
+        for (int t = 0; t < kWgWaves; ++t) {
+          uint4 kw[Sh::KL];
+          kw[q] = kq[t];
+          sc[t] = Ops::qk(mfma_k_operand<KV, MT, D>(kw, kst), qop[kst], sc[t]);
+        }
+      }
+    }
+    const int lim = min(thi, limit);
+    float x[kWgWaves][4];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int t = 0; t < kWgWaves; ++t) {
+      const int j = st * kWgWaves + t;
+      const int bi = min((j * 16) >> p.log2_bs, 63);
+      const bool bvalid = __builtin_amdgcn_readlane(tab, bi) >= 0;
+      const int t0 = tlo + j * 16 + 4 * kg;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        x[t][i] = (valid && bvalid && t0 + i < lim) ? sc[t][i] * qsc : -INFINITY;
+        mx = fmaxf(mx, x[t][i]);
+      }
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float mn = fmaxf(mx_run, mx);
+    const float mu = mn == -INFINITY ? 0.0f : mn;
+    const float alpha = fexp2(mx_run - mu);
+    mx_run = mn;
+    uint32_t ph[kWgWaves][2], pr[kWgWaves][2];
+    float psum = 0.0f;
+#pragma unroll
+    for (int t = 0; t < kWgWaves; ++t) {
+      float e[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) e[i] = fexp2(x[t][i] - mu);
+      psum += (e[0] + e[1]) + (e[2] + e[3]);
+      ph[t][0] = Ops::pack(e[0], e[1]);
+      ph[t][1] = Ops::pack(e[2], e[3]);
+      pr[t][0] = Ops::pack(e[0] - Ops::lo(ph[t][0]), e[1] - Ops::hi(ph[t][0]));
+      pr[t][1] = Ops::pack(e[2] - Ops::lo(ph[t][1]), e[3] - Ops::hi(ph[t][1]));
+    }
+    l = l * alpha + psum;
+    if (__ballot(alpha != 1.0f)) {
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) acc[dt] *= alpha;
+    }
+    const int tro = (4 * kg + (j16 >> 2)) * LSTRIDE + (lane & 3) * 8;
+#pragma unroll
+    for (int pair = 0; pair < kWgWaves / 2; ++pair) {
+      const int ta = 2 * pair, tb = 2 * pair + 1;
+      const uint4 bh = make_uint4(ph[ta][0], ph[ta][1], ph[tb][0], ph[tb][1]);
+      const uint4 br = make_uint4(pr[ta][0], pr[ta][1], pr[tb][0], pr[tb][1]);
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const uint2 va = __builtin_bit_cast(uint2, Ops::read_tr(vlds + ta * VBYTES + tro + dt * 32));
+        const uint2 vb = __builtin_bit_cast(uint2, Ops::read_tr(vlds + tb * VBYTES + tro + dt * 32));
+        const uint4 a = make_uint4(va.x, va.y, vb.x, vb.y);
+        acc[dt] = Ops::qk(a, br, Ops::qk(a, bh, acc[dt]));
+      }
+    }
+  };
+
+  int tab = load_table_window(p, trow, 0, len);
+  for (int wb = 0; wb < len; wb += 64) {
+    const int cnt = min(64, len - wb);
+    const int tab_next = wb + 64 < len ? load_table_window(p, trow, wb + 64, len) : -1;
+    const int tlo = (off + wb) << p.log2_bs;
+    const int thi = min((off + wb + cnt) << p.log2_bs, n);
+    const int tiles = (thi - tlo + 15) >> 4;
+    const int steps = (tiles + kWgWaves - 1) / kWgWaves;
+    MfmaTileRegs<KV, D> a, b;
+    auto run_step = [&](const MfmaTileRegs<KV, D>& t, int st) {
+      __syncthreads();   // every wave is done reading the previous step
+      stage(t);
+      __syncthreads();
+      compute_step(tab, tlo, thi, st);
+    };
+    // two register sets in flight; issues are unconditional (tiles past the
+    // window read zeros and are masked)
+    mfma_issue<KV, D, kStreamPolicy>(c, tab, tlo, thi, wave, a);
+    for (int st = 0; st < steps; st += 2) {
+      mfma_issue<KV, D, kStreamPolicy>(c, tab, tlo, thi, (st + 1) * kWgWaves + wave, b);
+      run_step(a, st);
+      mfma_issue<KV, D, kStreamPolicy>(c, tab, tlo, thi, (st + 2) * kWgWaves + wave, a);
+      if (st + 1 < steps) run_step(b, st + 1);
+    }
+    tab = tab_next;
+  }
+
+  l += __shfl_xor(l, 16);
+  l += __shfl_xor(l, 32);
+
+  if (off == 0 && off + len == nb) {   // the whole row block is ours
+    if (valid) {
+      const float mul = l > 0.0f ? vsc / l : 0.0f;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const float v4[4] = {acc[dt][0], acc[dt][1], acc[dt][2], acc[dt][3]};
+        store_row<QT, 4>(p.out + (qoff + dt * 16 + 4 * kg) * QE, v4, mul);
+      }
+    }
+    return;
+  }
+
+  // publish this wave's 16 rows of the 64-row record, then one arrival for
+  // the work-group
+  const RecordRef rec = record_ref<D, kWgRows>(partial_record<D, kWgRows>(p, w, wstart, pos));
+  if (valid) {
+    const int rg = (wave * 16 + j16) * (D + 4);
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+      record_store4(rec, rg + dt * 16 + 4 * kg, acc[dt][0], acc[dt][1], acc[dt][2], acc[dt][3]);
+    if (kg == 0) record_store4(rec, rg + D, mx_run, l, 0.0f, 0.0f);
+  }
+  const int seg_start = pos - off;
+  const int first_w = seg_start / chunk;
+  const int last_w = (seg_start + nb - 1) / chunk;
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();   // every wave's record stores have completed
+  if (threadIdx.x == 0) {
+    const int done = __hip_atomic_fetch_add(p.counters + first_w, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    last_flag = done == last_w - first_w;
+  }
+  __syncthreads();
+  if (last_flag)
+    merge_records<QT, D, kWgRows, BlockRows, kWgWaves * 64>(
+        p, first_w, last_w, seg_start, chunk, BlockRows{qs, rb, m, Q, Hq, h * G, G, D}, vsc);
+}
+
+template <typename KV, typename QT, int D, int G>
+__device__ inline void prefill_wg_chunk(const DecodeParams& p, int v, int chunk, int T, int total) {
+  constexpr int QB = kWgWaves * (16 / G);   // tokens per row block
+  const int lane = (int)(threadIdx.x & 63);
+  const int S = p.num_seqs;
+  const int max_len = p.max_blocks << p.log2_bs;
+  const int start = v * chunk;
+  if (start >= T) return;
+  const int end = min(start + chunk, T);
+  int h = start / total;
+  const int rr = start - h * total;
+
+  int s = 0, pre = 0;
+  bool found = false;
+  {
+    int carry = 0;
+    for (int base = 0; base < S; base += 64) {
+      const int sl = base + lane;
+      int nb = 0;
+      if (sl < S) {
+        int n, m, q0;
+        prefill_lengths(p, sl, max_len, n, m, q0);
+        nb = sequence_rowblock_blocks(n, m, QB, p.log2_bs);
+      }
+      const int incl = wave_inclusive_scan_i32(nb, lane);
+      const int excl = carry + incl - nb;
+      const unsigned long long hit = __ballot(nb > 0 && excl <= rr && rr < excl + nb);
+      if (hit) {
+        const int src = __builtin_ctzll(hit);
+        s = base + src;
+        pre = __shfl(excl, src);
+        found = true;
+        break;
+      }
+      carry += __shfl(incl, 63);
+    }
+  }
+  if (!found) return;
+  s = uniform(s);
+  int n, m, qs;
+  prefill_lengths(p, s, max_len, n, m, qs);
+  n = uniform(n);
+  m = uniform(m);
+  qs = uniform(qs);
+  int rb = 0, off = uniform(rr - pre);
+  for (;;) {
+    const int nb = (tile_limit(n, m, QB, rb) + (1 << p.log2_bs) - 1) >> p.log2_bs;
+    if (off < nb) break;
+    off -= nb;
+    ++rb;
+  }
+  int pos = start;
+  while (true) {
+    const int nb = (tile_limit(n, m, QB, rb) + (1 << p.log2_bs) - 1) >> p.log2_bs;
+    const int len = min(nb - off, end - pos);
+    prefill_wg_run<KV, QT, D, G>(p, v, chunk, start, pos, s, h, rb, off, len, n, m, qs);
+    pos += len;
+    if (pos >= end) break;
+    off = 0;
+    if ((++rb) * QB < m) continue;
+    rb = 0;
+    do {
+      if (++s == S) {
+        s = 0;
+        if (++h == p.num_kv_heads) return;
+      }
+      prefill_lengths(p, s, max_len, n, m, qs);
+      n = uniform(n);
+      m = uniform(m);
+      qs = uniform(qs);
+    } while (m == 0);
+  }
+}
+
+template <typename KV, typename QT, int D, int G>
+__global__ __launch_bounds__(256) void paged_prefill_wg_kernel(const DecodeParams p) {
+  constexpr int QB = kWgWaves * (16 / G);
+  const int lane = (int)(threadIdx.x & 63);
+  const int S = p.num_seqs;
+  const int max_len = p.max_blocks << p.log2_bs;
+  int64_t total64 = 0;
+  for (int base = 0; base < S; base += 64) {
+    const int s = base + lane;
+    int nb = 0;
+    if (s < S) {
+      int n, m, q0;
+      prefill_lengths(p, s, max_len, n, m, q0);
+      nb = sequence_rowblock_blocks(n, m, QB, p.log2_bs);
+    }
+    total64 += wave_sum_i64(nb);
+    if (total64 * p.num_kv_heads > (1LL << 30)) return;   // the same in every wave: no barrier is left waiting
+  }
+  const int total = uniform((int)total64);
+  const int T = total * p.num_kv_heads;
+  if (T == 0) return;
+  const int chunk = max(1, (T + p.num_workers - 1) / p.num_workers);
+  const int nv = (T + chunk - 1) / chunk;
+  const int per_round = (nv + 7) & ~7;
+  if ((int)blockIdx.x >= per_round) return;
+  const int v = (int)(blockIdx.x & 7) * (per_round >> 3) + (int)(blockIdx.x >> 3);
+  if (v >= nv) return;
+  prefill_wg_chunk<KV, QT, D, G>(p, v, chunk, T, total);
+}
+
 template <typename KV, typename QT>
-kv_status_t launch_prefill(const DecodeParams& p, int D, int G, hipStream_t stream) {
-#define PKV_PCASE(DD, GG)                                                                                     \
-  if (D == DD && G == GG) {                                                                                   \
-    hipLaunchKernelGGL((paged_prefill_kernel<KV, QT, DD, GG>), dim3(p.num_workers), dim3(64), 0, stream, p); \
-    return launch_status();                                                                                   \
+kv_status_t launch_prefill(const DecodeParams& p, int D, int G, bool wg, hipStream_t stream) {
+#define PKV_PCASE(DD, GG)                                                                                         \
+  if (D == DD && G == GG) {                                                                                       \
+    if (wg)                                                                                                       \
+      hipLaunchKernelGGL((paged_prefill_wg_kernel<KV, QT, DD, GG>), dim3(p.num_workers), dim3(kWgWaves * 64), 0, \
+                         stream, p);                                                                              \
+    else                                                                                                          \
+      hipLaunchKernelGGL((paged_prefill_kernel<KV, QT, DD, GG>), dim3(p.num_workers), dim3(64), 0, stream, p);   \
+    return launch_status();                                                                                       \
   }
 #define PKV_PCASES(DD) PKV_PCASE(DD, 1) PKV_PCASE(DD, 2) PKV_PCASE(DD, 4) PKV_PCASE(DD, 8) PKV_PCASE(DD, 16)
   PKV_PCASES(64)
@@ -211,9 +589,9 @@ kv_status_t launch_prefill(const DecodeParams& p, int D, int G, hipStream_t stre
   return KV_ERR_UNSUPPORTED;
 }
 
-kv_status_t launch_prefill_bf16_bf16(const DecodeParams& p, int D, int G, hipStream_t s);
-kv_status_t launch_prefill_f16_f16(const DecodeParams& p, int D, int G, hipStream_t s);
-kv_status_t launch_prefill_fp8_bf16(const DecodeParams& p, int D, int G, hipStream_t s);
-kv_status_t launch_prefill_fp8_f16(const DecodeParams& p, int D, int G, hipStream_t s);
+kv_status_t launch_prefill_bf16_bf16(const DecodeParams& p, int D, int G, bool wg, hipStream_t s);
+kv_status_t launch_prefill_f16_f16(const DecodeParams& p, int D, int G, bool wg, hipStream_t s);
+kv_status_t launch_prefill_fp8_bf16(const DecodeParams& p, int D, int G, bool wg, hipStream_t s);
+kv_status_t launch_prefill_fp8_f16(const DecodeParams& p, int D, int G, bool wg, hipStream_t s);
 
 }  // namespace pkv

@@ -6,7 +6,9 @@ speculative verification) through the C ABI against the CPU oracle.
     decode tolerances (the kernel computes in the same precisions), every
     unowned slot poisoned with NaN bytes;
   * at the full sizes: sampled sequences (the oracle computes them one by
-    one) plus properties checked on every row (finite, bitwise repeatable).
+    one) plus properties checked on every row (finite, bitwise repeatable);
+  * both kernels: one-wave 16-row tiles and four-wave 64-row blocks (forced
+    with PAGEDKV_PREFILL_PATH; the full sizes use the library's choice).
 """
 import numpy as np
 import pytest
@@ -26,8 +28,19 @@ def gpu():
     return run_gpu_prefill
 
 
+@pytest.fixture(params=["auto", "wave", "group"])
+def path(request, monkeypatch):
+    """The library picks one-wave 16-row tiles or four-wave 64-row blocks
+    from the rows per sequence; both paths are forced here as well."""
+    if request.param != "auto":
+        monkeypatch.setenv("PAGEDKV_PREFILL_PATH", request.param)
+    from gpu_harness import announce
+    announce(f"prefill path {request.param}")
+    return request.param
+
+
 @pytest.mark.parametrize("name", SMALL)
-def test_prefill_matches_oracle(gpu, name):
+def test_prefill_matches_oracle(gpu, name, path):
     wl = W.small_multi_token_configs()[name]
     got = gpu(wl)
     ref = OracleRun(wl)
@@ -41,7 +54,7 @@ def test_prefill_matches_oracle(gpu, name):
 
 @pytest.mark.parametrize("G,D,kv,q", [(1, 128, "bf16", "bf16"), (2, 64, "f16", "f16"), (4, 128, "fp8e4m3", "bf16"),
                                       (8, 256, "bf16", "bf16"), (16, 64, "fp8e4m3", "f16")])
-def test_ragged_and_empty_query_counts(gpu, G, D, kv, q):
+def test_ragged_and_empty_query_counts(gpu, G, D, kv, q, path):
     """Sequences with no new tokens, one, a partial tile, several tiles,
     chunks that start mid-block and chunks equal to the whole context."""
     ctx = [50, 17, 64, 5, 130, 33]
@@ -61,12 +74,12 @@ def test_one_new_token_matches_decode_oracle(gpu):
     check_close(got["out"], OracleRun(wl).decode(), wl.kv_dtype)
 
 
-def test_block_size_32(gpu):
+def test_block_size_32(gpu, path):
     wl = W._make("bs32", 14, 8, 2, 128, "bf16", "bf16", 32, ctx_lens=[100, 64, 31], query_lens=[70, 33, 31])
     check_close(gpu(wl)["out"], OracleRun(wl).prefill(), wl.kv_dtype)
 
 
-def test_repeat_is_bitwise_deterministic(gpu):
+def test_repeat_is_bitwise_deterministic(gpu, path):
     wl = W.small_multi_token_configs()["p3s_fp8"]
     got = gpu(wl, repeat=3)
     for o in got["outs"][1:]:

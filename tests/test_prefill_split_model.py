@@ -13,11 +13,12 @@ import numpy as np
 import pytest
 
 COUNTER_SLOTS = 65536
-WAVES_PER_CU = 8
+WAVES_PER_CU = 8      # one-wave workers, 16-row tiles
+GROUPS_PER_CU = 2     # four-wave work-groups, 64-row blocks
 
 
-def workers_for(num_cus):
-    w = num_cus * WAVES_PER_CU
+def workers_for(num_cus, rows=16):
+    w = num_cus * (WAVES_PER_CU if rows == 16 else GROUPS_PER_CU)
     w = max(8, (w + 7) & ~7)
     return min(w, COUNTER_SLOTS)
 
@@ -42,11 +43,13 @@ def tiles_of(n, m, Q, bs):
     return [-(-tile_limit(n, m, Q, r) // bs) for r in range(-(-m // Q))]
 
 
-def replay(ctx, qs, total_q, hkv, G, max_blocks, bs, num_cus=256):
-    Q = 16 // G
+def replay(ctx, qs, total_q, hkv, G, max_blocks, bs, num_cus=256, rows=16):
+    """rows = 16: one-wave 16-row tiles; rows = 64: four-wave 64-row blocks
+    (row j of block rb is token rb * (64 / G) + j / G, head j % G)."""
+    Q = rows // G
     S = len(ctx)
     max_len = max_blocks * bs
-    W = workers_for(num_cus)
+    W = workers_for(num_cus, rows)
     # host bound on a consistent stream
     tiles_bound = -(-total_q * G // 16) + S
     assert tiles_bound * max_blocks * hkv <= (1 << 30)
@@ -98,15 +101,15 @@ def replay(ctx, qs, total_q, hkv, G, max_blocks, bs, num_cus=256):
             for b in range(off, off + ln):
                 key = (h, s, r, b)
                 streamed[key] = streamed.get(key, 0) + 1
-            rows = []
-            for j in range(16):
+            out_rows = []
+            for j in range(rows):
                 tok = j // G
                 if r * Q + tok < m:
                     row = q0 + r * Q + tok
                     assert 0 <= row < total_q
-                    rows.append((row, h * G + j % G))
+                    out_rows.append((row, h * G + j % G))
             if off == 0 and off + ln == nb:
-                for row in rows:
+                for row in out_rows:
                     written[row] += 1
             else:
                 slot = 2 * v + (0 if pos == start else 1)
@@ -120,7 +123,7 @@ def replay(ctx, qs, total_q, hkv, G, max_blocks, bs, num_cus=256):
                     for u in range(first_w, last_w + 1):
                         k = 0 if u * chunk >= seg_start else 1
                         assert records.get(2 * u + k) == (h, s, r)
-                    for row in rows:
+                    for row in out_rows:
                         written[row] += 1
                     counters[first_w] = 0
             pos += ln
@@ -156,9 +159,10 @@ def _consistent(ctx, m):
     return qs, int(qs[-1])
 
 
+@pytest.mark.parametrize("rows", [16, 64])
 @pytest.mark.parametrize("G", [1, 2, 4, 8, 16])
 @pytest.mark.parametrize("bs", [16, 32])
-def test_consistent_rows_written_once(G, bs):
+def test_consistent_rows_written_once(G, bs, rows):
     rng = np.random.default_rng(G * 100 + bs)
     for _ in range(4):
         S = int(rng.integers(1, 12))
@@ -169,24 +173,26 @@ def test_consistent_rows_written_once(G, bs):
         mb = int(-(-ctx.max() // bs)) + int(rng.integers(0, 3))
         hkv = int(rng.integers(1, 4))
         for cus in (1, 4, 256):
-            written = replay(ctx, qs, tq, hkv, G, mb, bs, num_cus=cus)
+            written = replay(ctx, qs, tq, hkv, G, mb, bs, num_cus=cus, rows=rows)
             if tq:
                 assert written is not None and (written == 1).all()
 
 
-def test_inconsistent_query_start_stays_in_bounds():
+@pytest.mark.parametrize("rows", [16, 64])
+def test_inconsistent_query_start_stays_in_bounds(rows):
     rng = np.random.default_rng(7)
     for _ in range(20):
         S = int(rng.integers(1, 9))
         ctx = rng.integers(-5, 200, size=S)
         qs = rng.integers(-20, 60, size=S + 1)
         tq = int(rng.integers(1, 50))
-        replay(ctx, qs, tq, 2, 4, 16, 16, num_cus=2)   # asserts every index in range
+        replay(ctx, qs, tq, 2, 4, 16, 16, num_cus=2, rows=rows)   # asserts every index in range
 
 
-def test_workload_shapes_fit():
+@pytest.mark.parametrize("rows", [16, 64])
+def test_workload_shapes_fit(rows):
     import workloads as W
     for wl in list(W.multi_token_configs().values()) + list(W.small_multi_token_configs().values()):
         written = replay(wl.context_lens, wl.query_start, wl.total_q, wl.num_kv_heads, wl.group,
-                         wl.max_blocks_per_seq, wl.block_size)
+                         wl.max_blocks_per_seq, wl.block_size, rows=rows)
         assert (written == 1).all()
