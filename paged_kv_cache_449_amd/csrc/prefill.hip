@@ -9,12 +9,13 @@ namespace {
 
 using namespace pkv;
 
-// One-wave workers (16-row tiles) and four-wave work-groups (64-row blocks).
+// One-wave workers (16-row tiles) and multi-wave work-groups (128- or
+// 64-row blocks).
 constexpr int kPrefillWavesPerCu = 8;
-constexpr int kPrefillGroupsPerCu = 2;
-// Rows per (sequence, kv head), on average, from which the four-wave
-// work-groups pay off: below it most of a 64-row block would be empty.
-constexpr int kGroupMinRows = 48;
+constexpr int kPrefillGroupsPerCu = 1;
+// Rows per (sequence, kv head), on average, from which the work-groups pay
+// off: below it most of a row block would be empty.
+constexpr int kGroupMinRows = 96;
 
 int64_t round_workers(int64_t w) {
   w = (w + 7) & ~7LL;
@@ -33,7 +34,7 @@ kv_status_t prefill_plan(const kv_pool_t* pool, int32_t num_q_heads, bool wg, in
   *workers = (int32_t)(wg ? w_wg : w_wave);
   *counters_bytes = (size_t)kCounterSlots * sizeof(int32_t);
   const size_t rec = (size_t)(pool->head_dim + 4) * sizeof(float);
-  const size_t wave_recs = (size_t)2 * w_wave * 16 * rec, wg_recs = (size_t)2 * w_wg * kWgRows * rec;
+  const size_t wave_recs = (size_t)2 * w_wave * 16 * rec, wg_recs = (size_t)2 * w_wg * kMaxWgRows * rec;
   *bytes = *counters_bytes + (wave_recs > wg_recs ? wave_recs : wg_recs);
   return KV_OK;
 }

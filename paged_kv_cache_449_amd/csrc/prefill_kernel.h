@@ -205,13 +205,19 @@ void paged_prefill_kernel(const DecodeParams p) {
 // split row blocks leave 64-row records that the last-arriving work-group
 // merges with all its threads.
 
-constexpr int kWgWaves = 4;
-constexpr int kWgRows = 16 * kWgWaves;
+// Waves per work-group (16 rows each): 8 (128-row blocks) where two
+// buffers of 8 tiles fit in LDS, else 4.
+template <int D>
+constexpr int wg_waves() { return D <= 128 ? 8 : 4; }
+constexpr int kMaxWgRows = 128;   // records are sized for the largest block
+constexpr int kTileGroup = 4;     // tiles a wave computes together
+constexpr float kRescaleSlack = 8.0f;
 
-// Out rows of a row block's records: row j is row tile 4rb + j / 16, slot
-// j % 16 of it.
+// Out rows of a row block's records: row j is row tile waves * rb + j / 16,
+// slot j % 16 of it.
 struct BlockRows {
   int64_t qs;      // the sequence's first query row
+  int waves;       // row tiles per block
   int rb;
   int m;
   int q;           // tokens per row tile (16 / G)
@@ -220,7 +226,7 @@ struct BlockRows {
   int g;
   int d;
   __device__ int64_t operator()(int j) const {
-    const int r = kWgWaves * rb + j / 16;
+    const int r = waves * rb + j / 16;
     const int tok = r * q + (j % 16) / g;
     if (tok >= m) return -1;
     return ((qs + tok) * hq + hG + (j % 16) % g) * (int64_t)d;
@@ -241,12 +247,15 @@ __device__ inline void prefill_wg_run(const DecodeParams& p, int w, int chunk, i
   using MT = typename mfma_operand<KV, QT>::type;
   using Ops = mfma_ops<MT>;
   using Sh = MfmaShape<KV, D>;
+  constexpr int W = wg_waves<D>();
   constexpr int Q = 16 / G;
   constexpr int KS = Sh::KS, DT = Sh::DT, LSTRIDE = Sh::LSTRIDE, KSTRIDE = Sh::KSTRIDE;
   constexpr int QE = elem_size<QT>::value;
   constexpr int VBYTES = 16 * LSTRIDE, KBYTES = 16 * KSTRIDE;
-  __shared__ __attribute__((aligned(16))) uint8_t vlds[kWgWaves * VBYTES];
-  __shared__ __attribute__((aligned(16))) uint8_t klds[kWgWaves * KBYTES];
+  // two buffers of W tile slots: step st computes from buffer st & 1
+  // while the waves stage step st + 1 into the other
+  __shared__ __attribute__((aligned(16))) uint8_t vbuf[2 * W * VBYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t kbuf[2 * W * KBYTES];
   __shared__ int last_flag;
 
   const int wave = (int)(threadIdx.x >> 6);
@@ -256,13 +265,14 @@ __device__ inline void prefill_wg_run(const DecodeParams& p, int w, int chunk, i
   const int Hq = p.num_kv_heads * G;
   const float qsc = run_q_scale(p, h), vsc = run_v_scale(p, h);
 
-  // this wave's rows: row tile r = 4 rb + wave
-  const int r = kWgWaves * rb + wave;
+  // this wave's rows: row tile r = W rb + wave
+  const int r = W * rb + wave;
   const int tok = r * Q + j16 / G;
   const bool valid = tok < m;
   const int64_t qoff = ((int64_t)(qs + tok) * Hq + (int64_t)h * G + j16 % G) * D;
   const int limit = n - m + tok + 1;
-  const int lim_blk = tile_limit(n, m, kWgWaves * Q, rb);   // tokens the row block reads
+  const int lim_blk = tile_limit(n, m, W * Q, rb);   // tokens the row block reads
+  const int first_limit = n - m + W * rb * Q + 1;     // smallest causal limit of the block's rows
   const int nb = (lim_blk + (1 << p.log2_bs) - 1) >> p.log2_bs;
 
   uint4 qop[KS];
@@ -292,10 +302,10 @@ __device__ inline void prefill_wg_run(const DecodeParams& p, int w, int chunk, i
   c.bs_mask = (1 << p.log2_bs) - 1;
   const int32_t* trow = p.block_tables + (int64_t)s * p.max_blocks + off;
 
-  // this wave's tile of the step, into LDS slot `wave`
-  auto stage = [&](const MfmaTileRegs<KV, D>& t) {
-    uint8_t* vb = vlds + wave * VBYTES;
-    uint8_t* kb = klds + wave * KBYTES;
+  // this wave's tile of a step, into slot `wave` of buffer `buf`
+  auto stage = [&](const MfmaTileRegs<KV, D>& t, int buf) {
+    uint8_t* vb = vbuf + (buf * W + wave) * VBYTES;
+    uint8_t* kb = kbuf + (buf * W + wave) * KBYTES;
 #pragma unroll
     for (int u = 0; u < Sh::VL; ++u) {
       const int byte = (u * 64 + lane) * 16;
@@ -314,60 +324,80 @@ __device__ inline void prefill_wg_run(const DecodeParams& p, int w, int chunk, i
     }
   };
 
-  // this wave's 16 rows against the four tiles of step st (LDS slots 0..3,
-  // tiles 4st .. 4st+3 of the window): QK of the four tiles interleaved, one
-  // online-softmax update for the 64 tokens, then PV on 16x16x32 steps that
+  // this wave's 16 rows against tiles g0 .. g0+3 of step st (LDS slots g0..,
+  // tiles st*W + g0 .. of the window): QK of the four tiles interleaved, one
+  // online-softmax update for their 64 tokens, then PV on 16x16x32 steps that
   // pair tiles (0, 1) and (2, 3).  In a paired step the contraction index
   // 8kg + e stands for token 4kg + e of the first tile (e < 4) and token
   // 4kg + e - 4 of the second, on both operands: two transposing reads give
   // the V^T words, the two tiles' score words the P words.
-  auto compute_step = [&](int tab, int tlo, int thi, int st) {
-    f32x4 sc[kWgWaves];
+  auto compute_group = [&](int tab, int tlo, int thi, int st, int g0, int unmasked_end) {
+    const uint8_t* vlds = vbuf + ((st & 1) * W + g0) * VBYTES;
+    const uint8_t* klds = kbuf + ((st & 1) * W + g0) * KBYTES;
+    const int j0 = st * W + g0;   // window tile index of slot g0
+    f32x4 sc[kTileGroup];
 #pragma unroll
-    for (int t = 0; t < kWgWaves; ++t) sc[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int t = 0; t < kTileGroup; ++t) sc[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int q = 0; q < Sh::KL; ++q) {
-      uint4 kq[kWgWaves];
+      uint4 kq[kTileGroup];
 #pragma unroll
-      for (int t = 0; t < kWgWaves; ++t)
+      for (int t = 0; t < kTileGroup; ++t)
         kq[t] = *(const uint4*)(klds + t * KBYTES + j16 * KSTRIDE + kg * (Sh::ROW / 4) + q * 16);
       // the QK steps this quarter-row word feeds: one (16-bit K) or two (fp8 K)
 #pragma unroll
       for (int k = 0; k < KS / Sh::KL; ++k) {
         const int kst = q * (KS / Sh::KL) + k;
 #pragma unroll
-        for (int t = 0; t < kWgWaves; ++t) {
+        for (int t = 0; t < kTileGroup; ++t) {
           uint4 kw[Sh::KL];
           kw[q] = kq[t];
           sc[t] = Ops::qk(mfma_k_operand<KV, MT, D>(kw, kst), qop[kst], sc[t]);
         }
       }
     }
-    const int lim = min(thi, limit);
-    float x[kWgWaves][4];
-    float mx = -INFINITY;
+    // Scores in log2 units.  Masking (causal limits, the window's end, table
+    // entries outside the pool) is needed only where a step reaches past the
+    // block's smallest limit or the window holds an invalid entry.
+    float x[kTileGroup][4];
 #pragma unroll
-    for (int t = 0; t < kWgWaves; ++t) {
-      const int j = st * kWgWaves + t;
-      const int bi = min((j * 16) >> p.log2_bs, 63);
-      const bool bvalid = __builtin_amdgcn_readlane(tab, bi) >= 0;
-      const int t0 = tlo + j * 16 + 4 * kg;
+    for (int t = 0; t < kTileGroup; ++t)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        x[t][i] = (valid && bvalid && t0 + i < lim) ? sc[t][i] * qsc : -INFINITY;
-        mx = fmaxf(mx, x[t][i]);
+      for (int i = 0; i < 4; ++i) x[t][i] = sc[t][i] * qsc;
+    if (tlo + (j0 + kTileGroup) * 16 > unmasked_end) {
+      const int lim = min(thi, limit);
+#pragma unroll
+      for (int t = 0; t < kTileGroup; ++t) {
+        const int j = j0 + t;
+        const bool bvalid = __builtin_amdgcn_readlane(tab, min((j * 16) >> p.log2_bs, 63)) >= 0;
+        const int t0 = tlo + j * 16 + 4 * kg;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (!(bvalid && t0 + i < lim)) x[t][i] = -INFINITY;
       }
     }
+    float mx = fmaxf(fmaxf(fmaxf(x[0][0], x[0][1]), fmaxf(x[0][2], x[0][3])),
+                     fmaxf(fmaxf(x[1][0], x[1][1]), fmaxf(x[1][2], x[1][3])));
+    mx = fmaxf(mx, fmaxf(fmaxf(fmaxf(x[2][0], x[2][1]), fmaxf(x[2][2], x[2][3])),
+                         fmaxf(fmaxf(x[3][0], x[3][1]), fmaxf(x[3][2], x[3][3]))));
     mx = fmaxf(mx, __shfl_xor(mx, 16));
     mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float mn = fmaxf(mx_run, mx);
-    const float mu = mn == -INFINITY ? 0.0f : mn;
-    const float alpha = fexp2(mx_run - mu);
-    mx_run = mn;
-    uint32_t ph[kWgWaves][2], pr[kWgWaves][2];
+    // Lazy rescaling: the reference max mx_run moves only when a row's max
+    // passes it by more than kRescaleSlack (log2 units), so weights stay
+    // below 2^kRescaleSlack and acc is rescaled rarely, not every step.
+    if (__ballot(mx > mx_run + kRescaleSlack)) {
+      const float mn = fmaxf(mx_run, mx);
+      const float alpha = mx_run == -INFINITY ? 0.0f : fexp2(mx_run - mn);
+      mx_run = mn;
+      l *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) acc[dt] *= alpha;
+    }
+    const float mu = mx_run == -INFINITY ? 0.0f : mx_run;
+    uint32_t ph[kTileGroup][2], pr[kTileGroup][2];
     float psum = 0.0f;
 #pragma unroll
-    for (int t = 0; t < kWgWaves; ++t) {
+    for (int t = 0; t < kTileGroup; ++t) {
       float e[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) e[i] = fexp2(x[t][i] - mu);
@@ -377,14 +407,10 @@ __device__ inline void prefill_wg_run(const DecodeParams& p, int w, int chunk, i
       pr[t][0] = Ops::pack(e[0] - Ops::lo(ph[t][0]), e[1] - Ops::hi(ph[t][0]));
       pr[t][1] = Ops::pack(e[2] - Ops::lo(ph[t][1]), e[3] - Ops::hi(ph[t][1]));
     }
-    l = l * alpha + psum;
-    if (__ballot(alpha != 1.0f)) {
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) acc[dt] *= alpha;
-    }
+    l += psum;
     const int tro = (4 * kg + (j16 >> 2)) * LSTRIDE + (lane & 3) * 8;
 #pragma unroll
-    for (int pair = 0; pair < kWgWaves / 2; ++pair) {
+    for (int pair = 0; pair < kTileGroup / 2; ++pair) {
       const int ta = 2 * pair, tb = 2 * pair + 1;
       const uint4 bh = make_uint4(ph[ta][0], ph[ta][1], ph[tb][0], ph[tb][1]);
       const uint4 br = make_uint4(pr[ta][0], pr[ta][1], pr[tb][0], pr[tb][1]);
@@ -405,22 +431,27 @@ __device__ inline void prefill_wg_run(const DecodeParams& p, int w, int chunk, i
     const int tlo = (off + wb) << p.log2_bs;
     const int thi = min((off + wb + cnt) << p.log2_bs, n);
     const int tiles = (thi - tlo + 15) >> 4;
-    const int steps = (tiles + kWgWaves - 1) / kWgWaves;
-    MfmaTileRegs<KV, D> a, b;
-    auto run_step = [&](const MfmaTileRegs<KV, D>& t, int st) {
-      __syncthreads();   // every wave is done reading the previous step
-      stage(t);
+    const int steps = (tiles + W - 1) / W;
+    // tokens below this need no mask: the block's first row sees up to
+    // first_limit - 1, and every table entry of the window is in the pool
+    const bool all_in_pool = __ballot(lane < cnt && tab < 0) == 0;
+    const int unmasked_end = all_in_pool ? min(thi, first_limit) : tlo;
+    // One register set: the tile of step st + 1 is loaded while step st
+    // computes, then staged into the other buffer; one barrier per step.
+    // Issues are unconditional (tiles past the window read zeros, masked).
+    MfmaTileRegs<KV, D> rt;
+    mfma_issue<KV, D, kStreamPolicy>(c, tab, tlo, thi, wave, rt);
+    stage(rt, 0);
+    mfma_issue<KV, D, kStreamPolicy>(c, tab, tlo, thi, W + wave, rt);
+    __syncthreads();
+    for (int st = 0; st < steps; ++st) {
+#pragma unroll
+      for (int g0 = 0; g0 < W; g0 += kTileGroup) compute_group(tab, tlo, thi, st, g0, unmasked_end);
+      if (st + 1 < steps) {
+        stage(rt, (st + 1) & 1);
+        mfma_issue<KV, D, kStreamPolicy>(c, tab, tlo, thi, (st + 2) * W + wave, rt);
+      }
       __syncthreads();
-      compute_step(tab, tlo, thi, st);
-    };
-    // two register sets in flight; issues are unconditional (tiles past the
-    // window read zeros and are masked)
-    mfma_issue<KV, D, kStreamPolicy>(c, tab, tlo, thi, wave, a);
-    for (int st = 0; st < steps; st += 2) {
-      mfma_issue<KV, D, kStreamPolicy>(c, tab, tlo, thi, (st + 1) * kWgWaves + wave, b);
-      run_step(a, st);
-      mfma_issue<KV, D, kStreamPolicy>(c, tab, tlo, thi, (st + 2) * kWgWaves + wave, a);
-      if (st + 1 < steps) run_step(b, st + 1);
     }
     tab = tab_next;
   }
@@ -442,7 +473,7 @@ __device__ inline void prefill_wg_run(const DecodeParams& p, int w, int chunk, i
 
   // publish this wave's 16 rows of the 64-row record, then one arrival for
   // the work-group
-  const RecordRef rec = record_ref<D, kWgRows>(partial_record<D, kWgRows>(p, w, wstart, pos));
+  const RecordRef rec = record_ref<D, 16 * W>(partial_record<D, 16 * W>(p, w, wstart, pos));
   if (valid) {
     const int rg = (wave * 16 + j16) * (D + 4);
 #pragma unroll
@@ -461,13 +492,13 @@ __device__ inline void prefill_wg_run(const DecodeParams& p, int w, int chunk, i
   }
   __syncthreads();
   if (last_flag)
-    merge_records<QT, D, kWgRows, BlockRows, kWgWaves * 64>(
-        p, first_w, last_w, seg_start, chunk, BlockRows{qs, rb, m, Q, Hq, h * G, G, D}, vsc);
+    merge_records<QT, D, 16 * W, BlockRows, 64 * W>(
+        p, first_w, last_w, seg_start, chunk, BlockRows{qs, W, rb, m, Q, Hq, h * G, G, D}, vsc);
 }
 
 template <typename KV, typename QT, int D, int G>
 __device__ inline void prefill_wg_chunk(const DecodeParams& p, int v, int chunk, int T, int total) {
-  constexpr int QB = kWgWaves * (16 / G);   // tokens per row block
+  constexpr int QB = wg_waves<D>() * (16 / G);   // tokens per row block
   const int lane = (int)(threadIdx.x & 63);
   const int S = p.num_seqs;
   const int max_len = p.max_blocks << p.log2_bs;
@@ -540,8 +571,8 @@ __device__ inline void prefill_wg_chunk(const DecodeParams& p, int v, int chunk,
 }
 
 template <typename KV, typename QT, int D, int G>
-__global__ __launch_bounds__(256) void paged_prefill_wg_kernel(const DecodeParams p) {
-  constexpr int QB = kWgWaves * (16 / G);
+__global__ __launch_bounds__(64 * wg_waves<D>()) void paged_prefill_wg_kernel(const DecodeParams p) {
+  constexpr int QB = wg_waves<D>() * (16 / G);
   const int lane = (int)(threadIdx.x & 63);
   const int S = p.num_seqs;
   const int max_len = p.max_blocks << p.log2_bs;
@@ -574,7 +605,7 @@ kv_status_t launch_prefill(const DecodeParams& p, int D, int G, bool wg, hipStre
 #define PKV_PCASE(DD, GG)                                                                                         \
   if (D == DD && G == GG) {                                                                                       \
     if (wg)                                                                                                       \
-      hipLaunchKernelGGL((paged_prefill_wg_kernel<KV, QT, DD, GG>), dim3(p.num_workers), dim3(kWgWaves * 64), 0, \
+      hipLaunchKernelGGL((paged_prefill_wg_kernel<KV, QT, DD, GG>), dim3(p.num_workers), dim3(64 * wg_waves<DD>()), 0, \
                          stream, p);                                                                              \
     else                                                                                                          \
       hipLaunchKernelGGL((paged_prefill_kernel<KV, QT, DD, GG>), dim3(p.num_workers), dim3(64), 0, stream, p);   \

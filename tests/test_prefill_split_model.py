@@ -14,7 +14,7 @@ import pytest
 
 COUNTER_SLOTS = 65536
 WAVES_PER_CU = 8      # one-wave workers, 16-row tiles
-GROUPS_PER_CU = 2     # four-wave work-groups, 64-row blocks
+GROUPS_PER_CU = 1     # multi-wave work-groups: 128-row blocks (64 for head_dim 256)
 
 
 def workers_for(num_cus, rows=16):
@@ -44,8 +44,8 @@ def tiles_of(n, m, Q, bs):
 
 
 def replay(ctx, qs, total_q, hkv, G, max_blocks, bs, num_cus=256, rows=16):
-    """rows = 16: one-wave 16-row tiles; rows = 64: four-wave 64-row blocks
-    (row j of block rb is token rb * (64 / G) + j / G, head j % G)."""
+    """rows = 16: one-wave 16-row tiles; rows = 64 / 128: work-group row
+    blocks (row j of block rb is token rb * (rows / G) + j / G, head j % G)."""
     Q = rows // G
     S = len(ctx)
     max_len = max_blocks * bs
@@ -159,7 +159,7 @@ def _consistent(ctx, m):
     return qs, int(qs[-1])
 
 
-@pytest.mark.parametrize("rows", [16, 64])
+@pytest.mark.parametrize("rows", [16, 64, 128])
 @pytest.mark.parametrize("G", [1, 2, 4, 8, 16])
 @pytest.mark.parametrize("bs", [16, 32])
 def test_consistent_rows_written_once(G, bs, rows):
@@ -178,7 +178,7 @@ def test_consistent_rows_written_once(G, bs, rows):
                 assert written is not None and (written == 1).all()
 
 
-@pytest.mark.parametrize("rows", [16, 64])
+@pytest.mark.parametrize("rows", [16, 64, 128])
 def test_inconsistent_query_start_stays_in_bounds(rows):
     rng = np.random.default_rng(7)
     for _ in range(20):
@@ -189,7 +189,7 @@ def test_inconsistent_query_start_stays_in_bounds(rows):
         replay(ctx, qs, tq, 2, 4, 16, 16, num_cus=2, rows=rows)   # asserts every index in range
 
 
-@pytest.mark.parametrize("rows", [16, 64])
+@pytest.mark.parametrize("rows", [16, 64, 128])
 def test_workload_shapes_fit(rows):
     import workloads as W
     for wl in list(W.multi_token_configs().values()) + list(W.small_multi_token_configs().values()):
