@@ -16,6 +16,8 @@ constexpr int kPrefillGroupsPerCu = 1;
 // Rows per (sequence, kv head), on average, from which the work-groups pay
 // off: below it most of a row block would be empty.
 constexpr int kGroupMinRows = 96;
+// Row blocks per CU from which one work-group per row block balances well.
+constexpr int kUnitsPerCu = 4;
 
 int64_t round_workers(int64_t w) {
   w = (w + 7) & ~7LL;
@@ -39,13 +41,19 @@ kv_status_t prefill_plan(const kv_pool_t* pool, int32_t num_q_heads, bool wg, in
   return KV_OK;
 }
 
-// PAGEDKV_PREFILL_PATH=wave / group forces a path (tests); otherwise the
-// average rows per (sequence, kv head) decides.
-bool use_groups(int64_t total_q, int G, int num_seqs) {
+// Launch shape: 0 one-wave tiles, 1 split work-groups, 2 one work-group per
+// row block.  PAGEDKV_PREFILL_PATH=wave / group / unit forces one (tests);
+// otherwise the average rows per (sequence, kv head) picks the work-groups,
+// and units when there are enough row blocks to fill the chip several times.
+int prefill_mode(int64_t total_q, int G, int num_seqs, int num_kv_heads, int D, int num_cus) {
   const char* e = getenv("PAGEDKV_PREFILL_PATH");
-  if (e && strcmp(e, "wave") == 0) return false;
-  if (e && strcmp(e, "group") == 0) return true;
-  return total_q * G >= (int64_t)kGroupMinRows * num_seqs;
+  if (e && strcmp(e, "wave") == 0) return 0;
+  if (e && strcmp(e, "group") == 0) return 1;
+  if (e && strcmp(e, "unit") == 0) return 2;
+  if (total_q * G < (int64_t)kGroupMinRows * num_seqs) return 0;
+  const int64_t rows = 16LL * (D <= 128 ? 8 : 4);
+  const int64_t units = total_q * G / rows * num_kv_heads;
+  return units >= (int64_t)kUnitsPerCu * num_cus ? 2 : 1;
 }
 
 }  // namespace
@@ -65,9 +73,11 @@ extern "C" kv_status_t paged_attention_prefill(const kv_pool_t* pool, const void
                                                void* workspace, size_t workspace_bytes, void* stream) {
   int32_t workers;
   size_t counters_bytes, need;
-  const bool wg = pool && num_q_heads > 0 && num_q_heads % pool->num_kv_heads == 0 &&
-                  use_groups(total_q, num_q_heads / pool->num_kv_heads, num_seqs > 0 ? num_seqs : 1);
-  kv_status_t st = prefill_plan(pool, num_q_heads, wg, &workers, &counters_bytes, &need);
+  const int mode = pool && num_q_heads > 0 && num_q_heads % pool->num_kv_heads == 0
+                       ? prefill_mode(total_q, num_q_heads / pool->num_kv_heads, num_seqs > 0 ? num_seqs : 1,
+                                      pool->num_kv_heads, pool->head_dim, pool->num_cus)
+                       : 0;
+  kv_status_t st = prefill_plan(pool, num_q_heads, mode == 1, &workers, &counters_bytes, &need);
   if (st != KV_OK) return st;
   if (num_seqs < 0 || total_q < 0 || max_blocks <= 0 || !valid_dtype(q_dtype)) return KV_ERR_INVALID_ARG;
   if (num_seqs == 0 || total_q == 0) return KV_OK;
@@ -81,6 +91,14 @@ extern "C" kv_status_t paged_attention_prefill(const kv_pool_t* pool, const void
   if (tiles * max_blocks * pool->num_kv_heads > (1LL << 30) || (int64_t)max_blocks * pool->block_size > (1LL << 30))
     return KV_ERR_INVALID_ARG;
   if (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255)) return KV_ERR_WORKSPACE;
+  if (mode == 2) {
+    // at most total_q * G / rows + num_seqs row blocks per kv head when
+    // query_start is consistent (the tiles bound above keeps this far below
+    // 2^31); units past the grid of an inconsistent one are left undone
+    const int64_t rows = 16LL * (pool->head_dim <= 128 ? 8 : 4);
+    const int64_t units = ((int64_t)total_q * G / rows + num_seqs + 1) * pool->num_kv_heads;
+    workers = (int32_t)((units + 7) & ~7LL);
+  }
 
   DecodeParams p;
   p.k_pool = (const uint8_t*)pool->k;
@@ -108,9 +126,9 @@ extern "C" kv_status_t paged_attention_prefill(const kv_pool_t* pool, const void
 
   const int D = pool->head_dim;
   hipStream_t s = (hipStream_t)stream;
-  if (pool->dtype == KV_BF16 && q_dtype == KV_BF16) return launch_prefill_bf16_bf16(p, D, G, wg, s);
-  if (pool->dtype == KV_F16 && q_dtype == KV_F16) return launch_prefill_f16_f16(p, D, G, wg, s);
-  if (fp8 && q_dtype == KV_BF16) return launch_prefill_fp8_bf16(p, D, G, wg, s);
-  if (fp8 && q_dtype == KV_F16) return launch_prefill_fp8_f16(p, D, G, wg, s);
+  if (pool->dtype == KV_BF16 && q_dtype == KV_BF16) return launch_prefill_bf16_bf16(p, D, G, mode, s);
+  if (pool->dtype == KV_F16 && q_dtype == KV_F16) return launch_prefill_f16_f16(p, D, G, mode, s);
+  if (fp8 && q_dtype == KV_BF16) return launch_prefill_fp8_bf16(p, D, G, mode, s);
+  if (fp8 && q_dtype == KV_F16) return launch_prefill_fp8_f16(p, D, G, mode, s);
   return KV_ERR_UNSUPPORTED;
 }

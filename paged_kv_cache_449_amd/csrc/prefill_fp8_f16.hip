@@ -2,7 +2,7 @@
 #include "prefill_kernel.h"
 
 namespace pkv {
-kv_status_t launch_prefill_fp8_f16(const DecodeParams& p, int D, int G, bool wg, hipStream_t s) {
-  return launch_prefill<fp8_t, f16_t>(p, D, G, wg, s);
+kv_status_t launch_prefill_fp8_f16(const DecodeParams& p, int D, int G, int mode, hipStream_t s) {
+  return launch_prefill<fp8_t, f16_t>(p, D, G, mode, s);
 }
 }  // namespace pkv

@@ -600,11 +600,85 @@ __global__ __launch_bounds__(64 * wg_waves<D>()) void paged_prefill_wg_kernel(co
   prefill_wg_chunk<KV, QT, D, G>(p, v, chunk, T, total);
 }
 
+// Unit mode: one work-group per whole row block, units in (kv head,
+// sequence, row block) order.  Consecutive units go to the same XCD in
+// dispatch order, so the row blocks of one (sequence, kv head) run at the
+// same time there and stream the same prefix through its L2; no run is split
+// (no records).  The grid may exceed the units; the rest exit at once.
+template <typename KV, typename QT, int D, int G>
+__global__ __launch_bounds__(64 * wg_waves<D>()) void paged_prefill_unit_kernel(const DecodeParams p) {
+  constexpr int QB = wg_waves<D>() * (16 / G);
+  const int lane = (int)(threadIdx.x & 63);
+  const int S = p.num_seqs;
+  const int max_len = p.max_blocks << p.log2_bs;
+  int64_t per_head64 = 0;
+  for (int base = 0; base < S; base += 64) {
+    const int s = base + lane;
+    int cnt = 0;
+    if (s < S) {
+      int n, m, q0;
+      prefill_lengths(p, s, max_len, n, m, q0);
+      cnt = (m + QB - 1) / QB;
+    }
+    per_head64 += wave_sum_i64(cnt);
+  }
+  if (per_head64 == 0 || per_head64 * p.num_kv_heads > (1LL << 30)) return;
+  const int per_head = uniform((int)per_head64);
+  const int U = per_head * p.num_kv_heads;
+  const int per_xcd = (U + 7) >> 3;
+  const int k = (int)(blockIdx.x >> 3);
+  const int u = (int)(blockIdx.x & 7) * per_xcd + k;
+  if (k >= per_xcd || u >= U) return;
+  const int h = u / per_head;
+  const int r = u - h * per_head;
+  // the sequence holding unit r of kv head h
+  int s = 0, pre = 0;
+  bool found = false;
+  {
+    int carry = 0;
+    for (int base = 0; base < S; base += 64) {
+      const int sl = base + lane;
+      int cnt = 0;
+      if (sl < S) {
+        int n, m, q0;
+        prefill_lengths(p, sl, max_len, n, m, q0);
+        cnt = (m + QB - 1) / QB;
+      }
+      const int incl = wave_inclusive_scan_i32(cnt, lane);
+      const int excl = carry + incl - cnt;
+      const unsigned long long hit = __ballot(cnt > 0 && excl <= r && r < excl + cnt);
+      if (hit) {
+        const int src = __builtin_ctzll(hit);
+        s = base + src;
+        pre = __shfl(excl, src);
+        found = true;
+        break;
+      }
+      carry += __shfl(incl, 63);
+    }
+  }
+  if (!found) return;
+  s = uniform(s);
+  const int rb = uniform(r - pre);
+  int n, m, qs;
+  prefill_lengths(p, s, max_len, n, m, qs);
+  n = uniform(n);
+  m = uniform(m);
+  qs = uniform(qs);
+  const int nb = (tile_limit(n, m, QB, rb) + (1 << p.log2_bs) - 1) >> p.log2_bs;
+  // the whole row block: stored directly, no record
+  prefill_wg_run<KV, QT, D, G>(p, 0, 1, 0, 0, s, h, rb, 0, nb, n, m, qs);
+}
+
+// Prefill launch shape: 0 one-wave tiles, 1 split work-groups, 2 units.
 template <typename KV, typename QT>
-kv_status_t launch_prefill(const DecodeParams& p, int D, int G, bool wg, hipStream_t stream) {
+kv_status_t launch_prefill(const DecodeParams& p, int D, int G, int mode, hipStream_t stream) {
 #define PKV_PCASE(DD, GG)                                                                                         \
   if (D == DD && G == GG) {                                                                                       \
-    if (wg)                                                                                                       \
+    if (mode == 2)                                                                                                \
+      hipLaunchKernelGGL((paged_prefill_unit_kernel<KV, QT, DD, GG>), dim3(p.num_workers),                       \
+                         dim3(64 * wg_waves<DD>()), 0, stream, p);                                                \
+    else if (mode == 1)                                                                                           \
       hipLaunchKernelGGL((paged_prefill_wg_kernel<KV, QT, DD, GG>), dim3(p.num_workers), dim3(64 * wg_waves<DD>()), 0, \
                          stream, p);                                                                              \
     else                                                                                                          \
@@ -620,9 +694,9 @@ kv_status_t launch_prefill(const DecodeParams& p, int D, int G, bool wg, hipStre
   return KV_ERR_UNSUPPORTED;
 }
 
-kv_status_t launch_prefill_bf16_bf16(const DecodeParams& p, int D, int G, bool wg, hipStream_t s);
-kv_status_t launch_prefill_f16_f16(const DecodeParams& p, int D, int G, bool wg, hipStream_t s);
-kv_status_t launch_prefill_fp8_bf16(const DecodeParams& p, int D, int G, bool wg, hipStream_t s);
-kv_status_t launch_prefill_fp8_f16(const DecodeParams& p, int D, int G, bool wg, hipStream_t s);
+kv_status_t launch_prefill_bf16_bf16(const DecodeParams& p, int D, int G, int mode, hipStream_t s);
+kv_status_t launch_prefill_f16_f16(const DecodeParams& p, int D, int G, int mode, hipStream_t s);
+kv_status_t launch_prefill_fp8_bf16(const DecodeParams& p, int D, int G, int mode, hipStream_t s);
+kv_status_t launch_prefill_fp8_f16(const DecodeParams& p, int D, int G, int mode, hipStream_t s);
 
 }  // namespace pkv

@@ -7,8 +7,9 @@ speculative verification) through the C ABI against the CPU oracle.
     unowned slot poisoned with NaN bytes;
   * at the full sizes: sampled sequences (the oracle computes them one by
     one) plus properties checked on every row (finite, bitwise repeatable);
-  * both kernels: one-wave 16-row tiles and four-wave 64-row blocks (forced
-    with PAGEDKV_PREFILL_PATH; the full sizes use the library's choice).
+  * every launch shape: one-wave 16-row tiles, split work-group row blocks
+    and one work-group per row block (forced with PAGEDKV_PREFILL_PATH; the
+    full sizes use the library's choice).
 """
 import numpy as np
 import pytest
@@ -28,10 +29,11 @@ def gpu():
     return run_gpu_prefill
 
 
-@pytest.fixture(params=["auto", "wave", "group"])
+@pytest.fixture(params=["auto", "wave", "group", "unit"])
 def path(request, monkeypatch):
-    """The library picks one-wave 16-row tiles or four-wave 64-row blocks
-    from the rows per sequence; both paths are forced here as well."""
+    """The library picks one-wave 16-row tiles, split work-group row blocks
+    or one work-group per row block from the rows per sequence; each is
+    forced here as well."""
     if request.param != "auto":
         monkeypatch.setenv("PAGEDKV_PREFILL_PATH", request.param)
     from gpu_harness import announce

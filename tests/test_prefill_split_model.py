@@ -196,3 +196,45 @@ def test_workload_shapes_fit(rows):
         written = replay(wl.context_lens, wl.query_start, wl.total_q, wl.num_kv_heads, wl.group,
                          wl.max_blocks_per_seq, wl.block_size, rows=rows)
         assert (written == 1).all()
+
+
+def replay_units(ctx, qs, total_q, hkv, G, D=128):
+    """Unit mode: one work-group per whole row block, units in (kv head,
+    sequence, row block) order, consecutive units on one XCD.  Checks the
+    host's grid bound and that every row block is computed exactly once."""
+    W = 8 if D <= 128 else 4
+    rows = 16 * W
+    QB = rows // G
+    S = len(ctx)
+    L = lengths(ctx, qs, total_q, 1 << 30)
+    cnt = [-(-m // QB) for _, m, _ in L]
+    per_head = sum(cnt)
+    U = per_head * hkv
+    grid = ((total_q * G // rows + S + 1) * hkv + 7) & ~7
+    seen = set()
+    per_xcd = (U + 7) >> 3
+    pre = np.concatenate([[0], np.cumsum(cnt)])
+    for b in range(grid):
+        k, u = b >> 3, (b & 7) * per_xcd + (b >> 3)
+        if k >= per_xcd or u >= U:
+            continue
+        h, r = divmod(u, per_head)
+        s = next(i for i in range(S) if cnt[i] > 0 and pre[i] <= r < pre[i] + cnt[i])
+        key = (h, s, r - pre[s])
+        assert key not in seen
+        seen.add(key)
+    return seen, U
+
+
+@pytest.mark.parametrize("G", [1, 4, 16])
+def test_units_cover_every_row_block_once(G):
+    rng = np.random.default_rng(G)
+    for _ in range(5):
+        S = int(rng.integers(1, 40))
+        m = rng.integers(0, 700, size=S)
+        ctx = m + rng.integers(0, 300, size=S)
+        ctx = np.maximum(ctx, 1)
+        qs = np.concatenate([[0], np.cumsum(m)])
+        for D in (128, 256):
+            seen, U = replay_units(ctx, qs, int(qs[-1]), int(rng.integers(1, 9)), G, D)
+            assert len(seen) == U
