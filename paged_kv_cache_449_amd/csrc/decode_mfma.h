@@ -138,13 +138,20 @@ struct MfmaTileRegs {
   uint4 v[MfmaShape<KV, D>::VL];
 };
 
-// Tiles loaded and computed together in one pipeline step.  One: two fp8
-// tiles per step (8 KiB, as one 16-bit tile) measured 2% slower on MI355X.
+// Tiles loaded and computed together in one pipeline step.  Two tiles per
+// step (PV paired into 16x16x32 steps, 8 KiB of fp8 in flight per wave)
+// measured 11% slower than one on the fp8 GQA decode workload on MI355X,
+// so runs take one tile per step; the paired form stays for TPS = 2.
 template <typename KV, int D>
 struct MfmaStep {
   static constexpr int TPS = 1;
   MfmaTileRegs<KV, D> t[TPS];
 };
+
+// Lazy rescaling: a run's reference max moves only when a row's max passes
+// it by more than this (log2 units), so weights stay below 2^8 and the
+// accumulator is rescaled rarely rather than at every tile.
+constexpr float kRescaleSlack = 8.0f;
 
 // Issue the loads of 16-token tile j of the current table window (tokens
 // tlo + 16j ...).  Tokens at or past thi and blocks whose table entry is out
@@ -202,6 +209,7 @@ struct MfmaRow {
   bool valid;     // row j holds a query
   int64_t qoff;   // element offset of its q row (and of its out row)
   int limit;      // tokens at or past this index are masked for the row
+  int min_limit;  // the smallest limit of the run's valid rows (uniform)
 };
 
 // One run of up to 16 query rows against blocks [off, off+len) of the
@@ -218,8 +226,8 @@ __device__ inline void mfma_rows_run(const DecodeParams& p, int w, int chunk, in
   constexpr int KS = Sh::KS, DT = Sh::DT, LSTRIDE = Sh::LSTRIDE;
   constexpr int TPS = MfmaStep<KV, D>::TPS;
   constexpr int QE = elem_size<QT>::value;
-  __shared__ __attribute__((aligned(16))) uint8_t vlds[16 * LSTRIDE];
-  __shared__ __attribute__((aligned(16))) uint8_t klds[16 * Sh::KSTRIDE];
+  __shared__ __attribute__((aligned(16))) uint8_t vlds[TPS * 16 * LSTRIDE];
+  __shared__ __attribute__((aligned(16))) uint8_t klds[TPS * 16 * Sh::KSTRIDE];
 
   const int lane = threadIdx.x;
   const int j16 = lane & 15;   // token row (QK A) / query row (B, D)
@@ -239,7 +247,7 @@ __device__ inline void mfma_rows_run(const DecodeParams& p, int w, int chunk, in
   f32x4 acc[DT];
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-  float m = -INFINITY;   // running max of row j16 (log2 units)
+  float m = -INFINITY;   // reference max of row j16 (log2 units)
   float l = 0.0f;        // this lane's share of the running sum
 
   RunCtx c;
@@ -254,71 +262,111 @@ __device__ inline void mfma_rows_run(const DecodeParams& p, int w, int chunk, in
   c.bs_mask = (1 << p.log2_bs) - 1;
   const int32_t* trow = p.block_tables + (int64_t)s * p.max_blocks + off;
 
-  auto compute = [&](const MfmaTileRegs<KV, D>& r, int tab, int tlo, int thi, int j) {
-    // stage the tile in LDS: V as the operand type (rows padded to LSTRIDE
-    // bytes), K as loaded (rows padded to KSTRIDE bytes)
-    __syncthreads();   // the previous tile's LDS reads are done
+  // One pipeline step: TPS tiles staged in LDS (V as the operand type, rows
+  // padded to LSTRIDE; K as loaded, rows padded to KSTRIDE), QK for each, one
+  // online-softmax update for the step, then PV.  With two tiles, PV runs
+  // 16x16x32 steps whose contraction index 8kg + e stands for token 4kg + e
+  // of the first tile (e < 4) and 4kg + e - 4 of the second, on both
+  // operands.
+  auto compute = [&](const MfmaStep<KV, D>& r, int tab, int tlo, int thi, int st, int unmasked_end) {
+    __syncthreads();   // the previous step's LDS reads are done
 #pragma unroll
-    for (int u = 0; u < Sh::VL; ++u) {
-      const int byte = (u * 64 + lane) * 16;
-      const int vr = byte / Sh::ROW, ve = (byte % Sh::ROW) / Sh::EB;   // row, first element
-      uint8_t* dst = vlds + vr * LSTRIDE + ve * 2;
-      if constexpr (Sh::EB == 2) {
-        *(uint4*)dst = r.v[u];
-      } else {
-        const uint4 w4 = r.v[u];
-        *(uint4*)dst = make_uint4(Ops::template from_fp8<false>(w4.x), Ops::template from_fp8<true>(w4.x),
-                                  Ops::template from_fp8<false>(w4.y), Ops::template from_fp8<true>(w4.y));
-        *(uint4*)(dst + 16) = make_uint4(Ops::template from_fp8<false>(w4.z), Ops::template from_fp8<true>(w4.z),
-                                         Ops::template from_fp8<false>(w4.w), Ops::template from_fp8<true>(w4.w));
+    for (int q = 0; q < TPS; ++q) {
+#pragma unroll
+      for (int u = 0; u < Sh::VL; ++u) {
+        const int byte = (u * 64 + lane) * 16;
+        const int vr = byte / Sh::ROW, ve = (byte % Sh::ROW) / Sh::EB;   // row, first element
+        uint8_t* dst = vlds + (q * 16 + vr) * LSTRIDE + ve * 2;
+        if constexpr (Sh::EB == 2) {
+          *(uint4*)dst = r.t[q].v[u];
+        } else {
+          const uint4 w4 = r.t[q].v[u];
+          *(uint4*)dst = make_uint4(Ops::template from_fp8<false>(w4.x), Ops::template from_fp8<true>(w4.x),
+                                    Ops::template from_fp8<false>(w4.y), Ops::template from_fp8<true>(w4.y));
+          *(uint4*)(dst + 16) = make_uint4(Ops::template from_fp8<false>(w4.z), Ops::template from_fp8<true>(w4.z),
+                                           Ops::template from_fp8<false>(w4.w), Ops::template from_fp8<true>(w4.w));
+        }
+        *(uint4*)(klds + (q * 16 + vr) * Sh::KSTRIDE + (byte % Sh::ROW)) = r.t[q].k[u];
       }
-      *(uint4*)(klds + vr * Sh::KSTRIDE + (byte % Sh::ROW)) = r.k[u];
     }
     __syncthreads();
-    // K operand: lane (kg, t) holds the quarter row kg of token t
-    uint4 kq[Sh::KL];
+    // S^T tiles: lane (kg, j16) gets scores of tokens 4kg + i, i = 0..3, row j16
+    f32x4 sc[TPS];
 #pragma unroll
-    for (int q = 0; q < Sh::KL; ++q) kq[q] = *(const uint4*)(klds + j16 * Sh::KSTRIDE + kg * (Sh::ROW / 4) + q * 16);
-    // S^T tile: lane (kg, j16) gets scores of tokens 4kg + i, i = 0..3, row j16
-    f32x4 sc = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int q = 0; q < TPS; ++q) {
+      uint4 kq[Sh::KL];
 #pragma unroll
-    for (int st = 0; st < KS; ++st) sc = Ops::qk(mfma_k_operand<KV, MT, D>(kq, st), qop[st], sc);
-    const int bi = min((j * 16) >> p.log2_bs, 63);
-    const bool bvalid = __builtin_amdgcn_readlane(tab, bi) >= 0;
-    const int t0 = tlo + j * 16 + 4 * kg;
-    const int lim = min(thi, row.limit);
-    float x[4];
+      for (int w = 0; w < Sh::KL; ++w)
+        kq[w] = *(const uint4*)(klds + (q * 16 + j16) * Sh::KSTRIDE + kg * (Sh::ROW / 4) + w * 16);
+      sc[q] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-    for (int i = 0; i < 4; ++i) x[i] = (row.valid && bvalid && t0 + i < lim) ? sc[i] * qs : -INFINITY;
-    float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+      for (int k = 0; k < KS; ++k) sc[q] = Ops::qk(mfma_k_operand<KV, MT, D>(kq, k), qop[k], sc[q]);
+    }
+    float x[TPS][4];
+#pragma unroll
+    for (int q = 0; q < TPS; ++q)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) x[q][i] = sc[q][i] * qs;
+    if (tlo + (st + 1) * TPS * 16 > unmasked_end) {   // some token of the step may be masked
+      const int lim = min(thi, row.limit);
+#pragma unroll
+      for (int q = 0; q < TPS; ++q) {
+        const int j = st * TPS + q;
+        const bool bvalid = __builtin_amdgcn_readlane(tab, min((j * 16) >> p.log2_bs, 63)) >= 0;
+        const int t0 = tlo + j * 16 + 4 * kg;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (!(bvalid && t0 + i < lim)) x[q][i] = -INFINITY;
+      }
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int q = 0; q < TPS; ++q) mx = fmaxf(mx, fmaxf(fmaxf(x[q][0], x[q][1]), fmaxf(x[q][2], x[q][3])));
     mx = fmaxf(mx, __shfl_xor(mx, 16));
     mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float mn = fmaxf(m, mx);
-    const float mu = mn == -INFINITY ? 0.0f : mn;
-    const float alpha = fexp2(m - mu);
-    m = mn;
-    float e[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) e[i] = fexp2(x[i] - mu);
-    l = l * alpha + ((e[0] + e[1]) + (e[2] + e[3]));
-    // The weights enter the matrix cores as a rounded head plus the rounded
-    // remainder: one 16-bit operand alone (8 significant bits for bf16) would
-    // leave an error of up to ~2^-8 of the spread of V in rows that see few
-    // tokens.
-    const uint32_t h01 = Ops::pack(e[0], e[1]), h23 = Ops::pack(e[2], e[3]);
-    const uint32_t r01 = Ops::pack(e[0] - Ops::lo(h01), e[1] - Ops::hi(h01));
-    const uint32_t r23 = Ops::pack(e[2] - Ops::lo(h23), e[3] - Ops::hi(h23));
-    if (__ballot(alpha != 1.0f)) {
+    if (__ballot(mx > m + kRescaleSlack)) {
+      const float mn = fmaxf(m, mx);
+      const float alpha = m == -INFINITY ? 0.0f : fexp2(m - mn);
+      m = mn;
+      l *= alpha;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) acc[dt] *= alpha;
     }
-    const uint2 ph = make_uint2(h01, h23), pr = make_uint2(r01, r23);
-    // lane (kg, i) needs V[4kg + e][16 dt + i], e = 0..3: one transposing read
-    const uint8_t* tr = vlds + (4 * kg + (j16 >> 2)) * LSTRIDE + (lane & 3) * 8;
+    const float mu = m == -INFINITY ? 0.0f : m;
+    // weights as a rounded head plus the rounded remainder: one 16-bit
+    // operand alone (8 significant bits for bf16) would leave an error of up
+    // to ~2^-8 of the spread of V in rows that see few tokens
+    uint32_t ph[TPS][2], pr[TPS][2];
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      const auto vt = Ops::read_tr(tr + dt * 32);
-      acc[dt] = Ops::pv(vt, pr, Ops::pv(vt, ph, acc[dt]));
+    for (int q = 0; q < TPS; ++q) {
+      float e[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) e[i] = fexp2(x[q][i] - mu);
+      l += (e[0] + e[1]) + (e[2] + e[3]);
+      ph[q][0] = Ops::pack(e[0], e[1]);
+      ph[q][1] = Ops::pack(e[2], e[3]);
+      pr[q][0] = Ops::pack(e[0] - Ops::lo(ph[q][0]), e[1] - Ops::hi(ph[q][0]));
+      pr[q][1] = Ops::pack(e[2] - Ops::lo(ph[q][1]), e[3] - Ops::hi(ph[q][1]));
+    }
+    // lane (kg, i) needs V[4kg + e][16 dt + i], e = 0..3: one transposing read per tile
+    const uint8_t* tr = vlds + (4 * kg + (j16 >> 2)) * LSTRIDE + (lane & 3) * 8;
+    if constexpr (TPS == 2) {
+      const uint4 bh = make_uint4(ph[0][0], ph[0][1], ph[1][0], ph[1][1]);
+      const uint4 br = make_uint4(pr[0][0], pr[0][1], pr[1][0], pr[1][1]);
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const uint2 va = Ops::read_tr(tr + dt * 32);
+        const uint2 vb = Ops::read_tr(tr + 16 * LSTRIDE + dt * 32);
+        const uint4 a = make_uint4(va.x, va.y, vb.x, vb.y);
+        acc[dt] = Ops::qk(a, br, Ops::qk(a, bh, acc[dt]));
+      }
+    } else {
+      const uint2 bh = make_uint2(ph[0][0], ph[0][1]), br = make_uint2(pr[0][0], pr[0][1]);
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const auto vt = Ops::read_tr(tr + dt * 32);
+        acc[dt] = Ops::pv(vt, br, Ops::pv(vt, bh, acc[dt]));
+      }
     }
   };
 
@@ -329,6 +377,10 @@ __device__ inline void mfma_rows_run(const DecodeParams& p, int w, int chunk, in
     const int tlo = (off + wb) << p.log2_bs;
     const int thi = min((off + wb + cnt) << p.log2_bs, n);
     const int tiles = (thi - tlo + 15) >> 4;
+    // tokens below this need no mask: every row of the run sees them and
+    // every table entry of the window is in the pool
+    const bool all_in_pool = __ballot(lane < cnt && tab < 0) == 0;
+    const int unmasked_end = all_in_pool ? min(thi, row.min_limit) : tlo;
     // Two step register sets in flight: issue the next step, compute this
     // one.  Issues are unconditional so the compiler's wait counts stay
     // exact (a tile past the window reads zeros and its scores are all
@@ -339,16 +391,12 @@ __device__ inline void mfma_rows_run(const DecodeParams& p, int w, int chunk, in
 #pragma unroll
       for (int q = 0; q < TPS; ++q) mfma_issue<KV, D, POL>(c, tab, tlo, thi, st * TPS + q, r.t[q]);
     };
-    auto run_step = [&](const MfmaStep<KV, D>& r, int st) {
-#pragma unroll
-      for (int q = 0; q < TPS; ++q) compute(r.t[q], tab, tlo, thi, st * TPS + q);
-    };
     issue(a, 0);
     for (int st = 0; st < steps; st += 2) {
       issue(b, st + 1);
-      run_step(a, st);
+      compute(a, tab, tlo, thi, st, unmasked_end);
       issue(a, st + 2);
-      run_step(b, st + 1);
+      compute(b, tab, tlo, thi, st + 1, unmasked_end);
     }
     tab = tab_next;
   }
@@ -395,6 +443,7 @@ __device__ inline void mfma_run(const DecodeParams& p, int w, int chunk, int wst
   row.valid = j16 < G;
   row.qoff = orow + (int64_t)j16 * D;
   row.limit = n;
+  row.min_limit = n;
   mfma_rows_run<KV, QT, D, G, POL>(p, w, chunk, wstart, pos, s, h, off, len, n, nb, row, ContiguousRows{orow, D});
 }
 

@@ -79,6 +79,7 @@ __device__ inline void prefill_run(const DecodeParams& p, int w, int chunk, int 
   row.valid = r * Q + tok < m;
   row.qoff = ((int64_t)(q0 + tok) * Hq + (int64_t)h * G + j16 % G) * D;
   row.limit = n - m + r * Q + tok + 1;
+  row.min_limit = n - m + r * Q + 1;   // the tile's first row
   const TokenRows rows{q0, m - r * Q, Hq, h * G, G, D};
   mfma_rows_run<KV, QT, D, 16, kStreamPolicy>(p, w, chunk, wstart, pos, s, h, off, len, lim, nb, row, rows);
 }
@@ -211,7 +212,6 @@ template <int D>
 constexpr int wg_waves() { return D <= 128 ? 8 : 4; }
 constexpr int kMaxWgRows = 128;   // records are sized for the largest block
 constexpr int kTileGroup = 4;     // tiles a wave computes together
-constexpr float kRescaleSlack = 8.0f;
 
 // Out rows of a row block's records: row j is row tile waves * rb + j / 16,
 // slot j % 16 of it.
