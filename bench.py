@@ -133,6 +133,31 @@ def cpu_baseline_prefill(wl: W.Workload, target_s: float = 12.0) -> dict:
                       f"{dt:.1f} s single-threaded fp64"}
 
 
+def grouped_bytes(wl: W.Workload, sess) -> dict:
+    """Algorithmic bytes of one grouped decode: each group's shared prefix
+    (whole blocks, as the library cuts it) once per kv head, every
+    sequence's remaining tokens, q and out, and the table entries read."""
+    n = wl.context_lens.astype(np.int64)
+    bs = wl.block_size
+    gs = sess.group_start.cpu().numpy()
+    gsh = sess.group_shared.cpu().numpy()
+    limit = max(1, 16 // wl.group)
+    shared = np.zeros_like(n)
+    unique_tokens = 0
+    for g in range(gsh.shape[0]):
+        a, b = int(gs[g]), min(int(gs[g + 1]), int(gs[g]) + limit)
+        sh = (min(int(gsh[g]) * bs, int(n[a:b].min())) // bs) * bs if b > a else 0
+        shared[a:b] = sh
+        unique_tokens += sh
+    unique_tokens += int((n - shared).sum())
+    per_tok = 2 * wl.num_kv_heads * wl.head_dim * W.ELEM_BYTES[wl.kv_dtype]
+    qb = W.ELEM_BYTES[wl.q_dtype]
+    kv = unique_tokens * per_tok
+    qo = 2 * wl.num_seqs * wl.num_q_heads * wl.head_dim * qb
+    tables = int((-(-n // bs)).sum()) * 4 + wl.num_seqs * 4
+    return {"kv": kv, "total": kv + qo + tables, "tokens": unique_tokens}
+
+
 def cpu_baseline(wl: W.Workload, target_s: float = 12.0) -> dict:
     """The fp64 oracle on one host core over the first sequences of the
     workload, sized to about target_s seconds of CPU work."""
@@ -323,6 +348,9 @@ def main(argv=None) -> int:
                     help="shuffled: blocks from a seeded random free list (the workload); sequential: "
                          "the free list in id order, so each sequence's blocks are contiguous (the "
                          "paged-vs-contiguous comparison)")
+    ap.add_argument("--grouped", action="store_true",
+                    help="decode with paged_attention_decode_grouped: each shared prefix (forked candidates) is "
+                         "read once per group")
     ap.add_argument("--block-manager", action="store_true",
                     help="host block manager only (no GPU): reservation rate, oracle beside it, trace accounting")
     args = ap.parse_args(argv)
@@ -360,6 +388,9 @@ def main(argv=None) -> int:
         if multi:
             pk.paged_attention_prefill(pool, q, sess.block_tables, sess.context_lens, sess.query_start, wl.scale,
                                        out=out)
+        elif args.grouped:
+            pk.paged_attention_decode_grouped(pool, q, sess.block_tables, sess.context_lens, wl.scale,
+                                              sess.group_start, sess.group_shared, out=out)
         else:
             pk.paged_attention_decode(pool, q, sess.block_tables, sess.context_lens, wl.scale, out=out,
                                       partition_tokens=pt)
@@ -398,6 +429,9 @@ def main(argv=None) -> int:
         return 0
     nb = decode_bytes(wl)
     dec_mean_s = float(dec_ms.mean()) / 1e3
+    logical_total = nb["total"]
+    if args.grouped:
+        nb = grouped_bytes(wl, sess)
     achieved = nb["total"] / dec_mean_s / 1e9
     print(f"[bench] decode kernel mean {dec_ms.mean() * 1e3:.1f} us (min {dec_ms.min() * 1e3:.1f}, "
           f"max {dec_ms.max() * 1e3:.1f}); step {step_ms * 1e3:.1f} us", file=sys.stderr, flush=True)
@@ -421,11 +455,15 @@ def main(argv=None) -> int:
                    "num_kv_heads": wl.num_kv_heads, "head_dim": wl.head_dim, "block_size": wl.block_size,
                    "kv_dtype": wl.kv_dtype, "q_dtype": wl.q_dtype, "cached_tokens": nb["tokens"],
                    "kv_bytes_per_step": nb["kv"], "partition_tokens": pt, "placement": args.placement,
+                   "decode": "grouped" if args.grouped else "flat",
                    "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(wl.name),
-                     "kernel": "paged_decode_kernel", "kernel_us": round(float(dec_ms.mean()) * 1e3, 2),
-                     "bytes_per_launch": nb["total"]},
+                     "kernel": ("paged_decode_shared_kernel + paged_decode_suffix_kernel" if args.grouped
+                                else "paged_decode_kernel"),
+                     "kernel_us": round(float(dec_ms.mean()) * 1e3, 2),
+                     "bytes_per_launch": nb["total"],
+                     "logical_gbs": round(logical_total / dec_mean_s / 1e9, 1)},
     }
     if args.swap_blocks > 0:
         res["swap"] = swap_measurement(pool, min(args.swap_blocks, wl.num_blocks))

@@ -209,6 +209,44 @@ kv_status_t paged_attention_workspace_size(const kv_pool_t* pool, int32_t num_se
                                            int32_t max_blocks, int32_t partition_tokens, size_t* bytes);
 
 /*
+ * paged_attention_decode_grouped -- the same result as paged_attention_decode,
+ * for batches in which groups of sequences share the blocks of a common
+ * prefix (parallel sampling: n candidates forked from one prompt share its
+ * blocks with ref_count n, "vLLM — 把操作系统的分页搬进 GPU KV cache", core
+ * mechanism 3 and case 2).  The shared prefix is read once per group: its
+ * members' query rows (members x query heads of a kv head, at most 16) are
+ * the rows of one matrix-core pass; each member's remaining blocks are read
+ * per sequence.
+ *
+ * group_start: device int32 [num_groups + 1], ascending; group g is
+ *   sequences group_start[g] .. group_start[g+1]-1 (groups need not cover
+ *   every sequence: the others are decoded on their own).
+ * group_shared: device int32 [num_groups]; the first group_shared[g] table
+ *   entries are identical in every member's table (caller's contract).
+ * Members beyond 16 / (num_q_heads / num_kv_heads) in a group, and tokens
+ * past a member's context, are handled without sharing, and the shared part
+ * is cut to whole blocks.  Inconsistent groups (overlapping, unsorted, or
+ * sharing that the tables do not have) give wrong rows but stay inside every
+ * buffer.  The other arguments are paged_attention_decode's; workspace:
+ * paged_attention_decode_grouped_workspace_size() bytes, 256-byte aligned,
+ * contents free (no state across calls).
+ * Supported: bf16/bf16, f16/f16, fp8 with bf16 or f16 queries; block_size
+ * >= 16 (KV_ERR_UNSUPPORTED otherwise: call paged_attention_decode).
+ * Two kernels run on `stream`.
+ */
+kv_status_t paged_attention_decode_grouped(const kv_pool_t* pool, const void* q, kv_dtype_t q_dtype, void* out,
+                                           const int32_t* block_tables, int32_t max_blocks,
+                                           const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
+                                           float scale, const int32_t* group_start, const int32_t* group_shared,
+                                           int32_t num_groups, void* workspace, size_t workspace_bytes,
+                                           void* stream);
+
+/* paged_attention_decode_grouped_workspace_size -- bytes of workspace the
+ * call above needs: one partial record per (sequence, query head). */
+kv_status_t paged_attention_decode_grouped_workspace_size(const kv_pool_t* pool, int32_t num_seqs,
+                                                          int32_t num_q_heads, size_t* bytes);
+
+/*
  * paged_attention_prefill -- several new query tokens per sequence attend
  * causally to the cached context through the block table: a chunk of a
  * prompt being prefilled into the pool, or speculative tokens being verified

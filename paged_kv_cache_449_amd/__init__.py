@@ -64,6 +64,9 @@ def lib() -> ctypes.CDLL:
         L.paged_attention_prefill.argtypes = [vp, vp, ctypes.c_int, vp, vp, i32, vp, vp, i32, i32, i32, f32, vp,
                                               sz, vp]
         L.paged_attention_prefill_workspace_size.argtypes = [vp, i32, ctypes.POINTER(sz)]
+        L.paged_attention_decode_grouped.argtypes = [vp, vp, ctypes.c_int, vp, vp, i32, vp, i32, i32, f32, vp, vp,
+                                                     i32, vp, sz, vp]
+        L.paged_attention_decode_grouped_workspace_size.argtypes = [vp, i32, i32, ctypes.POINTER(sz)]
         L.kv_status_string.argtypes = [ctypes.c_int]
         L.kv_status_string.restype = ctypes.c_char_p
         # host block manager (block_manager.h)
@@ -88,7 +91,8 @@ def lib() -> ctypes.CDLL:
         for fn in ("kv_pool_create", "kv_pool_create_from", "kv_pool_destroy", "kv_pool_info", "kv_pool_set_scales",
                    "kv_pool_set_head_scales",
                    "reshape_and_cache", "paged_attention_decode", "paged_attention_workspace_size", "copy_blocks",
-                   "swap_blocks", "paged_attention_prefill", "paged_attention_prefill_workspace_size"):
+                   "swap_blocks", "paged_attention_prefill", "paged_attention_prefill_workspace_size",
+                   "paged_attention_decode_grouped", "paged_attention_decode_grouped_workspace_size"):
             getattr(L, fn).restype = ctypes.c_int
         _lib_handle = L
     return _lib_handle
@@ -311,6 +315,71 @@ def paged_attention_prefill(pool: KVPool, q: torch.Tensor, block_tables: torch.T
                                          _dev_ptr(workspace, "workspace", d),
                                          workspace.numel() * workspace.element_size(), _stream(d, stream)),
            "paged_attention_prefill")
+    return out
+
+
+def shared_prefix_groups(block_tables, context_lens, group_size_limit: int):
+    """Groups of consecutive sequences that share their leading blocks (host
+    arrays in, numpy int32 arrays out): (group_start [num_groups + 1],
+    group_shared [num_groups]).  A group is a run of sequences whose first
+    table entry is the same physical block, cut to at most group_size_limit
+    members; its shared length is the number of leading entries every member
+    holds in common (the library cuts it to whole blocks within every
+    member's context).  Sequences that share nothing form groups of one with
+    shared length 0, so the groups cover the batch."""
+    import numpy as np
+    bt = np.asarray(block_tables)
+    cl = np.asarray(context_lens)
+    S = bt.shape[0]
+    starts, shared = [], []
+    s = 0
+    while s < S:
+        e = s + 1
+        while e < S and e - s < group_size_limit and bt[e, 0] >= 0 and bt[e, 0] == bt[s, 0]:
+            e += 1
+        k = 0
+        if e - s > 1:
+            rows = bt[s:e]
+            same = np.all(rows == rows[0], axis=0)
+            k = int(np.argmin(same)) if not same.all() else bt.shape[1]
+        starts.append(s)
+        shared.append(k)
+        s = e
+    return np.asarray(starts + [S], dtype=np.int32), np.asarray(shared, dtype=np.int32)
+
+
+def paged_attention_decode_grouped(pool: KVPool, q: torch.Tensor, block_tables: torch.Tensor,
+                                   context_lens: torch.Tensor, scale: float, group_start: torch.Tensor,
+                                   group_shared: torch.Tensor, out: Optional[torch.Tensor] = None,
+                                   workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Decode attention with the shared prefix of each group of sequences read
+    once per group (group_start [G + 1], group_shared [G]: device int32)."""
+    if q.dim() != 3 or q.shape[2] != pool.head_dim or q.dtype not in DTYPE_CODE:
+        raise ValueError(f"q must be [S][Hq][{pool.head_dim}] of a supported dtype")
+    S, Hq = q.shape[0], q.shape[1]
+    if block_tables.dtype != torch.int32 or block_tables.dim() != 2 or block_tables.shape[0] != S:
+        raise ValueError("block_tables must be int32 [S][max_blocks]")
+    if context_lens.dtype != torch.int32 or context_lens.shape != (S,):
+        raise ValueError("context_lens must be int32 [S]")
+    ng = group_shared.shape[0]
+    if group_start.dtype != torch.int32 or group_shared.dtype != torch.int32 or group_start.shape != (ng + 1,):
+        raise ValueError("group_start must be int32 [G + 1] and group_shared int32 [G]")
+    if out is None:
+        out = torch.empty_like(q)
+    n = ctypes.c_size_t()
+    _check(lib().paged_attention_decode_grouped_workspace_size(pool.handle, S, Hq, ctypes.byref(n)),
+           "paged_attention_decode_grouped_workspace_size")
+    if workspace is None:
+        workspace = pool.workspace(n.value)
+    d = pool.device
+    _check(lib().paged_attention_decode_grouped(pool.handle, _dev_ptr(q, "q", d), DTYPE_CODE[q.dtype],
+                                                _dev_ptr(out, "out", d), _dev_ptr(block_tables, "block_tables", d),
+                                                block_tables.shape[1], _dev_ptr(context_lens, "context_lens", d), S,
+                                                Hq, float(scale), _dev_ptr(group_start, "group_start", d),
+                                                _dev_ptr(group_shared, "group_shared", d) if ng else None, ng,
+                                                _dev_ptr(workspace, "workspace", d),
+                                                workspace.numel() * workspace.element_size(), _stream(d, stream)),
+           "paged_attention_decode_grouped")
     return out
 
 

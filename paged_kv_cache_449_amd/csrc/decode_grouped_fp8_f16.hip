@@ -1,0 +1,9 @@
+// Prefix-grouped decode instantiations for fp8 KV pools with f16 queries.
+#include "decode_grouped.h"
+
+namespace pkv {
+kv_status_t launch_grouped_fp8_f16(const DecodeParams& p, int D, int G, const int32_t* gs, const int32_t* gsh, int ng,
+                                 hipStream_t s) {
+  return launch_grouped<fp8_t, f16_t>(p, D, G, gs, gsh, ng, s);
+}
+}  // namespace pkv

@@ -358,44 +358,19 @@ __device__ inline int load_table_window(const DecodeParams& p, const int32_t* tr
   return (uint32_t)e < (uint32_t)p.num_blocks ? e : -1;
 }
 
-// One run on the vector ALUs: blocks [off, off+len) of the (kv head h,
-// sequence s) stream, which has nb blocks and n tokens.  pos is the run's
-// place in the flattened stream and wstart the worker's first block.  All
-// scalars are uniform.
-template <typename KV, typename QT, int D, int G, int POL>
-__device__ inline void valu_run(const DecodeParams& p, int w, int chunk, int wstart, int pos, int s, int h,
-                                int off, int len, int n, int nb) {
+// Stream blocks [off, off+len) of the (kv head h, sequence s) context of n
+// tokens through one wave's online-softmax state (per-row-group m, l, acc of
+// the G query rows, qv pre-scaled into log2 units).
+template <typename KV, int D, int G, int POL>
+__device__ inline void valu_stream(const DecodeParams& p, int s, int h, int off, int len, int n,
+                                   const float (&qv)[G][DecodeShape<KV, D>::VEC], float (&m)[G], float (&l)[G],
+                                   float (&acc)[G][DecodeShape<KV, D>::VEC]) {
   using Sh = DecodeShape<KV, D>;
-  constexpr int VEC = Sh::VEC, L = Sh::L, TPL = Sh::TPL, REC = Sh::REC;
+  constexpr int VEC = Sh::VEC, L = Sh::L, TPL = Sh::TPL;
   constexpr int U = kLoadsPerStep;
-  constexpr int QE = elem_size<QT>::value;
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x & 63;
   const int row = lane / L;
   const int col = lane % L;
-  const int Hq = p.num_kv_heads * G;
-  const float qs = run_q_scale(p, h), vs = run_v_scale(p, h);
-
-  // query rows of the G heads served by kv head h, pre-scaled into log2 units
-  float qv[G][VEC];
-  {
-    const int64_t qe = ((int64_t)s * Hq + (int64_t)h * G) * D + (int64_t)col * VEC;
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      load_row_f32<QT, VEC>(p.q + (qe + (int64_t)g * D) * QE, qv[g]);
-#pragma unroll
-      for (int i = 0; i < VEC; ++i) qv[g][i] *= qs;
-    }
-  }
-
-  float m[G], l[G], acc[G][VEC];
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    m[g] = -INFINITY;
-    l[g] = 0.0f;
-#pragma unroll
-    for (int i = 0; i < VEC; ++i) acc[g][i] = 0.0f;
-  }
-
   RunCtx c;
   const int64_t tile = ((int64_t)D * Sh::EB) << p.log2_bs;
   c.k_head = p.k_pool + tile * h;
@@ -429,6 +404,47 @@ __device__ inline void valu_run(const DecodeParams& p, int w, int chunk, int wst
     }
     tab = tab_next;
   }
+
+}
+
+// One run on the vector ALUs: blocks [off, off+len) of the (kv head h,
+// sequence s) stream, which has nb blocks and n tokens.  pos is the run's
+// place in the flattened stream and wstart the worker's first block.  All
+// scalars are uniform.
+template <typename KV, typename QT, int D, int G, int POL>
+__device__ inline void valu_run(const DecodeParams& p, int w, int chunk, int wstart, int pos, int s, int h,
+                                int off, int len, int n, int nb) {
+  using Sh = DecodeShape<KV, D>;
+  constexpr int VEC = Sh::VEC, L = Sh::L, REC = Sh::REC;
+  constexpr int QE = elem_size<QT>::value;
+  const int lane = threadIdx.x;
+  const int row = lane / L;
+  const int col = lane % L;
+  const int Hq = p.num_kv_heads * G;
+  const float qs = run_q_scale(p, h), vs = run_v_scale(p, h);
+
+  // query rows of the G heads served by kv head h, pre-scaled into log2 units
+  float qv[G][VEC];
+  {
+    const int64_t qe = ((int64_t)s * Hq + (int64_t)h * G) * D + (int64_t)col * VEC;
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      load_row_f32<QT, VEC>(p.q + (qe + (int64_t)g * D) * QE, qv[g]);
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) qv[g][i] *= qs;
+    }
+  }
+
+  float m[G], l[G], acc[G][VEC];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    m[g] = -INFINITY;
+    l[g] = 0.0f;
+#pragma unroll
+    for (int i = 0; i < VEC; ++i) acc[g][i] = 0.0f;
+  }
+
+  valu_stream<KV, D, G, POL>(p, s, h, off, len, n, qv, m, l, acc);
 
   // merge the TPL row states (rows hold the same columns)
 #pragma unroll

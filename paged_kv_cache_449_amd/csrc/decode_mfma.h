@@ -210,13 +210,18 @@ struct MfmaRow {
   int64_t qoff;   // element offset of its q row (and of its out row)
   int limit;      // tokens at or past this index are masked for the row
   int min_limit;  // the smallest limit of the run's valid rows (uniform)
+  int64_t part;   // PART runs: index of the row's partial record
 };
 
 // One run of up to 16 query rows against blocks [off, off+len) of the
 // (kv head h, sequence s) stream, which has nb blocks and n tokens; `rows`
 // maps record row j to the element offset of its out row (-1: no query).
 // R is the number of record rows.  All scalars are uniform.
-template <typename KV, typename QT, int D, int R, int POL, typename Rows>
+//
+// PART runs (whole runs only) leave each valid row's unnormalised state
+// (acc[D], reference max, sum) as record row.part of p.partials instead of
+// writing out, for a later kernel to continue.
+template <typename KV, typename QT, int D, int R, int POL, typename Rows, bool PART = false>
 __device__ inline void mfma_rows_run(const DecodeParams& p, int w, int chunk, int wstart, int pos, int s, int h,
                                      int off, int len, int n, int nb, const MfmaRow& row, const Rows& rows) {
   using MT = typename mfma_operand<KV, QT>::type;
@@ -406,6 +411,15 @@ __device__ inline void mfma_rows_run(const DecodeParams& p, int w, int chunk, in
   l += __shfl_xor(l, 32);
 
   // lane (kg, j16) holds O[j16][16 dt + 4kg + i], i = 0..3
+  if constexpr (PART) {
+    if (row.valid) {
+      float* rec = p.partials + row.part * (D + 4);
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) *(f32x4*)(rec + dt * 16 + 4 * kg) = acc[dt];
+      if (kg == 0) *(float2*)(rec + D) = make_float2(m, l);
+    }
+    return;
+  }
   if (off == 0 && off + len == nb) {   // the whole run is ours
     if (row.valid) {
       const float mul = l > 0.0f ? vs / l : 0.0f;

@@ -18,7 +18,8 @@ from typing import Hashable, List, Optional, Sequence
 import numpy as np
 import torch
 
-from . import KVPool, copy_blocks, paged_attention_decode, paged_attention_prefill, reshape_and_cache
+from . import (KVPool, copy_blocks, paged_attention_decode, paged_attention_decode_grouped,
+               paged_attention_prefill, reshape_and_cache, shared_prefix_groups)
 from .block_manager import BlockManager
 
 
@@ -33,6 +34,9 @@ class DecodeSession:
         self.block_tables: Optional[torch.Tensor] = None
         self.context_lens: Optional[torch.Tensor] = None
         self.query_start: Optional[torch.Tensor] = None
+        self.group_start: Optional[torch.Tensor] = None
+        self.group_shared: Optional[torch.Tensor] = None
+        self.shared_blocks = 0
 
     def _dev(self, a: np.ndarray) -> torch.Tensor:
         return torch.from_numpy(np.ascontiguousarray(a)).to(self.pool.device, non_blocking=False)
@@ -67,9 +71,17 @@ class DecodeSession:
         slots, pairs = self.manager.append_batch(self.seqs, counts)
         self.slot_mapping = self._dev(slots)
         self.pairs = self._dev(np.asarray(pairs, dtype=np.int32).reshape(-1, 2))
-        self.block_tables = self._dev(self.manager.block_tables(self.seqs, max_blocks))
-        self.context_lens = self._dev(self.manager.context_lens(self.seqs))
+        tables = self.manager.block_tables(self.seqs, max_blocks)
+        lens = self.manager.context_lens(self.seqs)
+        self.block_tables = self._dev(tables)
+        self.context_lens = self._dev(lens)
         self.query_start = self._dev(np.concatenate([[0], np.cumsum(counts)]).astype(np.int32))
+        # groups of sequences sharing leading blocks (forked candidates), for
+        # the grouped decode; at most 16 query rows per group and kv head
+        group = max(1, self.num_q_heads // self.pool.num_kv_heads)
+        gs, gsh = shared_prefix_groups(tables, lens, max(1, 16 // group))
+        self.group_start, self.group_shared = self._dev(gs), self._dev(gsh)
+        self.shared_blocks = int(gsh.sum())
 
     def step_multi(self, q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
                    out: Optional[torch.Tensor] = None, scale: Optional[float] = None) -> torch.Tensor:
@@ -82,11 +94,21 @@ class DecodeSession:
                                        out=out)
 
     def step(self, q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor, out: Optional[torch.Tensor] = None,
-             partition_tokens: int = 0, scale: Optional[float] = None) -> torch.Tensor:
+             partition_tokens: int = 0, scale: Optional[float] = None, grouped: bool = False) -> torch.Tensor:
         """Enqueue one decode step; re-running it after the same prepare_step
-        rewrites the same bytes and recomputes the same outputs."""
+        rewrites the same bytes and recomputes the same outputs.  grouped:
+        read each shared prefix once per group of forked sequences."""
         scale = (1.0 / self.pool.head_dim ** 0.5) if scale is None else scale
         copy_blocks(self.pool, self.pairs)
         reshape_and_cache(self.pool, k_new, v_new, self.slot_mapping)
+        return self.attend(q, out=out, partition_tokens=partition_tokens, scale=scale, grouped=grouped)
+
+    def attend(self, q: torch.Tensor, out: Optional[torch.Tensor] = None, partition_tokens: int = 0,
+               scale: Optional[float] = None, grouped: bool = False) -> torch.Tensor:
+        """Decode attention alone, over the prepared step's tables."""
+        scale = (1.0 / self.pool.head_dim ** 0.5) if scale is None else scale
+        if grouped:
+            return paged_attention_decode_grouped(self.pool, q, self.block_tables, self.context_lens, scale,
+                                                  self.group_start, self.group_shared, out=out)
         return paged_attention_decode(self.pool, q, self.block_tables, self.context_lens, scale, out=out,
                                       partition_tokens=partition_tokens)

@@ -20,17 +20,18 @@ def announce(msg: str) -> None:
     print(f"[gpu-test] {msg}", file=sys.stderr, flush=True)
 
 
-def run_gpu(wl, partition_tokens=None, free_order=None, repeat: int = 1):
+def run_gpu(wl, partition_tokens=None, free_order=None, repeat: int = 1, grouped: bool = False):
     """Build the workload on the GPU and run `repeat` decode steps.
     Returns a dict with host copies of the pools (raw bytes), the output of
     each step (float64) and the session's step inputs."""
-    announce(f"{wl.name} partition={partition_tokens if partition_tokens is not None else wl.partition_tokens}")
+    announce(f"{wl.name} partition={partition_tokens if partition_tokens is not None else wl.partition_tokens}"
+             f"{' grouped' if grouped else ''}")
     dev = device()
     sess, q, kn, vn = bench.build_session(wl, dev, free_order=free_order)
     pt = wl.partition_tokens if partition_tokens is None else partition_tokens
     outs = []
     for _ in range(repeat):
-        out = sess.step(q, kn, vn, partition_tokens=pt, scale=wl.scale)
+        out = sess.step(q, kn, vn, partition_tokens=pt, scale=wl.scale, grouped=grouped)
         torch.cuda.synchronize(dev)
         outs.append(out.float().cpu().double().numpy())
     pool = sess.pool
@@ -43,6 +44,7 @@ def run_gpu(wl, partition_tokens=None, free_order=None, repeat: int = 1):
         "tables": sess.block_tables.cpu().numpy(),
         "pairs": sess.pairs.cpu().numpy(),
         "slots": sess.slot_mapping.cpu().numpy(),
+        "q": q,
     }
 
 
