@@ -190,7 +190,8 @@ def cpu_baseline(wl: W.Workload, target_s: float = 12.0) -> dict:
 
 _CSRC = "paged_kv_cache_449_amd/csrc/"
 KERNEL_SOURCES = {
-    "decode": tuple(_CSRC + f for f in ("common.h", "decode_kernel.h", "decode_mfma.h", "decode.hip")),
+    "decode": tuple(_CSRC + f for f in ("common.h", "decode_kernel.h", "decode_mfma.h", "decode.hip",
+                                        "decode_grouped.h", "decode_grouped.hip")),
     "prefill": tuple(_CSRC + f for f in ("common.h", "decode_kernel.h", "decode_mfma.h", "prefill_kernel.h",
                                          "prefill.hip")),
 }
@@ -458,7 +459,8 @@ def main(argv=None) -> int:
                    "decode": "grouped" if args.grouped else "flat",
                    "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(wl.name),
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic(wl.name + (":grouped" if args.grouped else "")),
                      "kernel": ("paged_decode_shared_kernel + paged_decode_suffix_kernel" if args.grouped
                                 else "paged_decode_kernel"),
                      "kernel_us": round(float(dec_ms.mean()) * 1e3, 2),
