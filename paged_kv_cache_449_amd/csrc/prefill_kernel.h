@@ -206,15 +206,23 @@ void paged_prefill_kernel(const DecodeParams p) {
 // split row blocks leave 64-row records that the last-arriving work-group
 // merges with all its threads.
 
-// Waves per work-group (16 rows each): 8 (128-row blocks) where two
-// buffers of 8 tiles fit in LDS, else 4.
+// Waves per work-group and 16-row tiles per wave: 8 x 1 (128-row blocks)
+// for head dim up to 128, 4 x 1 (64-row blocks) for head dim 256, whose two
+// LDS buffers of 8 tiles would not fit.  Two row tiles per wave (4 x 2, so
+// every LDS read of K and V feeds 32 rows) measured 8-10% slower on MI355X:
+// the extra registers halve the waves per CU.
 template <int D>
 constexpr int wg_waves() { return D <= 128 ? 8 : 4; }
+template <int D>
+constexpr int wg_row_tiles() { return 1; }
+// rows per block
+template <int D>
+constexpr int wg_rows() { return 16 * wg_waves<D>() * wg_row_tiles<D>(); }
 constexpr int kMaxWgRows = 128;   // records are sized for the largest block
 constexpr int kTileGroup = 4;     // tiles a wave computes together
 
-// Out rows of a row block's records: row j is row tile waves * rb + j / 16,
-// slot j % 16 of it.
+// Out rows of a row block's records: row j is row tile waves * rb + j / 16
+// (waves: row tiles per block), slot j % 16 of it.
 struct BlockRows {
   int64_t qs;      // the sequence's first query row
   int waves;       // row tiles per block
@@ -248,6 +256,8 @@ __device__ inline void prefill_wg_run(const DecodeParams& p, int w, int chunk, i
   using Ops = mfma_ops<MT>;
   using Sh = MfmaShape<KV, D>;
   constexpr int W = wg_waves<D>();
+  constexpr int RT = wg_row_tiles<D>();   // 16-row tiles per wave
+  constexpr int TB = W * RT;              // row tiles per block
   constexpr int Q = 16 / G;
   constexpr int KS = Sh::KS, DT = Sh::DT, LSTRIDE = Sh::LSTRIDE, KSTRIDE = Sh::KSTRIDE;
   constexpr int QE = elem_size<QT>::value;
@@ -265,30 +275,43 @@ __device__ inline void prefill_wg_run(const DecodeParams& p, int w, int chunk, i
   const int Hq = p.num_kv_heads * G;
   const float qsc = run_q_scale(p, h), vsc = run_v_scale(p, h);
 
-  // this wave's rows: row tile r = W rb + wave
-  const int r = W * rb + wave;
-  const int tok = r * Q + j16 / G;
-  const bool valid = tok < m;
-  const int64_t qoff = ((int64_t)(qs + tok) * Hq + (int64_t)h * G + j16 % G) * D;
-  const int limit = n - m + tok + 1;
-  const int lim_blk = tile_limit(n, m, W * Q, rb);   // tokens the row block reads
-  const int first_limit = n - m + W * rb * Q + 1;     // smallest causal limit of the block's rows
+  // this wave's rows: row tiles TB rb + RT wave + t, t < RT
+  int tok[RT], limit[RT];
+  bool valid[RT];
+  int64_t qoff[RT];
+#pragma unroll
+  for (int t = 0; t < RT; ++t) {
+    const int r = TB * rb + RT * wave + t;
+    tok[t] = r * Q + j16 / G;
+    valid[t] = tok[t] < m;
+    qoff[t] = ((int64_t)(qs + tok[t]) * Hq + (int64_t)h * G + j16 % G) * D;
+    limit[t] = n - m + tok[t] + 1;
+  }
+  const int lim_blk = tile_limit(n, m, TB * Q, rb);   // tokens the row block reads
+  const int first_limit = n - m + TB * rb * Q + 1;     // smallest causal limit of the block's rows
   const int nb = (lim_blk + (1 << p.log2_bs) - 1) >> p.log2_bs;
 
-  uint4 qop[KS];
+  uint4 qop[RT][KS];
 #pragma unroll
-  for (int st = 0; st < KS; ++st) qop[st] = make_uint4(0u, 0u, 0u, 0u);
-  if (valid) {
-    const int64_t qe = qoff + kg * (D / 4);
+  for (int t = 0; t < RT; ++t) {
 #pragma unroll
-    for (int st = 0; st < KS; ++st) qop[st] = *(const uint4*)(p.q + (qe + st * 8) * QE);
+    for (int k = 0; k < KS; ++k) qop[t][k] = make_uint4(0u, 0u, 0u, 0u);
+    if (valid[t]) {
+      const int64_t qe = qoff[t] + kg * (D / 4);
+#pragma unroll
+      for (int k = 0; k < KS; ++k) qop[t][k] = *(const uint4*)(p.q + (qe + k * 8) * QE);
+    }
   }
 
-  f32x4 acc[DT];
+  f32x4 acc[RT][DT];
+  float mx_run[RT], l[RT];
 #pragma unroll
-  for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-  float mx_run = -INFINITY;
-  float l = 0.0f;
+  for (int t = 0; t < RT; ++t) {
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) acc[t][dt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    mx_run[t] = -INFINITY;
+    l[t] = 0.0f;
+  }
 
   RunCtx c;
   const int64_t tile = (int64_t)Sh::ROW << p.log2_bs;
@@ -324,20 +347,24 @@ __device__ inline void prefill_wg_run(const DecodeParams& p, int w, int chunk, i
     }
   };
 
-  // this wave's 16 rows against tiles g0 .. g0+3 of step st (LDS slots g0..,
-  // tiles st*W + g0 .. of the window): QK of the four tiles interleaved, one
-  // online-softmax update for their 64 tokens, then PV on 16x16x32 steps that
-  // pair tiles (0, 1) and (2, 3).  In a paired step the contraction index
-  // 8kg + e stands for token 4kg + e of the first tile (e < 4) and token
-  // 4kg + e - 4 of the second, on both operands: two transposing reads give
-  // the V^T words, the two tiles' score words the P words.
+  // this wave's RT row tiles against tiles g0 .. g0+3 of step st (LDS slots
+  // g0.., tiles st*W + g0 .. of the window): every K word and V^T read from
+  // LDS feeds all RT row tiles.  Per row tile: QK of the four tiles
+  // interleaved, one online-softmax update for their 64 tokens, then PV on
+  // 16x16x32 steps that pair tiles (0, 1) and (2, 3).  In a paired step the
+  // contraction index 8kg + e stands for token 4kg + e of the first tile
+  // (e < 4) and token 4kg + e - 4 of the second, on both operands: two
+  // transposing reads give the V^T words, the two tiles' score words the P
+  // words.
   auto compute_group = [&](int tab, int tlo, int thi, int st, int g0, int unmasked_end) {
     const uint8_t* vlds = vbuf + ((st & 1) * W + g0) * VBYTES;
     const uint8_t* klds = kbuf + ((st & 1) * W + g0) * KBYTES;
     const int j0 = st * W + g0;   // window tile index of slot g0
-    f32x4 sc[kTileGroup];
+    f32x4 sc[RT][kTileGroup];
 #pragma unroll
-    for (int t = 0; t < kTileGroup; ++t) sc[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+      for (int t = 0; t < kTileGroup; ++t) sc[rt][t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int q = 0; q < Sh::KL; ++q) {
       uint4 kq[kTileGroup];
@@ -352,74 +379,82 @@ __device__ inline void prefill_wg_run(const DecodeParams& p, int w, int chunk, i
         for (int t = 0; t < kTileGroup; ++t) {
           uint4 kw[Sh::KL];
           kw[q] = kq[t];
-          sc[t] = Ops::qk(mfma_k_operand<KV, MT, D>(kw, kst), qop[kst], sc[t]);
+          const uint4 ka = mfma_k_operand<KV, MT, D>(kw, kst);
+#pragma unroll
+          for (int rt = 0; rt < RT; ++rt) sc[rt][t] = Ops::qk(ka, qop[rt][kst], sc[rt][t]);
         }
       }
     }
-    // Scores in log2 units.  Masking (causal limits, the window's end, table
-    // entries outside the pool) is needed only where a step reaches past the
-    // block's smallest limit or the window holds an invalid entry.
-    float x[kTileGroup][4];
+    const bool masked = tlo + (j0 + kTileGroup) * 16 > unmasked_end;
+    uint32_t ph[RT][kTileGroup][2], pr[RT][kTileGroup][2];
 #pragma unroll
-    for (int t = 0; t < kTileGroup; ++t)
+    for (int rt = 0; rt < RT; ++rt) {
+      // Scores in log2 units.  Masking (causal limits, the window's end,
+      // table entries outside the pool) is needed only where a group reaches
+      // past the block's smallest limit or the window holds an invalid entry.
+      float x[kTileGroup][4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) x[t][i] = sc[t][i] * qsc;
-    if (tlo + (j0 + kTileGroup) * 16 > unmasked_end) {
-      const int lim = min(thi, limit);
+      for (int t = 0; t < kTileGroup; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) x[t][i] = sc[rt][t][i] * qsc;
+      if (masked) {
+        const int lim = min(thi, limit[rt]);
+#pragma unroll
+        for (int t = 0; t < kTileGroup; ++t) {
+          const int j = j0 + t;
+          const bool bvalid = __builtin_amdgcn_readlane(tab, min((j * 16) >> p.log2_bs, 63)) >= 0;
+          const int t0 = tlo + j * 16 + 4 * kg;
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (!(bvalid && t0 + i < lim)) x[t][i] = -INFINITY;
+        }
+      }
+      float mx = fmaxf(fmaxf(fmaxf(x[0][0], x[0][1]), fmaxf(x[0][2], x[0][3])),
+                       fmaxf(fmaxf(x[1][0], x[1][1]), fmaxf(x[1][2], x[1][3])));
+      mx = fmaxf(mx, fmaxf(fmaxf(fmaxf(x[2][0], x[2][1]), fmaxf(x[2][2], x[2][3])),
+                           fmaxf(fmaxf(x[3][0], x[3][1]), fmaxf(x[3][2], x[3][3]))));
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      // Lazy rescaling: the reference max moves only when a row's max passes
+      // it by more than kRescaleSlack (log2 units).
+      if (__ballot(mx > mx_run[rt] + kRescaleSlack)) {
+        const float mn = fmaxf(mx_run[rt], mx);
+        const float alpha = mx_run[rt] == -INFINITY ? 0.0f : fexp2(mx_run[rt] - mn);
+        mx_run[rt] = mn;
+        l[rt] *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) acc[rt][dt] *= alpha;
+      }
+      const float mu = mx_run[rt] == -INFINITY ? 0.0f : mx_run[rt];
+      float psum = 0.0f;
 #pragma unroll
       for (int t = 0; t < kTileGroup; ++t) {
-        const int j = j0 + t;
-        const bool bvalid = __builtin_amdgcn_readlane(tab, min((j * 16) >> p.log2_bs, 63)) >= 0;
-        const int t0 = tlo + j * 16 + 4 * kg;
+        float e[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (!(bvalid && t0 + i < lim)) x[t][i] = -INFINITY;
+        for (int i = 0; i < 4; ++i) e[i] = fexp2(x[t][i] - mu);
+        psum += (e[0] + e[1]) + (e[2] + e[3]);
+        ph[rt][t][0] = Ops::pack(e[0], e[1]);
+        ph[rt][t][1] = Ops::pack(e[2], e[3]);
+        pr[rt][t][0] = Ops::pack(e[0] - Ops::lo(ph[rt][t][0]), e[1] - Ops::hi(ph[rt][t][0]));
+        pr[rt][t][1] = Ops::pack(e[2] - Ops::lo(ph[rt][t][1]), e[3] - Ops::hi(ph[rt][t][1]));
       }
+      l[rt] += psum;
     }
-    float mx = fmaxf(fmaxf(fmaxf(x[0][0], x[0][1]), fmaxf(x[0][2], x[0][3])),
-                     fmaxf(fmaxf(x[1][0], x[1][1]), fmaxf(x[1][2], x[1][3])));
-    mx = fmaxf(mx, fmaxf(fmaxf(fmaxf(x[2][0], x[2][1]), fmaxf(x[2][2], x[2][3])),
-                         fmaxf(fmaxf(x[3][0], x[3][1]), fmaxf(x[3][2], x[3][3]))));
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    // Lazy rescaling: the reference max mx_run moves only when a row's max
-    // passes it by more than kRescaleSlack (log2 units), so weights stay
-    // below 2^kRescaleSlack and acc is rescaled rarely, not every step.
-    if (__ballot(mx > mx_run + kRescaleSlack)) {
-      const float mn = fmaxf(mx_run, mx);
-      const float alpha = mx_run == -INFINITY ? 0.0f : fexp2(mx_run - mn);
-      mx_run = mn;
-      l *= alpha;
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) acc[dt] *= alpha;
-    }
-    const float mu = mx_run == -INFINITY ? 0.0f : mx_run;
-    uint32_t ph[kTileGroup][2], pr[kTileGroup][2];
-    float psum = 0.0f;
-#pragma unroll
-    for (int t = 0; t < kTileGroup; ++t) {
-      float e[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) e[i] = fexp2(x[t][i] - mu);
-      psum += (e[0] + e[1]) + (e[2] + e[3]);
-      ph[t][0] = Ops::pack(e[0], e[1]);
-      ph[t][1] = Ops::pack(e[2], e[3]);
-      pr[t][0] = Ops::pack(e[0] - Ops::lo(ph[t][0]), e[1] - Ops::hi(ph[t][0]));
-      pr[t][1] = Ops::pack(e[2] - Ops::lo(ph[t][1]), e[3] - Ops::hi(ph[t][1]));
-    }
-    l += psum;
     const int tro = (4 * kg + (j16 >> 2)) * LSTRIDE + (lane & 3) * 8;
 #pragma unroll
     for (int pair = 0; pair < kTileGroup / 2; ++pair) {
       const int ta = 2 * pair, tb = 2 * pair + 1;
-      const uint4 bh = make_uint4(ph[ta][0], ph[ta][1], ph[tb][0], ph[tb][1]);
-      const uint4 br = make_uint4(pr[ta][0], pr[ta][1], pr[tb][0], pr[tb][1]);
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
-        const uint2 va = __builtin_bit_cast(uint2, Ops::read_tr(vlds + ta * VBYTES + tro + dt * 32));
-        const uint2 vb = __builtin_bit_cast(uint2, Ops::read_tr(vlds + tb * VBYTES + tro + dt * 32));
+        const uint2 va = Ops::read_tr(vlds + ta * VBYTES + tro + dt * 32);
+        const uint2 vb = Ops::read_tr(vlds + tb * VBYTES + tro + dt * 32);
         const uint4 a = make_uint4(va.x, va.y, vb.x, vb.y);
-        acc[dt] = Ops::qk(a, br, Ops::qk(a, bh, acc[dt]));
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+          const uint4 bh = make_uint4(ph[rt][ta][0], ph[rt][ta][1], ph[rt][tb][0], ph[rt][tb][1]);
+          const uint4 br = make_uint4(pr[rt][ta][0], pr[rt][ta][1], pr[rt][tb][0], pr[rt][tb][1]);
+          acc[rt][dt] = Ops::qk(a, br, Ops::qk(a, bh, acc[rt][dt]));
+        }
       }
     }
   };
@@ -456,30 +491,39 @@ __device__ inline void prefill_wg_run(const DecodeParams& p, int w, int chunk, i
     tab = tab_next;
   }
 
-  l += __shfl_xor(l, 16);
-  l += __shfl_xor(l, 32);
+#pragma unroll
+  for (int t = 0; t < RT; ++t) {
+    l[t] += __shfl_xor(l[t], 16);
+    l[t] += __shfl_xor(l[t], 32);
+  }
 
   if (off == 0 && off + len == nb) {   // the whole row block is ours
-    if (valid) {
-      const float mul = l > 0.0f ? vsc / l : 0.0f;
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        const float v4[4] = {acc[dt][0], acc[dt][1], acc[dt][2], acc[dt][3]};
-        store_row<QT, 4>(p.out + (qoff + dt * 16 + 4 * kg) * QE, v4, mul);
+    for (int t = 0; t < RT; ++t) {
+      if (valid[t]) {
+        const float mul = l[t] > 0.0f ? vsc / l[t] : 0.0f;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+          const float v4[4] = {acc[t][dt][0], acc[t][dt][1], acc[t][dt][2], acc[t][dt][3]};
+          store_row<QT, 4>(p.out + (qoff[t] + dt * 16 + 4 * kg) * QE, v4, mul);
+        }
       }
     }
     return;
   }
 
-  // publish this wave's 16 rows of the 64-row record, then one arrival for
+  // publish this wave's rows of the block's record, then one arrival for
   // the work-group
-  const RecordRef rec = record_ref<D, 16 * W>(partial_record<D, 16 * W>(p, w, wstart, pos));
-  if (valid) {
-    const int rg = (wave * 16 + j16) * (D + 4);
+  const RecordRef rec = record_ref<D, 16 * TB>(partial_record<D, 16 * TB>(p, w, wstart, pos));
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
-      record_store4(rec, rg + dt * 16 + 4 * kg, acc[dt][0], acc[dt][1], acc[dt][2], acc[dt][3]);
-    if (kg == 0) record_store4(rec, rg + D, mx_run, l, 0.0f, 0.0f);
+  for (int t = 0; t < RT; ++t) {
+    if (valid[t]) {
+      const int rg = ((RT * wave + t) * 16 + j16) * (D + 4);
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+        record_store4(rec, rg + dt * 16 + 4 * kg, acc[t][dt][0], acc[t][dt][1], acc[t][dt][2], acc[t][dt][3]);
+      if (kg == 0) record_store4(rec, rg + D, mx_run[t], l[t], 0.0f, 0.0f);
+    }
   }
   const int seg_start = pos - off;
   const int first_w = seg_start / chunk;
@@ -492,13 +536,13 @@ __device__ inline void prefill_wg_run(const DecodeParams& p, int w, int chunk, i
   }
   __syncthreads();
   if (last_flag)
-    merge_records<QT, D, 16 * W, BlockRows, 64 * W>(
-        p, first_w, last_w, seg_start, chunk, BlockRows{qs, W, rb, m, Q, Hq, h * G, G, D}, vsc);
+    merge_records<QT, D, 16 * TB, BlockRows, 64 * W>(
+        p, first_w, last_w, seg_start, chunk, BlockRows{qs, TB, rb, m, Q, Hq, h * G, G, D}, vsc);
 }
 
 template <typename KV, typename QT, int D, int G>
 __device__ inline void prefill_wg_chunk(const DecodeParams& p, int v, int chunk, int T, int total) {
-  constexpr int QB = wg_waves<D>() * (16 / G);   // tokens per row block
+  constexpr int QB = wg_rows<D>() / G;   // tokens per row block
   const int lane = (int)(threadIdx.x & 63);
   const int S = p.num_seqs;
   const int max_len = p.max_blocks << p.log2_bs;
@@ -572,7 +616,7 @@ __device__ inline void prefill_wg_chunk(const DecodeParams& p, int v, int chunk,
 
 template <typename KV, typename QT, int D, int G>
 __global__ __launch_bounds__(64 * wg_waves<D>()) void paged_prefill_wg_kernel(const DecodeParams p) {
-  constexpr int QB = wg_waves<D>() * (16 / G);
+  constexpr int QB = wg_rows<D>() / G;
   const int lane = (int)(threadIdx.x & 63);
   const int S = p.num_seqs;
   const int max_len = p.max_blocks << p.log2_bs;
@@ -607,7 +651,7 @@ __global__ __launch_bounds__(64 * wg_waves<D>()) void paged_prefill_wg_kernel(co
 // (no records).  The grid may exceed the units; the rest exit at once.
 template <typename KV, typename QT, int D, int G>
 __global__ __launch_bounds__(64 * wg_waves<D>()) void paged_prefill_unit_kernel(const DecodeParams p) {
-  constexpr int QB = wg_waves<D>() * (16 / G);
+  constexpr int QB = wg_rows<D>() / G;
   const int lane = (int)(threadIdx.x & 63);
   const int S = p.num_seqs;
   const int max_len = p.max_blocks << p.log2_bs;

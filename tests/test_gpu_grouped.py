@@ -14,9 +14,10 @@ from oracle.run import OracleRun, check_close
 pytestmark = pytest.mark.gpu
 
 
-def _shared_wl(name, index, hq, hkv, kv, q, prompt_lens, n):
+def _shared_wl(name, index, hq, hkv, kv, q, prompt_lens, n, head_scales=False, bs=16):
     parent = [p for p in range(len(prompt_lens)) for _ in range(n)]
-    return W._make(name, index, hq, hkv, 128, kv, q, 16, prompt_lens=prompt_lens, parent=parent)
+    return W._make(name, index, hq, hkv, 128, kv, q, bs, prompt_lens=prompt_lens, parent=parent,
+                   head_scales=head_scales)
 
 
 CASES = {
@@ -27,6 +28,9 @@ CASES = {
     "gqa4_fp8": _shared_wl("gqa4_fp8", 41, 8, 2, "fp8e4m3", "bf16", [95, 80, 130], 4),
     "gqa8_f16_split": _shared_wl("gqa8_f16_split", 42, 16, 2, "f16", "f16", [63, 200], 4),
     "mha_bf16_n6": _shared_wl("mha_bf16_n6", 43, 4, 4, "bf16", "bf16", [33, 47], 6),
+    "gqa2_fp8_headscale_f16": _shared_wl("gqa2_fp8_headscale_f16", 44, 8, 4, "fp8e4m3", "f16", [70, 150], 3,
+                                         head_scales=True),
+    "mha_f16_bs32": _shared_wl("mha_f16_bs32", 45, 4, 4, "f16", "f16", [95, 64], 4, bs=32),
 }
 
 

@@ -21,6 +21,8 @@ from oracle.run import OracleRun, check_close
 pytestmark = pytest.mark.gpu
 
 SMALL = list(W.small_multi_token_configs())
+ALL_SMALL = {**W.small_multi_token_configs(),
+             **{k: v for k, v in W.small_variant_configs().items() if v.multi_token}}
 
 
 @pytest.fixture(scope="module")
@@ -41,9 +43,9 @@ def path(request, monkeypatch):
     return request.param
 
 
-@pytest.mark.parametrize("name", SMALL)
+@pytest.mark.parametrize("name", list(ALL_SMALL))
 def test_prefill_matches_oracle(gpu, name, path):
-    wl = W.small_multi_token_configs()[name]
+    wl = ALL_SMALL[name]
     got = gpu(wl)
     ref = OracleRun(wl)
     np.testing.assert_array_equal(got["tables"], ref.tables)
