@@ -100,6 +100,10 @@ __global__ __launch_bounds__(64) void paged_decode_suffix_kernel(const DecodePar
     if (s >= gi.gs && s < gi.ge) shared = gi.shared;
   }
 
+  const int bs = 1 << p.log2_bs;
+  const int off = shared >> p.log2_bs;   // shared is a whole number of blocks, at most n
+  const int nb = (n + bs - 1) >> p.log2_bs;
+  const int tab = nb > off ? load_table_window(p, run_table(p, s, off), 0, nb - off) : -1;
   const float qs = run_q_scale(p, h), vs = run_v_scale(p, h);
   float qv[G][VEC];
   {
@@ -128,11 +132,7 @@ __global__ __launch_bounds__(64) void paged_decode_suffix_kernel(const DecodePar
       l[g] = rec[D + 1];
     }
   }
-  const int bs = 1 << p.log2_bs;
-  const int off = shared >> p.log2_bs;   // shared is a whole number of blocks, at most n
-  const int nb = (n + bs - 1) >> p.log2_bs;
-  if (shared < n && nb > off)
-    valu_stream<KV, D, G, kStreamPolicy>(p, s, h, off, nb - off, n, qv, m, l, acc);
+  if (shared < n && nb > off) valu_stream<KV, D, G, kStreamPolicy>(p, s, h, off, nb - off, n, tab, qv, m, l, acc);
 
 #pragma unroll
   for (int o = L; o < 64; o <<= 1) {

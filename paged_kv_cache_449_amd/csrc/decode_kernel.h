@@ -315,35 +315,76 @@ struct ContiguousRows {   // G query heads of one sequence: rows orow + j*D
 // counter for the next call.  seg_start is the run's first position in the
 // flattened stream.  Each of the NT threads owns 4 consecutive elements of
 // [G][D] per pass.
+//
+// The records are read through the coherence point, a full memory round
+// trip each, so they are fetched in batches of B workers with every load of
+// a batch (all passes) issued before any is used: a run split over up to B
+// workers costs one round trip.  Within a batch the weights are taken
+// against the batch's maximum; a later batch with a larger maximum rescales
+// what is summed so far.
 template <typename QT, int D, int G, typename Rows, int NT = 64>
 __device__ inline void merge_records(const DecodeParams& p, int first_w, int last_w, int seg_start, int chunk,
                                      const Rows& rows, float v_scale) {
   constexpr int REC = D + 4;
   constexpr int QE = elem_size<QT>::value;
   static_assert(D % 4 == 0, "record layout");
-  for (int e0 = threadIdx.x * 4; e0 < G * D; e0 += 4 * NT) {
+  constexpr int PASSES = (G * D + 4 * NT - 1) / (4 * NT);
+  constexpr int B = PASSES >= 8 ? 1 : 8 / PASSES;   // about 64 registers of loads in flight
+  float M[PASSES], lsum[PASSES], o[PASSES][4];
+#pragma unroll
+  for (int q = 0; q < PASSES; ++q) {
+    M[q] = -INFINITY;
+    lsum[q] = 0.0f;
+    o[q][0] = o[q][1] = o[q][2] = o[q][3] = 0.0f;
+  }
+  for (int v0 = first_w; v0 <= last_w; v0 += B) {
+    float4 ml[B][PASSES], a[B][PASSES];
+#pragma unroll
+    for (int b = 0; b < B; ++b) {
+      const int v = min(v0 + b, last_w);   // past the run: a repeat, not used
+      const RecordRef r = record_ref<D, G>(p.partials + (int64_t)(2 * v + (v * chunk >= seg_start ? 0 : 1)) * G * REC);
+#pragma unroll
+      for (int q = 0; q < PASSES; ++q) {
+        const int e0 = min((int)threadIdx.x * 4 + q * 4 * NT, G * D - 4);
+        const int g = e0 / D, d = e0 % D;
+        ml[b][q] = record_load4(r, g * REC + D);
+        a[b][q] = record_load4(r, g * REC + d);
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < PASSES; ++q) {
+      float mb = -INFINITY;
+#pragma unroll
+      for (int b = 0; b < B; ++b)
+        if (v0 + b <= last_w) mb = fmaxf(mb, ml[b][q].x);
+      const float mn = fmaxf(M[q], mb);
+      if (mn > M[q] && M[q] != -INFINITY) {   // rescale the earlier batches
+        const float r = fexp2(M[q] - mn);
+        lsum[q] *= r;
+        o[q][0] *= r; o[q][1] *= r; o[q][2] *= r; o[q][3] *= r;
+      }
+      M[q] = mn;
+      const float mu = mn == -INFINITY ? 0.0f : mn;
+#pragma unroll
+      for (int b = 0; b < B; ++b) {
+        if (v0 + b > last_w) continue;
+        const float f = fexp2(ml[b][q].x - mu);
+        lsum[q] = fmaf(f, ml[b][q].y, lsum[q]);
+        o[q][0] = fmaf(f, a[b][q].x, o[q][0]);
+        o[q][1] = fmaf(f, a[b][q].y, o[q][1]);
+        o[q][2] = fmaf(f, a[b][q].z, o[q][2]);
+        o[q][3] = fmaf(f, a[b][q].w, o[q][3]);
+      }
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < PASSES; ++q) {
+    const int e0 = (int)threadIdx.x * 4 + q * 4 * NT;
+    if (e0 >= G * D) continue;
     const int g = e0 / D, d = e0 % D;
     const int64_t orow = rows(g);
     if (orow < 0) continue;
-    float M = -INFINITY;
-    for (int v = first_w; v <= last_w; ++v) {
-      const RecordRef r = record_ref<D, G>(p.partials + (int64_t)(2 * v + (v * chunk >= seg_start ? 0 : 1)) * G * REC);
-      M = fmaxf(M, record_load4(r, g * REC + D).x);
-    }
-    const float mu = M == -INFINITY ? 0.0f : M;
-    float lsum = 0.0f, o[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-    for (int v = first_w; v <= last_w; ++v) {
-      const RecordRef r = record_ref<D, G>(p.partials + (int64_t)(2 * v + (v * chunk >= seg_start ? 0 : 1)) * G * REC);
-      const float4 ml = record_load4(r, g * REC + D);
-      const float4 a = record_load4(r, g * REC + d);
-      const float f = fexp2(ml.x - mu);
-      lsum = fmaf(f, ml.y, lsum);
-      o[0] = fmaf(f, a.x, o[0]);
-      o[1] = fmaf(f, a.y, o[1]);
-      o[2] = fmaf(f, a.z, o[2]);
-      o[3] = fmaf(f, a.w, o[3]);
-    }
-    store_row<QT, 4>(p.out + (orow + d) * QE, o, lsum > 0.0f ? v_scale / lsum : 0.0f);
+    store_row<QT, 4>(p.out + (orow + d) * QE, o[q], lsum[q] > 0.0f ? v_scale / lsum[q] : 0.0f);
   }
   if (threadIdx.x == 0) __hip_atomic_store(p.counters + first_w, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -358,11 +399,18 @@ __device__ inline int load_table_window(const DecodeParams& p, const int32_t* tr
   return (uint32_t)e < (uint32_t)p.num_blocks ? e : -1;
 }
 
+// The run's table row from logical block off on.
+__device__ inline const int32_t* run_table(const DecodeParams& p, int s, int off) {
+  return p.block_tables + (int64_t)s * p.max_blocks + off;
+}
+
 // Stream blocks [off, off+len) of the (kv head h, sequence s) context of n
 // tokens through one wave's online-softmax state (per-row-group m, l, acc of
-// the G query rows, qv pre-scaled into log2 units).
+// the G query rows, qv pre-scaled into log2 units).  tab is the run's first
+// table window, load_table_window(p, run_table(p, s, off), 0, len), which the
+// caller loads before its query rows so the two loads overlap.
 template <typename KV, int D, int G, int POL>
-__device__ inline void valu_stream(const DecodeParams& p, int s, int h, int off, int len, int n,
+__device__ inline void valu_stream(const DecodeParams& p, int s, int h, int off, int len, int n, int tab,
                                    const float (&qv)[G][DecodeShape<KV, D>::VEC], float (&m)[G], float (&l)[G],
                                    float (&acc)[G][DecodeShape<KV, D>::VEC]) {
   using Sh = DecodeShape<KV, D>;
@@ -381,9 +429,8 @@ __device__ inline void valu_stream(const DecodeParams& p, int s, int h, int off,
   c.row_bytes = D * Sh::EB;
   c.log2_bs = p.log2_bs;
   c.bs_mask = (1 << p.log2_bs) - 1;
-  const int32_t* trow = p.block_tables + (int64_t)s * p.max_blocks + off;
+  const int32_t* trow = run_table(p, s, off);
 
-  int tab = load_table_window(p, trow, 0, len);
   for (int wb = 0; wb < len; wb += 64) {
     const int cnt = min(64, len - wb);
     // the next window's table entries load while this window streams
@@ -422,6 +469,7 @@ __device__ inline void valu_run(const DecodeParams& p, int w, int chunk, int wst
   const int col = lane % L;
   const int Hq = p.num_kv_heads * G;
   const float qs = run_q_scale(p, h), vs = run_v_scale(p, h);
+  const int tab = load_table_window(p, run_table(p, s, off), 0, len);
 
   // query rows of the G heads served by kv head h, pre-scaled into log2 units
   float qv[G][VEC];
@@ -444,7 +492,7 @@ __device__ inline void valu_run(const DecodeParams& p, int w, int chunk, int wst
     for (int i = 0; i < VEC; ++i) acc[g][i] = 0.0f;
   }
 
-  valu_stream<KV, D, G, POL>(p, s, h, off, len, n, qv, m, l, acc);
+  valu_stream<KV, D, G, POL>(p, s, h, off, len, n, tab, qv, m, l, acc);
 
   // merge the TPL row states (rows hold the same columns)
 #pragma unroll
@@ -519,21 +567,26 @@ __device__ inline void decode_chunk(const DecodeParams& p, int v, int chunk, int
   bool found = false;
   {
     int carry = 0;
-    for (int base = 0; base < S; base += 64) {
-      const int sl = base + lane;
-      int nb = 0;
-      if (sl < S) nb = (clamp_len(p.context_lens[sl], max_len) + bs - 1) >> p.log2_bs;
-      const int incl = wave_inclusive_scan_i32(nb, lane);
-      const int excl = carry + incl - nb;
-      const unsigned long long hit = __ballot(nb > 0 && excl <= r && r < excl + nb);
-      if (hit) {
-        const int src = __builtin_ctzll(hit);
-        s = base + src;
-        pre = __shfl(excl, src);
-        found = true;
-        break;
+    for (int base = 0; base < S && !found; base += 4 * 64) {
+      int nl[4];   // four slices' lengths loaded together
+#pragma unroll
+      for (int k = 0; k < 4; ++k) nl[k] = p.context_lens[min(base + 64 * k + lane, S - 1)];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        if (found) break;
+        const int sl = base + 64 * k + lane;
+        const int nb = sl < S ? (clamp_len(nl[k], max_len) + bs - 1) >> p.log2_bs : 0;
+        const int incl = wave_inclusive_scan_i32(nb, lane);
+        const int excl = carry + incl - nb;
+        const unsigned long long hit = __ballot(nb > 0 && excl <= r && r < excl + nb);
+        if (hit) {
+          const int src = __builtin_ctzll(hit);
+          s = base + 64 * k + src;
+          pre = __shfl(excl, src);
+          found = true;
+        }
+        carry += __shfl(incl, 63);
       }
-      carry += __shfl(incl, 63);
     }
   }
 
@@ -576,21 +629,34 @@ void paged_decode_kernel(const DecodeParams p) {
   // Blocks per kv head; whether some sequence is empty; whether some
   // sequence starts with the same physical block as its predecessor
   // (copy-on-write candidates sharing a prompt).
+  // Every worker computes these before streaming, so the loads of four
+  // 64-sequence slices are issued together (one memory round trip per 256
+  // sequences; entries past S repeat the last sequence and are not used).
   int total = 0;
   bool empty = false, shared = false;
-  for (int base = 0; base < S; base += 64) {
-    const int s = base + lane;
-    int nb = 0;
-    if (s < S) {
-      const int n = clamp_len(p.context_lens[s], max_len);
-      nb = (n + bs - 1) >> p.log2_bs;
-      empty |= n == 0;
-      if (s > 0 && n > 0 && clamp_len(p.context_lens[s - 1], max_len) > 0) {
-        const int b0 = p.block_tables[(int64_t)s * p.max_blocks];
-        shared |= (uint32_t)b0 < (uint32_t)p.num_blocks && b0 == p.block_tables[(int64_t)(s - 1) * p.max_blocks];
-      }
+  for (int base = 0; base < S; base += 4 * 64) {
+    int nl[4], npl[4], b0[4], bp[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int sc = min(base + 64 * k + lane, S - 1), sp = max(sc - 1, 0);
+      nl[k] = p.context_lens[sc];
+      npl[k] = p.context_lens[sp];
+      b0[k] = p.block_tables[(int64_t)sc * p.max_blocks];
+      bp[k] = p.block_tables[(int64_t)sp * p.max_blocks];
     }
-    total += wave_sum_i32(nb);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int s = base + 64 * k + lane;
+      int nb = 0;
+      if (s < S) {
+        const int n = clamp_len(nl[k], max_len);
+        nb = (n + bs - 1) >> p.log2_bs;
+        empty |= n == 0;
+        if (s > 0 && n > 0 && clamp_len(npl[k], max_len) > 0)
+          shared |= (uint32_t)b0[k] < (uint32_t)p.num_blocks && b0[k] == bp[k];
+      }
+      total += wave_sum_i32(nb);
+    }
   }
   total = uniform(total);
   const bool any_shared = __ballot(shared) != 0;

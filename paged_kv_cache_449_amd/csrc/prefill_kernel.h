@@ -65,6 +65,29 @@ __device__ inline void prefill_lengths(const DecodeParams& p, int s, int max_len
   m = min(b - a, n);
 }
 
+// Per-lane sequence tile blocks of the four 64-sequence slices from base
+// (0 past S), with every length load issued before any is used: the scans
+// below take one memory round trip per 256 sequences.
+__device__ inline void slice_tile_blocks4(const DecodeParams& p, int base, int max_len, int Q, int (&nb)[4]) {
+  const int lane = (int)(threadIdx.x & 63);
+  const int S = p.num_seqs;
+  int cl[4], qa[4], qb[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int sc = min(base + 64 * k + lane, S - 1);
+    cl[k] = p.context_lens[sc];
+    qa[k] = p.query_start[sc];
+    qb[k] = p.query_start[sc + 1];
+  }
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int n = clamp_len(cl[k], max_len);
+    const int a = min(max(qa[k], 0), p.total_q);
+    const int b = min(max(qb[k], a), p.total_q);
+    nb[k] = base + 64 * k + lane < S ? sequence_tile_blocks(n, min(b - a, n), Q, p.log2_bs) : 0;
+  }
+}
+
 template <typename KV, typename QT, int D, int G>
 __device__ inline void prefill_run(const DecodeParams& p, int w, int chunk, int wstart, int pos, int s, int h, int r,
                                    int off, int len, int n, int m, int qs) {
@@ -103,25 +126,24 @@ __device__ inline void prefill_chunk(const DecodeParams& p, int v, int chunk, in
   bool found = false;
   {
     int carry = 0;
-    for (int base = 0; base < S; base += 64) {
-      const int sl = base + lane;
-      int nb = 0;
-      if (sl < S) {
-        int n, m, q0;
-        prefill_lengths(p, sl, max_len, n, m, q0);
-        nb = sequence_tile_blocks(n, m, Q, p.log2_bs);
+    for (int base = 0; base < S && !found; base += 4 * 64) {
+      int nbs[4];
+      slice_tile_blocks4(p, base, max_len, Q, nbs);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        if (found) break;
+        const int nb = nbs[k];
+        const int incl = wave_inclusive_scan_i32(nb, lane);
+        const int excl = carry + incl - nb;
+        const unsigned long long hit = __ballot(nb > 0 && excl <= rr && rr < excl + nb);
+        if (hit) {
+          const int src = __builtin_ctzll(hit);
+          s = base + 64 * k + src;
+          pre = __shfl(excl, src);
+          found = true;
+        }
+        carry += __shfl(incl, 63);
       }
-      const int incl = wave_inclusive_scan_i32(nb, lane);
-      const int excl = carry + incl - nb;
-      const unsigned long long hit = __ballot(nb > 0 && excl <= rr && rr < excl + nb);
-      if (hit) {
-        const int src = __builtin_ctzll(hit);
-        s = base + src;
-        pre = __shfl(excl, src);
-        found = true;
-        break;
-      }
-      carry += __shfl(incl, 63);
     }
   }
   if (!found) return;  // lengths changed under the launch: nothing consistent to do
@@ -166,21 +188,16 @@ template <typename KV, typename QT, int D, int G>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(D <= 128 ? 2 : 1)))
 void paged_prefill_kernel(const DecodeParams p) {
   constexpr int Q = 16 / G;
-  const int lane = threadIdx.x;
   const int S = p.num_seqs;
   const int max_len = p.max_blocks << p.log2_bs;
   // Host checks bound the stream of a consistent query_start by 2^30 blocks;
   // an inconsistent one can exceed that, and then nothing is computed.
   int64_t total64 = 0;
-  for (int base = 0; base < S; base += 64) {
-    const int s = base + lane;
-    int nb = 0;
-    if (s < S) {
-      int n, m, q0;
-      prefill_lengths(p, s, max_len, n, m, q0);
-      nb = sequence_tile_blocks(n, m, Q, p.log2_bs);
-    }
-    total64 += wave_sum_i64(nb);   // the same in every lane
+  for (int base = 0; base < S; base += 4 * 64) {
+    int nbs[4];
+    slice_tile_blocks4(p, base, max_len, Q, nbs);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) total64 += wave_sum_i64(nbs[k]);   // the same in every lane
     if (total64 * p.num_kv_heads > (1LL << 30)) return;
   }
   const int total = uniform((int)total64);
