@@ -286,7 +286,7 @@ def multi_token_result(wl: W.Workload, args, kern_ms: np.ndarray, step_ms: float
                    "block_size": wl.block_size, "kv_dtype": wl.kv_dtype, "q_dtype": wl.q_dtype,
                    "cached_tokens": c["tokens"], "row_token_pairs": c["row_token_pairs"],
                    "flops_per_launch": c["flops"], "bytes_per_launch": c["total"], "placement": args.placement,
-                   "parallelism": "single GPU"},
+                   "flush": args.flush, "parallelism": "single GPU"},
         "roofline": {"bound": "mfma" if mfma else "hbm", "achieved": round(achieved, 2), "peak": peak,
                      "unit": unit, "frac": round(achieved / peak, 4), "traffic": measured_traffic(wl.name, "prefill"),
                      "kernel": "paged_prefill_kernel", "kernel_us": round(float(kern_ms.mean()) * 1e3, 2),
@@ -349,6 +349,13 @@ def main(argv=None) -> int:
                     help="shuffled: blocks from a seeded random free list (the workload); sequential: "
                          "the free list in id order, so each sequence's blocks are contiguous (the "
                          "paged-vs-contiguous comparison)")
+    ap.add_argument("--partition-tokens", type=int, default=None,
+                    help="context split of paged_attention_decode: 0 lets the library size it, k*block_size fixes "
+                         "the chunk length (default: the workload's own setting)")
+    ap.add_argument("--flush", choices=["none", "read", "write"], default="none",
+                    help="before every step, outside its events, read (read) or write (write) a 512 MiB buffer: "
+                         "read evicts the Infinity Cache and L2 of the KV data, write also leaves dirty lines that "
+                         "drain during the next kernels; ms_per_step then sums the steps' own event intervals")
     ap.add_argument("--grouped", action="store_true",
                     help="decode with paged_attention_decode_grouped: each shared prefix (forked candidates) is "
                          "read once per group")
@@ -377,7 +384,9 @@ def main(argv=None) -> int:
     sess, q, kn, vn = build_session(wl, dev, free_order=order)
     out = torch.empty_like(q)
     pool = sess.pool
-    pt = wl.partition_tokens
+    pt = wl.partition_tokens if args.partition_tokens is None else args.partition_tokens
+    # counters taken at the workload's own split describe only that split
+    traffic_key = wl.name + (":grouped" if args.grouped else "") + ("" if pt == wl.partition_tokens else f":pt{pt}")
 
     multi = wl.multi_token
 
@@ -406,21 +415,36 @@ def main(argv=None) -> int:
         torch.bitwise_not(src, out=dst)
         torch.cuda.synchronize(dev)
         del src, dst
+    scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev) if args.flush != "none" else None
+
+    def flush():
+        if args.flush == "read":
+            scratch.max()
+        elif args.flush == "write":
+            scratch.zero_()
+
     for _ in range(args.warmup):
+        flush()
         one_step()
     torch.cuda.synchronize(dev)
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    sevs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize(dev)
     t0 = time.perf_counter()
     g0.record()
     for i in range(args.steps):
+        flush()
+        sevs[i][0].record()
         one_step(evs[i])
+        sevs[i][1].record()
     g1.record()
     torch.cuda.synchronize(dev)
     wall = time.perf_counter() - t0
     dec_ms = np.array([a.elapsed_time(b) for a, b in evs])
-    step_ms = wall * 1e3 / args.steps
+    # without a flush the steps run back to back and the bracket around all
+    # of them gives the step time; with one, the steps' own intervals do
+    step_ms = wall * 1e3 / args.steps if scratch is None else float(np.mean([a.elapsed_time(b) for a, b in sevs]))
     if multi:
         res = multi_token_result(wl, args, dec_ms, step_ms)
         if not args.no_cpu_baseline:
@@ -456,11 +480,12 @@ def main(argv=None) -> int:
                    "num_kv_heads": wl.num_kv_heads, "head_dim": wl.head_dim, "block_size": wl.block_size,
                    "kv_dtype": wl.kv_dtype, "q_dtype": wl.q_dtype, "cached_tokens": nb["tokens"],
                    "kv_bytes_per_step": nb["kv"], "partition_tokens": pt, "placement": args.placement,
+                   "flush": args.flush,
                    "decode": "grouped" if args.grouped else "flat",
                    "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": measured_traffic(wl.name + (":grouped" if args.grouped else "")),
+                     "traffic": measured_traffic(traffic_key),
                      "kernel": ("paged_decode_shared_kernel + paged_decode_suffix_kernel" if args.grouped
                                 else "paged_decode_kernel"),
                      "kernel_us": round(float(dec_ms.mean()) * 1e3, 2),

@@ -2,8 +2,9 @@
 forked candidates read their shared prompt blocks once per group.  Outputs
 must match the oracle's decode (which knows nothing of groups) within the
 decode tolerances, on MHA and GQA query groups, 16-bit and fp8 pools, groups
-cut to the 16-row limit by the host helper or by the library, and groups
-whose stated sharing is zero or longer than the contexts."""
+cut to the 16-row limit by the host helper or by the library, more groups
+than one 64-lane slice of group starts, and groups whose stated sharing is
+zero or longer than the contexts."""
 import numpy as np
 import pytest
 import torch
@@ -31,6 +32,8 @@ CASES = {
     "gqa2_fp8_headscale_f16": _shared_wl("gqa2_fp8_headscale_f16", 44, 8, 4, "fp8e4m3", "f16", [70, 150], 3,
                                          head_scales=True),
     "mha_f16_bs32": _shared_wl("mha_f16_bs32", 45, 4, 4, "f16", "f16", [95, 64], 4, bs=32),
+    # more groups than one 64-lane slice of group starts
+    "many_groups_f16": _shared_wl("many_groups_f16", 46, 4, 4, "f16", "f16", [20 + 9 * (i % 7) for i in range(70)], 2),
 }
 
 
