@@ -7,9 +7,11 @@ One step = one decode iteration of the whole hot path for a batch resident in
 HBM: copy_blocks (copy-on-write pairs, none for workloads without sharing),
 reshape_and_cache (the new token of every sequence) and paged_attention_decode.
 Prints one JSON line.  `value` is KV bytes read per step / wall time per step
-(GB/s); `roofline` is the decode kernel's algorithmic bytes over its own
-event-timed duration against the MI355X HBM peak; `cpu_baseline` is the fp64
-CPU oracle timed on a bounded sample of the same workload.
+(GB/s), from K steps run back to back between two synchronisations; `roofline`
+is the decode kernel's algorithmic bytes over its own duration, from HIP events
+around each launch in K further steps, against the MI355X HBM peak;
+`cpu_baseline` is the fp64 CPU oracle timed on a bounded sample of the same
+workload.
 """
 from __future__ import annotations
 
@@ -286,7 +288,7 @@ def multi_token_result(wl: W.Workload, args, kern_ms: np.ndarray, step_ms: float
                    "block_size": wl.block_size, "kv_dtype": wl.kv_dtype, "q_dtype": wl.q_dtype,
                    "cached_tokens": c["tokens"], "row_token_pairs": c["row_token_pairs"],
                    "flops_per_launch": c["flops"], "bytes_per_launch": c["total"], "placement": args.placement,
-                   "flush": args.flush, "parallelism": "single GPU"},
+                   "flush": args.flush, "graph": args.graph, "parallelism": "single GPU"},
         "roofline": {"bound": "mfma" if mfma else "hbm", "achieved": round(achieved, 2), "peak": peak,
                      "unit": unit, "frac": round(achieved / peak, 4), "traffic": measured_traffic(wl.name, "prefill"),
                      "kernel": "paged_prefill_kernel", "kernel_us": round(float(kern_ms.mean()) * 1e3, 2),
@@ -356,6 +358,9 @@ def main(argv=None) -> int:
                     help="before every step, outside its events, read (read) or write (write) a 512 MiB buffer: "
                          "read evicts the Infinity Cache and L2 of the KV data, write also leaves dirty lines that "
                          "drain during the next kernels; ms_per_step then sums the steps' own event intervals")
+    ap.add_argument("--graph", action="store_true",
+                    help="capture one step (its copy_blocks, cache write and decode launches) in a HIP graph and "
+                         "time replays of it for ms_per_step; the kernel time still comes from eager steps")
     ap.add_argument("--grouped", action="store_true",
                     help="decode with paged_attention_decode_grouped: each shared prefix (forked candidates) is "
                          "read once per group")
@@ -427,24 +432,46 @@ def main(argv=None) -> int:
         flush()
         one_step()
     torch.cuda.synchronize(dev)
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    step = one_step
+    if args.graph:
+        # out and the workspace exist after the warm-up, so the captured
+        # launches allocate nothing and record no memset
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            one_step()
+        torch.cuda.synchronize(dev)
+        step = graph.replay
+        for _ in range(2):
+            step()
+        torch.cuda.synchronize(dev)
+
+    # 1. The step time: K steps back to back between two synchronisations,
+    #    with no event inside (each event record is a packet of its own on
+    #    the queue, about 5 us apart from the kernels).  With a flush, the
+    #    steps' own event intervals leave it out.
     sevs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
-    g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize(dev)
     t0 = time.perf_counter()
-    g0.record()
     for i in range(args.steps):
         flush()
-        sevs[i][0].record()
-        one_step(evs[i])
-        sevs[i][1].record()
-    g1.record()
+        if scratch is not None:
+            sevs[i][0].record()
+        step()
+        if scratch is not None:
+            sevs[i][1].record()
     torch.cuda.synchronize(dev)
     wall = time.perf_counter() - t0
-    dec_ms = np.array([a.elapsed_time(b) for a, b in evs])
-    # without a flush the steps run back to back and the bracket around all
-    # of them gives the step time; with one, the steps' own intervals do
     step_ms = wall * 1e3 / args.steps if scratch is None else float(np.mean([a.elapsed_time(b) for a, b in sevs]))
+
+    # 2. The kernel time: K more steps with HIP events around each launch,
+    #    recorded on the stream the library launches on.
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize(dev)
+    for i in range(args.steps):
+        flush()
+        one_step(evs[i])
+    torch.cuda.synchronize(dev)
+    dec_ms = np.array([a.elapsed_time(b) for a, b in evs])
     if multi:
         res = multi_token_result(wl, args, dec_ms, step_ms)
         if not args.no_cpu_baseline:
@@ -480,7 +507,7 @@ def main(argv=None) -> int:
                    "num_kv_heads": wl.num_kv_heads, "head_dim": wl.head_dim, "block_size": wl.block_size,
                    "kv_dtype": wl.kv_dtype, "q_dtype": wl.q_dtype, "cached_tokens": nb["tokens"],
                    "kv_bytes_per_step": nb["kv"], "partition_tokens": pt, "placement": args.placement,
-                   "flush": args.flush,
+                   "flush": args.flush, "graph": args.graph,
                    "decode": "grouped" if args.grouped else "flat",
                    "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",

@@ -1,6 +1,6 @@
-"""GPU parity at the workloads' stated sizes, in the launch configuration the
+"""GPU parity at the workloads' stated sizes, in the launch configurations the
 benchmark times (library-sized work split; 512-token runs for the GQA
-long-context workload).  The oracle recomputes sampled sequences one by one
+long-context workload, and the library-sized split there too).  The oracle recomputes sampled sequences one by one
 (the longest, the shortest and seeded random picks); copy-on-write pools are
 compared byte for byte in full."""
 import numpy as np
@@ -40,6 +40,17 @@ def test_full_size_sampled(name):
     from gpu_harness import run_gpu
     wl = W.full_configs()[name]
     got = run_gpu(wl)
+    assert np.isfinite(got["out"]).all()
+    _check_sampled(wl, got)
+
+
+@pytest.mark.parametrize("name", ["c5_gqa_long_fp8e4m3", "c5_gqa_long_bf16"])
+def test_full_size_library_split(name):
+    """The GQA long-context workloads with the library-sized split
+    (bench.py --partition-tokens 0) instead of their 512-token runs."""
+    from gpu_harness import run_gpu
+    wl = W.full_configs()[name]
+    got = run_gpu(wl, partition_tokens=0)
     assert np.isfinite(got["out"]).all()
     _check_sampled(wl, got)
 
