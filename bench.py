@@ -229,6 +229,30 @@ def measured_traffic(wl_name: str, kind: str = "decode"):
     return entry.get("traffic_bytes_per_launch")
 
 
+def achievable_read(dev, gib: int = 2, tile_bytes: int = 4096, reps: int = 5) -> dict:
+    """HBM read rate of a plain streaming kernel of the decode kernel's load
+    form (kv_stream_read): gib GiB of tile_bytes tiles in a seeded random
+    order, mean of reps launches timed with HIP events."""
+    import paged_kv_cache_449_amd as pk
+    buf = torch.empty(gib << 30, dtype=torch.uint8, device=dev)
+    buf.fill_(1)
+    n = buf.numel() // tile_bytes
+    tiles = torch.randperm(n, generator=torch.Generator().manual_seed(449)).to(torch.int32).to(dev)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    for _ in range(2):
+        pk.kv_stream_read(buf, tile_bytes, tiles, sink)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for a, e in ev:
+        a.record()
+        pk.kv_stream_read(buf, tile_bytes, tiles, sink)
+        e.record()
+    torch.cuda.synchronize(dev)
+    us = float(np.mean([a.elapsed_time(e) for a, e in ev])) * 1e3
+    del buf
+    return {"kernel": "kv_stream_read", "value": round(n * tile_bytes / us / 1e3, 1), "unit": "GB/s",
+            "tile_bytes": tile_bytes, "bytes": n * tile_bytes, "order": "random", "us": round(us, 1)}
+
+
 def swap_measurement(pool, n: int, reps: int = 5) -> dict:
     """swap_blocks of n pool blocks (K and V) to pinned host memory and back
     into the same blocks (their contents are unchanged), HIP-event timed."""
@@ -474,6 +498,9 @@ def main(argv=None) -> int:
     dec_ms = np.array([a.elapsed_time(b) for a, b in evs])
     if multi:
         res = multi_token_result(wl, args, dec_ms, step_ms)
+        res["achievable"] = achievable_read(dev)
+        if res["roofline"]["unit"] == "GB/s":
+            res["roofline"]["frac_of_achievable"] = round(res["roofline"]["achieved"] / res["achievable"]["value"], 4)
         if not args.no_cpu_baseline:
             print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
             res["cpu_baseline"] = cpu_baseline_prefill(wl)
@@ -521,6 +548,8 @@ def main(argv=None) -> int:
     }
     if args.swap_blocks > 0:
         res["swap"] = swap_measurement(pool, min(args.swap_blocks, wl.num_blocks))
+    res["achievable"] = achievable_read(dev)
+    res["roofline"]["frac_of_achievable"] = round(achieved / res["achievable"]["value"], 4)
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(wl)

@@ -332,6 +332,30 @@ typedef enum {
 kv_status_t swap_blocks(kv_pool_t* pool, void* host_k, void* host_v, int64_t num_host_blocks, const int32_t* pairs,
                         int32_t num_pairs, kv_swap_dir_t direction, void* stream);
 
+/*
+ * kv_stream_read -- measurement primitive, not part of the pages' method: read
+ * whole tiles of a device buffer with the load form of the decode kernel
+ * (16-byte non-temporal buffer loads; 256 lanes per work-group, 32 KiB in
+ * flight per work-group, 8 work-groups per compute unit) and compute
+ * nothing.  Timed over a random tile order, it gives the HBM read rate a
+ * streaming kernel reaches on the part, which the decode kernel's achieved
+ * rate is set against.  Decode is bound by that read rate ("vLLM — 把操作系统
+ * 的分页搬进 GPU KV cache": lessons).
+ *
+ *   buf, bytes   device buffer (16-byte aligned); tile i covers bytes
+ *                [i * tile_bytes, (i + 1) * tile_bytes)
+ *   tile_bytes   a positive multiple of 4096, at most bytes
+ *   tiles        device int32 [num_tiles]: tile ids in the order read; an id
+ *                outside [0, bytes / tile_bytes) reads nothing
+ *   sink         device uint32 [1]: written only if the data read hash to one
+ *                fixed value (this keeps the loads); its content has no meaning
+ * Runs on the current device.  num_tiles == 0 enqueues nothing.  Errors:
+ * KV_ERR_INVALID_ARG for a null pointer, a misaligned buffer or a bad tile
+ * size; KV_ERR_HIP if the device cannot be queried or the launch fails.
+ */
+kv_status_t kv_stream_read(const void* buf, size_t bytes, int32_t tile_bytes, const int32_t* tiles, int32_t num_tiles,
+                           uint32_t* sink, void* stream);
+
 /* kv_status_string -- static description of a status code. */
 const char* kv_status_string(kv_status_t status);
 

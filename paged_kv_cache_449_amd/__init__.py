@@ -67,6 +67,7 @@ def lib() -> ctypes.CDLL:
         L.paged_attention_decode_grouped.argtypes = [vp, vp, ctypes.c_int, vp, vp, i32, vp, i32, i32, f32, vp, vp,
                                                      i32, vp, sz, vp]
         L.paged_attention_decode_grouped_workspace_size.argtypes = [vp, i32, i32, ctypes.POINTER(sz)]
+        L.kv_stream_read.argtypes = [vp, sz, i32, vp, i32, vp, vp]
         L.kv_status_string.argtypes = [ctypes.c_int]
         L.kv_status_string.restype = ctypes.c_char_p
         # host block manager (block_manager.h)
@@ -92,7 +93,8 @@ def lib() -> ctypes.CDLL:
                    "kv_pool_set_head_scales",
                    "reshape_and_cache", "paged_attention_decode", "paged_attention_workspace_size", "copy_blocks",
                    "swap_blocks", "paged_attention_prefill", "paged_attention_prefill_workspace_size",
-                   "paged_attention_decode_grouped", "paged_attention_decode_grouped_workspace_size"):
+                   "paged_attention_decode_grouped", "paged_attention_decode_grouped_workspace_size",
+                   "kv_stream_read"):
             getattr(L, fn).restype = ctypes.c_int
         _lib_handle = L
     return _lib_handle
@@ -381,6 +383,23 @@ def paged_attention_decode_grouped(pool: KVPool, q: torch.Tensor, block_tables: 
                                                 workspace.numel() * workspace.element_size(), _stream(d, stream)),
            "paged_attention_decode_grouped")
     return out
+
+
+def kv_stream_read(buf: torch.Tensor, tile_bytes: int, tiles: torch.Tensor, sink: torch.Tensor, stream=None) -> None:
+    """Measurement primitive: read the tiles of buf (tile_bytes each) listed
+    in tiles (int32, device) with the decode kernel's load form; sink is a
+    device int32/uint32 tensor of at least one element."""
+    if not buf.is_cuda or not buf.is_contiguous():
+        raise ValueError("buf must be a contiguous device tensor")
+    if tiles.dtype != torch.int32 or tiles.dim() != 1:
+        raise ValueError("tiles must be int32 [num_tiles]")
+    if sink.numel() < 1 or sink.element_size() != 4:
+        raise ValueError("sink must hold at least one 32-bit element")
+    d = buf.device
+    with torch.cuda.device(d):   # the call runs on the current device
+        _check(lib().kv_stream_read(_dev_ptr(buf, "buf", d), buf.numel() * buf.element_size(), int(tile_bytes),
+                                    _dev_ptr(tiles, "tiles", d), tiles.numel(), _dev_ptr(sink, "sink", d),
+                                    _stream(d, stream)), "kv_stream_read")
 
 
 def paged_attention_decode(pool: KVPool, q: torch.Tensor, block_tables: torch.Tensor, context_lens: torch.Tensor,

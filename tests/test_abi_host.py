@@ -35,9 +35,9 @@ def _declared_functions(path=None):
 def test_header_declares_the_four_calls_and_helpers():
     names = _declared_functions(HEADER)
     for n in ["kv_pool_create", "reshape_and_cache", "paged_attention_decode", "copy_blocks", "swap_blocks",
-              "paged_attention_prefill"]:
+              "paged_attention_prefill", "kv_stream_read"]:
         assert n in names
-    assert len(names) == 16, names
+    assert len(names) == 17, names
 
 
 def test_block_manager_header_declares_its_calls():
@@ -79,6 +79,14 @@ def test_null_and_shape_arguments_rejected_on_host():
     n = ctypes.c_size_t()
     assert L.paged_attention_workspace_size(None, 4, 4, 4, 0, ctypes.byref(n)) == pk.KV_ERR_INVALID_ARG
     assert L.kv_pool_destroy(None) == pk.KV_OK
+    sink = ctypes.c_uint32()
+    assert L.kv_stream_read(None, 1 << 20, 4096, None, 4, None, None) == pk.KV_ERR_INVALID_ARG
+    buf = ctypes.create_string_buffer(1 << 13)   # host memory: rejected before any device call
+    addr = (ctypes.addressof(buf) + 15) & ~15
+    assert L.kv_stream_read(addr, 4096, 1000, addr, 4, ctypes.byref(sink), None) == pk.KV_ERR_INVALID_ARG
+    assert L.kv_stream_read(addr, 4096, 8192, addr, 4, ctypes.byref(sink), None) == pk.KV_ERR_INVALID_ARG
+    assert L.kv_stream_read(addr, 4096, 4096, addr, -1, ctypes.byref(sink), None) == pk.KV_ERR_INVALID_ARG
+    assert L.kv_stream_read(addr, 4096, 4096, addr, 0, ctypes.byref(sink), None) == pk.KV_OK
 
 
 # ---------------------------------------------------------------- host manager
