@@ -160,9 +160,10 @@ def grouped_bytes(wl: W.Workload, sess) -> dict:
     return {"kv": kv, "total": kv + qo + tables, "tokens": unique_tokens}
 
 
-def cpu_baseline(wl: W.Workload, target_s: float = 12.0) -> dict:
+def cpu_baseline(wl: W.Workload, target_s: float = 12.0):
     """The fp64 oracle on one host core over the first sequences of the
-    workload, sized to about target_s seconds of CPU work."""
+    workload, sized to about target_s seconds of CPU work.  Returns the
+    result, the oracle run and the sampled sequences."""
     from oracle.run import OracleRun
 
     n = wl.context_lens.astype(np.int64)
@@ -187,7 +188,37 @@ def cpu_baseline(wl: W.Workload, target_s: float = 12.0) -> dict:
     toks = int(n[seqs].sum())
     return {"value": round(toks * per_tok / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
             "sample": f"sequences 0..{k - 1} of {wl.num_seqs} ({toks} of {int(n.sum())} cached tokens), "
-                      f"{dt:.1f} s single-threaded fp64"}
+                      f"{dt:.1f} s single-threaded fp64"}, run, seqs
+
+
+def host_threads(limit: int = 16) -> int:
+    """Host cores this process may use, at most `limit`."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(n, limit))
+
+
+def cpu_baseline_parallel(wl: W.Workload, run, seqs, threads: int) -> dict:
+    """The same oracle on the same sample, its sequences dealt (longest first)
+    to `threads` host threads; each thread's call runs the unchanged oracle on
+    its own sequences."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    n = wl.context_lens.astype(np.int64)
+    per_tok = 2 * wl.num_kv_heads * wl.head_dim * W.ELEM_BYTES[wl.kv_dtype]
+    order = sorted(seqs, key=lambda s: -int(n[s]))
+    parts = [order[i::threads] for i in range(threads)]
+    parts = [p for p in parts if p]
+    t = time.perf_counter()
+    with ThreadPoolExecutor(len(parts)) as ex:
+        list(ex.map(run.decode, parts))
+    dt = time.perf_counter() - t
+    toks = int(n[seqs].sum())
+    return {"value": round(toks * per_tok / dt / 1e9, 4), "unit": "GB/s", "cores": len(parts), "kind": "oracle",
+            "sample": f"the single-core sample ({len(seqs)} sequences, {toks} cached tokens), sequences dealt to "
+                      f"{len(parts)} threads, {dt:.2f} s fp64"}
 
 
 _CSRC = "paged_kv_cache_449_amd/csrc/"
@@ -543,6 +574,8 @@ def main(argv=None) -> int:
                      "kernel": ("paged_decode_shared_kernel + paged_decode_suffix_kernel" if args.grouped
                                 else "paged_decode_kernel"),
                      "kernel_us": round(float(dec_ms.mean()) * 1e3, 2),
+                     "kernel_us_p10_median_p90": [round(float(x) * 1e3, 1)
+                                                  for x in np.percentile(dec_ms, [10, 50, 90])],
                      "bytes_per_launch": nb["total"],
                      "logical_gbs": round(logical_total / dec_mean_s / 1e9, 1)},
     }
@@ -552,7 +585,8 @@ def main(argv=None) -> int:
     res["roofline"]["frac_of_achievable"] = round(achieved / res["achievable"]["value"], 4)
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
-        res["cpu_baseline"] = cpu_baseline(wl)
+        res["cpu_baseline"], run, seqs = cpu_baseline(wl)
+        res["cpu_baseline_parallel"] = cpu_baseline_parallel(wl, run, seqs, host_threads())
     print(json.dumps(res), flush=True)
     return 0
 
