@@ -1,0 +1,169 @@
+"""The device path driven from plain C, with no Python and no torch in the
+process: a C11 program creates a library-owned pool (kv_pool_create), writes
+every token of four sequences with reshape_and_cache, copies one block with
+copy_blocks and runs paged_attention_decode, with buffers from the HIP runtime
+API.  The same program runs the CPU oracle's C functions on host copies of the
+same inputs and checks both pools byte for byte and the output within the
+fp32 tolerance.  Shapes: the tiny workload's (4 MHA heads of 64, fp32, block
+size 16, a 32-block pool, context lengths 1, 15, 16 and 33) with seeded
+values and a seeded placement."""
+import os
+import subprocess
+import tempfile
+
+import pytest
+
+from conftest import ROOT
+
+pytestmark = pytest.mark.gpu
+
+C_PROGRAM = r"""
+#include <math.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+#include <hip/hip_runtime_api.h>
+#include "pagedkv.h"
+
+/* the CPU oracle (oracle/oracle.c), type codes 0 = fp32 */
+int oracle_reshape_and_cache(void* kpool, void* vpool, int pool_dtype, int64_t num_blocks, int B, int H, int D,
+                             float k_scale, float v_scale, const void* k, const void* v, int src_dtype,
+                             const int64_t* slots, int64_t T, const float* k_head, const float* v_head);
+int oracle_copy_blocks(void* kpool, void* vpool, int64_t block_bytes, int64_t num_blocks, const int32_t* pairs,
+                       int64_t P);
+int oracle_decode(const void* kpool, const void* vpool, int kv_dtype, int64_t num_blocks, int B, int H, int D,
+                  double k_scale, double v_scale, const void* q, int q_dtype, int S, int Hq,
+                  const int32_t* block_tables, int max_blocks, const int32_t* context_lens, double scale,
+                  const int32_t* seqs, int n_seqs, double* out, const float* k_head, const float* v_head);
+
+enum { NB = 32, B = 16, H = 4, D = 64, S = 4, MAXB = 3 };
+
+static uint64_t rng_state = 449;
+static uint64_t next_u64(void) {   /* splitmix64 */
+  uint64_t z = (rng_state += 0x9E3779B97F4A7C15ull);
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
+}
+static float next_value(void) {    /* uniform in [-2, 2) */
+  return (float)((double)(next_u64() >> 11) * (4.0 / 9007199254740992.0) - 2.0);
+}
+
+#define HIP_OK(x) do { if ((x) != hipSuccess) { printf("hip error at line %d\n", __LINE__); return 90; } } while (0)
+#define KV_OK_(x) do { kv_status_t st_ = (x); if (st_ != KV_OK) { printf("status %d at line %d: %s\n", (int)st_, __LINE__, kv_status_string(st_)); return 91; } } while (0)
+
+int main(void) {
+  const int32_t lens[S] = {1, 15, 16, 33};
+  int32_t perm[NB], tables[S * MAXB];
+  for (int i = 0; i < NB; ++i) perm[i] = i;
+  for (int i = NB - 1; i > 0; --i) {   /* seeded placement */
+    int j = (int)(next_u64() % (uint64_t)(i + 1));
+    int t = perm[i]; perm[i] = perm[j]; perm[j] = t;
+  }
+  int used = 0;
+  for (int s = 0; s < S; ++s)
+    for (int b = 0; b < MAXB; ++b) tables[s * MAXB + b] = b * B < lens[s] ? perm[used++] : -1;
+  int64_t T = 0;
+  for (int s = 0; s < S; ++s) T += lens[s];
+  int64_t* slots = malloc(sizeof(int64_t) * T);
+  int64_t ti = 0;
+  for (int s = 0; s < S; ++s)
+    for (int t = 0; t < lens[s]; ++t) slots[ti++] = (int64_t)tables[s * MAXB + t / B] * B + t % B;
+  float* kn = malloc(sizeof(float) * T * H * D);
+  float* vn = malloc(sizeof(float) * T * H * D);
+  float* q = malloc(sizeof(float) * S * H * D);
+  for (int64_t i = 0; i < T * H * D; ++i) { kn[i] = next_value(); vn[i] = next_value(); }
+  for (int i = 0; i < S * H * D; ++i) q[i] = next_value();
+  const int32_t pair[2] = {tables[3 * MAXB + 0], perm[used]};   /* copy a full block to a free one */
+  const float scale = 0.125f;
+
+  /* device path */
+  kv_pool_t* pool = NULL;
+  KV_OK_(kv_pool_create(NB, B, H, D, KV_F32, &pool));
+  void *dk = NULL, *dvp = NULL;
+  size_t pool_bytes = 0;
+  int64_t strides[4];
+  KV_OK_(kv_pool_info(pool, &dk, &dvp, &pool_bytes, strides));
+  if (pool_bytes != (size_t)NB * H * B * D * 4 || strides[0] != (int64_t)H * B * D || strides[3] != 1) return 2;
+  HIP_OK(hipMemset(dk, 0xFF, pool_bytes));   /* every unwritten slot holds NaN */
+  HIP_OK(hipMemset(dvp, 0xFF, pool_bytes));
+  void *d_kn, *d_vn, *d_slots, *d_q, *d_out, *d_tab, *d_lens, *d_pair, *d_ws;
+  size_t ws_bytes = 0;
+  KV_OK_(paged_attention_workspace_size(pool, S, H, MAXB, 0, &ws_bytes));
+  HIP_OK(hipMalloc(&d_kn, sizeof(float) * T * H * D));
+  HIP_OK(hipMalloc(&d_vn, sizeof(float) * T * H * D));
+  HIP_OK(hipMalloc(&d_slots, sizeof(int64_t) * T));
+  HIP_OK(hipMalloc(&d_q, sizeof(float) * S * H * D));
+  HIP_OK(hipMalloc(&d_out, sizeof(float) * S * H * D));
+  HIP_OK(hipMalloc(&d_tab, sizeof(tables)));
+  HIP_OK(hipMalloc(&d_lens, sizeof(lens)));
+  HIP_OK(hipMalloc(&d_pair, sizeof(pair)));
+  HIP_OK(hipMalloc(&d_ws, ws_bytes));
+  HIP_OK(hipMemset(d_ws, 0, ws_bytes));
+  HIP_OK(hipMemcpy(d_kn, kn, sizeof(float) * T * H * D, hipMemcpyHostToDevice));
+  HIP_OK(hipMemcpy(d_vn, vn, sizeof(float) * T * H * D, hipMemcpyHostToDevice));
+  HIP_OK(hipMemcpy(d_slots, slots, sizeof(int64_t) * T, hipMemcpyHostToDevice));
+  HIP_OK(hipMemcpy(d_q, q, sizeof(float) * S * H * D, hipMemcpyHostToDevice));
+  HIP_OK(hipMemcpy(d_tab, tables, sizeof(tables), hipMemcpyHostToDevice));
+  HIP_OK(hipMemcpy(d_lens, lens, sizeof(lens), hipMemcpyHostToDevice));
+  HIP_OK(hipMemcpy(d_pair, pair, sizeof(pair), hipMemcpyHostToDevice));
+  KV_OK_(reshape_and_cache(pool, d_kn, d_vn, KV_F32, (const int64_t*)d_slots, (int32_t)T, NULL));
+  KV_OK_(copy_blocks(pool, (const int32_t*)d_pair, 1, NULL));
+  KV_OK_(paged_attention_decode(pool, d_q, KV_F32, d_out, (const int32_t*)d_tab, MAXB, (const int32_t*)d_lens, S, H,
+                                scale, 0, d_ws, ws_bytes, NULL));
+  HIP_OK(hipDeviceSynchronize());
+  unsigned char* gk = malloc(pool_bytes);
+  unsigned char* gv = malloc(pool_bytes);
+  float* gout = malloc(sizeof(float) * S * H * D);
+  HIP_OK(hipMemcpy(gk, dk, pool_bytes, hipMemcpyDeviceToHost));
+  HIP_OK(hipMemcpy(gv, dvp, pool_bytes, hipMemcpyDeviceToHost));
+  HIP_OK(hipMemcpy(gout, d_out, sizeof(float) * S * H * D, hipMemcpyDeviceToHost));
+
+  /* the oracle on host copies of the same inputs */
+  unsigned char* hk = malloc(pool_bytes);
+  unsigned char* hv = malloc(pool_bytes);
+  memset(hk, 0xFF, pool_bytes);
+  memset(hv, 0xFF, pool_bytes);
+  if (oracle_reshape_and_cache(hk, hv, 0, NB, B, H, D, 1.0f, 1.0f, kn, vn, 0, slots, T, NULL, NULL)) return 3;
+  if (oracle_copy_blocks(hk, hv, (int64_t)H * B * D * 4, NB, pair, 1)) return 4;
+  double* ref = malloc(sizeof(double) * S * H * D);
+  if (oracle_decode(hk, hv, 0, NB, B, H, D, 1.0, 1.0, q, 0, S, H, tables, MAXB, lens, scale, NULL, 0, ref, NULL,
+                    NULL))
+    return 5;
+  if (memcmp(gk, hk, pool_bytes) || memcmp(gv, hv, pool_bytes)) { printf("pool bytes differ\n"); return 6; }
+  double worst = 0.0;
+  for (int i = 0; i < S * H * D; ++i) {
+    const double err = fabs((double)gout[i] - ref[i]);
+    const double bound = 2e-3 + 1e-2 * fabs(ref[i]);
+    if (!(err <= bound)) { printf("out[%d] = %.9g, oracle %.9g\n", i, gout[i], ref[i]); return 7; }
+    if (err / bound > worst) worst = err / bound;
+  }
+  /* a lone token (length 1) attends to itself only: its output is its value row exactly */
+  for (int h = 0; h < H; ++h)
+    for (int j = 0; j < D; ++j)
+      if (gout[h * D + j] != vn[(0 * H + h) * D + j]) { printf("length-1 row differs\n"); return 8; }
+  KV_OK_(kv_pool_destroy(pool));
+  printf("ok %lld tokens, worst error / tolerance %.3f\n", (long long)T, worst);
+  return 0;
+}
+"""
+
+
+def test_device_path_from_c_matches_the_oracle():
+    import oracle
+    import paged_kv_cache_449_amd as pk
+    from gpu_harness import announce
+    announce("C program: pool, cache write, copy, decode vs oracle")
+    lib_dir = os.path.dirname(pk.LIB_PATH)
+    oracle_dir = os.path.dirname(oracle.build())
+    with tempfile.TemporaryDirectory() as tmp:
+        src = os.path.join(tmp, "device_abi.c")
+        exe = os.path.join(tmp, "device_abi")
+        open(src, "w").write(C_PROGRAM)
+        subprocess.check_call(["gcc", "-std=c11", "-O1", "-Wall", "-Werror", "-D__HIP_PLATFORM_AMD__",
+                               "-I", os.path.join(ROOT, "include"), "-I", "/opt/rocm/include", src, "-o", exe,
+                               "-L", lib_dir, "-lpagedkv", "-L", oracle_dir, "-loracle", "-L", "/opt/rocm/lib",
+                               "-lamdhip64", "-lm", f"-Wl,-rpath,{lib_dir}:{oracle_dir}:/opt/rocm/lib"])
+        out = subprocess.run([exe], capture_output=True, text=True, timeout=120)
+        assert out.returncode == 0, (out.returncode, out.stdout, out.stderr)
+        assert out.stdout.startswith("ok 65 tokens"), out.stdout

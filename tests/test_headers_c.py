@@ -22,7 +22,7 @@ int main(void) {
                  (fn_t)paged_attention_decode, (fn_t)paged_attention_workspace_size,
                  (fn_t)paged_attention_decode_grouped, (fn_t)paged_attention_decode_grouped_workspace_size,
                  (fn_t)paged_attention_prefill, (fn_t)paged_attention_prefill_workspace_size, (fn_t)copy_blocks,
-                 (fn_t)swap_blocks, (fn_t)kv_status_string, (fn_t)bm_create, (fn_t)bm_destroy,
+                 (fn_t)swap_blocks, (fn_t)kv_stream_read, (fn_t)kv_status_string, (fn_t)bm_create, (fn_t)bm_destroy,
                  (fn_t)bm_add_sequence, (fn_t)bm_fork, (fn_t)bm_append_slots, (fn_t)bm_append_batch,
                  (fn_t)bm_free, (fn_t)bm_num_free_blocks, (fn_t)bm_sequence_info, (fn_t)bm_block_table,
                  (fn_t)bm_block_tables, (fn_t)bm_ref_count, (fn_t)bm_stats};
@@ -60,5 +60,5 @@ def test_headers_compile_as_c_and_drive_the_manager():
         out = subprocess.run([exe], capture_output=True, text=True)
         assert out.returncode == 0, (out.returncode, out.stderr)
         n, free_blocks, msg = out.stdout.split(" ", 2)
-        assert int(n) == 29 and msg.strip().startswith("no free")
+        assert int(n) == 30 and msg.strip().startswith("no free")
         assert int(free_blocks) == 8 - 4
