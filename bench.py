@@ -104,10 +104,11 @@ def prefill_cost(wl: W.Workload) -> dict:
     return {"flops": flops, "kv": kv, "total": kv + qo + tables, "tokens": int(n.sum()), "row_token_pairs": pairs}
 
 
-def cpu_baseline_prefill(wl: W.Workload, target_s: float = 12.0) -> dict:
+def cpu_baseline_prefill(wl: W.Workload, target_s: float = 12.0):
     """The fp64 oracle on one host core over the first sequences of a
     multi-token workload, sized to about target_s seconds, in the unit of the
-    workload's roofline bound."""
+    workload's roofline bound; then the same sample on the host's cores.
+    Returns (one core, all cores)."""
     from oracle.run import OracleRun
 
     n = wl.context_lens.astype(np.int64)
@@ -426,7 +427,8 @@ def main(argv=None) -> int:
     ap.add_argument("--flush", choices=["none", "read", "write"], default="none",
                     help="before every step, outside its events, read (read) or write (write) a 512 MiB buffer: "
                          "read evicts the Infinity Cache and L2 of the KV data, write also leaves dirty lines that "
-                         "drain during the next kernels; ms_per_step then sums the steps' own event intervals")
+                         "drain during the next kernels; ms_per_step is then the mean of the steps' own event "
+                         "intervals")
     ap.add_argument("--graph", action="store_true",
                     help="capture one step (its copy_blocks, cache write and decode launches) in a HIP graph and "
                          "time replays of it for ms_per_step; the kernel time still comes from eager steps")
