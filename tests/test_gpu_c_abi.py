@@ -4,9 +4,13 @@ every token of four sequences with reshape_and_cache, copies one block with
 copy_blocks and runs paged_attention_decode, with buffers from the HIP runtime
 API.  The same program runs the CPU oracle's C functions on host copies of the
 same inputs and checks both pools byte for byte and the output within the
-fp32 tolerance.  Shapes: the tiny workload's (4 MHA heads of 64, fp32, block
-size 16, a 32-block pool, context lengths 1, 15, 16 and 33) with seeded
-values and a seeded placement."""
+tolerance of the pool dtype.  Two cases, block size 16, a 32-block pool,
+context lengths 1, 15, 16 and 33, seeded values and placement:
+  f32     the tiny workload's shape: 4 MHA heads of 64, fp32 pool and queries,
+          library-sized split; a length-1 row must equal its value row exactly;
+  fp8gqa  2 kv heads of 128 serving 8 query heads, an fp8 E4M3FN pool written
+          from bf16 with per-tensor scales, bf16 queries, 16-token partitions
+          (matrix-core runs and split-run merges)."""
 import os
 import subprocess
 import tempfile
@@ -36,7 +40,7 @@ int oracle_decode(const void* kpool, const void* vpool, int kv_dtype, int64_t nu
                   const int32_t* block_tables, int max_blocks, const int32_t* context_lens, double scale,
                   const int32_t* seqs, int n_seqs, double* out, const float* k_head, const float* v_head);
 
-enum { NB = 32, B = 16, H = 4, D = 64, S = 4, MAXB = 3 };
+enum { NB = 32, B = 16, S = 4, MAXB = 3, DMAX = 128 };
 
 static uint64_t rng_state = 449;
 static uint64_t next_u64(void) {   /* splitmix64 */
@@ -48,11 +52,30 @@ static uint64_t next_u64(void) {   /* splitmix64 */
 static float next_value(void) {    /* uniform in [-2, 2) */
   return (float)((double)(next_u64() >> 11) * (4.0 / 9007199254740992.0) - 2.0);
 }
+static uint16_t to_bf16(float f) {  /* round to nearest even (finite inputs) */
+  uint32_t u;
+  memcpy(&u, &f, 4);
+  return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+}
+static float from_bf16(uint16_t b) {
+  uint32_t u = (uint32_t)b << 16;
+  float f;
+  memcpy(&f, &u, 4);
+  return f;
+}
 
 #define HIP_OK(x) do { if ((x) != hipSuccess) { printf("hip error at line %d\n", __LINE__); return 90; } } while (0)
 #define KV_OK_(x) do { kv_status_t st_ = (x); if (st_ != KV_OK) { printf("status %d at line %d: %s\n", (int)st_, __LINE__, kv_status_string(st_)); return 91; } } while (0)
 
-int main(void) {
+int main(int argc, char** argv) {
+  /* "f32": MHA, 4 heads of 64, fp32 pool and queries, library-sized split.
+     "fp8gqa": 2 kv heads of 128 serving 8 query heads, fp8 E4M3FN pool written
+     from bf16 with per-tensor scales, bf16 queries, 16-token partitions. */
+  const int fp8 = argc > 1 && strcmp(argv[1], "fp8gqa") == 0;
+  const int H = fp8 ? 2 : 4, Hq = fp8 ? 8 : 4, D = fp8 ? 128 : 64;
+  const int src_dt = fp8 ? 2 : 0, pool_dt = fp8 ? 3 : 0, esz = fp8 ? 1 : 4, qsz = fp8 ? 2 : 4;
+  const int partition = fp8 ? 16 : 0;
+  const float k_scale = fp8 ? 0.0078125f : 1.0f, v_scale = fp8 ? 0.00390625f : 1.0f;   /* powers of two */
   const int32_t lens[S] = {1, 15, 16, 33};
   int32_t perm[NB], tables[S * MAXB];
   for (int i = 0; i < NB; ++i) perm[i] = i;
@@ -69,81 +92,99 @@ int main(void) {
   int64_t ti = 0;
   for (int s = 0; s < S; ++s)
     for (int t = 0; t < lens[s]; ++t) slots[ti++] = (int64_t)tables[s * MAXB + t / B] * B + t % B;
-  float* kn = malloc(sizeof(float) * T * H * D);
-  float* vn = malloc(sizeof(float) * T * H * D);
-  float* q = malloc(sizeof(float) * S * H * D);
-  for (int64_t i = 0; i < T * H * D; ++i) { kn[i] = next_value(); vn[i] = next_value(); }
-  for (int i = 0; i < S * H * D; ++i) q[i] = next_value();
+  /* new K/V in the source dtype (fp32, or bf16 bits), q in the query dtype */
+  void* kn = malloc((size_t)T * H * D * 4);
+  void* vn = malloc((size_t)T * H * D * 4);
+  void* q = malloc((size_t)S * Hq * D * 4);
+  for (int64_t i = 0; i < T * H * D; ++i) {
+    const float a = next_value(), b = next_value();
+    if (fp8) { ((uint16_t*)kn)[i] = to_bf16(a); ((uint16_t*)vn)[i] = to_bf16(b); }
+    else { ((float*)kn)[i] = a; ((float*)vn)[i] = b; }
+  }
+  for (int i = 0; i < S * Hq * D; ++i) {
+    const float a = next_value();
+    if (fp8) ((uint16_t*)q)[i] = to_bf16(a); else ((float*)q)[i] = a;
+  }
   const int32_t pair[2] = {tables[3 * MAXB + 0], perm[used]};   /* copy a full block to a free one */
-  const float scale = 0.125f;
+  const float scale = fp8 ? 0.08838834764831845f : 0.125f;
 
   /* device path */
   kv_pool_t* pool = NULL;
-  KV_OK_(kv_pool_create(NB, B, H, D, KV_F32, &pool));
+  KV_OK_(kv_pool_create(NB, B, H, D, fp8 ? KV_FP8_E4M3FN : KV_F32, &pool));
+  if (fp8) KV_OK_(kv_pool_set_scales(pool, k_scale, v_scale));
   void *dk = NULL, *dvp = NULL;
   size_t pool_bytes = 0;
   int64_t strides[4];
   KV_OK_(kv_pool_info(pool, &dk, &dvp, &pool_bytes, strides));
-  if (pool_bytes != (size_t)NB * H * B * D * 4 || strides[0] != (int64_t)H * B * D || strides[3] != 1) return 2;
+  if (pool_bytes != (size_t)NB * H * B * D * esz || strides[0] != (int64_t)H * B * D || strides[3] != 1) return 2;
   HIP_OK(hipMemset(dk, 0xFF, pool_bytes));   /* every unwritten slot holds NaN */
   HIP_OK(hipMemset(dvp, 0xFF, pool_bytes));
   void *d_kn, *d_vn, *d_slots, *d_q, *d_out, *d_tab, *d_lens, *d_pair, *d_ws;
   size_t ws_bytes = 0;
-  KV_OK_(paged_attention_workspace_size(pool, S, H, MAXB, 0, &ws_bytes));
-  HIP_OK(hipMalloc(&d_kn, sizeof(float) * T * H * D));
-  HIP_OK(hipMalloc(&d_vn, sizeof(float) * T * H * D));
+  KV_OK_(paged_attention_workspace_size(pool, S, Hq, MAXB, partition, &ws_bytes));
+  const size_t kv_new_bytes = (size_t)T * H * D * (fp8 ? 2 : 4), q_bytes = (size_t)S * Hq * D * qsz;
+  HIP_OK(hipMalloc(&d_kn, kv_new_bytes));
+  HIP_OK(hipMalloc(&d_vn, kv_new_bytes));
   HIP_OK(hipMalloc(&d_slots, sizeof(int64_t) * T));
-  HIP_OK(hipMalloc(&d_q, sizeof(float) * S * H * D));
-  HIP_OK(hipMalloc(&d_out, sizeof(float) * S * H * D));
+  HIP_OK(hipMalloc(&d_q, q_bytes));
+  HIP_OK(hipMalloc(&d_out, q_bytes));
   HIP_OK(hipMalloc(&d_tab, sizeof(tables)));
   HIP_OK(hipMalloc(&d_lens, sizeof(lens)));
   HIP_OK(hipMalloc(&d_pair, sizeof(pair)));
   HIP_OK(hipMalloc(&d_ws, ws_bytes));
   HIP_OK(hipMemset(d_ws, 0, ws_bytes));
-  HIP_OK(hipMemcpy(d_kn, kn, sizeof(float) * T * H * D, hipMemcpyHostToDevice));
-  HIP_OK(hipMemcpy(d_vn, vn, sizeof(float) * T * H * D, hipMemcpyHostToDevice));
+  HIP_OK(hipMemcpy(d_kn, kn, kv_new_bytes, hipMemcpyHostToDevice));
+  HIP_OK(hipMemcpy(d_vn, vn, kv_new_bytes, hipMemcpyHostToDevice));
   HIP_OK(hipMemcpy(d_slots, slots, sizeof(int64_t) * T, hipMemcpyHostToDevice));
-  HIP_OK(hipMemcpy(d_q, q, sizeof(float) * S * H * D, hipMemcpyHostToDevice));
+  HIP_OK(hipMemcpy(d_q, q, q_bytes, hipMemcpyHostToDevice));
   HIP_OK(hipMemcpy(d_tab, tables, sizeof(tables), hipMemcpyHostToDevice));
   HIP_OK(hipMemcpy(d_lens, lens, sizeof(lens), hipMemcpyHostToDevice));
   HIP_OK(hipMemcpy(d_pair, pair, sizeof(pair), hipMemcpyHostToDevice));
-  KV_OK_(reshape_and_cache(pool, d_kn, d_vn, KV_F32, (const int64_t*)d_slots, (int32_t)T, NULL));
+  const kv_dtype_t io_dt = fp8 ? KV_BF16 : KV_F32;
+  KV_OK_(reshape_and_cache(pool, d_kn, d_vn, io_dt, (const int64_t*)d_slots, (int32_t)T, NULL));
   KV_OK_(copy_blocks(pool, (const int32_t*)d_pair, 1, NULL));
-  KV_OK_(paged_attention_decode(pool, d_q, KV_F32, d_out, (const int32_t*)d_tab, MAXB, (const int32_t*)d_lens, S, H,
-                                scale, 0, d_ws, ws_bytes, NULL));
+  KV_OK_(paged_attention_decode(pool, d_q, io_dt, d_out, (const int32_t*)d_tab, MAXB, (const int32_t*)d_lens, S, Hq,
+                                scale, partition, d_ws, ws_bytes, NULL));
   HIP_OK(hipDeviceSynchronize());
   unsigned char* gk = malloc(pool_bytes);
   unsigned char* gv = malloc(pool_bytes);
-  float* gout = malloc(sizeof(float) * S * H * D);
+  void* gout = malloc(q_bytes);
   HIP_OK(hipMemcpy(gk, dk, pool_bytes, hipMemcpyDeviceToHost));
   HIP_OK(hipMemcpy(gv, dvp, pool_bytes, hipMemcpyDeviceToHost));
-  HIP_OK(hipMemcpy(gout, d_out, sizeof(float) * S * H * D, hipMemcpyDeviceToHost));
+  HIP_OK(hipMemcpy(gout, d_out, q_bytes, hipMemcpyDeviceToHost));
 
   /* the oracle on host copies of the same inputs */
   unsigned char* hk = malloc(pool_bytes);
   unsigned char* hv = malloc(pool_bytes);
   memset(hk, 0xFF, pool_bytes);
   memset(hv, 0xFF, pool_bytes);
-  if (oracle_reshape_and_cache(hk, hv, 0, NB, B, H, D, 1.0f, 1.0f, kn, vn, 0, slots, T, NULL, NULL)) return 3;
-  if (oracle_copy_blocks(hk, hv, (int64_t)H * B * D * 4, NB, pair, 1)) return 4;
-  double* ref = malloc(sizeof(double) * S * H * D);
-  if (oracle_decode(hk, hv, 0, NB, B, H, D, 1.0, 1.0, q, 0, S, H, tables, MAXB, lens, scale, NULL, 0, ref, NULL,
-                    NULL))
+  if (oracle_reshape_and_cache(hk, hv, pool_dt, NB, B, H, D, k_scale, v_scale, kn, vn, src_dt, slots, T, NULL,
+                               NULL))
+    return 3;
+  if (oracle_copy_blocks(hk, hv, (int64_t)H * B * D * esz, NB, pair, 1)) return 4;
+  double* ref = malloc(sizeof(double) * S * Hq * D);
+  if (oracle_decode(hk, hv, pool_dt, NB, B, H, D, k_scale, v_scale, q, fp8 ? 2 : 0, S, Hq, tables, MAXB, lens,
+                    scale, NULL, 0, ref, NULL, NULL))
     return 5;
   if (memcmp(gk, hk, pool_bytes) || memcmp(gv, hv, pool_bytes)) { printf("pool bytes differ\n"); return 6; }
   double worst = 0.0;
-  for (int i = 0; i < S * H * D; ++i) {
-    const double err = fabs((double)gout[i] - ref[i]);
-    const double bound = 2e-3 + 1e-2 * fabs(ref[i]);
-    if (!(err <= bound)) { printf("out[%d] = %.9g, oracle %.9g\n", i, gout[i], ref[i]); return 7; }
+  const double rtol = fp8 ? 5e-2 : 1e-2;
+  for (int i = 0; i < S * Hq * D; ++i) {
+    const double got = fp8 ? (double)from_bf16(((uint16_t*)gout)[i]) : (double)((float*)gout)[i];
+    const double err = fabs(got - ref[i]);
+    const double bound = 2e-3 + rtol * fabs(ref[i]);
+    if (!(err <= bound)) { printf("out[%d] = %.9g, oracle %.9g\n", i, got, ref[i]); return 7; }
     if (err / bound > worst) worst = err / bound;
   }
-  /* a lone token (length 1) attends to itself only: its output is its value row exactly */
-  for (int h = 0; h < H; ++h)
-    for (int j = 0; j < D; ++j)
-      if (gout[h * D + j] != vn[(0 * H + h) * D + j]) { printf("length-1 row differs\n"); return 8; }
+  if (!fp8) {
+    /* a lone token (length 1) attends to itself only: its output is its value row exactly */
+    for (int h = 0; h < H; ++h)
+      for (int j = 0; j < D; ++j)
+        if (((float*)gout)[h * D + j] != ((float*)vn)[(0 * H + h) * D + j]) { printf("length-1 row differs\n"); return 8; }
+  }
   KV_OK_(kv_pool_destroy(pool));
   printf("ok %lld tokens, worst error / tolerance %.3f\n", (long long)T, worst);
+  (void)DMAX;
   return 0;
 }
 """
@@ -164,6 +205,7 @@ def test_device_path_from_c_matches_the_oracle():
                                "-I", os.path.join(ROOT, "include"), "-I", "/opt/rocm/include", src, "-o", exe,
                                "-L", lib_dir, "-lpagedkv", "-L", oracle_dir, "-loracle", "-L", "/opt/rocm/lib",
                                "-lamdhip64", "-lm", f"-Wl,-rpath,{lib_dir}:{oracle_dir}:/opt/rocm/lib"])
-        out = subprocess.run([exe], capture_output=True, text=True, timeout=120)
-        assert out.returncode == 0, (out.returncode, out.stdout, out.stderr)
-        assert out.stdout.startswith("ok 65 tokens"), out.stdout
+        for mode in ("f32", "fp8gqa"):
+            out = subprocess.run([exe, mode], capture_output=True, text=True, timeout=120)
+            assert out.returncode == 0, (mode, out.returncode, out.stdout, out.stderr)
+            assert out.stdout.startswith("ok 65 tokens"), (mode, out.stdout)
