@@ -203,3 +203,23 @@ def test_workspace_reuse_with_smaller_batch(pk, gpu):
                                           partition_tokens=16).cpu().double().numpy()
         check_close(o_all, ref, wl.kv_dtype)
         check_close(o_sub, ref[sub], wl.kv_dtype)
+
+
+def test_partition_lengthened_past_counter_slots(pk, gpu):
+    """A caller-sized split that would need more runs than there are arrival
+    counters (64 sequences x 32 kv heads x 63 table entries at one block per
+    run: 129,024) has its runs lengthened to two blocks; the result still
+    matches the oracle on sampled sequences."""
+    lens = [1000 - 7 * (i % 5) for i in range(64)]
+    wl = W.custom("many_runs_bf16", 32, 32, 128, "bf16", "bf16", 16, lens, index=95)
+    mb = wl.max_blocks_per_seq
+    assert 64 * 32 * mb > 65528
+    pool = pk.KVPool(8, 16, 32, 128, torch.bfloat16, _dev())
+    one_block = pk.paged_attention_workspace_size(pool, 64, 32, mb, 16)
+    two_blocks = pk.paged_attention_workspace_size(pool, 64, 32, mb, 32)
+    assert one_block == two_blocks   # the same plan: runs of two blocks
+    got = gpu(wl, partition_tokens=16)
+    assert np.isfinite(got["out"]).all()
+    seqs = [0, 17, 40, 63]
+    ref = OracleRun(wl, prompts=sorted({wl.parent[s] for s in seqs}))
+    check_close(got["out"][seqs], ref.decode(seqs)[seqs], wl.kv_dtype)
