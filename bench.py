@@ -299,6 +299,25 @@ def achievable_read(dev, gib: int = 2, tile_bytes: int = 4096, reps: int = 5) ->
             "tile_bytes": tile_bytes, "bytes": n * tile_bytes, "order": "random", "us": round(us, 1)}
 
 
+def write_kernels(wl: W.Workload, sess, pool, wevs) -> dict:
+    """The step's two writes from the HIP events around them: copy_blocks
+    (each pair reads and writes one block of K and one of V) and
+    reshape_and_cache (each new token's K and V rows read in the source dtype,
+    written in the pool dtype, plus its slot).  Median over the steps."""
+    P = int(sess.pairs.shape[0])
+    T = int(sess.slot_mapping.shape[0])
+    row = wl.num_kv_heads * wl.head_dim
+    res = {}
+    if P > 0:
+        us = float(np.median([w[0].elapsed_time(w[1]) for w in wevs])) * 1e3
+        nbytes = P * 2 * 2 * pool.block_bytes
+        res["copy_blocks"] = {"pairs": P, "us": round(us, 2), "bytes": nbytes, "GBs": round(nbytes / us / 1e3, 1)}
+    us = float(np.median([w[1].elapsed_time(w[2]) for w in wevs])) * 1e3
+    nbytes = T * (2 * row * (W.ELEM_BYTES[wl.src_dtype] + W.ELEM_BYTES[wl.kv_dtype]) + 8)
+    res["reshape_and_cache"] = {"tokens": T, "us": round(us, 2), "bytes": nbytes, "GBs": round(nbytes / us / 1e3, 1)}
+    return res
+
+
 def swap_measurement(pool, n: int, reps: int = 5) -> dict:
     """swap_blocks of n pool blocks (K and V) to pinned host memory and back
     into the same blocks (their contents are unchanged), HIP-event timed."""
@@ -466,9 +485,15 @@ def main(argv=None) -> int:
 
     multi = wl.multi_token
 
-    def one_step(ev=None):
+    def one_step(ev=None, wev=None):
+        if wev is not None:
+            wev[0].record()
         pk.copy_blocks(pool, sess.pairs)
+        if wev is not None:
+            wev[1].record()
         pk.reshape_and_cache(pool, kn, vn, sess.slot_mapping)
+        if wev is not None:
+            wev[2].record()
         if ev is not None:
             ev[0].record()
         if multi:
@@ -537,14 +562,17 @@ def main(argv=None) -> int:
     # 2. The kernel time: K more steps with HIP events around each launch,
     #    recorded on the stream the library launches on.
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    wevs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     torch.cuda.synchronize(dev)
     for i in range(args.steps):
         flush()
-        one_step(evs[i])
+        one_step(evs[i], wevs[i])
     torch.cuda.synchronize(dev)
     dec_ms = np.array([a.elapsed_time(b) for a, b in evs])
+    writes = write_kernels(wl, sess, pool, wevs)
     if multi:
         res = multi_token_result(wl, args, dec_ms, step_ms)
+        res["writes"] = writes
         res["achievable"] = achievable_read(dev)
         if res["roofline"]["unit"] == "GB/s":
             res["roofline"]["frac_of_achievable"] = round(res["roofline"]["achieved"] / res["achievable"]["value"], 4)
@@ -597,6 +625,7 @@ def main(argv=None) -> int:
     }
     if args.swap_blocks > 0:
         res["swap"] = swap_measurement(pool, min(args.swap_blocks, wl.num_blocks))
+    res["writes"] = writes
     res["achievable"] = achievable_read(dev)
     res["roofline"]["frac_of_achievable"] = round(achieved / res["achievable"]["value"], 4)
     if not args.no_cpu_baseline:
