@@ -6,8 +6,6 @@
 
 #include <algorithm>
 #include <cstring>
-#include <deque>
-#include <list>
 #include <new>
 #include <unordered_map>
 #include <vector>
@@ -29,6 +27,56 @@ uint64_t prefix_hash(uint64_t parent, uint64_t extra, const int32_t* tokens, int
   return h;
 }
 
+// First-in first-out queue of block ids in a ring sized once for every
+// block, so queueing a released block never allocates.
+struct BlockRing {
+  std::vector<int32_t> buf;
+  int64_t head = 0, count = 0;
+  void init(int64_t capacity) { buf.assign((size_t)capacity, 0); }
+  bool empty() const { return count == 0; }
+  int64_t size() const { return count; }
+  int32_t front() const { return buf[(size_t)head]; }
+  void pop_front() {
+    if (++head == (int64_t)buf.size()) head = 0;
+    --count;
+  }
+  void push_back(int32_t b) {
+    int64_t i = head + count;   // < 2 * capacity
+    if (i >= (int64_t)buf.size()) i -= (int64_t)buf.size();
+    buf[(size_t)i] = b;
+    ++count;
+  }
+};
+
+// Doubly linked list of block ids through per-block links, oldest first:
+// appending, unlinking and taking the oldest never allocate.
+struct BlockLru {
+  std::vector<int32_t> prev, next;
+  int32_t head = -1, tail = -1;
+  int64_t count = 0;
+  void init(int64_t n) {
+    prev.assign((size_t)n, -1);
+    next.assign((size_t)n, -1);
+  }
+  int64_t size() const { return count; }
+  int32_t front() const { return head; }
+  void push_back(int32_t b) {
+    prev[(size_t)b] = tail;
+    next[(size_t)b] = -1;
+    if (tail >= 0) next[(size_t)tail] = b; else head = b;
+    tail = b;
+    ++count;
+  }
+  void erase(int32_t b) {
+    const int32_t p = prev[(size_t)b], n = next[(size_t)b];
+    if (p >= 0) next[(size_t)p] = n; else head = n;
+    if (n >= 0) prev[(size_t)n] = p; else tail = p;
+    prev[(size_t)b] = next[(size_t)b] = -1;
+    --count;
+  }
+  void pop_front() { erase(head); }
+};
+
 struct Block {
   int32_t ref = 0;
   uint64_t last_access = 0;
@@ -37,7 +85,6 @@ struct Block {
   uint64_t extra = 0;
   uint64_t hash = 0;
   std::vector<int32_t> tokens;     // the block's tokens while registered
-  std::list<int32_t>::iterator lru_pos;
   bool in_lru = false;
 };
 
@@ -56,15 +103,15 @@ struct bm_manager {
   int32_t bs = 0;
   bool prefix = false;
   std::vector<Block> blocks;
-  std::deque<int32_t> free_list;                    // unreferenced, no cached prefix
-  std::list<int32_t> lru;                           // unreferenced cached blocks, oldest first
+  BlockRing free_list;                              // unreferenced, no cached prefix
+  BlockLru lru;                                     // unreferenced cached blocks, oldest first
   std::unordered_multimap<uint64_t, int32_t> index; // prefix hash -> registered block
   std::unordered_map<int64_t, Sequence> seqs;
   uint64_t clock = 0;
   uint64_t next_serial = 1;
   bm_stats_t st{};
 
-  int64_t available() const { return (int64_t)free_list.size() + (int64_t)lru.size(); }
+  int64_t available() const { return free_list.size() + lru.size(); }
 
   void unregister(int32_t b) {
     Block& k = blocks[b];
@@ -103,7 +150,7 @@ struct bm_manager {
     if (--k.ref > 0) return;
     if (k.serial != 0) {
       k.last_access = ++clock;
-      k.lru_pos = lru.insert(lru.end(), b);
+      lru.push_back(b);
       k.in_lru = true;
     } else {
       free_list.push_back(b);
@@ -115,7 +162,7 @@ struct bm_manager {
   void acquire(int32_t b) {
     Block& k = blocks[b];
     if (k.in_lru) {
-      lru.erase(k.lru_pos);
+      lru.erase(b);
       k.in_lru = false;
     }
     ++k.ref;
@@ -205,6 +252,7 @@ namespace {
 
 bool valid_block_size(int32_t bs) { return bs > 0 && bs <= (1 << 20); }
 
+
 }  // namespace
 
 extern "C" kv_status_t bm_create(int64_t num_blocks, int32_t block_size, const int32_t* free_order,
@@ -219,6 +267,8 @@ extern "C" kv_status_t bm_create(int64_t num_blocks, int32_t block_size, const i
     bm->bs = block_size;
     bm->prefix = prefix_caching != 0;
     bm->blocks.resize((size_t)num_blocks);
+    bm->free_list.init(num_blocks);
+    bm->lru.init(num_blocks);
     if (free_order) {
       std::vector<char> seen((size_t)num_blocks, 0);
       for (int64_t i = 0; i < num_blocks; ++i) {
@@ -375,6 +425,8 @@ extern "C" kv_status_t bm_append_batch(bm_manager_t* bm, const int64_t* seqs, co
   return KV_OK;
 }
 
+// Releasing blocks only relinks them (free ring, LRU links), so this call
+// allocates nothing and cannot fail part way.
 extern "C" kv_status_t bm_free(bm_manager_t* bm, int64_t seq) {
   if (!bm) return KV_ERR_INVALID_ARG;
   auto it = bm->seqs.find(seq);
@@ -437,8 +489,8 @@ extern "C" kv_status_t bm_stats(const bm_manager_t* bm, bm_stats_t* out) {
   if (!bm || !out) return KV_ERR_INVALID_ARG;
   bm_stats_t s = bm->st;
   s.num_blocks = bm->num_blocks;
-  s.free_blocks = (int64_t)bm->free_list.size();
-  s.cached_blocks = (int64_t)bm->lru.size();
+  s.free_blocks = bm->free_list.size();
+  s.cached_blocks = bm->lru.size();
   s.used_blocks = bm->num_blocks - s.free_blocks - s.cached_blocks;
   s.num_sequences = (int64_t)bm->seqs.size();
   s.tokens = 0;
