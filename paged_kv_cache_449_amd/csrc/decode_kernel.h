@@ -39,7 +39,13 @@
 namespace pkv {
 
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr int kLoadsPerStep = 4;  // wave loads of K (and of V) issued together
+// Wave loads of K (and of V) issued together per step of a vector-ALU run:
+// four when blocks are shared, so reads served by the L2 have a deep
+// pipeline; one when every byte streams from HBM once, which measured 1-3%
+// faster than four on MI355X (the other waves of a CU keep HBM busy, and
+// shorter steps leave less masked issue at the end of each window).
+constexpr int kLoadsPerStep = 4;
+constexpr int kStreamLoadsPerStep = 1;
 // Arrival counters of split runs, indexed by the run's first worker (a worker
 // starts at most one run that continues past its end).  The region has a
 // fixed size and sits at the start of the workspace, so calls with different
@@ -415,7 +421,7 @@ __device__ inline void valu_stream(const DecodeParams& p, int s, int h, int off,
                                    float (&acc)[G][DecodeShape<KV, D>::VEC]) {
   using Sh = DecodeShape<KV, D>;
   constexpr int VEC = Sh::VEC, L = Sh::L, TPL = Sh::TPL;
-  constexpr int U = kLoadsPerStep;
+  constexpr int U = POL == kStreamPolicy ? kStreamLoadsPerStep : kLoadsPerStep;
   const int lane = threadIdx.x & 63;
   const int row = lane / L;
   const int col = lane % L;
