@@ -386,22 +386,33 @@ __device__ inline void mfma_rows_run(const DecodeParams& p, int w, int chunk, in
     // every table entry of the window is in the pool
     const bool all_in_pool = __ballot(lane < cnt && tab < 0) == 0;
     const int unmasked_end = all_in_pool ? min(thi, row.min_limit) : tlo;
-    // Two step register sets in flight: issue the next step, compute this
-    // one.  Issues are unconditional so the compiler's wait counts stay
-    // exact (a tile past the window reads zeros and its scores are all
-    // masked).
+    // fp8 keeps two step register sets in flight (issue the next step,
+    // compute this one); 16-bit elements issue and compute one set, whose
+    // loads already carry twice the bytes.  On MI355X two sets were 10-12%
+    // faster for fp8 GQA decode and one set 2-5% faster for bf16 and f16
+    // (GQA decode, grouped decode, speculative verification).  Issues are
+    // unconditional so the compiler's wait counts stay exact (a tile past
+    // the window reads zeros and its scores are all masked).
     const int steps = (tiles + TPS - 1) / TPS;
-    MfmaStep<KV, D> a, b;
+    MfmaStep<KV, D> a;
     auto issue = [&](MfmaStep<KV, D>& r, int st) {
 #pragma unroll
       for (int q = 0; q < TPS; ++q) mfma_issue<KV, D, POL>(c, tab, tlo, thi, st * TPS + q, r.t[q]);
     };
-    issue(a, 0);
-    for (int st = 0; st < steps; st += 2) {
-      issue(b, st + 1);
-      compute(a, tab, tlo, thi, st, unmasked_end);
-      issue(a, st + 2);
-      compute(b, tab, tlo, thi, st + 1, unmasked_end);
+    if constexpr (Sh::EB == 1) {
+      MfmaStep<KV, D> b;
+      issue(a, 0);
+      for (int st = 0; st < steps; st += 2) {
+        issue(b, st + 1);
+        compute(a, tab, tlo, thi, st, unmasked_end);
+        issue(a, st + 2);
+        compute(b, tab, tlo, thi, st + 1, unmasked_end);
+      }
+    } else {
+      for (int st = 0; st < steps; ++st) {
+        issue(a, st);
+        compute(a, tab, tlo, thi, st, unmasked_end);
+      }
     }
     tab = tab_next;
   }
