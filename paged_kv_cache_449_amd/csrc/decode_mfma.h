@@ -389,7 +389,8 @@ __device__ inline void mfma_rows_run(const DecodeParams& p, int w, int chunk, in
     // fp8 keeps two step register sets in flight (issue the next step,
     // compute this one); 16-bit elements issue and compute one set, whose
     // loads already carry twice the bytes.  On MI355X two sets were 10-12%
-    // faster for fp8 GQA decode and one set 2-5% faster for bf16 and f16
+    // faster for fp8 GQA decode with the library-sized split (3% slower
+    // with 512-token partitions), and one set 2-5% faster for bf16 and f16
     // (GQA decode, grouped decode, speculative verification).  Issues are
     // unconditional so the compiler's wait counts stay exact (a tile past
     // the window reads zeros and its scores are all masked).
