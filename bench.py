@@ -154,8 +154,11 @@ def unique_bytes(wl: W.Workload, sess) -> dict:
     """HBM lower bound of one decode when sequences share blocks: every
     physical block read once, up to the furthest token any sequence uses in
     it, plus q, out, the table entries and the lengths."""
-    tables = sess.block_tables.cpu().numpy()
-    n = sess.context_lens.cpu().numpy().astype(np.int64)
+    return _unique_from_tables(wl, sess.block_tables.cpu().numpy())
+
+
+def _unique_from_tables(wl: W.Workload, tables: np.ndarray) -> dict:
+    n = wl.context_lens.astype(np.int64)
     bs = wl.block_size
     used = {}
     for s in range(tables.shape[0]):
@@ -172,11 +175,15 @@ def grouped_bytes(wl: W.Workload, sess) -> dict:
     """Algorithmic bytes of one grouped decode: each group's shared prefix
     (whole blocks, as the library cuts it) once per kv head, every
     sequence's remaining tokens, q and out, and the table entries read."""
+    return _grouped_from_tables(wl, sess.block_tables.cpu().numpy())
+
+
+def _grouped_from_tables(wl: W.Workload, tables: np.ndarray) -> dict:
+    from paged_kv_cache_449_amd import shared_prefix_groups
     n = wl.context_lens.astype(np.int64)
     bs = wl.block_size
-    gs = sess.group_start.cpu().numpy()
-    gsh = sess.group_shared.cpu().numpy()
     limit = max(1, 16 // wl.group)
+    gs, gsh = shared_prefix_groups(tables, n, limit)
     shared = np.zeros_like(n)
     unique_tokens = 0
     for g in range(gsh.shape[0]):
@@ -224,13 +231,39 @@ def cpu_baseline(wl: W.Workload, target_s: float = 12.0):
                       f"{dt:.1f} s single-threaded fp64"}, run, seqs
 
 
-def host_threads(limit: int = 16) -> int:
+# Host threads of the all-cores oracle leg: at most the CPU share one GPU's
+# job is given on the measurement host (16 cores), whatever the machine has.
+HOST_THREAD_CAP = 16
+
+
+def host_threads(limit: int = HOST_THREAD_CAP) -> int:
     """Host cores this process may use, at most `limit`."""
     try:
         n = len(os.sched_getaffinity(0))
     except AttributeError:
         n = os.cpu_count() or 1
     return max(1, min(n, limit))
+
+
+def host_facts() -> dict:
+    """What the oracle timings ran on: the machine's logical CPU count, the
+    cores this process may use, the thread cap of the all-cores leg, and the
+    CPU model."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except AttributeError:
+        usable = os.cpu_count()
+    return {"os_cpu_count": os.cpu_count(), "usable_cores": usable, "thread_cap": HOST_THREAD_CAP,
+            "cpu_model": model}
 
 
 def cpu_baseline_parallel(wl: W.Workload, run, seqs, threads: int) -> dict:
@@ -441,6 +474,129 @@ def block_manager_result(steps: int = 512, num_seqs: int = 256) -> dict:
     }
 
 
+def _pmc_rows(csv_path: str):
+    import csv
+    with open(csv_path) as f:
+        return sorted(csv.DictReader(f), key=lambda r: int(r["Dispatch_Id"]))
+
+
+def summarise_pmc(fetch_csv: str, write_csv: str, kernel_match, calib_match=("bitwise_not", "BitwiseNot")) -> dict:
+    """HBM bytes per launch from two rocprofv3 --pmc runs (FETCH_SIZE, then
+    WRITE_SIZE; counter_collection.csv, KiB per dispatch).  Each counter is
+    scaled by what it read for the calibration kernel of --calibrate-copy,
+    which reads 1 GiB and writes 1 GiB.  kernel_match: substrings of the
+    kernel names that make up one launch of the call (several kernels of one
+    call are summed in dispatch order; a launch ends at the last name in
+    kernel_match)."""
+    out = {}
+    for ctr, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        rows = _pmc_rows(path)
+        cal = [float(r["Counter_Value"]) for r in rows if any(c in r["Kernel_Name"] for c in calib_match)]
+        seq = [(r["Kernel_Name"], float(r["Counter_Value"])) for r in rows
+               if any(k in r["Kernel_Name"] for k in kernel_match)]
+        launches, cur = [], 0.0
+        for name, v in seq:
+            cur += v
+            if kernel_match[-1] in name:
+                launches.append(cur)
+                cur = 0.0
+        if not cal or not launches:
+            raise SystemExit(f"{path}: no calibration or no {kernel_match} dispatches")
+        out[ctr] = (float(np.mean(launches)), len(launches), cal[0])
+    f_kib, nd, f_cal = out["FETCH_SIZE"]
+    w_kib, _, w_cal = out["WRITE_SIZE"]
+    fetch_scale, write_scale = 1048576.0 / f_cal, 1048576.0 / w_cal
+    fb = int(round(f_kib * 1024 * fetch_scale))
+    wb = int(round(w_kib * 1024 * write_scale))
+    return {"kernels": list(kernel_match), "dispatches": nd, "FETCH_SIZE_KiB_per_dispatch": round(f_kib, 6),
+            "WRITE_SIZE_KiB_per_dispatch": round(w_kib, 6), "calibration_FETCH_SIZE_KiB": f_cal,
+            "calibration_WRITE_SIZE_KiB": w_cal, "fetch_scale": round(fetch_scale, 6),
+            "write_scale": round(write_scale, 6), "fetch_bytes_per_launch": fb, "write_bytes_per_launch": wb,
+            "traffic_bytes_per_launch": fb + wb}
+
+
+def record_traffic(kind: str, key: str, entry: dict, algorithmic: int, commands) -> None:
+    """Merge one workload's counter summary into profiles/<kind>_traffic.json,
+    stamped with the current kernel sources' digest (entries taken on other
+    sources are dropped)."""
+    path = TRAFFIC_FILES[kind]
+    digest = kernel_source_digest(kind)
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        rec = {}
+    if rec.get("kernel_source_sha256") != digest:
+        rec = {"what": f"HBM bytes per {kind} launch from rocprofv3 counters, scaled by a plain elementwise kernel "
+                       "that reads 1 GiB and writes 1 GiB (bench.py --calibrate-copy) in the same run",
+               "kernel_source_sha256": digest, "kernel_sources": list(KERNEL_SOURCES[kind]), "workloads": {}}
+    entry = dict(entry, algorithmic_bytes_per_launch=int(algorithmic), commands=list(commands))
+    entry["traffic_over_algorithmic"] = round(entry["traffic_bytes_per_launch"] / algorithmic, 4)
+    rec["workloads"][key] = entry
+    with open(path, "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps({key: entry}), flush=True)
+
+
+def decode_summary(name: str, dev, steps: int, warmup: int) -> dict:
+    """One more decode workload in the same run: build it, warm up, then time
+    `steps` whole steps back to back (step time) and `steps` more with HIP
+    events around each decode launch (kernel time), as for the main line.
+    Shared blocks are counted once (the HBM lower bound)."""
+    import paged_kv_cache_449_amd as pk
+    wl = get_workload(name)
+    print(f"[bench] building {wl.name}", file=sys.stderr, flush=True)
+    sess, q, kn, vn = build_session(wl, dev)
+    out = torch.empty_like(q)
+    pool = sess.pool
+    pt = wl.partition_tokens
+
+    def one_step(ev=None):
+        pk.copy_blocks(pool, sess.pairs)
+        pk.reshape_and_cache(pool, kn, vn, sess.slot_mapping)
+        if ev is not None:
+            ev[0].record()
+        pk.paged_attention_decode(pool, q, sess.block_tables, sess.context_lens, wl.scale, out=out,
+                                  partition_tokens=pt)
+        if ev is not None:
+            ev[1].record()
+
+    for _ in range(warmup):
+        one_step()
+    torch.cuda.synchronize(dev)
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        one_step()
+    torch.cuda.synchronize(dev)
+    step_us = (time.perf_counter() - t0) * 1e6 / steps
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for e in evs:
+        one_step(e)
+    torch.cuda.synchronize(dev)
+    us = np.array([a.elapsed_time(b) for a, b in evs]) * 1e3
+    nb = unique_bytes(wl, sess) if sess.shared_blocks > 0 else decode_bytes(wl)
+    logical = decode_bytes(wl)
+    achieved = nb["total"] / (float(us.mean()) / 1e6) / 1e9
+    res = {"workload": wl.name, "num_seqs": wl.num_seqs, "block_size": wl.block_size, "kv_dtype": wl.kv_dtype,
+           "partition_tokens": pt, "kernel_us": round(float(us.mean()), 2),
+           "kernel_us_p10_median_p90": [round(float(x), 1) for x in np.percentile(us, [10, 50, 90])],
+           "us_per_step": round(step_us, 1), "bytes_per_launch": nb["total"],
+           "bytes_counted": "unique (each shared block once)" if sess.shared_blocks > 0 else "algorithmic",
+           "achieved": round(achieved, 1), "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+           "kv_gbs_per_step": round(nb["kv"] / (step_us / 1e6) / 1e9, 1),
+           "logical_gbs": round(logical["total"] / (float(us.mean()) / 1e6) / 1e9, 1)}
+    print(f"[bench] {wl.name}: decode {us.mean():.1f} us, frac {res['frac']}", file=sys.stderr, flush=True)
+    del sess, q, kn, vn, out, pool
+    torch.cuda.empty_cache()
+    return res
+
+
+# The batch-256 workloads of the headline metric besides the default one:
+# the LLaMA-7B shape at block size 32, and parallel sampling (64 prompts x 4
+# candidates sharing their prompt's blocks).
+ALSO_DEFAULT = ("c3_llama7b_bf16_bs32", "c4_parallel_sampling_f16_p1023")
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -474,10 +630,20 @@ def main(argv=None) -> int:
                          "read once per group")
     ap.add_argument("--block-manager", action="store_true",
                     help="host block manager only (no GPU): reservation rate, oracle beside it, trace accounting")
+    ap.add_argument("--also", default=None,
+                    help="comma-separated decode workloads timed after the main one and reported under 'also' "
+                         "(default: the other batch-256 headline workloads when the main one is the default; "
+                         "'none' for none)")
+    ap.add_argument("--summarise-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"), default=None,
+                    help="no GPU work: turn the counter_collection.csv files of a rocprofv3 --pmc FETCH_SIZE run "
+                         "and a --pmc WRITE_SIZE run of this same command line (with --calibrate-copy) into HBM "
+                         "bytes per launch, and record them in profiles/<kind>_traffic.json")
     args = ap.parse_args(argv)
     if args.block_manager:
         print(json.dumps(block_manager_result()), flush=True)
         return 0
+    if args.summarise_pmc:
+        return summarise_main(args, argv)
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU: this build runs the decode path on a single MI355X "
@@ -648,16 +814,72 @@ def main(argv=None) -> int:
                      "bytes_per_launch": nb["total"],
                      "logical_gbs": round(logical_total / dec_mean_s / 1e9, 1)},
     }
+    if args.flush == "none" and not args.graph:
+        # 3. The serving-realistic cache state: a 512 MiB write before each
+        #    step (the layer's own projections write just before decode), so
+        #    dirty lines drain while the decode kernel reads.
+        scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        fevs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                for _ in range(args.steps)]
+        torch.cuda.synchronize(dev)
+        for i in range(args.steps):
+            scratch.zero_()
+            one_step(fevs[i])
+        torch.cuda.synchronize(dev)
+        fus = np.array([a.elapsed_time(b) for a, b in fevs]) * 1e3
+        fach = nb["total"] / (float(fus.mean()) / 1e6) / 1e9
+        res["roofline"]["flush_write"] = {"what": "512 MiB written before every step, outside the events",
+                                          "kernel_us": round(float(fus.mean()), 2),
+                                          "achieved": round(fach, 1), "frac": round(fach / HBM_PEAK_GBS, 4)}
+        del scratch
     if args.swap_blocks > 0:
         res["swap"] = swap_measurement(pool, min(args.swap_blocks, wl.num_blocks))
     res["writes"] = writes
     res["achievable"] = achievable_read(dev)
     res["roofline"]["frac_of_achievable"] = round(achieved / res["achievable"]["value"], 4)
+    also = args.also
+    if also is None:
+        also = ",".join(ALSO_DEFAULT) if wl.name == DEFAULT_WORKLOAD and not (args.grouped or args.graph) else "none"
+    if also != "none":
+        del sess, q, kn, vn, out, pool
+        torch.cuda.empty_cache()
+        res["also"] = [decode_summary(n, dev, args.steps, args.warmup) for n in also.split(",") if n]
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
         res["cpu_baseline"], run, seqs = cpu_baseline(wl)
         res["cpu_baseline_parallel"] = cpu_baseline_parallel(wl, run, seqs, host_threads())
+        res["cpu_baseline"]["host"] = res["cpu_baseline_parallel"]["host"] = host_facts()
     print(json.dumps(res), flush=True)
+    return 0
+
+
+def summarise_main(args, argv) -> int:
+    """--summarise-pmc: the counter files of one workload's two --pmc runs
+    into its entry of profiles/<kind>_traffic.json."""
+    wl = get_workload(args.workload)
+    kind = "prefill" if wl.multi_token else "decode"
+    pt = wl.partition_tokens if args.partition_tokens is None else args.partition_tokens
+    key = wl.name + (":grouped" if args.grouped else "") + ("" if pt == wl.partition_tokens else f":pt{pt}")
+    if wl.multi_token:
+        match = ("paged_prefill",)
+        algorithmic = prefill_cost(wl)["total"]
+    else:
+        from oracle.paging import plan
+        tables = plan(wl, W.free_list_order(wl))["tables"]
+        if args.grouped:
+            match = ("paged_decode_shared_kernel", "paged_decode_suffix_kernel")
+            algorithmic = _grouped_from_tables(wl, tables)["total"]
+        else:
+            match = ("paged_decode_plan_kernel", "paged_decode_kernel")
+            shared = bool(np.any((tables[1:, 0] >= 0) & (tables[1:, 0] == tables[:-1, 0])))
+            algorithmic = (_unique_from_tables(wl, tables) if shared else decode_bytes(wl))["total"]
+    entry = summarise_pmc(args.summarise_pmc[0], args.summarise_pmc[1], match)
+    rest = [a for a in (argv if argv is not None else sys.argv[1:])]
+    i = rest.index("--summarise-pmc")
+    base = " ".join(rest[:i] + rest[i + 3:])
+    cmds = [f"rocprofv3 --pmc {c} --output-format csv -d <dir> -o pmc -- python3 bench.py {base} --calibrate-copy"
+            for c in ("FETCH_SIZE", "WRITE_SIZE")]
+    record_traffic(kind, key, entry, algorithmic, cmds)
     return 0
 
 

@@ -24,8 +24,17 @@
  *     when the pool was created; the caller owns them and keeps them alive
  *     until the stream work that uses them has finished.
  *   - `stream` is a hipStream_t (NULL = the default stream).  Work is only
- *     enqueued: no call synchronises the device and, apart from
- *     kv_pool_create, none allocates device memory.
+ *     enqueued: no call synchronises the device, and only the two pool
+ *     constructors allocate device memory (kv_pool_create: the pools and,
+ *     for fp8, the per-head scale table; kv_pool_create_from: that table).
+ *   - Launch-shape overrides are read from the environment once, when a pool
+ *     is made, and hold for its life: PAGEDKV_DECODE_WAVES_PER_CU (worker
+ *     wavefronts per compute unit of the library-sized decode split, 1..64,
+ *     default 8), PAGEDKV_DECODE_MFMA=0 (query groups of decode on the
+ *     vector ALUs instead of the matrix cores) and PAGEDKV_PREFILL_PATH=
+ *     wave|group|unit (the launch shape of paged_attention_prefill).  They
+ *     exist for tuning and tests; results agree within the tolerances
+ *     whatever they say.
  *   - Host-side arguments are checked before anything is enqueued; a failed
  *     check returns an error status and enqueues nothing.
  *   - Device-side data (lengths, table entries, slots, pairs) are
@@ -119,16 +128,19 @@ kv_status_t kv_pool_set_scales(kv_pool_t* pool, float k_scale, float v_scale);
  * kv_pool_set_head_scales -- fp8 pools: one k and one v scale per kv head
  * instead of one per tensor, for heads whose value ranges differ (a variant
  * of the fp8 KV cache option, "vLLM KV Cache 实现机制" §2.3 table).
- * k_scales and v_scales are host arrays of num_kv_heads fp32 values, each
- * finite and > 0; they are copied into device memory the pool owns.  From
- * then on reshape_and_cache encodes head h with its own scales and the
- * attention calls decode with them.  Both NULL returns to the per-tensor
- * scales (kv_pool_set_scales also does).  Call it while no kernel that
- * reads or writes the pool is in flight.  KV_ERR_INVALID_ARG: not an fp8
- * pool, exactly one array NULL, or a bad value; KV_ERR_OOM / KV_ERR_HIP for
- * the device copy.
+ * k_scales and v_scales are DEVICE arrays of num_kv_heads fp32 values, each
+ * finite and > 0 (a precondition, like other device data: a bad value gives
+ * wrong numbers, never an access outside any buffer).  They are copied, in
+ * stream order on `stream`, into the pool's scale table (allocated when the
+ * pool was made, so nothing is allocated here).  Work enqueued on `stream`
+ * after this call encodes (reshape_and_cache) and decodes (the attention
+ * calls) head h with its own scales; work enqueued before it sees the
+ * previous table.  Both NULL returns to the per-tensor scales (so does
+ * kv_pool_set_scales), for calls made from then on.  The source arrays must
+ * stay alive until the copy has run.  KV_ERR_INVALID_ARG: not an fp8 pool or
+ * exactly one array NULL; KV_ERR_HIP if the copy cannot be enqueued.
  */
-kv_status_t kv_pool_set_head_scales(kv_pool_t* pool, const float* k_scales, const float* v_scales);
+kv_status_t kv_pool_set_head_scales(kv_pool_t* pool, const float* k_scales, const float* v_scales, void* stream);
 
 /*
  * reshape_and_cache -- store the K and V of num_tokens new tokens into their
@@ -171,8 +183,10 @@ kv_status_t reshape_and_cache(kv_pool_t* pool, const void* k_new, const void* v_
  * and V are decoded exactly and multiplied by their scales.
  *
  * q_dtype must equal the pool dtype, except fp8 pools, which take f32, f16
- * or bf16 queries.  num_q_heads must be a multiple of num_kv_heads, with at
- * most 8 query heads per kv head.
+ * or bf16 queries.  num_q_heads must be num_kv_heads times 1, 2, 4, 8 or 16.
+ * 16 query heads per kv head run only on the matrix cores (bf16 or f16
+ * queries, block_size >= 16, matrix cores not switched off):
+ * KV_ERR_UNSUPPORTED otherwise.
  *
  * Work split: the cached tokens of all (kv head, sequence) pairs are laid end
  * to end and cut into equal runs of whole blocks, one per worker wavefront,
@@ -185,8 +199,8 @@ kv_status_t reshape_and_cache(kv_pool_t* pool, const void* k_new, const void* v_
  * by the worker that finishes last (log-sum-exp merge of the partial results,
  * in a fixed order, so results are bitwise reproducible).  Query groups
  * (num_q_heads > num_kv_heads) with a 16-bit operand type (bf16 or f16
- * queries) and block_size >= 16 run on the matrix cores; the environment
- * variable PAGEDKV_DECODE_MFMA=0 keeps them on the vector ALUs.
+ * queries) and block_size >= 16 run on the matrix cores (unless the pool
+ * was made with PAGEDKV_DECODE_MFMA=0).
  *
  * When partition_tokens is given and the batch would need more than 65528
  * runs, the runs are lengthened to the smallest whole number of blocks that
@@ -228,8 +242,11 @@ kv_status_t paged_attention_workspace_size(const kv_pool_t* pool, int32_t num_se
  * is cut to whole blocks.  Inconsistent groups (overlapping, unsorted, or
  * sharing that the tables do not have) give wrong rows but stay inside every
  * buffer.  The other arguments are paged_attention_decode's; workspace:
- * paged_attention_decode_grouped_workspace_size() bytes, 256-byte aligned,
- * contents free (no state across calls).
+ * paged_attention_decode_grouped_workspace_size() bytes, 256-byte aligned.
+ * Its first 256 KiB are the arrival-counter header of paged_attention_decode
+ * and paged_attention_prefill: this call neither reads nor writes them, so
+ * one workspace serves all three calls.  The rest holds per-row records and
+ * keeps no state across calls.
  * Supported: bf16/bf16, f16/f16, fp8 with bf16 or f16 queries; block_size
  * >= 16 (KV_ERR_UNSUPPORTED otherwise: call paged_attention_decode).
  * Two kernels run on `stream`.
@@ -242,7 +259,8 @@ kv_status_t paged_attention_decode_grouped(const kv_pool_t* pool, const void* q,
                                            void* stream);
 
 /* paged_attention_decode_grouped_workspace_size -- bytes of workspace the
- * call above needs: one partial record per (sequence, query head). */
+ * call above needs: the 256 KiB counter header it leaves alone, then one
+ * partial record per (sequence, query head). */
 kv_status_t paged_attention_decode_grouped_workspace_size(const kv_pool_t* pool, int32_t num_seqs,
                                                           int32_t num_q_heads, size_t* bytes);
 

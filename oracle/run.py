@@ -22,26 +22,35 @@ from .paging import plan
 
 class OracleRun:
     def __init__(self, wl, prompts: Optional[Sequence[int]] = None, scales=None, prompt_kv=None,
-                 free_order=None):
+                 free_order=None, threads: int = 1):
         """prompts: restrict the prompt writes to these prompts (sampled checks);
         scales: precomputed (k_scale, v_scale) for fp8 pools;
         prompt_kv: optional dict prompt -> (k, v) already drawn;
-        free_order: override the workload's free-list order (placement tests)."""
+        free_order: override the workload's free-list order (placement tests);
+        threads: host threads for the prompt writes (each prompt's tokens go
+        to slots no other prompt owns, so the writes are independent)."""
         self.wl = wl
         order = workloads.free_list_order(wl) if free_order is None else free_order
         self.plan = plan(wl, order)
-        ks, vs = scales if scales is not None else workloads.fp8_scales(wl)
+        ks, vs = scales if scales is not None else workloads.fp8_scales(wl, threads=max(threads, 8))
         self.k_scale, self.v_scale = ks, vs
         hs = workloads.fp8_head_scales(wl) if wl.head_scales else None
         self.head_scales = hs
         self.pool = HostPool(wl.num_blocks, wl.block_size, wl.num_kv_heads, wl.head_dim, wl.kv_dtype, ks, vs,
                              head_scales=hs)
-        todo = range(wl.num_prompts) if prompts is None else prompts
-        for p in todo:
-            if wl.prompt_lens[p] == 0:
-                continue
+        todo = [p for p in (range(wl.num_prompts) if prompts is None else prompts) if wl.prompt_lens[p] > 0]
+
+        def write(p):
             k, v = prompt_kv[p] if prompt_kv is not None and p in prompt_kv else workloads.prompt_kv(wl, p)
             self.pool.reshape_and_cache(k, v, wl.src_dtype, self.plan["prompt_slots"][p])
+
+        if threads > 1 and len(todo) > 1:
+            from concurrent.futures import ThreadPoolExecutor
+            with ThreadPoolExecutor(min(threads, len(todo))) as ex:
+                list(ex.map(write, todo))
+        else:
+            for p in todo:
+                write(p)
         self.pool.copy_blocks(self.plan["pairs"])
         kn, vn = workloads.new_kv(wl)
         slots = self.plan["new_slots"]
@@ -58,6 +67,21 @@ class OracleRun:
     def decode(self, seqs: Optional[Sequence[int]] = None) -> np.ndarray:
         wl = self.wl
         return self.pool.decode(self.q, wl.q_dtype, self.tables, wl.context_lens, wl.scale, wl.num_q_heads, seqs)
+
+    def decode_parallel(self, threads: int) -> np.ndarray:
+        """decode() of every sequence, the sequences dealt (longest first) to
+        `threads` host threads; each thread's call computes its own rows."""
+        wl = self.wl
+        n = wl.context_lens
+        order = sorted(range(wl.num_seqs), key=lambda s: -int(n[s]))
+        parts = [p for p in (order[i::threads] for i in range(max(1, threads))) if p]
+        from concurrent.futures import ThreadPoolExecutor
+        with ThreadPoolExecutor(len(parts)) as ex:
+            outs = list(ex.map(self.decode, parts))
+        out = outs[0]
+        for part, o in zip(parts[1:], outs[1:]):
+            out[part] = o[part]
+        return out
 
     def prefill(self, seqs: Optional[Sequence[int]] = None) -> np.ndarray:
         """Causal attention of every sequence's new tokens ([total_q][Hq][D]);

@@ -55,7 +55,7 @@ def lib() -> ctypes.CDLL:
         L.kv_pool_destroy.argtypes = [vp]
         L.kv_pool_info.argtypes = [vp, pp, pp, ctypes.POINTER(sz), ctypes.POINTER(i64)]
         L.kv_pool_set_scales.argtypes = [vp, f32, f32]
-        L.kv_pool_set_head_scales.argtypes = [vp, vp, vp]
+        L.kv_pool_set_head_scales.argtypes = [vp, vp, vp, vp]
         L.reshape_and_cache.argtypes = [vp, vp, vp, ctypes.c_int, vp, i32, vp]
         L.paged_attention_decode.argtypes = [vp, vp, ctypes.c_int, vp, vp, i32, vp, i32, i32, f32, i32, vp, sz, vp]
         L.paged_attention_workspace_size.argtypes = [vp, i32, i32, i32, i32, ctypes.POINTER(sz)]
@@ -178,20 +178,27 @@ def kv_pool_set_scales(pool: KVPool, k_scale: float, v_scale: float) -> None:
     pool.head_scales = None
 
 
-def kv_pool_set_head_scales(pool: KVPool, k_scales, v_scales) -> None:
-    """fp8 pools: one scale per kv head (sequences of num_kv_heads floats);
-    None, None returns to the per-tensor scales."""
+def kv_pool_set_head_scales(pool: KVPool, k_scales, v_scales, stream=None) -> None:
+    """fp8 pools: one scale per kv head (sequences of num_kv_heads floats,
+    each finite and > 0); None, None returns to the per-tensor scales.  The
+    values are uploaded to a device tensor that the library copies, in stream
+    order, into the pool's own scale table."""
     import numpy as np
+    d = pool.device
     if k_scales is None and v_scales is None:
-        _check(lib().kv_pool_set_head_scales(pool.handle, None, None), "kv_pool_set_head_scales")
+        _check(lib().kv_pool_set_head_scales(pool.handle, None, None, _stream(d, stream)), "kv_pool_set_head_scales")
         pool.head_scales = None
         return
     k = np.ascontiguousarray(k_scales, dtype=np.float32)
     v = np.ascontiguousarray(v_scales, dtype=np.float32)
     if k.shape != (pool.num_kv_heads,) or v.shape != (pool.num_kv_heads,):
         raise ValueError(f"need {pool.num_kv_heads} scales each")
-    with torch.cuda.device(pool.device):
-        _check(lib().kv_pool_set_head_scales(pool.handle, k.ctypes.data, v.ctypes.data), "kv_pool_set_head_scales")
+    if not (np.all(np.isfinite(k)) and np.all(np.isfinite(v)) and np.all(k > 0) and np.all(v > 0)):
+        raise ValueError("scales must be finite and > 0")
+    dev = torch.from_numpy(np.concatenate([k, v])).to(d)
+    _check(lib().kv_pool_set_head_scales(pool.handle, dev.data_ptr(), dev.data_ptr() + 4 * pool.num_kv_heads,
+                                         _stream(d, stream)), "kv_pool_set_head_scales")
+    pool._head_scale_src = dev   # alive until the stream copy has run
     pool.head_scales = (k.copy(), v.copy())
 
 

@@ -19,10 +19,14 @@ struct kv_pool {
   bool owned;
   float k_scale;
   float v_scale;
-  float* head_scales;   // device [2][num_kv_heads] (k then v) fp8 per-head scales
+  float* head_scales;   // device [2][num_kv_heads] (k then v) fp8 per-head scales, allocated with the pool
   bool per_head;        // head_scales in use
   int device;
   int num_cus;
+  // dispatch settings, read from the environment once when the pool is made
+  int decode_waves_per_cu;  // PAGEDKV_DECODE_WAVES_PER_CU (default 8)
+  bool decode_mfma;         // PAGEDKV_DECODE_MFMA=0 keeps query groups on the vector ALUs
+  int prefill_shape;        // PAGEDKV_PREFILL_PATH: -1 auto, 0 wave, 1 group, 2 unit
 };
 
 namespace pkv {

@@ -1,31 +1,10 @@
 // Host entry points of paged decode attention: argument checks, work split,
 // workspace layout and dispatch to the kernel instantiations.
-#include <stdlib.h>
-
 #include "decode_kernel.h"
 
 namespace {
 
 using namespace pkv;
-
-// Worker wavefronts per compute unit when the library sizes the split.
-// PAGEDKV_DECODE_WAVES_PER_CU overrides it (tuning).
-int waves_per_cu() {
-  static int v = [] {
-    const char* e = getenv("PAGEDKV_DECODE_WAVES_PER_CU");
-    int x = e ? atoi(e) : 0;
-    return (x >= 1 && x <= 64) ? x : 8;
-  }();
-  return v;
-}
-
-// Query groups (G > 1) run on the matrix cores where the dtype pair has a
-// 16-bit operand type and blocks hold whole 16-token tiles;
-// PAGEDKV_DECODE_MFMA=0 keeps them on the vector ALUs (read at every call).
-bool mfma_allowed() {
-  const char* e = getenv("PAGEDKV_DECODE_MFMA");
-  return !(e && e[0] == '0');
-}
 
 struct Plan {
   int32_t chunk;        // 0 = derived in the kernel
@@ -39,7 +18,7 @@ kv_status_t make_plan(const kv_pool_t* pool, int32_t num_seqs, int32_t num_q_hea
   if (!pool || num_seqs < 0 || num_q_heads <= 0 || max_blocks <= 0 || partition_tokens < 0) return KV_ERR_INVALID_ARG;
   if (num_q_heads % pool->num_kv_heads) return KV_ERR_INVALID_ARG;
   const int G = num_q_heads / pool->num_kv_heads;
-  if (G != 1 && G != 2 && G != 4 && G != 8) return KV_ERR_UNSUPPORTED;
+  if (G != 1 && G != 2 && G != 4 && G != 8 && G != 16) return KV_ERR_UNSUPPORTED;
   const int64_t units = (int64_t)num_seqs * pool->num_kv_heads * max_blocks;  // upper bound of blocks
   if (units > (1LL << 30) || (int64_t)max_blocks * pool->block_size > (1LL << 30)) return KV_ERR_INVALID_ARG;
   int64_t workers;
@@ -53,7 +32,7 @@ kv_status_t make_plan(const kv_pool_t* pool, int32_t num_seqs, int32_t num_q_hea
     workers = (units + chunk - 1) / chunk;
   } else {
     plan->chunk = 0;
-    workers = (int64_t)pool->num_cus * waves_per_cu();
+    workers = (int64_t)pool->num_cus * pool->decode_waves_per_cu;
     if (workers > units) workers = units;
   }
   if (workers < 1) workers = 1;
@@ -126,7 +105,10 @@ extern "C" kv_status_t paged_attention_decode(const kv_pool_t* pool, const void*
   if (64 / lanes_per_row > pool->block_size) return KV_ERR_UNSUPPORTED;
 
   hipStream_t s = (hipStream_t)stream;
-  const bool mfma = G > 1 && mfma_allowed();
+  // Query groups (G > 1) run on the matrix cores where the dtype pair has a
+  // 16-bit operand type and blocks hold whole 16-token tiles, unless the
+  // pool was made with PAGEDKV_DECODE_MFMA=0.
+  const bool mfma = G > 1 && pool->decode_mfma;
   if (!fp8) {
     if (q_dtype != pool->dtype) return KV_ERR_UNSUPPORTED;
     switch (pool->dtype) {

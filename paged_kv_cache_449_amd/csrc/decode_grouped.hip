@@ -7,8 +7,10 @@ using namespace pkv;
 extern "C" kv_status_t paged_attention_decode_grouped_workspace_size(const kv_pool_t* pool, int32_t num_seqs,
                                                                      int32_t num_q_heads, size_t* bytes) {
   if (!pool || !bytes || num_seqs < 0 || num_q_heads <= 0) return KV_ERR_INVALID_ARG;
-  *bytes = (size_t)num_seqs * num_q_heads * (pool->head_dim + 4) * sizeof(float);
-  if (*bytes < 256) *bytes = 256;
+  // the counter header of paged_attention_decode / _prefill is skipped and
+  // left untouched, so one workspace serves all three calls
+  *bytes = (size_t)kCounterSlots * sizeof(int32_t) +
+           (size_t)num_seqs * num_q_heads * (pool->head_dim + 4) * sizeof(float);
   return KV_OK;
 }
 
@@ -46,7 +48,7 @@ extern "C" kv_status_t paged_attention_decode_grouped(const kv_pool_t* pool, con
   p.context_lens = context_lens;
   p.query_start = nullptr;
   p.counters = nullptr;
-  p.partials = (float*)workspace;
+  p.partials = (float*)((uint8_t*)workspace + (size_t)kCounterSlots * sizeof(int32_t));
   p.num_seqs = num_seqs;
   p.total_q = 0;
   p.num_kv_heads = pool->num_kv_heads;

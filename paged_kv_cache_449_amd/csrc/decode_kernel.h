@@ -725,11 +725,25 @@ kv_status_t launch_decode(const DecodeParams& p, int D, int G, bool use_mfma, hi
                        stream, p);                                                                         \
     return launch_status();                                                                                \
   }
-#define PKV_CASES(DD) PKV_CASE(DD, 1) PKV_CASE(DD, 2) PKV_CASE(DD, 4) PKV_CASE(DD, 8)
+  // 16 query heads per kv head fill the matrix-core tile's 16 rows; the
+  // vector-ALU run does not hold that many query rows in registers
+#define PKV_CASE16(DD)                                                                                     \
+  if (D == DD && G == 16) {                                                                                \
+    if constexpr (kHasMfma) {                                                                              \
+      if (mfma) {                                                                                          \
+        hipLaunchKernelGGL((paged_decode_kernel<KV, QT, DD, 16, true>), dim3(p.num_workers), dim3(64), 0,  \
+                           stream, p);                                                                     \
+        return launch_status();                                                                            \
+      }                                                                                                    \
+    }                                                                                                      \
+    return KV_ERR_UNSUPPORTED;                                                                             \
+  }
+#define PKV_CASES(DD) PKV_CASE(DD, 1) PKV_CASE(DD, 2) PKV_CASE(DD, 4) PKV_CASE(DD, 8) PKV_CASE16(DD)
   PKV_CASES(64)
   PKV_CASES(128)
   PKV_CASES(256)
 #undef PKV_CASES
+#undef PKV_CASE16
 #undef PKV_CASE
   return KV_ERR_UNSUPPORTED;
 }

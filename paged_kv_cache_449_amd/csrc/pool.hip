@@ -5,6 +5,9 @@
 // 分页搬进 GPU KV cache", case 1).  One hipMalloc per pool keeps the blocks in
 // a few large physically contiguous fragments, which keeps address
 // translation cheap for the scattered block reads of decode.
+#include <stdlib.h>
+#include <string.h>
+
 #include <new>
 
 #include "common.h"
@@ -37,6 +40,22 @@ kv_status_t fill(kv_pool_t* p, int32_t num_blocks, int32_t block_size, int32_t n
   if (hipGetDevice(&p->device) != hipSuccess) return KV_ERR_HIP;
   if (hipDeviceGetAttribute(&p->num_cus, hipDeviceAttributeMultiprocessorCount, p->device) != hipSuccess)
     return KV_ERR_HIP;
+  // tuning and test overrides of the launch shape, fixed for the pool's life
+  const char* e = getenv("PAGEDKV_DECODE_WAVES_PER_CU");
+  const int w = e ? atoi(e) : 0;
+  p->decode_waves_per_cu = (w >= 1 && w <= 64) ? w : 8;
+  e = getenv("PAGEDKV_DECODE_MFMA");
+  p->decode_mfma = !(e && e[0] == '0');
+  e = getenv("PAGEDKV_PREFILL_PATH");
+  p->prefill_shape = !e ? -1 : strcmp(e, "wave") == 0 ? 0 : strcmp(e, "group") == 0 ? 1 : strcmp(e, "unit") == 0 ? 2 : -1;
+  // fp8 pools: the per-kv-head scale table, so that setting scales later
+  // allocates nothing
+  if (dtype == KV_FP8_E4M3FN) {
+    if (hipMalloc(&p->head_scales, 2 * (size_t)num_kv_heads * sizeof(float)) != hipSuccess) {
+      p->head_scales = nullptr;
+      return KV_ERR_OOM;
+    }
+  }
   return KV_OK;
 }
 
@@ -52,15 +71,18 @@ extern "C" kv_status_t kv_pool_create(int32_t num_blocks, int32_t block_size, in
   kv_pool_t* p = new (std::nothrow) kv_pool_t();
   if (!p) return KV_ERR_OOM;
   if ((st = fill(p, num_blocks, block_size, num_kv_heads, head_dim, dtype)) != KV_OK) {
+    if (p->head_scales) (void)hipFree(p->head_scales);
     delete p;
     return st;
   }
   if (hipMalloc(&p->k, bytes) != hipSuccess) {
+    if (p->head_scales) (void)hipFree(p->head_scales);
     delete p;
     return KV_ERR_OOM;
   }
   if (hipMalloc(&p->v, bytes) != hipSuccess) {
     (void)hipFree(p->k);
+    if (p->head_scales) (void)hipFree(p->head_scales);
     delete p;
     return KV_ERR_OOM;
   }
@@ -83,6 +105,7 @@ extern "C" kv_status_t kv_pool_create_from(int32_t num_blocks, int32_t block_siz
   kv_pool_t* p = new (std::nothrow) kv_pool_t();
   if (!p) return KV_ERR_OOM;
   if ((st = fill(p, num_blocks, block_size, num_kv_heads, head_dim, dtype)) != KV_OK) {
+    if (p->head_scales) (void)hipFree(p->head_scales);
     delete p;
     return st;
   }
@@ -130,29 +153,18 @@ extern "C" kv_status_t kv_pool_set_scales(kv_pool_t* pool, float k_scale, float 
   return KV_OK;
 }
 
-extern "C" kv_status_t kv_pool_set_head_scales(kv_pool_t* pool, const float* k_scales, const float* v_scales) {
+extern "C" kv_status_t kv_pool_set_head_scales(kv_pool_t* pool, const float* k_scales, const float* v_scales,
+                                               void* stream) {
   if (!pool || pool->dtype != KV_FP8_E4M3FN || (!k_scales) != (!v_scales)) return KV_ERR_INVALID_ARG;
   if (!k_scales) {
     pool->per_head = false;
     return KV_OK;
   }
-  const int H = pool->num_kv_heads;
-  for (int h = 0; h < H; ++h) {
-    const float a = k_scales[h], b = v_scales[h];
-    if (!(a > 0.0f) || !(b > 0.0f) || a > 3.0e38f || b > 3.0e38f) return KV_ERR_INVALID_ARG;
-  }
-  if (!pool->head_scales) {
-    int cur = -1;
-    if (hipGetDevice(&cur) != hipSuccess || hipSetDevice(pool->device) != hipSuccess) return KV_ERR_HIP;
-    const hipError_t e = hipMalloc(&pool->head_scales, 2 * (size_t)H * sizeof(float));
-    (void)hipSetDevice(cur);
-    if (e != hipSuccess) {
-      pool->head_scales = nullptr;
-      return KV_ERR_OOM;
-    }
-  }
-  if (hipMemcpy(pool->head_scales, k_scales, (size_t)H * sizeof(float), hipMemcpyHostToDevice) != hipSuccess ||
-      hipMemcpy(pool->head_scales + H, v_scales, (size_t)H * sizeof(float), hipMemcpyHostToDevice) != hipSuccess)
+  if (!pool->head_scales) return KV_ERR_INVALID_ARG;
+  const size_t n = (size_t)pool->num_kv_heads * sizeof(float);
+  hipStream_t s = (hipStream_t)stream;
+  if (hipMemcpyAsync(pool->head_scales, k_scales, n, hipMemcpyDeviceToDevice, s) != hipSuccess ||
+      hipMemcpyAsync(pool->head_scales + pool->num_kv_heads, v_scales, n, hipMemcpyDeviceToDevice, s) != hipSuccess)
     return KV_ERR_HIP;
   pool->per_head = true;
   return KV_OK;

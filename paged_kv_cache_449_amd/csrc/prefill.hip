@@ -2,9 +2,6 @@
 // workspace layout and dispatch to the kernel instantiations.
 #include "prefill_kernel.h"
 
-#include <cstdlib>
-#include <cstring>
-
 namespace {
 
 using namespace pkv;
@@ -42,14 +39,12 @@ kv_status_t prefill_plan(const kv_pool_t* pool, int32_t num_q_heads, bool wg, in
 }
 
 // Launch shape: 0 one-wave tiles, 1 split work-groups, 2 one work-group per
-// row block.  PAGEDKV_PREFILL_PATH=wave / group / unit forces one (tests);
-// otherwise the average rows per (sequence, kv head) picks the work-groups,
-// and units when there are enough row blocks to fill the chip several times.
-int prefill_mode(int64_t total_q, int G, int num_seqs, int num_kv_heads, int D, int num_cus) {
-  const char* e = getenv("PAGEDKV_PREFILL_PATH");
-  if (e && strcmp(e, "wave") == 0) return 0;
-  if (e && strcmp(e, "group") == 0) return 1;
-  if (e && strcmp(e, "unit") == 0) return 2;
+// row block.  A pool made with PAGEDKV_PREFILL_PATH=wave / group / unit
+// forces one (tests); otherwise the average rows per (sequence, kv head)
+// picks the work-groups, and units when there are enough row blocks to fill
+// the chip several times.
+int prefill_mode(int forced, int64_t total_q, int G, int num_seqs, int num_kv_heads, int D, int num_cus) {
+  if (forced >= 0) return forced;
   if (total_q * G < (int64_t)kGroupMinRows * num_seqs) return 0;
   const int64_t rows = 16LL * (D <= 128 ? 8 : 4);
   const int64_t units = total_q * G / rows * num_kv_heads;
@@ -74,7 +69,8 @@ extern "C" kv_status_t paged_attention_prefill(const kv_pool_t* pool, const void
   int32_t workers;
   size_t counters_bytes, need;
   const int mode = pool && num_q_heads > 0 && num_q_heads % pool->num_kv_heads == 0
-                       ? prefill_mode(total_q, num_q_heads / pool->num_kv_heads, num_seqs > 0 ? num_seqs : 1,
+                       ? prefill_mode(pool->prefill_shape, total_q, num_q_heads / pool->num_kv_heads,
+                                      num_seqs > 0 ? num_seqs : 1,
                                       pool->num_kv_heads, pool->head_dim, pool->num_cus)
                        : 0;
   kv_status_t st = prefill_plan(pool, num_q_heads, mode == 1, &workers, &counters_bytes, &need);

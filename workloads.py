@@ -307,9 +307,9 @@ def variant_configs() -> Dict[str, Workload]:
 
 
 def small_variant_configs() -> Dict[str, Workload]:
-    """Reduced variants for parity: block sizes 8 and 64, 8:1 groups,
-    per-head fp8 scales with bf16 and f16 queries, and per-head scales in a
-    multi-token step."""
+    """Reduced variants for parity: block sizes 8 and 64, 8:1 and 16:1
+    groups, per-head fp8 scales with bf16 and f16 queries, and per-head scales
+    in a multi-token step."""
     ws = [
         config_c3(8, num_seqs=10, heads=3, lo=16, hi=500, name="c3s_bf16_bs8"),
         config_c3(64, num_seqs=10, heads=3, lo=16, hi=900, name="c3s_bf16_bs64"),
@@ -319,6 +319,8 @@ def small_variant_configs() -> Dict[str, Workload]:
                   name="c5s_fp8_headscale_mha_f16"),
         _make("p6s_fp8_headscale", 15, 8, 4, 128, "fp8e4m3", "bf16", 16, ctx_lens=[60, 37, 130],
               query_lens=[20, 37, 9], head_scales=True),
+        config_c5("bf16", num_seqs=4, lo=100, hi=700, hq=16, hkv=1, name="c5s_gqa16_bf16"),
+        config_c5("fp8e4m3", num_seqs=4, lo=100, hi=700, hq=32, hkv=2, q="f16", name="c5s_gqa16_fp8_f16"),
     ]
     return {w.name: w for w in ws}
 
