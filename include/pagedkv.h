@@ -217,7 +217,30 @@ kv_status_t paged_attention_decode(const kv_pool_t* pool, const void* q, kv_dtyp
                                    int32_t num_seqs, int32_t num_q_heads, float scale, int32_t partition_tokens,
                                    void* workspace, size_t workspace_bytes, void* stream);
 
-/* paged_attention_workspace_size -- bytes of workspace the call above needs
+/*
+ * paged_attention_decode_noalloc -- paged_attention_decode for callers that
+ * cannot allocate device memory or pass a workspace: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation.  Same
+ * arguments, result and kernels as paged_attention_decode, without
+ * workspace/workspace_bytes: the call uses a fixed scratch area of
+ * PAGEDKV_DECODE_SCRATCH_BYTES (64 MiB) that the library holds in device
+ * memory on every device it runs on, until the process ends.  It allocates
+ * nothing.  The first call on a device looks the area up and clears its
+ * arrival counters on `stream` (one small kernel); every call leaves them
+ * zero again.  All calls on one device share the area: two calls that
+ * overlap in time on one device (different streams, or threads without
+ * ordering) race and give wrong results.  KV_ERR_WORKSPACE: the shape needs
+ * more than PAGEDKV_DECODE_SCRATCH_BYTES of workspace
+ * (paged_attention_workspace_size tells how much); other errors as
+ * paged_attention_decode.
+ */
+#define PAGEDKV_DECODE_SCRATCH_BYTES (64u << 20)
+kv_status_t paged_attention_decode_noalloc(const kv_pool_t* pool, const void* q, kv_dtype_t q_dtype, void* out,
+                                           const int32_t* block_tables, int32_t max_blocks,
+                                           const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
+                                           float scale, int32_t partition_tokens, void* stream);
+
+/* paged_attention_workspace_size -- bytes of workspace paged_attention_decode needs
  * for these arguments (depends on the pool's device, not on lengths). */
 kv_status_t paged_attention_workspace_size(const kv_pool_t* pool, int32_t num_seqs, int32_t num_q_heads,
                                            int32_t max_blocks, int32_t partition_tokens, size_t* bytes);

@@ -1,5 +1,7 @@
 // Host entry points of paged decode attention: argument checks, work split,
 // workspace layout and dispatch to the kernel instantiations.
+#include <mutex>
+
 #include "decode_kernel.h"
 
 namespace {
@@ -59,11 +61,11 @@ extern "C" kv_status_t paged_attention_workspace_size(const kv_pool_t* pool, int
   return KV_OK;
 }
 
-extern "C" kv_status_t paged_attention_decode(const kv_pool_t* pool, const void* q, kv_dtype_t q_dtype, void* out,
-                                              const int32_t* block_tables, int32_t max_blocks,
-                                              const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
-                                              float scale, int32_t partition_tokens, void* workspace,
-                                              size_t workspace_bytes, void* stream) {
+namespace {
+
+kv_status_t decode(const kv_pool_t* pool, const void* q, kv_dtype_t q_dtype, void* out, const int32_t* block_tables,
+                   int32_t max_blocks, const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
+                   float scale, int32_t partition_tokens, void* workspace, size_t workspace_bytes, void* stream) {
   Plan plan;
   kv_status_t st = make_plan(pool, num_seqs, num_q_heads, max_blocks, partition_tokens, &plan);
   if (st != KV_OK) return st;
@@ -124,4 +126,82 @@ extern "C" kv_status_t paged_attention_decode(const kv_pool_t* pool, const void*
     case KV_BF16: return launch_decode_fp8_bf16(p, D, G, mfma, s);
     default: return KV_ERR_UNSUPPORTED;
   }
+}
+
+}  // namespace
+
+extern "C" kv_status_t paged_attention_decode(const kv_pool_t* pool, const void* q, kv_dtype_t q_dtype, void* out,
+                                              const int32_t* block_tables, int32_t max_blocks,
+                                              const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
+                                              float scale, int32_t partition_tokens, void* workspace,
+                                              size_t workspace_bytes, void* stream) {
+  return decode(pool, q, q_dtype, out, block_tables, max_blocks, context_lens, num_seqs, num_q_heads, scale,
+                partition_tokens, workspace, workspace_bytes, stream);
+}
+
+// ------------------------------------------------- allocation-free variant
+//
+// paged_attention_decode_noalloc runs the same kernels with the workspace in
+// this file-scope device array instead of a caller's buffer, for callers that
+// cannot allocate (code under graph capture, tight serving loops).  Every
+// device the library runs on holds its own copy until the process ends.  In
+// host code `scratch` names a host-side stand-in, never the device memory:
+// the device address is fetched once per device with hipGetSymbolAddress and
+// only that address is passed on.
+static __device__ __align__(256) uint8_t scratch[PAGEDKV_DECODE_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch[kMaxDevices];   // device address of `scratch` per device (null: not set up)
+
+__global__ void clear_words_kernel(uint32_t* p, int words) {
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < words; i += gridDim.x * blockDim.x) p[i] = 0u;
+}
+
+// The device address of the pool's device's scratch, set up on first use:
+// the address is looked up with that device current, and the arrival
+// counters at its start are cleared on `stream` (a kernel, not a memset, so
+// a captured first call records no memset).
+kv_status_t device_scratch(const kv_pool_t* pool, hipStream_t stream, void** out) {
+  if (pool->device < 0 || pool->device >= kMaxDevices) return KV_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch[pool->device]) {
+    int cur = -1;
+    if (hipGetDevice(&cur) != hipSuccess) return KV_ERR_HIP;
+    if (cur != pool->device && hipSetDevice(pool->device) != hipSuccess) return KV_ERR_HIP;
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    kv_status_t st = KV_OK;
+    if (e != hipSuccess || !ptr) {
+      st = KV_ERR_HIP;
+    } else {
+      const int words = (int)(kCounterSlots);
+      hipLaunchKernelGGL(clear_words_kernel, dim3(64), dim3(256), 0, stream, (uint32_t*)ptr, words);
+      st = launch_status();
+    }
+    if (cur != pool->device) (void)hipSetDevice(cur);
+    if (st != KV_OK) return st;
+    g_scratch[pool->device] = ptr;
+  }
+  *out = g_scratch[pool->device];
+  return KV_OK;
+}
+
+}  // namespace
+
+extern "C" kv_status_t paged_attention_decode_noalloc(const kv_pool_t* pool, const void* q, kv_dtype_t q_dtype,
+                                                      void* out, const int32_t* block_tables, int32_t max_blocks,
+                                                      const int32_t* context_lens, int32_t num_seqs,
+                                                      int32_t num_q_heads, float scale, int32_t partition_tokens,
+                                                      void* stream) {
+  Plan plan;
+  kv_status_t st = make_plan(pool, num_seqs, num_q_heads, max_blocks, partition_tokens, &plan);
+  if (st != KV_OK) return st;
+  if (plan.bytes > (size_t)PAGEDKV_DECODE_SCRATCH_BYTES) return KV_ERR_WORKSPACE;
+  void* ws = nullptr;
+  if ((st = device_scratch(pool, (hipStream_t)stream, &ws)) != KV_OK) return st;
+  return decode(pool, q, q_dtype, out, block_tables, max_blocks, context_lens, num_seqs, num_q_heads, scale,
+                partition_tokens, ws, PAGEDKV_DECODE_SCRATCH_BYTES, stream);
 }
