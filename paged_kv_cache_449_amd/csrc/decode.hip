@@ -1,19 +1,368 @@
 // Host entry points of paged decode attention: argument checks, work split,
 // workspace layout and dispatch to the kernel instantiations.
+#include <algorithm>
 #include <mutex>
 
 #include "decode_kernel.h"
+
+namespace pkv {
+
+// Lay out the items of every sequence, grouped or flat, and the chunk size;
+// in grouped mode also every item's record rows.  Only the planner's state
+// is written here (each sequence's S-item, each group's G-item, every item's
+// first block in item_pos when it is in LDS); returns ok = false when a
+// grouped layout's records would not fit the workspace.
+struct Layout {
+  int NI, TB, chunk, rounds, flags;
+  int64_t RH;
+  bool ok;
+};
+
+__device__ __attribute__((always_inline)) inline Layout plan_layout(const PlanParams& pp, PlanScratch* scr,
+                                                                    PlanGroup* grp, int* item_pos, bool grouped,
+                                                                    bool has_eq, int* lds) {
+  const int S = pp.num_seqs;
+  const int tid = threadIdx.x;
+  // blocks per kv head first: they fix the chunk size, which the record
+  // rows depend on
+  int TB = 0;
+  for (int base = 0; base < S; base += kPlanThreads) {
+    const int s = base + tid;
+    int nbk = 0;
+    if (s < S) {
+      const SeqItems it = seq_items(scr, grp, pp.log2_bs, s, grouped);
+      nbk = (it.lead ? it.k : 0) + it.suffix;
+    }
+    int tot;
+    plan_scan_sum(nbk, lds, &tot);
+    TB += tot;
+  }
+  const int flags = grouped ? kPlanGrouped : (has_eq ? kPlanShared : 0);
+  const int rounds = (pp.chunk == 0 && (flags & kPlanShared)) ? pp.shared_split : 1;
+  const int64_t T64 = (int64_t)TB * pp.num_kv_heads;
+  const int64_t workers = (int64_t)pp.num_workers * rounds;
+  const int chunk = pp.chunk > 0 ? pp.chunk : (int)max((int64_t)1, (T64 + workers - 1) / workers);
+
+  int icarry = 0, bcarry = 0;
+  int64_t rcarry = 0;
+  for (int base = 0; base < S; base += kPlanThreads) {
+    const int s = base + tid;
+    SeqItems it{false, 0, 0, 0};
+    if (s < S) it = seq_items(scr, grp, pp.log2_bs, s, grouped);
+    // record rows: at most ceil(len / chunk) + 1 pieces, each with the
+    // item's rows (G-item: members x query heads)
+    const int gp = (grouped && it.lead) ? ((it.k + chunk - 1) / chunk + 1) * it.m * pp.G : 0;
+    const int sp = (grouped && it.suffix > 0) ? ((it.suffix + chunk - 1) / chunk + 1) * pp.G : 0;
+    int3 tot;
+    const int3 ex = plan_scan_sum3(make_int3((it.lead ? 1 : 0) + (it.suffix > 0 ? 1 : 0),
+                                             (it.lead ? it.k : 0) + it.suffix, gp + sp), lds, &tot);
+    const int ib = icarry + ex.x, bb = bcarry + ex.y;
+    const int64_t rb = rcarry + ex.z;
+    if (s < S) {
+      PlanScratch* sc = scr + s;
+      if (it.lead) {
+        PlanGroup* g = grp + sc->gid;
+        g->item = ib;
+        g->pos = bb;
+        g->rbase = (int32_t)rb;
+        if (item_pos) item_pos[ib] = bb;
+      }
+      sc->s_item = it.suffix > 0 ? ib + (it.lead ? 1 : 0) : -1;
+      sc->s_pos = bb + (it.lead ? it.k : 0);
+      sc->s_len = it.suffix;
+      sc->s_rbase = (int32_t)(rb + gp);
+      if (item_pos && it.suffix > 0) item_pos[sc->s_item] = sc->s_pos;
+    }
+    icarry += tot.x;
+    bcarry += tot.y;
+    rcarry += tot.z;
+    if (rcarry > ((int64_t)1 << 30)) return Layout{0, 0, 0, 0, 0, 0, false};   // past any workspace
+  }
+  if (grouped && rcarry * pp.num_kv_heads > pp.grec_rows) return Layout{0, 0, 0, 0, 0, 0, false};
+  return Layout{icarry, bcarry, chunk, rounds, flags, rcarry, true};
+}
+
+// The items and each sequence's entry, from the planner's state.
+__device__ __attribute__((always_inline)) inline void plan_write_items(const PlanParams& pp, const PlanScratch* scr,
+                                                                       const PlanGroup* grp, bool grouped) {
+  for (int s = threadIdx.x; s < pp.num_seqs; s += kPlanThreads) {
+    const PlanScratch sc = scr[s];
+    PlanGroup g{0, 0, 0, 0, 0, 0};
+    if (grouped && sc.n > 0) g = grp[sc.gid];
+    const bool member = grouped && sc.n > 0 && real_group(g);
+    if (member && g.first == s)
+      put_item(pp.items + g.item, PlanItem{s, 0, g.k, g.k << pp.log2_bs, g.pos, g.m, g.rbase, 0, 0, 0, 0, 0});
+    if (sc.s_item >= 0) {
+      PlanItem q{s, 0, sc.s_len, sc.n, sc.s_pos, 0, sc.s_rbase, 0, 0, 0, 0, 0};
+      if (member) {
+        q.off = g.k;
+        q.member = s - g.first;
+        q.g_pos = g.pos;
+        q.g_len = g.k;
+        q.g_rbase = g.rbase;
+        q.g_m = g.m;
+      }
+      put_item(pp.items + sc.s_item, q);
+    }
+    *(int4*)(pp.seqs + s) = make_int4(sc.s_item, sc.s_pos, sc.s_len, sc.s_rbase);
+  }
+}
+
+// The descriptors: thread t writes those of a contiguous range of chunk ids,
+// finding the first chunk's item by binary search over the items' first
+// blocks and walking forward from there.  Chunk v of round v / per_round
+// goes to the worker slot whose XCD-ordered id it is (slot b runs on XCD
+// b % 8 and takes id (b % 8) * (per_round / 8) + b / 8 in each round).
+// Slots without a chunk are marked empty.
+__device__ __attribute__((always_inline)) inline void plan_write_descs(const PlanParams& pp, const Layout& L,
+                                                                       const int32_t* posp, int stride) {
+  const int tid = threadIdx.x;
+  const int C = L.chunk, TB = L.TB, W = pp.num_workers;
+  const int T = TB * pp.num_kv_heads;
+  const int nv = (T + C - 1) / C;
+  const int per_round = L.rounds == 1 ? ((nv + 7) & ~7) : W;
+  const int q8 = per_round >> 3;
+  auto pos_of = [&](int i) { return posp[(int64_t)i * stride]; };
+  auto find = [&](int r) {   // the last item whose first block is <= r
+    int lo = 0, hi = L.NI;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (pos_of(mid) <= r) lo = mid; else hi = mid;
+    }
+    return lo;
+  };
+  const int per = (nv + kPlanThreads - 1) / kPlanThreads;
+  int v = tid * per;
+  const int vend = min(v + per, nv);
+  if (v < vend) {
+    const int start = v * C;
+    int h = start / TB, r = start - h * TB;
+    int i = find(r);
+    int rd = v / per_round, u = v - rd * per_round;
+    int uq = u / q8, ur = u - uq * q8;
+    for (;;) {
+      while (i + 1 < L.NI && pos_of(i + 1) <= r) ++i;
+      put_desc(pp.desc + rd * W + ur * 8 + uq, PlanDesc{v, h, i, r - pos_of(i)});
+      if (++v >= vend) break;
+      r += C;
+      if (r >= TB) {   // a later kv head: its items start again from the first
+        while (r >= TB) {
+          r -= TB;
+          ++h;
+        }
+        i = find(r);
+      }
+      if (++ur == q8) {
+        ur = 0;
+        if (++uq == 8) {
+          uq = 0;
+          ++rd;
+        }
+      }
+    }
+  }
+  for (int k = tid; k < L.rounds * W; k += kPlanThreads) {
+    const int rd = k / W, wg = k - rd * W;
+    if (!(wg < per_round && rd * per_round + (wg & 7) * q8 + (wg >> 3) < nv)) put_desc(pp.desc + k, PlanDesc{-1, 0, 0, 0});
+  }
+  if (tid == 0) *pp.header = PlanHeader{C, T, TB, L.NI, L.flags, L.rounds, (int32_t)L.RH, 0};
+}
+
+template <bool IN_LDS>
+__device__ __attribute__((always_inline)) inline void plan_body(const PlanParams& pp, PlanScratch* scr, PlanGroup* grp, int* item_pos, int* lds,
+                                 int* any) {
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int S = pp.num_seqs;
+  const int max_len = pp.max_blocks << pp.log2_bs;
+
+  // A. Lengths, and whether a sequence starts on its predecessor's first
+  //    block (both sequences' lengths and first entries loaded together).
+  bool eq_any = false, empty_any = false;
+  for (int s = tid; s < S; s += kPlanThreads) {
+    const int sp = max(s - 1, 0);
+    const int n = plan_clamp(pp.context_lens[s], max_len);
+    const int np = plan_clamp(pp.context_lens[sp], max_len);
+    const int b0 = pp.block_tables[(int64_t)s * pp.max_blocks];
+    const int bp = pp.block_tables[(int64_t)sp * pp.max_blocks];
+    const bool eq = s > 0 && n > 0 && np > 0 && (uint32_t)b0 < (uint32_t)pp.num_blocks && b0 == bp;
+    scr[s] = PlanScratch{n, eq ? 1 : 0, 0, s, -1, 0, 0, 0};
+    eq_any |= eq;
+    empty_any |= n == 0;
+  }
+  if (eq_any) atomicOr(&any[0], 1);
+  if (empty_any) atomicOr(&any[1], 1);
+  __syncthreads();
+  const bool has_eq = any[0] != 0, has_empty = any[1] != 0;
+  bool grouped = has_eq && pp.max_members >= 2 && (int64_t)pp.num_kv_heads * S <= (int64_t)pp.counter_slots;
+
+  if (grouped) {
+    // B. Leading full blocks shared with the predecessor.  A wave compares
+    //    the two table rows of up to 16 of its sequences at a time, 64
+    //    consecutive entries per row per load (all loads issued together).
+    constexpr int K = 16;
+    for (int s0 = wave; s0 < S; s0 += kPlanWaves * K) {
+      int cap[K], c[K];
+      bool open[K];
+#pragma unroll
+      for (int j = 0; j < K; ++j) {
+        const int s = s0 + j * kPlanWaves;
+        const bool e = s < S && scr[s].eq;
+        cap[j] = e ? min(scr[s].n, scr[s - 1].n) >> pp.log2_bs : 0;
+        c[j] = 0;
+        open[j] = cap[j] > 0;
+      }
+      for (int base = 0;; base += 64) {
+        bool any_open = false;
+#pragma unroll
+        for (int j = 0; j < K; ++j) any_open |= open[j];
+        if (!any_open) break;
+        int x[K], y[K];
+        const int e = base + lane;
+#pragma unroll
+        for (int j = 0; j < K; ++j) {
+          const int s = s0 + j * kPlanWaves;
+          const int32_t* a = pp.block_tables + (int64_t)s * pp.max_blocks;
+          const bool ld = open[j] && e < cap[j];
+          x[j] = ld ? a[e] : 0;
+          y[j] = ld ? a[e - pp.max_blocks] : 0;
+        }
+#pragma unroll
+        for (int j = 0; j < K; ++j) {
+          if (!open[j]) continue;
+          const unsigned long long mism = __ballot(e < cap[j] && x[j] != y[j]);
+          if (mism) {
+            c[j] = base + __builtin_ctzll(mism);
+            open[j] = false;
+          } else if (base + 64 >= cap[j]) {
+            c[j] = cap[j];
+            open[j] = false;
+          }
+        }
+      }
+      if (lane == 0) {
+#pragma unroll
+        for (int j = 0; j < K; ++j) {
+          const int s = s0 + j * kPlanWaves;
+          if (s < S) scr[s].c = c[j];
+        }
+      }
+    }
+    __syncthreads();
+
+    // C. Groups: runs of sequences linked to their predecessor by a shared
+    //    full block, cut every max_members sequences.
+    int run_carry = 0, gid_carry = 0;
+    for (int base = 0; base < S; base += kPlanThreads) {
+      const int s = base + tid;
+      const bool link = s < S && scr[s].c >= 1;
+      int mx;
+      const int run_start = max(run_carry, plan_scan_max(link ? -1 : s, lds, &mx));
+      const bool lead = s < S && ((s - run_start) % pp.max_members) == 0;
+      int nl;
+      const int excl = plan_scan_sum(lead ? 1 : 0, lds, &nl);
+      if (s < S) scr[s].gid = gid_carry + excl - (lead ? 0 : 1);
+      run_carry = max(run_carry, mx);
+      gid_carry += nl;
+    }
+    __syncthreads();
+    // each group's first member gathers its members (at most 15 more)
+    bool real_any = false;
+    for (int s = tid; s < S; s += kPlanThreads) {
+      const int gid = scr[s].gid;
+      if (s > 0 && scr[s - 1].gid == gid) continue;
+      int k = INT32_MAX, m = 1;
+      for (int j = 1; j < pp.max_members && s + j < S; ++j) {
+        const PlanScratch t = scr[s + j];
+        if (t.gid != gid) break;
+        k = min(k, t.c);
+        ++m;
+      }
+      const PlanGroup g{k, m, s, -1, 0, 0};
+      grp[gid] = g;
+      real_any |= real_group(g);
+    }
+    if (tid == 0) any[0] = 0;
+    __syncthreads();
+    if (real_any) atomicOr(&any[0], 1);
+    __syncthreads();
+    grouped = any[0] != 0;   // no group shares a whole block: the flat shared mode
+  }
+
+  // D. Items and the chunk size (grouped records that would not fit the
+  //    workspace: laid out again without groups).
+  Layout L = plan_layout(pp, scr, grp, item_pos, grouped, has_eq, lds);
+  if (!L.ok) {
+    __syncthreads();
+    L = plan_layout(pp, scr, grp, item_pos, false, has_eq, lds);
+  }
+  if (!(L.flags & kPlanGrouped)) L.RH = 0;
+  __syncthreads();   // the planner's state is complete
+
+  // E. The plan itself: items, per-sequence entries, worker descriptors and
+  //    the header.  With the state in LDS nothing written here is read back,
+  //    so no barrier waits for these stores; in the workspace the descriptor
+  //    search reads the items' first blocks from the items.
+  plan_write_items(pp, scr, grp, (L.flags & kPlanGrouped) != 0);
+  if constexpr (!IN_LDS) __syncthreads();
+  plan_write_descs(pp, L, IN_LDS ? item_pos : &pp.items[0].pos,
+                   IN_LDS ? 1 : (int)(sizeof(PlanItem) / sizeof(int32_t)));
+
+  // F. Empty contexts attend to nothing: their output rows are zero.
+  if (has_empty) {
+    for (int s = tid; s < S; s += kPlanThreads) {
+      if (scr[s].n != 0) continue;
+      uint32_t* o = (uint32_t*)(pp.out + (int64_t)s * pp.out_row_bytes);
+      for (int w = 0; w < pp.out_row_bytes / 4; ++w) o[w] = 0u;
+    }
+  }
+}
+
+// One work-group of kPlanThreads threads.  For batches of up to
+// kPlanLdsSeqs sequences the planner's state stays in LDS, so the plan costs
+// one round of length and table-head loads (and, when tables share blocks,
+// one coalesced wave load per 64 table entries compared).
+__global__ __launch_bounds__(kPlanThreads) void paged_decode_plan_kernel(const PlanParams pp) {
+  __shared__ int lds[3 * kPlanWaves];
+  __shared__ int any[2];
+  __shared__ PlanScratch scr_lds[kPlanLdsSeqs];
+  __shared__ PlanGroup grp_lds[kPlanLdsSeqs];
+  __shared__ int pos_lds[kPlanLdsItems];
+  if (threadIdx.x < 2) any[threadIdx.x] = 0;
+  __syncthreads();
+  if (pp.num_seqs <= kPlanLdsSeqs)
+    plan_body<true>(pp, scr_lds, grp_lds, pos_lds, lds, any);
+  else
+    plan_body<false>(pp, pp.scr, pp.groups, nullptr, lds, any);
+}
+
+}  // namespace pkv
 
 namespace {
 
 using namespace pkv;
 
+// Workspace layout of one call: the arrival counters, the launch's plan
+// (worker descriptors, items, per-sequence entries and the planner's
+// scratch), then the partial records.  Flat and grouped plans share the
+// record area; it is sized for the larger.
 struct Plan {
-  int32_t chunk;        // 0 = derived in the kernel
+  int32_t chunk;        // 0 = derived in the planner
   int32_t num_workers;  // multiple of 8
-  size_t counters_bytes;
+  int32_t desc_rounds;  // rounds the descriptor table holds
+  int32_t max_members;  // sequences per group (< 2: no grouping)
+  size_t header_off, desc_off, items_off, seqs_off, scr_off, groups_off, recs_off;
+  int64_t grec_rows;    // record rows a grouped plan may use
   size_t bytes;
 };
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Query groups up to 8 per kv head with a matrix-core operand type can read a
+// shared prefix once for all members of a group (16 query rows per group).
+bool groupable(const kv_pool_t* pool, int G) {
+  return pool->dtype != KV_F32 && pool->log2_block_size >= 4 && pool->decode_mfma && G <= 8;
+}
 
 kv_status_t make_plan(const kv_pool_t* pool, int32_t num_seqs, int32_t num_q_heads, int32_t max_blocks,
                       int32_t partition_tokens, Plan* plan) {
@@ -41,11 +390,36 @@ kv_status_t make_plan(const kv_pool_t* pool, int32_t num_seqs, int32_t num_q_hea
   workers = (workers + 7) & ~7LL;
   // chunks (virtual workers): the library-sized split may cut the stream
   // kSharedSplit times finer when sequences share blocks
-  const int64_t chunks = partition_tokens > 0 ? workers : workers * kSharedSplit;
+  plan->desc_rounds = partition_tokens > 0 ? 1 : kSharedSplit;
+  const int64_t chunks = workers * plan->desc_rounds;
   if (chunks > kCounterSlots) return KV_ERR_INVALID_ARG;
   plan->num_workers = (int32_t)workers;
-  plan->counters_bytes = (size_t)kCounterSlots * sizeof(int32_t);
-  plan->bytes = plan->counters_bytes + (size_t)2 * chunks * G * (pool->head_dim + 4) * sizeof(float);
+  const bool grouping = groupable(pool, G) && (int64_t)pool->num_kv_heads * num_seqs <= kCounterSlots;
+  plan->max_members = grouping ? 16 / G : 0;
+  const size_t S = (size_t)num_seqs;
+  size_t off = (size_t)kCounterSlots * sizeof(int32_t);
+  plan->header_off = off;
+  off = align256(off + sizeof(PlanHeader));
+  plan->desc_off = off;
+  off = align256(off + (size_t)chunks * sizeof(PlanDesc));
+  plan->items_off = off;
+  off = align256(off + (S + S / 2 + 1) * sizeof(PlanItem));
+  plan->seqs_off = off;
+  off = align256(off + (S + 1) * sizeof(PlanSeq));
+  plan->scr_off = off;
+  off = align256(off + (S + 1) * sizeof(PlanScratch));
+  plan->groups_off = off;
+  off = align256(off + (S + 1) * sizeof(PlanGroup));
+  plan->recs_off = off;
+  const size_t row = (size_t)(pool->head_dim + 4) * sizeof(float);
+  const size_t flat = (size_t)2 * chunks * G * row;
+  // record rows of a grouped plan: at most 2 pieces plus one per chunk of
+  // every item, so 4 * Hkv * S * G rows plus 16 per chunk boundary; past
+  // 8192 chunks a grouped plan that does not fit falls back to a flat one
+  plan->grec_rows = grouping ? 4LL * pool->num_kv_heads * num_seqs * G + 16LL * std::min<int64_t>(workers, 8192) : 0;
+  const size_t grouped = (size_t)plan->grec_rows * row;
+  plan->bytes = off + std::max(flat, grouped);
+  if (!grouping) plan->grec_rows = 0;
   return KV_OK;
 }
 
@@ -78,7 +452,24 @@ kv_status_t decode(const kv_pool_t* pool, const void* q, kv_dtype_t q_dtype, voi
 
   const int D = pool->head_dim;
   const int G = num_q_heads / pool->num_kv_heads;
-  DecodeParams p;
+  const bool fp8 = pool->dtype == KV_FP8_E4M3FN;
+  // dtype pairs: q in the pool dtype, or f32/f16/bf16 q over an fp8 pool
+  if (fp8 ? q_dtype == KV_FP8_E4M3FN : q_dtype != pool->dtype) return KV_ERR_UNSUPPORTED;
+  // pairs with a 16-bit matrix-core operand type
+  const bool pair_mfma = (pool->dtype == KV_BF16 && q_dtype == KV_BF16) ||
+                         (pool->dtype == KV_F16 && q_dtype == KV_F16) ||
+                         (fp8 && (q_dtype == KV_BF16 || q_dtype == KV_F16));
+  // Query groups (G > 1) run on the matrix cores where the dtype pair has a
+  // 16-bit operand type and blocks hold whole 16-token tiles, unless the
+  // pool was made with PAGEDKV_DECODE_MFMA=0.
+  const bool mfma = G > 1 && pool->decode_mfma;
+  // 16 query rows per kv head only on the matrix cores
+  if (G == 16 && !(mfma && pair_mfma && pool->log2_block_size >= 4)) return KV_ERR_UNSUPPORTED;
+  // a wave load covers 64 / (lanes per token row) tokens of one block
+  const int lanes_per_row = D * (int)elem_bytes(pool->dtype) / 16;
+  if (64 / lanes_per_row > pool->block_size) return KV_ERR_UNSUPPORTED;
+
+  DecodeParams p{};
   p.k_pool = (const uint8_t*)pool->k;
   p.v_pool = (const uint8_t*)pool->v;
   p.q = (const uint8_t*)q;
@@ -87,8 +478,13 @@ kv_status_t decode(const kv_pool_t* pool, const void* q, kv_dtype_t q_dtype, voi
   p.context_lens = context_lens;
   p.query_start = nullptr;
   p.total_q = 0;
-  p.counters = (int32_t*)workspace;
-  p.partials = (float*)((uint8_t*)workspace + plan.counters_bytes);
+  uint8_t* ws = (uint8_t*)workspace;
+  p.counters = (int32_t*)ws;
+  p.partials = (float*)(ws + plan.recs_off);
+  p.header = (const PlanHeader*)(ws + plan.header_off);
+  p.desc = (const PlanDesc*)(ws + plan.desc_off);
+  p.items = (const PlanItem*)(ws + plan.items_off);
+  p.pseqs = (const PlanSeq*)(ws + plan.seqs_off);
   p.num_seqs = num_seqs;
   p.num_kv_heads = pool->num_kv_heads;
   p.max_blocks = max_blocks;
@@ -96,21 +492,38 @@ kv_status_t decode(const kv_pool_t* pool, const void* q, kv_dtype_t q_dtype, voi
   p.log2_bs = pool->log2_block_size;
   p.chunk = plan.chunk;
   p.num_workers = plan.num_workers;
-  const bool fp8 = pool->dtype == KV_FP8_E4M3FN;
   p.q_scale = scale * kLog2e * (fp8 ? pool->k_scale : 1.0f);
   p.v_scale = fp8 ? pool->v_scale : 1.0f;
   p.qk_scale = scale * kLog2e;
   p.head_scales = fp8 && pool->per_head ? pool->head_scales : nullptr;
 
-  // a wave load covers 64 / (lanes per token row) tokens of one block
-  const int lanes_per_row = D * (int)elem_bytes(pool->dtype) / 16;
-  if (64 / lanes_per_row > pool->block_size) return KV_ERR_UNSUPPORTED;
-
   hipStream_t s = (hipStream_t)stream;
-  // Query groups (G > 1) run on the matrix cores where the dtype pair has a
-  // 16-bit operand type and blocks hold whole 16-token tiles, unless the
-  // pool was made with PAGEDKV_DECODE_MFMA=0.
-  const bool mfma = G > 1 && pool->decode_mfma;
+  PlanParams pp;
+  pp.block_tables = block_tables;
+  pp.context_lens = context_lens;
+  pp.out = (uint8_t*)out;
+  pp.scr = (PlanScratch*)(ws + plan.scr_off);
+  pp.groups = (PlanGroup*)(ws + plan.groups_off);
+  pp.items = (PlanItem*)(ws + plan.items_off);
+  pp.seqs = (PlanSeq*)(ws + plan.seqs_off);
+  pp.desc = (PlanDesc*)(ws + plan.desc_off);
+  pp.header = (PlanHeader*)(ws + plan.header_off);
+  pp.grec_rows = plan.grec_rows;
+  pp.num_seqs = num_seqs;
+  pp.num_kv_heads = pool->num_kv_heads;
+  pp.max_blocks = max_blocks;
+  pp.num_blocks = pool->num_blocks;
+  pp.log2_bs = pool->log2_block_size;
+  pp.G = G;
+  pp.out_row_bytes = (int32_t)((size_t)num_q_heads * D * elem_bytes(q_dtype));
+  pp.chunk = plan.chunk;
+  pp.num_workers = plan.num_workers;
+  pp.desc_rounds = plan.desc_rounds;
+  pp.max_members = pair_mfma ? plan.max_members : 0;   // groups run on the matrix cores
+  pp.shared_split = kSharedSplit;
+  pp.counter_slots = kCounterSlots;
+  hipLaunchKernelGGL(paged_decode_plan_kernel, dim3(1), dim3(kPlanThreads), 0, s, pp);
+  if (launch_status() != KV_OK) return KV_ERR_HIP;
   if (!fp8) {
     if (q_dtype != pool->dtype) return KV_ERR_UNSUPPORTED;
     switch (pool->dtype) {

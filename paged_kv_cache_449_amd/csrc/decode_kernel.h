@@ -35,6 +35,7 @@
 #include <type_traits>
 
 #include "common.h"
+#include "decode_plan.h"
 
 namespace pkv {
 
@@ -80,6 +81,11 @@ struct DecodeParams {
   float v_scale;
   const float* head_scales;  // fp8 per-kv-head scales [2][num_kv_heads] (k then v), or null
   float qk_scale;            // softmax scale * log2(e) (per-head scales multiply it)
+  // decode: the launch's work plan (written by paged_decode_plan_kernel)
+  const PlanHeader* header;  // what every worker of the launch shares
+  const PlanDesc* desc;      // [rounds][num_workers]
+  const PlanItem* items;     // items of a kv head's stream
+  const PlanSeq* pseqs;      // [num_seqs], grouped mode
 };
 
 // Scales a run of kv head h uses: the per-tensor ones, or head h's.
@@ -268,6 +274,11 @@ template <int D, int G>
 __device__ inline RecordRef record_ref(const float* rec) {
   return {__builtin_amdgcn_make_buffer_rsrc((void*)rec, (short)0, G * (D + 4) * 4, kBufferWord3)};
 }
+// a record of `rows` rows (rows known at run time)
+template <int D>
+__device__ inline RecordRef record_ref_rows(const float* rec, int rows) {
+  return {__builtin_amdgcn_make_buffer_rsrc((void*)rec, (short)0, rows * (D + 4) * 4, kBufferWord3)};
+}
 // store floats [i, i+4) of the record (i a multiple of 4)
 __device__ inline void record_store4(const RecordRef& r, int i, float a, float b, float c, float d) {
   const uint4 v = make_uint4(__float_as_uint(a), __float_as_uint(b), __float_as_uint(c), __float_as_uint(d));
@@ -316,21 +327,21 @@ struct ContiguousRows {   // G query heads of one sequence: rows orow + j*D
   __device__ int64_t operator()(int j) const { return orow + (int64_t)j * d; }
 };
 
-// Merge the records of workers first_w..last_w (in worker order, so results
-// are reproducible) into the out rows that `rows` names, then clear the run's
-// counter for the next call.  seg_start is the run's first position in the
-// flattened stream.  Each of the NT threads owns 4 consecutive elements of
-// [G][D] per pass.
+// Merge `count` partial records -- record c starts at rec_at(c) and holds
+// G rows of [D + 4] floats -- in the order c = 0, 1, ... (results are
+// reproducible) into the out rows that `rows` names, then clear the
+// arrival counter `ctr` for the next call.  Each of the NT threads owns 4
+// consecutive elements of [G][D] per pass.
 //
 // The records are read through the coherence point, a full memory round
-// trip each, so they are fetched in batches of B workers with every load of
-// a batch (all passes) issued before any is used: a run split over up to B
-// workers costs one round trip.  Within a batch the weights are taken
-// against the batch's maximum; a later batch with a larger maximum rescales
-// what is summed so far.
-template <typename QT, int D, int G, typename Rows, int NT = 64>
-__device__ inline void merge_records(const DecodeParams& p, int first_w, int last_w, int seg_start, int chunk,
-                                     const Rows& rows, float v_scale) {
+// trip each, so they are fetched in batches of B records with every load of
+// a batch (all passes) issued before any is used: up to B records cost one
+// round trip.  Within a batch the weights are taken against the batch's
+// maximum; a later batch with a larger maximum rescales what is summed so
+// far.
+template <typename QT, int D, int G, typename RecAt, typename Rows, int NT = 64>
+__device__ inline void merge_list(const DecodeParams& p, int count, const RecAt& rec_at, const Rows& rows,
+                                  float v_scale, int32_t* ctr) {
   constexpr int REC = D + 4;
   constexpr int QE = elem_size<QT>::value;
   static_assert(D % 4 == 0, "record layout");
@@ -343,12 +354,12 @@ __device__ inline void merge_records(const DecodeParams& p, int first_w, int las
     lsum[q] = 0.0f;
     o[q][0] = o[q][1] = o[q][2] = o[q][3] = 0.0f;
   }
-  for (int v0 = first_w; v0 <= last_w; v0 += B) {
+  for (int c0 = 0; c0 < count; c0 += B) {
     float4 ml[B][PASSES], a[B][PASSES];
 #pragma unroll
     for (int b = 0; b < B; ++b) {
-      const int v = min(v0 + b, last_w);   // past the run: a repeat, not used
-      const RecordRef r = record_ref<D, G>(p.partials + (int64_t)(2 * v + (v * chunk >= seg_start ? 0 : 1)) * G * REC);
+      const int c = min(c0 + b, count - 1);   // past the list: a repeat, not used
+      const RecordRef r = record_ref<D, G>(rec_at(c));
 #pragma unroll
       for (int q = 0; q < PASSES; ++q) {
         const int e0 = min((int)threadIdx.x * 4 + q * 4 * NT, G * D - 4);
@@ -362,7 +373,7 @@ __device__ inline void merge_records(const DecodeParams& p, int first_w, int las
       float mb = -INFINITY;
 #pragma unroll
       for (int b = 0; b < B; ++b)
-        if (v0 + b <= last_w) mb = fmaxf(mb, ml[b][q].x);
+        if (c0 + b < count) mb = fmaxf(mb, ml[b][q].x);
       const float mn = fmaxf(M[q], mb);
       if (mn > M[q] && M[q] != -INFINITY) {   // rescale the earlier batches
         const float r = fexp2(M[q] - mn);
@@ -373,7 +384,7 @@ __device__ inline void merge_records(const DecodeParams& p, int first_w, int las
       const float mu = mn == -INFINITY ? 0.0f : mn;
 #pragma unroll
       for (int b = 0; b < B; ++b) {
-        if (v0 + b > last_w) continue;
+        if (c0 + b >= count) continue;
         const float f = fexp2(ml[b][q].x - mu);
         lsum[q] = fmaf(f, ml[b][q].y, lsum[q]);
         o[q][0] = fmaf(f, a[b][q].x, o[q][0]);
@@ -392,7 +403,20 @@ __device__ inline void merge_records(const DecodeParams& p, int first_w, int las
     if (orow < 0) continue;
     store_row<QT, 4>(p.out + (orow + d) * QE, o[q], lsum[q] > 0.0f ? v_scale / lsum[q] : 0.0f);
   }
-  if (threadIdx.x == 0) __hip_atomic_store(p.counters + first_w, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (threadIdx.x == 0) __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Merge the records of workers first_w..last_w (in worker order) of a run
+// whose first position in the flattened stream is seg_start.
+template <typename QT, int D, int G, typename Rows, int NT = 64>
+__device__ inline void merge_records(const DecodeParams& p, int first_w, int last_w, int seg_start, int chunk,
+                                     const Rows& rows, float v_scale) {
+  auto rec_at = [&](int c) {
+    const int v = first_w + c;
+    return (const float*)p.partials + (int64_t)(2 * v + (v * chunk >= seg_start ? 0 : 1)) * G * (D + 4);
+  };
+  merge_list<QT, D, G, decltype(rec_at), Rows, NT>(p, last_w - first_w + 1, rec_at, rows, v_scale,
+                                                   p.counters + first_w);
 }
 
 // Table window: lane i holds the physical block of logical block wb + i of
@@ -460,21 +484,21 @@ __device__ inline void valu_stream(const DecodeParams& p, int s, int h, int off,
 
 }
 
-// One run on the vector ALUs: blocks [off, off+len) of the (kv head h,
-// sequence s) stream, which has nb blocks and n tokens.  pos is the run's
-// place in the flattened stream and wstart the worker's first block.  All
-// scalars are uniform.
+// The state of one run on the vector ALUs: the G query rows of sequence s
+// served by kv head h, over blocks [off, off+len) of its n tokens.  On return
+// every row group of the wave holds the merged (m, l, acc) of the run, in
+// log2 units, lane col holding elements [col*VEC, (col+1)*VEC).  All scalars
+// are uniform.
 template <typename KV, typename QT, int D, int G, int POL>
-__device__ inline void valu_run(const DecodeParams& p, int w, int chunk, int wstart, int pos, int s, int h,
-                                int off, int len, int n, int nb) {
+__device__ inline void valu_core(const DecodeParams& p, int s, int h, int off, int len, int n, float (&m)[G],
+                                 float (&l)[G], float (&acc)[G][DecodeShape<KV, D>::VEC]) {
   using Sh = DecodeShape<KV, D>;
-  constexpr int VEC = Sh::VEC, L = Sh::L, REC = Sh::REC;
+  constexpr int VEC = Sh::VEC, L = Sh::L;
   constexpr int QE = elem_size<QT>::value;
   const int lane = threadIdx.x;
-  const int row = lane / L;
   const int col = lane % L;
   const int Hq = p.num_kv_heads * G;
-  const float qs = run_q_scale(p, h), vs = run_v_scale(p, h);
+  const float qs = run_q_scale(p, h);
   const int tab = load_table_window(p, run_table(p, s, off), 0, len);
 
   // query rows of the G heads served by kv head h, pre-scaled into log2 units
@@ -489,7 +513,6 @@ __device__ inline void valu_run(const DecodeParams& p, int w, int chunk, int wst
     }
   }
 
-  float m[G], l[G], acc[G][VEC];
 #pragma unroll
   for (int g = 0; g < G; ++g) {
     m[g] = -INFINITY;
@@ -516,20 +539,17 @@ __device__ inline void valu_run(const DecodeParams& p, int w, int chunk, int wst
       m[g] = mn;
     }
   }
+}
 
-  const int64_t oe = ((int64_t)s * Hq + (int64_t)h * G) * D + (int64_t)col * VEC;
-  if (off == 0 && off + len == nb) {   // the whole run is ours
-    if (row == 0) {
-#pragma unroll
-      for (int g = 0; g < G; ++g)
-        store_row<QT, VEC>(p.out + (oe + (int64_t)g * D) * QE, acc[g], l[g] > 0.0f ? vs / l[g] : 0.0f);
-    }
-    return;
-  }
-
-  // Partial: publish (acc, m, l) through the device coherence point; the
-  // worker that completes the run's count merges.
-  const RecordRef rec = record_ref<D, G>(partial_record<D, G>(p, w, wstart, pos));
+// Store a vector-ALU run's state as a partial record (row group 0 writes).
+template <typename KV, int D, int G>
+__device__ inline void valu_store_record(const RecordRef& rec, const float (&m)[G], const float (&l)[G],
+                                         const float (&acc)[G][DecodeShape<KV, D>::VEC]) {
+  using Sh = DecodeShape<KV, D>;
+  constexpr int VEC = Sh::VEC, L = Sh::L, REC = Sh::REC;
+  const int lane = threadIdx.x;
+  const int row = lane / L;
+  const int col = lane % L;
   if (row == 0) {
 #pragma unroll
     for (int g = 0; g < G; ++g) {
@@ -539,6 +559,50 @@ __device__ inline void valu_run(const DecodeParams& p, int w, int chunk, int wst
       if (col == 0) record_store4(rec, g * REC + D, m[g], l[g], 0.0f, 0.0f);
     }
   }
+}
+
+// Write a vector-ALU run's state as the output rows of sequence s (row
+// group 0 writes).
+template <typename KV, typename QT, int D, int G>
+__device__ inline void valu_store_out(const DecodeParams& p, int s, int h, float vs, const float (&l)[G],
+                                      const float (&acc)[G][DecodeShape<KV, D>::VEC]) {
+  using Sh = DecodeShape<KV, D>;
+  constexpr int VEC = Sh::VEC, L = Sh::L;
+  constexpr int QE = elem_size<QT>::value;
+  const int lane = threadIdx.x;
+  const int row = lane / L;
+  const int col = lane % L;
+  const int Hq = p.num_kv_heads * G;
+  const int64_t oe = ((int64_t)s * Hq + (int64_t)h * G) * D + (int64_t)col * VEC;
+  if (row == 0) {
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+      store_row<QT, VEC>(p.out + (oe + (int64_t)g * D) * QE, acc[g], l[g] > 0.0f ? vs / l[g] : 0.0f);
+  }
+}
+
+// One run on the vector ALUs: blocks [off, off+len) of the (kv head h,
+// sequence s) stream, which has nb blocks and n tokens.  pos is the run's
+// place in the flattened stream and wstart the worker's first block.  All
+// scalars are uniform.
+template <typename KV, typename QT, int D, int G, int POL>
+__device__ inline void valu_run(const DecodeParams& p, int w, int chunk, int wstart, int pos, int s, int h,
+                                int off, int len, int n, int nb) {
+  using Sh = DecodeShape<KV, D>;
+  constexpr int VEC = Sh::VEC;
+  const int Hq = p.num_kv_heads * G;
+  float m[G], l[G], acc[G][VEC];
+  valu_core<KV, QT, D, G, POL>(p, s, h, off, len, n, m, l, acc);
+  const float vs = run_v_scale(p, h);
+
+  if (off == 0 && off + len == nb) {   // the whole run is ours
+    valu_store_out<KV, QT, D, G>(p, s, h, vs, l, acc);
+    return;
+  }
+
+  // Partial: publish (acc, m, l) through the device coherence point; the
+  // worker that completes the run's count merges.
+  valu_store_record<KV, D, G>(record_ref<D, G>(partial_record<D, G>(p, w, wstart, pos)), m, l, acc);
   const int seg_start = pos - off;
   const int first_w = seg_start / chunk;
   const int last_w = (seg_start + nb - 1) / chunk;
@@ -550,158 +614,70 @@ __device__ inline void valu_run(const DecodeParams& p, int w, int chunk, int wst
 }  // namespace pkv
 
 #include "decode_mfma.h"
+#include "decode_items.h"
 
 namespace pkv {
 
-// Stream chunk v: blocks [v*chunk, (v+1)*chunk) of the flattened
-// (kv head, sequence, block) stream, which has `total` blocks per kv head
-// and T in all.
+// Stream chunk d.v: blocks [v*chunk, (v+1)*chunk) of the flat (kv head,
+// sequence, block) stream, whose items are the non-empty sequences.
 template <typename KV, typename QT, int D, int G, bool MFMA, int POL>
-__device__ inline void decode_chunk(const DecodeParams& p, int v, int chunk, int T, int total) {
-  const int lane = threadIdx.x;
-  const int S = p.num_seqs;
-  const int bs = 1 << p.log2_bs;
-  const int max_len = p.max_blocks << p.log2_bs;
-  const int start = v * chunk;
-  if (start >= T) return;
-  const int end = min(start + chunk, T);
-  int h = start / total;
-  const int r = start - h * total;
-
-  // the sequence whose run contains block r of kv head h
-  int s = 0, pre = 0;
-  bool found = false;
-  {
-    int carry = 0;
-    for (int base = 0; base < S && !found; base += 4 * 64) {
-      int nl[4];   // four slices' lengths loaded together
-#pragma unroll
-      for (int k = 0; k < 4; ++k) nl[k] = p.context_lens[min(base + 64 * k + lane, S - 1)];
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        if (found) break;
-        const int sl = base + 64 * k + lane;
-        const int nb = sl < S ? (clamp_len(nl[k], max_len) + bs - 1) >> p.log2_bs : 0;
-        const int incl = wave_inclusive_scan_i32(nb, lane);
-        const int excl = carry + incl - nb;
-        const unsigned long long hit = __ballot(nb > 0 && excl <= r && r < excl + nb);
-        if (hit) {
-          const int src = __builtin_ctzll(hit);
-          s = base + 64 * k + src;
-          pre = __shfl(excl, src);
-          found = true;
-        }
-        carry += __shfl(incl, 63);
-      }
-    }
-  }
-
-  if (!found) return;  // lengths changed under the launch: nothing consistent to do
-  s = uniform(s);
-  int off = uniform(r - pre);
-  int pos = start;
-  int n = uniform(clamp_len(p.context_lens[s], max_len));
-  int nb = (n + bs - 1) >> p.log2_bs;
+__device__ inline void decode_chunk(const DecodeParams& p, const ChunkCtx& d) {
+  const int chunk = d.chunk;
+  const int start = d.v * chunk;
+  const int end = min(start + chunk, d.T);
+  int h = d.h, i = d.i, off = d.off, pos = start;
+  PlanItem it = load_item(p.items + i);
   while (true) {
-    const int len = min(nb - off, end - pos);
+    const int len = min(it.len - off, end - pos);
+    // the next run's item loads while this run streams
+    int ni = i + 1, nh = h;
+    if (ni == d.NI) {
+      ni = 0;
+      ++nh;
+    }
+    const bool more = pos + len < end;
+    const PlanItem nx = load_item(p.items + (more ? ni : i));
     if constexpr (MFMA)
-      mfma_run<KV, QT, D, G, POL>(p, v, chunk, start, pos, s, h, off, len, n, nb);
+      mfma_run<KV, QT, D, G, POL>(p, d.v, chunk, start, pos, it.s, h, off, len, it.n, it.len);
     else
-      valu_run<KV, QT, D, G, POL>(p, v, chunk, start, pos, s, h, off, len, n, nb);
+      valu_run<KV, QT, D, G, POL>(p, d.v, chunk, start, pos, it.s, h, off, len, it.n, it.len);
     pos += len;
-    if (pos >= end) break;
-    do {
-      if (++s == S) {
-        s = 0;
-        if (++h == p.num_kv_heads) return;
-      }
-      n = uniform(clamp_len(p.context_lens[s], max_len));
-      nb = (n + bs - 1) >> p.log2_bs;
-    } while (nb == 0);
+    if (!more) break;
+    i = ni;
+    h = nh;
+    it = nx;
     off = 0;
   }
 }
 
 // One worker wavefront per work-group.  MFMA selects the matrix-core run
 // (query groups with a 16-bit operand type) over the vector-ALU run.  The
-// fp8 matrix-core run with up to 4 query heads per kv head fits 168 VGPRs
+// matrix-core runs with up to 4 query heads per kv head fit 168 VGPRs
 // without spilling, which leaves room for 3 waves per SIMD: launches with
 // more work-groups than worker slots (fixed-size partitions) gain 2% from
-// the third wave on MI355X.
+// the third wave on MI355X for fp8.
+//
+// The plan kernel, run just before on the same stream, gives each worker
+// one descriptor per round: the chunk it streams and where that chunk
+// starts.  Grouped plans (shared prefixes read once per group) run where the
+// dtype pair has a matrix-core operand type.
 template <typename KV, typename QT, int D, int G, bool MFMA>
 __global__ __launch_bounds__(64)
-__attribute__((amdgpu_waves_per_eu(MFMA && D <= 128 ? (sizeof(KV) == 1 && G <= 4 ? 3 : 2) : 1)))
+__attribute__((amdgpu_waves_per_eu(MFMA && D <= 128 ? (G <= 4 ? 3 : 2) : 1)))
 void paged_decode_kernel(const DecodeParams p) {
-  const int lane = threadIdx.x;
-  const int S = p.num_seqs;
-  const int bs = 1 << p.log2_bs;
-  const int max_len = p.max_blocks << p.log2_bs;
-
-  // Blocks per kv head; whether some sequence is empty; whether some
-  // sequence starts with the same physical block as its predecessor
-  // (copy-on-write candidates sharing a prompt).
-  // Every worker computes these before streaming, so the loads of four
-  // 64-sequence slices are issued together (one memory round trip per 256
-  // sequences; entries past S repeat the last sequence and are not used).
-  int total = 0;
-  bool empty = false, shared = false;
-  for (int base = 0; base < S; base += 4 * 64) {
-    int nl[4], npl[4], b0[4], bp[4];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int sc = min(base + 64 * k + lane, S - 1), sp = max(sc - 1, 0);
-      nl[k] = p.context_lens[sc];
-      npl[k] = p.context_lens[sp];
-      b0[k] = p.block_tables[(int64_t)sc * p.max_blocks];
-      bp[k] = p.block_tables[(int64_t)sp * p.max_blocks];
+  constexpr bool kGroupable = !std::is_void<typename mfma_operand<KV, QT>::type>::value && G <= 8;
+  const PlanHeader H = load_header(p.header);
+  const PlanDesc* dp = p.desc + blockIdx.x;
+  for (int rd = 0; rd < H.rounds; ++rd) {
+    const ChunkCtx d = chunk_ctx(H, load_desc(dp + (int64_t)rd * p.num_workers));
+    if (d.v < 0) continue;
+    if (d.flags & kPlanGrouped) {
+      if constexpr (kGroupable) grouped_chunk<KV, QT, D, G, MFMA>(p, d);
+    } else if (d.flags & kPlanShared) {
+      decode_chunk<KV, QT, D, G, MFMA, kSharedPolicy>(p, d);
+    } else {
+      decode_chunk<KV, QT, D, G, MFMA, kStreamPolicy>(p, d);
     }
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int s = base + 64 * k + lane;
-      int nb = 0;
-      if (s < S) {
-        const int n = clamp_len(nl[k], max_len);
-        nb = (n + bs - 1) >> p.log2_bs;
-        empty |= n == 0;
-        if (s > 0 && n > 0 && clamp_len(npl[k], max_len) > 0)
-          shared |= (uint32_t)b0[k] < (uint32_t)p.num_blocks && b0[k] == bp[k];
-      }
-      total += wave_sum_i32(nb);
-    }
-  }
-  total = uniform(total);
-  const bool any_shared = __ballot(shared) != 0;
-
-  if (blockIdx.x == 0 && __ballot(empty)) {
-    // empty contexts attend to nothing: their rows are zero
-    constexpr int QE = elem_size<QT>::value;
-    const int Hq = p.num_kv_heads * G;
-    for (int s = 0; s < S; ++s) {
-      if (clamp_len(p.context_lens[s], max_len) != 0) continue;
-      uint8_t* o = p.out + (int64_t)s * Hq * D * QE;
-      for (int i = lane * 4; i < Hq * D * QE; i += 256) *(uint32_t*)(o + i) = 0u;
-    }
-  }
-
-  // The stream of T blocks is cut into chunks of `chunk` blocks, one per
-  // virtual worker v (records and counters are indexed by v).  Work-group b
-  // takes one chunk per round; in every round the ids are spread over the 8
-  // XCDs (work-group b runs on XCD b % 8 and takes id
-  // round_base + (b % 8) * (per_round / 8) + b / 8), so each XCD holds one
-  // contiguous range of the stream and neighbouring runs share its L2.
-  const int T = total * p.num_kv_heads;
-  const int rounds = (p.chunk == 0 && any_shared) ? kSharedSplit : 1;
-  const int chunk = p.chunk > 0 ? p.chunk : max(1, (T + p.num_workers * rounds - 1) / (p.num_workers * rounds));
-  const int nv = (T + chunk - 1) / chunk;                               // chunks with blocks
-  const int per_round = rounds == 1 ? ((nv + 7) & ~7) : p.num_workers;  // <= num_workers
-  if ((int)blockIdx.x >= per_round) return;
-  for (int rd = 0; rd < rounds; ++rd) {
-    const int v = rd * per_round + (int)(blockIdx.x & 7) * (per_round >> 3) + (int)(blockIdx.x >> 3);
-    if (v >= nv) continue;
-    if (any_shared)
-      decode_chunk<KV, QT, D, G, MFMA, kSharedPolicy>(p, v, chunk, T, total);
-    else
-      decode_chunk<KV, QT, D, G, MFMA, kStreamPolicy>(p, v, chunk, T, total);
   }
 }
 

@@ -148,6 +148,22 @@ struct MfmaStep {
   MfmaTileRegs<KV, D> t[TPS];
 };
 
+// LDS staging of a matrix-core run's tiles (V as the operand type, K as
+// loaded).  One pair of arrays per (dtype, head dim), shared by every run of
+// a kernel whatever its cache policy: the runs of a one-wave work-group
+// follow one another.
+template <typename KV, int D>
+struct MfmaStage {
+  __device__ static uint8_t* v() {
+    __shared__ __attribute__((aligned(16))) uint8_t a[MfmaStep<KV, D>::TPS * 16 * MfmaShape<KV, D>::LSTRIDE];
+    return a;
+  }
+  __device__ static uint8_t* k() {
+    __shared__ __attribute__((aligned(16))) uint8_t a[MfmaStep<KV, D>::TPS * 16 * MfmaShape<KV, D>::KSTRIDE];
+    return a;
+  }
+};
+
 // Lazy rescaling: a run's reference max moves only when a row's max passes
 // it by more than this (log2 units), so weights stay below 2^8 and the
 // accumulator is rescaled rarely rather than at every tile.
@@ -221,23 +237,26 @@ struct MfmaRow {
 // PART runs (whole runs only) leave each valid row's unnormalised state
 // (acc[D], reference max, sum) as record row.part of p.partials instead of
 // writing out, for a later kernel to continue.
-template <typename KV, typename QT, int D, int R, int POL, typename Rows, bool PART = false>
-__device__ inline void mfma_rows_run(const DecodeParams& p, int w, int chunk, int wstart, int pos, int s, int h,
-                                     int off, int len, int n, int nb, const MfmaRow& row, const Rows& rows) {
+//
+// mfma_rows_core runs the stream and leaves the run's state: lane (kg, j16)
+// holds acc[dt] = O[j16][16 dt + 4kg + i], i = 0..3 (unnormalised), the
+// row's reference max m (log2 units) and its whole running sum l.
+template <typename KV, typename QT, int D, int POL>
+__device__ inline void mfma_rows_core(const DecodeParams& p, int s, int h, int off, int len, int n,
+                                      const MfmaRow& row, f32x4 (&acc)[MfmaShape<KV, D>::DT], float& m, float& l) {
   using MT = typename mfma_operand<KV, QT>::type;
   using Ops = mfma_ops<MT>;
   using Sh = MfmaShape<KV, D>;
-  static_assert(R >= 1 && R <= 16, "query rows");
   constexpr int KS = Sh::KS, DT = Sh::DT, LSTRIDE = Sh::LSTRIDE;
   constexpr int TPS = MfmaStep<KV, D>::TPS;
   constexpr int QE = elem_size<QT>::value;
-  __shared__ __attribute__((aligned(16))) uint8_t vlds[TPS * 16 * LSTRIDE];
-  __shared__ __attribute__((aligned(16))) uint8_t klds[TPS * 16 * Sh::KSTRIDE];
+  uint8_t* vlds = MfmaStage<KV, D>::v();
+  uint8_t* klds = MfmaStage<KV, D>::k();
 
   const int lane = threadIdx.x;
   const int j16 = lane & 15;   // token row (QK A) / query row (B, D)
   const int kg = lane >> 4;    // k group
-  const float qs = run_q_scale(p, h), vs = run_v_scale(p, h);
+  const float qs = run_q_scale(p, h);
 
   // q operand: lane (kg, j) holds q row j at dims kg*D/4 + 8st .. +8 for step st
   uint4 qop[KS];
@@ -249,11 +268,10 @@ __device__ inline void mfma_rows_run(const DecodeParams& p, int w, int chunk, in
     for (int st = 0; st < KS; ++st) qop[st] = *(const uint4*)(p.q + (qe + st * 8) * QE);
   }
 
-  f32x4 acc[DT];
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-  float m = -INFINITY;   // reference max of row j16 (log2 units)
-  float l = 0.0f;        // this lane's share of the running sum
+  m = -INFINITY;   // reference max of row j16 (log2 units)
+  l = 0.0f;        // this lane's share of the running sum, until the end
 
   RunCtx c;
   const int64_t tile = (int64_t)Sh::ROW << p.log2_bs;
@@ -421,6 +439,22 @@ __device__ inline void mfma_rows_run(const DecodeParams& p, int w, int chunk, in
   // total sum of row j16 over the four k groups
   l += __shfl_xor(l, 16);
   l += __shfl_xor(l, 32);
+}
+
+template <typename KV, typename QT, int D, int R, int POL, typename Rows, bool PART = false>
+__device__ inline void mfma_rows_run(const DecodeParams& p, int w, int chunk, int wstart, int pos, int s, int h,
+                                     int off, int len, int n, int nb, const MfmaRow& row, const Rows& rows) {
+  using Sh = MfmaShape<KV, D>;
+  static_assert(R >= 1 && R <= 16, "query rows");
+  constexpr int DT = Sh::DT;
+  constexpr int QE = elem_size<QT>::value;
+  const int lane = threadIdx.x;
+  const int j16 = lane & 15;
+  const int kg = lane >> 4;
+  f32x4 acc[DT];
+  float m, l;
+  mfma_rows_core<KV, QT, D, POL>(p, s, h, off, len, n, row, acc, m, l);
+  const float vs = run_v_scale(p, h);
 
   // lane (kg, j16) holds O[j16][16 dt + 4kg + i], i = 0..3
   if constexpr (PART) {

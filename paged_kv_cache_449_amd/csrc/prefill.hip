@@ -96,7 +96,7 @@ extern "C" kv_status_t paged_attention_prefill(const kv_pool_t* pool, const void
     workers = (int32_t)((units + 7) & ~7LL);
   }
 
-  DecodeParams p;
+  DecodeParams p{};
   p.k_pool = (const uint8_t*)pool->k;
   p.v_pool = (const uint8_t*)pool->v;
   p.q = (const uint8_t*)q;

@@ -1,0 +1,85 @@
+"""paged_attention_decode with its launch plan (the plan kernel's items,
+worker descriptors and, where tables share a prefix, groups read once on the
+matrix cores): outputs against the oracle's decode, which knows nothing of
+plans or groups.
+
+Covers forked candidates of every shape family (MHA and query groups, 16-bit
+and fp8, block sizes 16 and 32, groups cut to the 16-row limit), the
+library-sized split and fixed 16- and 64-token runs, batches above the
+planner's 1024-sequence LDS capacity (state in the workspace), mixed batches
+of forked and independent sequences with empty ones, and bitwise
+reproducibility ("vLLM — 把操作系统的分页搬进 GPU KV cache": core mechanism 3
+and case 2 for the sharing; core mechanisms for the table walk)."""
+import numpy as np
+import pytest
+
+import workloads as W
+from oracle.run import OracleRun, check_close
+from test_gpu_grouped import CASES
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("pt", [0, 16, 64])
+@pytest.mark.parametrize("name", list(CASES))
+def test_plain_decode_of_shared_prefixes(name, pt):
+    from gpu_harness import run_gpu
+    wl = CASES[name]
+    if pt % wl.block_size:
+        pytest.skip("runs are whole blocks")
+    got = run_gpu(wl, partition_tokens=pt)
+    ref = OracleRun(wl)
+    assert np.isfinite(got["out"]).all()
+    check_close(got["out"], ref.decode(), wl.kv_dtype)
+
+
+def _forked(name, index, prompts, n, hq=4, hkv=2, kv="f16", q="f16", bs=16):
+    parent = [p for p in range(len(prompts)) for _ in range(n)]
+    return W._make(name, index, hq, hkv, 128, kv, q, bs, prompt_lens=prompts, parent=parent)
+
+
+LARGE = {
+    # above the planner's LDS capacity: its per-sequence state lives in the workspace
+    "flat_1100_bf16": W._make("flat_1100_bf16", 60, 2, 2, 128, "bf16", "bf16", 16,
+                              ctx_lens=(np.random.default_rng(60).integers(1, 120, size=1100)).tolist()),
+    "forked_1100_f16": _forked("forked_1100_f16", 61, [16 + (7 * i) % 90 for i in range(275)], 4),
+    "forked_1100_fp8_gqa": _forked("forked_1100_fp8_gqa", 62, [40 + (5 * i) % 60 for i in range(275)], 4,
+                                   hq=8, hkv=2, kv="fp8e4m3", q="bf16"),
+}
+
+
+@pytest.mark.parametrize("pt", [0, 32])
+@pytest.mark.parametrize("name", list(LARGE))
+def test_batches_past_the_planner_lds(name, pt):
+    from gpu_harness import run_gpu
+    wl = LARGE[name]
+    got = run_gpu(wl, partition_tokens=pt)
+    check_close(got["out"], OracleRun(wl).decode(), wl.kv_dtype)
+
+
+def test_mixed_batch_with_empty_contexts():
+    """Forked groups between independent sequences, some contexts empty:
+    empty rows are zero, the rest match the oracle."""
+    import torch
+    from gpu_harness import announce, run_gpu
+    wl = _forked("mixed_f16", 63, [95, 30, 200, 17, 64, 5], 3)
+    announce("mixed batch with empty contexts")
+    got = run_gpu(wl)
+    sess, q = got["session"], got["q"]
+    lens = sess.context_lens.clone()
+    empty = [1, 7, 8, 17]
+    lens[empty] = 0
+    out = __import__("paged_kv_cache_449_amd").paged_attention_decode(sess.pool, q, sess.block_tables, lens, wl.scale)
+    torch.cuda.synchronize()
+    got2 = out.float().cpu().double().numpy()
+    assert not got2[empty].any()
+    keep = [s for s in range(wl.num_seqs) if s not in empty]
+    check_close(got2[keep], OracleRun(wl).decode()[keep], wl.kv_dtype)
+
+
+@pytest.mark.parametrize("name", ["c4s_cow_f16", "gqa4_fp8", "many_groups_f16"])
+def test_grouped_plans_are_bitwise_reproducible(name):
+    from gpu_harness import run_gpu
+    got = run_gpu(CASES[name], partition_tokens=16, repeat=3)
+    for o in got["outs"][1:]:
+        assert np.array_equal(o, got["outs"][0])
