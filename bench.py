@@ -554,12 +554,16 @@ def decode_summary(name: str, dev, steps: int, warmup: int) -> dict:
     def one_step(ev=None):
         pk.copy_blocks(pool, sess.pairs)
         pk.reshape_and_cache(pool, kn, vn, sess.slot_mapping)
-        if ev is not None:
-            ev[0].record()
-        pk.paged_attention_decode(pool, q, sess.block_tables, sess.context_lens, wl.scale, out=out,
-                                  partition_tokens=pt)
-        if ev is not None:
-            ev[1].record()
+        if ev is None:
+            pk.paged_attention_decode(pool, q, sess.block_tables, sess.context_lens, wl.scale, out=out,
+                                      partition_tokens=pt)
+            return
+        ev[0].record()
+        ws = pk.paged_attention_plan(pool, q, sess.block_tables, sess.context_lens, partition_tokens=pt)
+        ev[1].record()
+        pk.paged_attention_decode_planned(pool, q, sess.block_tables, sess.context_lens, wl.scale, ws, out=out,
+                                          partition_tokens=pt)
+        ev[2].record()
 
     for _ in range(warmup):
         one_step()
@@ -569,11 +573,12 @@ def decode_summary(name: str, dev, steps: int, warmup: int) -> dict:
         one_step()
     torch.cuda.synchronize(dev)
     step_us = (time.perf_counter() - t0) * 1e6 / steps
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(steps)]
     for e in evs:
         one_step(e)
     torch.cuda.synchronize(dev)
-    us = np.array([a.elapsed_time(b) for a, b in evs]) * 1e3
+    us = np.array([b.elapsed_time(c) for a, b, c in evs]) * 1e3
+    plan_us = np.array([a.elapsed_time(b) for a, b, c in evs]) * 1e3
     nb = unique_bytes(wl, sess) if sess.shared_blocks > 0 else decode_bytes(wl)
     logical = decode_bytes(wl)
     achieved = nb["total"] / (float(us.mean()) / 1e6) / 1e9
@@ -584,8 +589,12 @@ def decode_summary(name: str, dev, steps: int, warmup: int) -> dict:
            "bytes_counted": "unique (each shared block once)" if sess.shared_blocks > 0 else "algorithmic",
            "achieved": round(achieved, 1), "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
            "kv_gbs_per_step": round(nb["kv"] / (step_us / 1e6) / 1e9, 1),
-           "logical_gbs": round(logical["total"] / (float(us.mean()) / 1e6) / 1e9, 1)}
-    print(f"[bench] {wl.name}: decode {us.mean():.1f} us, frac {res['frac']}", file=sys.stderr, flush=True)
+           "logical_gbs": round(logical["total"] / (float(us.mean()) / 1e6) / 1e9, 1),
+           "plan_us": round(float(plan_us.mean()), 2),
+           "call_us": round(float((plan_us + us).mean()), 2),
+           "call_frac": round(nb["total"] / (float((plan_us + us).mean()) / 1e6) / 1e9 / HBM_PEAK_GBS, 4)}
+    print(f"[bench] {wl.name}: decode kernel {us.mean():.1f} us, frac {res['frac']}; plan kernel "
+          f"{plan_us.mean():.1f} us, call frac {res['call_frac']}", file=sys.stderr, flush=True)
     del sess, q, kn, vn, out, pool
     torch.cuda.empty_cache()
     return res
@@ -686,11 +695,18 @@ def main(argv=None) -> int:
         elif args.grouped:
             pk.paged_attention_decode_grouped(pool, q, sess.block_tables, sess.context_lens, wl.scale,
                                               sess.group_start, sess.group_shared, out=out)
+        elif ev is not None and len(ev) == 3:
+            # the two halves of the call, so the decode kernel is timed on its
+            # own: ev[0]..ev[1] the plan kernel, ev[1]..ev[2] the decode kernel
+            ws = pk.paged_attention_plan(pool, q, sess.block_tables, sess.context_lens, partition_tokens=pt)
+            ev[1].record()
+            pk.paged_attention_decode_planned(pool, q, sess.block_tables, sess.context_lens, wl.scale, ws, out=out,
+                                              partition_tokens=pt)
         else:
             pk.paged_attention_decode(pool, q, sess.block_tables, sess.context_lens, wl.scale, out=out,
                                       partition_tokens=pt)
         if ev is not None:
-            ev[1].record()
+            ev[-1].record()
 
     if args.calibrate_copy:
         # an elementwise kernel that reads 1 GiB and writes 1 GiB (a plain
@@ -745,14 +761,17 @@ def main(argv=None) -> int:
 
     # 2. The kernel time: K more steps with HIP events around each launch,
     #    recorded on the stream the library launches on.
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    split = not (multi or args.grouped)   # flat decode: plan and decode kernels timed apart
+    nev = 3 if split else 2
+    evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(nev)) for _ in range(args.steps)]
     wevs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     torch.cuda.synchronize(dev)
     for i in range(args.steps):
         flush()
         one_step(evs[i], wevs[i])
     torch.cuda.synchronize(dev)
-    dec_ms = np.array([a.elapsed_time(b) for a, b in evs])
+    dec_ms = np.array([e[-2].elapsed_time(e[-1]) for e in evs])
+    plan_ms = np.array([e[0].elapsed_time(e[1]) for e in evs]) if split else None
     writes = write_kernels(wl, sess, pool, wevs)
     if multi:
         res = multi_token_result(wl, args, dec_ms, step_ms)
@@ -778,7 +797,8 @@ def main(argv=None) -> int:
     logical_total = logical["total"]
     achieved = nb["total"] / dec_mean_s / 1e9
     print(f"[bench] decode kernel mean {dec_ms.mean() * 1e3:.1f} us (min {dec_ms.min() * 1e3:.1f}, "
-          f"max {dec_ms.max() * 1e3:.1f}); step {step_ms * 1e3:.1f} us", file=sys.stderr, flush=True)
+          f"max {dec_ms.max() * 1e3:.1f}); step {step_ms * 1e3:.1f} us"
+          + (f"; plan kernel {plan_ms.mean() * 1e3:.1f} us" if split else ""), file=sys.stderr, flush=True)
 
     res = {
         "metric": METRIC,
@@ -814,19 +834,26 @@ def main(argv=None) -> int:
                      "bytes_per_launch": nb["total"],
                      "logical_gbs": round(logical_total / dec_mean_s / 1e9, 1)},
     }
+    if split:
+        # the whole paged_attention_decode call: the plan kernel, then the
+        # decode kernel (a serving step plans once for all its layers)
+        call_s = float((plan_ms + dec_ms).mean()) / 1e3
+        res["roofline"]["plan_kernel"] = "paged_decode_plan_kernel"
+        res["roofline"]["plan_us"] = round(float(plan_ms.mean()) * 1e3, 2)
+        res["roofline"]["call_us"] = round(call_s * 1e6, 2)
+        res["roofline"]["call_frac"] = round(nb["total"] / call_s / 1e9 / HBM_PEAK_GBS, 4)
     if args.flush == "none" and not args.graph:
         # 3. The serving-realistic cache state: a 512 MiB write before each
         #    step (the layer's own projections write just before decode), so
         #    dirty lines drain while the decode kernel reads.
         scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
-        fevs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                for _ in range(args.steps)]
+        fevs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(nev)) for _ in range(args.steps)]
         torch.cuda.synchronize(dev)
         for i in range(args.steps):
             scratch.zero_()
             one_step(fevs[i])
         torch.cuda.synchronize(dev)
-        fus = np.array([a.elapsed_time(b) for a, b in fevs]) * 1e3
+        fus = np.array([e[-2].elapsed_time(e[-1]) for e in fevs]) * 1e3
         fach = nb["total"] / (float(fus.mean()) / 1e6) / 1e9
         res["roofline"]["flush_write"] = {"what": "512 MiB written before every step, outside the events",
                                           "kernel_us": round(float(fus.mean()), 2),

@@ -188,16 +188,29 @@ kv_status_t reshape_and_cache(kv_pool_t* pool, const void* k_new, const void* v_
  * queries, block_size >= 16, matrix cores not switched off):
  * KV_ERR_UNSUPPORTED otherwise.
  *
+ * Two kernels run on `stream`: a one-work-group plan kernel
+ * (paged_attention_plan below) and the decode kernel.
+ *
  * Work split: the cached tokens of all (kv head, sequence) pairs are laid end
  * to end and cut into equal runs of whole blocks, one per worker wavefront,
  * so long and short sequences cost the same per token.  partition_tokens == 0
- * lets the library size the runs from the device's compute-unit count (four
- * times finer when some sequence starts with the same physical block as the
- * one before it, so candidates sharing a prompt's blocks are read at the same
- * time); otherwise each run is partition_tokens tokens (a multiple of
- * block_size).  A sequence cut into several runs is merged in the same launch
- * by the worker that finishes last (log-sum-exp merge of the partial results,
- * in a fixed order, so results are bitwise reproducible).  Query groups
+ * lets the library size the runs from the device's compute-unit count;
+ * otherwise each run is partition_tokens tokens (a multiple of block_size).
+ * A sequence cut into several runs is merged in the same launch by the
+ * worker that finishes last (log-sum-exp merge of the partial results, in a
+ * fixed order, so results are bitwise reproducible).
+ *
+ * Shared prefixes: consecutive sequences whose table rows start with the
+ * same whole blocks (candidates forked from one prompt, "vLLM — 把操作系统的
+ * 分页搬进 GPU KV cache": core mechanism 3 and case 2) form groups of up to 16
+ * query rows (16 / (num_q_heads / num_kv_heads) sequences); each group's
+ * common full blocks are read once, on the matrix cores, for every member,
+ * and each member's own blocks separately.  This needs a 16-bit operand type
+ * (bf16 or f16 queries), block_size >= 16, at most 8 query heads per kv head
+ * and num_kv_heads * num_seqs <= 65536; otherwise, or when no group holds a
+ * whole shared block, the blocks are read per sequence with the default
+ * cache policy and a four times finer split, so candidates meet in the L2.
+ * Query groups
  * (num_q_heads > num_kv_heads) with a 16-bit operand type (bf16 or f16
  * queries) and block_size >= 16 run on the matrix cores (unless the pool
  * was made with PAGEDKV_DECODE_MFMA=0).
@@ -210,12 +223,49 @@ kv_status_t reshape_and_cache(kv_pool_t* pool, const void* k_new, const void* v_
  * bytes, 256-byte aligned.  Its first 256 KiB hold arrival counters and must
  * be zero before the first use; every completed call leaves them zero again,
  * so one workspace serves calls of any shape without clearing.  The rest holds
- * partial results.  Calls sharing a workspace must not overlap.
+ * the launch plan and partial results.  Calls sharing a workspace must not
+ * overlap.
  */
 kv_status_t paged_attention_decode(const kv_pool_t* pool, const void* q, kv_dtype_t q_dtype, void* out,
                                    const int32_t* block_tables, int32_t max_blocks, const int32_t* context_lens,
                                    int32_t num_seqs, int32_t num_q_heads, float scale, int32_t partition_tokens,
                                    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * paged_attention_plan, paged_attention_decode_planned -- the two halves of
+ * paged_attention_decode, for callers that decode many times over the same
+ * tables: every layer of a model in one serving step reads its own pool
+ * through the same block tables and context lengths ("vLLM KV Cache 实现机制"
+ * §1.2: one block table per sequence, shared by all layers' caches).
+ *
+ * paged_attention_plan enqueues the plan kernel: one work-group reads the
+ * lengths and table heads (and compares the rows of sequences that start on
+ * the same block), and writes the launch plan into `workspace` -- the runs of
+ * blocks the stream is made of, where every worker's share starts, and the
+ * groups of sequences whose shared prefix is read once.  It depends only on
+ * the tables, the lengths, the shapes and q_dtype; no q, out or scale.
+ *
+ * paged_attention_decode_planned enqueues the decode kernel alone, using the
+ * plan in `workspace`.  Preconditions (not checked): a paged_attention_plan
+ * call made earlier on the same stream (or ordered before this one) wrote it
+ * with the same block_tables, max_blocks, context_lens, num_seqs,
+ * num_q_heads, partition_tokens and q_dtype, for a pool of the same shape
+ * (num_blocks, block_size, num_kv_heads, head_dim, dtype, matrix-core
+ * setting); the tables and lengths have not changed since; and no other call
+ * has used the workspace in between.  Any number of planned decodes may
+ * follow one plan, on different pools of that shape and different q, out
+ * and scale.  Same workspace size and arguments as paged_attention_decode;
+ * the result is bitwise the same.
+ */
+kv_status_t paged_attention_plan(const kv_pool_t* pool, kv_dtype_t q_dtype, const int32_t* block_tables,
+                                 int32_t max_blocks, const int32_t* context_lens, int32_t num_seqs,
+                                 int32_t num_q_heads, int32_t partition_tokens, void* workspace,
+                                 size_t workspace_bytes, void* stream);
+kv_status_t paged_attention_decode_planned(const kv_pool_t* pool, const void* q, kv_dtype_t q_dtype, void* out,
+                                           const int32_t* block_tables, int32_t max_blocks,
+                                           const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
+                                           float scale, int32_t partition_tokens, void* workspace,
+                                           size_t workspace_bytes, void* stream);
 
 /*
  * paged_attention_decode_noalloc -- paged_attention_decode for callers that

@@ -60,6 +60,9 @@ def lib() -> ctypes.CDLL:
         L.paged_attention_decode.argtypes = [vp, vp, ctypes.c_int, vp, vp, i32, vp, i32, i32, f32, i32, vp, sz, vp]
         L.paged_attention_workspace_size.argtypes = [vp, i32, i32, i32, i32, ctypes.POINTER(sz)]
         L.paged_attention_decode_noalloc.argtypes = [vp, vp, ctypes.c_int, vp, vp, i32, vp, i32, i32, f32, i32, vp]
+        L.paged_attention_plan.argtypes = [vp, ctypes.c_int, vp, i32, vp, i32, i32, i32, vp, sz, vp]
+        L.paged_attention_decode_planned.argtypes = [vp, vp, ctypes.c_int, vp, vp, i32, vp, i32, i32, f32, i32, vp,
+                                                     sz, vp]
         L.copy_blocks.argtypes = [vp, vp, i32, vp]
         L.swap_blocks.argtypes = [vp, vp, vp, i64, vp, i32, ctypes.c_int, vp]
         L.paged_attention_prefill.argtypes = [vp, vp, ctypes.c_int, vp, vp, i32, vp, vp, i32, i32, i32, f32, vp,
@@ -93,7 +96,7 @@ def lib() -> ctypes.CDLL:
         for fn in ("kv_pool_create", "kv_pool_create_from", "kv_pool_destroy", "kv_pool_info", "kv_pool_set_scales",
                    "kv_pool_set_head_scales",
                    "reshape_and_cache", "paged_attention_decode", "paged_attention_workspace_size", "copy_blocks",
-                   "paged_attention_decode_noalloc",
+                   "paged_attention_decode_noalloc", "paged_attention_plan", "paged_attention_decode_planned",
                    "swap_blocks", "paged_attention_prefill", "paged_attention_prefill_workspace_size",
                    "paged_attention_decode_grouped", "paged_attention_decode_grouped_workspace_size",
                    "kv_stream_read"):
@@ -464,4 +467,56 @@ def paged_attention_decode_noalloc(pool: KVPool, q: torch.Tensor, block_tables: 
                                                 block_tables.shape[1], _dev_ptr(context_lens, "context_lens", d), S,
                                                 Hq, float(scale), partition_tokens, _stream(d, stream)),
            "paged_attention_decode_noalloc")
+    return out
+
+
+def _decode_args(pool: KVPool, q, block_tables, context_lens):
+    if q.dim() != 3 or q.shape[2] != pool.head_dim or q.dtype not in DTYPE_CODE:
+        raise ValueError(f"q must be [S][Hq][{pool.head_dim}] of a supported dtype")
+    S = q.shape[0]
+    if block_tables.dtype != torch.int32 or block_tables.dim() != 2 or block_tables.shape[0] != S:
+        raise ValueError("block_tables must be int32 [S][max_blocks]")
+    if context_lens.dtype != torch.int32 or context_lens.shape != (S,):
+        raise ValueError("context_lens must be int32 [S]")
+
+
+def paged_attention_plan(pool: KVPool, q: torch.Tensor, block_tables: torch.Tensor, context_lens: torch.Tensor,
+                         partition_tokens: int = 0, workspace: Optional[torch.Tensor] = None,
+                         stream=None) -> torch.Tensor:
+    """Write the launch plan of a decode over these tables into `workspace`
+    (returned); q supplies only the shape and dtype."""
+    _decode_args(pool, q, block_tables, context_lens)
+    S, Hq = q.shape[0], q.shape[1]
+    need = paged_attention_workspace_size(pool, S, Hq, block_tables.shape[1], partition_tokens)
+    if workspace is None:
+        workspace = pool.workspace(need)
+    d = pool.device
+    _check(lib().paged_attention_plan(pool.handle, DTYPE_CODE[q.dtype], _dev_ptr(block_tables, "block_tables", d),
+                                      block_tables.shape[1], _dev_ptr(context_lens, "context_lens", d), S, Hq,
+                                      partition_tokens, _dev_ptr(workspace, "workspace", d),
+                                      workspace.numel() * workspace.element_size(), _stream(d, stream)),
+           "paged_attention_plan")
+    return workspace
+
+
+def paged_attention_decode_planned(pool: KVPool, q: torch.Tensor, block_tables: torch.Tensor,
+                                   context_lens: torch.Tensor, scale: float, workspace: torch.Tensor,
+                                   out: Optional[torch.Tensor] = None, partition_tokens: int = 0,
+                                   stream=None) -> torch.Tensor:
+    """The decode kernel alone, over the plan paged_attention_plan wrote into
+    `workspace` for the same tables, lengths, shapes and split."""
+    _decode_args(pool, q, block_tables, context_lens)
+    S, Hq = q.shape[0], q.shape[1]
+    if out is None:
+        out = torch.empty_like(q)
+    elif out.shape != q.shape or out.dtype != q.dtype:
+        raise ValueError("out must match q")
+    d = pool.device
+    _check(lib().paged_attention_decode_planned(pool.handle, _dev_ptr(q, "q", d), DTYPE_CODE[q.dtype],
+                                                _dev_ptr(out, "out", d), _dev_ptr(block_tables, "block_tables", d),
+                                                block_tables.shape[1], _dev_ptr(context_lens, "context_lens", d), S,
+                                                Hq, float(scale), partition_tokens,
+                                                _dev_ptr(workspace, "workspace", d),
+                                                workspace.numel() * workspace.element_size(), _stream(d, stream)),
+           "paged_attention_decode_planned")
     return out

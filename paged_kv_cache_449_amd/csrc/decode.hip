@@ -297,6 +297,7 @@ __device__ __attribute__((always_inline)) inline void plan_body(const PlanParams
     L = plan_layout(pp, scr, grp, item_pos, false, has_eq, lds);
   }
   if (!(L.flags & kPlanGrouped)) L.RH = 0;
+  if (has_empty) L.flags |= kPlanEmpty;
   __syncthreads();   // the planner's state is complete
 
   // E. The plan itself: items, per-sequence entries, worker descriptors and
@@ -308,14 +309,6 @@ __device__ __attribute__((always_inline)) inline void plan_body(const PlanParams
   plan_write_descs(pp, L, IN_LDS ? item_pos : &pp.items[0].pos,
                    IN_LDS ? 1 : (int)(sizeof(PlanItem) / sizeof(int32_t)));
 
-  // F. Empty contexts attend to nothing: their output rows are zero.
-  if (has_empty) {
-    for (int s = tid; s < S; s += kPlanThreads) {
-      if (scr[s].n != 0) continue;
-      uint32_t* o = (uint32_t*)(pp.out + (int64_t)s * pp.out_row_bytes);
-      for (int w = 0; w < pp.out_row_bytes / 4; ++w) o[w] = 0u;
-    }
-  }
 }
 
 // One work-group of kPlanThreads threads.  For batches of up to
@@ -437,17 +430,24 @@ extern "C" kv_status_t paged_attention_workspace_size(const kv_pool_t* pool, int
 
 namespace {
 
+// Which kernels a call enqueues: the planner, the decode kernel, or both.
+enum Stage { kPlanAndRun, kPlanOnly, kRunOnly };
+
 kv_status_t decode(const kv_pool_t* pool, const void* q, kv_dtype_t q_dtype, void* out, const int32_t* block_tables,
                    int32_t max_blocks, const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
-                   float scale, int32_t partition_tokens, void* workspace, size_t workspace_bytes, void* stream) {
+                   float scale, int32_t partition_tokens, void* workspace, size_t workspace_bytes, void* stream,
+                   Stage stage) {
   Plan plan;
   kv_status_t st = make_plan(pool, num_seqs, num_q_heads, max_blocks, partition_tokens, &plan);
   if (st != KV_OK) return st;
   if (!valid_dtype(q_dtype)) return KV_ERR_INVALID_ARG;
   if (num_seqs == 0) return KV_OK;
-  if (!q || !out || !block_tables || !context_lens) return KV_ERR_INVALID_ARG;
-  if ((((uintptr_t)q) | ((uintptr_t)out)) & 15) return KV_ERR_INVALID_ARG;
-  if (!(scale == scale) || scale > 3.0e38f || scale < -3.0e38f) return KV_ERR_INVALID_ARG;
+  if (!block_tables || !context_lens) return KV_ERR_INVALID_ARG;
+  if (stage != kPlanOnly) {
+    if (!q || !out) return KV_ERR_INVALID_ARG;
+    if ((((uintptr_t)q) | ((uintptr_t)out)) & 15) return KV_ERR_INVALID_ARG;
+    if (!(scale == scale) || scale > 3.0e38f || scale < -3.0e38f) return KV_ERR_INVALID_ARG;
+  }
   if (!workspace || workspace_bytes < plan.bytes || ((uintptr_t)workspace & 255)) return KV_ERR_WORKSPACE;
 
   const int D = pool->head_dim;
@@ -498,32 +498,33 @@ kv_status_t decode(const kv_pool_t* pool, const void* q, kv_dtype_t q_dtype, voi
   p.head_scales = fp8 && pool->per_head ? pool->head_scales : nullptr;
 
   hipStream_t s = (hipStream_t)stream;
-  PlanParams pp;
-  pp.block_tables = block_tables;
-  pp.context_lens = context_lens;
-  pp.out = (uint8_t*)out;
-  pp.scr = (PlanScratch*)(ws + plan.scr_off);
-  pp.groups = (PlanGroup*)(ws + plan.groups_off);
-  pp.items = (PlanItem*)(ws + plan.items_off);
-  pp.seqs = (PlanSeq*)(ws + plan.seqs_off);
-  pp.desc = (PlanDesc*)(ws + plan.desc_off);
-  pp.header = (PlanHeader*)(ws + plan.header_off);
-  pp.grec_rows = plan.grec_rows;
-  pp.num_seqs = num_seqs;
-  pp.num_kv_heads = pool->num_kv_heads;
-  pp.max_blocks = max_blocks;
-  pp.num_blocks = pool->num_blocks;
-  pp.log2_bs = pool->log2_block_size;
-  pp.G = G;
-  pp.out_row_bytes = (int32_t)((size_t)num_q_heads * D * elem_bytes(q_dtype));
-  pp.chunk = plan.chunk;
-  pp.num_workers = plan.num_workers;
-  pp.desc_rounds = plan.desc_rounds;
-  pp.max_members = pair_mfma ? plan.max_members : 0;   // groups run on the matrix cores
-  pp.shared_split = kSharedSplit;
-  pp.counter_slots = kCounterSlots;
-  hipLaunchKernelGGL(paged_decode_plan_kernel, dim3(1), dim3(kPlanThreads), 0, s, pp);
-  if (launch_status() != KV_OK) return KV_ERR_HIP;
+  if (stage != kRunOnly) {
+    PlanParams pp;
+    pp.block_tables = block_tables;
+    pp.context_lens = context_lens;
+    pp.scr = (PlanScratch*)(ws + plan.scr_off);
+    pp.groups = (PlanGroup*)(ws + plan.groups_off);
+    pp.items = (PlanItem*)(ws + plan.items_off);
+    pp.seqs = (PlanSeq*)(ws + plan.seqs_off);
+    pp.desc = (PlanDesc*)(ws + plan.desc_off);
+    pp.header = (PlanHeader*)(ws + plan.header_off);
+    pp.grec_rows = plan.grec_rows;
+    pp.num_seqs = num_seqs;
+    pp.num_kv_heads = pool->num_kv_heads;
+    pp.max_blocks = max_blocks;
+    pp.num_blocks = pool->num_blocks;
+    pp.log2_bs = pool->log2_block_size;
+    pp.G = G;
+    pp.chunk = plan.chunk;
+    pp.num_workers = plan.num_workers;
+    pp.desc_rounds = plan.desc_rounds;
+    pp.max_members = pair_mfma ? plan.max_members : 0;   // groups run on the matrix cores
+    pp.shared_split = kSharedSplit;
+    pp.counter_slots = kCounterSlots;
+    hipLaunchKernelGGL(paged_decode_plan_kernel, dim3(1), dim3(kPlanThreads), 0, s, pp);
+    if (launch_status() != KV_OK) return KV_ERR_HIP;
+  }
+  if (stage == kPlanOnly) return KV_OK;
   if (!fp8) {
     if (q_dtype != pool->dtype) return KV_ERR_UNSUPPORTED;
     switch (pool->dtype) {
@@ -549,7 +550,24 @@ extern "C" kv_status_t paged_attention_decode(const kv_pool_t* pool, const void*
                                               float scale, int32_t partition_tokens, void* workspace,
                                               size_t workspace_bytes, void* stream) {
   return decode(pool, q, q_dtype, out, block_tables, max_blocks, context_lens, num_seqs, num_q_heads, scale,
-                partition_tokens, workspace, workspace_bytes, stream);
+                partition_tokens, workspace, workspace_bytes, stream, kPlanAndRun);
+}
+
+extern "C" kv_status_t paged_attention_plan(const kv_pool_t* pool, kv_dtype_t q_dtype, const int32_t* block_tables,
+                                            int32_t max_blocks, const int32_t* context_lens, int32_t num_seqs,
+                                            int32_t num_q_heads, int32_t partition_tokens, void* workspace,
+                                            size_t workspace_bytes, void* stream) {
+  return decode(pool, nullptr, q_dtype, nullptr, block_tables, max_blocks, context_lens, num_seqs, num_q_heads, 1.0f,
+                partition_tokens, workspace, workspace_bytes, stream, kPlanOnly);
+}
+
+extern "C" kv_status_t paged_attention_decode_planned(const kv_pool_t* pool, const void* q, kv_dtype_t q_dtype,
+                                                      void* out, const int32_t* block_tables, int32_t max_blocks,
+                                                      const int32_t* context_lens, int32_t num_seqs,
+                                                      int32_t num_q_heads, float scale, int32_t partition_tokens,
+                                                      void* workspace, size_t workspace_bytes, void* stream) {
+  return decode(pool, q, q_dtype, out, block_tables, max_blocks, context_lens, num_seqs, num_q_heads, scale,
+                partition_tokens, workspace, workspace_bytes, stream, kRunOnly);
 }
 
 // ------------------------------------------------- allocation-free variant
@@ -616,5 +634,5 @@ extern "C" kv_status_t paged_attention_decode_noalloc(const kv_pool_t* pool, con
   void* ws = nullptr;
   if ((st = device_scratch(pool, (hipStream_t)stream, &ws)) != KV_OK) return st;
   return decode(pool, q, q_dtype, out, block_tables, max_blocks, context_lens, num_seqs, num_q_heads, scale,
-                partition_tokens, ws, PAGEDKV_DECODE_SCRATCH_BYTES, stream);
+                partition_tokens, ws, PAGEDKV_DECODE_SCRATCH_BYTES, stream, kPlanAndRun);
 }

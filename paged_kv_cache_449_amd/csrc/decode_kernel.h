@@ -661,12 +661,33 @@ __device__ inline void decode_chunk(const DecodeParams& p, const ChunkCtx& d) {
 // one descriptor per round: the chunk it streams and where that chunk
 // starts.  Grouped plans (shared prefixes read once per group) run where the
 // dtype pair has a matrix-core operand type.
+// Empty contexts attend to nothing: their output rows are zero.  The first
+// worker checks 64 lengths per load and clears the rows of the empty ones.
+template <typename QT, int D, int G>
+__device__ inline void zero_empty_rows(const DecodeParams& p) {
+  constexpr int QE = elem_size<QT>::value;
+  const int lane = threadIdx.x;
+  const int words = p.num_kv_heads * G * D * QE / 4;
+  for (int base = 0; base < p.num_seqs; base += 64) {
+    const int s = base + lane;
+    const bool empty = s < p.num_seqs && p.context_lens[s] <= 0;
+    unsigned long long mask = __ballot(empty);
+    while (mask) {
+      const int e = base + __builtin_ctzll(mask);
+      mask &= mask - 1;
+      uint32_t* o = (uint32_t*)(p.out + (int64_t)e * words * 4);
+      for (int w = lane; w < words; w += 64) o[w] = 0u;
+    }
+  }
+}
+
 template <typename KV, typename QT, int D, int G, bool MFMA>
 __global__ __launch_bounds__(64)
 __attribute__((amdgpu_waves_per_eu(MFMA && D <= 128 ? (G <= 4 ? 3 : 2) : 1)))
 void paged_decode_kernel(const DecodeParams p) {
   constexpr bool kGroupable = !std::is_void<typename mfma_operand<KV, QT>::type>::value && G <= 8;
   const PlanHeader H = load_header(p.header);
+  if ((H.flags & kPlanEmpty) && blockIdx.x == 0) zero_empty_rows<QT, D, G>(p);
   const PlanDesc* dp = p.desc + blockIdx.x;
   for (int rd = 0; rd < H.rounds; ++rd) {
     const ChunkCtx d = chunk_ctx(H, load_desc(dp + (int64_t)rd * p.num_workers));

@@ -74,7 +74,7 @@ struct PlanHeader {
   int32_t T;       // blocks in the stream (all kv heads)
   int32_t TB;      // blocks per kv head
   int32_t NI;      // items per kv head
-  int32_t flags;   // kPlanShared | kPlanGrouped
+  int32_t flags;   // kPlanShared | kPlanGrouped | kPlanEmpty
   int32_t rounds;  // chunks per worker
   int32_t RH;      // grouped mode: record rows per kv head
   int32_t pad;
@@ -92,6 +92,8 @@ struct ChunkCtx {
 constexpr int kPlanShared = 1;
 // Grouped mode: G-items read shared prefixes once per group.
 constexpr int kPlanGrouped = 2;
+// Some context is empty: the decode kernel zeroes those output rows.
+constexpr int kPlanEmpty = 4;
 
 // Per-sequence state of the planner (32 bytes).
 struct PlanScratch {
@@ -118,7 +120,6 @@ struct PlanGroup {
 struct PlanParams {
   const int32_t* block_tables;
   const int32_t* context_lens;
-  uint8_t* out;              // rows of empty contexts are zeroed here
   PlanScratch* scr;          // [num_seqs] (batches past the LDS capacity)
   PlanGroup* groups;         // [num_seqs] (same)
   PlanItem* items;           // [3 * num_seqs / 2 + 1]
@@ -132,7 +133,6 @@ struct PlanParams {
   int32_t num_blocks;
   int32_t log2_bs;
   int32_t G;                 // query heads per kv head
-  int32_t out_row_bytes;     // bytes of one sequence's output rows (all query heads)
   int32_t chunk;             // blocks per chunk; 0 = sized from num_workers
   int32_t num_workers;       // decode work-groups launched (multiple of 8)
   int32_t desc_rounds;       // rounds the descriptor table holds (1, or kSharedSplit)

@@ -83,3 +83,61 @@ def test_grouped_plans_are_bitwise_reproducible(name):
     got = run_gpu(CASES[name], partition_tokens=16, repeat=3)
     for o in got["outs"][1:]:
         assert np.array_equal(o, got["outs"][0])
+
+
+@pytest.mark.parametrize("name,pt", [("c3s_bf16_bs16", 0), ("c4s_cow_f16", 0), ("c4s_cow_f16", 16),
+                                     ("c5s_fp8", 512), ("c5s_fp8", 0), ("c1_tiny_f32", 0)])
+def test_one_plan_serves_every_layer(name, pt):
+    """paged_attention_plan once, then paged_attention_decode_planned for
+    several 'layers' -- other queries, and a second pool of the same shape
+    read through the same tables -- each bit-identical to the one-call
+    paged_attention_decode of that layer."""
+    import torch
+    import paged_kv_cache_449_amd as pk
+    from gpu_harness import announce, run_gpu
+    wl = W.small_configs()[name]
+    got = run_gpu(wl, partition_tokens=pt)
+    sess, q = got["session"], got["q"]
+    announce(f"one plan, several layers: {name} pt={pt}")
+    pool = sess.pool
+    pool2 = pk.KVPool(pool.num_blocks, pool.block_size, pool.num_kv_heads, pool.head_dim, pool.dtype, pool.device,
+                      pool.k_scale, pool.v_scale)
+    if pool.dtype == torch.float8_e4m3fn:   # flip the sign bit: an exact, different layer
+        pool2.k_cache.view(torch.uint8).copy_(pool.k_cache.view(torch.uint8) ^ 0x80)
+        pool2.v_cache.view(torch.uint8).copy_(pool.v_cache.view(torch.uint8) ^ 0x80)
+    else:
+        pool2.k_cache.copy_(-pool.k_cache)
+        pool2.v_cache.copy_(pool.v_cache * 2)
+    bt, cl = sess.block_tables, sess.context_lens
+    layers = [(pool, q), (pool, (-q).contiguous()), (pool2, q), (pool2, (q * 2).contiguous())]
+    ws = pk.paged_attention_plan(pool, q, bt, cl, partition_tokens=pt)
+    planned = [pk.paged_attention_decode_planned(pl, qq, bt, cl, wl.scale, ws, partition_tokens=pt)
+               for pl, qq in layers]
+    torch.cuda.synchronize()
+    for (pl, qq), o in zip(layers, planned):
+        ref = pk.paged_attention_decode(pl, qq, bt, cl, wl.scale, partition_tokens=pt)
+        torch.cuda.synchronize()
+        assert torch.equal(o.view(torch.uint8), ref.view(torch.uint8))
+    check_close(planned[0].float().cpu().double().numpy(), OracleRun(wl).decode(), wl.kv_dtype)
+
+
+def test_plan_call_checks_its_arguments():
+    import torch
+    import paged_kv_cache_449_amd as pk
+    from gpu_harness import announce, device
+    announce("plan argument checks")
+    dev = device()
+    pool = pk.KVPool(8, 16, 2, 64, torch.bfloat16, dev)
+    L = pk.lib()
+    bt = torch.zeros(2, 1, dtype=torch.int32, device=dev)
+    cl = torch.ones(2, dtype=torch.int32, device=dev)
+    ws = torch.zeros(1 << 20, dtype=torch.uint8, device=dev)
+    assert L.paged_attention_plan(pool.handle, pk.KV_BF16, None, 1, cl.data_ptr(), 2, 2, 0, ws.data_ptr(),
+                                  ws.numel(), None) == pk.KV_ERR_INVALID_ARG
+    assert L.paged_attention_plan(pool.handle, pk.KV_BF16, bt.data_ptr(), 1, cl.data_ptr(), 2, 3, 0, ws.data_ptr(),
+                                  ws.numel(), None) == pk.KV_ERR_INVALID_ARG     # 3 q heads over 2 kv heads
+    assert L.paged_attention_plan(pool.handle, pk.KV_BF16, bt.data_ptr(), 1, cl.data_ptr(), 2, 2, 0, ws.data_ptr(),
+                                  16, None) == pk.KV_ERR_WORKSPACE
+    assert L.paged_attention_plan(pool.handle, pk.KV_BF16, bt.data_ptr(), 1, cl.data_ptr(), 2, 2, 0, ws.data_ptr(),
+                                  ws.numel(), None) == pk.KV_OK
+    torch.cuda.synchronize()

@@ -20,7 +20,8 @@ int main(void) {
   fn_t fns[] = {(fn_t)kv_pool_create, (fn_t)kv_pool_create_from, (fn_t)kv_pool_destroy, (fn_t)kv_pool_info,
                  (fn_t)kv_pool_set_scales, (fn_t)kv_pool_set_head_scales, (fn_t)reshape_and_cache,
                  (fn_t)paged_attention_decode, (fn_t)paged_attention_workspace_size,
-                 (fn_t)paged_attention_decode_noalloc,
+                 (fn_t)paged_attention_decode_noalloc, (fn_t)paged_attention_plan,
+                 (fn_t)paged_attention_decode_planned,
                  (fn_t)paged_attention_decode_grouped, (fn_t)paged_attention_decode_grouped_workspace_size,
                  (fn_t)paged_attention_prefill, (fn_t)paged_attention_prefill_workspace_size, (fn_t)copy_blocks,
                  (fn_t)swap_blocks, (fn_t)kv_stream_read, (fn_t)kv_status_string, (fn_t)bm_create, (fn_t)bm_destroy,
@@ -61,5 +62,5 @@ def test_headers_compile_as_c_and_drive_the_manager():
         out = subprocess.run([exe], capture_output=True, text=True)
         assert out.returncode == 0, (out.returncode, out.stderr)
         n, free_blocks, msg = out.stdout.split(" ", 2)
-        assert int(n) == 31 and msg.strip().startswith("no free")
+        assert int(n) == 33 and msg.strip().startswith("no free")
         assert int(free_blocks) == 8 - 4
