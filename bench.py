@@ -544,12 +544,13 @@ def decode_summary(name: str, dev, steps: int, warmup: int) -> dict:
     events around each decode launch (kernel time), as for the main line.
     Shared blocks are counted once (the HBM lower bound)."""
     import paged_kv_cache_449_amd as pk
+    name, _, pt_text = name.partition(":")   # "workload:tokens" overrides its partition size
     wl = get_workload(name)
     print(f"[bench] building {wl.name}", file=sys.stderr, flush=True)
     sess, q, kn, vn = build_session(wl, dev)
     out = torch.empty_like(q)
     pool = sess.pool
-    pt = wl.partition_tokens
+    pt = int(pt_text) if pt_text else wl.partition_tokens
 
     def one_step(ev=None):
         pk.copy_blocks(pool, sess.pairs)
@@ -642,7 +643,7 @@ def main(argv=None) -> int:
     ap.add_argument("--also", default=None,
                     help="comma-separated decode workloads timed after the main one and reported under 'also' "
                          "(default: the other batch-256 headline workloads when the main one is the default; "
-                         "'none' for none)")
+                         "'none' for none; 'name:tokens' overrides a workload's partition size)")
     ap.add_argument("--summarise-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"), default=None,
                     help="no GPU work: turn the counter_collection.csv files of a rocprofv3 --pmc FETCH_SIZE run "
                          "and a --pmc WRITE_SIZE run of this same command line (with --calibrate-copy) into HBM "

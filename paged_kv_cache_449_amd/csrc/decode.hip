@@ -13,10 +13,15 @@ namespace pkv {
 // first block in item_pos when it is in LDS); returns ok = false when a
 // grouped layout's records would not fit the workspace.
 struct Layout {
-  int NI, TB, chunk, rounds, flags;
+  int NI, TB, chunk, span, q, rounds, flags;
   int64_t RH;
   bool ok;
 };
+
+// Most pieces (parts inside one chunk) a run of len blocks can be cut into.
+__device__ inline int max_pieces(int len, int chunk, int span, int q) {
+  return (len + chunk - 1) / chunk + 1 + (q > 1 ? (len + span - 1) / span : 0);
+}
 
 __device__ __attribute__((always_inline)) inline Layout plan_layout(const PlanParams& pp, PlanScratch* scr,
                                                                     PlanGroup* grp, int* item_pos, bool grouped,
@@ -38,10 +43,23 @@ __device__ __attribute__((always_inline)) inline Layout plan_layout(const PlanPa
     TB += tot;
   }
   const int flags = grouped ? kPlanGrouped : (has_eq ? kPlanShared : 0);
-  const int rounds = (pp.chunk == 0 && (flags & kPlanShared)) ? pp.shared_split : 1;
   const int64_t T64 = (int64_t)TB * pp.num_kv_heads;
-  const int64_t workers = (int64_t)pp.num_workers * rounds;
-  const int chunk = pp.chunk > 0 ? pp.chunk : (int)max((int64_t)1, (T64 + workers - 1) / workers);
+  int rounds, chunk, span, q;
+  if (pp.chunk > 0) {
+    // caller-sized partitions: every worker takes an equal span of the
+    // stream and runs it as q chunks of at most pp.chunk blocks, one per
+    // round
+    span = (int)max((int64_t)1, (T64 + pp.num_workers - 1) / pp.num_workers);
+    chunk = min(pp.chunk, span);
+    q = (span + chunk - 1) / chunk;
+    rounds = q;
+  } else {
+    rounds = (flags & kPlanShared) ? pp.shared_split : 1;
+    const int64_t w = (int64_t)pp.num_workers * rounds;
+    chunk = (int)max((int64_t)1, (T64 + w - 1) / w);
+    span = chunk;
+    q = 1;
+  }
 
   int icarry = 0, bcarry = 0;
   int64_t rcarry = 0;
@@ -51,8 +69,8 @@ __device__ __attribute__((always_inline)) inline Layout plan_layout(const PlanPa
     if (s < S) it = seq_items(scr, grp, pp.log2_bs, s, grouped);
     // record rows: at most ceil(len / chunk) + 1 pieces, each with the
     // item's rows (G-item: members x query heads)
-    const int gp = (grouped && it.lead) ? ((it.k + chunk - 1) / chunk + 1) * it.m * pp.G : 0;
-    const int sp = (grouped && it.suffix > 0) ? ((it.suffix + chunk - 1) / chunk + 1) * pp.G : 0;
+    const int gp = (grouped && it.lead) ? max_pieces(it.k, chunk, span, q) * it.m * pp.G : 0;
+    const int sp = (grouped && it.suffix > 0) ? max_pieces(it.suffix, chunk, span, q) * pp.G : 0;
     int3 tot;
     const int3 ex = plan_scan_sum3(make_int3((it.lead ? 1 : 0) + (it.suffix > 0 ? 1 : 0),
                                              (it.lead ? it.k : 0) + it.suffix, gp + sp), lds, &tot);
@@ -76,10 +94,10 @@ __device__ __attribute__((always_inline)) inline Layout plan_layout(const PlanPa
     icarry += tot.x;
     bcarry += tot.y;
     rcarry += tot.z;
-    if (rcarry > ((int64_t)1 << 30)) return Layout{0, 0, 0, 0, 0, 0, false};   // past any workspace
+    if (rcarry > ((int64_t)1 << 30)) return Layout{0, 0, 0, 0, 0, 0, 0, 0, false};   // past any workspace
   }
-  if (grouped && rcarry * pp.num_kv_heads > pp.grec_rows) return Layout{0, 0, 0, 0, 0, 0, false};
-  return Layout{icarry, bcarry, chunk, rounds, flags, rcarry, true};
+  if (grouped && rcarry * pp.num_kv_heads > pp.grec_rows) return Layout{0, 0, 0, 0, 0, 0, 0, 0, false};
+  return Layout{icarry, bcarry, chunk, span, q, rounds, flags, rcarry, true};
 }
 
 // The items and each sequence's entry, from the planner's state.
@@ -108,20 +126,47 @@ __device__ __attribute__((always_inline)) inline void plan_write_items(const Pla
   }
 }
 
-// The descriptors: thread t writes those of a contiguous range of chunk ids,
-// finding the first chunk's item by binary search over the items' first
-// blocks and walking forward from there.  Chunk v of round v / per_round
-// goes to the worker slot whose XCD-ordered id it is (slot b runs on XCD
-// b % 8 and takes id (b % 8) * (per_round / 8) + b / 8 in each round).
+// The descriptors.  Thread t takes a contiguous range of chunk ids (stream
+// order), finds the first one's item by binary search over the items' first
+// blocks and walks forward from there.  Where a chunk runs:
+//   - uniform cut (q = 1): chunk v in round v / per_round, with id
+//     v % per_round;
+//   - partitions (q > 1): chunk v, the (v % q)-th of span v / q, in round
+//     v % q, with id v / q, so a worker runs its span's chunks in order;
+// slot b runs on XCD b % 8 and takes id (b % 8) * (per_round / 8) + b / 8.
 // Slots without a chunk are marked empty.
 __device__ __attribute__((always_inline)) inline void plan_write_descs(const PlanParams& pp, const Layout& L,
                                                                        const int32_t* posp, int stride) {
   const int tid = threadIdx.x;
-  const int C = L.chunk, TB = L.TB, W = pp.num_workers;
+  const ChunkGrid g{L.chunk, L.span, L.q};
+  const int TB = L.TB, W = pp.num_workers;
   const int T = TB * pp.num_kv_heads;
-  const int nv = (T + C - 1) / C;
-  const int per_round = L.rounds == 1 ? ((nv + 7) & ~7) : W;
+  const int spans = (T + L.span - 1) / L.span;
+  // chunk ids; those of the last span that start past the stream's end hold
+  // no chunk (and are the last ids)
+  const int nid = spans * L.q;
+  int per_round, rounds;
+  if (L.q > 1) {
+    per_round = (spans + 7) & ~7;   // spans <= W, a multiple of 8
+    rounds = L.q;
+  } else {
+    // spread evenly over the rounds: a multiple of 8, at most W
+    per_round = min(W, ((nid + L.rounds - 1) / L.rounds + 7) & ~7);
+    rounds = nid > 0 ? (nid + per_round - 1) / per_round : 0;   // rounds that hold a chunk
+  }
   const int q8 = per_round >> 3;
+  auto slot_of = [&](int v) {
+    int rd, u;
+    if (L.q > 1) {
+      u = v / L.q;
+      rd = v - u * L.q;
+    } else {
+      rd = v / per_round;
+      u = v - rd * per_round;
+    }
+    const int uq = u / q8;
+    return rd * W + (u - uq * q8) * 8 + uq;
+  };
   auto pos_of = [&](int i) { return posp[(int64_t)i * stride]; };
   auto find = [&](int r) {   // the last item whose first block is <= r
     int lo = 0, hi = L.NI;
@@ -131,41 +176,29 @@ __device__ __attribute__((always_inline)) inline void plan_write_descs(const Pla
     }
     return lo;
   };
-  const int per = (nv + kPlanThreads - 1) / kPlanThreads;
-  int v = tid * per;
-  const int vend = min(v + per, nv);
-  if (v < vend) {
-    const int start = v * C;
-    int h = start / TB, r = start - h * TB;
-    int i = find(r);
-    int rd = v / per_round, u = v - rd * per_round;
-    int uq = u / q8, ur = u - uq * q8;
-    for (;;) {
-      while (i + 1 < L.NI && pos_of(i + 1) <= r) ++i;
-      put_desc(pp.desc + rd * W + ur * 8 + uq, PlanDesc{v, h, i, r - pos_of(i)});
-      if (++v >= vend) break;
-      r += C;
-      if (r >= TB) {   // a later kv head: its items start again from the first
-        while (r >= TB) {
-          r -= TB;
-          ++h;
-        }
-        i = find(r);
-      }
-      if (++ur == q8) {
-        ur = 0;
-        if (++uq == 8) {
-          uq = 0;
-          ++rd;
-        }
-      }
+  const int per = (nid + kPlanThreads - 1) / kPlanThreads;
+  const int vend = min((tid + 1) * per, nid);
+  int h = -1, i = 0;
+  for (int v = tid * per; v < vend; ++v) {
+    const int st = g.start(v);
+    if (st >= T) break;
+    const int nh = st / TB, r = st - nh * TB;
+    if (nh != h) {   // this thread's first chunk of a kv head: its items start again
+      h = nh;
+      i = find(r);
     }
+    while (i + 1 < L.NI && pos_of(i + 1) <= r) ++i;
+    put_desc(pp.desc + slot_of(v), PlanDesc{v, h, i, r - pos_of(i)});
   }
-  for (int k = tid; k < L.rounds * W; k += kPlanThreads) {
-    const int rd = k / W, wg = k - rd * W;
-    if (!(wg < per_round && rd * per_round + (wg & 7) * q8 + (wg >> 3) < nv)) put_desc(pp.desc + k, PlanDesc{-1, 0, 0, 0});
+  // the first round's descriptors are written even when no chunk exists
+  for (int k = tid; k < max(rounds, 1) * W; k += kPlanThreads) {
+    const int rd = k / W, b = k - rd * W;
+    const int u = (b & 7) * q8 + (b >> 3);
+    const int v = L.q > 1 ? u * L.q + rd : rd * per_round + u;
+    if (!(b < per_round && v < nid && g.start(v) < T)) put_desc(pp.desc + k, PlanDesc{-1, 0, 0, 0});
   }
-  if (tid == 0) *pp.header = PlanHeader{C, T, TB, L.NI, L.flags, L.rounds, (int32_t)L.RH, 0};
+  if (tid == 0)
+    *pp.header = PlanHeader{L.chunk, T, TB, L.NI, L.flags, rounds, (int32_t)L.RH, L.span, L.q, {0, 0, 0}};
 }
 
 template <bool IN_LDS>
@@ -365,27 +398,38 @@ kv_status_t make_plan(const kv_pool_t* pool, int32_t num_seqs, int32_t num_q_hea
   if (G != 1 && G != 2 && G != 4 && G != 8 && G != 16) return KV_ERR_UNSUPPORTED;
   const int64_t units = (int64_t)num_seqs * pool->num_kv_heads * max_blocks;  // upper bound of blocks
   if (units > (1LL << 30) || (int64_t)max_blocks * pool->block_size > (1LL << 30)) return KV_ERR_INVALID_ARG;
-  int64_t workers;
+  // The decode grid is resident: num_cus x decode_waves_per_cu one-wave
+  // workers, each taking one chunk per round.  With caller-sized partitions
+  // every worker gets an equal span of the stream, cut into partitions of
+  // at most partition_tokens tokens; the library-sized split makes one chunk
+  // per worker, or kSharedSplit finer ones when sequences share blocks.
+  int64_t workers = (int64_t)pool->num_cus * pool->decode_waves_per_cu;
+  int64_t chunks;   // chunk ids the descriptor table and the records cover
   if (partition_tokens > 0) {
     if (partition_tokens % pool->block_size) return KV_ERR_INVALID_ARG;
+    if (workers > units) workers = units;
+    if (workers < 1) workers = 1;
+    workers = (workers + 7) & ~7LL;
+    // each worker's span of the stream is cut into partitions; longer ones
+    // when the batch would need more chunk ids than counter slots
     int64_t chunk = partition_tokens / pool->block_size;
-    // longer runs when the batch would need more runs than counter slots
-    const int64_t min_chunk = (units + kCounterSlots - 9) / (kCounterSlots - 8);
-    if (chunk < min_chunk) chunk = min_chunk;
+    const int64_t span_max = (units + workers - 1) / workers;
+    const int64_t max_q = kCounterSlots / workers;
+    if ((span_max + chunk - 1) / chunk > max_q) chunk = (span_max + max_q - 1) / max_q;
     plan->chunk = (int32_t)chunk;
-    workers = (units + chunk - 1) / chunk;
+    plan->desc_rounds = (int32_t)std::max<int64_t>(1, (span_max + chunk - 1) / chunk);
+    chunks = workers * plan->desc_rounds;
   } else {
     plan->chunk = 0;
-    workers = (int64_t)pool->num_cus * pool->decode_waves_per_cu;
     if (workers > units) workers = units;
+    if (workers < 1) workers = 1;
+    workers = (workers + 7) & ~7LL;
+    plan->desc_rounds = kSharedSplit;
+    chunks = workers * kSharedSplit;
   }
-  if (workers < 1) workers = 1;
-  workers = (workers + 7) & ~7LL;
-  // chunks (virtual workers): the library-sized split may cut the stream
-  // kSharedSplit times finer when sequences share blocks
-  plan->desc_rounds = partition_tokens > 0 ? 1 : kSharedSplit;
-  const int64_t chunks = workers * plan->desc_rounds;
+  // arrival counters are indexed by chunk id
   if (chunks > kCounterSlots) return KV_ERR_INVALID_ARG;
+  const int64_t descs = workers * plan->desc_rounds;
   plan->num_workers = (int32_t)workers;
   const bool grouping = groupable(pool, G) && (int64_t)pool->num_kv_heads * num_seqs <= kCounterSlots;
   plan->max_members = grouping ? 16 / G : 0;
@@ -394,7 +438,7 @@ kv_status_t make_plan(const kv_pool_t* pool, int32_t num_seqs, int32_t num_q_hea
   plan->header_off = off;
   off = align256(off + sizeof(PlanHeader));
   plan->desc_off = off;
-  off = align256(off + (size_t)chunks * sizeof(PlanDesc));
+  off = align256(off + (size_t)descs * sizeof(PlanDesc));
   plan->items_off = off;
   off = align256(off + (S + S / 2 + 1) * sizeof(PlanItem));
   plan->seqs_off = off;
@@ -409,7 +453,7 @@ kv_status_t make_plan(const kv_pool_t* pool, int32_t num_seqs, int32_t num_q_hea
   // record rows of a grouped plan: at most 2 pieces plus one per chunk of
   // every item, so 4 * Hkv * S * G rows plus 16 per chunk boundary; past
   // 8192 chunks a grouped plan that does not fit falls back to a flat one
-  plan->grec_rows = grouping ? 4LL * pool->num_kv_heads * num_seqs * G + 16LL * std::min<int64_t>(workers, 8192) : 0;
+  plan->grec_rows = grouping ? 4LL * pool->num_kv_heads * num_seqs * G + 16LL * std::min<int64_t>(chunks, 8192) : 0;
   const size_t grouped = (size_t)plan->grec_rows * row;
   plan->bytes = off + std::max(flat, grouped);
   if (!grouping) plan->grec_rows = 0;

@@ -67,8 +67,8 @@ void paged_decode_shared_kernel(const DecodeParams p, const int32_t* group_start
   row.min_limit = gi.shared;
   if (gi.shared == 0) return;   // nothing shared: the suffix kernel reads the whole context
   const int nb = gi.shared >> p.log2_bs;
-  mfma_rows_run<KV, QT, D, 16, kStreamPolicy, ContiguousRows, true>(p, 0, 1, 0, 0, gi.gs, h, 0, nb, gi.shared, nb,
-                                                                   row, ContiguousRows{0, D});
+  mfma_rows_run<KV, QT, D, 16, kStreamPolicy, ContiguousRows, true>(p, 0, uniform_grid(1), 0, 0, gi.gs, h, 0, nb,
+                                                                   gi.shared, nb, row, ContiguousRows{0, D});
 }
 
 template <typename KV, typename QT, int D, int G>

@@ -20,10 +20,11 @@ namespace pkv {
 
 // Pieces of an item of kv head h that starts at block `ipos` of the head's
 // stream and holds `ilen` blocks: the chunks it spans.
-__device__ inline int item_first_chunk(const ChunkCtx& d, int h, int ipos) { return (h * d.TB + ipos) / d.chunk; }
+__device__ inline int item_first_chunk(const ChunkCtx& d, int h, int ipos) { return d.grid().of(h * d.TB + ipos); }
 __device__ inline int item_pieces(const ChunkCtx& d, int h, int ipos, int ilen) {
   const int a = h * d.TB + ipos;
-  return (a + ilen - 1) / d.chunk - a / d.chunk + 1;
+  const ChunkGrid g = d.grid();
+  return g.of(a + ilen - 1) - g.of(a) + 1;
 }
 
 // First float of piece k of an item (kv head h, first record row rbase)
@@ -79,20 +80,6 @@ __device__ inline void mfma_store_out(const DecodeParams& p, const MfmaRow& row,
     }
   }
 }
-template <typename KV, int D>
-__device__ inline void mfma_store_record(const RecordRef& rec, bool valid, const f32x4 (&acc)[MfmaShape<KV, D>::DT],
-                                         float m, float l) {
-  constexpr int DT = MfmaShape<KV, D>::DT;
-  const int j16 = threadIdx.x & 15, kg = threadIdx.x >> 4;
-  if (valid) {
-    const int rg = j16 * (D + 4);
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
-      record_store4(rec, rg + dt * 16 + 4 * kg, acc[dt][0], acc[dt][1], acc[dt][2], acc[dt][3]);
-    if (kg == 0) record_store4(rec, rg + D, m, l, 0.0f, 0.0f);
-  }
-}
-
 // A piece of an S-item: blocks [off, off + len) of the item (sequence it.s).
 template <typename KV, typename QT, int D, int G, bool MFMA>
 __device__ inline void seq_piece(const DecodeParams& p, const ChunkCtx& d, int h, const PlanItem& it, int off,
@@ -177,14 +164,16 @@ __device__ inline void group_piece(const DecodeParams& p, const ChunkCtx& d, int
   }
 }
 
-// Stream chunk d.v of a grouped plan.
+// Stream chunk d.v of a grouped plan, whose first item `first` the caller
+// has loaded; returns item `next_i`, loaded while the chunk's last piece
+// streams.
 template <typename KV, typename QT, int D, int G, bool MFMA>
-__device__ inline void grouped_chunk(const DecodeParams& p, const ChunkCtx& d) {
-  const int chunk = d.chunk;
-  const int start = d.v * chunk;
-  const int end = min(start + chunk, d.T);
+__device__ inline PlanItem grouped_chunk(const DecodeParams& p, const ChunkCtx& d, const PlanItem& first,
+                                         int next_i) {
+  const int start = d.grid().start(d.v);
+  const int end = d.grid().end(d.v, d.T);
   int h = d.h, i = d.i, off = d.off, pos = start;
-  PlanItem it = load_item(p.items + i);
+  PlanItem it = first;
   while (true) {
     const int len = min(it.len - off, end - pos);
     int ni = i + 1, nh = h;
@@ -193,13 +182,13 @@ __device__ inline void grouped_chunk(const DecodeParams& p, const ChunkCtx& d) {
       ++nh;
     }
     const bool more = pos + len < end;
-    const PlanItem nx = load_item(p.items + (more ? ni : i));   // in flight during the run
+    const PlanItem nx = load_item(p.items + (more ? ni : next_i));   // in flight during the run
     if (it.m > 0)
       group_piece<KV, QT, D, G>(p, d, h, it, off, len);
     else
       seq_piece<KV, QT, D, G, MFMA>(p, d, h, it, off, len);
     pos += len;
-    if (!more) break;
+    if (!more) return nx;
     i = ni;
     h = nh;
     it = nx;

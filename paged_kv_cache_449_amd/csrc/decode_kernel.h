@@ -310,13 +310,15 @@ __device__ inline float* partial_record(const DecodeParams& p, int w, int wstart
 // worker that completes the count, which then merges.  Its loads of the
 // records are coherent loads, so no cache-wide writeback or invalidate is
 // needed on either side.
-__device__ inline bool arrive(const DecodeParams& p, int first_w, int last_w) {
+// `pieces` counts in that many records of the run at once (a run that
+// crosses chunk boundaries leaves one per chunk).
+__device__ inline bool arrive(const DecodeParams& p, int first_w, int last_w, int pieces = 1) {
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   int done = 0;
   if (threadIdx.x == 0)
-    done = __hip_atomic_fetch_add(p.counters + first_w, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    done = __hip_atomic_fetch_add(p.counters + first_w, pieces, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   done = uniform(__shfl(done, 0));
-  return done == last_w - first_w;
+  return done + pieces == last_w - first_w + 1;
 }
 
 // Output rows of a run's records: record row j -> element offset of its out
@@ -409,11 +411,11 @@ __device__ inline void merge_list(const DecodeParams& p, int count, const RecAt&
 // Merge the records of workers first_w..last_w (in worker order) of a run
 // whose first position in the flattened stream is seg_start.
 template <typename QT, int D, int G, typename Rows, int NT = 64>
-__device__ inline void merge_records(const DecodeParams& p, int first_w, int last_w, int seg_start, int chunk,
-                                     const Rows& rows, float v_scale) {
+__device__ inline void merge_records(const DecodeParams& p, int first_w, int last_w, int seg_start,
+                                     const ChunkGrid& grid, const Rows& rows, float v_scale) {
   auto rec_at = [&](int c) {
     const int v = first_w + c;
-    return (const float*)p.partials + (int64_t)(2 * v + (v * chunk >= seg_start ? 0 : 1)) * G * (D + 4);
+    return (const float*)p.partials + (int64_t)(2 * v + (grid.start(v) >= seg_start ? 0 : 1)) * G * (D + 4);
   };
   merge_list<QT, D, G, decltype(rec_at), Rows, NT>(p, last_w - first_w + 1, rec_at, rows, v_scale,
                                                    p.counters + first_w);
@@ -586,11 +588,16 @@ __device__ inline void valu_store_out(const DecodeParams& p, int s, int h, float
 // place in the flattened stream and wstart the worker's first block.  All
 // scalars are uniform.
 template <typename KV, typename QT, int D, int G, int POL>
-__device__ inline void valu_run(const DecodeParams& p, int w, int chunk, int wstart, int pos, int s, int h,
-                                int off, int len, int n, int nb) {
+__device__ inline void valu_run(const DecodeParams& p, int w, const ChunkGrid& grid, int wstart, int pos, int s,
+                                int h, int off, int len, int n, int nb) {
   using Sh = DecodeShape<KV, D>;
   constexpr int VEC = Sh::VEC;
   const int Hq = p.num_kv_heads * G;
+  // the chunks the whole run spans (worked out before the run, while few
+  // registers are live)
+  const int seg_start = pos - off;
+  const int first_w = grid.of(seg_start);
+  const int last_w = grid.of(seg_start + nb - 1);
   float m[G], l[G], acc[G][VEC];
   valu_core<KV, QT, D, G, POL>(p, s, h, off, len, n, m, l, acc);
   const float vs = run_v_scale(p, h);
@@ -603,11 +610,8 @@ __device__ inline void valu_run(const DecodeParams& p, int w, int chunk, int wst
   // Partial: publish (acc, m, l) through the device coherence point; the
   // worker that completes the run's count merges.
   valu_store_record<KV, D, G>(record_ref<D, G>(partial_record<D, G>(p, w, wstart, pos)), m, l, acc);
-  const int seg_start = pos - off;
-  const int first_w = seg_start / chunk;
-  const int last_w = (seg_start + nb - 1) / chunk;
   if (arrive(p, first_w, last_w))
-    merge_records<QT, D, G>(p, first_w, last_w, seg_start, chunk,
+    merge_records<QT, D, G>(p, first_w, last_w, seg_start, grid,
                             ContiguousRows{((int64_t)s * Hq + (int64_t)h * G) * D, D}, vs);
 }
 
@@ -618,15 +622,19 @@ __device__ inline void valu_run(const DecodeParams& p, int w, int chunk, int wst
 
 namespace pkv {
 
-// Stream chunk d.v: blocks [v*chunk, (v+1)*chunk) of the flat (kv head,
-// sequence, block) stream, whose items are the non-empty sequences.
-template <typename KV, typename QT, int D, int G, bool MFMA, int POL>
-__device__ inline void decode_chunk(const DecodeParams& p, const ChunkCtx& d) {
-  const int chunk = d.chunk;
-  const int start = d.v * chunk;
-  const int end = min(start + chunk, d.T);
+// Stream chunk d.v of a flat plan, whose items are the non-empty sequences,
+// and whose first item `first` the caller has loaded; returns item `next_i`
+// (the first item of the worker's next chunk), loaded while the chunk's last
+// run streams.  SPAN (matrix-core runs over partitions): stream the chunk's
+// whole span, the runs leaving a record at every chunk boundary they cross.
+template <typename KV, typename QT, int D, int G, bool MFMA, int POL, bool SPAN = false>
+__device__ inline FlatItem decode_chunk(const DecodeParams& p, const ChunkCtx& d, const FlatItem& first, int next_i) {
+  static_assert(!SPAN || MFMA, "span runs are matrix-core runs");
+  const ChunkGrid grid = d.grid();
+  const int start = grid.start(d.v);
+  const int end = SPAN ? grid.span_end(d.v, d.T) : grid.end(d.v, d.T);
   int h = d.h, i = d.i, off = d.off, pos = start;
-  PlanItem it = load_item(p.items + i);
+  FlatItem it = first;
   while (true) {
     const int len = min(it.len - off, end - pos);
     // the next run's item loads while this run streams
@@ -636,17 +644,41 @@ __device__ inline void decode_chunk(const DecodeParams& p, const ChunkCtx& d) {
       ++nh;
     }
     const bool more = pos + len < end;
-    const PlanItem nx = load_item(p.items + (more ? ni : i));
+    const FlatItem nx = load_flat_item(p.items + (more ? ni : next_i));
+    // the chunk where the run starts, and that chunk's first block
+    const int w = SPAN ? grid.of(pos) : d.v;
+    const int wstart = SPAN ? grid.start(w) : start;
     if constexpr (MFMA)
-      mfma_run<KV, QT, D, G, POL>(p, d.v, chunk, start, pos, it.s, h, off, len, it.n, it.len);
+      mfma_run<KV, QT, D, G, POL>(p, w, grid, wstart, pos, it.s, h, off, len, it.n, it.len);
     else
-      valu_run<KV, QT, D, G, POL>(p, d.v, chunk, start, pos, it.s, h, off, len, it.n, it.len);
+      valu_run<KV, QT, D, G, POL>(p, w, grid, wstart, pos, it.s, h, off, len, it.n, it.len);
     pos += len;
-    if (!more) break;
+    if (!more) return nx;
     i = ni;
     h = nh;
     it = nx;
     off = 0;
+  }
+}
+
+// A worker's chunks, one per round.  The next round's descriptor loads as
+// the current chunk starts, and its first item while the chunk's last run
+// streams, so a new chunk starts with the loads of its first run.  Item is
+// the plan entry the chunks read (FlatItem or PlanItem).
+template <typename Item, typename Load, typename Chunk>
+__device__ inline void run_rounds(const DecodeParams& p, const PlanHeader& H, int rounds, Load load, Chunk chunk) {
+  const PlanDesc* dp = p.desc + blockIdx.x;
+  PlanDesc cur = load_desc(dp);
+  Item it = load(p.items + max(cur.i, 0));
+  for (int rd = 0; rd < rounds; ++rd) {
+    const PlanDesc nxt = load_desc(dp + (int64_t)min(rd + 1, rounds - 1) * p.num_workers);
+    // an empty slot's item index is 0, so this load stays in the items
+    const int next_i = max(nxt.i, 0);
+    if (cur.v < 0)
+      it = load(p.items + next_i);
+    else
+      it = chunk(chunk_ctx(H, cur), it, next_i);
+    cur = nxt;
   }
 }
 
@@ -688,17 +720,39 @@ void paged_decode_kernel(const DecodeParams p) {
   constexpr bool kGroupable = !std::is_void<typename mfma_operand<KV, QT>::type>::value && G <= 8;
   const PlanHeader H = load_header(p.header);
   if ((H.flags & kPlanEmpty) && blockIdx.x == 0) zero_empty_rows<QT, D, G>(p);
-  const PlanDesc* dp = p.desc + blockIdx.x;
-  for (int rd = 0; rd < H.rounds; ++rd) {
-    const ChunkCtx d = chunk_ctx(H, load_desc(dp + (int64_t)rd * p.num_workers));
-    if (d.v < 0) continue;
-    if (d.flags & kPlanGrouped) {
-      if constexpr (kGroupable) grouped_chunk<KV, QT, D, G, MFMA>(p, d);
-    } else if (d.flags & kPlanShared) {
-      decode_chunk<KV, QT, D, G, MFMA, kSharedPolicy>(p, d);
-    } else {
-      decode_chunk<KV, QT, D, G, MFMA, kStreamPolicy>(p, d);
+  if (H.rounds == 0) return;
+  auto flat = [](const PlanItem* a) { return load_flat_item(a); };
+  if (H.flags & kPlanGrouped) {
+    if constexpr (kGroupable)
+      run_rounds<PlanItem>(p, H, H.rounds, [](const PlanItem* a) { return load_item(a); },
+                           [&](const ChunkCtx& d, const PlanItem& it, int next_i) {
+                             return grouped_chunk<KV, QT, D, G, MFMA>(p, d, it, next_i);
+                           });
+    return;
+  }
+  if constexpr (MFMA) {
+    // partitions: a matrix-core worker streams its span in one pass (the
+    // first round's chunk opens it), leaving a record per partition
+    if (H.q > 1) {
+      if (H.flags & kPlanShared)
+        run_rounds<FlatItem>(p, H, 1, flat, [&](const ChunkCtx& d, const FlatItem& it, int next_i) {
+          return decode_chunk<KV, QT, D, G, MFMA, kSharedPolicy, true>(p, d, it, next_i);
+        });
+      else
+        run_rounds<FlatItem>(p, H, 1, flat, [&](const ChunkCtx& d, const FlatItem& it, int next_i) {
+          return decode_chunk<KV, QT, D, G, MFMA, kStreamPolicy, true>(p, d, it, next_i);
+        });
+      return;
     }
+  }
+  if (H.flags & kPlanShared) {
+    run_rounds<FlatItem>(p, H, H.rounds, flat, [&](const ChunkCtx& d, const FlatItem& it, int next_i) {
+      return decode_chunk<KV, QT, D, G, MFMA, kSharedPolicy>(p, d, it, next_i);
+    });
+  } else {
+    run_rounds<FlatItem>(p, H, H.rounds, flat, [&](const ChunkCtx& d, const FlatItem& it, int next_i) {
+      return decode_chunk<KV, QT, D, G, MFMA, kStreamPolicy>(p, d, it, next_i);
+    });
   }
 }
 

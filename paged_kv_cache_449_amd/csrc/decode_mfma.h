@@ -220,6 +220,19 @@ __device__ inline uint4 mfma_k_operand(const uint4 (&kq)[MfmaShape<KV, D>::KL], 
   }
 }
 
+// Cuts inside a run: a run that crosses chunk boundaries leaves the state
+// of each finished chunk's part as that chunk's record and starts the next
+// part from zero, without leaving its load pipeline.  `first` and `every`
+// count 16-token tiles: to the first cut, and between cuts; `cuts` is their
+// number (a run that ends on a chunk boundary has no cut there: its last
+// part is the caller's); the functor stores part k.  NoCut: one part.
+struct NoCut {
+  static constexpr bool kActive = false;
+  int first = 0, every = 0, cuts = 0;
+  template <int DT>
+  __device__ void operator()(int, const f32x4 (&)[DT], float, float) const {}
+};
+
 // Query row served by lane (kg, j) of a matrix-core run.
 struct MfmaRow {
   bool valid;     // row j holds a query
@@ -241,9 +254,10 @@ struct MfmaRow {
 // mfma_rows_core runs the stream and leaves the run's state: lane (kg, j16)
 // holds acc[dt] = O[j16][16 dt + 4kg + i], i = 0..3 (unnormalised), the
 // row's reference max m (log2 units) and its whole running sum l.
-template <typename KV, typename QT, int D, int POL>
+template <typename KV, typename QT, int D, int POL, typename Cut = NoCut>
 __device__ inline void mfma_rows_core(const DecodeParams& p, int s, int h, int off, int len, int n,
-                                      const MfmaRow& row, f32x4 (&acc)[MfmaShape<KV, D>::DT], float& m, float& l) {
+                                      const MfmaRow& row, f32x4 (&acc)[MfmaShape<KV, D>::DT], float& m, float& l,
+                                      const Cut& cut = Cut{}) {
   using MT = typename mfma_operand<KV, QT>::type;
   using Ops = mfma_ops<MT>;
   using Sh = MfmaShape<KV, D>;
@@ -284,6 +298,8 @@ __device__ inline void mfma_rows_core(const DecodeParams& p, int s, int h, int o
   c.log2_bs = p.log2_bs;
   c.bs_mask = (1 << p.log2_bs) - 1;
   const int32_t* trow = p.block_tables + (int64_t)s * p.max_blocks + off;
+  static_assert(!Cut::kActive || TPS == 1, "cuts fall between single-tile steps");
+  int to_cut = cut.first, part = 0;
 
   // One pipeline step: TPS tiles staged in LDS (V as the operand type, rows
   // padded to LSTRIDE; K as loaded, rows padded to KSTRIDE), QK for each, one
@@ -291,7 +307,7 @@ __device__ inline void mfma_rows_core(const DecodeParams& p, int s, int h, int o
   // 16x16x32 steps whose contraction index 8kg + e stands for token 4kg + e
   // of the first tile (e < 4) and 4kg + e - 4 of the second, on both
   // operands.
-  auto compute = [&](const MfmaStep<KV, D>& r, int tab, int tlo, int thi, int st, int unmasked_end) {
+  auto compute = [&](const MfmaStep<KV, D>& r, int tab, int tlo, int thi, int st, int unmasked_end, bool real) {
     __syncthreads();   // the previous step's LDS reads are done
 #pragma unroll
     for (int q = 0; q < TPS; ++q) {
@@ -391,6 +407,22 @@ __device__ inline void mfma_rows_core(const DecodeParams& p, int s, int h, int o
         acc[dt] = Ops::pv(vt, br, Ops::pv(vt, bh, acc[dt]));
       }
     }
+    if constexpr (Cut::kActive) {
+      // the tile ends a chunk: its part is done (a step past the window,
+      // issued only to keep the wait counts exact, is no tile)
+      if (real && part < cut.cuts && --to_cut == 0) {
+        float lt = l;
+        lt += __shfl_xor(lt, 16);
+        lt += __shfl_xor(lt, 32);
+        cut(part, acc, m, lt);
+        ++part;
+        to_cut = cut.every;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        m = -INFINITY;
+        l = 0.0f;
+      }
+    }
   };
 
   int tab = load_table_window(p, trow, 0, len);
@@ -423,14 +455,14 @@ __device__ inline void mfma_rows_core(const DecodeParams& p, int s, int h, int o
       issue(a, 0);
       for (int st = 0; st < steps; st += 2) {
         issue(b, st + 1);
-        compute(a, tab, tlo, thi, st, unmasked_end);
+        compute(a, tab, tlo, thi, st, unmasked_end, true);
         issue(a, st + 2);
-        compute(b, tab, tlo, thi, st + 1, unmasked_end);
+        compute(b, tab, tlo, thi, st + 1, unmasked_end, st + 1 < steps);
       }
     } else {
       for (int st = 0; st < steps; ++st) {
         issue(a, st);
-        compute(a, tab, tlo, thi, st, unmasked_end);
+        compute(a, tab, tlo, thi, st, unmasked_end, true);
       }
     }
     tab = tab_next;
@@ -441,9 +473,92 @@ __device__ inline void mfma_rows_core(const DecodeParams& p, int s, int h, int o
   l += __shfl_xor(l, 32);
 }
 
-template <typename KV, typename QT, int D, int R, int POL, typename Rows, bool PART = false>
-__device__ inline void mfma_rows_run(const DecodeParams& p, int w, int chunk, int wstart, int pos, int s, int h,
-                                     int off, int len, int n, int nb, const MfmaRow& row, const Rows& rows) {
+// Matrix-core state of a part -> its record (rows j16 < R of valid lanes).
+template <typename KV, int D>
+__device__ inline void mfma_store_record(const RecordRef& rec, bool valid, const f32x4 (&acc)[MfmaShape<KV, D>::DT],
+                                         float m, float l) {
+  constexpr int DT = MfmaShape<KV, D>::DT;
+  const int j16 = threadIdx.x & 15, kg = threadIdx.x >> 4;
+  if (valid) {
+    const int rg = j16 * (D + 4);
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+      record_store4(rec, rg + dt * 16 + 4 * kg, acc[dt][0], acc[dt][1], acc[dt][2], acc[dt][3]);
+    if (kg == 0) record_store4(rec, rg + D, m, l, 0.0f, 0.0f);
+  }
+}
+
+// The parts a run leaves in the chunks it crosses: part k goes to chunk
+// v0 + k, as the chunk's first part (slot 0), except part 0 of a run that
+// starts inside its chunk (slot 1).
+//
+// The first NP parts wait in LDS until the run ends.  A record stored in the
+// middle of the stream would hold up the run: a wave's vector memory
+// operations complete in issue order, so the next tile's loads would wait
+// for the stores to be written through.  NP fits the LDS a work-group may
+// hold with 8 per CU (20 KiB, the tile staging included); parts past NP are
+// stored at once.
+template <typename KV, int D, int R>
+struct RecordCuts {
+  static constexpr bool kActive = true;
+  static constexpr int kRec = R * (D + 4);   // floats per part
+  static constexpr int kStage =
+      MfmaStep<KV, D>::TPS * 16 * (MfmaShape<KV, D>::LSTRIDE + MfmaShape<KV, D>::KSTRIDE);
+  static constexpr int kFit = kStage + kRec * 4 > 20480 ? 0 : (20480 - kStage) / (kRec * 4);
+  static constexpr int NP = kFit > 8 ? 8 : kFit;
+  int first, every, cuts;
+  float* partials;
+  int v0, slot0;
+  bool valid;
+  __device__ static float* lds() {
+    __shared__ __attribute__((aligned(16))) float a[NP > 0 ? NP * kRec : 4];
+    return a;
+  }
+  __device__ RecordRef record(int k) const {
+    return record_ref<D, R>(partials + (int64_t)(2 * (v0 + k) + (k == 0 ? slot0 : 0)) * kRec);
+  }
+  __device__ void operator()(int k, const f32x4 (&acc)[MfmaShape<KV, D>::DT], float m, float l) const {
+    constexpr int DT = MfmaShape<KV, D>::DT;
+    if (k < NP) {   // the lane's own elements, as it will store them
+      const int j16 = threadIdx.x & 15, kg = threadIdx.x >> 4;
+      float* b = lds() + k * kRec + j16 * (D + 4);
+      if (valid) {
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) *(f32x4*)(b + dt * 16 + 4 * kg) = acc[dt];
+        if (kg == 0) *(float2*)(b + D) = make_float2(m, l);
+      }
+    } else {
+      mfma_store_record<KV, D>(record(k), valid, acc, m, l);
+    }
+  }
+  // store the parts held in LDS (each lane reads back what it wrote)
+  __device__ void flush() const {
+    constexpr int DT = MfmaShape<KV, D>::DT;
+    const int j16 = threadIdx.x & 15, kg = threadIdx.x >> 4;
+    for (int k = 0; k < min(cuts, NP); ++k) {
+      const float* b = lds() + k * kRec + j16 * (D + 4);
+      const RecordRef rec = record(k);
+      if (valid) {
+        const int rg = j16 * (D + 4);
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+          const f32x4 x = *(const f32x4*)(b + dt * 16 + 4 * kg);
+          record_store4(rec, rg + dt * 16 + 4 * kg, x[0], x[1], x[2], x[3]);
+        }
+        if (kg == 0) {
+          const float2 ml = *(const float2*)(b + D);
+          record_store4(rec, rg + D, ml.x, ml.y, 0.0f, 0.0f);
+        }
+      }
+    }
+  }
+};
+
+// CUTS: the run may cross chunk boundaries of the grid (a worker streaming a
+// span of partitions), leaving one record per chunk crossed.
+template <typename KV, typename QT, int D, int R, int POL, typename Rows, bool PART = false, bool CUTS = false>
+__device__ inline void mfma_rows_run(const DecodeParams& p, int w, const ChunkGrid& grid, int wstart, int pos, int s,
+                                     int h, int off, int len, int n, int nb, const MfmaRow& row, const Rows& rows) {
   using Sh = MfmaShape<KV, D>;
   static_assert(R >= 1 && R <= 16, "query rows");
   constexpr int DT = Sh::DT;
@@ -451,9 +566,29 @@ __device__ inline void mfma_rows_run(const DecodeParams& p, int w, int chunk, in
   const int lane = threadIdx.x;
   const int j16 = lane & 15;
   const int kg = lane >> 4;
+  // the chunks the whole run spans (worked out before the run, while few
+  // registers are live)
+  const int seg_start = pos - off;
+  const int first_w = grid.of(seg_start);
+  const int last_w = grid.of(seg_start + nb - 1);
   f32x4 acc[DT];
   float m, l;
-  mfma_rows_core<KV, QT, D, POL>(p, s, h, off, len, n, row, acc, m, l);
+  int pieces = 1;    // records this run leaves
+  int last_v = w;    // chunk of its last part
+  if constexpr (CUTS) {
+    last_v = grid.of(pos + len - 1);
+    pieces = last_v - w + 1;
+  }
+  if (CUTS && pieces > 1) {
+    // cuts fall on chunk starts, every grid.chunk blocks within the span
+    const int tpb = 1 << (p.log2_bs - 4);   // tiles per block
+    const RecordCuts<KV, D, R> cut{(grid.start(w + 1) - pos) * tpb, grid.chunk * tpb, pieces - 1, p.partials, w,
+                                   pos == wstart ? 0 : 1, row.valid && j16 < R};
+    mfma_rows_core<KV, QT, D, POL>(p, s, h, off, len, n, row, acc, m, l, cut);
+    cut.flush();
+  } else {
+    mfma_rows_core<KV, QT, D, POL>(p, s, h, off, len, n, row, acc, m, l);
+  }
   const float vs = run_v_scale(p, h);
 
   // lane (kg, j16) holds O[j16][16 dt + 4kg + i], i = 0..3
@@ -466,7 +601,7 @@ __device__ inline void mfma_rows_run(const DecodeParams& p, int w, int chunk, in
     }
     return;
   }
-  if (off == 0 && off + len == nb) {   // the whole run is ours
+  if (off == 0 && off + len == nb && pieces == 1) {   // the whole run is ours
     if (row.valid) {
       const float mul = l > 0.0f ? vs / l : 0.0f;
 #pragma unroll
@@ -478,24 +613,17 @@ __device__ inline void mfma_rows_run(const DecodeParams& p, int w, int chunk, in
     return;
   }
 
-  const RecordRef rec = record_ref<D, R>(partial_record<D, R>(p, w, wstart, pos));
-  if (row.valid && j16 < R) {
-    const int rg = j16 * (D + 4);
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
-      record_store4(rec, rg + dt * 16 + 4 * kg, acc[dt][0], acc[dt][1], acc[dt][2], acc[dt][3]);
-    if (kg == 0) record_store4(rec, rg + D, m, l, 0.0f, 0.0f);
-  }
-  const int seg_start = pos - off;
-  const int first_w = seg_start / chunk;
-  const int last_w = (seg_start + nb - 1) / chunk;
-  if (arrive(p, first_w, last_w)) merge_records<QT, D, R>(p, first_w, last_w, seg_start, chunk, rows, vs);
+  // the last part: its chunk's first part unless it is the run's only one
+  const int slot = (pieces == 1 && pos != wstart) ? 1 : 0;
+  const RecordRef rec = record_ref<D, R>(p.partials + (int64_t)(2 * last_v + slot) * R * (D + 4));
+  mfma_store_record<KV, D>(rec, row.valid && j16 < R, acc, m, l);
+  if (arrive(p, first_w, last_w, pieces)) merge_records<QT, D, R>(p, first_w, last_w, seg_start, grid, rows, vs);
 }
 
 // Decode: the G query heads of sequence s served by kv head h, one token each.
 template <typename KV, typename QT, int D, int G, int POL>
-__device__ inline void mfma_run(const DecodeParams& p, int w, int chunk, int wstart, int pos, int s, int h, int off,
-                                int len, int n, int nb) {
+__device__ inline void mfma_run(const DecodeParams& p, int w, const ChunkGrid& grid, int wstart, int pos, int s,
+                                int h, int off, int len, int n, int nb) {
   const int Hq = p.num_kv_heads * G;
   const int j16 = threadIdx.x & 15;
   const int64_t orow = ((int64_t)s * Hq + (int64_t)h * G) * D;
@@ -504,7 +632,8 @@ __device__ inline void mfma_run(const DecodeParams& p, int w, int chunk, int wst
   row.qoff = orow + (int64_t)j16 * D;
   row.limit = n;
   row.min_limit = n;
-  mfma_rows_run<KV, QT, D, G, POL>(p, w, chunk, wstart, pos, s, h, off, len, n, nb, row, ContiguousRows{orow, D});
+  mfma_rows_run<KV, QT, D, G, POL, ContiguousRows, false, true>(p, w, grid, wstart, pos, s, h, off, len, n, nb, row,
+                                                                 ContiguousRows{orow, D});
 }
 
 }  // namespace pkv

@@ -68,7 +68,36 @@ struct PlanDesc {
   int32_t off;     // block of the chunk's start within that item
 };
 
-// What every worker of a launch shares (32 bytes).
+// How the stream of T blocks is cut into chunks: spans of `span` blocks,
+// each cut into q chunks of `chunk` blocks (the last chunk of a span may be
+// shorter, and the last span).  Chunk ids follow stream order.  With q = 1
+// (span = chunk) the cut is uniform.
+struct ChunkGrid {
+  int32_t chunk, span, q;
+  // chunk holding stream block x
+  __device__ int of(int x) const {
+    if (q == 1) return x / chunk;
+    const int u = x / span;
+    return u * q + (x - u * span) / chunk;
+  }
+  // first block of chunk v
+  __device__ int start(int v) const {
+    if (q == 1) return v * chunk;
+    const int u = v / q;
+    return u * span + (v - u * q) * chunk;
+  }
+  // one past its last block
+  __device__ int end(int v, int T) const {
+    if (q == 1) return min((v + 1) * chunk, T);
+    const int u = v / q;
+    return min(min(u * span + (v - u * q + 1) * chunk, (u + 1) * span), T);
+  }
+  // one past the last block of its span
+  __device__ int span_end(int v, int T) const { return min((v / q + 1) * span, T); }
+};
+__device__ inline ChunkGrid uniform_grid(int chunk) { return ChunkGrid{chunk, chunk, 1}; }
+
+// What every worker of a launch shares (48 bytes).
 struct PlanHeader {
   int32_t chunk;   // blocks per chunk
   int32_t T;       // blocks in the stream (all kv heads)
@@ -77,13 +106,16 @@ struct PlanHeader {
   int32_t flags;   // kPlanShared | kPlanGrouped | kPlanEmpty
   int32_t rounds;  // chunks per worker
   int32_t RH;      // grouped mode: record rows per kv head
-  int32_t pad;
+  int32_t span;    // blocks per span (the chunk grid)
+  int32_t q;       // chunks per span
+  int32_t pad[3];
 };
 
 // A worker's view of one chunk: the launch's header and the chunk's start.
 struct ChunkCtx {
-  int32_t chunk, T, TB, NI, flags, rounds, RH;
+  int32_t chunk, T, TB, NI, flags, rounds, RH, span, q;
   int32_t v, h, i, off;
+  __device__ ChunkGrid grid() const { return ChunkGrid{chunk, span, q}; }
 };
 
 // Flat mode in which some sequence starts on its predecessor's first block
@@ -135,7 +167,7 @@ struct PlanParams {
   int32_t G;                 // query heads per kv head
   int32_t chunk;             // blocks per chunk; 0 = sized from num_workers
   int32_t num_workers;       // decode work-groups launched (multiple of 8)
-  int32_t desc_rounds;       // rounds the descriptor table holds (1, or kSharedSplit)
+  int32_t desc_rounds;       // rounds the descriptor table holds
   int32_t max_members;       // sequences per group; < 2 = no grouping
   int32_t shared_split;      // rounds of the shared mode (kSharedSplit)
   int32_t counter_slots;     // arrival counters (grouped mode uses one per (kv head, sequence))
@@ -165,16 +197,25 @@ __device__ inline PlanItem load_item(const PlanItem* it) {
   const const_words w = (const_words)it;
   return PlanItem{w[0], w[1], w[2], w[3], w[4], w[5], w[6], w[7], w[8], w[9], w[10], w[11]};
 }
+// What a flat plan's chunks read of an item: its sequence, blocks and token
+// limit.
+struct FlatItem {
+  int32_t s, len, n;
+};
+__device__ inline FlatItem load_flat_item(const PlanItem* it) {
+  const const_words w = (const_words)it;
+  return FlatItem{w[0], w[2], w[3]};
+}
 __device__ inline PlanHeader load_header(const PlanHeader* h) {
   const const_words w = (const_words)h;
-  return PlanHeader{w[0], w[1], w[2], w[3], w[4], w[5], w[6], w[7]};
+  return PlanHeader{w[0], w[1], w[2], w[3], w[4], w[5], w[6], w[7], w[8], {0, 0, 0}};
 }
 __device__ inline PlanDesc load_desc(const PlanDesc* d) {
   const const_words w = (const_words)d;
   return PlanDesc{w[0], w[1], w[2], w[3]};
 }
 __device__ inline ChunkCtx chunk_ctx(const PlanHeader& H, const PlanDesc& d) {
-  return ChunkCtx{H.chunk, H.T, H.TB, H.NI, H.flags, H.rounds, H.RH, d.v, d.h, d.i, d.off};
+  return ChunkCtx{H.chunk, H.T, H.TB, H.NI, H.flags, H.rounds, H.RH, H.span, H.q, d.v, d.h, d.i, d.off};
 }
 
 constexpr int kPlanThreads = 1024;

@@ -104,7 +104,8 @@ __device__ inline void prefill_run(const DecodeParams& p, int w, int chunk, int 
   row.limit = n - m + r * Q + tok + 1;
   row.min_limit = n - m + r * Q + 1;   // the tile's first row
   const TokenRows rows{q0, m - r * Q, Hq, h * G, G, D};
-  mfma_rows_run<KV, QT, D, 16, kStreamPolicy>(p, w, chunk, wstart, pos, s, h, off, len, lim, nb, row, rows);
+  mfma_rows_run<KV, QT, D, 16, kStreamPolicy>(p, w, uniform_grid(chunk), wstart, pos, s, h, off, len, lim, nb, row,
+                                              rows);
 }
 
 // Chunk v of the (kv head, sequence, tile, block) stream, `total` blocks per
@@ -554,7 +555,7 @@ __device__ inline void prefill_wg_run(const DecodeParams& p, int w, int chunk, i
   __syncthreads();
   if (last_flag)
     merge_records<QT, D, 16 * TB, BlockRows, 64 * W>(
-        p, first_w, last_w, seg_start, chunk, BlockRows{qs, TB, rb, m, Q, Hq, h * G, G, D}, vsc);
+        p, first_w, last_w, seg_start, uniform_grid(chunk), BlockRows{qs, TB, rb, m, Q, Hq, h * G, G, D}, vsc);
 }
 
 template <typename KV, typename QT, int D, int G>

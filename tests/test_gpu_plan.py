@@ -7,7 +7,8 @@ Covers forked candidates of every shape family (MHA and query groups, 16-bit
 and fp8, block sizes 16 and 32, groups cut to the 16-row limit), the
 library-sized split and fixed 16- and 64-token runs, batches above the
 planner's 1024-sequence LDS capacity (state in the workspace), mixed batches
-of forked and independent sequences with empty ones, and bitwise
+of forked and independent sequences with empty ones, caller-sized
+partitions over worker spans of several partitions, and bitwise
 reproducibility ("vLLM — 把操作系统的分页搬进 GPU KV cache": core mechanism 3
 and case 2 for the sharing; core mechanisms for the table walk)."""
 import numpy as np
@@ -55,6 +56,46 @@ def test_batches_past_the_planner_lds(name, pt):
     wl = LARGE[name]
     got = run_gpu(wl, partition_tokens=pt)
     check_close(got["out"], OracleRun(wl).decode(), wl.kv_dtype)
+
+
+# Caller-sized partitions over a stream longer than the worker grid: every
+# worker streams a span of several partitions in one pass, leaving a record
+# at each partition boundary it crosses.  One-block partitions put a
+# boundary at the end of every run; one wave per CU makes the spans long.
+SPANS = {
+    "spans_fp8_gqa4": W.config_c5("fp8e4m3", num_seqs=64, lo=200, hi=1200, hq=8, hkv=2, index=64,
+                                  name="spans_fp8_gqa4"),
+    "spans_bf16_gqa8": W.config_c5("bf16", num_seqs=40, lo=100, hi=1500, hq=16, hkv=2, index=65,
+                                   name="spans_bf16_gqa8"),
+    "spans_f16_mha": W._make("spans_f16_mha", 66, 4, 4, 128, "f16", "f16", 16,
+                             ctx_lens=np.random.default_rng(66).integers(1, 900, size=48).tolist()),
+    "spans_bf16_gqa4_bs32": W._make("spans_bf16_gqa4_bs32", 67, 8, 2, 128, "bf16", "bf16", 32,
+                                    ctx_lens=np.random.default_rng(67).integers(1, 2000, size=40).tolist()),
+}
+
+
+@pytest.mark.parametrize("waves", [1, 8])
+@pytest.mark.parametrize("pt", [16, 32, 64, 160, 512])
+@pytest.mark.parametrize("name", list(SPANS))
+def test_partitions_over_worker_spans(name, pt, waves, monkeypatch):
+    from gpu_harness import run_gpu
+    wl = SPANS[name]
+    if pt % wl.block_size:
+        pytest.skip("partitions are whole blocks")
+    monkeypatch.setenv("PAGEDKV_DECODE_WAVES_PER_CU", str(waves))   # read when the pool is made
+    got = run_gpu(wl, partition_tokens=pt)
+    assert np.isfinite(got["out"]).all()
+    check_close(got["out"], _ref(wl), wl.kv_dtype)
+
+
+_REFS = {}
+
+
+def _ref(wl):
+    if wl.name not in _REFS:
+        _REFS.clear()
+        _REFS[wl.name] = OracleRun(wl).decode()
+    return _REFS[wl.name]
 
 
 def test_mixed_batch_with_empty_contexts():

@@ -19,26 +19,55 @@ COUNTER_SLOTS = 65536
 SHARED_SPLIT = 4
 
 
+class Grid:
+    """ChunkGrid: spans of `span` blocks, each cut into q chunks of `chunk`."""
+
+    def __init__(self, chunk, span, q):
+        self.chunk, self.span, self.q = chunk, span, q
+
+    def of(self, x):
+        u, r = divmod(x, self.span)
+        return u * self.q + r // self.chunk
+
+    def start(self, v):
+        u, r = divmod(v, self.q)
+        return u * self.span + r * self.chunk
+
+    def end(self, v, T):
+        u, r = divmod(v, self.q)
+        return min(u * self.span + (r + 1) * self.chunk, (u + 1) * self.span, T)
+
+
+def max_pieces(ln, chunk, span, q):
+    return -(-ln // chunk) + 1 + (-(-ln // span) if q > 1 else 0)
+
+
 def host_plan(S, hkv, max_blocks, bs, G, pt, num_cus=256, waves_per_cu=8, groupable=True):
     """make_plan in decode.hip: split, descriptor rounds, grouping limits."""
     units = S * hkv * max_blocks
+    workers = num_cus * waves_per_cu
     if pt > 0:
+        workers = max(min(workers, units), 1)
+        workers = (workers + 7) & ~7
         chunk = pt // bs
-        min_chunk = (units + COUNTER_SLOTS - 9) // (COUNTER_SLOTS - 8)
-        chunk = max(chunk, min_chunk)
-        workers = -(-units // chunk)
+        span_max = -(-units // workers)
+        max_q = COUNTER_SLOTS // workers
+        if -(-span_max // chunk) > max_q:
+            chunk = -(-span_max // max_q)
+        desc_rounds = max(1, -(-span_max // chunk))
+        chunks = workers * desc_rounds
     else:
         chunk = 0
-        workers = min(num_cus * waves_per_cu, units)
-    workers = max(workers, 1)
-    workers = (workers + 7) & ~7
-    desc_rounds = 1 if pt > 0 else SHARED_SPLIT
-    assert workers * desc_rounds <= COUNTER_SLOTS
+        workers = max(min(workers, units), 1)
+        workers = (workers + 7) & ~7
+        desc_rounds = SHARED_SPLIT
+        chunks = workers * SHARED_SPLIT
+    assert chunks <= COUNTER_SLOTS
     grouping = groupable and G <= 8 and bs >= 16 and hkv * S <= COUNTER_SLOTS
-    return {"chunk": chunk, "workers": workers, "desc_rounds": desc_rounds,
+    return {"chunk": chunk, "workers": workers, "desc_rounds": desc_rounds, "chunks": chunks,
             "max_members": 16 // G if grouping else 0,
-            "grec_rows": (4 * hkv * S * G + 16 * min(workers, 8192)) if grouping else 0,
-            "flat_rows": 2 * workers * desc_rounds * G}
+            "grec_rows": (4 * hkv * S * G + 16 * min(chunks, 8192)) if grouping else 0,
+            "flat_rows": 2 * chunks * G}
 
 
 def device_plan(tables, lens, hkv, bs, num_blocks, G, hp):
@@ -112,9 +141,15 @@ def device_plan(tables, lens, hkv, bs, num_blocks, G, hp):
         items, seqs, TB = lay_out(grouped)
         T = TB * hkv
         flags = 2 if grouped else (1 if eq.any() else 0)
-        rounds = SHARED_SPLIT if (hp["chunk"] == 0 and flags & 1) else 1
-        workers = hp["workers"] * rounds
-        chunk = hp["chunk"] if hp["chunk"] > 0 else max(1, -(-T // workers))
+        if hp["chunk"] > 0:
+            span = max(1, -(-T // hp["workers"]))
+            chunk = min(hp["chunk"], span)
+            qn = -(-span // chunk)
+            rounds = qn
+        else:
+            rounds = SHARED_SPLIT if flags & 1 else 1
+            chunk = max(1, -(-T // (hp["workers"] * rounds)))
+            span, qn = chunk, 1
         if not grouped:
             break
         RH = 0
@@ -124,13 +159,13 @@ def device_plan(tables, lens, hkv, bs, num_blocks, G, hp):
                 continue
             gr = groups[int(gid[s])]
             lead = real(s) and gr["first"] == s
-            gp = ((gr["k"] + chunk - 1) // chunk + 1) * gr["m"] * G if lead else 0
+            gp = max_pieces(gr["k"], chunk, span, qn) * gr["m"] * G if lead else 0
             if lead:
                 items[gr["item"]]["rbase"] = RH
             if q["s_item"] >= 0:
                 it = items[q["s_item"]]
                 it["rbase"] = RH + gp
-                RH += gp + ((it["len"] + chunk - 1) // chunk + 1) * G
+                RH += gp + max_pieces(it["len"], chunk, span, qn) * G
             else:
                 RH += gp
         for s in range(S):
@@ -144,39 +179,69 @@ def device_plan(tables, lens, hkv, bs, num_blocks, G, hp):
         if RH * hkv <= hp["grec_rows"]:
             break
         grouped = False
-    nv = -(-T // chunk)
-    per_round = ((nv + 7) & ~7) if rounds == 1 else hp["workers"]
+    g = Grid(chunk, span, qn)
     W = hp["workers"]
-    assert rounds <= hp["desc_rounds"]
-    desc = {}
+    spans = -(-T // span)
+    nid = spans * qn
+    if qn > 1:
+        per_round = (spans + 7) & ~7
+        assert per_round <= W
+        used_rounds = qn
+    else:
+        per_round = min(W, (-(-nid // rounds) + 7) & ~7)
+        used_rounds = -(-nid // per_round) if nid else 0
+        # every worker runs `rounds` or `rounds - 1` chunks
+        assert nid == 0 or (used_rounds - 1) * per_round < nid <= used_rounds * per_round
+    assert used_rounds <= hp["desc_rounds"] and nid <= hp["chunks"]
     q8 = per_round >> 3
+
+    def slot(v):
+        if qn > 1:
+            u, rd = divmod(v, qn)
+        else:
+            rd, u = divmod(v, per_round)
+        return rd, (u % q8) * 8 + u // q8
+
+    desc = {}
     for i, it in enumerate(items):
         for h in range(hkv):
             a = h * TB + it["pos"]
             e = a + it["len"]
-            v = (a + chunk - 1) // chunk
-            while v * chunk < e:
-                rd, u = divmod(v, per_round)
-                wg = (u % q8) * 8 + u // q8
-                assert 0 <= rd < rounds and 0 <= wg < W
-                assert (rd, wg) not in desc
-                desc[(rd, wg)] = {"v": v, "h": h, "i": i, "off": v * chunk - a}
+            v = g.of(a)
+            if g.start(v) < a:
                 v += 1
+            while v < nid and g.start(v) < e:
+                rd, wg = slot(v)
+                assert 0 <= rd < used_rounds and 0 <= wg < W
+                assert (rd, wg) not in desc
+                desc[(rd, wg)] = {"v": v, "h": h, "i": i, "off": g.start(v) - a}
+                v += 1
+    nv = sum(1 for v in range(nid) if g.start(v) < T)
     assert len(desc) == nv
-    assert walk_descs(items, TB, hkv, chunk, rounds, hp["workers"]) == desc
+    if qn > 1:   # equal spans: every worker's share is within one block of the others'
+        shares = {}
+        for (rd, wg), d in desc.items():
+            shares[wg] = shares.get(wg, 0) + g.end(d["v"], T) - g.start(d["v"])
+        short = [x for x in shares.values() if x != span]
+        assert len(shares) == spans and short in ([], [T - (spans - 1) * span])
+    assert walk_descs(items, TB, hkv, g, rounds, W) == desc
     return {"items": items, "seqs": seqs, "desc": desc, "T": T, "TB": TB, "NI": len(items), "chunk": chunk,
-            "rounds": rounds, "flags": flags, "RH": RH, "n": n, "groups": groups, "gid": gid,
-            "grouped": grouped}
+            "span": span, "q": qn, "grid": g, "rounds": used_rounds, "flags": flags, "RH": RH, "n": n,
+            "groups": groups, "gid": gid, "grouped": grouped}
 
 
-def walk_descs(items, TB, hkv, C, rounds, W, threads=1024):
+def walk_descs(items, TB, hkv, g, rounds, W, threads=1024):
     """plan_write_descs: each thread takes a contiguous range of chunk ids,
-    binary-searches the first one's item and walks forward."""
+    binary-searches its first chunk's item in each kv head and walks forward."""
     pos = [it["pos"] for it in items]
     NI = len(items)
     T = TB * hkv
-    nv = -(-T // C)
-    per_round = ((nv + 7) & ~7) if rounds == 1 else W
+    spans = -(-T // g.span)
+    nid = spans * g.q
+    if g.q > 1:
+        per_round = (spans + 7) & ~7
+    else:
+        per_round = min(W, (-(-nid // rounds) + 7) & ~7)
     q8 = per_round >> 3
 
     def find(r):
@@ -190,44 +255,35 @@ def walk_descs(items, TB, hkv, C, rounds, W, threads=1024):
         return lo
 
     out = {}
-    per = -(-nv // threads)
+    per = -(-nid // threads)
     for t in range(threads):
-        v = t * per
-        vend = min(v + per, nv)
-        if v >= vend:
-            continue
-        start = v * C
-        h, r = divmod(start, TB)
-        i = find(r)
-        rd, u = divmod(v, per_round)
-        uq, ur = divmod(u, q8)
-        while True:
+        h, i = -1, 0
+        for v in range(t * per, min((t + 1) * per, nid)):
+            st = g.start(v)
+            if st >= T:
+                break
+            nh, r = divmod(st, TB)
+            if nh != h:
+                h, i = nh, find(r)
             while i + 1 < NI and pos[i + 1] <= r:
                 i += 1
-            key = (rd, ur * 8 + uq)
+            if g.q > 1:
+                u, rd = divmod(v, g.q)
+            else:
+                rd, u = divmod(v, per_round)
+            key = (rd, (u % q8) * 8 + u // q8)
             assert key not in out
             out[key] = {"v": v, "h": h, "i": i, "off": r - pos[i]}
-            v += 1
-            if v >= vend:
-                break
-            r += C
-            if r >= TB:
-                while r >= TB:
-                    r -= TB
-                    h += 1
-                i = find(r)
-            ur += 1
-            if ur == q8:
-                ur = 0
-                uq += 1
-                if uq == 8:
-                    uq, rd = 0, rd + 1
     return out
 
 
-def walk(pl, hkv, bs, G, hp, max_blocks):
-    """Every worker's chunks (decode_chunk / grouped_chunk) and merges."""
-    items, T, TB, NI, C = pl["items"], pl["T"], pl["TB"], pl["NI"], pl["chunk"]
+def walk(pl, hkv, bs, G, hp, max_blocks, span_runs=False):
+    """Every worker's chunks (decode_chunk / grouped_chunk) and merges.
+
+    span_runs: flat plans with partitions as the matrix-core runs take them:
+    a worker streams its whole span from its first round's chunk, and a run
+    that crosses chunk boundaries leaves one record per chunk."""
+    items, T, TB, NI, g = pl["items"], pl["T"], pl["TB"], pl["NI"], pl["grid"]
     n = pl["n"]
     S = len(n)
     nb = -(-n // bs)
@@ -241,11 +297,16 @@ def walk(pl, hkv, bs, G, hp, max_blocks):
 
     def pieces(h, ipos, ilen):
         a = h * TB + ipos
-        return (a + ilen - 1) // C - a // C + 1
+        return g.of(a + ilen - 1) - g.of(a) + 1
 
     order = sorted(pl["desc"].items(), key=lambda kv: np.random.default_rng(kv[1]["v"]).random())
+    span_runs = span_runs and g.q > 1 and not grouped
     for (rd, wg), d in order:
-        start, end = d["v"] * C, min(d["v"] * C + C, T)
+        if span_runs and rd > 0:
+            continue
+        start, end = g.start(d["v"]), g.end(d["v"], T)
+        if span_runs:
+            end = min((d["v"] // g.q + 1) * g.span, T)
         h, i, off, pos = d["h"], d["i"], d["off"], start
         while True:
             it = items[i]
@@ -261,8 +322,8 @@ def walk(pl, hkv, bs, G, hp, max_blocks):
                         assert b < n[s + j] // bs   # inside every member's full blocks
                         shared_reads[(h, s + j, b)] = shared_reads.get((h, s + j, b), 0) + 1
                 pg = pieces(h, it["pos"], it["len"])
-                k = d["v"] - (h * TB + it["pos"]) // C
-                assert 0 <= k < pg <= -(-it["len"] // C) + 1
+                k = d["v"] - g.of(h * TB + it["pos"])
+                assert 0 <= k < pg <= max_pieces(it["len"], g.chunk, g.span, g.q)
                 rows = it["m"] * G
                 row0 = h * pl["RH"] + it["rbase"] + k * rows
                 for j in range(it["m"]):
@@ -279,29 +340,36 @@ def walk(pl, hkv, bs, G, hp, max_blocks):
                 pg = pieces(h, it["g_pos"], it["g_len"]) if grouped and it.get("g_len", 0) > 0 else 0
                 whole = ps + pg == 1
                 if not grouped:
-                    whole = off == 0 and off + ln == it["len"]
+                    whole = off == 0 and off + ln == it["len"] and g.of(pos) == g.of(pos + ln - 1)
                 if whole:
                     written[h, s] += 1
                 elif grouped:
-                    k = d["v"] - (h * TB + it["pos"]) // C
+                    k = d["v"] - g.of(h * TB + it["pos"])
+                    assert k < max_pieces(it["len"], g.chunk, g.span, g.q)
                     row0 = h * pl["RH"] + it["rbase"] + k * G
                     for r in range(G):
                         key = row0 + r
                         assert key not in recs and 0 <= key < hkv * pl["RH"] <= cap_rows
                         recs[key] = (h, s, "s", k)
                     counters[(h, s)] = counters.get((h, s), 0) + 1
-                else:   # flat: slot 0/1 of the worker, counter of the run's first worker
-                    kk = 0 if pos == start else 1
-                    key = ("flat", 2 * d["v"] + kk)
-                    assert key not in recs and 2 * d["v"] + kk < 2 * hp["workers"] * hp["desc_rounds"]
-                    recs[key] = (h, s)
+                else:   # flat: slot 0/1 of each chunk, counter of the run's first chunk
+                    w = g.of(pos)
+                    wstart = g.start(w)
+                    assert span_runs or (w == d["v"] and wstart == start)
+                    nparts = g.of(pos + ln - 1) - w + 1
+                    assert span_runs or nparts == 1
+                    for k in range(nparts):
+                        kk = (0 if pos == wstart else 1) if k == 0 else 0
+                        key = ("flat", 2 * (w + k) + kk)
+                        assert key not in recs and 2 * (w + k) + kk < 2 * hp["chunks"]
+                        recs[key] = (h, s)
                     seg = pos - off
-                    fw, lw = seg // C, (seg + it["len"] - 1) // C
+                    fw, lw = g.of(seg), g.of(seg + it["len"] - 1)
                     assert fw < lw and fw < COUNTER_SLOTS
-                    counters[("flat", fw)] = counters.get(("flat", fw), 0) + 1
+                    counters[("flat", fw)] = counters.get(("flat", fw), 0) + nparts
                     if counters[("flat", fw)] == lw - fw + 1:
                         for v in range(fw, lw + 1):
-                            kk2 = 0 if v * C >= seg else 1
+                            kk2 = 0 if g.start(v) >= seg else 1
                             assert recs.get(("flat", 2 * v + kk2)) == (h, s)
                         written[h, s] += 1
                         counters[("flat", fw)] = 0
@@ -350,6 +418,8 @@ def replay(tables, lens, hkv, bs, pt, G=1, num_blocks=None, **kw):
     hp = host_plan(S, hkv, mb, bs, G, pt, **kw)
     pl = device_plan(tables, np.asarray(lens), hkv, bs, num_blocks, G, hp)
     walk(pl, hkv, bs, G, hp, mb)
+    if pl["q"] > 1:
+        walk(pl, hkv, bs, G, hp, mb, span_runs=True)
     return pl
 
 
@@ -478,3 +548,5 @@ def test_workload_shapes_fit():
                     G=wl.group, num_blocks=wl.num_blocks)
         shared = len(set(wl.parent)) < wl.num_seqs
         assert bool(pl["flags"] & 2) == shared, wl.name
+        if wl.partition_tokens:   # equal spans per worker, each cut into whole partitions and a rest
+            assert pl["chunk"] == wl.partition_tokens // wl.block_size and pl["q"] > 1, wl.name

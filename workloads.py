@@ -299,10 +299,14 @@ def small_configs() -> Dict[str, Workload]:
 def variant_configs() -> Dict[str, Workload]:
     """Variants of the decode workloads at full size: block sizes 8 and 64
     for the LLaMA-7B shape, an 8:1 query group (32 q / 4 KV heads) in fp8 and
-    bf16, and per-head fp8 scales on the GQA long-context batch."""
+    bf16, per-head fp8 scales on the GQA long-context batch, and the LLaMA-7B
+    shape at 1024 and 2048 sequences (the batch past which a decode launch's
+    fixed cost would show)."""
     ws = [config_c3(8), config_c3(64),
           config_c5("fp8e4m3", hkv=4, name="c5_gqa8_long_fp8e4m3"), config_c5("bf16", hkv=4, name="c5_gqa8_long_bf16"),
-          config_c5("fp8e4m3", head_scales=True, name="c5_gqa_long_fp8_headscale")]
+          config_c5("fp8e4m3", head_scales=True, name="c5_gqa_long_fp8_headscale"),
+          config_c3(16, num_seqs=1024, index=16, name="c3_llama7b_bf16_bs16_s1024"),
+          config_c3(16, num_seqs=2048, index=17, name="c3_llama7b_bf16_bs16_s2048")]
     return {w.name: w for w in ws}
 
 
