@@ -9,9 +9,9 @@ namespace pkv {
 
 // Lay out the items of every sequence, grouped or flat, and the chunk size;
 // in grouped mode also every item's record rows.  Only the planner's state
-// is written here (each sequence's S-item, each group's G-item, every item's
-// first block in item_pos when it is in LDS); returns ok = false when a
-// grouped layout's records would not fit the workspace.
+// is written here (each sequence's S-item, each group's G-item, and, when it
+// is in LDS, every item's first block and sequence in item_ls); returns
+// ok = false when a grouped layout's records would not fit the workspace.
 struct Layout {
   int NI, TB, chunk, span, q, rounds, flags;
   int64_t RH;
@@ -24,7 +24,7 @@ __device__ inline int max_pieces(int len, int chunk, int span, int q) {
 }
 
 __device__ __attribute__((always_inline)) inline Layout plan_layout(const PlanParams& pp, PlanScratch* scr,
-                                                                    PlanGroup* grp, int* item_pos, bool grouped,
+                                                                    PlanGroup* grp, int2* item_ls, bool grouped,
                                                                     bool has_eq, int* lds) {
   const int S = pp.num_seqs;
   const int tid = threadIdx.x;
@@ -83,13 +83,13 @@ __device__ __attribute__((always_inline)) inline Layout plan_layout(const PlanPa
         g->item = ib;
         g->pos = bb;
         g->rbase = (int32_t)rb;
-        if (item_pos) item_pos[ib] = bb;
+        if (item_ls) item_ls[ib] = make_int2(bb, s);
       }
       sc->s_item = it.suffix > 0 ? ib + (it.lead ? 1 : 0) : -1;
       sc->s_pos = bb + (it.lead ? it.k : 0);
       sc->s_len = it.suffix;
       sc->s_rbase = (int32_t)(rb + gp);
-      if (item_pos && it.suffix > 0) item_pos[sc->s_item] = sc->s_pos;
+      if (item_ls && it.suffix > 0) item_ls[sc->s_item] = make_int2(sc->s_pos, s);
     }
     icarry += tot.x;
     bcarry += tot.y;
@@ -128,82 +128,156 @@ __device__ __attribute__((always_inline)) inline void plan_write_items(const Pla
 
 // The descriptors.  Thread t takes a contiguous range of chunk ids (stream
 // order), finds the first one's item by binary search over the items' first
-// blocks and walks forward from there.  Where a chunk runs:
+// blocks and walks forward from there, stepping chunk positions and worker
+// slots without divisions.  Where a chunk runs:
 //   - uniform cut (q = 1): chunk v in round v / per_round, with id
 //     v % per_round;
 //   - partitions (q > 1): chunk v, the (v % q)-th of span v / q, in round
 //     v % q, with id v / q, so a worker runs its span's chunks in order;
 // slot b runs on XCD b % 8 and takes id (b % 8) * (per_round / 8) + b / 8.
-// Slots without a chunk are marked empty.
+// A descriptor also carries the sequence, blocks and token limit of the
+// chunk's first item (flat plans start from them without an item load).
+// Slots without a chunk are marked empty.  item_at(i) gives item i's first
+// block, sequence, blocks and token limit.
+template <typename ItemAt>
 __device__ __attribute__((always_inline)) inline void plan_write_descs(const PlanParams& pp, const Layout& L,
-                                                                       const int32_t* posp, int stride) {
+                                                                       const ItemAt& item_at) {
   const int tid = threadIdx.x;
-  const ChunkGrid g{L.chunk, L.span, L.q};
-  const int TB = L.TB, W = pp.num_workers;
+  const int TB = L.TB, W = pp.num_workers, C = L.chunk, SP = L.span, Q = L.q;
   const int T = TB * pp.num_kv_heads;
-  const int spans = (T + L.span - 1) / L.span;
+  const int spans = (T + SP - 1) / SP;
   // chunk ids; those of the last span that start past the stream's end hold
   // no chunk (and are the last ids)
-  const int nid = spans * L.q;
+  const int nid = spans * Q;
   int per_round, rounds;
-  if (L.q > 1) {
+  if (Q > 1) {
     per_round = (spans + 7) & ~7;   // spans <= W, a multiple of 8
-    rounds = L.q;
+    rounds = Q;
   } else {
     // spread evenly over the rounds: a multiple of 8, at most W
     per_round = min(W, ((nid + L.rounds - 1) / L.rounds + 7) & ~7);
     rounds = nid > 0 ? (nid + per_round - 1) / per_round : 0;   // rounds that hold a chunk
   }
   const int q8 = per_round >> 3;
-  auto slot_of = [&](int v) {
-    int rd, u;
-    if (L.q > 1) {
-      u = v / L.q;
-      rd = v - u * L.q;
-    } else {
-      rd = v / per_round;
-      u = v - rd * per_round;
-    }
-    const int uq = u / q8;
-    return rd * W + (u - uq * q8) * 8 + uq;
-  };
-  auto pos_of = [&](int i) { return posp[(int64_t)i * stride]; };
+  // one pass per span (flat plans): only the first chunk of each span has a
+  // descriptor (round 0, id = span)
+  const bool one_pass = Q > 1 && pp.span_runs && !(L.flags & kPlanGrouped);
   auto find = [&](int r) {   // the last item whose first block is <= r
     int lo = 0, hi = L.NI;
     while (hi - lo > 1) {
       const int mid = (lo + hi) >> 1;
-      if (pos_of(mid) <= r) lo = mid; else hi = mid;
+      if (item_at(mid).x <= r) lo = mid; else hi = mid;
     }
     return lo;
   };
-  const int per = (nid + kPlanThreads - 1) / kPlanThreads;
-  const int vend = min((tid + 1) * per, nid);
-  int h = -1, i = 0;
-  for (int v = tid * per; v < vend; ++v) {
-    const int st = g.start(v);
-    if (st >= T) break;
-    const int nh = st / TB, r = st - nh * TB;
-    if (nh != h) {   // this thread's first chunk of a kv head: its items start again
-      h = nh;
-      i = find(r);
+  if (one_pass) {
+    const int per = (spans + kPlanThreads - 1) / kPlanThreads;
+    int u = tid * per;
+    const int uend = min(u + per, spans);
+    if (u < uend) {
+      int h = u * SP / TB, rr = u * SP - h * TB;
+      int i = find(rr);
+      int idq = u / q8, idr = u - idq * q8;
+      for (;;) {
+        while (i + 1 < L.NI && item_at(i + 1).x <= rr) ++i;
+        const int4 it = item_at(i);
+        put_desc(pp.desc + idr * 8 + idq, PlanDesc{u * Q, h, i, rr - it.x, it.y, it.z, it.w, 0});
+        if (++u >= uend) break;
+        if (++idr == q8) {
+          idr = 0;
+          ++idq;
+        }
+        rr += SP;
+        if (rr >= TB) {
+          while (rr >= TB) {
+            rr -= TB;
+            ++h;
+          }
+          i = find(rr);
+        }
+      }
     }
-    while (i + 1 < L.NI && pos_of(i + 1) <= r) ++i;
-    put_desc(pp.desc + slot_of(v), PlanDesc{v, h, i, r - pos_of(i)});
+  }
+  const int per = one_pass ? 0 : (nid + kPlanThreads - 1) / kPlanThreads;
+  int v = tid * per;
+  const int vend = min(v + per, nid);
+  if (v < vend) {
+    // chunk v: span u, its r-th chunk; stream block st; round rd, id (idq, idr)
+    int u, r, rd, id;
+    if (Q > 1) {
+      u = v / Q;
+      r = v - u * Q;
+      rd = r;
+      id = u;
+    } else {
+      u = v;
+      r = 0;
+      rd = v / per_round;
+      id = v - rd * per_round;
+    }
+    int st = u * SP + r * C;
+    int h = st / TB, rr = st - h * TB;
+    int i = find(rr);
+    int idq = id / q8, idr = id - idq * q8;
+    while (st < T) {
+      while (i + 1 < L.NI && item_at(i + 1).x <= rr) ++i;
+      const int4 it = item_at(i);
+      put_desc(pp.desc + rd * W + idr * 8 + idq, PlanDesc{v, h, i, rr - it.x, it.y, it.z, it.w, 0});
+      if (++v >= vend) break;
+      int nst;
+      if (Q > 1 && ++r < Q) {   // the span's next chunk, in the next round
+        nst = st + C;
+        ++rd;
+      } else {                  // the next span (or chunk), on the next id
+        r = 0;
+        nst = ++u * SP;
+        if (Q > 1) rd = 0;
+        if (++idr == q8) {
+          idr = 0;
+          if (++idq == 8) {
+            idq = 0;
+            ++rd;
+          }
+        }
+      }
+      rr += nst - st;
+      st = nst;
+      if (rr >= TB) {   // a later kv head: its items start again from the first
+        while (rr >= TB) {
+          rr -= TB;
+          ++h;
+        }
+        i = find(rr);
+      }
+    }
   }
   // the first round's descriptors are written even when no chunk exists
-  for (int k = tid; k < max(rounds, 1) * W; k += kPlanThreads) {
-    const int rd = k / W, b = k - rd * W;
-    const int u = (b & 7) * q8 + (b >> 3);
-    const int v = L.q > 1 ? u * L.q + rd : rd * per_round + u;
-    if (!(b < per_round && v < nid && g.start(v) < T)) put_desc(pp.desc + k, PlanDesc{-1, 0, 0, 0});
+  const int n_slots = one_pass ? W : max(rounds, 1) * W;
+  int b = tid % W, brd = tid / W;
+  const int db = kPlanThreads % W, drd = kPlanThreads / W;
+  for (int k = tid; k < n_slots; k += kPlanThreads) {
+    const int uu = (b & 7) * q8 + (b >> 3);
+    bool has = b < per_round;
+    if (Q > 1)
+      has = has && uu < spans && brd < Q && uu * SP + brd * C < T;
+    else
+      has = has && brd * per_round + uu < nid;
+    if (!has) put_desc(pp.desc + k, PlanDesc{-1, 0, 0, 0, 0, 0, 0, 0});
+    b += db;
+    brd += drd;
+    if (b >= W) {
+      b -= W;
+      ++brd;
+    }
   }
   if (tid == 0)
-    *pp.header = PlanHeader{L.chunk, T, TB, L.NI, L.flags, rounds, (int32_t)L.RH, L.span, L.q, {0, 0, 0}};
+    *pp.header = PlanHeader{L.chunk, T, TB, L.NI, L.flags, one_pass ? 1 : rounds, (int32_t)L.RH, L.span, L.q,
+                            {0, 0, 0}};
 }
 
 template <bool IN_LDS>
-__device__ __attribute__((always_inline)) inline void plan_body(const PlanParams& pp, PlanScratch* scr, PlanGroup* grp, int* item_pos, int* lds,
-                                 int* any) {
+__device__ __attribute__((always_inline)) inline void plan_body(const PlanParams& pp, PlanScratch* scr,
+                                                                PlanGroup* grp, int2* item_ls, int* lds, int* any) {
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int S = pp.num_seqs;
@@ -324,10 +398,10 @@ __device__ __attribute__((always_inline)) inline void plan_body(const PlanParams
 
   // D. Items and the chunk size (grouped records that would not fit the
   //    workspace: laid out again without groups).
-  Layout L = plan_layout(pp, scr, grp, item_pos, grouped, has_eq, lds);
+  Layout L = plan_layout(pp, scr, grp, item_ls, grouped, has_eq, lds);
   if (!L.ok) {
     __syncthreads();
-    L = plan_layout(pp, scr, grp, item_pos, false, has_eq, lds);
+    L = plan_layout(pp, scr, grp, item_ls, false, has_eq, lds);
   }
   if (!(L.flags & kPlanGrouped)) L.RH = 0;
   if (has_empty) L.flags |= kPlanEmpty;
@@ -338,9 +412,20 @@ __device__ __attribute__((always_inline)) inline void plan_body(const PlanParams
   //    so no barrier waits for these stores; in the workspace the descriptor
   //    search reads the items' first blocks from the items.
   plan_write_items(pp, scr, grp, (L.flags & kPlanGrouped) != 0);
-  if constexpr (!IN_LDS) __syncthreads();
-  plan_write_descs(pp, L, IN_LDS ? item_pos : &pp.items[0].pos,
-                   IN_LDS ? 1 : (int)(sizeof(PlanItem) / sizeof(int32_t)));
+  if constexpr (IN_LDS) {
+    // flat items are whole sequences: blocks and token limit from the length
+    plan_write_descs(pp, L, [&](int i) {
+      const int2 e = item_ls[i];
+      const int n = scr[e.y].n;
+      return make_int4(e.x, e.y, (n + (1 << pp.log2_bs) - 1) >> pp.log2_bs, n);
+    });
+  } else {
+    __syncthreads();
+    plan_write_descs(pp, L, [&](int i) {
+      const PlanItem* it = pp.items + i;
+      return make_int4(it->pos, it->s, it->len, it->n);
+    });
+  }
 
 }
 
@@ -353,11 +438,11 @@ __global__ __launch_bounds__(kPlanThreads) void paged_decode_plan_kernel(const P
   __shared__ int any[2];
   __shared__ PlanScratch scr_lds[kPlanLdsSeqs];
   __shared__ PlanGroup grp_lds[kPlanLdsSeqs];
-  __shared__ int pos_lds[kPlanLdsItems];
+  __shared__ int2 item_lds[kPlanLdsItems];
   if (threadIdx.x < 2) any[threadIdx.x] = 0;
   __syncthreads();
   if (pp.num_seqs <= kPlanLdsSeqs)
-    plan_body<true>(pp, scr_lds, grp_lds, pos_lds, lds, any);
+    plan_body<true>(pp, scr_lds, grp_lds, item_lds, lds, any);
   else
     plan_body<false>(pp, pp.scr, pp.groups, nullptr, lds, any);
 }
@@ -563,6 +648,8 @@ kv_status_t decode(const kv_pool_t* pool, const void* q, kv_dtype_t q_dtype, voi
     pp.num_workers = plan.num_workers;
     pp.desc_rounds = plan.desc_rounds;
     pp.max_members = pair_mfma ? plan.max_members : 0;   // groups run on the matrix cores
+    // matrix-core runs stream a span of partitions in one pass
+    pp.span_runs = mfma && pair_mfma && pool->log2_block_size >= 4 ? 1 : 0;
     pp.shared_split = kSharedSplit;
     pp.counter_slots = kCounterSlots;
     hipLaunchKernelGGL(paged_decode_plan_kernel, dim3(1), dim3(kPlanThreads), 0, s, pp);

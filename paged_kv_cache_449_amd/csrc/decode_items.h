@@ -164,16 +164,13 @@ __device__ inline void group_piece(const DecodeParams& p, const ChunkCtx& d, int
   }
 }
 
-// Stream chunk d.v of a grouped plan, whose first item `first` the caller
-// has loaded; returns item `next_i`, loaded while the chunk's last piece
-// streams.
+// Stream chunk d.v of a grouped plan.
 template <typename KV, typename QT, int D, int G, bool MFMA>
-__device__ inline PlanItem grouped_chunk(const DecodeParams& p, const ChunkCtx& d, const PlanItem& first,
-                                         int next_i) {
+__device__ inline void grouped_chunk(const DecodeParams& p, const ChunkCtx& d) {
   const int start = d.grid().start(d.v);
   const int end = d.grid().end(d.v, d.T);
   int h = d.h, i = d.i, off = d.off, pos = start;
-  PlanItem it = first;
+  PlanItem it = load_item(p.items + i);
   while (true) {
     const int len = min(it.len - off, end - pos);
     int ni = i + 1, nh = h;
@@ -182,13 +179,13 @@ __device__ inline PlanItem grouped_chunk(const DecodeParams& p, const ChunkCtx& 
       ++nh;
     }
     const bool more = pos + len < end;
-    const PlanItem nx = load_item(p.items + (more ? ni : next_i));   // in flight during the run
+    const PlanItem nx = load_item(p.items + ni);   // in flight during the run
     if (it.m > 0)
       group_piece<KV, QT, D, G>(p, d, h, it, off, len);
     else
       seq_piece<KV, QT, D, G, MFMA>(p, d, h, it, off, len);
     pos += len;
-    if (!more) return nx;
+    if (!more) return;
     i = ni;
     h = nh;
     it = nx;

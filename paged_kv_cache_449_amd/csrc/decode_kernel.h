@@ -622,19 +622,18 @@ __device__ inline void valu_run(const DecodeParams& p, int w, const ChunkGrid& g
 
 namespace pkv {
 
-// Stream chunk d.v of a flat plan, whose items are the non-empty sequences,
-// and whose first item `first` the caller has loaded; returns item `next_i`
-// (the first item of the worker's next chunk), loaded while the chunk's last
-// run streams.  SPAN (matrix-core runs over partitions): stream the chunk's
-// whole span, the runs leaving a record at every chunk boundary they cross.
+// Stream chunk d.v of a flat plan, whose items are the non-empty sequences;
+// the descriptor names the chunk's first item.  SPAN (matrix-core runs over
+// partitions): stream the chunk's whole span, the runs leaving a record at
+// every chunk boundary they cross.
 template <typename KV, typename QT, int D, int G, bool MFMA, int POL, bool SPAN = false>
-__device__ inline FlatItem decode_chunk(const DecodeParams& p, const ChunkCtx& d, const FlatItem& first, int next_i) {
+__device__ inline void decode_chunk(const DecodeParams& p, const ChunkCtx& d) {
   static_assert(!SPAN || MFMA, "span runs are matrix-core runs");
   const ChunkGrid grid = d.grid();
   const int start = grid.start(d.v);
   const int end = SPAN ? grid.span_end(d.v, d.T) : grid.end(d.v, d.T);
   int h = d.h, i = d.i, off = d.off, pos = start;
-  FlatItem it = first;
+  FlatItem it{d.s, d.len, d.n};
   while (true) {
     const int len = min(it.len - off, end - pos);
     // the next run's item loads while this run streams
@@ -644,7 +643,7 @@ __device__ inline FlatItem decode_chunk(const DecodeParams& p, const ChunkCtx& d
       ++nh;
     }
     const bool more = pos + len < end;
-    const FlatItem nx = load_flat_item(p.items + (more ? ni : next_i));
+    const FlatItem nx = load_flat_item(p.items + ni);
     // the chunk where the run starts, and that chunk's first block
     const int w = SPAN ? grid.of(pos) : d.v;
     const int wstart = SPAN ? grid.start(w) : start;
@@ -653,7 +652,7 @@ __device__ inline FlatItem decode_chunk(const DecodeParams& p, const ChunkCtx& d
     else
       valu_run<KV, QT, D, G, POL>(p, w, grid, wstart, pos, it.s, h, off, len, it.n, it.len);
     pos += len;
-    if (!more) return nx;
+    if (!more) return;
     i = ni;
     h = nh;
     it = nx;
@@ -661,23 +660,15 @@ __device__ inline FlatItem decode_chunk(const DecodeParams& p, const ChunkCtx& d
   }
 }
 
-// A worker's chunks, one per round.  The next round's descriptor loads as
-// the current chunk starts, and its first item while the chunk's last run
-// streams, so a new chunk starts with the loads of its first run.  Item is
-// the plan entry the chunks read (FlatItem or PlanItem).
-template <typename Item, typename Load, typename Chunk>
-__device__ inline void run_rounds(const DecodeParams& p, const PlanHeader& H, int rounds, Load load, Chunk chunk) {
+// A worker's chunks, one per round; the next round's descriptor loads as the
+// current chunk starts.
+template <typename Chunk>
+__device__ inline void run_rounds(const DecodeParams& p, const PlanHeader& H, int rounds, Chunk chunk) {
   const PlanDesc* dp = p.desc + blockIdx.x;
   PlanDesc cur = load_desc(dp);
-  Item it = load(p.items + max(cur.i, 0));
   for (int rd = 0; rd < rounds; ++rd) {
     const PlanDesc nxt = load_desc(dp + (int64_t)min(rd + 1, rounds - 1) * p.num_workers);
-    // an empty slot's item index is 0, so this load stays in the items
-    const int next_i = max(nxt.i, 0);
-    if (cur.v < 0)
-      it = load(p.items + next_i);
-    else
-      it = chunk(chunk_ctx(H, cur), it, next_i);
+    if (cur.v >= 0) chunk(chunk_ctx(H, cur));
     cur = nxt;
   }
 }
@@ -721,39 +712,29 @@ void paged_decode_kernel(const DecodeParams p) {
   const PlanHeader H = load_header(p.header);
   if ((H.flags & kPlanEmpty) && blockIdx.x == 0) zero_empty_rows<QT, D, G>(p);
   if (H.rounds == 0) return;
-  auto flat = [](const PlanItem* a) { return load_flat_item(a); };
   if (H.flags & kPlanGrouped) {
     if constexpr (kGroupable)
-      run_rounds<PlanItem>(p, H, H.rounds, [](const PlanItem* a) { return load_item(a); },
-                           [&](const ChunkCtx& d, const PlanItem& it, int next_i) {
-                             return grouped_chunk<KV, QT, D, G, MFMA>(p, d, it, next_i);
-                           });
+      run_rounds(p, H, H.rounds, [&](const ChunkCtx& d) { grouped_chunk<KV, QT, D, G, MFMA>(p, d); });
     return;
   }
   if constexpr (MFMA) {
     // partitions: a matrix-core worker streams its span in one pass (the
-    // first round's chunk opens it), leaving a record per partition
+    // span's first chunk, its one descriptor, opens it), leaving a record per
+    // partition
     if (H.q > 1) {
       if (H.flags & kPlanShared)
-        run_rounds<FlatItem>(p, H, 1, flat, [&](const ChunkCtx& d, const FlatItem& it, int next_i) {
-          return decode_chunk<KV, QT, D, G, MFMA, kSharedPolicy, true>(p, d, it, next_i);
-        });
+        run_rounds(p, H, 1,
+                   [&](const ChunkCtx& d) { decode_chunk<KV, QT, D, G, MFMA, kSharedPolicy, true>(p, d); });
       else
-        run_rounds<FlatItem>(p, H, 1, flat, [&](const ChunkCtx& d, const FlatItem& it, int next_i) {
-          return decode_chunk<KV, QT, D, G, MFMA, kStreamPolicy, true>(p, d, it, next_i);
-        });
+        run_rounds(p, H, 1,
+                   [&](const ChunkCtx& d) { decode_chunk<KV, QT, D, G, MFMA, kStreamPolicy, true>(p, d); });
       return;
     }
   }
-  if (H.flags & kPlanShared) {
-    run_rounds<FlatItem>(p, H, H.rounds, flat, [&](const ChunkCtx& d, const FlatItem& it, int next_i) {
-      return decode_chunk<KV, QT, D, G, MFMA, kSharedPolicy>(p, d, it, next_i);
-    });
-  } else {
-    run_rounds<FlatItem>(p, H, H.rounds, flat, [&](const ChunkCtx& d, const FlatItem& it, int next_i) {
-      return decode_chunk<KV, QT, D, G, MFMA, kStreamPolicy>(p, d, it, next_i);
-    });
-  }
+  if (H.flags & kPlanShared)
+    run_rounds(p, H, H.rounds, [&](const ChunkCtx& d) { decode_chunk<KV, QT, D, G, MFMA, kSharedPolicy>(p, d); });
+  else
+    run_rounds(p, H, H.rounds, [&](const ChunkCtx& d) { decode_chunk<KV, QT, D, G, MFMA, kStreamPolicy>(p, d); });
 }
 
 // Launch one instantiation; defined per KV/Q dtype pair in decode_*.hip.

@@ -60,12 +60,16 @@ struct PlanSeq {
   int32_t s_rbase;
 };
 
-// Start of one worker's chunk in one round (16 bytes).
+// Start of one worker's chunk in one round (32 bytes).
 struct PlanDesc {
   int32_t v;       // chunk id; -1: no chunk for this worker in this round
   int32_t h;       // kv head of the chunk's first block
   int32_t i;       // item of the chunk's first block
   int32_t off;     // block of the chunk's start within that item
+  int32_t s;       // that item's sequence, blocks and token limit (flat
+  int32_t len;     // plans; a grouped chunk loads its item)
+  int32_t n;
+  int32_t pad;
 };
 
 // How the stream of T blocks is cut into chunks: spans of `span` blocks,
@@ -114,7 +118,7 @@ struct PlanHeader {
 // A worker's view of one chunk: the launch's header and the chunk's start.
 struct ChunkCtx {
   int32_t chunk, T, TB, NI, flags, rounds, RH, span, q;
-  int32_t v, h, i, off;
+  int32_t v, h, i, off, s, len, n;
   __device__ ChunkGrid grid() const { return ChunkGrid{chunk, span, q}; }
 };
 
@@ -171,6 +175,7 @@ struct PlanParams {
   int32_t max_members;       // sequences per group; < 2 = no grouping
   int32_t shared_split;      // rounds of the shared mode (kSharedSplit)
   int32_t counter_slots;     // arrival counters (grouped mode uses one per (kv head, sequence))
+  int32_t span_runs;         // the decode kernel streams a span of partitions in one pass
 };
 
 // Sequences whose planner state fits the work-group's LDS; larger batches
@@ -185,7 +190,11 @@ __device__ inline void put_item(PlanItem* dst, const PlanItem& v) {
   d[1] = make_int4(v.pos, v.m, v.rbase, v.member);
   d[2] = make_int4(v.g_pos, v.g_len, v.g_rbase, v.g_m);
 }
-__device__ inline void put_desc(PlanDesc* dst, const PlanDesc& v) { *(int4*)dst = make_int4(v.v, v.h, v.i, v.off); }
+__device__ inline void put_desc(PlanDesc* dst, const PlanDesc& v) {
+  int4* d = (int4*)dst;
+  d[0] = make_int4(v.v, v.h, v.i, v.off);
+  d[1] = make_int4(v.s, v.len, v.n, 0);
+}
 
 // The decode kernel reads the plan with scalar loads: the addresses are
 // uniform, and the data was written by the planner before the launch started
@@ -212,10 +221,11 @@ __device__ inline PlanHeader load_header(const PlanHeader* h) {
 }
 __device__ inline PlanDesc load_desc(const PlanDesc* d) {
   const const_words w = (const_words)d;
-  return PlanDesc{w[0], w[1], w[2], w[3]};
+  return PlanDesc{w[0], w[1], w[2], w[3], w[4], w[5], w[6], 0};
 }
 __device__ inline ChunkCtx chunk_ctx(const PlanHeader& H, const PlanDesc& d) {
-  return ChunkCtx{H.chunk, H.T, H.TB, H.NI, H.flags, H.rounds, H.RH, H.span, H.q, d.v, d.h, d.i, d.off};
+  return ChunkCtx{H.chunk, H.T, H.TB, H.NI, H.flags, H.rounds, H.RH, H.span, H.q,
+                  d.v, d.h, d.i, d.off, d.s, d.len, d.n};
 }
 
 constexpr int kPlanThreads = 1024;

@@ -47,7 +47,11 @@ kv_status_t fill(kv_pool_t* p, int32_t num_blocks, int32_t block_size, int32_t n
   e = getenv("PAGEDKV_DECODE_MFMA");
   p->decode_mfma = !(e && e[0] == '0');
   e = getenv("PAGEDKV_PREFILL_PATH");
-  p->prefill_shape = !e ? -1 : strcmp(e, "wave") == 0 ? 0 : strcmp(e, "group") == 0 ? 1 : strcmp(e, "unit") == 0 ? 2 : -1;
+  p->prefill_shape = !e                          ? -1
+                     : strcmp(e, "wave") == 0   ? 0
+                     : strcmp(e, "group") == 0  ? 1
+                     : strcmp(e, "unit") == 0   ? 2
+                                                : -1;
   // fp8 pools: the per-kv-head scale table, so that setting scales later
   // allocates nothing
   if (dtype == KV_FP8_E4M3FN) {

@@ -70,7 +70,7 @@ def host_plan(S, hkv, max_blocks, bs, G, pt, num_cus=256, waves_per_cu=8, groupa
             "flat_rows": 2 * chunks * G}
 
 
-def device_plan(tables, lens, hkv, bs, num_blocks, G, hp):
+def device_plan(tables, lens, hkv, bs, num_blocks, G, hp, span_runs=False):
     """paged_decode_plan_kernel, sequentially (its scans give the same values)."""
     S, max_blocks = tables.shape
     max_len = max_blocks * bs
@@ -202,6 +202,7 @@ def device_plan(tables, lens, hkv, bs, num_blocks, G, hp):
             rd, u = divmod(v, per_round)
         return rd, (u % q8) * 8 + u // q8
 
+    one_pass = qn > 1 and span_runs and not grouped
     desc = {}
     for i, it in enumerate(items):
         for h in range(hkv):
@@ -211,37 +212,48 @@ def device_plan(tables, lens, hkv, bs, num_blocks, G, hp):
             if g.start(v) < a:
                 v += 1
             while v < nid and g.start(v) < e:
+                if one_pass and v % qn:   # only each span's first chunk
+                    v += 1
+                    continue
                 rd, wg = slot(v)
                 assert 0 <= rd < used_rounds and 0 <= wg < W
                 assert (rd, wg) not in desc
-                desc[(rd, wg)] = {"v": v, "h": h, "i": i, "off": g.start(v) - a}
+                desc[(rd, wg)] = {"v": v, "h": h, "i": i, "off": g.start(v) - a, "s": it["s"], "n": it["n"],
+                                  "len": it["len"]}
                 v += 1
-    nv = sum(1 for v in range(nid) if g.start(v) < T)
+    nv = sum(1 for v in range(nid) if g.start(v) < T and not (one_pass and v % qn))
     assert len(desc) == nv
-    if qn > 1:   # equal spans: every worker's share is within one block of the others'
+    if qn > 1 and not one_pass:   # equal spans: every worker's share is within one block of the others'
         shares = {}
         for (rd, wg), d in desc.items():
             shares[wg] = shares.get(wg, 0) + g.end(d["v"], T) - g.start(d["v"])
         short = [x for x in shares.values() if x != span]
         assert len(shares) == spans and short in ([], [T - (spans - 1) * span])
-    assert walk_descs(items, TB, hkv, g, rounds, W) == desc
+    got = walk_descs(items, TB, hkv, g, rounds, W, one_pass=one_pass)
+    keys = ("v", "h", "i", "off") if grouped else ("v", "h", "i", "off", "s", "len", "n")
+    assert got.keys() == desc.keys()
+    assert all(all(got[k][f] == desc[k][f] for f in keys) for k in desc)
     return {"items": items, "seqs": seqs, "desc": desc, "T": T, "TB": TB, "NI": len(items), "chunk": chunk,
-            "span": span, "q": qn, "grid": g, "rounds": used_rounds, "flags": flags, "RH": RH, "n": n,
+            "span": span, "q": qn, "grid": g, "rounds": 1 if one_pass else used_rounds, "flags": flags, "RH": RH, "n": n,
             "groups": groups, "gid": gid, "grouped": grouped}
 
 
-def walk_descs(items, TB, hkv, g, rounds, W, threads=1024):
-    """plan_write_descs: each thread takes a contiguous range of chunk ids,
-    binary-searches its first chunk's item in each kv head and walks forward."""
+def walk_descs(items, TB, hkv, g, rounds, W, threads=1024, one_pass=False):
+    """plan_write_descs as the device runs it: each thread takes a contiguous
+    range of chunk ids, binary-searches its first chunk's item and steps
+    positions and worker slots without divisions; then the slots left empty."""
     pos = [it["pos"] for it in items]
     NI = len(items)
     T = TB * hkv
-    spans = -(-T // g.span)
-    nid = spans * g.q
-    if g.q > 1:
+    C, SP, Q = g.chunk, g.span, g.q
+    spans = -(-T // SP)
+    nid = spans * Q
+    if Q > 1:
         per_round = (spans + 7) & ~7
+        n_rounds = Q
     else:
         per_round = min(W, (-(-nid // rounds) + 7) & ~7)
+        n_rounds = -(-nid // per_round) if nid else 0
     q8 = per_round >> 3
 
     def find(r):
@@ -255,25 +267,104 @@ def walk_descs(items, TB, hkv, g, rounds, W, threads=1024):
         return lo
 
     out = {}
-    per = -(-nid // threads)
-    for t in range(threads):
-        h, i = -1, 0
-        for v in range(t * per, min((t + 1) * per, nid)):
-            st = g.start(v)
-            if st >= T:
-                break
-            nh, r = divmod(st, TB)
-            if nh != h:
-                h, i = nh, find(r)
-            while i + 1 < NI and pos[i + 1] <= r:
+    if one_pass:   # one descriptor per span: round 0, id = span
+        per = -(-spans // threads)
+        for t in range(threads):
+            u, uend = t * per, min(t * per + per, spans)
+            if u >= uend:
+                continue
+            h, rr = divmod(u * SP, TB)
+            i = find(rr)
+            idq, idr = divmod(u, q8)
+            while True:
+                while i + 1 < NI and pos[i + 1] <= rr:
+                    i += 1
+                key = (0, idr * 8 + idq)
+                assert key not in out
+                out[key] = {"v": u * Q, "h": h, "i": i, "off": rr - pos[i], "s": items[i]["s"],
+                            "len": items[i]["len"], "n": items[i]["n"]}
+                u += 1
+                if u >= uend:
+                    break
+                idr += 1
+                if idr == q8:
+                    idr, idq = 0, idq + 1
+                rr += SP
+                if rr >= TB:
+                    while rr >= TB:
+                        rr -= TB
+                        h += 1
+                    i = find(rr)
+    per = 0 if one_pass else -(-nid // threads)
+    for t in range(threads if per else 0):
+        v, vend = t * per, min(t * per + per, nid)
+        if v >= vend:
+            continue
+        if Q > 1:
+            u, r = divmod(v, Q)
+            rd, ident = r, u
+        else:
+            u, r = v, 0
+            rd, ident = divmod(v, per_round)
+        st = u * SP + r * C
+        h, rr = divmod(st, TB)
+        i = find(rr)
+        idq, idr = divmod(ident, q8)
+        while st < T:
+            while i + 1 < NI and pos[i + 1] <= rr:
                 i += 1
-            if g.q > 1:
-                u, rd = divmod(v, g.q)
+            key = (rd, idr * 8 + idq)
+            assert key not in out and g.start(v) == st
+            out[key] = {"v": v, "h": h, "i": i, "off": rr - pos[i], "s": items[i]["s"], "len": items[i]["len"],
+                        "n": items[i]["n"]}
+            v += 1
+            if v >= vend:
+                break
+            if Q > 1 and r + 1 < Q:
+                r += 1
+                nst = st + C
+                rd += 1
             else:
-                rd, u = divmod(v, per_round)
-            key = (rd, (u % q8) * 8 + u // q8)
-            assert key not in out
-            out[key] = {"v": v, "h": h, "i": i, "off": r - pos[i]}
+                r = 0
+                u += 1
+                nst = u * SP
+                if Q > 1:
+                    rd = 0
+                idr += 1
+                if idr == q8:
+                    idr = 0
+                    idq += 1
+                    if idq == 8:
+                        idq = 0
+                        rd += 1
+            rr += nst - st
+            st = nst
+            if rr >= TB:
+                while rr >= TB:
+                    rr -= TB
+                    h += 1
+                i = find(rr)
+    # the empty-slot pass: exactly the slots without a chunk
+    n_slots = W if one_pass else max(n_rounds, 1) * W
+    filled = set()
+    for t in range(threads):
+        b, brd = t % W, t // W
+        for k in range(t, n_slots, threads):
+            uu = (b & 7) * q8 + (b >> 3)
+            has = b < per_round
+            if Q > 1:
+                has = has and uu < spans and brd < Q and uu * SP + brd * C < T
+            else:
+                has = has and brd * per_round + uu < nid
+            assert (brd, b) == divmod(k, W)
+            if has:
+                filled.add((brd, b))
+            b += threads % W
+            brd += threads // W
+            if b >= W:
+                b -= W
+                brd += 1
+    assert filled == set(out), "the empty-slot pass and the chunks disagree"
     return out
 
 
@@ -418,8 +509,9 @@ def replay(tables, lens, hkv, bs, pt, G=1, num_blocks=None, **kw):
     hp = host_plan(S, hkv, mb, bs, G, pt, **kw)
     pl = device_plan(tables, np.asarray(lens), hkv, bs, num_blocks, G, hp)
     walk(pl, hkv, bs, G, hp, mb)
-    if pl["q"] > 1:
-        walk(pl, hkv, bs, G, hp, mb, span_runs=True)
+    if pl["q"] > 1 and not pl["grouped"]:   # matrix-core runs: one descriptor and one pass per span
+        one = device_plan(tables, np.asarray(lens), hkv, bs, num_blocks, G, hp, span_runs=True)
+        walk(one, hkv, bs, G, hp, mb, span_runs=True)
     return pl
 
 
