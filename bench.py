@@ -289,10 +289,10 @@ def cpu_baseline_parallel(wl: W.Workload, run, seqs, threads: int) -> dict:
 
 _CSRC = "paged_kv_cache_449_amd/csrc/"
 KERNEL_SOURCES = {
-    "decode": tuple(_CSRC + f for f in ("common.h", "decode_kernel.h", "decode_mfma.h", "decode.hip",
-                                        "decode_grouped.h", "decode_grouped.hip")),
-    "prefill": tuple(_CSRC + f for f in ("common.h", "decode_kernel.h", "decode_mfma.h", "prefill_kernel.h",
-                                         "prefill.hip")),
+    "decode": tuple(_CSRC + f for f in ("common.h", "decode_plan.h", "decode_kernel.h", "decode_mfma.h",
+                                        "decode_items.h", "decode.hip", "decode_grouped.h", "decode_grouped.hip")),
+    "prefill": tuple(_CSRC + f for f in ("common.h", "decode_plan.h", "decode_kernel.h", "decode_mfma.h",
+                                         "decode_items.h", "prefill_kernel.h", "prefill.hip")),
 }
 _PROFILES = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles")
 TRAFFIC_FILES = {"decode": os.path.join(_PROFILES, "decode_traffic.json"),
@@ -648,7 +648,13 @@ def main(argv=None) -> int:
                     help="no GPU work: turn the counter_collection.csv files of a rocprofv3 --pmc FETCH_SIZE run "
                          "and a --pmc WRITE_SIZE run of this same command line (with --calibrate-copy) into HBM "
                          "bytes per launch, and record them in profiles/<kind>_traffic.json")
+    ap.add_argument("--summarise-trace", nargs=2, metavar=("TRACE_DIR", "BENCH_LOG"), default=None,
+                    help="no GPU work: turn a rocprofv3 --kernel-trace --stats run of this same command line "
+                         "(its output directory, prefix kt, and the run's stderr) into "
+                         "profiles/<kind>_<workload>_kernel_trace.md")
     args = ap.parse_args(argv)
+    if args.summarise_trace:
+        return summarise_trace_main(args, argv)
     if args.block_manager:
         print(json.dumps(block_manager_result()), flush=True)
         return 0
@@ -898,7 +904,7 @@ def summarise_main(args, argv) -> int:
             match = ("paged_decode_shared_kernel", "paged_decode_suffix_kernel")
             algorithmic = _grouped_from_tables(wl, tables)["total"]
         else:
-            match = ("paged_decode_plan_kernel", "paged_decode_kernel")
+            match = ("paged_decode_kernel",)   # the decode kernel alone (the plan kernel is timed apart)
             shared = bool(np.any((tables[1:, 0] >= 0) & (tables[1:, 0] == tables[:-1, 0])))
             algorithmic = (_unique_from_tables(wl, tables) if shared else decode_bytes(wl))["total"]
     entry = summarise_pmc(args.summarise_pmc[0], args.summarise_pmc[1], match)
@@ -908,6 +914,58 @@ def summarise_main(args, argv) -> int:
     cmds = [f"rocprofv3 --pmc {c} --output-format csv -d <dir> -o pmc -- python3 bench.py {base} --calibrate-copy"
             for c in ("FETCH_SIZE", "WRITE_SIZE")]
     record_traffic(kind, key, entry, algorithmic, cmds)
+    return 0
+
+
+def summarise_trace_main(args, argv) -> int:
+    """--summarise-trace: a kernel trace of one bench.py run -> a short
+    markdown summary under profiles/: the per-kernel statistics and, for the
+    dominant kernel, the average over each timed region of the run (warm-up,
+    back-to-back steps, HIP-event steps, and steps after a 512 MiB write)."""
+    import csv
+    tdir, log = args.summarise_trace
+    wl = get_workload(args.workload)
+    kind = "prefill" if wl.multi_token else "decode"
+    stats = list(csv.DictReader(open(os.path.join(tdir, "kt_kernel_stats.csv"))))
+    trace = sorted(csv.DictReader(open(os.path.join(tdir, "kt_kernel_trace.csv"))),
+                   key=lambda r: int(r["Start_Timestamp"]))
+    main_name = "paged_prefill" if wl.multi_token else "paged_decode_kernel"
+    durs = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in trace if main_name in r["Kernel_Name"]]
+    plan = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in trace
+            if "paged_decode_plan_kernel" in r["Kernel_Name"]]
+    W, K = args.warmup, args.steps
+    names = ["warm-up", "steps back to back", "steps with HIP events", "steps after a 512 MiB write"]
+    bounds = [0, W, W + K, W + 2 * K, W + 3 * K]
+    rows = []
+    for i, nm in enumerate(names):
+        seg = durs[bounds[i]:bounds[i + 1]]
+        if seg:
+            rows.append(f"| {nm} | {len(seg)} | {np.mean(seg):.1f} | {np.min(seg):.1f} | {np.max(seg):.1f} |")
+    rest = list(argv if argv is not None else sys.argv[1:])
+    i = rest.index("--summarise-trace")
+    base = " ".join(rest[:i] + rest[i + 3:])
+    bench_lines = [ln.strip() for ln in open(log) if ln.startswith("[bench]") and ("kernel" in ln or "step" in ln)]
+    out = [f"# Kernel trace: {wl.name}", "",
+           "Command (from the repository root, on one MI355X):", "", "```",
+           f"rocprofv3 --kernel-trace --stats --output-format csv -d <dir> -o kt -- python3 bench.py {base}",
+           "```", "", "| kernel | calls | average (µs) | min (µs) | max (µs) | share of GPU time |",
+           "|---|---|---|---|---|---|"]
+    for r in stats[:8]:
+        out.append(f"| `{r['Name'][:110]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+                   f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | {float(r['Percentage']):.1f}% |")
+    out += ["", f"`{main_name}` by region of the run (launches in dispatch order):", "",
+            "| region | launches | average (µs) | min (µs) | max (µs) |", "|---|---|---|---|---|", *rows]
+    if plan:
+        out += ["", f"`paged_decode_plan_kernel`: {len(plan)} launches, average {np.mean(plan):.1f} µs "
+                    f"(min {np.min(plan):.1f}, max {np.max(plan):.1f})."]
+    if bench_lines:
+        out += ["", "bench.py's own timing in the same run:", "", *[f"    {ln}" for ln in bench_lines]]
+    tag = wl.name + ("" if args.partition_tokens is None or args.partition_tokens == wl.partition_tokens
+                     else f"_pt{args.partition_tokens}")
+    path = os.path.join(_PROFILES, f"{kind}_{tag}_kernel_trace.md")
+    with open(path, "w") as f:
+        f.write("\n".join(out) + "\n")
+    print(path)
     return 0
 
 
