@@ -224,11 +224,9 @@ void paged_prefill_kernel(const DecodeParams p) {
 // split row blocks leave 64-row records that the last-arriving work-group
 // merges with all its threads.
 
-// Waves per work-group and 16-row tiles per wave: 8 x 1 (128-row blocks)
-// for head dim up to 128, 4 x 1 (64-row blocks) for head dim 256, whose two
-// LDS buffers of 8 tiles would not fit.  Two row tiles per wave (4 x 2, so
-// every LDS read of K and V feeds 32 rows) measured 8-10% slower on MI355X:
-// the extra registers halve the waves per CU.
+// Waves per work-group and 16-row tiles per wave of the split work-groups:
+// 8 x 1 (128-row blocks) for head dim up to 128, 4 x 1 (64-row blocks) for
+// head dim 256, whose two LDS buffers of 8 tiles would not fit.
 template <int D>
 constexpr int wg_waves() { return D <= 128 ? 8 : 4; }
 template <int D>
@@ -238,6 +236,21 @@ template <int D>
 constexpr int wg_rows() { return 16 * wg_waves<D>() * wg_row_tiles<D>(); }
 constexpr int kMaxWgRows = 128;   // records are sized for the largest block
 constexpr int kTileGroup = 4;     // tiles a wave computes together
+
+// The one-work-group-per-block kernel takes the same 128-row blocks as
+// 4 waves x 2 row tiles for head dim up to 128: every K and V word a wave
+// reads from LDS then feeds 32 rows, and two work-groups share a CU (two
+// waves per SIMD, 240-248 VGPRs).  On MI355X that took the chunked-prefill
+// workload from 770 to 702 us and the fp8 GQA chunks from 427 to 373 us.
+// fp8 pools compute 4 tiles together; 16-bit pools 2, which keeps them
+// clear of spills at the 256-VGPR cap (4 and 2 time alike on bf16).  The
+// split work-groups keep 8 x 1: their merge code would spill at that cap.
+template <int D>
+constexpr int unit_waves() { return D <= 128 ? 4 : wg_waves<D>(); }
+template <int D>
+constexpr int unit_row_tiles() { return D <= 128 ? 2 : 1; }
+template <typename KV, int D>
+constexpr int unit_tile_group() { return D <= 128 && elem_size<KV>::value == 2 ? 2 : 4; }
 
 // Out rows of a row block's records: row j is row tile waves * rb + j / 16
 // (waves: row tiles per block), slot j % 16 of it.
@@ -267,14 +280,15 @@ __device__ inline int sequence_rowblock_blocks(int n, int m, int QB, int log2_bs
   return tot;
 }
 
-template <typename KV, typename QT, int D, int G>
+// W waves of RT 16-row tiles each; TG tiles computed together.
+template <typename KV, typename QT, int D, int G, int W, int RT, int TG>
 __device__ inline void prefill_wg_run(const DecodeParams& p, int w, int chunk, int wstart, int pos, int s, int h,
                                       int rb, int off, int len, int n, int m, int qs) {
   using MT = typename mfma_operand<KV, QT>::type;
   using Ops = mfma_ops<MT>;
   using Sh = MfmaShape<KV, D>;
-  constexpr int W = wg_waves<D>();
-  constexpr int RT = wg_row_tiles<D>();   // 16-row tiles per wave
+  constexpr int kTileGroup = TG;
+  static_assert(TG == 2 || TG == 4, "tiles computed together");
   constexpr int TB = W * RT;              // row tiles per block
   constexpr int Q = 16 / G;
   constexpr int KS = Sh::KS, DT = Sh::DT, LSTRIDE = Sh::LSTRIDE, KSTRIDE = Sh::KSTRIDE;
@@ -427,10 +441,9 @@ __device__ inline void prefill_wg_run(const DecodeParams& p, int w, int chunk, i
             if (!(bvalid && t0 + i < lim)) x[t][i] = -INFINITY;
         }
       }
-      float mx = fmaxf(fmaxf(fmaxf(x[0][0], x[0][1]), fmaxf(x[0][2], x[0][3])),
-                       fmaxf(fmaxf(x[1][0], x[1][1]), fmaxf(x[1][2], x[1][3])));
-      mx = fmaxf(mx, fmaxf(fmaxf(fmaxf(x[2][0], x[2][1]), fmaxf(x[2][2], x[2][3])),
-                           fmaxf(fmaxf(x[3][0], x[3][1]), fmaxf(x[3][2], x[3][3]))));
+      float mx = -INFINITY;
+#pragma unroll
+      for (int t = 0; t < kTileGroup; ++t) mx = fmaxf(mx, fmaxf(fmaxf(x[t][0], x[t][1]), fmaxf(x[t][2], x[t][3])));
       mx = fmaxf(mx, __shfl_xor(mx, 16));
       mx = fmaxf(mx, __shfl_xor(mx, 32));
       // Lazy rescaling: the reference max moves only when a row's max passes
@@ -613,7 +626,8 @@ __device__ inline void prefill_wg_chunk(const DecodeParams& p, int v, int chunk,
   while (true) {
     const int nb = (tile_limit(n, m, QB, rb) + (1 << p.log2_bs) - 1) >> p.log2_bs;
     const int len = min(nb - off, end - pos);
-    prefill_wg_run<KV, QT, D, G>(p, v, chunk, start, pos, s, h, rb, off, len, n, m, qs);
+    prefill_wg_run<KV, QT, D, G, wg_waves<D>(), wg_row_tiles<D>(), kTileGroup>(p, v, chunk, start, pos, s, h, rb,
+                                                                              off, len, n, m, qs);
     pos += len;
     if (pos >= end) break;
     off = 0;
@@ -668,7 +682,9 @@ __global__ __launch_bounds__(64 * wg_waves<D>()) void paged_prefill_wg_kernel(co
 // same time there and stream the same prefix through its L2; no run is split
 // (no records).  The grid may exceed the units; the rest exit at once.
 template <typename KV, typename QT, int D, int G>
-__global__ __launch_bounds__(64 * wg_waves<D>()) void paged_prefill_unit_kernel(const DecodeParams p) {
+__global__ __launch_bounds__(64 * unit_waves<D>()) __attribute__((amdgpu_waves_per_eu(D <= 128 ? 2 : 1)))
+void paged_prefill_unit_kernel(const DecodeParams p) {
+  static_assert(16 * unit_waves<D>() * unit_row_tiles<D>() == wg_rows<D>(), "the split work-groups' blocks");
   constexpr int QB = wg_rows<D>() / G;
   const int lane = (int)(threadIdx.x & 63);
   const int S = p.num_seqs;
@@ -729,7 +745,8 @@ __global__ __launch_bounds__(64 * wg_waves<D>()) void paged_prefill_unit_kernel(
   qs = uniform(qs);
   const int nb = (tile_limit(n, m, QB, rb) + (1 << p.log2_bs) - 1) >> p.log2_bs;
   // the whole row block: stored directly, no record
-  prefill_wg_run<KV, QT, D, G>(p, 0, 1, 0, 0, s, h, rb, 0, nb, n, m, qs);
+  prefill_wg_run<KV, QT, D, G, unit_waves<D>(), unit_row_tiles<D>(), unit_tile_group<KV, D>()>(p, 0, 1, 0, 0, s, h, rb, 0,
+                                                                                           nb, n, m, qs);
 }
 
 // Prefill launch shape: 0 one-wave tiles, 1 split work-groups, 2 units.
@@ -739,7 +756,7 @@ kv_status_t launch_prefill(const DecodeParams& p, int D, int G, int mode, hipStr
   if (D == DD && G == GG) {                                                                                       \
     if (mode == 2)                                                                                                \
       hipLaunchKernelGGL((paged_prefill_unit_kernel<KV, QT, DD, GG>), dim3(p.num_workers),                       \
-                         dim3(64 * wg_waves<DD>()), 0, stream, p);                                                \
+                         dim3(64 * unit_waves<DD>()), 0, stream, p);                                              \
     else if (mode == 1)                                                                                           \
       hipLaunchKernelGGL((paged_prefill_wg_kernel<KV, QT, DD, GG>), dim3(p.num_workers), dim3(64 * wg_waves<DD>()), 0, \
                          stream, p);                                                                              \
