@@ -536,9 +536,13 @@ kv_status_t make_plan(const kv_pool_t* pool, int32_t num_seqs, int32_t num_q_hea
   const size_t row = (size_t)(pool->head_dim + 4) * sizeof(float);
   const size_t flat = (size_t)2 * chunks * G * row;
   // record rows of a grouped plan: at most 2 pieces plus one per chunk of
-  // every item, so 4 * Hkv * S * G rows plus 16 per chunk boundary; past
-  // 8192 chunks a grouped plan that does not fit falls back to a flat one
-  plan->grec_rows = grouping ? 4LL * pool->num_kv_heads * num_seqs * G + 16LL * std::min<int64_t>(chunks, 8192) : 0;
+  // every item, so 4 * Hkv * S * G rows plus 16 per chunk boundary (grouped
+  // plans of the library split have one chunk per worker; with partitions,
+  // up to `chunks`); past 8192 chunks a grouped plan that does not fit falls
+  // back to a flat one
+  const int64_t grouped_chunks = partition_tokens > 0 ? chunks : workers;
+  plan->grec_rows =
+      grouping ? 4LL * pool->num_kv_heads * num_seqs * G + 16LL * std::min<int64_t>(grouped_chunks, 8192) : 0;
   const size_t grouped = (size_t)plan->grec_rows * row;
   plan->bytes = off + std::max(flat, grouped);
   if (!grouping) plan->grec_rows = 0;

@@ -66,7 +66,7 @@ def host_plan(S, hkv, max_blocks, bs, G, pt, num_cus=256, waves_per_cu=8, groupa
     grouping = groupable and G <= 8 and bs >= 16 and hkv * S <= COUNTER_SLOTS
     return {"chunk": chunk, "workers": workers, "desc_rounds": desc_rounds, "chunks": chunks,
             "max_members": 16 // G if grouping else 0,
-            "grec_rows": (4 * hkv * S * G + 16 * min(chunks, 8192)) if grouping else 0,
+            "grec_rows": (4 * hkv * S * G + 16 * min(chunks if pt > 0 else workers, 8192)) if grouping else 0,
             "flat_rows": 2 * chunks * G}
 
 
