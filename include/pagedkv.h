@@ -192,13 +192,14 @@ kv_status_t reshape_and_cache(kv_pool_t* pool, const void* k_new, const void* v_
  * (paged_attention_plan below) and the decode kernel.
  *
  * Work split: the cached tokens of all (kv head, sequence) pairs are laid end
- * to end and cut into equal runs of whole blocks, one per worker wavefront,
- * so long and short sequences cost the same per token.  partition_tokens == 0
- * lets the library size the runs from the device's compute-unit count;
- * otherwise each run is partition_tokens tokens (a multiple of block_size).
- * A sequence cut into several runs is merged in the same launch by the
- * worker that finishes last (log-sum-exp merge of the partial results, in a
- * fixed order, so results are bitwise reproducible).
+ * to end and cut into equal spans of whole blocks, one per resident worker
+ * wavefront, so long and short sequences cost the same per token.
+ * partition_tokens == 0 makes each span one run; otherwise (a multiple of
+ * block_size) each span is cut into partitions of partition_tokens tokens,
+ * the last of a span shorter, and every partition leaves its partial result.
+ * A sequence cut into several runs or partitions is merged in the same
+ * launch by the worker that finishes last (log-sum-exp merge of the partial
+ * results, in a fixed order, so results are bitwise reproducible).
  *
  * Shared prefixes: consecutive sequences whose table rows start with the
  * same whole blocks (candidates forked from one prompt, "vLLM — 把操作系统的
@@ -215,9 +216,9 @@ kv_status_t reshape_and_cache(kv_pool_t* pool, const void* k_new, const void* v_
  * queries) and block_size >= 16 run on the matrix cores (unless the pool
  * was made with PAGEDKV_DECODE_MFMA=0).
  *
- * When partition_tokens is given and the batch would need more than 65528
- * runs, the runs are lengthened to the smallest whole number of blocks that
- * fits.
+ * When partition_tokens is given and the batch would need more than 65536
+ * partitions in all, they are lengthened to the smallest whole number of
+ * blocks that fits.
  *
  * workspace: device memory of at least paged_attention_workspace_size()
  * bytes, 256-byte aligned.  Its first 256 KiB hold arrival counters and must

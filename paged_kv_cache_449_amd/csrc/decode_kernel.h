@@ -68,7 +68,7 @@ struct DecodeParams {
   const int32_t* context_lens;
   const int32_t* query_start;  // multi-token attention: [num_seqs + 1] query row offsets
   int32_t* counters;     // [kCounterSlots], zero between calls
-  float* partials;       // [2 * num_workers][G][head_dim + 4]
+  float* partials;       // [2 * chunk ids][rows][head_dim + 4] (grouped plans: per item)
   int32_t num_seqs;
   int32_t total_q;       // multi-token attention: rows of q and out
   int32_t num_kv_heads;
