@@ -71,6 +71,15 @@ SPANS = {
                              ctx_lens=np.random.default_rng(66).integers(1, 900, size=48).tolist()),
     "spans_bf16_gqa4_bs32": W._make("spans_bf16_gqa4_bs32", 67, 8, 2, 128, "bf16", "bf16", 32,
                                     ctx_lens=np.random.default_rng(67).integers(1, 2000, size=40).tolist()),
+    # 16 query rows per kv head (one part fits the LDS), 2 rows, and head
+    # dims 64 and 256 (at 256 the tile staging leaves no room: parts are
+    # stored as they finish)
+    "spans_bf16_gqa16": W._make("spans_bf16_gqa16", 68, 16, 1, 128, "bf16", "bf16", 16,
+                                ctx_lens=np.random.default_rng(68).integers(1, 1500, size=48).tolist()),
+    "spans_f16_gqa2_d64": W._make("spans_f16_gqa2_d64", 69, 4, 2, 64, "f16", "f16", 16,
+                                  ctx_lens=np.random.default_rng(69).integers(1, 1500, size=48).tolist()),
+    "spans_fp8_gqa4_d256_f16q": W._make("spans_fp8_gqa4_d256_f16q", 70, 8, 2, 256, "fp8e4m3", "f16", 16,
+                                        ctx_lens=np.random.default_rng(70).integers(1, 1200, size=32).tolist()),
 }
 
 
