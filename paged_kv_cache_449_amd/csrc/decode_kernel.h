@@ -673,17 +673,6 @@ __device__ inline void run_rounds(const DecodeParams& p, const PlanHeader& H, in
   }
 }
 
-// One worker wavefront per work-group.  MFMA selects the matrix-core run
-// (query groups with a 16-bit operand type) over the vector-ALU run.  The
-// matrix-core runs with up to 4 query heads per kv head fit 168 VGPRs
-// without spilling, which leaves room for 3 waves per SIMD: launches with
-// more work-groups than worker slots (fixed-size partitions) gain 2% from
-// the third wave on MI355X for fp8.
-//
-// The plan kernel, run just before on the same stream, gives each worker
-// one descriptor per round: the chunk it streams and where that chunk
-// starts.  Grouped plans (shared prefixes read once per group) run where the
-// dtype pair has a matrix-core operand type.
 // Empty contexts attend to nothing: their output rows are zero.  The first
 // worker checks 64 lengths per load and clears the rows of the empty ones.
 template <typename QT, int D, int G>
@@ -704,9 +693,20 @@ __device__ inline void zero_empty_rows(const DecodeParams& p) {
   }
 }
 
+// One worker wavefront per work-group.  MFMA selects the matrix-core run
+// (query groups with a 16-bit operand type) over the vector-ALU run.  The
+// grid is 8 workers per CU, two per SIMD, so the matrix-core runs may take
+// up to 256 VGPRs: with the earlier cap of 168 (three waves per SIMD, which
+// only short-lived partition work-groups could use) the fp8 GQA workloads
+// ran about 2% slower on MI355X.
+//
+// The plan kernel, run just before on the same stream, gives each worker
+// one descriptor per round: the chunk it streams and where that chunk
+// starts.  Grouped plans (shared prefixes read once per group) run where the
+// dtype pair has a matrix-core operand type.
 template <typename KV, typename QT, int D, int G, bool MFMA>
 __global__ __launch_bounds__(64)
-__attribute__((amdgpu_waves_per_eu(MFMA && D <= 128 ? (G <= 4 ? 3 : 2) : 1)))
+__attribute__((amdgpu_waves_per_eu(MFMA && D <= 128 ? 2 : 1)))
 void paged_decode_kernel(const DecodeParams p) {
   constexpr bool kGroupable = !std::is_void<typename mfma_operand<KV, QT>::type>::value && G <= 8;
   const PlanHeader H = load_header(p.header);
