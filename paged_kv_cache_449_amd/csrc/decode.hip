@@ -126,17 +126,16 @@ __device__ __attribute__((always_inline)) inline void plan_write_items(const Pla
   }
 }
 
-// The descriptors.  Thread t takes a contiguous range of chunk ids (stream
-// order), finds the first one's item by binary search over the items' first
-// blocks and walks forward from there, stepping chunk positions and worker
-// slots without divisions.  Where a chunk runs:
+// The descriptors, one worker slot per thread, so the stores of a wave fill
+// whole cache lines.  Where a chunk runs:
 //   - uniform cut (q = 1): chunk v in round v / per_round, with id
 //     v % per_round;
 //   - partitions (q > 1): chunk v, the (v % q)-th of span v / q, in round
 //     v % q, with id v / q, so a worker runs its span's chunks in order;
 // slot b runs on XCD b % 8 and takes id (b % 8) * (per_round / 8) + b / 8.
-// A descriptor also carries the sequence, blocks and token limit of the
-// chunk's first item (flat plans start from them without an item load).
+// A slot finds its chunk's first item by binary search over the items'
+// first blocks.  A descriptor also carries the sequence, blocks and token
+// limit of that item (flat plans start from them without an item load).
 // Slots without a chunk are marked empty.  item_at(i) gives item i's first
 // block, sequence, blocks and token limit.
 template <typename ItemAt>
@@ -147,7 +146,7 @@ __device__ __attribute__((always_inline)) inline void plan_write_descs(const Pla
   const int T = TB * pp.num_kv_heads;
   const int spans = (T + SP - 1) / SP;
   // chunk ids; those of the last span that start past the stream's end hold
-  // no chunk (and are the last ids)
+  // no chunk
   const int nid = spans * Q;
   int per_round, rounds;
   if (Q > 1) {
@@ -170,104 +169,27 @@ __device__ __attribute__((always_inline)) inline void plan_write_descs(const Pla
     }
     return lo;
   };
-  if (one_pass) {
-    const int per = (spans + kPlanThreads - 1) / kPlanThreads;
-    int u = tid * per;
-    const int uend = min(u + per, spans);
-    if (u < uend) {
-      int h = u * SP / TB, rr = u * SP - h * TB;
-      int i = find(rr);
-      int idq = u / q8, idr = u - idq * q8;
-      for (;;) {
-        while (i + 1 < L.NI && item_at(i + 1).x <= rr) ++i;
-        const int4 it = item_at(i);
-        put_desc(pp.desc + idr * 8 + idq, PlanDesc{u * Q, h, i, rr - it.x, it.y, it.z, it.w, 0});
-        if (++u >= uend) break;
-        if (++idr == q8) {
-          idr = 0;
-          ++idq;
-        }
-        rr += SP;
-        if (rr >= TB) {
-          while (rr >= TB) {
-            rr -= TB;
-            ++h;
-          }
-          i = find(rr);
-        }
-      }
-    }
-  }
-  const int per = one_pass ? 0 : (nid + kPlanThreads - 1) / kPlanThreads;
-  int v = tid * per;
-  const int vend = min(v + per, nid);
-  if (v < vend) {
-    // chunk v: span u, its r-th chunk; stream block st; round rd, id (idq, idr)
-    int u, r, rd, id;
-    if (Q > 1) {
-      u = v / Q;
-      r = v - u * Q;
-      rd = r;
-      id = u;
-    } else {
-      u = v;
-      r = 0;
-      rd = v / per_round;
-      id = v - rd * per_round;
-    }
-    int st = u * SP + r * C;
-    int h = st / TB, rr = st - h * TB;
-    int i = find(rr);
-    int idq = id / q8, idr = id - idq * q8;
-    while (st < T) {
-      while (i + 1 < L.NI && item_at(i + 1).x <= rr) ++i;
-      const int4 it = item_at(i);
-      put_desc(pp.desc + rd * W + idr * 8 + idq, PlanDesc{v, h, i, rr - it.x, it.y, it.z, it.w, 0});
-      if (++v >= vend) break;
-      int nst;
-      if (Q > 1 && ++r < Q) {   // the span's next chunk, in the next round
-        nst = st + C;
-        ++rd;
-      } else {                  // the next span (or chunk), on the next id
-        r = 0;
-        nst = ++u * SP;
-        if (Q > 1) rd = 0;
-        if (++idr == q8) {
-          idr = 0;
-          if (++idq == 8) {
-            idq = 0;
-            ++rd;
-          }
-        }
-      }
-      rr += nst - st;
-      st = nst;
-      if (rr >= TB) {   // a later kv head: its items start again from the first
-        while (rr >= TB) {
-          rr -= TB;
-          ++h;
-        }
-        i = find(rr);
-      }
-    }
-  }
   // the first round's descriptors are written even when no chunk exists
   const int n_slots = one_pass ? W : max(rounds, 1) * W;
-  int b = tid % W, brd = tid / W;
+  int b = tid % W, rd = tid / W;
   const int db = kPlanThreads % W, drd = kPlanThreads / W;
   for (int k = tid; k < n_slots; k += kPlanThreads) {
-    const int uu = (b & 7) * q8 + (b >> 3);
-    bool has = b < per_round;
-    if (Q > 1)
-      has = has && uu < spans && brd < Q && uu * SP + brd * C < T;
-    else
-      has = has && brd * per_round + uu < nid;
-    if (!has) put_desc(pp.desc + k, PlanDesc{-1, 0, 0, 0, 0, 0, 0, 0});
+    const int u = (b & 7) * q8 + (b >> 3);
+    const int v = Q > 1 ? u * Q + rd : rd * per_round + u;
+    const int st = Q > 1 ? u * SP + rd * C : v * C;
+    PlanDesc d{-1, 0, 0, 0, 0, 0, 0, 0};
+    if (b < per_round && v < nid && st < T) {
+      const int h = st / TB, r = st - h * TB;
+      const int i = find(r);
+      const int4 it = item_at(i);
+      d = PlanDesc{v, h, i, r - it.x, it.y, it.z, it.w, 0};
+    }
+    put_desc(pp.desc + k, d);
     b += db;
-    brd += drd;
+    rd += drd;
     if (b >= W) {
       b -= W;
-      ++brd;
+      ++rd;
     }
   }
   if (tid == 0)
@@ -326,13 +248,16 @@ __device__ __attribute__((always_inline)) inline void plan_body(const PlanParams
         if (!any_open) break;
         int x[K], y[K];
         const int e = base + lane;
+        // every load unconditional (an entry of the row, or of the first row
+        // for sequences not compared), so all 2K are in flight together
+        const int ec = min(e, pp.max_blocks - 1);
 #pragma unroll
         for (int j = 0; j < K; ++j) {
           const int s = s0 + j * kPlanWaves;
-          const int32_t* a = pp.block_tables + (int64_t)s * pp.max_blocks;
-          const bool ld = open[j] && e < cap[j];
-          x[j] = ld ? a[e] : 0;
-          y[j] = ld ? a[e - pp.max_blocks] : 0;
+          const int sr = (open[j] && s < S) ? s : 1;
+          const int32_t* a = pp.block_tables + (int64_t)sr * pp.max_blocks + ec;
+          x[j] = a[0];
+          y[j] = a[-pp.max_blocks];
         }
 #pragma unroll
         for (int j = 0; j < K; ++j) {

@@ -239,9 +239,9 @@ def device_plan(tables, lens, hkv, bs, num_blocks, G, hp, span_runs=False):
 
 
 def walk_descs(items, TB, hkv, g, rounds, W, threads=1024, one_pass=False):
-    """plan_write_descs as the device runs it: each thread takes a contiguous
-    range of chunk ids, binary-searches its first chunk's item and steps
-    positions and worker slots without divisions; then the slots left empty."""
+    """plan_write_descs as the device runs it: thread t takes worker slots
+    t, t + threads, ... (stepping slot and round without divisions), and
+    each slot with a chunk binary-searches its first item."""
     pos = [it["pos"] for it in items]
     NI = len(items)
     T = TB * hkv
@@ -267,104 +267,26 @@ def walk_descs(items, TB, hkv, g, rounds, W, threads=1024, one_pass=False):
         return lo
 
     out = {}
-    if one_pass:   # one descriptor per span: round 0, id = span
-        per = -(-spans // threads)
-        for t in range(threads):
-            u, uend = t * per, min(t * per + per, spans)
-            if u >= uend:
-                continue
-            h, rr = divmod(u * SP, TB)
-            i = find(rr)
-            idq, idr = divmod(u, q8)
-            while True:
-                while i + 1 < NI and pos[i + 1] <= rr:
-                    i += 1
-                key = (0, idr * 8 + idq)
-                assert key not in out
-                out[key] = {"v": u * Q, "h": h, "i": i, "off": rr - pos[i], "s": items[i]["s"],
-                            "len": items[i]["len"], "n": items[i]["n"]}
-                u += 1
-                if u >= uend:
-                    break
-                idr += 1
-                if idr == q8:
-                    idr, idq = 0, idq + 1
-                rr += SP
-                if rr >= TB:
-                    while rr >= TB:
-                        rr -= TB
-                        h += 1
-                    i = find(rr)
-    per = 0 if one_pass else -(-nid // threads)
-    for t in range(threads if per else 0):
-        v, vend = t * per, min(t * per + per, nid)
-        if v >= vend:
-            continue
-        if Q > 1:
-            u, r = divmod(v, Q)
-            rd, ident = r, u
-        else:
-            u, r = v, 0
-            rd, ident = divmod(v, per_round)
-        st = u * SP + r * C
-        h, rr = divmod(st, TB)
-        i = find(rr)
-        idq, idr = divmod(ident, q8)
-        while st < T:
-            while i + 1 < NI and pos[i + 1] <= rr:
-                i += 1
-            key = (rd, idr * 8 + idq)
-            assert key not in out and g.start(v) == st
-            out[key] = {"v": v, "h": h, "i": i, "off": rr - pos[i], "s": items[i]["s"], "len": items[i]["len"],
-                        "n": items[i]["n"]}
-            v += 1
-            if v >= vend:
-                break
-            if Q > 1 and r + 1 < Q:
-                r += 1
-                nst = st + C
-                rd += 1
-            else:
-                r = 0
-                u += 1
-                nst = u * SP
-                if Q > 1:
-                    rd = 0
-                idr += 1
-                if idr == q8:
-                    idr = 0
-                    idq += 1
-                    if idq == 8:
-                        idq = 0
-                        rd += 1
-            rr += nst - st
-            st = nst
-            if rr >= TB:
-                while rr >= TB:
-                    rr -= TB
-                    h += 1
-                i = find(rr)
-    # the empty-slot pass: exactly the slots without a chunk
     n_slots = W if one_pass else max(n_rounds, 1) * W
-    filled = set()
+    db, drd = threads % W, threads // W
     for t in range(threads):
-        b, brd = t % W, t // W
+        b, rd = t % W, t // W
         for k in range(t, n_slots, threads):
-            uu = (b & 7) * q8 + (b >> 3)
-            has = b < per_round
-            if Q > 1:
-                has = has and uu < spans and brd < Q and uu * SP + brd * C < T
-            else:
-                has = has and brd * per_round + uu < nid
-            assert (brd, b) == divmod(k, W)
-            if has:
-                filled.add((brd, b))
-            b += threads % W
-            brd += threads // W
+            assert (rd, b) == divmod(k, W)
+            u = (b & 7) * q8 + (b >> 3)
+            v = u * Q + rd if Q > 1 else rd * per_round + u
+            st = u * SP + rd * C if Q > 1 else v * C
+            if b < per_round and v < nid and st < T:
+                assert g.start(v) == st
+                h, r = divmod(st, TB)
+                i = find(r)
+                out[(rd, b)] = {"v": v, "h": h, "i": i, "off": r - pos[i], "s": items[i]["s"],
+                                "len": items[i]["len"], "n": items[i]["n"]}
+            b += db
+            rd += drd
             if b >= W:
                 b -= W
-                brd += 1
-    assert filled == set(out), "the empty-slot pass and the chunks disagree"
+                rd += 1
     return out
 
 
