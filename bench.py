@@ -648,11 +648,17 @@ def main(argv=None) -> int:
                     help="no GPU work: turn the counter_collection.csv files of a rocprofv3 --pmc FETCH_SIZE run "
                          "and a --pmc WRITE_SIZE run of this same command line (with --calibrate-copy) into HBM "
                          "bytes per launch, and record them in profiles/<kind>_traffic.json")
+    ap.add_argument("--summarise-l2", default=None, metavar="PMC_CSV",
+                    help="no GPU work: the counter_collection.csv of a rocprofv3 --pmc TCC_HIT_sum TCC_MISS_sum run "
+                         "of this same command line -> one markdown row per decode kernel (L2 hits and misses per "
+                         "dispatch, hit rate, misses in bytes)")
     ap.add_argument("--summarise-trace", nargs=2, metavar=("TRACE_DIR", "BENCH_LOG"), default=None,
                     help="no GPU work: turn a rocprofv3 --kernel-trace --stats run of this same command line "
                          "(its output directory, prefix kt, and the run's stderr) into "
                          "profiles/<kind>_<workload>_kernel_trace.md")
     args = ap.parse_args(argv)
+    if args.summarise_l2:
+        return summarise_l2_main(args)
     if args.summarise_trace:
         return summarise_trace_main(args, argv)
     if args.block_manager:
@@ -914,6 +920,29 @@ def summarise_main(args, argv) -> int:
     cmds = [f"rocprofv3 --pmc {c} --output-format csv -d <dir> -o pmc -- python3 bench.py {base} --calibrate-copy"
             for c in ("FETCH_SIZE", "WRITE_SIZE")]
     record_traffic(kind, key, entry, algorithmic, cmds)
+    return 0
+
+
+def summarise_l2_main(args) -> int:
+    """--summarise-l2: L2 (TCC) hits and misses per dispatch of the attention
+    kernels of one run, averaged over its dispatches; one request is one
+    128-byte line."""
+    rows = _pmc_rows(args.summarise_l2)
+    per = {}
+    for r in rows:
+        name = r["Kernel_Name"]
+        if not any(k in name for k in ("paged_decode", "paged_prefill")):
+            continue
+        d = per.setdefault(name, {}).setdefault(r["Dispatch_Id"], {})
+        d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    wl = get_workload(args.workload)
+    for name, disp in per.items():
+        hits = float(np.mean([d.get("TCC_HIT_sum", 0.0) for d in disp.values()]))
+        miss = float(np.mean([d.get("TCC_MISS_sum", 0.0) for d in disp.values()]))
+        rate = hits / (hits + miss) if hits + miss else 0.0
+        short = name.split("(")[0].replace("void ", "").replace("pkv::", "")
+        print(f"| {wl.name} | `{short}` | {len(disp)} | {hits:,.0f} | {miss:,.0f} | {rate:.3f} | "
+              f"{miss * 128 / 1e9:.3f} GB |")
     return 0
 
 
