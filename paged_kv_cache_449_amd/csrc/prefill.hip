@@ -1,5 +1,7 @@
 // Host entry points of multi-token paged attention: argument checks,
 // workspace layout and dispatch to the kernel instantiations.
+#include <algorithm>
+
 #include "prefill_kernel.h"
 
 namespace {
@@ -87,6 +89,7 @@ extern "C" kv_status_t paged_attention_prefill(const kv_pool_t* pool, const void
   if (tiles * max_blocks * pool->num_kv_heads > (1LL << 30) || (int64_t)max_blocks * pool->block_size > (1LL << 30))
     return KV_ERR_INVALID_ARG;
   if (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255)) return KV_ERR_WORKSPACE;
+  int32_t unit_run = 0;
   if (mode == 2) {
     // at most total_q * G / rows + num_seqs row blocks per kv head when
     // query_start is consistent (the tiles bound above keeps this far below
@@ -94,6 +97,14 @@ extern "C" kv_status_t paged_attention_prefill(const kv_pool_t* pool, const void
     const int64_t rows = 16LL * (pool->head_dim <= 128 ? 8 : 4);
     const int64_t units = ((int64_t)total_q * G / rows + num_seqs + 1) * pool->num_kv_heads;
     workers = (int32_t)((units + 7) & ~7LL);
+    if (num_seqs <= kUnitRankSeqs) {
+      // ranked order dealt to the XCDs in runs of about one (sequence, kv
+      // head) pair's row blocks; each XCD gets ceil(units / 8c) runs at most
+      const int64_t c = std::min<int64_t>(16, std::max<int64_t>(1, ((int64_t)total_q * G + rows * num_seqs - 1) /
+                                                                       (rows * num_seqs)));
+      unit_run = (int32_t)c;
+      workers = (int32_t)(8 * ((units + 8 * c - 1) / (8 * c)) * c);
+    }
   }
 
   DecodeParams p{};
@@ -112,7 +123,7 @@ extern "C" kv_status_t paged_attention_prefill(const kv_pool_t* pool, const void
   p.max_blocks = max_blocks;
   p.num_blocks = pool->num_blocks;
   p.log2_bs = pool->log2_block_size;
-  p.chunk = 0;
+  p.chunk = unit_run;   // unit mode: the run length of the XCD deal
   p.num_workers = workers;
   const bool fp8 = pool->dtype == KV_FP8_E4M3FN;
   p.q_scale = scale * kLog2e * (fp8 ? pool->k_scale : 1.0f);

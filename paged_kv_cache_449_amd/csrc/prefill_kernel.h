@@ -676,11 +676,78 @@ __global__ __launch_bounds__(64 * wg_waves<D>()) void paged_prefill_wg_kernel(co
   prefill_wg_chunk<KV, QT, D, G>(p, v, chunk, T, total);
 }
 
-// Unit mode: one work-group per whole row block, units in (kv head,
-// sequence, row block) order.  Consecutive units go to the same XCD in
-// dispatch order, so the row blocks of one (sequence, kv head) run at the
-// same time there and stream the same prefix through its L2; no run is split
-// (no records).  The grid may exceed the units; the rest exit at once.
+// Unit mode: one work-group per whole row block; no run is split (no
+// records).
+//
+// Order.  Row blocks differ in length by the cached prefix and by their
+// causal limit, and only a handful of work-groups per CU run them, so a long
+// row block dispatched last sets the launch's end: in (kv head, sequence,
+// row block) order the CUs' slots sat idle for about a quarter of the
+// chunked-prefill launches (per-work-group timestamps on MI355X, and a
+// simulation of the dispatch).  Up to kUnitRankSeqs sequences every
+// work-group therefore ranks the sequences by context length (longest first,
+// those without new rows last) and takes its unit from the list (rank, kv
+// head, row block last-first).  The list is dealt to the XCDs in runs of
+// p.chunk units (run j to XCD j % 8; a work-group's XCD is its index mod 8,
+// the order in which its units are dispatched there is its index / 8).  A
+// run is sized to a (sequence, kv head) pair's row blocks, which then run
+// side by side on one XCD and stream the shared prefix through its L2; the
+// XCDs see the ranks in the same order, longest first.  Above kUnitRankSeqs
+// sequences the units keep (kv head, sequence, row block) order, in
+// contiguous ranges per XCD.
+constexpr int kUnitRankSeqs = 256;
+
+// Unit u = (i-th of the list) of the ranked order: its sequence, kv head and
+// row block, or false past the list.
+template <int QB, int NT>
+__device__ inline bool ranked_unit(const DecodeParams& p, int i, int& s, int& h, int& rb) {
+  __shared__ int key[kUnitRankSeqs];
+  __shared__ int rows_of[kUnitRankSeqs];     // row blocks of sequence j
+  __shared__ int rank_seq[kUnitRankSeqs];    // the sequence of rank r
+  __shared__ int rank_rows[kUnitRankSeqs];   // its row blocks
+  const int tid = (int)threadIdx.x, lane = tid & 63;
+  const int S = p.num_seqs, H = p.num_kv_heads;
+  const int max_len = p.max_blocks << p.log2_bs;
+  for (int j = tid; j < S; j += NT) {
+    int n, m, q0;
+    prefill_lengths(p, j, max_len, n, m, q0);
+    key[j] = m > 0 ? n : -1;
+    rows_of[j] = (m + QB - 1) / QB;
+  }
+  __syncthreads();
+  for (int j = tid; j < S; j += NT) {
+    const int kj = key[j];
+    int r = 0;
+    for (int o = 0; o < S; ++o) {
+      const int ko = key[o];
+      r += (ko > kj || (ko == kj && o < j)) ? 1 : 0;
+    }
+    rank_seq[r] = j;
+    rank_rows[r] = rows_of[j];
+  }
+  __syncthreads();
+  // the rank holding list entry i: rank r owns H * rank_rows[r] entries
+  int carry = 0;
+  for (int base = 0; base < S; base += 64) {
+    const int c = base + lane < S ? H * rank_rows[base + lane] : 0;
+    const int incl = wave_inclusive_scan_i32(c, lane);
+    const int excl = carry + incl - c;
+    const unsigned long long hit = __ballot(c > 0 && excl <= i && i < excl + c);
+    if (hit) {
+      const int src = __builtin_ctzll(hit);
+      const int r = base + src;
+      const int R = uniform(rank_rows[r]);
+      const int off = i - uniform(__shfl(excl, src));
+      s = uniform(rank_seq[r]);
+      h = off / R;
+      rb = R - 1 - (off - h * R);
+      return true;
+    }
+    carry += __shfl(incl, 63);
+  }
+  return false;
+}
+
 template <typename KV, typename QT, int D, int G>
 __global__ __launch_bounds__(64 * unit_waves<D>()) __attribute__((amdgpu_waves_per_eu(D <= 128 ? 2 : 1)))
 void paged_prefill_unit_kernel(const DecodeParams p) {
@@ -689,30 +756,35 @@ void paged_prefill_unit_kernel(const DecodeParams p) {
   const int lane = (int)(threadIdx.x & 63);
   const int S = p.num_seqs;
   const int max_len = p.max_blocks << p.log2_bs;
-  int64_t per_head64 = 0;
-  for (int base = 0; base < S; base += 64) {
-    const int s = base + lane;
-    int cnt = 0;
-    if (s < S) {
-      int n, m, q0;
-      prefill_lengths(p, s, max_len, n, m, q0);
-      cnt = (m + QB - 1) / QB;
+  int s = 0, h = 0, rb = 0;
+  if (S <= kUnitRankSeqs) {
+    // work-group k of XCD x: entry (k / c) 8c + x c + k % c of the list
+    const int c = p.chunk, x = (int)(blockIdx.x & 7), k = (int)(blockIdx.x >> 3);
+    if (!ranked_unit<QB, 64 * unit_waves<D>()>(p, (k / c) * 8 * c + x * c + k % c, s, h, rb)) return;
+  } else {
+    int64_t per_head64 = 0;
+    for (int base = 0; base < S; base += 64) {
+      const int sl = base + lane;
+      int cnt = 0;
+      if (sl < S) {
+        int n, m, q0;
+        prefill_lengths(p, sl, max_len, n, m, q0);
+        cnt = (m + QB - 1) / QB;
+      }
+      per_head64 += wave_sum_i64(cnt);
     }
-    per_head64 += wave_sum_i64(cnt);
-  }
-  if (per_head64 == 0 || per_head64 * p.num_kv_heads > (1LL << 30)) return;
-  const int per_head = uniform((int)per_head64);
-  const int U = per_head * p.num_kv_heads;
-  const int per_xcd = (U + 7) >> 3;
-  const int k = (int)(blockIdx.x >> 3);
-  const int u = (int)(blockIdx.x & 7) * per_xcd + k;
-  if (k >= per_xcd || u >= U) return;
-  const int h = u / per_head;
-  const int r = u - h * per_head;
-  // the sequence holding unit r of kv head h
-  int s = 0, pre = 0;
-  bool found = false;
-  {
+    if (per_head64 == 0 || per_head64 * p.num_kv_heads > (1LL << 30)) return;
+    const int per_head = uniform((int)per_head64);
+    const int U = per_head * p.num_kv_heads;
+    const int per_xcd = (U + 7) >> 3;
+    const int k = (int)(blockIdx.x >> 3);
+    const int u = (int)(blockIdx.x & 7) * per_xcd + k;
+    if (k >= per_xcd || u >= U) return;
+    h = u / per_head;
+    const int r = u - h * per_head;
+    // the sequence holding unit r of kv head h
+    int pre = 0;
+    bool found = false;
     int carry = 0;
     for (int base = 0; base < S; base += 64) {
       const int sl = base + lane;
@@ -734,10 +806,10 @@ void paged_prefill_unit_kernel(const DecodeParams p) {
       }
       carry += __shfl(incl, 63);
     }
+    if (!found) return;
+    s = uniform(s);
+    rb = uniform(r - pre);
   }
-  if (!found) return;
-  s = uniform(s);
-  const int rb = uniform(r - pre);
   int n, m, qs;
   prefill_lengths(p, s, max_len, n, m, qs);
   n = uniform(n);

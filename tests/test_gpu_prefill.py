@@ -68,6 +68,19 @@ def test_ragged_and_empty_query_counts(gpu, G, D, kv, q, path):
     check_close(got["out"], OracleRun(wl).prefill(), wl.kv_dtype)
 
 
+@pytest.mark.parametrize("S", [256, 300])
+def test_units_at_and_past_the_rank_limit(gpu, S, monkeypatch):
+    """One work-group per row block with as many sequences as the kernel ranks
+    (longest first) and with more (dispatch order), some without new rows."""
+    monkeypatch.setenv("PAGEDKV_PREFILL_PATH", "unit")
+    rng = np.random.default_rng(S)
+    ctx = rng.integers(1, 60, size=S)
+    qn = np.minimum(ctx, rng.integers(0, 40, size=S))
+    qn[::9] = 0
+    wl = W._make(f"units_{S}", 15, 8, 2, 64, "bf16", "bf16", 16, ctx_lens=ctx.tolist(), query_lens=qn.tolist())
+    check_close(gpu(wl)["out"], OracleRun(wl).prefill(), wl.kv_dtype)
+
+
 def test_one_new_token_matches_decode_oracle(gpu):
     """m = 1 for every sequence is the decode step: the multi-token kernel
     agrees with the oracle's decode."""

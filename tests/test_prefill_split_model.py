@@ -198,10 +198,16 @@ def test_workload_shapes_fit(rows):
         assert (written == 1).all()
 
 
+RANK_SEQS = 256   # sequences the unit kernel ranks
+
+
 def replay_units(ctx, qs, total_q, hkv, G, D=128):
-    """Unit mode: one work-group per whole row block, units in (kv head,
-    sequence, row block) order, consecutive units on one XCD.  Checks the
-    host's grid bound and that every row block is computed exactly once."""
+    """Unit mode: one work-group per whole row block.  Up to RANK_SEQS
+    sequences the list is (rank by context length, longest first; kv head;
+    row block last-first), dealt to the XCDs in runs of c units; above it
+    the units keep (kv head, sequence, row block) order in contiguous ranges
+    per XCD.  Checks the host's grid and that every row block is computed
+    exactly once; returns the units each XCD runs, in dispatch order."""
     W = 8 if D <= 128 else 4
     rows = 16 * W
     QB = rows // G
@@ -210,20 +216,38 @@ def replay_units(ctx, qs, total_q, hkv, G, D=128):
     cnt = [-(-m // QB) for _, m, _ in L]
     per_head = sum(cnt)
     U = per_head * hkv
-    grid = ((total_q * G // rows + S + 1) * hkv + 7) & ~7
+    bound = (total_q * G // rows + S + 1) * hkv
+    grid = (bound + 7) & ~7
     seen = set()
-    per_xcd = (U + 7) >> 3
-    pre = np.concatenate([[0], np.cumsum(cnt)])
-    for b in range(grid):
-        k, u = b >> 3, (b & 7) * per_xcd + (b >> 3)
-        if k >= per_xcd or u >= U:
-            continue
-        h, r = divmod(u, per_head)
-        s = next(i for i in range(S) if cnt[i] > 0 and pre[i] <= r < pre[i] + cnt[i])
-        key = (h, s, r - pre[s])
-        assert key not in seen
-        seen.add(key)
-    return seen, U
+    order = [[] for _ in range(8)]
+    if S <= RANK_SEQS:
+        c = min(16, max(1, -(-(total_q * G) // (rows * S))))
+        grid = 8 * (-(-bound // (8 * c))) * c
+        key = [n if m > 0 else -1 for n, m, _ in L]
+        ranked = sorted(range(S), key=lambda j: (-key[j], j))
+        lst = [(h, s, rb) for s in ranked for h in range(hkv) for rb in reversed(range(cnt[s]))]
+        for b in range(grid):
+            x, k = b & 7, b >> 3
+            i = (k // c) * 8 * c + x * c + k % c
+            if i >= len(lst):
+                continue
+            assert lst[i] not in seen
+            seen.add(lst[i])
+            order[x].append((k, lst[i]))
+    else:
+        per_xcd = (U + 7) >> 3
+        pre = np.concatenate([[0], np.cumsum(cnt)])
+        for b in range(grid):
+            k, u = b >> 3, (b & 7) * per_xcd + (b >> 3)
+            if k >= per_xcd or u >= U:
+                continue
+            h, r = divmod(u, per_head)
+            s = next(i for i in range(S) if cnt[i] > 0 and pre[i] <= r < pre[i] + cnt[i])
+            key = (h, s, r - pre[s])
+            assert key not in seen
+            seen.add(key)
+            order[b & 7].append((k, key))
+    return seen, U, [[u for _, u in sorted(o)] for o in order]
 
 
 @pytest.mark.parametrize("G", [1, 4, 16])
@@ -236,5 +260,40 @@ def test_units_cover_every_row_block_once(G):
         ctx = np.maximum(ctx, 1)
         qs = np.concatenate([[0], np.cumsum(m)])
         for D in (128, 256):
-            seen, U = replay_units(ctx, qs, int(qs[-1]), int(rng.integers(1, 9)), G, D)
+            seen, U, _ = replay_units(ctx, qs, int(qs[-1]), int(rng.integers(1, 9)), G, D)
             assert len(seen) == U
+
+
+@pytest.mark.parametrize("S", [255, 256, 257, 300])
+def test_units_around_the_rank_limit(S):
+    """Both orders, at and around the number of sequences the kernel ranks,
+    with sequences that have no new rows."""
+    rng = np.random.default_rng(S)
+    m = rng.integers(0, 300, size=S)
+    m[::7] = 0
+    ctx = np.maximum(m + rng.integers(0, 200, size=S), 1)
+    qs = np.concatenate([[0], np.cumsum(m)])
+    for hkv in (1, 3, 8):
+        seen, U, _ = replay_units(ctx, qs, int(qs[-1]), hkv, 4)
+        assert len(seen) == U
+
+
+def test_ranked_units_run_longest_first_on_every_xcd():
+    """Each XCD receives its units by non-increasing context length of their
+    sequence, a sequence's row blocks last (longest) first, and the (sequence,
+    kv head) pairs of the chunked-prefill batch stay whole on one XCD."""
+    import workloads as W
+    for wl in W.multi_token_configs().values():
+        if wl.num_seqs > RANK_SEQS:
+            continue
+        ctx, qs = np.asarray(wl.context_lens), np.asarray(wl.query_start)
+        _, _, order = replay_units(ctx, qs, wl.total_q, wl.num_kv_heads, wl.group)
+        xcd_of = {}
+        for x, units in enumerate(order):
+            for (h0, s0, rb0), (h1, s1, rb1) in zip(units, units[1:]):
+                assert ctx[s0] >= ctx[s1], f"{wl.name}: XCD {x} not longest first"
+                assert (h0, s0) != (h1, s1) or rb0 > rb1
+            for h, s, rb in units:
+                xcd_of.setdefault((h, s), set()).add(x)
+        if wl.name.startswith("p1"):
+            assert all(len(v) == 1 for v in xcd_of.values())
