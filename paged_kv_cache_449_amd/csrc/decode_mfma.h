@@ -111,6 +111,20 @@ template <> struct mfma_ops<f16_t> {
   }
 };
 
+// Operand type of PV.  fp8 codes and f16 values are exact in f16, and
+// the weights P rounded once to f16 (relative error 2^-11) move an output by
+// at most 2^-11 of the largest |v| it averages, far inside the tolerance:
+// those pools take one f16 P operand.  bf16 values are not exact in f16 (its
+// range is smaller), and P rounded to bf16 (2^-8) is not accurate enough,
+// so bf16 pools take P as a rounded bf16 head plus the rounded remainder
+// (two PV instructions).
+template <typename KV, typename MT>
+struct pv_operand {
+  using type = typename std::conditional<std::is_same<MT, bf16_t>::value && elem_size<KV>::value == 2, bf16_t,
+                                         f16_t>::type;
+  static constexpr bool split = std::is_same<type, bf16_t>::value;
+};
+
 template <typename KV, int D>
 struct MfmaShape {
   static constexpr int EB = elem_size<KV>::value;
@@ -260,6 +274,9 @@ __device__ inline void mfma_rows_core(const DecodeParams& p, int s, int h, int o
                                       const Cut& cut = Cut{}) {
   using MT = typename mfma_operand<KV, QT>::type;
   using Ops = mfma_ops<MT>;
+  using PT = typename pv_operand<KV, MT>::type;
+  using PVOps = mfma_ops<PT>;
+  constexpr bool kSplitP = pv_operand<KV, MT>::split;
   using Sh = MfmaShape<KV, D>;
   constexpr int KS = Sh::KS, DT = Sh::DT, LSTRIDE = Sh::LSTRIDE;
   constexpr int TPS = MfmaStep<KV, D>::TPS;
@@ -320,10 +337,10 @@ __device__ inline void mfma_rows_core(const DecodeParams& p, int s, int h, int o
           *(uint4*)dst = r.t[q].v[u];
         } else {
           const uint4 w4 = r.t[q].v[u];
-          *(uint4*)dst = make_uint4(Ops::template from_fp8<false>(w4.x), Ops::template from_fp8<true>(w4.x),
-                                    Ops::template from_fp8<false>(w4.y), Ops::template from_fp8<true>(w4.y));
-          *(uint4*)(dst + 16) = make_uint4(Ops::template from_fp8<false>(w4.z), Ops::template from_fp8<true>(w4.z),
-                                           Ops::template from_fp8<false>(w4.w), Ops::template from_fp8<true>(w4.w));
+          *(uint4*)dst = make_uint4(PVOps::template from_fp8<false>(w4.x), PVOps::template from_fp8<true>(w4.x),
+                                    PVOps::template from_fp8<false>(w4.y), PVOps::template from_fp8<true>(w4.y));
+          *(uint4*)(dst + 16) = make_uint4(PVOps::template from_fp8<false>(w4.z), PVOps::template from_fp8<true>(w4.z),
+                                           PVOps::template from_fp8<false>(w4.w), PVOps::template from_fp8<true>(w4.w));
         }
         *(uint4*)(klds + (q * 16 + vr) * Sh::KSTRIDE + (byte % Sh::ROW)) = r.t[q].k[u];
       }
@@ -372,9 +389,11 @@ __device__ inline void mfma_rows_core(const DecodeParams& p, int s, int h, int o
       for (int dt = 0; dt < DT; ++dt) acc[dt] *= alpha;
     }
     const float mu = m == -INFINITY ? 0.0f : m;
-    // weights as a rounded head plus the rounded remainder: one 16-bit
-    // operand alone (8 significant bits for bf16) would leave an error of up
-    // to ~2^-8 of the spread of V in rows that see few tokens
+    // weights: one f16 operand where V is exact in f16 (fp8 codes, f16),
+    // else (bf16) a rounded head plus the rounded remainder -- one bf16
+    // operand alone (8 significant bits) would leave an error of up to ~2^-8
+    // of the spread of V in rows that see few tokens, f16's 2^-11 stays well
+    // inside the tolerance
     uint32_t ph[TPS][2], pr[TPS][2];
 #pragma unroll
     for (int q = 0; q < TPS; ++q) {
@@ -382,29 +401,32 @@ __device__ inline void mfma_rows_core(const DecodeParams& p, int s, int h, int o
 #pragma unroll
       for (int i = 0; i < 4; ++i) e[i] = fexp2(x[q][i] - mu);
       l += (e[0] + e[1]) + (e[2] + e[3]);
-      ph[q][0] = Ops::pack(e[0], e[1]);
-      ph[q][1] = Ops::pack(e[2], e[3]);
-      pr[q][0] = Ops::pack(e[0] - Ops::lo(ph[q][0]), e[1] - Ops::hi(ph[q][0]));
-      pr[q][1] = Ops::pack(e[2] - Ops::lo(ph[q][1]), e[3] - Ops::hi(ph[q][1]));
+      ph[q][0] = PVOps::pack(e[0], e[1]);
+      ph[q][1] = PVOps::pack(e[2], e[3]);
+      if constexpr (kSplitP) {
+        pr[q][0] = PVOps::pack(e[0] - PVOps::lo(ph[q][0]), e[1] - PVOps::hi(ph[q][0]));
+        pr[q][1] = PVOps::pack(e[2] - PVOps::lo(ph[q][1]), e[3] - PVOps::hi(ph[q][1]));
+      }
     }
     // lane (kg, i) needs V[4kg + e][16 dt + i], e = 0..3: one transposing read per tile
     const uint8_t* tr = vlds + (4 * kg + (j16 >> 2)) * LSTRIDE + (lane & 3) * 8;
     if constexpr (TPS == 2) {
       const uint4 bh = make_uint4(ph[0][0], ph[0][1], ph[1][0], ph[1][1]);
-      const uint4 br = make_uint4(pr[0][0], pr[0][1], pr[1][0], pr[1][1]);
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
-        const uint2 va = Ops::read_tr(tr + dt * 32);
-        const uint2 vb = Ops::read_tr(tr + 16 * LSTRIDE + dt * 32);
+        const uint2 va = PVOps::read_tr(tr + dt * 32);
+        const uint2 vb = PVOps::read_tr(tr + 16 * LSTRIDE + dt * 32);
         const uint4 a = make_uint4(va.x, va.y, vb.x, vb.y);
-        acc[dt] = Ops::qk(a, br, Ops::qk(a, bh, acc[dt]));
+        acc[dt] = PVOps::qk(a, bh, acc[dt]);
+        if constexpr (kSplitP) acc[dt] = PVOps::qk(a, make_uint4(pr[0][0], pr[0][1], pr[1][0], pr[1][1]), acc[dt]);
       }
     } else {
-      const uint2 bh = make_uint2(ph[0][0], ph[0][1]), br = make_uint2(pr[0][0], pr[0][1]);
+      const uint2 bh = make_uint2(ph[0][0], ph[0][1]);
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
-        const auto vt = Ops::read_tr(tr + dt * 32);
-        acc[dt] = Ops::pv(vt, br, Ops::pv(vt, bh, acc[dt]));
+        const auto vt = PVOps::read_tr(tr + dt * 32);
+        acc[dt] = PVOps::pv(vt, bh, acc[dt]);
+        if constexpr (kSplitP) acc[dt] = PVOps::pv(vt, make_uint2(pr[0][0], pr[0][1]), acc[dt]);
       }
     }
     if constexpr (Cut::kActive) {

@@ -286,6 +286,9 @@ __device__ inline void prefill_wg_run(const DecodeParams& p, int w, int chunk, i
                                       int rb, int off, int len, int n, int m, int qs) {
   using MT = typename mfma_operand<KV, QT>::type;
   using Ops = mfma_ops<MT>;
+  using PT = typename pv_operand<KV, MT>::type;   // one f16 P, or a split bf16 P
+  using PVOps = mfma_ops<PT>;
+  constexpr bool kSplitP = pv_operand<KV, MT>::split;
   using Sh = MfmaShape<KV, D>;
   constexpr int kTileGroup = TG;
   static_assert(TG == 2 || TG == 4, "tiles computed together");
@@ -370,10 +373,10 @@ __device__ inline void prefill_wg_run(const DecodeParams& p, int w, int chunk, i
         *(uint4*)dst = t.v[u];
       } else {
         const uint4 w4 = t.v[u];
-        *(uint4*)dst = make_uint4(Ops::template from_fp8<false>(w4.x), Ops::template from_fp8<true>(w4.x),
-                                  Ops::template from_fp8<false>(w4.y), Ops::template from_fp8<true>(w4.y));
-        *(uint4*)(dst + 16) = make_uint4(Ops::template from_fp8<false>(w4.z), Ops::template from_fp8<true>(w4.z),
-                                         Ops::template from_fp8<false>(w4.w), Ops::template from_fp8<true>(w4.w));
+        *(uint4*)dst = make_uint4(PVOps::template from_fp8<false>(w4.x), PVOps::template from_fp8<true>(w4.x),
+                                  PVOps::template from_fp8<false>(w4.y), PVOps::template from_fp8<true>(w4.y));
+        *(uint4*)(dst + 16) = make_uint4(PVOps::template from_fp8<false>(w4.z), PVOps::template from_fp8<true>(w4.z),
+                                         PVOps::template from_fp8<false>(w4.w), PVOps::template from_fp8<true>(w4.w));
       }
       *(uint4*)(kb + vr * KSTRIDE + (byte % Sh::ROW)) = t.k[u];
     }
@@ -464,10 +467,12 @@ __device__ inline void prefill_wg_run(const DecodeParams& p, int w, int chunk, i
 #pragma unroll
         for (int i = 0; i < 4; ++i) e[i] = fexp2(x[t][i] - mu);
         psum += (e[0] + e[1]) + (e[2] + e[3]);
-        ph[rt][t][0] = Ops::pack(e[0], e[1]);
-        ph[rt][t][1] = Ops::pack(e[2], e[3]);
-        pr[rt][t][0] = Ops::pack(e[0] - Ops::lo(ph[rt][t][0]), e[1] - Ops::hi(ph[rt][t][0]));
-        pr[rt][t][1] = Ops::pack(e[2] - Ops::lo(ph[rt][t][1]), e[3] - Ops::hi(ph[rt][t][1]));
+        ph[rt][t][0] = PVOps::pack(e[0], e[1]);
+        ph[rt][t][1] = PVOps::pack(e[2], e[3]);
+        if constexpr (kSplitP) {
+          pr[rt][t][0] = PVOps::pack(e[0] - PVOps::lo(ph[rt][t][0]), e[1] - PVOps::hi(ph[rt][t][0]));
+          pr[rt][t][1] = PVOps::pack(e[2] - PVOps::lo(ph[rt][t][1]), e[3] - PVOps::hi(ph[rt][t][1]));
+        }
       }
       l[rt] += psum;
     }
@@ -477,14 +482,17 @@ __device__ inline void prefill_wg_run(const DecodeParams& p, int w, int chunk, i
       const int ta = 2 * pair, tb = 2 * pair + 1;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
-        const uint2 va = Ops::read_tr(vlds + ta * VBYTES + tro + dt * 32);
-        const uint2 vb = Ops::read_tr(vlds + tb * VBYTES + tro + dt * 32);
+        const uint2 va = PVOps::read_tr(vlds + ta * VBYTES + tro + dt * 32);
+        const uint2 vb = PVOps::read_tr(vlds + tb * VBYTES + tro + dt * 32);
         const uint4 a = make_uint4(va.x, va.y, vb.x, vb.y);
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
           const uint4 bh = make_uint4(ph[rt][ta][0], ph[rt][ta][1], ph[rt][tb][0], ph[rt][tb][1]);
-          const uint4 br = make_uint4(pr[rt][ta][0], pr[rt][ta][1], pr[rt][tb][0], pr[rt][tb][1]);
-          acc[rt][dt] = Ops::qk(a, br, Ops::qk(a, bh, acc[rt][dt]));
+          acc[rt][dt] = PVOps::qk(a, bh, acc[rt][dt]);
+          if constexpr (kSplitP) {
+            const uint4 br = make_uint4(pr[rt][ta][0], pr[rt][ta][1], pr[rt][tb][0], pr[rt][tb][1]);
+            acc[rt][dt] = PVOps::qk(a, br, acc[rt][dt]);
+          }
         }
       }
     }
