@@ -280,15 +280,30 @@ __device__ inline int sequence_rowblock_blocks(int n, int m, int QB, int log2_bs
   return tot;
 }
 
+// LDS of a work-group's two staging buffers (V then K).
+template <int VSLOTS, int KSLOTS>
+__device__ inline uint8_t* wg_stage_lds() {
+  __shared__ __attribute__((aligned(16))) uint8_t buf[2 * (VSLOTS + KSLOTS)];
+  return buf;
+}
+
 // W waves of RT 16-row tiles each; TG tiles computed together.
-template <typename KV, typename QT, int D, int G, int W, int RT, int TG>
-__device__ inline void prefill_wg_run(const DecodeParams& p, int w, int chunk, int wstart, int pos, int s, int h,
+//
+// F16V (bf16 pools): V is staged in LDS as f16 and P is one f16 operand, as
+// for fp8 and f16 pools.  bf16 -> f16 is exact for every |v| below 65520
+// except in f16's subnormal range (|v| < 2^-14, absolute error at most
+// 2^-25); a wave that stages a value of magnitude 65536 or more (or a NaN)
+// flags it, and then the work-group returns false before storing anything,
+// for the caller to run the block again with F16V off (bf16 V, split P).
+template <typename KV, typename QT, int D, int G, int W, int RT, int TG, bool F16V = false>
+__device__ inline bool prefill_wg_run(const DecodeParams& p, int w, int chunk, int wstart, int pos, int s, int h,
                                       int rb, int off, int len, int n, int m, int qs) {
   using MT = typename mfma_operand<KV, QT>::type;
   using Ops = mfma_ops<MT>;
-  using PT = typename pv_operand<KV, MT>::type;   // one f16 P, or a split bf16 P
+  static_assert(!F16V || std::is_same<KV, bf16_t>::value, "f16 staging converts bf16 pools");
+  using PT = typename std::conditional<F16V, f16_t, typename pv_operand<KV, MT>::type>::type;
   using PVOps = mfma_ops<PT>;
-  constexpr bool kSplitP = pv_operand<KV, MT>::split;
+  constexpr bool kSplitP = !F16V && pv_operand<KV, MT>::split;
   using Sh = MfmaShape<KV, D>;
   constexpr int kTileGroup = TG;
   static_assert(TG == 2 || TG == 4, "tiles computed together");
@@ -298,9 +313,10 @@ __device__ inline void prefill_wg_run(const DecodeParams& p, int w, int chunk, i
   constexpr int QE = elem_size<QT>::value;
   constexpr int VBYTES = 16 * LSTRIDE, KBYTES = 16 * KSTRIDE;
   // two buffers of W tile slots: step st computes from buffer st & 1
-  // while the waves stage step st + 1 into the other
-  __shared__ __attribute__((aligned(16))) uint8_t vbuf[2 * W * VBYTES];
-  __shared__ __attribute__((aligned(16))) uint8_t kbuf[2 * W * KBYTES];
+  // while the waves stage step st + 1 into the other (shared by both F16V
+  // forms of a block: V elements are two bytes either way)
+  uint8_t* const vbuf = wg_stage_lds<W * VBYTES, W * KBYTES>();
+  uint8_t* const kbuf = vbuf + 2 * W * VBYTES;
   __shared__ int last_flag;
 
   const int wave = (int)(threadIdx.x >> 6);
@@ -361,6 +377,7 @@ __device__ inline void prefill_wg_run(const DecodeParams& p, int w, int chunk, i
   const int32_t* trow = p.block_tables + (int64_t)s * p.max_blocks + off;
 
   // this wave's tile of a step, into slot `wave` of buffer `buf`
+  uint32_t big = 0;   // F16V: max over staged V of |v| bits, per 16-bit half
   auto stage = [&](const MfmaTileRegs<KV, D>& t, int buf) {
     uint8_t* vb = vbuf + (buf * W + wave) * VBYTES;
     uint8_t* kb = kbuf + (buf * W + wave) * KBYTES;
@@ -369,7 +386,17 @@ __device__ inline void prefill_wg_run(const DecodeParams& p, int w, int chunk, i
       const int byte = (u * 64 + lane) * 16;
       const int vr = byte / Sh::ROW, ve = (byte % Sh::ROW) / Sh::EB;
       uint8_t* dst = vb + vr * LSTRIDE + ve * 2;
-      if constexpr (Sh::EB == 2) {
+      if constexpr (F16V) {
+        const uint32_t wv[4] = {t.v[u].x, t.v[u].y, t.v[u].z, t.v[u].w};
+        uint32_t hv[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          big = __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(u16x2v, big),
+                                                                       __builtin_bit_cast(u16x2v, wv[i] & 0x7fff7fffu)));
+          hv[i] = PVOps::pack(__uint_as_float(wv[i] << 16), __uint_as_float(wv[i] & 0xffff0000u));
+        }
+        *(uint4*)dst = make_uint4(hv[0], hv[1], hv[2], hv[3]);
+      } else if constexpr (Sh::EB == 2) {
         *(uint4*)dst = t.v[u];
       } else {
         const uint4 w4 = t.v[u];
@@ -529,6 +556,11 @@ __device__ inline void prefill_wg_run(const DecodeParams& p, int w, int chunk, i
     }
     tab = tab_next;
   }
+  if constexpr (F16V) {
+    // bf16 magnitude bits 0x4780 and up: 65536 or more, inf or NaN
+    const bool out_of_range = (big & 0xffffu) >= 0x4780u || (big >> 16) >= 0x4780u;
+    if (__syncthreads_or(out_of_range)) return false;
+  }
 
 #pragma unroll
   for (int t = 0; t < RT; ++t) {
@@ -548,7 +580,7 @@ __device__ inline void prefill_wg_run(const DecodeParams& p, int w, int chunk, i
         }
       }
     }
-    return;
+    return true;
   }
 
   // publish this wave's rows of the block's record, then one arrival for
@@ -577,6 +609,7 @@ __device__ inline void prefill_wg_run(const DecodeParams& p, int w, int chunk, i
   if (last_flag)
     merge_records<QT, D, 16 * TB, BlockRows, 64 * W>(
         p, first_w, last_w, seg_start, uniform_grid(chunk), BlockRows{qs, TB, rb, m, Q, Hq, h * G, G, D}, vsc);
+  return true;
 }
 
 template <typename KV, typename QT, int D, int G>
@@ -824,9 +857,13 @@ void paged_prefill_unit_kernel(const DecodeParams p) {
   m = uniform(m);
   qs = uniform(qs);
   const int nb = (tile_limit(n, m, QB, rb) + (1 << p.log2_bs) - 1) >> p.log2_bs;
-  // the whole row block: stored directly, no record
-  prefill_wg_run<KV, QT, D, G, unit_waves<D>(), unit_row_tiles<D>(), unit_tile_group<KV, D>()>(p, 0, 1, 0, 0, s, h, rb, 0,
-                                                                                           nb, n, m, qs);
+  // the whole row block: stored directly, no record; bf16 pools stage V as
+  // f16 and run again with bf16 V if it holds a value out of f16's range
+  constexpr int UW = unit_waves<D>(), URT = unit_row_tiles<D>(), UTG = unit_tile_group<KV, D>();
+  if constexpr (std::is_same<KV, bf16_t>::value) {
+    if (prefill_wg_run<KV, QT, D, G, UW, URT, UTG, true>(p, 0, 1, 0, 0, s, h, rb, 0, nb, n, m, qs)) return;
+  }
+  prefill_wg_run<KV, QT, D, G, UW, URT, UTG>(p, 0, 1, 0, 0, s, h, rb, 0, nb, n, m, qs);
 }
 
 // Prefill launch shape: 0 one-wave tiles, 1 split work-groups, 2 units.
