@@ -41,7 +41,6 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
-typedef unsigned short u16x2v __attribute__((ext_vector_type(2)));
 
 // Operand type of the matrix instructions for a (KV, query) dtype pair; void
 // where the pair runs on the vector ALUs instead.

@@ -280,6 +280,15 @@ __device__ inline int sequence_rowblock_blocks(int n, int m, int QB, int log2_bs
   return tot;
 }
 
+// max of x over lanes l, l ^ 16, l ^ 32 and l ^ 48: the 32-lane halves,
+// then the 16-lane rows, swapped between two copies of x (VALU, no LDS).
+__device__ inline float lane_max_xor32_xor16(float x) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  const float y = __builtin_elementwise_maximum(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(y), __float_as_uint(y), false, false);
+  return __builtin_elementwise_maximum(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
 // LDS of a work-group's two staging buffers (V then K).
 template <int VSLOTS, int KSLOTS>
 __device__ inline uint8_t* wg_stage_lds() {
@@ -325,6 +334,13 @@ __device__ inline bool prefill_wg_run(const DecodeParams& p, int w, int chunk, i
   const int kg = lane >> 4;
   const int Hq = p.num_kv_heads * G;
   const float qsc = run_q_scale(p, h), vsc = run_v_scale(p, h);
+  // Scores are scaled inside the exponent, exp2(sc * qabs - mu), and their
+  // max is taken before scaling, which needs a positive scale: a negative
+  // one flips the sign of the q operand instead (exact).  A zero scale
+  // becomes 1e-30, under which every score still rounds to exp2(0) = 1 and
+  // masked ones stay -inf.
+  const float qabs = fmaxf(fabsf(qsc), 1e-30f);
+  const uint32_t qflip = qsc < 0.0f ? 0x80008000u : 0u;
 
   // this wave's rows: row tiles TB rb + RT wave + t, t < RT
   int tok[RT], limit[RT];
@@ -350,17 +366,21 @@ __device__ inline bool prefill_wg_run(const DecodeParams& p, int w, int chunk, i
     if (valid[t]) {
       const int64_t qe = qoff[t] + kg * (D / 4);
 #pragma unroll
-      for (int k = 0; k < KS; ++k) qop[t][k] = *(const uint4*)(p.q + (qe + k * 8) * QE);
+      for (int k = 0; k < KS; ++k) {
+        const uint4 w4 = *(const uint4*)(p.q + (qe + k * 8) * QE);
+        qop[t][k] = make_uint4(w4.x ^ qflip, w4.y ^ qflip, w4.z ^ qflip, w4.w ^ qflip);
+      }
     }
   }
 
   f32x4 acc[RT][DT];
-  float mx_run[RT], l[RT];
+  float mx_run[RT], mu[RT], l[RT];   // reference max, the same as an exponent offset (0 while -inf), sum
 #pragma unroll
   for (int t = 0; t < RT; ++t) {
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) acc[t][dt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     mx_run[t] = -INFINITY;
+    mu[t] = 0.0f;
     l[t] = 0.0f;
   }
 
@@ -377,7 +397,7 @@ __device__ inline bool prefill_wg_run(const DecodeParams& p, int w, int chunk, i
   const int32_t* trow = p.block_tables + (int64_t)s * p.max_blocks + off;
 
   // this wave's tile of a step, into slot `wave` of buffer `buf`
-  uint32_t big = 0;   // F16V: max over staged V of |v| bits, per 16-bit half
+  float big = 0.0f;   // F16V: max |v| staged (NaN if a NaN was)
   auto stage = [&](const MfmaTileRegs<KV, D>& t, int buf) {
     uint8_t* vb = vbuf + (buf * W + wave) * VBYTES;
     uint8_t* kb = kbuf + (buf * W + wave) * KBYTES;
@@ -391,9 +411,9 @@ __device__ inline bool prefill_wg_run(const DecodeParams& p, int w, int chunk, i
         uint32_t hv[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          big = __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(u16x2v, big),
-                                                                       __builtin_bit_cast(u16x2v, wv[i] & 0x7fff7fffu)));
-          hv[i] = PVOps::pack(__uint_as_float(wv[i] << 16), __uint_as_float(wv[i] & 0xffff0000u));
+          const float lo = __uint_as_float(wv[i] << 16), hi = __uint_as_float(wv[i] & 0xffff0000u);
+          big = __builtin_elementwise_maximum(big, __builtin_elementwise_maximum(fabsf(lo), fabsf(hi)));
+          hv[i] = PVOps::pack(lo, hi);
         }
         *(uint4*)dst = make_uint4(hv[0], hv[1], hv[2], hv[3]);
       } else if constexpr (Sh::EB == 2) {
@@ -451,14 +471,15 @@ __device__ inline bool prefill_wg_run(const DecodeParams& p, int w, int chunk, i
     uint32_t ph[RT][kTileGroup][2], pr[RT][kTileGroup][2];
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
-      // Scores in log2 units.  Masking (causal limits, the window's end,
-      // table entries outside the pool) is needed only where a group reaches
-      // past the block's smallest limit or the window holds an invalid entry.
+      // Raw scores; qabs * score is in log2 units.  Masking (causal limits,
+      // the window's end, table entries outside the pool) is needed only
+      // where a group reaches past the block's smallest limit or the window
+      // holds an invalid entry.
       float x[kTileGroup][4];
 #pragma unroll
       for (int t = 0; t < kTileGroup; ++t)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) x[t][i] = sc[rt][t][i] * qsc;
+        for (int i = 0; i < 4; ++i) x[t][i] = sc[rt][t][i];
       if (masked) {
         const int lim = min(thi, limit[rt]);
 #pragma unroll
@@ -471,28 +492,32 @@ __device__ inline bool prefill_wg_run(const DecodeParams& p, int w, int chunk, i
             if (!(bvalid && t0 + i < lim)) x[t][i] = -INFINITY;
         }
       }
+      // the row's max over the group: the lane's values, then the four lane
+      // groups kg of the row (lanes j16 + 16 kg) by two half swaps.  NaN
+      // propagates, as it would through the exponentials.
       float mx = -INFINITY;
 #pragma unroll
-      for (int t = 0; t < kTileGroup; ++t) mx = fmaxf(mx, fmaxf(fmaxf(x[t][0], x[t][1]), fmaxf(x[t][2], x[t][3])));
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      for (int t = 0; t < kTileGroup; ++t)
+        mx = __builtin_elementwise_maximum(mx, __builtin_elementwise_maximum(__builtin_elementwise_maximum(x[t][0], x[t][1]),
+                                                                             __builtin_elementwise_maximum(x[t][2], x[t][3])));
+      mx = lane_max_xor32_xor16(mx) * qabs;
       // Lazy rescaling: the reference max moves only when a row's max passes
       // it by more than kRescaleSlack (log2 units).
       if (__ballot(mx > mx_run[rt] + kRescaleSlack)) {
         const float mn = fmaxf(mx_run[rt], mx);
         const float alpha = mx_run[rt] == -INFINITY ? 0.0f : fexp2(mx_run[rt] - mn);
         mx_run[rt] = mn;
+        mu[rt] = mn == -INFINITY ? 0.0f : mn;
         l[rt] *= alpha;
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) acc[rt][dt] *= alpha;
       }
-      const float mu = mx_run[rt] == -INFINITY ? 0.0f : mx_run[rt];
       float psum = 0.0f;
 #pragma unroll
       for (int t = 0; t < kTileGroup; ++t) {
         float e[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) e[i] = fexp2(x[t][i] - mu);
+        for (int i = 0; i < 4; ++i) e[i] = fexp2(__builtin_fmaf(x[t][i], qabs, -mu[rt]));
         psum += (e[0] + e[1]) + (e[2] + e[3]);
         ph[rt][t][0] = PVOps::pack(e[0], e[1]);
         ph[rt][t][1] = PVOps::pack(e[2], e[3]);
@@ -557,9 +582,9 @@ __device__ inline bool prefill_wg_run(const DecodeParams& p, int w, int chunk, i
     tab = tab_next;
   }
   if constexpr (F16V) {
-    // bf16 magnitude bits 0x4780 and up: 65536 or more, inf or NaN
-    const bool out_of_range = (big & 0xffffu) >= 0x4780u || (big >> 16) >= 0x4780u;
-    if (__syncthreads_or(out_of_range)) return false;
+    // the bf16 values next to f16's largest (65504) are 65280 and 65536:
+    // 65536 or more (inf included) or NaN is out of range
+    if (__syncthreads_or(!(big < 65536.0f))) return false;
   }
 
 #pragma unroll

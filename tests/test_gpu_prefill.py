@@ -114,6 +114,25 @@ def test_bf16_values_out_of_f16_range(gpu, value, monkeypatch):
         check_close(got2, want, wl.kv_dtype)
 
 
+@pytest.mark.parametrize("kv", ["bf16", "fp8e4m3"])
+@pytest.mark.parametrize("scale", [-0.11, 0.0, 0.9])
+def test_scale_sign_and_zero(gpu, kv, scale, path):
+    """The score scale enters inside the exponent and the row max is taken
+    before scaling: a negative scale (q's sign flipped), a zero one (every
+    visible token weighs the same) and a large one match the oracle."""
+    import paged_kv_cache_449_amd as pk
+    from gpu_harness import announce
+    wl = W._make(f"scale_{kv}", 17, 8, 2, 128, kv, "bf16", 16, ctx_lens=[200, 70, 33], query_lens=[150, 70, 20])
+    got = gpu(wl)
+    sess, q = got["session"], got["q"]
+    announce(f"prefill scale {scale} {kv}")
+    out = pk.paged_attention_prefill(sess.pool, q, sess.block_tables, sess.context_lens, sess.query_start, scale)
+    torch.cuda.synchronize()
+    ref = OracleRun(wl)
+    want = ref.pool.prefill(ref.q, wl.q_dtype, ref.tables, wl.context_lens, wl.query_start, scale, wl.num_q_heads)
+    check_close(out.float().cpu().double().numpy(), want, wl.kv_dtype)
+
+
 def test_one_new_token_matches_decode_oracle(gpu):
     """m = 1 for every sequence is the decode step: the multi-token kernel
     agrees with the oracle's decode."""
