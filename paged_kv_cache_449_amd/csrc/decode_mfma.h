@@ -190,32 +190,33 @@ template <typename KV, int D, int POL>
 __device__ inline void mfma_issue(const RunCtx& c, int tab, int tlo, int thi, int j, MfmaTileRegs<KV, D>& r) {
   using Sh = MfmaShape<KV, D>;
   const int lane = threadIdx.x & 63;
+  // the tile index and window are wave-uniform (the work-group kernels derive
+  // j from the wave index): say so, so the descriptors stay scalar
+  j = __builtin_amdgcn_readfirstlane(j);
+  tlo = __builtin_amdgcn_readfirstlane(tlo);
+  thi = __builtin_amdgcn_readfirstlane(thi);
   const int bi = min((j * 16) >> c.log2_bs, 63);
   const int phys = __builtin_amdgcn_readlane(tab, bi);
-  // an invalid entry (-1) gives an empty descriptor at the head's base
-  const int64_t boff = c.blk_stride * max(phys, 0);
-  const uint32_t nrec = c.tile_bytes & (uint32_t)~(phys >> 31);
-  __amdgpu_buffer_rsrc_t rk =
-      __builtin_amdgcn_make_buffer_rsrc((void*)(c.k_head + boff), (short)0, (int)nrec, kBufferWord3);
-  __amdgpu_buffer_rsrc_t rv =
-      __builtin_amdgcn_make_buffer_rsrc((void*)(c.v_head + boff), (short)0, (int)nrec, kBufferWord3);
   const int t0 = tlo + j * 16;             // first token of the tile
-  const int o0 = (j * 16) & c.bs_mask;     // its slot in the block
+  const int o0 = (j * 16) & c.bs_mask;     // its slot in the block (tiles never straddle blocks)
+  // The descriptors start at the tile and cover only its rows inside the
+  // window: rows at or past thi, and every row of a block whose table entry
+  // is out of range (-1), fall outside them and read as zeros, with no
+  // per-lane compare.  The lane offsets are then the same for every tile.
+  const int rows = __builtin_amdgcn_readfirstlane(phys < 0 ? 0 : max(0, min(16, thi - t0)));
+  const int64_t toff = c.blk_stride * max(phys, 0) + (int64_t)o0 * Sh::ROW;
+  const uint32_t nrec = (uint32_t)(rows * Sh::ROW);
+  __amdgpu_buffer_rsrc_t rk =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(c.k_head + toff), (short)0, (int)nrec, kBufferWord3);
+  __amdgpu_buffer_rsrc_t rv =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(c.v_head + toff), (short)0, (int)nrec, kBufferWord3);
   // K and V: the 16 x ROW tiles, contiguous, 16 bytes per lane per wave load
 #pragma unroll
-  for (int q = 0; q < Sh::KL; ++q) {
-    const int byte = (q * 64 + lane) * 16;
-    const int kr = byte / Sh::ROW, kc = byte % Sh::ROW;
-    const uint32_t ko = t0 + kr < thi ? (uint32_t)((o0 + kr) * Sh::ROW + kc) : kMaskedOffset;
-    r.k[q] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, ko, 0, POL));
-  }
+  for (int q = 0; q < Sh::KL; ++q)
+    r.k[q] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, (q * 64 + lane) * 16, 0, POL));
 #pragma unroll
-  for (int u = 0; u < Sh::VL; ++u) {
-    const int byte = (u * 64 + lane) * 16;
-    const int vr = byte / Sh::ROW, vc = byte % Sh::ROW;
-    const uint32_t vo = t0 + vr < thi ? (uint32_t)((o0 + vr) * Sh::ROW + vc) : kMaskedOffset;
-    r.v[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rv, vo, 0, POL));
-  }
+  for (int u = 0; u < Sh::VL; ++u)
+    r.v[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rv, (u * 64 + lane) * 16, 0, POL));
 }
 
 // K operand words of QK step st (8 elements of the operand type) from the

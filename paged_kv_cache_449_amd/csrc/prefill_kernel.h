@@ -328,7 +328,7 @@ __device__ inline bool prefill_wg_run(const DecodeParams& p, int w, int chunk, i
   uint8_t* const kbuf = vbuf + 2 * W * VBYTES;
   __shared__ int last_flag;
 
-  const int wave = (int)(threadIdx.x >> 6);
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));   // uniform: scalar LDS slot bases
   const int lane = (int)(threadIdx.x & 63);
   const int j16 = lane & 15;
   const int kg = lane >> 4;
@@ -374,14 +374,18 @@ __device__ inline bool prefill_wg_run(const DecodeParams& p, int w, int chunk, i
   }
 
   f32x4 acc[RT][DT];
-  float mx_run[RT], mu[RT], l[RT];   // reference max, the same as an exponent offset (0 while -inf), sum
+  float mx_run[RT], mu[RT];   // reference max, the same as an exponent offset (0 while -inf)
+  // Row sums on the matrix cores: P times a tile of ones, alongside PV, so
+  // the sum is of the very weights PV used and needs no cross-lane
+  // reduction (every element of lsum[t] holds the row's whole sum).
+  f32x4 lsum[RT];
 #pragma unroll
   for (int t = 0; t < RT; ++t) {
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) acc[t][dt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     mx_run[t] = -INFINITY;
     mu[t] = 0.0f;
-    l[t] = 0.0f;
+    lsum[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
   }
 
   RunCtx c;
@@ -412,7 +416,7 @@ __device__ inline bool prefill_wg_run(const DecodeParams& p, int w, int chunk, i
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const float lo = __uint_as_float(wv[i] << 16), hi = __uint_as_float(wv[i] & 0xffff0000u);
-          big = __builtin_elementwise_maximum(big, __builtin_elementwise_maximum(fabsf(lo), fabsf(hi)));
+          big = __builtin_elementwise_maximum(__builtin_elementwise_maximum(big, fabsf(lo)), fabsf(hi));
           hv[i] = PVOps::pack(lo, hi);
         }
         *(uint4*)dst = make_uint4(hv[0], hv[1], hv[2], hv[3]);
@@ -508,17 +512,15 @@ __device__ inline bool prefill_wg_run(const DecodeParams& p, int w, int chunk, i
         const float alpha = mx_run[rt] == -INFINITY ? 0.0f : fexp2(mx_run[rt] - mn);
         mx_run[rt] = mn;
         mu[rt] = mn == -INFINITY ? 0.0f : mn;
-        l[rt] *= alpha;
+        lsum[rt] *= alpha;
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) acc[rt][dt] *= alpha;
       }
-      float psum = 0.0f;
 #pragma unroll
       for (int t = 0; t < kTileGroup; ++t) {
         float e[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) e[i] = fexp2(__builtin_fmaf(x[t][i], qabs, -mu[rt]));
-        psum += (e[0] + e[1]) + (e[2] + e[3]);
         ph[rt][t][0] = PVOps::pack(e[0], e[1]);
         ph[rt][t][1] = PVOps::pack(e[2], e[3]);
         if constexpr (kSplitP) {
@@ -526,7 +528,6 @@ __device__ inline bool prefill_wg_run(const DecodeParams& p, int w, int chunk, i
           pr[rt][t][1] = PVOps::pack(e[2] - PVOps::lo(ph[rt][t][1]), e[3] - PVOps::hi(ph[rt][t][1]));
         }
       }
-      l[rt] += psum;
     }
     const int tro = (4 * kg + (j16 >> 2)) * LSTRIDE + (lane & 3) * 8;
 #pragma unroll
@@ -546,6 +547,14 @@ __device__ inline bool prefill_wg_run(const DecodeParams& p, int w, int chunk, i
             acc[rt][dt] = PVOps::qk(a, br, acc[rt][dt]);
           }
         }
+      }
+      const uint32_t one2 = PVOps::pack(1.0f, 1.0f);
+      const uint4 ones = make_uint4(one2, one2, one2, one2);
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) {
+        lsum[rt] = PVOps::qk(ones, make_uint4(ph[rt][ta][0], ph[rt][ta][1], ph[rt][tb][0], ph[rt][tb][1]), lsum[rt]);
+        if constexpr (kSplitP)
+          lsum[rt] = PVOps::qk(ones, make_uint4(pr[rt][ta][0], pr[rt][ta][1], pr[rt][tb][0], pr[rt][tb][1]), lsum[rt]);
       }
     }
   };
@@ -587,11 +596,9 @@ __device__ inline bool prefill_wg_run(const DecodeParams& p, int w, int chunk, i
     if (__syncthreads_or(!(big < 65536.0f))) return false;
   }
 
+  float l[RT];
 #pragma unroll
-  for (int t = 0; t < RT; ++t) {
-    l[t] += __shfl_xor(l[t], 16);
-    l[t] += __shfl_xor(l[t], 32);
-  }
+  for (int t = 0; t < RT; ++t) l[t] = lsum[t][0];
 
   if (off == 0 && off + len == nb) {   // the whole row block is ours
 #pragma unroll
