@@ -442,11 +442,9 @@ __device__ inline bool prefill_wg_run(const DecodeParams& p, int w, int chunk, i
   // (e < 4) and token 4kg + e - 4 of the second, on both operands: two
   // transposing reads give the V^T words, the two tiles' score words the P
   // words.
-  auto compute_group = [&](int tab, int tlo, int thi, int st, int g0, int unmasked_end) {
-    const uint8_t* vlds = vbuf + ((st & 1) * W + g0) * VBYTES;
+  // QK of the group's tiles (scores in sc) ...
+  auto qk_group = [&](int st, int g0, f32x4 (&sc)[RT][kTileGroup]) {
     const uint8_t* klds = kbuf + ((st & 1) * W + g0) * KBYTES;
-    const int j0 = st * W + g0;   // window tile index of slot g0
-    f32x4 sc[RT][kTileGroup];
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
@@ -471,44 +469,63 @@ __device__ inline bool prefill_wg_run(const DecodeParams& p, int w, int chunk, i
         }
       }
     }
+  };
+  // ... then the online softmax and PV.  Every row tile's max is taken
+  // before one rescale check for all of them, so the rare rescale is the
+  // only branch between the group's max and its exponentials.
+  auto softmax_pv_group = [&](int tab, int tlo, int thi, int st, int g0, int unmasked_end,
+                              const f32x4 (&sc)[RT][kTileGroup]) {
+    const uint8_t* vlds = vbuf + ((st & 1) * W + g0) * VBYTES;
+    const int j0 = st * W + g0;   // window tile index of slot g0
     const bool masked = tlo + (j0 + kTileGroup) * 16 > unmasked_end;
     uint32_t ph[RT][kTileGroup][2], pr[RT][kTileGroup][2];
+    float x[RT][kTileGroup][4], mx[RT];
+    // Raw scores; qabs * score is in log2 units.  Masking (causal limits, the
+    // window's end, table entries outside the pool) is needed only where a
+    // group reaches past the block's smallest limit or the window holds an
+    // invalid entry.
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
-      // Raw scores; qabs * score is in log2 units.  Masking (causal limits,
-      // the window's end, table entries outside the pool) is needed only
-      // where a group reaches past the block's smallest limit or the window
-      // holds an invalid entry.
-      float x[kTileGroup][4];
+    for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
       for (int t = 0; t < kTileGroup; ++t)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) x[t][i] = sc[rt][t][i];
-      if (masked) {
-        const int lim = min(thi, limit[rt]);
+        for (int i = 0; i < 4; ++i) x[rt][t][i] = sc[rt][t][i];
+    if (masked) {
 #pragma unroll
-        for (int t = 0; t < kTileGroup; ++t) {
-          const int j = j0 + t;
-          const bool bvalid = __builtin_amdgcn_readlane(tab, min((j * 16) >> p.log2_bs, 63)) >= 0;
-          const int t0 = tlo + j * 16 + 4 * kg;
+      for (int t = 0; t < kTileGroup; ++t) {
+        const int j = j0 + t;
+        const bool bvalid = __builtin_amdgcn_readlane(tab, min((j * 16) >> p.log2_bs, 63)) >= 0;
+        const int t0 = tlo + j * 16 + 4 * kg;
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+          const int lim = min(thi, limit[rt]);
 #pragma unroll
           for (int i = 0; i < 4; ++i)
-            if (!(bvalid && t0 + i < lim)) x[t][i] = -INFINITY;
+            if (!(bvalid && t0 + i < lim)) x[rt][t][i] = -INFINITY;
         }
       }
-      // the row's max over the group: the lane's values, then the four lane
-      // groups kg of the row (lanes j16 + 16 kg) by two half swaps.  NaN
-      // propagates, as it would through the exponentials.
-      float mx = -INFINITY;
+    }
+    // each row's max over the group: the lane's values, then the four lane
+    // groups kg of the row (lanes j16 + 16 kg) by two half swaps.  NaN
+    // propagates, as it would through the exponentials.
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      float m = -INFINITY;
 #pragma unroll
       for (int t = 0; t < kTileGroup; ++t)
-        mx = __builtin_elementwise_maximum(mx, __builtin_elementwise_maximum(__builtin_elementwise_maximum(x[t][0], x[t][1]),
-                                                                             __builtin_elementwise_maximum(x[t][2], x[t][3])));
-      mx = lane_max_xor32_xor16(mx) * qabs;
-      // Lazy rescaling: the reference max moves only when a row's max passes
-      // it by more than kRescaleSlack (log2 units).
-      if (__ballot(mx > mx_run[rt] + kRescaleSlack)) {
-        const float mn = fmaxf(mx_run[rt], mx);
+        m = __builtin_elementwise_maximum(m, __builtin_elementwise_maximum(__builtin_elementwise_maximum(x[rt][t][0], x[rt][t][1]),
+                                                                           __builtin_elementwise_maximum(x[rt][t][2], x[rt][t][3])));
+      mx[rt] = lane_max_xor32_xor16(m) * qabs;
+    }
+    // Lazy rescaling: the reference max moves only when a row's max passes
+    // it by more than kRescaleSlack (log2 units); all row tiles move together.
+    bool grow = false;
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) grow = grow || mx[rt] > mx_run[rt] + kRescaleSlack;
+    if (__ballot(grow)) {
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) {
+        const float mn = fmaxf(mx_run[rt], mx[rt]);
         const float alpha = mx_run[rt] == -INFINITY ? 0.0f : fexp2(mx_run[rt] - mn);
         mx_run[rt] = mn;
         mu[rt] = mn == -INFINITY ? 0.0f : mn;
@@ -516,11 +533,14 @@ __device__ inline bool prefill_wg_run(const DecodeParams& p, int w, int chunk, i
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) acc[rt][dt] *= alpha;
       }
+    }
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
 #pragma unroll
       for (int t = 0; t < kTileGroup; ++t) {
         float e[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) e[i] = fexp2(__builtin_fmaf(x[t][i], qabs, -mu[rt]));
+        for (int i = 0; i < 4; ++i) e[i] = fexp2(__builtin_fmaf(x[rt][t][i], qabs, -mu[rt]));
         ph[rt][t][0] = PVOps::pack(e[0], e[1]);
         ph[rt][t][1] = PVOps::pack(e[2], e[3]);
         if constexpr (kSplitP) {
@@ -580,8 +600,22 @@ __device__ inline bool prefill_wg_run(const DecodeParams& p, int w, int chunk, i
     mfma_issue<KV, D, kStreamPolicy>(c, tab, tlo, thi, W + wave, rt);
     __syncthreads();
     for (int st = 0; st < steps; ++st) {
+      if constexpr (W == 2 * kTileGroup) {
+        // both groups' QK first: the second group's runs on the matrix
+        // cores while the first group's softmax runs on the vector ALUs
+        f32x4 sa[RT][kTileGroup], sb[RT][kTileGroup];
+        qk_group(st, 0, sa);
+        qk_group(st, kTileGroup, sb);
+        softmax_pv_group(tab, tlo, thi, st, 0, unmasked_end, sa);
+        softmax_pv_group(tab, tlo, thi, st, kTileGroup, unmasked_end, sb);
+      } else {
 #pragma unroll
-      for (int g0 = 0; g0 < W; g0 += kTileGroup) compute_group(tab, tlo, thi, st, g0, unmasked_end);
+        for (int g0 = 0; g0 < W; g0 += kTileGroup) {
+          f32x4 sg[RT][kTileGroup];
+          qk_group(st, g0, sg);
+          softmax_pv_group(tab, tlo, thi, st, g0, unmasked_end, sg);
+        }
+      }
       if (st + 1 < steps) {
         stage(rt, (st + 1) & 1);
         mfma_issue<KV, D, kStreamPolicy>(c, tab, tlo, thi, (st + 2) * W + wave, rt);
