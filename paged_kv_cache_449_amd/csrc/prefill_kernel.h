@@ -242,15 +242,17 @@ constexpr int kTileGroup = 4;     // tiles a wave computes together
 // reads from LDS then feeds 32 rows, and two work-groups share a CU (two
 // waves per SIMD, 240-248 VGPRs).  On MI355X that took the chunked-prefill
 // workload from 770 to 702 us and the fp8 GQA chunks from 427 to 373 us.
-// fp8 pools compute 4 tiles together; 16-bit pools 2, which keeps them
-// clear of spills at the 256-VGPR cap (4 and 2 time alike on bf16).  The
-// split work-groups keep 8 x 1: their merge code would spill at that cap.
+// Every pool computes 4 tiles together (one group per 64-token step):
+// with one f16 P operand and the row sums on the matrix cores the 16-bit
+// loop fits the 256-VGPR cap at 4 as well, and ran 2-3% faster than 2 on
+// the chunked-prefill batch.  The split work-groups keep 8 x 1: their
+// merge code would spill at that cap.
 template <int D>
 constexpr int unit_waves() { return D <= 128 ? 4 : wg_waves<D>(); }
 template <int D>
 constexpr int unit_row_tiles() { return D <= 128 ? 2 : 1; }
 template <typename KV, int D>
-constexpr int unit_tile_group() { return D <= 128 && elem_size<KV>::value == 2 ? 2 : 4; }
+constexpr int unit_tile_group() { return 4; }
 
 // Out rows of a row block's records: row j is row tile waves * rb + j / 16
 // (waves: row tiles per block), slot j % 16 of it.
