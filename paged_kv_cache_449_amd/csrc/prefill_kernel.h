@@ -282,6 +282,18 @@ __device__ inline int sequence_rowblock_blocks(int n, int m, int QB, int log2_bs
   return tot;
 }
 
+// max of n values (n >= 3), folded two at a time into a running max so each
+// step is one v_maximum3_f32 (NaN propagates)
+template <int N>
+__device__ inline float max_of(const float* v) {
+  static_assert(N >= 3, "three or more values");
+  float m = __builtin_elementwise_maximum(__builtin_elementwise_maximum(v[0], v[1]), v[2]);
+#pragma unroll
+  for (int i = 3; i + 1 < N; i += 2) m = __builtin_elementwise_maximum(__builtin_elementwise_maximum(m, v[i]), v[i + 1]);
+  if constexpr (N % 2 == 0) m = __builtin_elementwise_maximum(m, v[N - 1]);
+  return m;
+}
+
 // max of x over lanes l, l ^ 16, l ^ 32 and l ^ 48: the 32-lane halves,
 // then the 16-lane rows, swapped between two copies of x (VALU, no LDS).
 __device__ inline float lane_max_xor32_xor16(float x) {
@@ -405,8 +417,9 @@ __device__ inline bool prefill_wg_run(const DecodeParams& p, int w, int chunk, i
   // this wave's tile of a step, into slot `wave` of buffer `buf`
   float big = 0.0f;   // F16V: max |v| staged (NaN if a NaN was)
   auto stage = [&](const MfmaTileRegs<KV, D>& t, int buf) {
-    uint8_t* vb = vbuf + (buf * W + wave) * VBYTES;
-    uint8_t* kb = kbuf + (buf * W + wave) * KBYTES;
+    const int slot = __builtin_amdgcn_readfirstlane(buf * W + wave);   // scalar slot bases
+    uint8_t* vb = vbuf + slot * VBYTES;
+    uint8_t* kb = kbuf + slot * KBYTES;
 #pragma unroll
     for (int u = 0; u < Sh::VL; ++u) {
       const int byte = (u * 64 + lane) * 16;
@@ -512,11 +525,7 @@ __device__ inline bool prefill_wg_run(const DecodeParams& p, int w, int chunk, i
     // propagates, as it would through the exponentials.
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
-      float m = -INFINITY;
-#pragma unroll
-      for (int t = 0; t < kTileGroup; ++t)
-        m = __builtin_elementwise_maximum(m, __builtin_elementwise_maximum(__builtin_elementwise_maximum(x[rt][t][0], x[rt][t][1]),
-                                                                           __builtin_elementwise_maximum(x[rt][t][2], x[rt][t][3])));
+      const float m = max_of<kTileGroup * 4>(&x[rt][0][0]);
       mx[rt] = lane_max_xor32_xor16(m) * qabs;
     }
     // Lazy rescaling: the reference max moves only when a row's max passes
