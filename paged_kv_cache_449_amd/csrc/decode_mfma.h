@@ -257,6 +257,27 @@ struct MfmaRow {
   int64_t part;   // PART runs: index of the row's partial record
 };
 
+// max of n values (n >= 3), folded two at a time into a running max so each
+// step is one v_maximum3_f32 (NaN propagates)
+template <int N>
+__device__ inline float max_of(const float* v) {
+  static_assert(N >= 3, "three or more values");
+  float m = __builtin_elementwise_maximum(__builtin_elementwise_maximum(v[0], v[1]), v[2]);
+#pragma unroll
+  for (int i = 3; i + 1 < N; i += 2) m = __builtin_elementwise_maximum(__builtin_elementwise_maximum(m, v[i]), v[i + 1]);
+  if constexpr (N % 2 == 0) m = __builtin_elementwise_maximum(m, v[N - 1]);
+  return m;
+}
+
+// max of x over lanes l, l ^ 16, l ^ 32 and l ^ 48: the 32-lane halves,
+// then the 16-lane rows, swapped between two copies of x (VALU, no LDS).
+__device__ inline float lane_max_xor32_xor16(float x) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  const float y = __builtin_elementwise_maximum(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(y), __float_as_uint(y), false, false);
+  return __builtin_elementwise_maximum(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
 // One run of up to 16 query rows against blocks [off, off+len) of the
 // (kv head h, sequence s) stream, which has nb blocks and n tokens; `rows`
 // maps record row j to the element offset of its out row (-1: no query).
@@ -288,7 +309,14 @@ __device__ inline void mfma_rows_core(const DecodeParams& p, int s, int h, int o
   const int lane = threadIdx.x;
   const int j16 = lane & 15;   // token row (QK A) / query row (B, D)
   const int kg = lane >> 4;    // k group
-  const float qs = run_q_scale(p, h);
+  // Scores are scaled inside the exponent, exp2(sc * qabs - mu), and their
+  // max is taken before scaling, which needs a positive scale: a negative
+  // one flips the sign of the q operand instead (exact).  A zero scale
+  // becomes 1e-30, under which every score still rounds to exp2(0) = 1 and
+  // masked ones stay -inf.
+  const float qsc = run_q_scale(p, h);
+  const float qabs = fmaxf(fabsf(qsc), 1e-30f);
+  const uint32_t qflip = qsc < 0.0f ? 0x80008000u : 0u;
 
   // q operand: lane (kg, j) holds q row j at dims kg*D/4 + 8st .. +8 for step st
   uint4 qop[KS];
@@ -297,13 +325,17 @@ __device__ inline void mfma_rows_core(const DecodeParams& p, int s, int h, int o
   if (row.valid) {
     const int64_t qe = row.qoff + kg * (D / 4);
 #pragma unroll
-    for (int st = 0; st < KS; ++st) qop[st] = *(const uint4*)(p.q + (qe + st * 8) * QE);
+    for (int st = 0; st < KS; ++st) {
+      const uint4 w4 = *(const uint4*)(p.q + (qe + st * 8) * QE);
+      qop[st] = make_uint4(w4.x ^ qflip, w4.y ^ qflip, w4.z ^ qflip, w4.w ^ qflip);
+    }
   }
 
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
   m = -INFINITY;   // reference max of row j16 (log2 units)
   l = 0.0f;        // this lane's share of the running sum, until the end
+  float mu = 0.0f; // m as the exponent offset (0 while m is -inf)
 
   RunCtx c;
   const int64_t tile = (int64_t)Sh::ROW << p.log2_bs;
@@ -363,7 +395,7 @@ __device__ inline void mfma_rows_core(const DecodeParams& p, int s, int h, int o
 #pragma unroll
     for (int q = 0; q < TPS; ++q)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) x[q][i] = sc[q][i] * qs;
+      for (int i = 0; i < 4; ++i) x[q][i] = sc[q][i];   // raw: qabs * score is in log2 units
     if (tlo + (st + 1) * TPS * 16 > unmasked_end) {   // some token of the step may be masked
       const int lim = min(thi, row.limit);
 #pragma unroll
@@ -376,20 +408,18 @@ __device__ inline void mfma_rows_core(const DecodeParams& p, int s, int h, int o
           if (!(bvalid && t0 + i < lim)) x[q][i] = -INFINITY;
       }
     }
-    float mx = -INFINITY;
-#pragma unroll
-    for (int q = 0; q < TPS; ++q) mx = fmaxf(mx, fmaxf(fmaxf(x[q][0], x[q][1]), fmaxf(x[q][2], x[q][3])));
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    // the row's max: the lane's values, then the four lane groups kg of the
+    // row by two half swaps (NaN propagates, as through the exponentials)
+    const float mx = lane_max_xor32_xor16(max_of<TPS * 4>(&x[0][0])) * qabs;
     if (__ballot(mx > m + kRescaleSlack)) {
       const float mn = fmaxf(m, mx);
       const float alpha = m == -INFINITY ? 0.0f : fexp2(m - mn);
       m = mn;
+      mu = mn == -INFINITY ? 0.0f : mn;
       l *= alpha;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) acc[dt] *= alpha;
     }
-    const float mu = m == -INFINITY ? 0.0f : m;
     // weights: one f16 operand where V is exact in f16 (fp8 codes, f16),
     // else (bf16) a rounded head plus the rounded remainder -- one bf16
     // operand alone (8 significant bits) would leave an error of up to ~2^-8
@@ -400,7 +430,7 @@ __device__ inline void mfma_rows_core(const DecodeParams& p, int s, int h, int o
     for (int q = 0; q < TPS; ++q) {
       float e[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) e[i] = fexp2(x[q][i] - mu);
+      for (int i = 0; i < 4; ++i) e[i] = fexp2(__builtin_fmaf(x[q][i], qabs, -mu));
       l += (e[0] + e[1]) + (e[2] + e[3]);
       ph[q][0] = PVOps::pack(e[0], e[1]);
       ph[q][1] = PVOps::pack(e[2], e[3]);
@@ -444,6 +474,7 @@ __device__ inline void mfma_rows_core(const DecodeParams& p, int s, int h, int o
         for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
         m = -INFINITY;
         l = 0.0f;
+        mu = 0.0f;
       }
     }
   };

@@ -282,27 +282,6 @@ __device__ inline int sequence_rowblock_blocks(int n, int m, int QB, int log2_bs
   return tot;
 }
 
-// max of n values (n >= 3), folded two at a time into a running max so each
-// step is one v_maximum3_f32 (NaN propagates)
-template <int N>
-__device__ inline float max_of(const float* v) {
-  static_assert(N >= 3, "three or more values");
-  float m = __builtin_elementwise_maximum(__builtin_elementwise_maximum(v[0], v[1]), v[2]);
-#pragma unroll
-  for (int i = 3; i + 1 < N; i += 2) m = __builtin_elementwise_maximum(__builtin_elementwise_maximum(m, v[i]), v[i + 1]);
-  if constexpr (N % 2 == 0) m = __builtin_elementwise_maximum(m, v[N - 1]);
-  return m;
-}
-
-// max of x over lanes l, l ^ 16, l ^ 32 and l ^ 48: the 32-lane halves,
-// then the 16-lane rows, swapped between two copies of x (VALU, no LDS).
-__device__ inline float lane_max_xor32_xor16(float x) {
-  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  const float y = __builtin_elementwise_maximum(__uint_as_float(a[0]), __uint_as_float(a[1]));
-  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(y), __float_as_uint(y), false, false);
-  return __builtin_elementwise_maximum(__uint_as_float(b[0]), __uint_as_float(b[1]));
-}
-
 // LDS of a work-group's two staging buffers (V then K).
 template <int VSLOTS, int KSLOTS>
 __device__ inline uint8_t* wg_stage_lds() {

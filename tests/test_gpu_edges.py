@@ -85,6 +85,25 @@ def test_fp8_scale_applies_to_values(pk):
     torch.testing.assert_close(out, torch.full_like(out, 0.25), rtol=1e-6, atol=0)
 
 
+@pytest.mark.parametrize("kv,hq,hkv,pt", [("bf16", 8, 2, 0), ("fp8e4m3", 8, 2, 32), ("f16", 4, 4, 0)])
+@pytest.mark.parametrize("scale", [-0.11, 0.0, 0.9])
+def test_scale_sign_and_zero(pk, gpu, kv, hq, hkv, pt, scale):
+    """The matrix-core runs scale scores inside the exponent and take the row
+    max before scaling: a negative scale (q's sign flipped), a zero one
+    (every token weighs the same) and a large one match the oracle, on the
+    matrix-core (query groups, with and without caller partitions) and the
+    vector-ALU path."""
+    wl = W._make(f"scale_{kv}_{hq}", 92, hq, hkv, 128, kv, "bf16" if kv != "f16" else "f16", 16,
+                 ctx_lens=[300, 45, 7, 130])
+    got = gpu(wl, partition_tokens=pt)
+    sess, q = got["session"], got["q"]
+    out = pk.paged_attention_decode(sess.pool, q, sess.block_tables, sess.context_lens, scale, partition_tokens=pt)
+    torch.cuda.synchronize()
+    ref = OracleRun(wl)
+    want = ref.pool.decode(ref.q, wl.q_dtype, ref.tables, wl.context_lens, scale, wl.num_q_heads)
+    check_close(out.float().cpu().double().numpy(), want, wl.kv_dtype)
+
+
 def test_empty_context_gives_zero_rows(pk):
     wl = W.custom("empty", 4, 4, 128, "f16", "f16", 16, [30, 47, 1, 64], index=91)
     from gpu_harness import run_gpu
