@@ -648,6 +648,9 @@ def main(argv=None) -> int:
                     help="no GPU work: turn the counter_collection.csv files of a rocprofv3 --pmc FETCH_SIZE run "
                          "and a --pmc WRITE_SIZE run of this same command line (with --calibrate-copy) into HBM "
                          "bytes per launch, and record them in profiles/<kind>_traffic.json")
+    ap.add_argument("--summarise-sq", nargs="+", default=None, metavar="PMC_CSV",
+                    help="print markdown rows of shader (SQ) counters per dispatch of the attention kernels, "
+                         "one rocprofv3 --pmc pass per CSV, with the ratios between them")
     ap.add_argument("--summarise-l2", default=None, metavar="PMC_CSV",
                     help="no GPU work: the counter_collection.csv of a rocprofv3 --pmc TCC_HIT_sum TCC_MISS_sum run "
                          "of this same command line -> one markdown row per decode kernel (L2 hits and misses per "
@@ -659,6 +662,8 @@ def main(argv=None) -> int:
     args = ap.parse_args(argv)
     if args.summarise_l2:
         return summarise_l2_main(args)
+    if args.summarise_sq:
+        return summarise_sq_main(args)
     if args.summarise_trace:
         return summarise_trace_main(args, argv)
     if args.block_manager:
@@ -920,6 +925,45 @@ def summarise_main(args, argv) -> int:
     cmds = [f"rocprofv3 --pmc {c} --output-format csv -d <dir> -o pmc -- python3 bench.py {base} --calibrate-copy"
             for c in ("FETCH_SIZE", "WRITE_SIZE")]
     record_traffic(kind, key, entry, algorithmic, cmds)
+    return 0
+
+
+def summarise_sq_main(args) -> int:
+    """--summarise-sq: shader counters of the attention kernels, summed over
+    the GPU per dispatch and averaged over the dispatches of each pass, then
+    the ratios between them.  Wave-cycle counters share one unit, so their
+    ratios are shares of the waves' lifetime; the matrix-core busy cycles are
+    set against 1024 SIMDs x the dispatch time at 2.4 GHz."""
+    vals, durs = {}, {}
+    name = None
+    for path in args.summarise_sq:
+        per = {}
+        for r in _pmc_rows(path):
+            if "paged_decode_kernel" not in r["Kernel_Name"] and "paged_prefill" not in r["Kernel_Name"]:
+                continue
+            name = r["Kernel_Name"].split("(")[0].replace("void ", "").replace("pkv::", "")
+            d = per.setdefault(r["Dispatch_Id"], {})
+            d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+            durs.setdefault(path, {})[r["Dispatch_Id"]] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+        for c in {c for d in per.values() for c in d}:
+            vals[c] = float(np.mean([d[c] for d in per.values() if c in d]))
+    us = float(np.mean([u for d in durs.values() for u in d.values()]))
+    wl = get_workload(args.workload)
+    print(f"| {wl.name} | `{name}` | {us:.1f} | " + " | ".join(f"{c} {v:.4g}" for c, v in sorted(vals.items())) + " |")
+    wc = vals.get("SQ_WAVE_CYCLES")
+    out = []
+    for c in ("SQ_ACTIVE_INST_VALU", "SQ_ACTIVE_INST_LDS", "SQ_WAIT_INST_ANY", "SQ_WAIT_INST_LDS", "SQ_WAIT_ANY"):
+        if wc and c in vals:
+            out.append(f"{c} / SQ_WAVE_CYCLES {vals[c] / wc:.3f}")
+    if "SQ_VALU_MFMA_BUSY_CYCLES" in vals:
+        out.append(f"matrix-core busy {vals['SQ_VALU_MFMA_BUSY_CYCLES'] / (1024 * us * 2400):.3f} of 1024 SIMDs")
+    if "SQ_LDS_BANK_CONFLICT" in vals and vals.get("SQ_LDS_IDX_ACTIVE"):
+        out.append(f"LDS bank conflicts / LDS active {vals['SQ_LDS_BANK_CONFLICT'] / vals['SQ_LDS_IDX_ACTIVE']:.3f}")
+    if "SQ_INSTS_MFMA" in vals:
+        for c in ("SQ_INSTS_VALU", "SQ_INSTS_VALU_TRANS_F32", "SQ_INSTS_LDS"):
+            if c in vals:
+                out.append(f"{c} per MFMA {vals[c] / vals['SQ_INSTS_MFMA']:.2f}")
+    print("| | " + "; ".join(out) + " |")
     return 0
 
 
