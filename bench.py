@@ -949,7 +949,7 @@ def summarise_sq_main(args) -> int:
             vals[c] = float(np.mean([d[c] for d in per.values() if c in d]))
     us = float(np.mean([u for d in durs.values() for u in d.values()]))
     wl = get_workload(args.workload)
-    print(f"| {wl.name} | `{name}` | {us:.1f} | " + " | ".join(f"{c} {v:.4g}" for c, v in sorted(vals.items())) + " |")
+    print(f"| {wl.name} | `{name}` | {us:.1f} | " + "; ".join(f"{c} {v:.4g}" for c, v in sorted(vals.items())) + " |")
     wc = vals.get("SQ_WAVE_CYCLES")
     out = []
     for c in ("SQ_ACTIVE_INST_VALU", "SQ_ACTIVE_INST_LDS", "SQ_WAIT_INST_ANY", "SQ_WAIT_INST_LDS", "SQ_WAIT_ANY"):
@@ -963,7 +963,7 @@ def summarise_sq_main(args) -> int:
         for c in ("SQ_INSTS_VALU", "SQ_INSTS_VALU_TRANS_F32", "SQ_INSTS_LDS"):
             if c in vals:
                 out.append(f"{c} per MFMA {vals[c] / vals['SQ_INSTS_MFMA']:.2f}")
-    print("| | " + "; ".join(out) + " |")
+    print("| | | | " + "; ".join(out) + " |")
     return 0
 
 
