@@ -799,10 +799,14 @@ __global__ __launch_bounds__(64 * wg_waves<D>()) void paged_prefill_wg_kernel(co
 constexpr int kUnitRankSeqs = 256;
 
 // Unit u = (i-th of the list) of the ranked order: its sequence, kv head and
-// row block, or false past the list.
+// row block, and that sequence's lengths and first query row (kept from the
+// ranking, so the unit needs no second round trip for them), or false past
+// the list.
 template <int QB, int NT>
-__device__ inline bool ranked_unit(const DecodeParams& p, int i, int& s, int& h, int& rb) {
-  __shared__ int key[kUnitRankSeqs];
+__device__ inline bool ranked_unit(const DecodeParams& p, int i, int& s, int& h, int& rb, int& n, int& m, int& qs) {
+  __shared__ int key[kUnitRankSeqs];         // context length, -1 without new rows
+  __shared__ int new_of[kUnitRankSeqs];      // new rows of sequence j
+  __shared__ int q0_of[kUnitRankSeqs];       // its first query row
   __shared__ int rows_of[kUnitRankSeqs];     // row blocks of sequence j
   __shared__ int rank_seq[kUnitRankSeqs];    // the sequence of rank r
   __shared__ int rank_rows[kUnitRankSeqs];   // its row blocks
@@ -810,10 +814,12 @@ __device__ inline bool ranked_unit(const DecodeParams& p, int i, int& s, int& h,
   const int S = p.num_seqs, H = p.num_kv_heads;
   const int max_len = p.max_blocks << p.log2_bs;
   for (int j = tid; j < S; j += NT) {
-    int n, m, q0;
-    prefill_lengths(p, j, max_len, n, m, q0);
-    key[j] = m > 0 ? n : -1;
-    rows_of[j] = (m + QB - 1) / QB;
+    int nj, mj, q0;
+    prefill_lengths(p, j, max_len, nj, mj, q0);
+    key[j] = mj > 0 ? nj : -1;
+    new_of[j] = mj;
+    q0_of[j] = q0;
+    rows_of[j] = (mj + QB - 1) / QB;
   }
   __syncthreads();
   for (int j = tid; j < S; j += NT) {
@@ -842,6 +848,9 @@ __device__ inline bool ranked_unit(const DecodeParams& p, int i, int& s, int& h,
       s = uniform(rank_seq[r]);
       h = off / R;
       rb = R - 1 - (off - h * R);
+      n = uniform(key[s]);
+      m = uniform(new_of[s]);
+      qs = uniform(q0_of[s]);
       return true;
     }
     carry += __shfl(incl, 63);
@@ -857,11 +866,11 @@ void paged_prefill_unit_kernel(const DecodeParams p) {
   const int lane = (int)(threadIdx.x & 63);
   const int S = p.num_seqs;
   const int max_len = p.max_blocks << p.log2_bs;
-  int s = 0, h = 0, rb = 0;
+  int s = 0, h = 0, rb = 0, n, m, qs;
   if (S <= kUnitRankSeqs) {
     // work-group k of XCD x: entry (k / c) 8c + x c + k % c of the list
     const int c = p.chunk, x = (int)(blockIdx.x & 7), k = (int)(blockIdx.x >> 3);
-    if (!ranked_unit<QB, 64 * unit_waves<D>()>(p, (k / c) * 8 * c + x * c + k % c, s, h, rb)) return;
+    if (!ranked_unit<QB, 64 * unit_waves<D>()>(p, (k / c) * 8 * c + x * c + k % c, s, h, rb, n, m, qs)) return;
   } else {
     int64_t per_head64 = 0;
     for (int base = 0; base < S; base += 64) {
@@ -910,12 +919,11 @@ void paged_prefill_unit_kernel(const DecodeParams p) {
     if (!found) return;
     s = uniform(s);
     rb = uniform(r - pre);
+    prefill_lengths(p, s, max_len, n, m, qs);
+    n = uniform(n);
+    m = uniform(m);
+    qs = uniform(qs);
   }
-  int n, m, qs;
-  prefill_lengths(p, s, max_len, n, m, qs);
-  n = uniform(n);
-  m = uniform(m);
-  qs = uniform(qs);
   const int nb = (tile_limit(n, m, QB, rb) + (1 << p.log2_bs) - 1) >> p.log2_bs;
   // the whole row block: stored directly, no record; bf16 pools stage V as
   // f16 and run again with bf16 V if it holds a value out of f16's range
